@@ -1,0 +1,256 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference of the routed-expert FFN step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this code; the GPU library never does.
+ * It shares no code with the GPU path (its own format decoding, rounding,
+ * selection and arithmetic), and it is deliberately unblocked and unfused.
+ *
+ * What it computes (LayerStoRm README, "TL;DR": the router tells which few
+ * experts each token activates; those experts' FFNs run and their outputs are
+ * combined; glm-flash-lite page, "How it works": 8 experts per layer per token):
+ *   1. logits  L[e] = fp32( sum_h x[h]*Wr[e,h] + b[e] ), summed in fp64 in index
+ *      order and rounded once to fp32 (round to nearest even);
+ *   2. top-k   the k largest logits, ties to the lower expert index, emitted in
+ *      order of descending logit then ascending index;
+ *   3. weights softmax over the k selected logits, in fp64;
+ *   4. expert FFN (SwiGLU):  g = W1 x, u = W3 x, h = silu(g) * u,
+ *      silu(z) = z / (1 + exp(-z)), y = W2 h, with every weight dequantised as
+ *      W = scale * q + min from its 4-bit code q and its block's fp16 scale/min;
+ *   5. combine out = sum_i w_i * y_{idx_i} + y_shared, in slot order i = 0..k-1,
+ *      then the shared expert with weight 1; reported in fp64 and rounded to bf16.
+ * Slab layout: see the header of the input generator (synth/synth.c); this file
+ * decodes it on its own from that description.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------- scalar formats ---------------- */
+double oracle_bf16_to_double(uint16_t b) {
+    /* bf16 is the upper half of an IEEE binary32 */
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+double oracle_fp16_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1F;
+    int mt = h & 0x3FF;
+    double v;
+    if (ex == 0) v = ldexp((double)mt, -24);                      /* subnormal */
+    else if (ex == 31) v = mt ? NAN : INFINITY;                    /* inf / nan */
+    else v = ldexp((double)(1024 + mt), ex - 25);                  /* normal */
+    return sign ? -v : v;
+}
+
+/* double -> bf16 bits, round to nearest, ties to even (8 significant bits,
+   binary32 exponent range including subnormals). */
+uint16_t oracle_double_to_bf16(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);              /* a = f * 2^e, 0.5 <= f < 1, i.e. unbiased exponent e-1 */
+    int ue = e - 1;
+    if (ue < -126) ue = -126;  /* subnormal: quantum 2^-133 */
+    double quantum = ldexp(1.0, ue - 7);
+    double n = a / quantum;    /* exact: power-of-two scaling */
+    double fl = floor(n);
+    double rem = n - fl;
+    if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = fl * quantum;
+    if (r > 3.3895313892515355e38) return sign | 0x7F80;  /* beyond the largest bf16 */
+    float f = (float)r;        /* exact: at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)((u >> 16) & 0x7FFF);
+}
+
+/* ---------------- slab decoding ---------------- */
+static int64_t matrix_bytes(int64_t rows, int64_t cols) { return rows * cols / 2 + rows * (cols / 32) * 4; }
+
+int64_t oracle_slab_bytes(int64_t H, int64_t I) { return 2 * matrix_bytes(I, H) + matrix_bytes(H, I); }
+
+/* Start of matrix `which` (0 = W1 gate [I x H], 1 = W3 up [I x H], 2 = W2 down [H x I]). */
+static const uint8_t *matrix_at(const uint8_t *slab, int64_t H, int64_t I, int which) {
+    return slab + (int64_t)which * matrix_bytes(I, H);
+}
+
+/* Dequantise row r of a [rows x cols] matrix into out[cols]. */
+static void dequant_row(const uint8_t *mat, int64_t rows, int64_t cols, int64_t r, double *out) {
+    const uint8_t *codes = mat + r * (cols / 2);
+    const uint8_t *params = mat + rows * cols / 2 + r * (cols / 32) * 4;
+    for (int64_t c = 0; c < cols; ++c) {
+        uint8_t byte = codes[c / 2];
+        int q = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+        const uint8_t *rec = params + (c / 32) * 4;
+        double scale = oracle_fp16_to_double((uint16_t)(rec[0] | (rec[1] << 8)));
+        double mn = oracle_fp16_to_double((uint16_t)(rec[2] | (rec[3] << 8)));
+        out[c] = scale * (double)q + mn;
+    }
+}
+
+/* Full dequantised matrix `which` of a slab, row-major. */
+void oracle_dequant(const uint8_t *slab, int64_t H, int64_t I, int which, double *out) {
+    int64_t rows = (which < 2) ? I : H, cols = (which < 2) ? H : I;
+    const uint8_t *mat = matrix_at(slab, H, I, which);
+    for (int64_t r = 0; r < rows; ++r) dequant_row(mat, rows, cols, r, out + r * cols);
+}
+
+/* ---------------- expert FFN ---------------- */
+/* One token through one expert.  g, u, h may be NULL (then scratch is used). */
+void oracle_expert_ffn(const uint8_t *slab, int64_t H, int64_t I, const double *x,
+                       double *g_out, double *u_out, double *h_out, double *y) {
+    double *row = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    double *g = g_out ? g_out : (double *)malloc(sizeof(double) * (size_t)I);
+    double *u = u_out ? u_out : (double *)malloc(sizeof(double) * (size_t)I);
+    double *h = h_out ? h_out : (double *)malloc(sizeof(double) * (size_t)I);
+    const uint8_t *w1 = matrix_at(slab, H, I, 0);
+    const uint8_t *w3 = matrix_at(slab, H, I, 1);
+    const uint8_t *w2 = matrix_at(slab, H, I, 2);
+    for (int64_t r = 0; r < I; ++r) {
+        double acc = 0.0;
+        dequant_row(w1, I, H, r, row);
+        for (int64_t c = 0; c < H; ++c) acc += row[c] * x[c];
+        g[r] = acc;
+        acc = 0.0;
+        dequant_row(w3, I, H, r, row);
+        for (int64_t c = 0; c < H; ++c) acc += row[c] * x[c];
+        u[r] = acc;
+        h[r] = g[r] / (1.0 + exp(-g[r])) * u[r];
+    }
+    for (int64_t r = 0; r < H; ++r) {
+        double acc = 0.0;
+        dequant_row(w2, H, I, r, row);
+        for (int64_t c = 0; c < I; ++c) acc += row[c] * h[c];
+        y[r] = acc;
+    }
+    free(row);
+    if (!g_out) free(g);
+    if (!u_out) free(u);
+    if (!h_out) free(h);
+}
+
+/* Down projection alone: y = W2 h (h has I entries, y has H). */
+void oracle_expert_down(const uint8_t *slab, int64_t H, int64_t I, const double *h, double *y) {
+    double *row = (double *)malloc(sizeof(double) * (size_t)I);
+    const uint8_t *w2 = matrix_at(slab, H, I, 2);
+    for (int64_t r = 0; r < H; ++r) {
+        double acc = 0.0;
+        dequant_row(w2, H, I, r, row);
+        for (int64_t c = 0; c < I; ++c) acc += row[c] * h[c];
+        y[r] = acc;
+    }
+    free(row);
+}
+
+/* ---------------- router ---------------- */
+/* logits[e] for one token (x is bf16 bits, Wr is [E x H] fp32, bias may be NULL). */
+static void token_logits(const uint16_t *x, int64_t H, const float *Wr, const float *bias, int64_t E,
+                         float *logits) {
+    for (int64_t e = 0; e < E; ++e) {
+        double acc = 0.0;
+        for (int64_t h = 0; h < H; ++h) acc += oracle_bf16_to_double(x[h]) * (double)Wr[e * H + h];
+        if (bias) acc += (double)bias[e];
+        logits[e] = (float)acc;  /* one rounding, to nearest even */
+    }
+}
+
+/* k largest logits, ties to the lower index, by repeated selection. */
+static void token_topk(const float *logits, int64_t E, int k, int32_t *idx) {
+    unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
+    for (int i = 0; i < k; ++i) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || logits[e] > logits[best]) best = e;  /* strict: equal keeps the lower index */
+        }
+        idx[i] = (int32_t)best;
+        taken[best] = 1;
+    }
+    free(taken);
+}
+
+/* Softmax restricted to the k selected logits, in fp64. */
+static void token_weights(const float *logits, const int32_t *idx, int k, double *w) {
+    double top = (double)logits[idx[0]];
+    double sum = 0.0;
+    for (int i = 0; i < k; ++i) {
+        w[i] = exp((double)logits[idx[i]] - top);
+        sum += w[i];
+    }
+    for (int i = 0; i < k; ++i) w[i] /= sum;
+}
+
+static int clamp_threads(int n) {
+#ifdef _OPENMP
+    if (n <= 0) n = omp_get_max_threads();
+#else
+    n = 1;
+#endif
+    return n < 1 ? 1 : n;
+}
+
+/* Routing for T tokens: logits [T x E] (may be NULL), idx [T x k], w [T x k]. */
+void oracle_router(const uint16_t *x, int64_t T, int64_t H, const float *Wr, const float *bias, int64_t E,
+                   int k, float *logits_out, int32_t *idx, double *w, int nthreads) {
+    nthreads = clamp_threads(nthreads);
+    #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        float *lg = (float *)malloc(sizeof(float) * (size_t)E);
+        token_logits(x + t * H, H, Wr, bias, E, lg);
+        token_topk(lg, E, k, idx + t * k);
+        token_weights(lg, idx + t * k, k, w + t * k);
+        if (logits_out) memcpy(logits_out + t * E, lg, sizeof(float) * (size_t)E);
+        free(lg);
+    }
+}
+
+/* ---------------- one MoE layer ---------------- */
+/* slabs[e] = host slab of routed expert e; shared = host slab of the always-on
+   shared expert or NULL.  Tokens listed in `rows` (n_rows of them; NULL = all T)
+   are the only ones computed; out64/out_bf16 are [T x H] and only those rows are
+   written.  idx/w are computed for every token. */
+void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                      const float *Wr, const float *bias, const uint8_t *const *slabs, const uint8_t *shared,
+                      const int32_t *rows, int64_t n_rows, int nthreads,
+                      int32_t *idx, double *w, double *out64, uint16_t *out_bf16) {
+    nthreads = clamp_threads(nthreads);
+    oracle_router(x, T, H, Wr, bias, E, k, NULL, idx, w, nthreads);
+    int64_t nt = rows ? n_rows : T;
+    int per = k + (shared ? 1 : 0);
+    int64_t npairs = nt * per;
+    double *y = (double *)malloc(sizeof(double) * (size_t)(npairs * H));
+    /* every (token, expert) pair independently */
+    #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t p = 0; p < npairs; ++p) {
+        int64_t j = p / per, i = p % per;
+        int64_t t = rows ? rows[j] : j;
+        double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+        for (int64_t h = 0; h < H; ++h) xd[h] = oracle_bf16_to_double(x[t * H + h]);
+        const uint8_t *slab = (i < k) ? slabs[idx[t * k + i]] : shared;
+        oracle_expert_ffn(slab, H, I, xd, NULL, NULL, NULL, y + p * H);
+        free(xd);
+    }
+    /* combine in slot order, then the shared expert */
+    #pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t j = 0; j < nt; ++j) {
+        int64_t t = rows ? rows[j] : j;
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int i = 0; i < k; ++i) acc += w[t * k + i] * y[(j * per + i) * H + h];
+            if (shared) acc += y[(j * per + k) * H + h];
+            out64[t * H + h] = acc;
+            out_bf16[t * H + h] = oracle_double_to_bf16(acc);
+        }
+    }
+    free(y);
+}

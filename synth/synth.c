@@ -1,0 +1,258 @@
+/*
+ * synth.c -- seeded, counter-based synthetic inputs for the routed-expert FFN step.
+ *
+ * This module only produces input bytes: hidden states, router weights, router
+ * bias and 4-bit expert slabs.  It holds none of the method's arithmetic
+ * (no routing, no dequantisation, no FFN), so both the CPU oracle and the GPU
+ * path may consume what it writes.
+ *
+ * Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC'11), keyed by the 64-bit config seed, with
+ * the 128-bit counter holding (index, expert, layer|kind|matrix, step).  Every
+ * element is therefore addressable on its own and the fill is parallel and
+ * order independent.  Normals use the Box-Muller transform.
+ *
+ * Expert slab byte layout (one contiguous slab per expert):
+ *   matrix 0 = W1 (gate) [I rows x H cols], matrix 1 = W3 (up) [I x H],
+ *   matrix 2 = W2 (down) [H rows x I cols]; each matrix with R rows and K cols:
+ *     codes : R*K/2 bytes, row-major; byte b of a row holds column 2b in bits
+ *             0-3 and column 2b+1 in bits 4-7 (codes are 0..15)
+ *     params: R*(K/32) records of 4 bytes, row-major over (row, block);
+ *             record = fp16 scale (bytes 0-1) then fp16 min (bytes 2-3)
+ *   matrix bytes = 0.625*R*K, slab = W1 | W3 | W2.
+ * Value distributions: x ~ N(0,1) rounded to bf16; router W ~ N(0, 0.02^2)
+ * rounded to fp32; codes uniform on 0..15; scale = fp16(|N(0, 0.02^2)|);
+ * min = -8*scale (exact in fp16).  The scale of block b is drawn from Philox
+ * call b/2 (cosine branch for even b, sine branch for odd b).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { KIND_X = 1, KIND_WR = 2, KIND_BIAS = 3, KIND_CODES = 4, KIND_PARAMS = 5 };
+
+/* ---------------- Philox4x32-10 ---------------- */
+static inline void mulhilo32(uint32_t a, uint32_t b, uint32_t *hi, uint32_t *lo) {
+    uint64_t p = (uint64_t)a * (uint64_t)b;
+    *hi = (uint32_t)(p >> 32);
+    *lo = (uint32_t)p;
+}
+
+static inline void philox_core(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        uint32_t hi0, lo0, hi1, lo1;
+        mulhilo32(0xD2511F53u, c0, &hi0, &lo0);
+        mulhilo32(0xCD9E8D57u, c2, &hi1, &lo1);
+        uint32_t n0 = hi1 ^ c1 ^ k0;
+        uint32_t n1 = lo1;
+        uint32_t n2 = hi0 ^ c3 ^ k1;
+        uint32_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+void synth_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+    philox_core(ctr_in, key_in, out);
+}
+
+static inline void draw(uint64_t seed, uint32_t kind, uint32_t step, uint32_t layer,
+                        uint32_t expert, uint32_t matrix, uint32_t index, uint32_t out[4]) {
+    uint32_t ctr[4] = { index, expert, (layer << 16) | (kind << 8) | (matrix & 0xFFu), step };
+    uint32_t key[2] = { (uint32_t)seed, (uint32_t)(seed >> 32) };
+    philox_core(ctr, key, out);
+}
+
+/* Standard normal from two 32-bit words (Box-Muller, cosine branch). */
+static inline double normal_from(uint32_t a, uint32_t b) {
+    const double two32 = 4294967296.0;
+    double u1 = ((double)a + 0.5) / two32; /* (0,1) */
+    double u2 = ((double)b + 0.5) / two32;
+    return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925286766559 * u2);
+}
+
+/* Two standard normals from two 32-bit words (Box-Muller, cosine and sine branch). */
+static inline void normal_pair_from(uint32_t a, uint32_t b, double *z0, double *z1) {
+    const double two32 = 4294967296.0;
+    double u1 = ((double)a + 0.5) / two32;
+    double u2 = ((double)b + 0.5) / two32;
+    double rad = sqrt(-2.0 * log(u1)), ang = 6.283185307179586476925286766559 * u2;
+    *z0 = rad * cos(ang);
+    *z1 = rad * sin(ang);
+}
+
+/* ---------------- input rounding (round to nearest, ties to even) ---------------- */
+/* Round a finite double to a float with `mant` explicit significand bits and the
+   exponent range of the target format, returning the rounded value as double. */
+static double round_to_format(double v, int sig_bits, int emin) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e = ilogb(v);          /* v = m * 2^e, 1 <= |m| < 2 */
+    if (e < emin) e = emin;    /* subnormal range: fixed quantum */
+    double q = ldexp(v, sig_bits - 1 - e);
+    q = nearbyint(q);          /* default rounding mode: to nearest, ties to even */
+    return ldexp(q, e - (sig_bits - 1));
+}
+
+uint16_t synth_double_to_bf16(double v) {
+    double r = round_to_format(v, 8, -126);
+    float f = (fabs(r) > 3.4028234663852886e38) ? (r > 0 ? INFINITY : -INFINITY)
+                                                 : (float)r; /* exact: <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* double -> fp16 bits, round to nearest even, on the integer significand. */
+uint16_t synth_double_to_fp16(double v) {
+    uint64_t u;
+    memcpy(&u, &v, 8);
+    uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+    int e = (int)((u >> 52) & 0x7FF) - 1023;
+    uint64_t frac = u & ((1ull << 52) - 1);
+    if (e == 1024) return sign | (frac ? 0x7E00u : 0x7C00u);   /* inf / nan */
+    if (e < -26) return sign;                                      /* below half the min subnormal */
+    uint64_t m = frac | (1ull << 52);                              /* significand, value m * 2^(e-52) */
+    int shift = (e >= -14) ? 42 : 42 + (-14 - e);                  /* keep 10 fraction bits (normal) */
+    uint64_t half = 1ull << (shift - 1);
+    uint64_t q = m >> shift, rem = m & ((1ull << shift) - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+    if (e >= -14) {
+        int ee = e;
+        if (q == 2048) { q = 1024; ++ee; }
+        if (ee > 15) return sign | 0x7C00u;
+        return sign | (uint16_t)(((uint32_t)(ee + 15) << 10) | (uint32_t)(q - 1024));
+    }
+    return sign | (uint16_t)q;  /* subnormal; q == 1024 rolls into the smallest normal */
+}
+
+static int clamp_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    return nthreads < 1 ? 1 : nthreads;
+}
+
+/* ---------------- generators ---------------- */
+/* x[t, h] for one (step, layer): N(0,1) rounded to bf16. */
+void synth_x_bf16(uint64_t seed, uint32_t step, uint32_t layer, int64_t T, int64_t H,
+                  uint16_t *out, int nthreads) {
+    int64_t n = T * H;
+    nthreads = clamp_threads(nthreads);
+    #pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t r[4];
+        draw(seed, KIND_X, step, layer, 0, 0, (uint32_t)i, r);
+        out[i] = synth_double_to_bf16(normal_from(r[0], r[1]));
+    }
+}
+
+/* router weight Wr[e, h] for one layer: N(0, 0.02^2) rounded to fp32. */
+void synth_router_w(uint64_t seed, uint32_t layer, int64_t E, int64_t H, float *out, int nthreads) {
+    int64_t n = E * H;
+    nthreads = clamp_threads(nthreads);
+    #pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t r[4];
+        draw(seed, KIND_WR, 0, layer, 0, 0, (uint32_t)i, r);
+        out[i] = (float)(0.02 * normal_from(r[0], r[1]));
+    }
+}
+
+/* Seeded permutation rank[e] in 1..E (Fisher-Yates driven by Philox words). */
+void synth_rank_permutation(uint64_t seed, uint32_t layer, int64_t E, int32_t *rank) {
+    for (int64_t e = 0; e < E; ++e) rank[e] = (int32_t)(e + 1);
+    for (int64_t i = E - 1; i > 0; --i) {
+        uint32_t r[4];
+        draw(seed, KIND_BIAS, 0, layer, 0, 0, (uint32_t)i, r);
+        uint64_t wide = ((uint64_t)r[0] << 32) | r[1];
+        int64_t j = (int64_t)(wide % (uint64_t)(i + 1));
+        int32_t t = rank[i]; rank[i] = rank[j]; rank[j] = t;
+    }
+}
+
+/* Zipf-popularity router bias: bias[e] = -s * ln(rank[e]), rounded to fp32. */
+void synth_zipf_bias(uint64_t seed, uint32_t layer, int64_t E, double s, float *out) {
+    int32_t *rank = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    synth_rank_permutation(seed, layer, E, rank);
+    for (int64_t e = 0; e < E; ++e) out[e] = (float)(-s * log((double)rank[e]));
+    free(rank);
+}
+
+int64_t synth_matrix_bytes(int64_t rows, int64_t cols) { return rows * cols / 2 + rows * (cols / 32) * 4; }
+int64_t synth_slab_bytes(int64_t H, int64_t I) { return 2 * synth_matrix_bytes(I, H) + synth_matrix_bytes(H, I); }
+
+static inline void write_params(double z, uint8_t *rec) {
+    uint16_t sc = synth_double_to_fp16(fabs(0.02 * z));
+    /* min = -8 * scale: decode the fp16 scale exactly, scale by -8 (exact in fp16). */
+    uint32_t ex = (sc >> 10) & 0x1F, mt = sc & 0x3FF;
+    double sv = ex ? ldexp((double)(mt | 0x400), (int)ex - 25) : ldexp((double)mt, -24);
+    uint16_t mn = synth_double_to_fp16(-8.0 * sv);
+    rec[0] = (uint8_t)(sc & 0xFF);
+    rec[1] = (uint8_t)(sc >> 8);
+    rec[2] = (uint8_t)(mn & 0xFF);
+    rec[3] = (uint8_t)(mn >> 8);
+}
+
+/* Scale of block b comes from Philox call b/2: the cosine branch for even b, the
+   sine branch for odd b. */
+static inline void params_for_pair(uint64_t seed, uint32_t layer, uint32_t expert, uint32_t m,
+                                   int64_t pair, int64_t nblocks, uint8_t *params) {
+    uint32_t r[4];
+    double z0, z1;
+    draw(seed, KIND_PARAMS, 0, layer, expert, m, (uint32_t)pair, r);
+    normal_pair_from(r[0], r[1], &z0, &z1);
+    write_params(z0, params + 8 * pair);
+    if (2 * pair + 1 < nblocks) write_params(z1, params + 8 * pair + 4);
+}
+
+/* Fill part `part` of `nparts` of one matrix (codes then params). */
+static void fill_matrix_part(uint64_t seed, uint32_t layer, uint32_t expert, uint32_t m,
+                             int64_t rows, int64_t cols, uint8_t *base, int64_t part, int64_t nparts) {
+    int64_t code_bytes = rows * cols / 2;
+    int64_t nchunks = code_bytes / 16;
+    int64_t nblocks = rows * (cols / 32);
+    int64_t c0 = nchunks * part / nparts, c1 = nchunks * (part + 1) / nparts;
+    for (int64_t c = c0; c < c1; ++c) {
+        uint32_t r[4];
+        draw(seed, KIND_CODES, 0, layer, expert, m, (uint32_t)c, r);
+        memcpy(base + 16 * c, r, 16);
+    }
+    uint8_t *params = base + code_bytes;
+    int64_t npairs = (nblocks + 1) / 2;
+    int64_t b0 = npairs * part / nparts, b1 = npairs * (part + 1) / nparts;
+    for (int64_t b = b0; b < b1; ++b) params_for_pair(seed, layer, expert, m, b, nblocks, params);
+}
+
+/* Many slabs in parallel: outs[i] receives expert experts[i] of `layer`.  Expert
+   ids >= E may be used for shared experts; they select another Philox stream. */
+void synth_expert_slabs(uint64_t seed, uint32_t layer, const uint32_t *experts, int64_t n,
+                        int64_t H, int64_t I, uint8_t *const *outs, int nthreads) {
+    nthreads = clamp_threads(nthreads);
+    /* Split every matrix into parts so a handful of slabs still keeps all threads busy. */
+    const int64_t nparts = 16;
+    int64_t m13 = synth_matrix_bytes(I, H);
+    int64_t njobs = n * 3 * nparts;
+    #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t job = 0; job < njobs; ++job) {
+        int64_t i = job / (3 * nparts);
+        uint32_t m = (uint32_t)((job / nparts) % 3);
+        int64_t part = job % nparts;
+        int64_t rows = (m < 2) ? I : H, cols = (m < 2) ? H : I;
+        fill_matrix_part(seed, layer, experts[i], m, rows, cols, outs[i] + m * m13, part, nparts);
+    }
+}
+
+void synth_expert_slab(uint64_t seed, uint32_t layer, uint32_t expert, int64_t H, int64_t I, uint8_t *out) {
+    uint8_t *outs[1] = { out };
+    synth_expert_slabs(seed, layer, &expert, 1, H, I, outs, 1);
+}
