@@ -1,0 +1,210 @@
+/*
+ * moe.h -- C ABI of the routed-expert FFN step on one AMD Instinct MI355X (gfx950).
+ *
+ * The step (LayerStoRm README, "TL;DR"): hidden states and a router go in; the
+ * router picks a few experts per token; the full expert set lives in pinned host
+ * RAM and GPU memory is used as a cache of experts, with the activated experts
+ * streamed over PCIe and overlapped with compute; the experts' FFN outputs are
+ * combined.  The GPU does all arithmetic and the host only manages the cache and
+ * moves data (rebasdaily article, section "keep the experts in the warehouse").
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers unless the name ends in _host.  The caller owns
+ *    every buffer; the library owns only the moe_cache object and the hipEvents
+ *    it creates.  No call allocates device memory.
+ *  - `stream` arguments are hipStream_t handles passed as void* (NULL = the
+ *    default stream).  Device work is enqueued asynchronously; nothing blocks
+ *    except where stated.
+ *  - Return value: MOE_OK (0) or a negative moe_status.  Arguments are validated
+ *    before anything is enqueued, so a failed call has enqueued nothing.  A HIP
+ *    runtime failure returns MOE_E_HIP and moe_last_hip_error() gives the
+ *    hipError_t; moe_last_error_message() describes the last failure of the
+ *    calling thread.  Device faults surface at the caller's next synchronisation.
+ *  - bf16 and fp16 values are passed as uint16_t bit patterns.
+ *  - Every kernel is deterministic: no floating-point atomics, fixed reduction
+ *    orders, so repeated calls on the same inputs give bit-identical outputs.
+ *
+ * Expert slab format (one contiguous slab per expert, hidden H, intermediate I,
+ * H % 32 == 0, I % 32 == 0):
+ *   matrix 0 = W1 (gate) [I rows x H cols], 1 = W3 (up) [I x H], 2 = W2 (down) [H x I].
+ *   Each matrix with R rows and K columns is R*K/2 code bytes (row-major; byte b
+ *   of a row holds column 2b in bits 0-3 and column 2b+1 in bits 4-7), followed by
+ *   R*(K/32) 4-byte records (row-major over (row, 32-column block)): fp16 scale,
+ *   then fp16 min.  Weight value = scale * code + min (exact in fp32).
+ *   Slab = W1 | W3 | W2, moe_expert_bytes(H, I) = 1.875 * H * I bytes.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_E_ARG = -1,        /* NULL pointer, negative size, bad enum value */
+    MOE_E_SHAPE = -2,      /* unsupported sizes (H or I not a multiple of 32, k > E, ...) */
+    MOE_E_NOT_PINNED = -3, /* a host expert slab is not page-locked memory */
+    MOE_E_NOMEM = -4,      /* caller-provided workspace or pool too small */
+    MOE_E_CAPACITY = -5,   /* more experts requested at once than the cache has slots */
+    MOE_E_HIP = -6,        /* a HIP runtime call failed; see moe_last_hip_error() */
+    MOE_E_STATE = -7       /* call not valid in the object's current state */
+} moe_status;
+
+/* Static description of a status code. */
+const char *moe_status_str(int status);
+/* hipError_t behind the calling thread's last MOE_E_HIP (0 if none). */
+int moe_last_hip_error(void);
+/* Human-readable detail of the calling thread's last failure ("" if none). */
+const char *moe_last_error_message(void);
+/* Library version, e.g. 100 for 1.0.0. */
+int moe_version(void);
+
+/* Bytes of one expert slab: 1.875 * hidden * inter (format above).  0 if the
+   sizes are not positive multiples of 32. */
+size_t moe_expert_bytes(int hidden, int inter);
+
+/* ------------------------------------------------------------------ router
+ * Router logits, top-k selection and renormalised gate weights (LayerStoRm
+ * README "TL;DR": the router tells which experts a token activates;
+ * glm-flash-lite page "How it works": 8 experts per layer per token).
+ *   logit[t,e] = fp32( sum_h x[t,h] * w_router[e,h] + bias[e] ), products and
+ *                sum in fp64, one final rounding to nearest even;
+ *   topk_idx[t,:] = the k largest logits, ties to the lower expert index, in
+ *                order of descending logit then ascending index;
+ *   topk_w[t,i] = exp(l_i - l_0) / sum_j exp(l_j - l_0) over the k selected (fp32).
+ * x [T,H] bf16 row-major; w_router [E,H] fp32 row-major; bias [E] fp32 or NULL;
+ * topk_idx [T,k] int32; topk_w [T,k] fp32.  1 <= k <= min(E, 64), E <= 1024,
+ * H % 32 == 0.  Inputs must be finite.
+ * workspace: moe_router_workspace_bytes(T, E) bytes of device memory whose first
+ * 256 bytes must be zero before the first call on that buffer (every call leaves
+ * them zero again); calls sharing a workspace must not overlap in time. */
+size_t moe_router_workspace_bytes(int T, int E);
+int moe_router_topk(const uint16_t *x, int T, int H, const float *w_router, const float *bias, int E,
+                    int k, int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* ------------------------------------------------------------------ dispatch
+ * Token -> expert permutation of the T*k (token, slot) pairs p = t*k + i:
+ * counting sort by expert, stable in p.  count[e] = pairs routed to e;
+ * offset[e] = exclusive prefix sum (offset[E] = T*k); pair_of_row[offset[e]+j] =
+ * the j-th smallest pair index routed to e.  Requires T*k <= 16384, E <= 1024. */
+int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
+                int32_t *pair_of_row, void *stream);
+
+/* ------------------------------------------------------------------ expert cache
+ * HBM-resident expert cache with per-layer LRU eviction, fed from pinned host RAM
+ * by hipMemcpyAsync on a copy stream (LayerStoRm README "TL;DR": the full expert
+ * set is pinned in host RAM, GPU memory is used as a cache, streaming overlaps
+ * compute).  Per layer there are `slots_per_layer` slots of moe_expert_bytes(H,I)
+ * bytes in `slot_pool` (layer l's slots start at l * slots * slab bytes).
+ * expert_table: device array [n_layers * n_experts] of slab pointers the library
+ * keeps current on the copy stream (NULL = not resident); kernels read layer l's
+ * entries at expert_table + l * n_experts.  experts_host: host array
+ * [n_layers * n_experts] of pinned host slab pointers.  The caller owns the
+ * pool, the table and the host slabs, which must outlive the cache.
+ * LRU rule per layer: a request touches its hits first (ascending expert id),
+ * then its misses (ascending id); each miss evicts the least recently touched slot
+ * that the same request does not need and no unreleased request holds (never-used
+ * slots first, ties to the lower slot).  Not thread-safe: one host thread per cache. */
+typedef struct moe_cache moe_cache;
+typedef struct moe_cache_desc {
+    int n_layers;
+    int n_experts;
+    int hidden;
+    int inter;
+    int slots_per_layer;
+} moe_cache_desc;
+
+/* Validates the description (slots <= experts), checks every host slab is pinned
+   (MOE_E_NOT_PINNED otherwise), creates the events, clears expert_table with a
+   blocking copy, and returns the cache in *out. */
+int moe_cache_create(const moe_cache_desc *desc, const void *const *experts_host, void *slot_pool,
+                     void **expert_table, void *copy_stream, moe_cache **out);
+/* Query only: slot_host[i] = slot of experts_host[i] or -1, *n_hits = number resident. */
+int moe_cache_lookup(moe_cache *cache, int layer, const int32_t *experts_host, int n, int32_t *slot_host,
+                     int *n_hits);
+/* Acquire n distinct experts of `layer` (n <= slots, else MOE_E_CAPACITY): touch
+   hits, pick victims, enqueue on the copy stream each victim's wait for its last
+   release, the H2D copy of each missed slab and the table update, then make
+   `compute_stream` wait for them.  *n_copies (may be NULL) = misses streamed.
+   The acquired slots stay held until moe_cache_release(layer).  On a HIP failure
+   the slots being filled are left empty (their experts are misses again). */
+int moe_cache_prefetch(moe_cache *cache, int layer, const int32_t *experts_host, int n,
+                       void *compute_stream, int *n_copies);
+/* Records on `compute_stream` that every slot held by `layer` may be overwritten
+   once the work enqueued so far on that stream is done, and un-holds them. */
+int moe_cache_release(moe_cache *cache, int layer, void *compute_stream);
+/* Cumulative hit / miss counts (per requested expert) and H2D bytes streamed. */
+int moe_cache_stats(const moe_cache *cache, uint64_t *hits, uint64_t *misses, uint64_t *h2d_bytes);
+/* Waits for outstanding copies, empties every slot, clears the table, zeroes stats. */
+int moe_cache_reset(moe_cache *cache);
+/* Waits for outstanding copies and frees the library's events and the object. */
+void moe_cache_destroy(moe_cache *cache);
+
+/* Test hook: a cache whose copy engine only records commands (no HIP calls).
+   slot_pool is then just a base address used to form slot pointers.  If
+   fail_copy_at > 0 the fail_copy_at-th copy reports MOE_E_HIP. */
+int moe_cache_create_recording(const moe_cache_desc *desc, uintptr_t slot_pool, int fail_copy_at,
+                               moe_cache **out);
+/* Recorded commands of a recording cache, 4 int64 per command:
+   (kind, a, b, c) with kind 1 = wait(slot, release_id, -), 2 = copy(layer, expert, slot),
+   3 = table(layer, expert, slot or -1), 4 = ready(layer, -, -), 5 = release(layer, id, n_slots).
+   Returns the total number of commands; writes at most max_cmds of them. */
+int64_t moe_cache_trace(const moe_cache *cache, int64_t *cmds, int64_t max_cmds);
+
+/* ------------------------------------------------------------------ expert FFN
+ * Fused 4-bit block dequant + SwiGLU expert FFN for every (token, slot) pair
+ * whose expert the mask admits, plus an always-on shared expert:
+ *   g = W1 x_t, u = W3 x_t, h = bf16(silu(g) * u), y = W2 h   (fp32 accumulation)
+ * x [T,H] bf16; topk_idx [T,k]; expert_table: device array [E] of this layer's
+ * slab pointers (entries of masked-off experts are never read); shared_slab:
+ * device slab of the shared expert or NULL; expert_mask: device uint8 [E]
+ * (nonzero = compute this expert's pairs) or NULL for all.
+ * y: [T*k + (shared ? T : 0), H] fp32; row t*k+i is pair (t, i), row T*k+t is the
+ * shared expert for token t.  Rows of masked-off pairs are left untouched.
+ * path: MOE_FFN_AUTO picks by T*k; the others force a kernel family (for tests).
+ * workspace: moe_expert_ffn_workspace_bytes(...) bytes, contents don't care. */
+enum { MOE_FFN_AUTO = 0, MOE_FFN_PAIRS = 1, MOE_FFN_GROUPED = 2, MOE_FFN_MFMA = 3 };
+size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int has_shared);
+int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                   const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                   float *y, void *workspace, size_t workspace_bytes, int path, void *stream);
+
+/* The two steps of moe_expert_ffn on their own, for callers that keep h or the
+ * permutation themselves (and to time each kernel alone):
+ *   moe_expert_gate_up: h = bf16(silu(W1 x) * (W3 x))   (dequant + gate/up + SwiGLU)
+ *   moe_expert_down:    y = W2 h                         (dequant + down projection)
+ * h: [T*k + (shared ? T : 0), I] bf16 with the same row numbering as y.
+ * count/offset/pair_of_row: a permutation from moe_permute on the same topk_idx
+ * (one kernel group per expert, weights read once per expert), or all three NULL
+ * (one group per (token, slot) pair).  path: MOE_FFN_AUTO follows the presence
+ * of the permutation; MOE_FFN_GROUPED requires it. */
+int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                       const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                       const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                       uint16_t *h, int path, void *stream);
+int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                    const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                    const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                    float *y, int path, void *stream);
+
+/* ------------------------------------------------------------------ combine
+ * Weighted combine in a fixed order, fp32, rounded once to bf16:
+ *   out[t,:] = bf16( sum_{i=0..k-1} topk_w[t,i] * y[t*k+i,:] + (has_shared ? y[T*k+t,:] : 0) ).
+ * y as produced by moe_expert_ffn; out [T,H] bf16. */
+int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,
+                void *stream);
+
+/* ------------------------------------------------------------------ debug
+ * Dequantise matrix `which` (0 = W1, 1 = W3, 2 = W2) of a device slab into out
+ * (fp32, row-major [rows x cols]); exact, for round-trip tests of the format. */
+int moe_debug_dequant(const void *slab, int H, int I, int which, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,56 @@
+// Status codes, thread-local error state and format helpers of the C ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "moe.h"
+
+namespace {
+thread_local int g_last_hip = 0;
+thread_local char g_last_msg[512] = "";
+}  // namespace
+
+namespace moe {
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_msg, sizeof g_last_msg, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int fail_hip(hipError_t err, const char *what) {
+    g_last_hip = (int)err;
+    snprintf(g_last_msg, sizeof g_last_msg, "%s failed: %s (%d)", what, hipGetErrorString(err), (int)err);
+    return MOE_E_HIP;
+}
+
+}  // namespace moe
+
+extern "C" const char *moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_E_ARG: return "invalid argument";
+        case MOE_E_SHAPE: return "unsupported shape";
+        case MOE_E_NOT_PINNED: return "host memory is not pinned";
+        case MOE_E_NOMEM: return "workspace or pool too small";
+        case MOE_E_CAPACITY: return "more experts requested than cache slots";
+        case MOE_E_HIP: return "HIP runtime error";
+        case MOE_E_STATE: return "invalid state";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int moe_last_hip_error(void) { return g_last_hip; }
+
+extern "C" const char *moe_last_error_message(void) { return g_last_msg; }
+
+extern "C" int moe_version(void) { return 100; }
+
+extern "C" size_t moe_expert_bytes(int hidden, int inter) {
+    if (hidden <= 0 || inter <= 0 || hidden % 32 || inter % 32) return 0;
+    // three matrices of hidden*inter 4-bit codes plus one 4-byte record per 32 codes
+    return (size_t)3 * hidden * inter * 5 / 8;
+}

@@ -1,0 +1,443 @@
+// HBM expert cache: per-layer slot table with LRU eviction, fed from pinned host
+// RAM by hipMemcpyAsync on a copy stream and ordered with hipEvents.
+//
+// LayerStoRm README ("TL;DR"): the full expert set stays pinned in host RAM,
+// GPU memory is used as a cache, activated experts are streamed over PCIe and
+// the transfers overlap compute; the rebasdaily article ("keep the experts in
+// the warehouse") adds that the host only manages the runtime and moves data.
+// The replacement rule (least recently used, hits touched before misses,
+// ascending expert id, never evict what the same request needs) is this
+// library's reading: the pages name the cache but not its policy.
+//
+// Ordering, per layer:
+//   copy stream   : [wait release of victim slot] -> H2D slab copy -> ... ->
+//                   table update kernel -> record ready
+//   compute stream: wait ready -> FFN kernels -> moe_cache_release records the
+//                   release event that the next copy into those slots waits for.
+#include <algorithm>
+#include <cstring>
+#include <memory>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kTableBatch = 64;
+constexpr int kReleaseRing = 8;
+
+struct TableUpdate {
+    int n;
+    int experts[kTableBatch];
+    const void *ptrs[kTableBatch];
+};
+
+__global__ void table_update_kernel(const void **table, TableUpdate u) {
+    const int i = threadIdx.x;
+    if (i < u.n) table[u.experts[i]] = u.ptrs[i];
+}
+
+__global__ void table_clear_kernel(const void **table, size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) table[i] = nullptr;
+}
+
+// ------------------------------------------------------------------ copy engines
+struct Engine {
+    virtual ~Engine() = default;
+    virtual int wait_release(int layer, int slot, long long release_id) = 0;
+    virtual int copy(int layer, int expert, int slot, void *dst, const void *src, size_t bytes) = 0;
+    virtual int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
+                      const std::vector<int> &slots) = 0;
+    virtual int ready(int layer, void *compute_stream) = 0;
+    virtual int release(int layer, long long release_id, int n_slots, void *compute_stream) = 0;
+    virtual int sync() = 0;
+    virtual int clear_table() = 0;
+};
+
+struct HipEngine final : Engine {
+    int L = 0, E = 0;
+    hipStream_t copy_stream = nullptr;
+    const void **tbl = nullptr;
+    std::vector<hipEvent_t> ready_ev;    // [L]
+    std::vector<hipEvent_t> release_ev;  // [L * kReleaseRing]
+
+    int init(int layers, int experts, hipStream_t cs, void **table_dev) {
+        L = layers;
+        E = experts;
+        copy_stream = cs;
+        tbl = (const void **)table_dev;
+        ready_ev.assign(L, nullptr);
+        release_ev.assign((size_t)L * kReleaseRing, nullptr);
+        for (auto &e : ready_ev) MOE_TRY_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        for (auto &e : release_ev) MOE_TRY_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        return MOE_OK;
+    }
+    ~HipEngine() override {
+        if (copy_stream) (void)hipStreamSynchronize(copy_stream);
+        for (auto e : ready_ev)
+            if (e) (void)hipEventDestroy(e);
+        for (auto e : release_ev)
+            if (e) (void)hipEventDestroy(e);
+    }
+    int wait_release(int layer, int, long long id) override {
+        MOE_TRY_HIP(hipStreamWaitEvent(copy_stream, release_ev[(size_t)layer * kReleaseRing + id % kReleaseRing], 0));
+        return MOE_OK;
+    }
+    int copy(int, int, int, void *dst, const void *src, size_t bytes) override {
+        MOE_TRY_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, copy_stream));
+        return MOE_OK;
+    }
+    int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
+              const std::vector<int> &) override {
+        for (size_t i = 0; i < experts.size(); i += kTableBatch) {
+            TableUpdate u{};
+            u.n = (int)std::min<size_t>(kTableBatch, experts.size() - i);
+            for (int j = 0; j < u.n; ++j) {
+                u.experts[j] = experts[i + j];
+                u.ptrs[j] = ptrs[i + j];
+            }
+            hipLaunchKernelGGL(table_update_kernel, dim3(1), dim3(kTableBatch), 0, copy_stream,
+                               tbl + (size_t)layer * E, u);
+            MOE_LAUNCH_CHECK("table_update_kernel");
+        }
+        return MOE_OK;
+    }
+    int ready(int layer, void *compute_stream) override {
+        MOE_TRY_HIP(hipEventRecord(ready_ev[layer], copy_stream));
+        MOE_TRY_HIP(hipStreamWaitEvent((hipStream_t)compute_stream, ready_ev[layer], 0));
+        return MOE_OK;
+    }
+    int release(int layer, long long id, int, void *compute_stream) override {
+        MOE_TRY_HIP(hipEventRecord(release_ev[(size_t)layer * kReleaseRing + id % kReleaseRing],
+                                   (hipStream_t)compute_stream));
+        return MOE_OK;
+    }
+    int sync() override {
+        MOE_TRY_HIP(hipStreamSynchronize(copy_stream));
+        return MOE_OK;
+    }
+    int clear_table() override {
+        const size_t n = (size_t)L * E;
+        hipLaunchKernelGGL(table_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, copy_stream, tbl, n);
+        MOE_LAUNCH_CHECK("table_clear_kernel");
+        MOE_TRY_HIP(hipStreamSynchronize(copy_stream));
+        return MOE_OK;
+    }
+};
+
+// Records every command instead of issuing it (host-only tests of the policy).
+struct RecordingEngine final : Engine {
+    std::vector<int64_t> cmds;  // 4 per command
+    int fail_copy_at = 0, copies = 0;
+    void put(int64_t k, int64_t a, int64_t b, int64_t c) {
+        cmds.push_back(k);
+        cmds.push_back(a);
+        cmds.push_back(b);
+        cmds.push_back(c);
+    }
+    int wait_release(int, int slot, long long id) override {
+        put(1, slot, id, -1);
+        return MOE_OK;
+    }
+    int copy(int layer, int expert, int slot, void *, const void *, size_t) override {
+        ++copies;
+        if (fail_copy_at > 0 && copies == fail_copy_at)
+            return moe::fail_hip(hipErrorInvalidValue, "recorded copy (injected failure)");
+        put(2, layer, expert, slot);
+        return MOE_OK;
+    }
+    int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &,
+              const std::vector<int> &slots) override {
+        for (size_t i = 0; i < experts.size(); ++i) put(3, layer, experts[i], slots[i]);
+        return MOE_OK;
+    }
+    int ready(int layer, void *) override {
+        put(4, layer, -1, -1);
+        return MOE_OK;
+    }
+    int release(int layer, long long id, int n_slots, void *) override {
+        put(5, layer, id, n_slots);
+        return MOE_OK;
+    }
+    int sync() override { return MOE_OK; }
+    int clear_table() override { return MOE_OK; }
+};
+
+}  // namespace
+
+struct moe_cache {
+    moe_cache_desc d{};
+    size_t slab_bytes = 0;
+    std::vector<const void *> host;  // [L * E]
+    uintptr_t pool = 0;
+    std::unique_ptr<Engine> engine;
+    RecordingEngine *recorder = nullptr;
+    // per layer state
+    std::vector<int> slot_of;            // [L * E]
+    std::vector<int> expert_of;          // [L * C]
+    std::vector<unsigned long long> stamp;  // [L * C], 0 = never used
+    std::vector<char> held;              // [L * C]
+    std::vector<long long> last_release; // [L * C], -1 = never released
+    std::vector<long long> next_release; // [L]
+    unsigned long long clock = 0;
+    uint64_t hits = 0, misses = 0, bytes = 0;
+
+    int C() const { return d.slots_per_layer; }
+    void *slot_ptr(int layer, int slot) const {
+        return (void *)(pool + ((size_t)layer * C() + slot) * slab_bytes);
+    }
+    void clear_state() {
+        const size_t L = d.n_layers, E = d.n_experts, Cs = C();
+        slot_of.assign(L * E, -1);
+        expert_of.assign(L * Cs, -1);
+        stamp.assign(L * Cs, 0);
+        held.assign(L * Cs, 0);
+        last_release.assign(L * Cs, -1);
+        next_release.assign(L, 0);
+        clock = 0;
+        hits = misses = bytes = 0;
+    }
+};
+
+namespace {
+
+int validate_desc(const moe_cache_desc *d) {
+    if (!d) return moe::fail(MOE_E_ARG, "cache: NULL desc");
+    if (d->n_layers < 1 || d->n_experts < 1 || d->slots_per_layer < 1)
+        return moe::fail(MOE_E_ARG, "cache: layers=%d experts=%d slots=%d", d->n_layers, d->n_experts,
+                         d->slots_per_layer);
+    if (d->slots_per_layer > d->n_experts)
+        return moe::fail(MOE_E_SHAPE, "cache: slots %d > experts %d", d->slots_per_layer, d->n_experts);
+    if (moe_expert_bytes(d->hidden, d->inter) == 0)
+        return moe::fail(MOE_E_SHAPE, "cache: hidden=%d inter=%d", d->hidden, d->inter);
+    return MOE_OK;
+}
+
+int check_request(const moe_cache *c, int layer, const int32_t *experts, int n) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache: NULL cache");
+    if (layer < 0 || layer >= c->d.n_layers) return moe::fail(MOE_E_ARG, "cache: layer %d", layer);
+    if (n < 0 || (n > 0 && !experts)) return moe::fail(MOE_E_ARG, "cache: n=%d", n);
+    std::vector<char> seen(c->d.n_experts, 0);
+    for (int i = 0; i < n; ++i) {
+        const int e = experts[i];
+        if (e < 0 || e >= c->d.n_experts) return moe::fail(MOE_E_ARG, "cache: expert %d out of range", e);
+        if (seen[e]) return moe::fail(MOE_E_ARG, "cache: expert %d requested twice", e);
+        seen[e] = 1;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+static int cache_make(const moe_cache_desc *desc, moe_cache **out) {
+    int rc = validate_desc(desc);
+    if (rc != MOE_OK) return rc;
+    if (!out) return moe::fail(MOE_E_ARG, "cache: NULL out");
+    auto *c = new moe_cache();
+    c->d = *desc;
+    c->slab_bytes = moe_expert_bytes(desc->hidden, desc->inter);
+    c->clear_state();
+    *out = c;
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_create(const moe_cache_desc *desc, const void *const *experts_host, void *slot_pool,
+                                void **expert_table, void *copy_stream, moe_cache **out) {
+    if (!experts_host || !slot_pool || !expert_table || !out) return moe::fail(MOE_E_ARG, "cache_create: NULL");
+    int rc = validate_desc(desc);
+    if (rc != MOE_OK) return rc;
+    const size_t n = (size_t)desc->n_layers * desc->n_experts;
+    for (size_t i = 0; i < n; ++i) {
+        hipPointerAttribute_t attr;
+        hipError_t e = hipPointerGetAttributes(&attr, experts_host[i]);
+        if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return moe::fail(MOE_E_NOT_PINNED, "cache_create: host slab %zu (%p) is not pinned", i, experts_host[i]);
+        }
+    }
+    moe_cache *c = nullptr;
+    rc = cache_make(desc, &c);
+    if (rc != MOE_OK) return rc;
+    c->host.assign(experts_host, experts_host + n);
+    c->pool = (uintptr_t)slot_pool;
+    auto eng = std::make_unique<HipEngine>();
+    rc = eng->init(desc->n_layers, desc->n_experts, (hipStream_t)copy_stream, expert_table);
+    if (rc == MOE_OK) rc = eng->clear_table();
+    if (rc != MOE_OK) {
+        delete c;
+        return rc;
+    }
+    c->engine = std::move(eng);
+    *out = c;
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_create_recording(const moe_cache_desc *desc, uintptr_t slot_pool, int fail_copy_at,
+                                          moe_cache **out) {
+    moe_cache *c = nullptr;
+    int rc = cache_make(desc, &c);
+    if (rc != MOE_OK) return rc;
+    c->host.assign((size_t)desc->n_layers * desc->n_experts, nullptr);
+    c->pool = slot_pool;
+    auto eng = std::make_unique<RecordingEngine>();
+    eng->fail_copy_at = fail_copy_at;
+    c->recorder = eng.get();
+    c->engine = std::move(eng);
+    *out = c;
+    return MOE_OK;
+}
+
+extern "C" int64_t moe_cache_trace(const moe_cache *c, int64_t *cmds, int64_t max_cmds) {
+    if (!c || !c->recorder) return -1;
+    const int64_t total = (int64_t)c->recorder->cmds.size() / 4;
+    if (cmds && max_cmds > 0) {
+        const int64_t n = std::min(total, max_cmds);
+        std::memcpy(cmds, c->recorder->cmds.data(), (size_t)n * 4 * sizeof(int64_t));
+    }
+    return total;
+}
+
+extern "C" int moe_cache_lookup(moe_cache *c, int layer, const int32_t *experts, int n, int32_t *slots,
+                                int *n_hits) {
+    int rc = check_request(c, layer, experts, n);
+    if (rc != MOE_OK) return rc;
+    if (n > 0 && !slots) return moe::fail(MOE_E_ARG, "cache_lookup: NULL slots");
+    int h = 0;
+    for (int i = 0; i < n; ++i) {
+        slots[i] = c->slot_of[(size_t)layer * c->d.n_experts + experts[i]];
+        h += slots[i] >= 0;
+    }
+    if (n_hits) *n_hits = h;
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_prefetch(moe_cache *c, int layer, const int32_t *experts, int n, void *compute_stream,
+                                  int *n_copies) {
+    int rc = check_request(c, layer, experts, n);
+    if (rc != MOE_OK) return rc;
+    const int Cs = c->C(), E = c->d.n_experts;
+    if (n > Cs) return moe::fail(MOE_E_CAPACITY, "cache_prefetch: %d experts > %d slots", n, Cs);
+    int *slot_of = &c->slot_of[(size_t)layer * E];
+    int *expert_of = &c->expert_of[(size_t)layer * Cs];
+    unsigned long long *stamp = &c->stamp[(size_t)layer * Cs];
+    char *held = &c->held[(size_t)layer * Cs];
+    long long *last_rel = &c->last_release[(size_t)layer * Cs];
+
+    std::vector<int> sorted(experts, experts + n);
+    std::sort(sorted.begin(), sorted.end());
+    std::vector<int> hit_list, miss_list;
+    for (int e : sorted) (slot_of[e] >= 0 ? hit_list : miss_list).push_back(e);
+    // capacity: misses need slots that are neither held nor needed by this request
+    int free_slots = 0;
+    std::vector<char> needed(Cs, 0);
+    for (int e : hit_list) needed[slot_of[e]] = 1;
+    for (int s = 0; s < Cs; ++s) free_slots += (!held[s] && !needed[s]);
+    if ((int)miss_list.size() > free_slots)
+        return moe::fail(MOE_E_CAPACITY, "cache_prefetch: %zu misses but only %d free slots (layer %d)",
+                         miss_list.size(), free_slots, layer);
+
+    std::vector<int> acquired;
+    for (int e : hit_list) {
+        const int s = slot_of[e];
+        stamp[s] = ++c->clock;
+        if (!held[s]) acquired.push_back(s);
+        held[s] = 1;
+    }
+    std::vector<int> t_exp, t_slot;
+    std::vector<const void *> t_ptr;
+    int copies = 0;
+    long long last_wait = -2;
+    for (int e : miss_list) {
+        int victim = -1;
+        for (int s = 0; s < Cs; ++s) {
+            if (held[s]) continue;
+            if (victim < 0 || stamp[s] < stamp[victim]) victim = s;  // ties keep the lower slot
+        }
+        const int old = expert_of[victim];
+        if (old >= 0) {
+            slot_of[old] = -1;
+            t_exp.push_back(old);
+            t_ptr.push_back(nullptr);
+            t_slot.push_back(-1);
+        }
+        expert_of[victim] = -1;
+        stamp[victim] = 0;
+        if (last_rel[victim] >= 0 && last_rel[victim] != last_wait) {
+            rc = c->engine->wait_release(layer, victim, last_rel[victim]);
+            if (rc != MOE_OK) break;
+            last_wait = last_rel[victim];
+        }
+        void *dst = c->slot_ptr(layer, victim);
+        rc = c->engine->copy(layer, e, victim, dst, c->host[(size_t)layer * E + e], c->slab_bytes);
+        if (rc != MOE_OK) break;
+        ++copies;
+        expert_of[victim] = e;
+        slot_of[e] = victim;
+        stamp[victim] = ++c->clock;
+        held[victim] = 1;
+        acquired.push_back(victim);
+        t_exp.push_back(e);
+        t_ptr.push_back(dst);
+        t_slot.push_back(victim);
+    }
+    if (rc != MOE_OK) {
+        // keep the table consistent with what is resident, then un-hold this request
+        (void)c->engine->table(layer, t_exp, t_ptr, t_slot);
+        for (int s : acquired) held[s] = 0;
+        return rc;
+    }
+    if (!t_exp.empty()) {
+        rc = c->engine->table(layer, t_exp, t_ptr, t_slot);
+        if (rc != MOE_OK) return rc;
+    }
+    if (copies > 0 || !t_exp.empty()) {
+        rc = c->engine->ready(layer, compute_stream);
+        if (rc != MOE_OK) return rc;
+    }
+    c->hits += hit_list.size();
+    c->misses += miss_list.size();
+    c->bytes += (uint64_t)copies * c->slab_bytes;
+    if (n_copies) *n_copies = copies;
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_release(moe_cache *c, int layer, void *compute_stream) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache_release: NULL cache");
+    if (layer < 0 || layer >= c->d.n_layers) return moe::fail(MOE_E_ARG, "cache_release: layer %d", layer);
+    const int Cs = c->C();
+    char *held = &c->held[(size_t)layer * Cs];
+    int n_held = 0;
+    for (int s = 0; s < Cs; ++s) n_held += held[s] != 0;
+    if (n_held == 0) return MOE_OK;
+    const long long id = c->next_release[layer]++;
+    int rc = c->engine->release(layer, id, n_held, compute_stream);
+    if (rc != MOE_OK) return rc;
+    long long *last_rel = &c->last_release[(size_t)layer * Cs];
+    for (int s = 0; s < Cs; ++s)
+        if (held[s]) {
+            held[s] = 0;
+            last_rel[s] = id;
+        }
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_stats(const moe_cache *c, uint64_t *hits, uint64_t *misses, uint64_t *h2d_bytes) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache_stats: NULL cache");
+    if (hits) *hits = c->hits;
+    if (misses) *misses = c->misses;
+    if (h2d_bytes) *h2d_bytes = c->bytes;
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_reset(moe_cache *c) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache_reset: NULL cache");
+    int rc = c->engine->sync();
+    if (rc != MOE_OK) return rc;
+    rc = c->engine->clear_table();
+    if (rc != MOE_OK) return rc;
+    c->clear_state();
+    return MOE_OK;
+}
+
+extern "C" void moe_cache_destroy(moe_cache *c) { delete c; }

@@ -1,0 +1,32 @@
+// Internal interface between the expert-FFN entry point and its kernel families.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+struct FfnArgs {
+    const uint16_t *x;          // [T, H] bf16 activations
+    int T, H, I, E, k;
+    const int32_t *topk_idx;    // [T, k]
+    const void *const *table;   // [E] slab pointers of this layer
+    const void *shared;         // shared expert slab or nullptr
+    const uint8_t *mask;        // [E] or nullptr
+    int grouped;                // 0: one group per (token, slot) pair; 1: one group per expert
+    int n_routed_groups;        // T*k (pairs) or E (grouped)
+    const int32_t *count;       // [E]     (grouped)
+    const int32_t *offset;      // [E + 1] (grouped)
+    const int32_t *pair_of_row; // [T*k]   (grouped)
+    uint16_t *h;                // [T*k + T*shared, I] bf16 SwiGLU output
+    float *y;                   // [T*k + T*shared, H] fp32 expert outputs
+};
+
+// Gate/up + SwiGLU (x -> h) and down projection (h -> y) with the dequant-GEMV
+// kernels.  max_m: largest number of tokens any group can have.
+int ffn_gemv_gate_up(const FfnArgs &a, int max_m, hipStream_t s);
+int ffn_gemv_down(const FfnArgs &a, int max_m, hipStream_t s);
+
+// Counting sort of pairs by expert (see moe_permute).
+int permute_launch(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
+                   int32_t *pair_of_row, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,294 @@
+// Entry points around the expert FFN: token->expert permutation, the FFN
+// dispatcher, the weighted combine and the dequantisation debug hook.
+#include "common.h"
+#include "ffn.h"
+
+namespace {
+
+constexpr int kPermMaxPairs = 16384;
+constexpr int kPermMaxE = 1024;
+
+// Counting sort of pairs p = t*k+i by expert, stable in p, in one workgroup:
+// histogram, exclusive scan, scatter with LDS cursors, then each expert's
+// segment is put in ascending pair order by rank counting (pair ids are
+// distinct, so the result does not depend on the scatter order).
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict__ idx, int n, int E,
+                                                       int32_t *__restrict__ count, int32_t *__restrict__ offset,
+                                                       int32_t *__restrict__ pair_of_row) {
+    __shared__ int cnt[kPermMaxE];
+    __shared__ int off[kPermMaxE + 1];
+    __shared__ int cur[kPermMaxE];
+    extern __shared__ int rows[];  // n entries
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int e = tid; e < E; e += nt) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < n; p += nt) atomicAdd(&cnt[idx[p]], 1);
+    __syncthreads();
+    if (tid == 0) {  // E <= 1024: a serial scan is cheap next to the rest
+        int acc = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = acc;
+            acc += cnt[e];
+        }
+        off[E] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += nt) {
+        cur[e] = off[e];
+        count[e] = cnt[e];
+        offset[e] = off[e];
+    }
+    if (tid == 0) offset[E] = off[E];
+    __syncthreads();
+    for (int p = tid; p < n; p += nt) rows[atomicAdd(&cur[idx[p]], 1)] = p;
+    __syncthreads();
+    // one wavefront per expert segment
+    const int wave = tid >> 6, lane = tid & 63, nwaves = nt >> 6;
+    for (int e = wave; e < E; e += nwaves) {
+        const int base = off[e], len = cnt[e];
+        for (int j = lane; j < len; j += 64) {
+            const int v = rows[base + j];
+            int rank = 0;
+            for (int l = 0; l < len; ++l) rank += rows[base + l] < v;
+            pair_of_row[base + rank] = v;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w, int T,
+                                                      int k, int H, int has_shared, uint16_t *__restrict__ out) {
+    const int t = blockIdx.y;
+    const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (j >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < k; ++i) {
+        const float wi = w[(size_t)t * k + i];
+        const float4 v = *reinterpret_cast<const float4 *>(y + ((size_t)t * k + i) * H + j);
+        acc.x = fmaf(wi, v.x, acc.x);
+        acc.y = fmaf(wi, v.y, acc.y);
+        acc.z = fmaf(wi, v.z, acc.z);
+        acc.w = fmaf(wi, v.w, acc.w);
+    }
+    if (has_shared) {
+        const float4 v = *reinterpret_cast<const float4 *>(y + ((size_t)T * k + t) * H + j);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    uint2 o;
+    o.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+    o.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+    *reinterpret_cast<uint2 *>(out + (size_t)t * H + j) = o;
+}
+
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ mat, int R, int K,
+                                                      float *__restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)R * K) return;
+    const size_t r = i / K, col = i - r * K;
+    const uint8_t byte = mat[r * (K / 2) + col / 2];
+    const uint32_t q = (col & 1) ? (byte >> 4) : (byte & 0xF);
+    const uint32_t rec = *reinterpret_cast<const uint32_t *>(mat + (size_t)R * K / 2 + (r * (K / 32) + col / 32) * 4);
+    out[i] = fmaf(fp16_bits_to_f32(rec & 0xFFFFu), (float)q, fp16_bits_to_f32(rec >> 16));
+}
+
+}  // namespace
+
+namespace moe {
+
+int permute_launch(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
+                   int32_t *pair_of_row, hipStream_t s) {
+    const int n = T * k;
+    const size_t lds = (size_t)(n > 0 ? n : 1) * sizeof(int);
+    static bool raised = false;
+    if (!raised) {
+        hipError_t e = hipFuncSetAttribute((const void *)permute_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kPermMaxPairs * (int)sizeof(int));
+        if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(permute_kernel)");
+        raised = true;
+    }
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, topk_idx, n, E, count, offset, pair_of_row);
+    MOE_LAUNCH_CHECK("permute_kernel");
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
+                           int32_t *pair_of_row, void *stream) {
+    if (T < 0 || k < 1 || E < 1) return moe::fail(MOE_E_ARG, "permute: T=%d k=%d E=%d", T, k, E);
+    if (!count || !offset || (T > 0 && (!topk_idx || !pair_of_row))) return moe::fail(MOE_E_ARG, "permute: NULL");
+    if ((long long)T * k > kPermMaxPairs || E > kPermMaxE || k > E)
+        return moe::fail(MOE_E_SHAPE, "permute: T*k=%lld (max %d), E=%d (max %d), k=%d", (long long)T * k,
+                         kPermMaxPairs, E, kPermMaxE, k);
+    return moe::permute_launch(topk_idx, T, k, E, count, offset, pair_of_row, (hipStream_t)stream);
+}
+
+namespace {
+
+struct FfnLayout {
+    size_t h, count, offset, pairs, total;
+};
+
+FfnLayout ffn_layout(int T, int I, int E, int k, int has_shared) {
+    FfnLayout L{};
+    const size_t P = (size_t)T * k + (has_shared ? (size_t)T : 0);
+    size_t o = 0;
+    L.h = o;
+    o += moe::align_up(P * I * sizeof(uint16_t), 256);
+    L.count = o;
+    o += moe::align_up((size_t)E * sizeof(int32_t), 256);
+    L.offset = o;
+    o += moe::align_up((size_t)(E + 1) * sizeof(int32_t), 256);
+    L.pairs = o;
+    o += moe::align_up((size_t)T * k * sizeof(int32_t), 256);
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+extern "C" size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int has_shared) {
+    (void)H;
+    if (T < 0 || I <= 0 || E <= 0 || k <= 0) return 0;
+    return ffn_layout(T, I, E, k, has_shared).total;
+}
+
+namespace {
+
+int validate_ffn(const void *act, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                 const void *const *expert_table, const void *out, int path, const char *who) {
+    if (!act || !topk_idx || !expert_table || !out) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
+    if (H <= 0 || I <= 0 || H % 32 || I % 32)
+        return moe::fail(MOE_E_SHAPE, "%s: H=%d and I=%d must be positive multiples of 32", who, H, I);
+    if (H > 16384 || I > 16384) return moe::fail(MOE_E_SHAPE, "%s: H=%d I=%d above 16384", who, H, I);
+    if (E < 1 || E > kPermMaxE || k < 1 || k > E) return moe::fail(MOE_E_SHAPE, "%s: E=%d k=%d", who, E, k);
+    if (path < MOE_FFN_AUTO || path > MOE_FFN_MFMA) return moe::fail(MOE_E_ARG, "%s: path=%d", who, path);
+    if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_STATE, "%s: the MFMA path is not built in this library", who);
+    return MOE_OK;
+}
+
+// Fills the kernel arguments; grouped iff a permutation is given.
+int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, int H, int I, int E,
+              const int32_t *topk_idx, int k, const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+              const void *const *table, const void *shared, const uint8_t *mask, int path, int *max_m,
+              const char *who) {
+    const bool have_perm = count && offset && pair_of_row;
+    if ((count || offset || pair_of_row) && !have_perm)
+        return moe::fail(MOE_E_ARG, "%s: count, offset and pair_of_row go together", who);
+    if (path == MOE_FFN_GROUPED && !have_perm) return moe::fail(MOE_E_ARG, "%s: grouped path needs a permutation", who);
+    const bool grouped = (path == MOE_FFN_GROUPED) || (path == MOE_FFN_AUTO && have_perm);
+    a = moe::FfnArgs{};
+    a.x = x;
+    a.h = h;
+    a.y = y;
+    a.T = T;
+    a.H = H;
+    a.I = I;
+    a.E = E;
+    a.k = k;
+    a.topk_idx = topk_idx;
+    a.table = table;
+    a.shared = shared;
+    a.mask = mask;
+    a.grouped = grouped ? 1 : 0;
+    a.n_routed_groups = grouped ? E : T * k;
+    a.count = count;
+    a.offset = offset;
+    a.pair_of_row = pair_of_row;
+    *max_m = grouped ? T : (shared ? T : 1);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                                  const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                                  const void *const *expert_table, const void *shared_slab,
+                                  const uint8_t *expert_mask, uint16_t *h, int path, void *stream) {
+    if (T < 0) return moe::fail(MOE_E_ARG, "expert_gate_up: T=%d < 0", T);
+    if (T == 0) return MOE_OK;
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, h, path, "expert_gate_up");
+    if (rc != MOE_OK) return rc;
+    moe::FfnArgs a;
+    int max_m = 1;
+    rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
+                   expert_mask, path, &max_m, "expert_gate_up");
+    if (rc != MOE_OK) return rc;
+    return moe::ffn_gemv_gate_up(a, max_m, (hipStream_t)stream);
+}
+
+extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                               const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                               const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                               float *y, int path, void *stream) {
+    if (T < 0) return moe::fail(MOE_E_ARG, "expert_down: T=%d < 0", T);
+    if (T == 0) return MOE_OK;
+    int rc = validate_ffn(h, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_down");
+    if (rc != MOE_OK) return rc;
+    moe::FfnArgs a;
+    int max_m = 1;
+    rc = make_args(a, nullptr, const_cast<uint16_t *>(h), y, T, H, I, E, topk_idx, k, count, offset, pair_of_row,
+                   expert_table, shared_slab, expert_mask, path, &max_m, "expert_down");
+    if (rc != MOE_OK) return rc;
+    return moe::ffn_gemv_down(a, max_m, (hipStream_t)stream);
+}
+
+extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                              const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                              float *y, void *workspace, size_t workspace_bytes, int path, void *stream) {
+    if (T < 0) return moe::fail(MOE_E_ARG, "expert_ffn: T=%d < 0", T);
+    if (T == 0) return MOE_OK;
+    if (!workspace) return moe::fail(MOE_E_ARG, "expert_ffn: NULL workspace");
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_ffn");
+    if (rc != MOE_OK) return rc;
+    const int has_shared = shared_slab != nullptr;
+    const FfnLayout Ly = ffn_layout(T, I, E, k, has_shared);
+    if (workspace_bytes < Ly.total)
+        return moe::fail(MOE_E_NOMEM, "expert_ffn: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
+    if (path == MOE_FFN_AUTO) path = ((long long)T * k <= 64) ? MOE_FFN_PAIRS : MOE_FFN_GROUPED;
+    if (path == MOE_FFN_GROUPED && (long long)T * k > kPermMaxPairs)
+        return moe::fail(MOE_E_SHAPE, "expert_ffn: grouped path needs T*k <= %d", kPermMaxPairs);
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    uint16_t *h = (uint16_t *)(ws + Ly.h);
+    int32_t *count = nullptr, *offset = nullptr, *pairs = nullptr;
+    if (path == MOE_FFN_GROUPED) {
+        count = (int32_t *)(ws + Ly.count);
+        offset = (int32_t *)(ws + Ly.offset);
+        pairs = (int32_t *)(ws + Ly.pairs);
+        rc = moe::permute_launch(topk_idx, T, k, E, count, offset, pairs, s);
+        if (rc != MOE_OK) return rc;
+    }
+    rc = moe_expert_gate_up(x, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask,
+                            h, path, stream);
+    if (rc != MOE_OK) return rc;
+    return moe_expert_down(h, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask,
+                           y, path, stream);
+}
+
+extern "C" int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,
+                           void *stream) {
+    if (T < 0 || k < 1 || H <= 0) return moe::fail(MOE_E_ARG, "combine: T=%d k=%d H=%d", T, k, H);
+    if (T == 0) return MOE_OK;
+    if (!y || !topk_w || !out) return moe::fail(MOE_E_ARG, "combine: NULL pointer");
+    if (H % 4) return moe::fail(MOE_E_SHAPE, "combine: H=%d must be a multiple of 4", H);
+    dim3 grid((H / 4 + 255) / 256, T);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, (hipStream_t)stream, y, topk_w, T, k, H, has_shared, out);
+    MOE_LAUNCH_CHECK("combine_kernel");
+    return MOE_OK;
+}
+
+extern "C" int moe_debug_dequant(const void *slab, int H, int I, int which, float *out, void *stream) {
+    if (!slab || !out) return moe::fail(MOE_E_ARG, "debug_dequant: NULL pointer");
+    if (H <= 0 || I <= 0 || H % 32 || I % 32) return moe::fail(MOE_E_SHAPE, "debug_dequant: H=%d I=%d", H, I);
+    if (which < 0 || which > 2) return moe::fail(MOE_E_ARG, "debug_dequant: which=%d", which);
+    const int R = which < 2 ? I : H, K = which < 2 ? H : I;
+    const uint8_t *mat = (const uint8_t *)slab + (size_t)which * ((size_t)I * H * 5 / 8);
+    const size_t n = (size_t)R * K;
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, mat, R,
+                       K, out);
+    MOE_LAUNCH_CHECK("dequant_kernel");
+    return MOE_OK;
+}

@@ -1,0 +1,264 @@
+// Expert FFN for few tokens per expert (decode): fused 4-bit block dequant +
+// GEMV, gate/up with SwiGLU in one kernel and the down projection in another.
+//
+// Method (LayerStoRm README "TL;DR": each token runs only the few experts the
+// router picked; the expert weights are 4-bit block-quantised, README
+// "Install": UD-Q4_K_XL weights): for each expert and each of its tokens
+//   g = W1 x, u = W3 x, h = bf16(silu(g) * u), y = W2 h,
+// W = scale * q + min per 32-column block.
+//
+// Kernel design (gfx950, wave64):
+//  * Each lane owns whole 32-column blocks: one 16-byte code load (32 nibbles)
+//    plus one 4-byte (scale, min) record per block, so a row is read with
+//    fully used, coalesced 16 B/lane loads.  LPR lanes share a row (LPR = 64
+//    for K = 4096/6144/2048, 16 for K = 1536), BPL blocks per lane.
+//  * The activation row(s) of the expert's tokens are staged once per
+//    workgroup in LDS, already permuted into the bf16 pairs the nibble
+//    extraction produces, so the inner loop is: mask+or a nibble pair into a
+//    bf16 pair (128 + q) and one v_dot2_f32_bf16 per two weights.  The block
+//    result is scale*acc + (min - 128*scale) * sum(x_block), which equals
+//    sum((scale*q + min) * x) exactly in real arithmetic.
+//  * Partial sums of the LPR lanes of a row meet in a fixed butterfly, so the
+//    output is reproducible run to run.
+#include "common.h"
+#include "ffn.h"
+
+namespace {
+
+constexpr int kMT = 4;        // tokens staged per pass
+constexpr int kRowIters = 4;  // rows per wave-subgroup per workgroup
+
+__device__ __forceinline__ float block_dot(const uint4 c, const uint4 *xb, int stride) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 X = xb[j * stride];
+        acc = dot2_bf16(((w[j]) & 0x000F000Fu) | 0x43004300u, X.x, acc);
+        acc = dot2_bf16(((w[j] >> 4) & 0x000F000Fu) | 0x43004300u, X.y, acc);
+        acc = dot2_bf16(((w[j] >> 8) & 0x000F000Fu) | 0x43004300u, X.z, acc);
+        acc = dot2_bf16(((w[j] >> 12) & 0x000F000Fu) | 0x43004300u, X.w, acc);
+    }
+    return acc;
+}
+
+// sum over the block of (scale*q + min) * x, from acc = sum (128+q) x and S = sum x
+__device__ __forceinline__ float block_value(uint32_t rec, float acc, float S) {
+    const float sc = fp16_bits_to_f32(rec & 0xFFFFu);
+    const float mn = fp16_bits_to_f32(rec >> 16);
+    const float cc = fmaf(-128.0f, sc, mn);  // exact: min - 128*scale
+    return fmaf(sc, acc, cc * S);
+}
+
+struct Group {
+    const uint8_t *slab;
+    int M;
+    int routed;  // group id within routed groups, or -1 for the shared expert
+};
+
+__device__ __forceinline__ Group resolve_group(const moe::FfnArgs &a, int g) {
+    Group out{nullptr, 0, -1};
+    if (g < a.n_routed_groups) {
+        int e;
+        int M;
+        if (a.grouped) {
+            e = g;
+            M = a.count[e];
+        } else {
+            e = a.topk_idx[g];
+            M = 1;
+        }
+        if (M == 0 || (a.mask && a.mask[e] == 0)) return out;
+        out.slab = (const uint8_t *)a.table[e];
+        out.M = M;
+        out.routed = g;
+    } else if (a.shared) {
+        out.slab = (const uint8_t *)a.shared;
+        out.M = a.T;
+    }
+    return out;
+}
+
+// Output row (in h / y) of the m-th token of a group.
+__device__ __forceinline__ int group_row(const moe::FfnArgs &a, const Group &gr, int m) {
+    if (gr.routed < 0) return a.T * a.k + m;
+    if (a.grouped) return a.pair_of_row[a.offset[gr.routed] + m];
+    return gr.routed;
+}
+
+// Stage mcount activation rows (bf16, K columns) into LDS:
+//   X[(m*4 + j)*nblk + b] = the 8 values of word j of block b, as bf16 pairs
+//                           (v0,v4), (v1,v5), (v2,v6), (v3,v7)
+//   S[m*nblk + b]         = fp32 sum of the block's 32 values (in index order)
+__device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ act, int K, const int *src_rows, int mcount,
+                                           uint4 *X, float *S) {
+    const int nblk = K >> 5;
+    for (int id = threadIdx.x; id < mcount * nblk * 4; id += blockDim.x) {
+        const int m = id / (nblk * 4), rem = id - m * nblk * 4;
+        const int b = rem >> 2, j = rem & 3;
+        const uint4 d = *reinterpret_cast<const uint4 *>(act + (size_t)src_rows[m] * K + 32 * b + 8 * j);
+        uint4 p;
+        p.x = (d.x & 0xFFFFu) | (d.z << 16);
+        p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
+        p.z = (d.y & 0xFFFFu) | (d.w << 16);
+        p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
+        X[(m * 4 + j) * nblk + b] = p;
+    }
+    for (int id = threadIdx.x; id < mcount * nblk; id += blockDim.x) {
+        const int m = id / nblk, b = id - m * nblk;
+        const uint4 *src = reinterpret_cast<const uint4 *>(act + (size_t)src_rows[m] * K + 32 * b);
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 d = src[j];
+            const uint32_t v[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s += bf16_bits_to_f32(v[q] & 0xFFFFu);
+                s += bf16_bits_to_f32(v[q] >> 16);
+            }
+        }
+        S[m * nblk + b] = s;
+    }
+}
+
+template <int LPR, int BPL, bool GATEUP>
+__global__ __launch_bounds__(256) void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap) {
+    constexpr int RPW = 64 / LPR;                     // rows per wave at a time
+    constexpr int ROWS_PER_WG = 4 * RPW * kRowIters;  // rows per workgroup
+    const int K = GATEUP ? a.H : a.I;
+    const int R = GATEUP ? a.I : a.H;
+    const int nblk = K >> 5;
+    const int g = blockIdx.x / tiles, tile = blockIdx.x - g * tiles;
+    const Group gr = resolve_group(a, g);
+    if (gr.M == 0) return;
+
+    const size_t m13 = (size_t)a.I * a.H * 5 / 8;  // bytes of W1 (= W3)
+    const uint8_t *mat0 = gr.slab + (GATEUP ? 0 : 2 * m13);
+    const uint8_t *mat1 = gr.slab + m13;
+    const uint8_t *par0 = mat0 + (size_t)R * K / 2;
+    const uint8_t *par1 = mat1 + (size_t)R * K / 2;
+
+    extern __shared__ uint4 lds[];
+    uint4 *X = lds;
+    float *S = reinterpret_cast<float *>(lds + (size_t)mt_cap * 4 * nblk);
+    __shared__ int src_rows[kMT];
+    __shared__ int out_rows[kMT];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane / LPR, c = lane % LPR;
+    const int r_begin = tile * ROWS_PER_WG;
+    const int r_end = min(R, r_begin + ROWS_PER_WG);
+
+    for (int pass = 0; pass < gr.M; pass += mt_cap) {
+        const int mcount = min(mt_cap, gr.M - pass);
+        if (threadIdx.x < mcount) {
+            const int row = group_row(a, gr, pass + threadIdx.x);
+            out_rows[threadIdx.x] = row;
+            src_rows[threadIdx.x] = GATEUP ? (gr.routed < 0 ? pass + (int)threadIdx.x : row / a.k) : row;
+        }
+        __syncthreads();
+        stage_rows(GATEUP ? a.x : a.h, K, src_rows, mcount, X, S);
+        __syncthreads();
+
+        for (int r = r_begin + wave * RPW + sub; r < r_end; r += 4 * RPW) {
+            uint4 c0[BPL], c1[BPL];
+            uint32_t p0[BPL], p1[BPL];
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                const int blk = c + b * LPR;
+                if (blk < nblk) {
+                    c0[b] = *reinterpret_cast<const uint4 *>(mat0 + (size_t)r * (K / 2) + 16 * blk);
+                    p0[b] = *reinterpret_cast<const uint32_t *>(par0 + ((size_t)r * nblk + blk) * 4);
+                    if (GATEUP) {
+                        c1[b] = *reinterpret_cast<const uint4 *>(mat1 + (size_t)r * (K / 2) + 16 * blk);
+                        p1[b] = *reinterpret_cast<const uint32_t *>(par1 + ((size_t)r * nblk + blk) * 4);
+                    }
+                }
+            }
+            for (int m = 0; m < mcount; ++m) {
+                float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    const int blk = c + b * LPR;
+                    if (blk < nblk) {
+                        const uint4 *xb = X + (size_t)(m * 4) * nblk + blk;
+                        const float Sb = S[m * nblk + blk];
+                        v0 += block_value(p0[b], block_dot(c0[b], xb, nblk), Sb);
+                        if (GATEUP) v1 += block_value(p1[b], block_dot(c1[b], xb, nblk), Sb);
+                    }
+                }
+                v0 = group_sum<LPR>(v0);
+                if (GATEUP) v1 = group_sum<LPR>(v1);
+                if (c == 0) {
+                    if (GATEUP) {
+                        const float hval = v0 / (1.0f + expf(-v0)) * v1;
+                        a.h[(size_t)out_rows[m] * a.I + r] = (uint16_t)f32_to_bf16_bits(hval);
+                    } else {
+                        a.y[(size_t)out_rows[m] * a.H + r] = v0;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int LPR, int BPL, bool GATEUP>
+int launch_one(const moe::FfnArgs &a, int R, int K, int n_groups, int max_m, hipStream_t s) {
+    constexpr int ROWS_PER_WG = 4 * (64 / LPR) * kRowIters;
+    const int tiles = (R + ROWS_PER_WG - 1) / ROWS_PER_WG;
+    const int nblk = K / 32;
+    const int mt_cap = max_m < kMT ? max_m : kMT;
+    const size_t lds_bytes = (size_t)mt_cap * nblk * (4 * 16 + 4);
+    if (lds_bytes > 64 * 1024) {
+        static bool raised = false;
+        if (!raised) {
+            hipError_t e = hipFuncSetAttribute((const void *)ffn_gemv_kernel<LPR, BPL, GATEUP>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return moe::fail_hip(e, "hipFuncSetAttribute(ffn_gemv_kernel)");
+            raised = true;
+        }
+    }
+    hipLaunchKernelGGL((ffn_gemv_kernel<LPR, BPL, GATEUP>), dim3((unsigned)n_groups * tiles), dim3(256), lds_bytes, s,
+                       a, tiles, mt_cap);
+    MOE_LAUNCH_CHECK("ffn_gemv_kernel");
+    return MOE_OK;
+}
+
+template <bool GATEUP>
+int launch_phase(const moe::FfnArgs &a, int n_groups, int max_m, hipStream_t s) {
+    const int K = GATEUP ? a.H : a.I;
+    const int R = GATEUP ? a.I : a.H;
+    const int nblk = K / 32;
+#define MOE_TRY_SHAPE(L, B) \
+    if (nblk == (L) * (B)) return launch_one<L, B, GATEUP>(a, R, K, n_groups, max_m, s);
+    MOE_TRY_SHAPE(64, 1) MOE_TRY_SHAPE(64, 2) MOE_TRY_SHAPE(64, 3) MOE_TRY_SHAPE(64, 4)
+    MOE_TRY_SHAPE(16, 1) MOE_TRY_SHAPE(16, 2) MOE_TRY_SHAPE(16, 3) MOE_TRY_SHAPE(16, 4)
+    MOE_TRY_SHAPE(8, 1) MOE_TRY_SHAPE(4, 1)
+#undef MOE_TRY_SHAPE
+    // other sizes: 64 lanes per row, guarded blocks
+    if (nblk <= 64) return launch_one<64, 1, GATEUP>(a, R, K, n_groups, max_m, s);
+    if (nblk <= 128) return launch_one<64, 2, GATEUP>(a, R, K, n_groups, max_m, s);
+    if (nblk <= 256) return launch_one<64, 4, GATEUP>(a, R, K, n_groups, max_m, s);
+    if (nblk <= 512) return launch_one<64, 8, GATEUP>(a, R, K, n_groups, max_m, s);
+    return moe::fail(MOE_E_SHAPE, "expert_ffn: K=%d too large (max 16384)", K);
+}
+
+}  // namespace
+
+namespace moe {
+
+int ffn_gemv_gate_up(const FfnArgs &a, int max_m, hipStream_t s) {
+    const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
+    if (n_groups == 0) return MOE_OK;
+    return launch_phase<true>(a, n_groups, max_m, s);
+}
+
+int ffn_gemv_down(const FfnArgs &a, int max_m, hipStream_t s) {
+    const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
+    if (n_groups == 0) return MOE_OK;
+    return launch_phase<false>(a, n_groups, max_m, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,279 @@
+"""Host runtime around the C ABI: a stack of routed-expert MoE layers.
+
+Device memory and streams come from torch; pinned host memory comes from the
+HIP runtime torch already loaded.  Every arithmetic step runs in libmoe.so's
+kernels; this module only allocates, fills inputs and orders the calls:
+
+  step:  router(l) for every layer            (compute stream)
+         [streaming] one D2H of the top-k ids + host wait, then per layer:
+             prefetch(l)   -> copy stream streams the misses, compute waits
+             expert_ffn(l) -> gate/up + SwiGLU, down
+             release(l)    -> slots may be overwritten after this point
+         combine(l)
+
+The routing of every layer is known at the start of a step because each
+(step, layer) gets its own synthetic hidden states; the prefetch of layer l+1
+therefore overlaps the FFN of layer l (LayerStoRm README "TL;DR": streaming is
+overlapped with compute).  When a layer needs more distinct experts than it has
+slots, it runs in waves: hits plus as many misses as fit first, then the
+remaining misses into slots released by the finished wave.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import synth
+
+from . import _lib as L
+
+
+class PinnedHost:
+    """Page-locked host buffer from hipHostMalloc (freed with hipHostFree)."""
+
+    def __init__(self, nbytes: int):
+        self.nbytes = int(nbytes)
+        hip = L.hip_runtime()
+        p = ctypes.c_void_p()
+        rc = hip.hipHostMalloc(ctypes.byref(p), ctypes.c_size_t(max(self.nbytes, 1)), ctypes.c_uint(0))
+        if rc != 0 or not p.value:
+            raise MemoryError(f"hipHostMalloc({self.nbytes}) failed with {rc}")
+        self.ptr = p.value
+        self._hip = hip
+        self.array = np.frombuffer((ctypes.c_uint8 * max(self.nbytes, 1)).from_address(self.ptr), dtype=np.uint8)
+
+    def free(self):
+        if self.ptr:
+            self.array = None
+            self._hip.hipHostFree(ctypes.c_void_p(self.ptr))
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def _bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+@dataclass
+class StepStats:
+    waves: int = 0
+    copies: int = 0
+
+
+class MoEStack:
+    """L routed-expert MoE layers of one configuration on one GPU.
+
+    cap: fraction of experts per layer held in HBM (None = the configuration's).
+    layers: number of layers to build (None = the configuration's).
+    """
+
+    def __init__(self, cfg: synth.Config, *, layers: int | None = None, cap: float | None = None,
+                 device: int = 0, threads: int = 0, path: int = L.MOE_FFN_AUTO):
+        L.lib()
+        self.cfg = cfg
+        self.L = layers or cfg.layers
+        self.T, self.H, self.I, self.E, self.k = cfg.tokens, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
+        self.has_shared = cfg.shared > 0
+        self.cap = cfg.cap if cap is None else cap
+        self.C = min(self.E, int(self.cap * self.E + 1e-9))
+        self.streaming = self.C < self.E
+        self.path = path
+        self.dev = torch.device("cuda", device)
+        torch.cuda.set_device(self.dev)
+        self.copy_stream = torch.cuda.Stream(self.dev)  # default priority
+        self.slab = L.moe_expert_bytes(self.H, self.I)
+        assert self.slab == synth.slab_bytes(self.H, self.I)
+        Lyr, T, H, I, E, k = self.L, self.T, self.H, self.I, self.E, self.k
+
+        # router weights and bias
+        self.wr = torch.empty((Lyr, E, H), dtype=torch.float32, device=self.dev)
+        self.bias = None if cfg.bias == "none" else torch.empty((Lyr, E), dtype=torch.float32, device=self.dev)
+        for l in range(Lyr):
+            self.wr[l].copy_(torch.from_numpy(synth.router_w(cfg.seed, l, E, H, threads)))
+            if self.bias is not None:
+                self.bias[l].copy_(torch.from_numpy(synth.router_bias(cfg, l)))
+
+        # shared experts: always resident
+        self.shared = None
+        if self.has_shared:
+            stage = PinnedHost(Lyr * self.slab)
+            synth.fill_slabs(cfg.seed, 0, [synth.shared_expert_id(cfg)], H, I, [stage.ptr], threads)
+            for l in range(1, Lyr):
+                synth.fill_slabs(cfg.seed, l, [synth.shared_expert_id(cfg)], H, I, [stage.ptr + l * self.slab],
+                                 threads)
+            self.shared = torch.empty((Lyr, self.slab), dtype=torch.uint8, device=self.dev)
+            self.shared.view(-1).copy_(torch.from_numpy(stage.array[:Lyr * self.slab]), non_blocking=False)
+            stage.free()
+
+        # routed experts
+        self.host = None
+        self.cache = None
+        if not self.streaming:
+            self.pool = torch.empty((Lyr * E, self.slab), dtype=torch.uint8, device=self.dev)
+            stage = PinnedHost(E * self.slab)
+            for l in range(Lyr):
+                synth.fill_slabs(cfg.seed, l, list(range(E)), H, I,
+                                 [stage.ptr + e * self.slab for e in range(E)], threads)
+                self.pool[l * E:(l + 1) * E].view(-1).copy_(torch.from_numpy(stage.array[:E * self.slab]))
+            stage.free()
+            base = self.pool.data_ptr()
+            ptrs = np.array([base + i * self.slab for i in range(Lyr * E)], dtype=np.int64).reshape(Lyr, E)
+            self.table = torch.from_numpy(ptrs).to(self.dev)
+        else:
+            self.host = PinnedHost(Lyr * E * self.slab)
+            for l in range(Lyr):
+                synth.fill_slabs(cfg.seed, l, list(range(E)), H, I,
+                                 [self.host.ptr + (l * E + e) * self.slab for e in range(E)], threads)
+            self.pool = torch.empty((Lyr * self.C, self.slab), dtype=torch.uint8, device=self.dev)
+            self.table = torch.zeros((Lyr, E), dtype=torch.int64, device=self.dev)
+            self._host_ptrs = (ctypes.c_void_p * (Lyr * E))(
+                *[self.host.ptr + i * self.slab for i in range(Lyr * E)])
+            desc = L.moe_cache_desc(Lyr, E, H, I, self.C)
+            torch.cuda.synchronize(self.dev)
+            self.cache = L.moe_cache_create(desc, ctypes.addressof(self._host_ptrs), self.pool, self.table,
+                                            self.copy_stream)
+        # workspaces and outputs
+        self.router_ws_bytes = L.moe_router_workspace_bytes(T, E)
+        self.router_ws = torch.zeros(self.router_ws_bytes, dtype=torch.uint8, device=self.dev)
+        self.ffn_ws_bytes = L.moe_expert_ffn_workspace_bytes(T, H, I, E, k, self.has_shared)
+        self.ffn_ws = torch.empty(self.ffn_ws_bytes, dtype=torch.uint8, device=self.dev)
+        self.idx = torch.empty((Lyr, T, k), dtype=torch.int32, device=self.dev)
+        self.w = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
+        P = T * k + (T if self.has_shared else 0)
+        self.y = torch.empty((P, H), dtype=torch.float32, device=self.dev)
+        self.max_waves = (E + self.C - 1) // self.C + 1
+        self.masks = torch.zeros((Lyr, self.max_waves, E), dtype=torch.uint8, device=self.dev)
+        self._idx_host = PinnedHost(Lyr * T * k * 4) if self.streaming else None
+        self._mask_host = PinnedHost(Lyr * self.max_waves * E) if self.streaming else None
+        torch.cuda.synchronize(self.dev)
+
+    # ------------------------------------------------------------------ inputs
+    def make_inputs(self, step: int, threads: int = 0) -> torch.Tensor:
+        """Hidden states [L, T, H] (bf16) of one step, resident on the device."""
+        xs = np.stack([synth.x_bf16(self.cfg.seed, step, l, self.T, self.H, threads) for l in range(self.L)])
+        return _bf16_tensor(xs, self.dev)
+
+    def new_output(self) -> torch.Tensor:
+        return torch.empty((self.L, self.T, self.H), dtype=torch.bfloat16, device=self.dev)
+
+    def layer_experts(self, l: int):
+        return self.pool, self.table[l]
+
+    # ------------------------------------------------------------------ step
+    @property
+    def stream(self):
+        """Kernels go to torch's current stream at call time (so graph capture works)."""
+        return torch.cuda.current_stream(self.dev)
+
+    def route(self, x: torch.Tensor, l: int):
+        L.moe_router_topk(x[l], self.T, self.H, self.wr[l], None if self.bias is None else self.bias[l], self.E,
+                          self.k, self.idx[l], self.w[l], self.router_ws, self.router_ws_bytes, self.stream)
+
+    def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True):
+        L.moe_expert_ffn(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l],
+                         self.shared[l] if (self.has_shared and shared) else None, mask, self.y, self.ffn_ws,
+                         self.ffn_ws_bytes, self.path, self.stream)
+
+    def combine(self, l: int, out: torch.Tensor):
+        L.moe_combine(self.y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l], self.stream)
+
+    def gate_up_only(self, x: torch.Tensor, l: int, h: torch.Tensor):
+        """Only the dequant + gate/up + SwiGLU kernel of layer l (pair grouping), for timing it."""
+        L.moe_expert_gate_up(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
+                             self.table[l], self.shared[l] if self.has_shared else None, None, h,
+                             L.MOE_FFN_PAIRS, self.stream)
+
+    def down_only(self, h: torch.Tensor, l: int):
+        """Only the dequant + down-projection kernel of layer l (pair grouping), for timing it."""
+        L.moe_expert_down(h, self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
+                          self.table[l], self.shared[l] if self.has_shared else None, None, self.y,
+                          L.MOE_FFN_PAIRS, self.stream)
+
+    def plan_waves(self, l: int, needed):
+        """Split a layer's sorted needed experts into waves of at most C experts,
+        resident ones (hits) first."""
+        slots, _ = L.moe_cache_lookup(self.cache, l, needed)
+        hits = [e for e, s in zip(needed, slots) if s >= 0]
+        misses = [e for e, s in zip(needed, slots) if s < 0]
+        order = hits + misses
+        return [sorted(order[i:i + self.C]) for i in range(0, len(order), self.C)]
+
+    def forward(self, x: torch.Tensor, out: torch.Tensor) -> StepStats:
+        """One step over all layers: x [L,T,H] bf16 -> out [L,T,H] bf16."""
+        st = StepStats()
+        for l in range(self.L):
+            self.route(x, l)
+        if not self.streaming:
+            for l in range(self.L):
+                self.ffn(x, l)
+                self.combine(l, out)
+            return st
+        # one small D2H per step, then the host plans every layer
+        idx_host = np.frombuffer(self._idx_host.array, dtype=np.int32, count=self.L * self.T * self.k)
+        torch.from_numpy(idx_host).copy_(self.idx.view(-1), non_blocking=True)
+        self.stream.synchronize()
+        idx_host = idx_host.reshape(self.L, self.T, self.k)
+        plans = [self.plan_waves(l, sorted(set(int(e) for e in idx_host[l].ravel()))) for l in range(self.L)]
+        need_masks = any(len(p) > 1 for p in plans)
+        if need_masks:
+            mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
+                               count=self.L * self.max_waves * self.E).reshape(self.L, self.max_waves, self.E)
+            mh[:] = 0
+            for l, waves in enumerate(plans):
+                for wv, experts in enumerate(waves):
+                    mh[l, wv, experts] = 1
+            self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
+        for l, waves in enumerate(plans):
+            for wv, experts in enumerate(waves):
+                st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
+                mask = self.masks[l, wv] if len(waves) > 1 else None
+                self.ffn(x, l, mask=mask, shared=(wv == 0))
+                L.moe_cache_release(self.cache, l, self.stream)
+                st.waves += 1
+            self.combine(l, out)
+        return st
+
+    def stats(self):
+        return L.moe_cache_stats(self.cache) if self.cache else (0, 0, 0)
+
+    def reset_cache(self):
+        if self.cache:
+            L.moe_cache_reset(self.cache)
+
+    def close(self):
+        if self.cache:
+            torch.cuda.synchronize(self.dev)
+            L.moe_cache_destroy(self.cache)
+            self.cache = None
+        if self.host is not None:
+            self.host.free()
+            self.host = None
+        for attr in ("_idx_host", "_mask_host"):
+            buf = getattr(self, attr, None)
+            if buf is not None:
+                buf.free()
+                setattr(self, attr, None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ host copies for checking
+    def host_slabs(self, l: int):
+        """Routed slabs of layer l as host numpy arrays (regenerated from the seed)."""
+        return [synth.expert_slab(self.cfg.seed, l, e, self.H, self.I) for e in range(self.E)]
+
+    def host_shared(self, l: int):
+        if not self.has_shared:
+            return None
+        return synth.expert_slab(self.cfg.seed, l, synth.shared_expert_id(self.cfg), self.H, self.I)

@@ -1,0 +1,235 @@
+"""Host-side tests of libmoe.so: exported symbols, argument validation, and the
+expert-cache policy through the recording copy engine (no GPU needed)."""
+import os
+import random
+import re
+
+import pytest
+
+from routed_expert_streaming_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_format_sizes():
+    assert L.moe_status_str(0) == "ok"
+    assert "slots" in L.moe_status_str(L.MOE_E_CAPACITY)
+    assert L.moe_expert_bytes(256, 128) == 61440
+    assert L.moe_expert_bytes(4096, 1536) == 11796480
+    assert L.moe_expert_bytes(6144, 2048) == 23592960
+    assert L.moe_expert_bytes(100, 128) == 0
+    assert L.moe_router_workspace_bytes(1, 128) >= 256 + 512
+
+
+def _status(fn, *args):
+    with pytest.raises(L.MoEError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_router_validation():
+    ws = L.moe_router_workspace_bytes(4, 16)
+    assert _status(L.moe_router_topk, None, 4, 256, FAKE, None, 16, 2, FAKE, FAKE, FAKE, ws) == L.MOE_E_ARG
+    assert _status(L.moe_router_topk, FAKE, 4, 250, FAKE, None, 16, 2, FAKE, FAKE, FAKE, ws) == L.MOE_E_SHAPE
+    assert _status(L.moe_router_topk, FAKE, 4, 256, FAKE, None, 16, 17, FAKE, FAKE, FAKE, ws) == L.MOE_E_SHAPE
+    assert _status(L.moe_router_topk, FAKE, 4, 256, FAKE, None, 2000, 2, FAKE, FAKE, FAKE, 10**8) == L.MOE_E_SHAPE
+    assert _status(L.moe_router_topk, FAKE, 4, 256, FAKE, None, 16, 2, FAKE, FAKE, FAKE, ws - 1) == L.MOE_E_NOMEM
+    L.moe_router_topk(None, 0, 256, None, None, 16, 2, None, None, None, 0)  # T = 0 is a no-op
+
+
+def test_ffn_combine_permute_validation():
+    ws = L.moe_expert_ffn_workspace_bytes(4, 256, 128, 16, 2, 0)
+    args = [FAKE, 4, 256, 128, 16, FAKE, 2, FAKE, None, None, FAKE, FAKE, ws]
+    assert _status(L.moe_expert_ffn, None, *args[1:]) == L.MOE_E_ARG
+    bad = list(args); bad[2] = 250
+    assert _status(L.moe_expert_ffn, *bad) == L.MOE_E_SHAPE
+    bad = list(args); bad[3] = 100
+    assert _status(L.moe_expert_ffn, *bad) == L.MOE_E_SHAPE
+    bad = list(args); bad[6] = 17
+    assert _status(L.moe_expert_ffn, *bad) == L.MOE_E_SHAPE
+    bad = list(args); bad[12] = ws - 1
+    assert _status(L.moe_expert_ffn, *bad) == L.MOE_E_NOMEM
+    assert _status(L.moe_expert_ffn, *args, 7) == L.MOE_E_ARG
+    assert _status(L.moe_combine, None, FAKE, 4, 2, 256, 0, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_combine, FAKE, FAKE, 4, 2, 254, 0, FAKE) == L.MOE_E_SHAPE
+    assert _status(L.moe_permute, FAKE, 4096, 8, 256, FAKE, FAKE, FAKE) == L.MOE_E_SHAPE
+    assert _status(L.moe_permute, FAKE, 4, 8, 4, FAKE, FAKE, FAKE) == L.MOE_E_SHAPE
+    assert _status(L.moe_debug_dequant, FAKE, 256, 128, 3, FAKE) == L.MOE_E_ARG
+
+
+# ----------------------------------------------------------------------------- cache policy
+class LRUModel:
+    """Brute-force model of the documented cache rule, one layer at a time."""
+
+    def __init__(self, layers, experts, slots):
+        self.E, self.C = experts, slots
+        self.slot_of = [dict() for _ in range(layers)]
+        self.expert_of = [[-1] * slots for _ in range(layers)]
+        self.stamp = [[0] * slots for _ in range(layers)]
+        self.held = [[False] * slots for _ in range(layers)]
+        self.last_rel = [[-1] * slots for _ in range(layers)]
+        self.next_rel = [0] * layers
+        self.clock = 0
+        self.hits = self.misses = 0
+
+    def prefetch(self, l, experts):
+        srt = sorted(experts)
+        hits = [e for e in srt if e in self.slot_of[l]]
+        misses = [e for e in srt if e not in self.slot_of[l]]
+        needed = {self.slot_of[l][e] for e in hits}
+        free = sum(1 for s in range(self.C) if not self.held[l][s] and s not in needed)
+        if len(experts) > self.C or len(misses) > free:
+            return "capacity", []
+        cmds = []
+        for e in hits:
+            s = self.slot_of[l][e]
+            self.clock += 1
+            self.stamp[l][s] = self.clock
+            self.held[l][s] = True
+        table = []
+        last_wait = -2
+        for e in misses:
+            victim = min((self.stamp[l][s], s) for s in range(self.C) if not self.held[l][s])[1]
+            old = self.expert_of[l][victim]
+            if old >= 0:
+                del self.slot_of[l][old]
+                table.append((3, l, old, -1))
+            if self.last_rel[l][victim] >= 0 and self.last_rel[l][victim] != last_wait:
+                cmds.append((1, victim, self.last_rel[l][victim], -1))
+                last_wait = self.last_rel[l][victim]
+            cmds.append((2, l, e, victim))
+            self.expert_of[l][victim] = e
+            self.slot_of[l][e] = victim
+            self.clock += 1
+            self.stamp[l][victim] = self.clock
+            self.held[l][victim] = True
+            table.append((3, l, e, victim))
+        cmds += table
+        if misses:
+            cmds.append((4, l, -1, -1))
+        self.hits += len(hits)
+        self.misses += len(misses)
+        return "ok", cmds
+
+    def release(self, l):
+        n = sum(self.held[l])
+        if n == 0:
+            return []
+        rid = self.next_rel[l]
+        self.next_rel[l] += 1
+        for s in range(self.C):
+            if self.held[l][s]:
+                self.held[l][s] = False
+                self.last_rel[l][s] = rid
+        return [(5, l, rid, n)]
+
+
+def _desc(layers, experts, slots, hidden=256, inter=128):
+    return L.moe_cache_desc(layers, experts, hidden, inter, slots)
+
+
+@pytest.mark.parametrize("seed,layers,experts,slots,maxreq", [
+    (1, 1, 16, 4, 4), (2, 3, 16, 8, 6), (3, 2, 128, 32, 8), (4, 2, 64, 25, 25), (5, 1, 8, 8, 8)])
+def test_cache_policy_matches_bruteforce_lru(seed, layers, experts, slots, maxreq):
+    rng = random.Random(seed)
+    cache = L.moe_cache_create_recording(_desc(layers, experts, slots), 1 << 40)
+    model = LRUModel(layers, experts, slots)
+    expected = []
+    for step in range(300):
+        l = rng.randrange(layers)
+        n = rng.randint(1, maxreq)
+        # Zipf-like popularity so that hits happen
+        pool = sorted(range(experts), key=lambda e: rng.random() * (e + 1) ** 1.1)
+        req = pool[:n]
+        status, cmds = model.prefetch(l, req)
+        if status == "capacity":
+            with pytest.raises(L.MoEError) as ei:
+                L.moe_cache_prefetch(cache, l, req)
+            assert ei.value.status == L.MOE_E_CAPACITY
+        else:
+            ncopies = L.moe_cache_prefetch(cache, l, req)
+            assert ncopies == sum(1 for c in cmds if c[0] == 2)
+            expected += cmds
+            slots_got, h = L.moe_cache_lookup(cache, l, req)
+            assert all(s >= 0 for s in slots_got) and h == len(req)
+        if rng.random() < 0.8:
+            L.moe_cache_release(cache, l)
+            expected += model.release(l)
+    assert L.moe_cache_trace(cache) == expected
+    hits, misses, nbytes = L.moe_cache_stats(cache)
+    assert (hits, misses) == (model.hits, model.misses)
+    assert nbytes == misses * L.moe_expert_bytes(256, 128)
+    L.moe_cache_destroy(cache)
+
+
+def test_cache_slot_addresses_and_capacity_rules():
+    slab = L.moe_expert_bytes(256, 128)
+    cache = L.moe_cache_create_recording(_desc(2, 16, 4), 1 << 40)
+    assert L.moe_cache_prefetch(cache, 1, [3, 1, 2]) == 3
+    slots, hits = L.moe_cache_lookup(cache, 1, [1, 2, 3, 4])
+    assert slots == [0, 1, 2, -1] and hits == 3  # misses fill never-used slots in ascending id order
+    # held slots cannot be evicted: 3 held + 2 new misses > 4 slots
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_cache_prefetch(cache, 1, [5, 6])
+    assert ei.value.status == L.MOE_E_CAPACITY
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_cache_prefetch(cache, 1, [0, 1, 2, 3, 4])
+    assert ei.value.status == L.MOE_E_CAPACITY
+    L.moe_cache_release(cache, 1)
+    assert L.moe_cache_prefetch(cache, 1, [5, 6]) == 2  # evicts LRU slot 3 (empty) then expert 1's slot 0
+    slots, _ = L.moe_cache_lookup(cache, 1, [1, 2, 3, 5, 6])
+    assert slots == [-1, 1, 2, 3, 0]
+    trace = L.moe_cache_trace(cache)
+    assert (1, 0, 0, -1) in trace  # copy into slot 0 waits for release 0 of layer 1
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_cache_prefetch(cache, 1, [7, 7])
+    assert ei.value.status == L.MOE_E_ARG
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_cache_prefetch(cache, 2, [1])
+    assert ei.value.status == L.MOE_E_ARG
+    L.moe_cache_reset(cache)
+    assert L.moe_cache_lookup(cache, 1, [2, 5])[1] == 0
+    assert L.moe_cache_stats(cache) == (0, 0, 0)
+    L.moe_cache_destroy(cache)
+    assert slab == 61440
+
+
+def test_cache_copy_failure_leaves_slot_empty():
+    cache = L.moe_cache_create_recording(_desc(1, 16, 6), 1 << 40, fail_copy_at=3)
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_cache_prefetch(cache, 0, [4, 7, 9, 11])
+    assert ei.value.status == L.MOE_E_HIP
+    slots, hits = L.moe_cache_lookup(cache, 0, [4, 7, 9, 11])
+    assert slots[:2] == [0, 1] and slots[2:] == [-1, -1] and hits == 2
+    # the request was un-held: a full-size request still fits and re-streams the failed ones
+    assert L.moe_cache_prefetch(cache, 0, [4, 7, 9, 11, 12, 13]) == 4
+    assert L.moe_cache_lookup(cache, 0, [9, 11])[1] == 2
+    L.moe_cache_destroy(cache)
+
+
+def test_cache_create_rejects_bad_descriptions():
+    for d in (_desc(0, 16, 4), _desc(1, 16, 0), _desc(1, 16, 17), _desc(1, 16, 4, hidden=100)):
+        with pytest.raises(L.MoEError):
+            L.moe_cache_create_recording(d)

@@ -1,0 +1,335 @@
+"""GPU parity: every result of the HIP path against the CPU oracle on the same
+seeded inputs, plus invariances (streamed == resident, run-to-run identity, and
+pair-grouped == expert-grouped kernels).
+
+Bars: expert indices bit-exact; gate weights within 1e-6; outputs within
+max|err| <= 2e-2 * max|ref| per (step, layer) tensor (bf16 activations, fp32
+accumulation); dequantisation exact.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from routed_expert_streaming_amd import _lib as L
+from routed_expert_streaming_amd.runtime import MoEStack
+from tests import slabkit as sk
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.lib()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_close(got_bits, ref64, what):
+    got = bf16_to_f64(got_bits)
+    scale = float(np.max(np.abs(ref64)))
+    err = float(np.max(np.abs(got - ref64)))
+    assert scale > 0
+    assert err <= TOL * scale, f"{what}: max abs err {err:.3e} > {TOL} * {scale:.3e}"
+    return err / scale
+
+
+def run_router(x_bits, Wr, bias, k):
+    T, H = x_bits.shape
+    E = Wr.shape[0]
+    x = bf16_dev(x_bits)
+    wr = torch.from_numpy(Wr).cuda()
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    nb = L.moe_router_workspace_bytes(T, E)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    L.moe_router_topk(x, T, H, wr, b, E, k, idx, w, ws, nb)
+    torch.cuda.synchronize()
+    logits = ws[256:256 + T * E * 4].view(torch.float32).view(T, E).cpu().numpy()
+    return idx.cpu().numpy(), w.cpu().numpy(), logits, ws
+
+
+def f32_ulp_diff(a, b):
+    ia = a.astype(np.float32).view(np.int32).astype(np.int64)
+    ib = b.astype(np.float32).view(np.int32).astype(np.int64)
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return np.abs(ia - ib)
+
+
+# ---------------------------------------------------------------------------- router
+ROUTER_CASES = [
+    # T, H, E, k, bias
+    (4, 256, 16, 2, None),
+    (1, 4096, 128, 8, "zipf"),
+    (32, 6144, 256, 8, "zipf"),
+    (33, 96, 40, 5, "rand"),
+    (100, 512, 64, 6, "rand"),
+    (7, 128, 1024, 64, None),
+    (2048, 6144, 256, 8, None),
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,bias", ROUTER_CASES)
+def test_router_topk_bit_exact(T, H, E, k, bias):
+    seed = 1000 + T + H + E
+    x = synth.x_bf16(seed, 0, 0, T, H)
+    Wr = synth.router_w(seed, 0, E, H)
+    b = None
+    if bias == "zipf":
+        b = np.empty(E, np.float32)
+        synth.lib().synth_zipf_bias(seed, 0, E, 1.1, b.ctypes.data)
+    elif bias == "rand":
+        b = np.random.default_rng(seed).standard_normal(E).astype(np.float32)
+    idx, w, logits, _ = run_router(x, Wr, b, k)
+    ref_logits, ref_idx, ref_w = oracle.router(x, Wr, b, k)
+    assert f32_ulp_diff(logits, ref_logits).max() <= 1
+    assert np.array_equal(idx, ref_idx)
+    assert np.max(np.abs(w - ref_w)) <= 1e-6
+    assert np.max(np.abs(w.sum(axis=1) - 1.0)) <= 4 * k * 2.0 ** -24
+
+
+def test_router_ties_and_degenerate_cases():
+    T, H, E = 9, 256, 32
+    x = synth.x_bf16(5, 0, 0, T, H)
+    Wr = synth.router_w(5, 0, E, H)
+    Wr[17] = Wr[4]
+    Wr[30] = Wr[4]
+    Wr[2] = Wr[9]
+    for k in (1, 2, 4, 8, 32):
+        idx, w, _, _ = run_router(x, Wr, None, k)
+        _, ref_idx, ref_w = oracle.router(x, Wr, None, k)
+        assert np.array_equal(idx, ref_idx)
+        assert np.max(np.abs(w - ref_w)) <= 1e-6
+    idx, w, _, _ = run_router(x, np.zeros((E, H), np.float32), None, 8)
+    assert (idx == np.arange(8)).all() and (w == np.float32(0.125)).all()
+    idx, w, _, _ = run_router(x, Wr, None, 1)
+    assert (w == 1.0).all()
+
+
+def test_router_workspace_ticket_is_left_zero():
+    x = synth.x_bf16(3, 0, 0, 2, 256)
+    Wr = synth.router_w(3, 0, 16, 256)
+    _, _, _, ws = run_router(x, Wr, None, 2)
+    assert int(ws[:256].sum().item()) == 0
+
+
+# ---------------------------------------------------------------------------- dequant
+def test_debug_dequant_round_trip_exact():
+    H, I = 64, 32
+    q1 = (np.arange(I)[:, None] + 3 * np.arange(H)[None, :]) % 16
+    s1 = sk.f16(2.0 ** -(np.arange(I * H // 32).reshape(I, H // 32) % 7))
+    m1 = sk.f16(-8.0 * s1.view(np.float16).astype(np.float64))
+    mats = [(q1, s1, m1), (q1[::-1].copy(), sk.f16(0.5), sk.f16(0.25)),
+            ((np.arange(H)[:, None] * 5 + np.arange(I)[None, :]) % 16, sk.f16(2.0 ** -24), sk.f16(-(2.0 ** -21)))]
+    slabs = [sk.build_slab(H, I, *mats), synth.expert_slab(77, 0, 3, 256, 128),
+             synth.expert_slab(78, 1, 5, 4096, 1536)]
+    for slab, (h, i) in zip(slabs, [(H, I), (256, 128), (4096, 1536)]):
+        d = torch.from_numpy(slab).cuda()
+        for which in range(3):
+            rows, cols = (i, h) if which < 2 else (h, i)
+            out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+            L.moe_debug_dequant(d, h, i, which, out)
+            assert np.array_equal(out.cpu().numpy().astype(np.float64), oracle.dequant(slab, h, i, which))
+
+
+# ---------------------------------------------------------------------------- one layer
+class Layer:
+    """One MoE layer's inputs on host and device."""
+
+    def __init__(self, T, H, I, E, k, shared, bias=None, seed=7, x_seed=None):
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.x = synth.x_bf16(x_seed or seed, 0, 0, T, H)
+        self.Wr = synth.router_w(seed, 0, E, H)
+        self.bias = None
+        if bias == "zipf":
+            self.bias = np.empty(E, np.float32)
+            synth.lib().synth_zipf_bias(seed, 0, E, 1.1, self.bias.ctypes.data)
+        slab = synth.slab_bytes(H, I)
+        self.slabs = [np.empty(slab, np.uint8) for _ in range(E)]
+        synth.fill_slabs(seed, 0, list(range(E)), H, I, [s.ctypes.data for s in self.slabs])
+        self.shared = synth.expert_slab(seed, 0, E, H, I) if shared else None
+        self.pool = torch.from_numpy(np.stack(self.slabs)).cuda()
+        self.table = torch.tensor([self.pool.data_ptr() + e * slab for e in range(E)], dtype=torch.int64,
+                                  device="cuda")
+        self.shared_dev = torch.from_numpy(self.shared).cuda() if shared else None
+
+    def run(self, path=L.MOE_FFN_AUTO, mask=None):
+        T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
+        x = bf16_dev(self.x)
+        wr = torch.from_numpy(self.Wr).cuda()
+        b = None if self.bias is None else torch.from_numpy(self.bias).cuda()
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        nb = L.moe_router_workspace_bytes(T, E)
+        rws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        L.moe_router_topk(x, T, H, wr, b, E, k, idx, w, rws, nb)
+        P = T * k + (T if self.shared is not None else 0)
+        y = torch.full((P, H), float("nan"), dtype=torch.float32, device="cuda")
+        fb = L.moe_expert_ffn_workspace_bytes(T, H, I, E, k, self.shared is not None)
+        fws = torch.empty(fb, dtype=torch.uint8, device="cuda")
+        L.moe_expert_ffn(x, T, H, I, E, idx, k, self.table, self.shared_dev, mask, y, fws, fb, path)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        L.moe_combine(y, w, T, k, H, self.shared is not None, out)
+        torch.cuda.synchronize()
+        return idx.cpu().numpy(), y.cpu().numpy(), out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def oracle(self, rows=None):
+        return oracle.moe_layer(self.x, self.Wr, self.bias, self.k, self.slabs, self.shared, self.I, rows=rows)
+
+
+LAYER_CASES = [
+    # name, T, H, I, E, k, shared, bias, oracle rows
+    ("tiny", 4, 256, 128, 16, 2, False, None, None),
+    ("decode1", 1, 4096, 1536, 128, 8, True, None, None),
+    ("ragged", 5, 96, 160, 12, 3, True, "zipf", None),
+    ("wide_k", 3, 1024, 512, 64, 16, True, None, None),
+    ("multi_pass", 64, 512, 256, 32, 4, True, None, None),
+    ("decode32", 32, 6144, 2048, 256, 8, True, "zipf", [0, 5, 17, 31]),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,shared,bias,rows", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_parity_all_paths(name, T, H, I, E, k, shared, bias, rows):
+    lay = Layer(T, H, I, E, k, shared, bias, seed=zlib.crc32(name.encode()) % 1000 + 11)
+    ref = lay.oracle(rows)
+    results = {}
+    paths = [L.MOE_FFN_PAIRS, L.MOE_FFN_GROUPED]
+    for path in paths:
+        idx, y, out = lay.run(path)
+        assert np.array_equal(idx, ref["idx"])
+        sel = slice(None) if rows is None else rows
+        ratio = check_close(out[sel], ref["out64"][sel], f"{name} path {path}")
+        results[path] = (y, out, ratio)
+    # both kernel groupings compute each (token, expert) pair with the same arithmetic
+    assert np.array_equal(results[paths[0]][0], results[paths[1]][0])
+    assert np.array_equal(results[paths[0]][1], results[paths[1]][1])
+    print(f"{name}: max err / max|ref| = {results[paths[0]][2]:.2e}")
+
+
+def test_mask_computes_only_admitted_experts():
+    lay = Layer(6, 256, 128, 16, 2, True, None, seed=31)
+    _, y_all, _ = lay.run(L.MOE_FFN_GROUPED)
+    idx = lay.oracle()["idx"]
+    mask_np = np.zeros(16, np.uint8)
+    mask_np[[int(e) for e in idx.ravel()[::3]]] = 1
+    mask = torch.from_numpy(mask_np).cuda()
+    for path in (L.MOE_FFN_PAIRS, L.MOE_FFN_GROUPED):
+        _, y, _ = lay.run(path, mask=mask)
+        for p in range(6 * 2):
+            if mask_np[idx.ravel()[p]]:
+                assert np.array_equal(y[p], y_all[p])
+            else:
+                assert np.isnan(y[p]).all()
+        assert np.array_equal(y[12:], y_all[12:])  # shared expert rows
+
+
+# ---------------------------------------------------------------------------- stacks
+def run_stack(stack, steps, x_steps=None):
+    outs = []
+    for s in range(steps):
+        x = stack.make_inputs(s) if x_steps is None else x_steps[s]
+        out = stack.new_output()
+        stack.forward(x, out)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    return outs
+
+
+def oracle_stack_step(stack, step, layers=None, rows=None):
+    cfg = stack.cfg
+    res = []
+    for l in (layers if layers is not None else range(stack.L)):
+        x = synth.x_bf16(cfg.seed, step, l, stack.T, stack.H)
+        Wr = synth.router_w(cfg.seed, l, stack.E, stack.H)
+        b = synth.router_bias(cfg, l)
+        res.append(oracle.moe_layer(x, Wr, b, stack.k, stack.host_slabs(l), stack.host_shared(l), stack.I, rows=rows))
+    return res
+
+
+def test_stack_tiny_full():
+    stack = MoEStack(synth.get("tiny"))
+    outs = run_stack(stack, 3)
+    for s in range(3):
+        ref = oracle_stack_step(stack, s)
+        for l in range(stack.L):
+            check_close(outs[s][l], ref[l]["out64"], f"tiny step {s} layer {l}")
+    stack.close()
+
+
+def test_stack_decode1_full_and_deterministic():
+    stack = MoEStack(synth.get("decode1"))
+    outs = run_stack(stack, 2)
+    again = run_stack(stack, 2)
+    for a, b in zip(outs, again):
+        assert np.array_equal(a, b)
+    ref = oracle_stack_step(stack, 1)
+    ratios = [check_close(outs[1][l], ref[l]["out64"], f"decode1 layer {l}") for l in range(stack.L)]
+    print("decode1 max err ratios:", ["%.1e" % r for r in ratios])
+    idx = stack.idx.cpu().numpy()
+    for l in range(stack.L):
+        assert np.array_equal(idx[l], ref[l]["idx"])
+    stack.close()
+
+
+def lru_replay(idx_steps, L_, C):
+    """Hits/misses of the documented LRU rule replayed on the routing trace."""
+    from tests.test_abi_cpu import LRUModel
+    model = LRUModel(L_, 10 ** 6, C)
+    for idx in idx_steps:
+        for l in range(L_):
+            needed = sorted(set(int(e) for e in idx[l].ravel()))
+            resident = [e for e in needed if e in model.slot_of[l]]
+            order = resident + [e for e in needed if e not in model.slot_of[l]]
+            for i in range(0, len(order), C):
+                status, _ = model.prefetch(l, sorted(order[i:i + C]))
+                assert status == "ok"
+                model.release(l)
+    return model.hits, model.misses
+
+
+@pytest.mark.parametrize("name,layers,steps", [("decode1_stream", 8, 12), ("decode32_stream", 2, 3)])
+def test_streaming_equals_resident_and_lru_replay(name, layers, steps):
+    cfg = synth.get(name)
+    streamed = MoEStack(cfg, layers=layers)
+    assert streamed.streaming
+    xs = [streamed.make_inputs(s) for s in range(steps)]
+    out_s, idx_trace = [], []
+    for s in range(steps):
+        out = streamed.new_output()
+        streamed.forward(xs[s], out)
+        torch.cuda.synchronize()
+        out_s.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
+        idx_trace.append(streamed.idx.cpu().numpy().copy())
+    hits, misses, nbytes = streamed.stats()
+    assert (hits, misses) == lru_replay(idx_trace, layers, streamed.C)
+    assert nbytes == misses * streamed.slab
+    print(f"{name}: hit rate {hits / (hits + misses):.3f}")
+    streamed.close()
+    resident = MoEStack(cfg, layers=layers, cap=1.0)
+    out_r = run_stack(resident, steps, xs)
+    for a, b in zip(out_s, out_r):
+        assert np.array_equal(a, b)
+    # oracle on the first step (sampled tokens for the batch-32 case)
+    rows = None if cfg.tokens <= 4 else [0, 9, 31]
+    ref = oracle_stack_step(resident, 0, rows=rows)
+    for l in range(layers):
+        sel = slice(None) if rows is None else rows
+        check_close(out_r[0][l][sel], ref[l]["out64"][sel], f"{name} layer {l}")
+    resident.close()
