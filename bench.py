@@ -183,7 +183,7 @@ def main():
                    "hidden": cfg.hidden, "inter": cfg.inter, "experts": cfg.experts, "shared": cfg.shared,
                    "top_k": cfg.top_k, "resident": True, "graph": graphs is not None,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "ffn_gemv_kernel<64,2,gate_up> (dequant + gate/up + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "decode_gate_up_kernel (dequant + gate/up + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},

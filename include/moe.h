@@ -79,9 +79,9 @@ size_t moe_expert_bytes(int hidden, int inter);
  * x [T,H] bf16 row-major; w_router [E,H] fp32 row-major; bias [E] fp32 or NULL;
  * topk_idx [T,k] int32; topk_w [T,k] fp32.  1 <= k <= min(E, 64), E <= 1024,
  * H % 32 == 0.  Inputs must be finite.
- * workspace: moe_router_workspace_bytes(T, E) bytes of device memory whose first
- * 256 bytes must be zero before the first call on that buffer (every call leaves
- * them zero again); calls sharing a workspace must not overlap in time. */
+ * workspace: moe_router_workspace_bytes(T, E) bytes of device memory (contents
+ * don't care; calls sharing a workspace must not overlap in time).  After the
+ * call the fp32 logits [T,E] are at byte offset 256 of the workspace. */
 size_t moe_router_workspace_bytes(int T, int E);
 int moe_router_topk(const uint16_t *x, int T, int H, const float *w_router, const float *bias, int E,
                     int k, int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes,
@@ -198,6 +198,16 @@ int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t
  * y as produced by moe_expert_ffn; out [T,H] bf16. */
 int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,
                 void *stream);
+
+/* Gate/up + SwiGLU, down projection and the weighted combine in one call:
+ * the same arithmetic, order and roundings as moe_expert_ffn followed by
+ * moe_combine, so the result is bit-identical; for a few tokens (decode) the
+ * down projection and the combine run in one kernel that owns whole output
+ * rows.  Every routed expert must be resident (no mask).  topk_w [T,k] fp32;
+ * out [T,H] bf16; workspace: moe_expert_ffn_workspace_bytes(...). */
+int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
+                           const float *topk_w, int k, const void *const *expert_table, const void *shared_slab,
+                           uint16_t *out, void *workspace, size_t workspace_bytes, int path, void *stream);
 
 /* ------------------------------------------------------------------ debug
  * Dequantise matrix `which` (0 = W1, 1 = W3, 2 = W2) of a device slab into out

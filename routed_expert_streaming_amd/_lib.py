@@ -12,7 +12,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB_PATH selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_E_ARG, MOE_E_SHAPE, MOE_E_NOT_PINNED, MOE_E_NOMEM, MOE_E_CAPACITY, MOE_E_HIP, MOE_E_STATE = \
     0, -1, -2, -3, -4, -5, -6, -7
@@ -69,6 +70,7 @@ def lib():
             "moe_expert_ffn": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, sz, i, vp], i),
             "moe_expert_gate_up": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, vp], i),
             "moe_expert_down": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, vp], i),
+            "moe_expert_ffn_combine": ([vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, i, vp], i),
             "moe_combine": ([vp, vp, i, i, i, i, vp, vp], i),
             "moe_debug_dequant": ([vp, i, i, i, vp, vp], i),
         }
@@ -247,6 +249,13 @@ def moe_expert_down(h, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expe
     _check(lib().moe_expert_down(_ptr(h), T, H, I, E, _ptr(topk_idx), k, _ptr(count), _ptr(offset),
                                  _ptr(pair_of_row), _ptr(expert_table), _ptr(shared_slab), _ptr(expert_mask),
                                  _ptr(y), path, _stream(stream)), "moe_expert_down")
+
+
+def moe_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, workspace,
+                           workspace_bytes, path=MOE_FFN_AUTO, stream=None):
+    _check(lib().moe_expert_ffn_combine(_ptr(x), T, H, I, E, _ptr(topk_idx), _ptr(topk_w), k, _ptr(expert_table),
+                                        _ptr(shared_slab), _ptr(out), _ptr(workspace), workspace_bytes, path,
+                                        _stream(stream)), "moe_expert_ffn_combine")
 
 
 def moe_combine(y, topk_w, T, k, H, has_shared, out, stream=None):

@@ -20,12 +20,14 @@ LIB = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "router.hip", "ffn_gemv.hip", "ffn_entry.hip", "cache.hip"]
+SOURCES = ["abi.cpp", "router.hip", "ffn_gemv.hip", "ffn_decode.hip", "ffn_entry.hip", "cache.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument"]
+# Extra -D tuning knobs (e.g. MOE_EXTRA_DEFINES="MOE_STREAM_NT=1 MOE_GEMV_BLOCKS_IN_FLIGHT=8")
+COMMON += [f"-D{d}" for d in os.environ.get("MOE_EXTRA_DEFINES", "").split() if d]
 
 
 def _compile(src: str) -> str:
@@ -38,22 +40,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str | None = None) -> str:
+    global BUILD_DIR
+    target = out or LIB
+    if out:
+        BUILD_DIR = os.path.join(ROOT, "_build", os.path.basename(out) + ".d")
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = target + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, target)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {target}")
+    return target
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, out=sys.argv[1] if len(sys.argv) > 1 else None)
     sys.exit(0)

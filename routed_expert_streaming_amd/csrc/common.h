@@ -34,6 +34,44 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // ------------------------------------------------------------------ device helpers
 typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
 
+typedef unsigned int moe_u32x4 __attribute__((ext_vector_type(4)));
+
+// Build-time tuning knobs of the weight-streaming kernels (defaults are the
+// tuned values; see the build script for how to override them).
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 0  // 1: weight loads marked non-temporal
+#endif
+
+// Global-address-space views: loads through them compile to global_load (not
+// flat_load, which would also count against the LDS wait counter and make every
+// LDS wait drain the weight stream).
+typedef __attribute__((address_space(1))) const moe_u32x4 moe_gu32x4;
+typedef __attribute__((address_space(1))) const uint32_t moe_gu32;
+
+// Weight loads: every weight byte is read once per launch.
+__device__ __forceinline__ uint4 load_stream_u4(const void *p) {
+    const moe_gu32x4 *g = (const moe_gu32x4 *)p;
+#if MOE_STREAM_NT
+    const moe_u32x4 v = __builtin_nontemporal_load(g);
+#else
+    const moe_u32x4 v = *g;
+#endif
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load_stream_u32(const void *p) {
+    const moe_gu32 *g = (const moe_gu32 *)p;
+#if MOE_STREAM_NT
+    return __builtin_nontemporal_load(g);
+#else
+    return *g;
+#endif
+}
+// Plain global loads of small operands (activations, tables).
+__device__ __forceinline__ uint4 load_global_u4(const void *p) {
+    const moe_u32x4 v = *(const moe_gu32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bits, round to nearest even (NaN kept quiet).

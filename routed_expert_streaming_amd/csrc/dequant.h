@@ -1,0 +1,85 @@
+// 4-bit block dequant + dot product helpers shared by every expert-FFN kernel,
+// so all kernel families compute each (token, expert) result with the same
+// operations in the same order (their outputs are bit-identical).
+//
+// Weight block: 32 codes q in 16 bytes (byte b: column 2b in bits 0-3, 2b+1 in
+// bits 4-7) plus one (fp16 scale, fp16 min) record; value = scale*q + min.
+// Activations are bf16, pre-arranged per 8-column word as the pairs
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7) that the nibble extraction below produces:
+// (w >> 4s) & 0x000F000F puts columns s and s+4 of the word in the two halves,
+// OR-ing 0x4300 makes each half the bf16 value 128 + q (exponent 2^7, ulp 1).
+// v_dot2_f32_bf16 then accumulates (128+q)*x exactly per product in fp32, and
+//   sum (scale*q + min) * x = scale * sum((128+q) x) + (min - 128*scale) * sum x.
+#pragma once
+#include "common.h"
+
+// The bf16 exponent pattern 0x4300 in both halves, held in a VGPR: gfx9 VOP3
+// instructions read at most one scalar/constant operand, so keeping this one in
+// a vector register lets (w & mask) | magic compile to a single v_and_or_b32.
+__device__ __forceinline__ uint32_t moe_magic_vgpr() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+    return m;
+}
+
+__device__ __forceinline__ uint32_t moe_and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+    return r;
+}
+
+// sum over one block of (128 + q) * x; two interleaved accumulators shorten the
+// dependency chain (fixed order: words 0,2 in acc0, words 1,3 in acc1).
+__device__ __forceinline__ float moe_block_dot(const uint4 c, const uint4 *xb, int stride, uint32_t magic) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t mask = 0x000F000Fu;
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 X = xb[j * stride];
+        float a = acc[j & 1];
+        a = dot2_bf16(moe_and_or(w[j], mask, magic), X.x, a);
+        a = dot2_bf16(moe_and_or(w[j] >> 4, mask, magic), X.y, a);
+        a = dot2_bf16(moe_and_or(w[j] >> 8, mask, magic), X.z, a);
+        a = dot2_bf16(moe_and_or(w[j] >> 12, mask, magic), X.w, a);
+        acc[j & 1] = a;
+    }
+    return acc[0] + acc[1];
+}
+
+// sum over the block of (scale*q + min) * x from acc = sum (128+q) x and S = sum x
+__device__ __forceinline__ float moe_block_value(uint32_t rec, float acc, float S) {
+    const float sc = fp16_bits_to_f32(rec & 0xFFFFu);
+    const float mn = fp16_bits_to_f32(rec >> 16);
+    return fmaf(sc, acc, fmaf(-128.0f, sc, mn) * S);  // min - 128*scale is exact in fp32
+}
+
+// Sum over groups of W consecutive lanes.  W = 16 and 64 use DPP row shifts and
+// row broadcasts (no LDS traffic); the total is valid in the LAST lane of each
+// group.  Other W use a butterfly and every lane holds the total.  The order of
+// additions is fixed, so results are reproducible.
+template <int W>
+__device__ __forceinline__ float moe_group_sum(float v) {
+    if constexpr (W == 16 || W == 64) {
+        // inclusive scan inside each 16-lane row: lane 15 of a row holds its sum
+        v += __builtin_amdgcn_update_dpp(0.0f, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+        v += __builtin_amdgcn_update_dpp(0.0f, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+        v += __builtin_amdgcn_update_dpp(0.0f, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+        v += __builtin_amdgcn_update_dpp(0.0f, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+        if constexpr (W == 64) {
+            v += __builtin_amdgcn_update_dpp(0.0f, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1,3
+            v += __builtin_amdgcn_update_dpp(0.0f, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2,3
+        }
+        return v;
+    } else {
+#pragma unroll
+        for (int o = W / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        return v;
+    }
+}
+
+// lane of a W-lane group that holds moe_group_sum's result
+template <int W>
+__device__ __forceinline__ bool moe_group_sum_owner(int lane_in_group) {
+    return (W == 16 || W == 64) ? lane_in_group == W - 1 : lane_in_group == 0;
+}

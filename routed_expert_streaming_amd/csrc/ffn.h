@@ -25,6 +25,12 @@ struct FfnArgs {
 int ffn_gemv_gate_up(const FfnArgs &a, int max_m, hipStream_t s);
 int ffn_gemv_down(const FfnArgs &a, int max_m, hipStream_t s);
 
+// Decode kernels (pair grouping, few tokens): true if this shape is covered.
+bool decode_supported(const FfnArgs &a);
+int decode_gate_up(const FfnArgs &a, hipStream_t s);
+// out == nullptr: write y; otherwise apply the weighted combine into out [T, H].
+int decode_down(const FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s);
+
 // Counting sort of pairs by expert (see moe_permute).
 int permute_launch(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
                    int32_t *pair_of_row, hipStream_t s);

@@ -128,10 +128,10 @@ extern "C" int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t
 namespace {
 
 struct FfnLayout {
-    size_t h, count, offset, pairs, total;
+    size_t h, count, offset, pairs, y, total;
 };
 
-FfnLayout ffn_layout(int T, int I, int E, int k, int has_shared) {
+FfnLayout ffn_layout(int T, int H, int I, int E, int k, int has_shared) {
     FfnLayout L{};
     const size_t P = (size_t)T * k + (has_shared ? (size_t)T : 0);
     size_t o = 0;
@@ -143,6 +143,8 @@ FfnLayout ffn_layout(int T, int I, int E, int k, int has_shared) {
     o += moe::align_up((size_t)(E + 1) * sizeof(int32_t), 256);
     L.pairs = o;
     o += moe::align_up((size_t)T * k * sizeof(int32_t), 256);
+    L.y = o;
+    o += moe::align_up(P * H * sizeof(float), 256);
     L.total = o;
     return L;
 }
@@ -150,9 +152,8 @@ FfnLayout ffn_layout(int T, int I, int E, int k, int has_shared) {
 }  // namespace
 
 extern "C" size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int has_shared) {
-    (void)H;
-    if (T < 0 || I <= 0 || E <= 0 || k <= 0) return 0;
-    return ffn_layout(T, I, E, k, has_shared).total;
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
+    return ffn_layout(T, H, I, E, k, has_shared).total;
 }
 
 namespace {
@@ -216,6 +217,7 @@ extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E,
     rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
                    expert_mask, path, &max_m, "expert_gate_up");
     if (rc != MOE_OK) return rc;
+    if (moe::decode_supported(a)) return moe::decode_gate_up(a, (hipStream_t)stream);
     return moe::ffn_gemv_gate_up(a, max_m, (hipStream_t)stream);
 }
 
@@ -232,6 +234,7 @@ extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, co
     rc = make_args(a, nullptr, const_cast<uint16_t *>(h), y, T, H, I, E, topk_idx, k, count, offset, pair_of_row,
                    expert_table, shared_slab, expert_mask, path, &max_m, "expert_down");
     if (rc != MOE_OK) return rc;
+    if (moe::decode_supported(a)) return moe::decode_down(a, nullptr, nullptr, (hipStream_t)stream);
     return moe::ffn_gemv_down(a, max_m, (hipStream_t)stream);
 }
 
@@ -244,7 +247,7 @@ extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, con
     int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_ffn");
     if (rc != MOE_OK) return rc;
     const int has_shared = shared_slab != nullptr;
-    const FfnLayout Ly = ffn_layout(T, I, E, k, has_shared);
+    const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "expert_ffn: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
     if (path == MOE_FFN_AUTO) path = ((long long)T * k <= 64) ? MOE_FFN_PAIRS : MOE_FFN_GROUPED;
@@ -266,6 +269,42 @@ extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, con
     if (rc != MOE_OK) return rc;
     return moe_expert_down(h, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask,
                            y, path, stream);
+}
+
+extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
+                                      const float *topk_w, int k, const void *const *expert_table,
+                                      const void *shared_slab, uint16_t *out, void *workspace, size_t workspace_bytes,
+                                      int path, void *stream) {
+    if (T < 0) return moe::fail(MOE_E_ARG, "expert_ffn_combine: T=%d < 0", T);
+    if (T == 0) return MOE_OK;
+    if (!workspace || !topk_w) return moe::fail(MOE_E_ARG, "expert_ffn_combine: NULL pointer");
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, path, "expert_ffn_combine");
+    if (rc != MOE_OK) return rc;
+    const int has_shared = shared_slab != nullptr;
+    const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
+    if (workspace_bytes < Ly.total)
+        return moe::fail(MOE_E_NOMEM, "expert_ffn_combine: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
+    if (path == MOE_FFN_AUTO) path = ((long long)T * k <= 64) ? MOE_FFN_PAIRS : MOE_FFN_GROUPED;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    uint16_t *h = (uint16_t *)(ws + Ly.h);
+    if (path == MOE_FFN_PAIRS) {
+        moe::FfnArgs a;
+        int max_m = 1;
+        rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, nullptr, nullptr, nullptr, expert_table,
+                       shared_slab, nullptr, MOE_FFN_PAIRS, &max_m, "expert_ffn_combine");
+        if (rc != MOE_OK) return rc;
+        if (moe::decode_supported(a)) {
+            rc = moe::decode_gate_up(a, s);
+            if (rc != MOE_OK) return rc;
+            return moe::decode_down(a, topk_w, out, s);
+        }
+    }
+    float *y = (float *)(ws + Ly.y);
+    rc = moe_expert_ffn(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, nullptr, y, workspace,
+                        workspace_bytes, path, stream);
+    if (rc != MOE_OK) return rc;
+    return moe_combine(y, topk_w, T, k, H, has_shared, out, stream);
 }
 
 extern "C" int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,

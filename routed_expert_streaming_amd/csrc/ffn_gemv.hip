@@ -21,34 +21,13 @@
 //  * Partial sums of the LPR lanes of a row meet in a fixed butterfly, so the
 //    output is reproducible run to run.
 #include "common.h"
+#include "dequant.h"
 #include "ffn.h"
 
 namespace {
 
-constexpr int kMT = 4;        // tokens staged per pass
-constexpr int kRowIters = 4;  // rows per wave-subgroup per workgroup
+constexpr int kMT = 4;  // tokens staged per pass
 
-__device__ __forceinline__ float block_dot(const uint4 c, const uint4 *xb, int stride) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint4 X = xb[j * stride];
-        acc = dot2_bf16(((w[j]) & 0x000F000Fu) | 0x43004300u, X.x, acc);
-        acc = dot2_bf16(((w[j] >> 4) & 0x000F000Fu) | 0x43004300u, X.y, acc);
-        acc = dot2_bf16(((w[j] >> 8) & 0x000F000Fu) | 0x43004300u, X.z, acc);
-        acc = dot2_bf16(((w[j] >> 12) & 0x000F000Fu) | 0x43004300u, X.w, acc);
-    }
-    return acc;
-}
-
-// sum over the block of (scale*q + min) * x, from acc = sum (128+q) x and S = sum x
-__device__ __forceinline__ float block_value(uint32_t rec, float acc, float S) {
-    const float sc = fp16_bits_to_f32(rec & 0xFFFFu);
-    const float mn = fp16_bits_to_f32(rec >> 16);
-    const float cc = fmaf(-128.0f, sc, mn);  // exact: min - 128*scale
-    return fmaf(sc, acc, cc * S);
-}
 
 struct Group {
     const uint8_t *slab;
@@ -93,25 +72,22 @@ __device__ __forceinline__ int group_row(const moe::FfnArgs &a, const Group &gr,
 __device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ act, int K, const int *src_rows, int mcount,
                                            uint4 *X, float *S) {
     const int nblk = K >> 5;
-    for (int id = threadIdx.x; id < mcount * nblk * 4; id += blockDim.x) {
-        const int m = id / (nblk * 4), rem = id - m * nblk * 4;
-        const int b = rem >> 2, j = rem & 3;
-        const uint4 d = *reinterpret_cast<const uint4 *>(act + (size_t)src_rows[m] * K + 32 * b + 8 * j);
-        uint4 p;
-        p.x = (d.x & 0xFFFFu) | (d.z << 16);
-        p.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
-        p.z = (d.y & 0xFFFFu) | (d.w << 16);
-        p.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
-        X[(m * 4 + j) * nblk + b] = p;
-    }
     for (int id = threadIdx.x; id < mcount * nblk; id += blockDim.x) {
         const int m = id / nblk, b = id - m * nblk;
         const uint4 *src = reinterpret_cast<const uint4 *>(act + (size_t)src_rows[m] * K + 32 * b);
+        uint4 d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = src[j];  // the whole block in one round trip
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint4 d = src[j];
-            const uint32_t v[4] = {d.x, d.y, d.z, d.w};
+            uint4 p;
+            p.x = (d[j].x & 0xFFFFu) | (d[j].z << 16);
+            p.y = (d[j].x >> 16) | (d[j].z & 0xFFFF0000u);
+            p.z = (d[j].y & 0xFFFFu) | (d[j].w << 16);
+            p.w = (d[j].y >> 16) | (d[j].w & 0xFFFF0000u);
+            X[(m * 4 + j) * nblk + b] = p;
+            const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 s += bf16_bits_to_f32(v[q] & 0xFFFFu);
@@ -122,10 +98,17 @@ __device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ act, int
     }
 }
 
-template <int LPR, int BPL, bool GATEUP>
-__global__ __launch_bounds__(256) void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap) {
-    constexpr int RPW = 64 / LPR;                     // rows per wave at a time
-    constexpr int ROWS_PER_WG = 4 * RPW * kRowIters;  // rows per workgroup
+// RIT rows per lane-group; the weights of all of them are requested before the
+// activations are staged, so each wave keeps RIT*BPL*(2 or 1)*16 bytes per lane
+// in flight while the workgroup waits for the staging barrier.
+#ifndef MOE_GEMV_WAVES_PER_EU
+#define MOE_GEMV_WAVES_PER_EU 2
+#endif
+template <int LPR, int BPL, int RIT, bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_GEMV_WAVES_PER_EU)))
+void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap) {
+    constexpr int RPW = 64 / LPR;                // rows per wave at a time
+    constexpr int ROWS_PER_WG = 4 * RPW * RIT;   // rows per workgroup
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
     const int nblk = K >> 5;
@@ -145,10 +128,29 @@ __global__ __launch_bounds__(256) void ffn_gemv_kernel(moe::FfnArgs a, int tiles
     __shared__ int src_rows[kMT];
     __shared__ int out_rows[kMT];
 
+    const uint32_t magic = moe_magic_vgpr();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane / LPR, c = lane % LPR;
-    const int r_begin = tile * ROWS_PER_WG;
-    const int r_end = min(R, r_begin + ROWS_PER_WG);
+    const int r0 = tile * ROWS_PER_WG + wave * RPW + sub;
+
+    uint4 c0[RIT][BPL], c1[RIT][BPL];
+    uint32_t p0[RIT][BPL], p1[RIT][BPL];
+#pragma unroll
+    for (int i = 0; i < RIT; ++i) {
+        const int r = r0 + i * 4 * RPW;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            const int blk = c + b * LPR;
+            if (r < R && blk < nblk) {
+                c0[i][b] = load_stream_u4(mat0 + (size_t)r * (K / 2) + 16 * blk);
+                p0[i][b] = load_stream_u32(par0 + ((size_t)r * nblk + blk) * 4);
+                if (GATEUP) {
+                    c1[i][b] = load_stream_u4(mat1 + (size_t)r * (K / 2) + 16 * blk);
+                    p1[i][b] = load_stream_u32(par1 + ((size_t)r * nblk + blk) * 4);
+                }
+            }
+        }
+    }
 
     for (int pass = 0; pass < gr.M; pass += mt_cap) {
         const int mcount = min(mt_cap, gr.M - pass);
@@ -161,21 +163,10 @@ __global__ __launch_bounds__(256) void ffn_gemv_kernel(moe::FfnArgs a, int tiles
         stage_rows(GATEUP ? a.x : a.h, K, src_rows, mcount, X, S);
         __syncthreads();
 
-        for (int r = r_begin + wave * RPW + sub; r < r_end; r += 4 * RPW) {
-            uint4 c0[BPL], c1[BPL];
-            uint32_t p0[BPL], p1[BPL];
 #pragma unroll
-            for (int b = 0; b < BPL; ++b) {
-                const int blk = c + b * LPR;
-                if (blk < nblk) {
-                    c0[b] = *reinterpret_cast<const uint4 *>(mat0 + (size_t)r * (K / 2) + 16 * blk);
-                    p0[b] = *reinterpret_cast<const uint32_t *>(par0 + ((size_t)r * nblk + blk) * 4);
-                    if (GATEUP) {
-                        c1[b] = *reinterpret_cast<const uint4 *>(mat1 + (size_t)r * (K / 2) + 16 * blk);
-                        p1[b] = *reinterpret_cast<const uint32_t *>(par1 + ((size_t)r * nblk + blk) * 4);
-                    }
-                }
-            }
+        for (int i = 0; i < RIT; ++i) {
+            const int r = r0 + i * 4 * RPW;
+            if (r >= R) break;  // uniform within a lane group
             for (int m = 0; m < mcount; ++m) {
                 float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
@@ -184,13 +175,13 @@ __global__ __launch_bounds__(256) void ffn_gemv_kernel(moe::FfnArgs a, int tiles
                     if (blk < nblk) {
                         const uint4 *xb = X + (size_t)(m * 4) * nblk + blk;
                         const float Sb = S[m * nblk + blk];
-                        v0 += block_value(p0[b], block_dot(c0[b], xb, nblk), Sb);
-                        if (GATEUP) v1 += block_value(p1[b], block_dot(c1[b], xb, nblk), Sb);
+                        v0 += moe_block_value(p0[i][b], moe_block_dot(c0[i][b], xb, nblk, magic), Sb);
+                        if (GATEUP) v1 += moe_block_value(p1[i][b], moe_block_dot(c1[i][b], xb, nblk, magic), Sb);
                     }
                 }
-                v0 = group_sum<LPR>(v0);
-                if (GATEUP) v1 = group_sum<LPR>(v1);
-                if (c == 0) {
+                v0 = moe_group_sum<LPR>(v0);
+                if (GATEUP) v1 = moe_group_sum<LPR>(v1);
+                if (moe_group_sum_owner<LPR>(c)) {
                     if (GATEUP) {
                         const float hval = v0 / (1.0f + expf(-v0)) * v1;
                         a.h[(size_t)out_rows[m] * a.I + r] = (uint16_t)f32_to_bf16_bits(hval);
@@ -204,9 +195,21 @@ __global__ __launch_bounds__(256) void ffn_gemv_kernel(moe::FfnArgs a, int tiles
     }
 }
 
+// rows requested up front per lane group: about MOE_GEMV_BLOCKS_IN_FLIGHT
+// 16-byte blocks per lane (at least one row)
+#ifndef MOE_GEMV_BLOCKS_IN_FLIGHT
+#define MOE_GEMV_BLOCKS_IN_FLIGHT 4
+#endif
+template <int BPL, bool GATEUP>
+constexpr int rows_in_flight() {
+    return ((GATEUP ? 2 : 1) * BPL >= MOE_GEMV_BLOCKS_IN_FLIGHT) ? 1
+                                                                 : MOE_GEMV_BLOCKS_IN_FLIGHT / ((GATEUP ? 2 : 1) * BPL);
+}
+
 template <int LPR, int BPL, bool GATEUP>
 int launch_one(const moe::FfnArgs &a, int R, int K, int n_groups, int max_m, hipStream_t s) {
-    constexpr int ROWS_PER_WG = 4 * (64 / LPR) * kRowIters;
+    constexpr int RIT = rows_in_flight<BPL, GATEUP>();
+    constexpr int ROWS_PER_WG = 4 * (64 / LPR) * RIT;
     const int tiles = (R + ROWS_PER_WG - 1) / ROWS_PER_WG;
     const int nblk = K / 32;
     const int mt_cap = max_m < kMT ? max_m : kMT;
@@ -214,13 +217,13 @@ int launch_one(const moe::FfnArgs &a, int R, int K, int n_groups, int max_m, hip
     if (lds_bytes > 64 * 1024) {
         static bool raised = false;
         if (!raised) {
-            hipError_t e = hipFuncSetAttribute((const void *)ffn_gemv_kernel<LPR, BPL, GATEUP>,
+            hipError_t e = hipFuncSetAttribute((const void *)ffn_gemv_kernel<LPR, BPL, RIT, GATEUP>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
             if (e != hipSuccess) return moe::fail_hip(e, "hipFuncSetAttribute(ffn_gemv_kernel)");
             raised = true;
         }
     }
-    hipLaunchKernelGGL((ffn_gemv_kernel<LPR, BPL, GATEUP>), dim3((unsigned)n_groups * tiles), dim3(256), lds_bytes, s,
+    hipLaunchKernelGGL((ffn_gemv_kernel<LPR, BPL, RIT, GATEUP>), dim3((unsigned)n_groups * tiles), dim3(256), lds_bytes, s,
                        a, tiles, mt_cap);
     MOE_LAUNCH_CHECK("ffn_gemv_kernel");
     return MOE_OK;

@@ -8,9 +8,9 @@
 // (up to fp64 rounding of the sum itself).
 //
 // Two logit kernels:
-//  * small T (decode, T <= 32): one wavefront per expert streams that expert's
-//    router row once for every token; the last workgroup to finish (atomic
-//    ticket) runs the top-k for all tokens, so decode needs one launch;
+//  * small T (decode, T <= 32): one wavefront per (expert, H slice) streams
+//    that piece of the router row once for every token, then one wavefront per
+//    token sums the slices in order and runs the top-k;
 //  * large T (prefill): 64x64 register-tiled fp64 product through LDS, then a
 //    top-k kernel with one wavefront per token.
 #include "common.h"
@@ -39,26 +39,23 @@ __device__ __forceinline__ int key_index(unsigned long long key) {
     return (int)(0xFFFFFFFFu - (uint32_t)key);
 }
 
-// One wavefront: top-k of one token's E logits, then the renormalised softmax.
-__device__ void wave_topk(const float *lg, int E, int k, int32_t *idx_out, float *w_out) {
+constexpr int kPer = kMaxE / 64;  // logits per lane at most
+
+// One wavefront: top-k over keys held in registers (lane l holds experts
+// l, l+64, ...), then the renormalised softmax over the selected k.
+template <int PER>
+__device__ void wave_topk_keys(unsigned long long (&keys)[PER], int k, int32_t *idx_out, float *w_out) {
     const int lane = threadIdx.x & 63;
-    constexpr int kPer = kMaxE / 64;
-    unsigned long long keys[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        int e = lane + 64 * j;
-        keys[j] = (e < E) ? topk_key(lg[e], e) : 0ull;
-    }
     float my_logit = 0.0f;
     int my_index = 0;
     for (int i = 0; i < k; ++i) {
         unsigned long long best = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) best = keys[j] > best ? keys[j] : best;
+        for (int j = 0; j < PER; ++j) best = keys[j] > best ? keys[j] : best;
         best = wave_max_u64(best);
-        int e = key_index(best);
+        const int e = key_index(best);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j)
+        for (int j = 0; j < PER; ++j)
             if (lane + 64 * j == e) keys[j] = 0ull;  // owner drops the winner
         if (lane == i) {
             my_logit = key_logit(best);
@@ -66,8 +63,8 @@ __device__ void wave_topk(const float *lg, int E, int k, int32_t *idx_out, float
         }
     }
     // softmax over the k selected, max is slot 0
-    float top = __shfl(my_logit, 0, 64);
-    float ex = (lane < k) ? expf(my_logit - top) : 0.0f;
+    const float top = __shfl(my_logit, 0, 64);
+    const float ex = (lane < k) ? expf(my_logit - top) : 0.0f;
     float sum = ex;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
@@ -77,54 +74,91 @@ __device__ void wave_topk(const float *lg, int E, int k, int32_t *idx_out, float
     }
 }
 
+// Top-k of one token's E logits stored in memory.
+__device__ void wave_topk(const float *lg, int E, int k, int32_t *idx_out, float *w_out) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long keys[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = lane + 64 * j;
+        keys[j] = (e < E) ? topk_key(lg[e], e) : 0ull;
+    }
+    wave_topk_keys(keys, k, idx_out, w_out);
+}
+
 // ---------------------------------------------------------------- small T
+// Kernel 1: one wavefront per (expert, 1024-column slice of H): 16 router
+// weights per lane loaded at once, fp64 products, a fixed butterfly, and the
+// slice's partial sum written per token.  Kernel 2: one wavefront per token adds
+// the partials of each logit in slice order plus the bias, rounds once to fp32
+// and runs the top-k.  (A single kernel with a last-workgroup ticket would need
+// an agent-scope fence per workgroup, which costs more than the second launch.)
+constexpr int kSlice = 1024;
+constexpr int kMaxSlices = 16;  // H <= 16384
+constexpr int kSmallT = 32;
+
 template <int TMAX>
-__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t *__restrict__ x, int T, int H,
-                                                           const float *__restrict__ wr,
-                                                           const float *__restrict__ bias, int E, int k,
-                                                           float *__restrict__ logits, unsigned *ticket,
-                                                           int32_t *__restrict__ idx, float *__restrict__ w) {
+__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t *__restrict__ x, int T, int H,
+                                                             const float *__restrict__ wr, int E,
+                                                             double *__restrict__ partial) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave;
-    if (e < E) {
-        double acc[TMAX];
+    const int nslices = (H + kSlice - 1) / kSlice;
+    const int item = blockIdx.x * 4 + wave;  // (expert, slice)
+    const int e = item / nslices, sl = item - e * nslices;
+    if (e >= E) return;
+    const int h0 = sl * kSlice;
+    const float *row = wr + (size_t)e * H;
+    float4 wv[4];
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) acc[t] = 0.0;
-        const float *row = wr + (size_t)e * H;
-        for (int h = lane * 4; h < H; h += 256) {
-            float4 wv = *reinterpret_cast<const float4 *>(row + h);
+    for (int j = 0; j < 4; ++j) {
+        const int h = h0 + lane * 4 + 256 * j;
+        wv[j] = (h < H) ? *reinterpret_cast<const float4 *>(row + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-            for (int t = 0; t < TMAX; ++t) {
-                if (t < T) {
-                    uint2 xv = *reinterpret_cast<const uint2 *>(x + (size_t)t * H + h);
-                    double a = acc[t];
-                    a += (double)bf16_bits_to_f32(xv.x & 0xFFFFu) * (double)wv.x;
-                    a += (double)bf16_bits_to_f32(xv.x >> 16) * (double)wv.y;
-                    a += (double)bf16_bits_to_f32(xv.y & 0xFFFFu) * (double)wv.z;
-                    a += (double)bf16_bits_to_f32(xv.y >> 16) * (double)wv.w;
-                    acc[t] = a;
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < T) {
+            double a = 0.0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = h0 + lane * 4 + 256 * j;
+                if (h < H) {
+                    const uint2 xv = *reinterpret_cast<const uint2 *>(x + (size_t)t * H + h);
+                    a += (double)bf16_bits_to_f32(xv.x & 0xFFFFu) * (double)wv[j].x;
+                    a += (double)bf16_bits_to_f32(xv.x >> 16) * (double)wv[j].y;
+                    a += (double)bf16_bits_to_f32(xv.y & 0xFFFFu) * (double)wv[j].z;
+                    a += (double)bf16_bits_to_f32(xv.y >> 16) * (double)wv[j].w;
                 }
             }
-        }
-        const double b = bias ? (double)bias[e] : 0.0;
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < T) {
-                double s = wave_sum_f64(acc[t]);
-                if (lane == 0) logits[(size_t)t * E + e] = (float)(s + b);
-            }
+            a = wave_sum_f64(a);
+            if (lane == 0) partial[((size_t)t * E + e) * kMaxSlices + sl] = a;
         }
     }
-    // Last workgroup to finish runs the top-k for every token.
-    __shared__ unsigned s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(ticket, 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int t = wave; t < T; t += 4) wave_topk(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
-    if (threadIdx.x == 0) *ticket = 0u;  // ready for the next call
+}
+
+template <int PER>
+__global__ __launch_bounds__(256) void router_finalize_kernel(const double *__restrict__ partial, int T, int H,
+                                                              const float *__restrict__ bias, int E, int k,
+                                                              float *__restrict__ logits, int32_t *__restrict__ idx,
+                                                              float *__restrict__ w) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int nslices = (H + kSlice - 1) / kSlice;
+    unsigned long long keys[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int e = lane + 64 * j;
+        keys[j] = 0ull;
+        if (e < E) {
+            const double *p = partial + ((size_t)t * E + e) * kMaxSlices;
+            double s = 0.0;
+            for (int q = 0; q < nslices; ++q) s += p[q];
+            const float l = (float)(s + (bias ? (double)bias[e] : 0.0));
+            logits[(size_t)t * E + e] = l;  // kept for inspection; the top-k reads registers
+            keys[j] = topk_key(l, e);
+        }
+    }
+    wave_topk_keys(keys, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
 // ---------------------------------------------------------------- large T
@@ -187,13 +221,15 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
     wave_topk(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
-constexpr size_t kTicketBytes = 256;
+constexpr size_t kTicketBytes = 256;  // reserved header before the logits
 
 }  // namespace
 
 extern "C" size_t moe_router_workspace_bytes(int T, int E) {
     if (T < 0 || E <= 0) return 0;
-    return kTicketBytes + moe::align_up((size_t)T * (size_t)E * sizeof(float), 256);
+    const size_t logits = moe::align_up((size_t)T * (size_t)E * sizeof(float), 256);
+    const size_t partial = T <= kSmallT ? (size_t)T * (size_t)E * kMaxSlices * sizeof(double) : 0;
+    return kTicketBytes + logits + partial;
 }
 
 extern "C" int moe_router_topk(const uint16_t *x, int T, int H, const float *w_router, const float *bias, int E,
@@ -208,25 +244,38 @@ extern "C" int moe_router_topk(const uint16_t *x, int T, int H, const float *w_r
     if (workspace_bytes < moe_router_workspace_bytes(T, E))
         return moe::fail(MOE_E_NOMEM, "router: workspace %zu < %zu bytes", workspace_bytes,
                          moe_router_workspace_bytes(T, E));
+    if (H > kSlice * kMaxSlices) return moe::fail(MOE_E_SHAPE, "router: H=%d above %d", H, kSlice * kMaxSlices);
     hipStream_t s = (hipStream_t)stream;
-    unsigned *ticket = (unsigned *)workspace;
     float *logits = (float *)((char *)workspace + kTicketBytes);
+    double *partial =
+        (double *)((char *)workspace + kTicketBytes + moe::align_up((size_t)T * (size_t)E * sizeof(float), 256));
     const dim3 block(256);
-    const dim3 grid_small((E + 3) / 4);
-    if (T <= 32) {
+    if (T <= kSmallT) {
+        const int nslices = (H + kSlice - 1) / kSlice;
+        const dim3 grid_p((E * nslices + 3) / 4);
         if (T == 1)
-            hipLaunchKernelGGL(router_small_kernel<1>, grid_small, block, 0, s, x, T, H, w_router, bias, E, k, logits,
-                               ticket, topk_idx, topk_w);
+            hipLaunchKernelGGL(router_partial_kernel<1>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
         else if (T <= 4)
-            hipLaunchKernelGGL(router_small_kernel<4>, grid_small, block, 0, s, x, T, H, w_router, bias, E, k, logits,
-                               ticket, topk_idx, topk_w);
+            hipLaunchKernelGGL(router_partial_kernel<4>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
         else if (T <= 8)
-            hipLaunchKernelGGL(router_small_kernel<8>, grid_small, block, 0, s, x, T, H, w_router, bias, E, k, logits,
-                               ticket, topk_idx, topk_w);
+            hipLaunchKernelGGL(router_partial_kernel<8>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
         else
-            hipLaunchKernelGGL(router_small_kernel<32>, grid_small, block, 0, s, x, T, H, w_router, bias, E, k,
-                               logits, ticket, topk_idx, topk_w);
-        MOE_LAUNCH_CHECK("router_small_kernel");
+            hipLaunchKernelGGL(router_partial_kernel<32>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
+        MOE_LAUNCH_CHECK("router_partial_kernel");
+        const dim3 grid_f((T + 3) / 4);
+        if (E <= 64)
+            hipLaunchKernelGGL(router_finalize_kernel<1>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
+                               topk_idx, topk_w);
+        else if (E <= 128)
+            hipLaunchKernelGGL(router_finalize_kernel<2>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
+                               topk_idx, topk_w);
+        else if (E <= 256)
+            hipLaunchKernelGGL(router_finalize_kernel<4>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
+                               topk_idx, topk_w);
+        else
+            hipLaunchKernelGGL(router_finalize_kernel<kPer>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
+                               topk_idx, topk_w);
+        MOE_LAUNCH_CHECK("router_finalize_kernel");
         return MOE_OK;
     }
     dim3 grid((T + kTT - 1) / kTT, (E + kTE - 1) / kTE);

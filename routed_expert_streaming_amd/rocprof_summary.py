@@ -1,0 +1,67 @@
+"""Summarise a rocprofv3 result database (rocpd SQLite) as plain text.
+
+  python -m routed_expert_streaming_amd.rocprof_summary RESULTS.db [--counters]
+
+Prints one line per kernel: dispatches, average / min / max duration, share of
+GPU time, grid, workgroup size and VGPRs; with --counters, the average of every
+PMC counter per kernel (as collected by ``rocprofv3 --pmc ...``).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import re
+import sqlite3
+
+
+def short_name(name: str) -> str:
+    s = name.replace("(anonymous namespace)::", "")
+    m = re.match(r"(?:void )?([\w:]+(?:<[^()]*>)?)", s)
+    return (m.group(1) if m else s)[:90]
+
+
+def kernel_stats(db: str):
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x, vgpr_count, lds_size "
+                     "from kernels").fetchall()
+    agg = collections.defaultdict(list)
+    meta = {}
+    for name, dur, gx, gy, gz, wx, vgpr, lds in rows:
+        k = short_name(name)
+        agg[k].append(dur)
+        meta[k] = (gx * gy * gz, wx, vgpr, lds)
+    total = sum(sum(v) for v in agg.values()) or 1
+    out = []
+    for k, durs in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        g, w, v, l = meta[k]
+        out.append((k, len(durs), sum(durs) / len(durs) / 1e3, min(durs) / 1e3, max(durs) / 1e3,
+                    100.0 * sum(durs) / total, g, w, v, l))
+    return out
+
+
+def counter_stats(db: str):
+    c = sqlite3.connect(db)
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for name, ctr, val in c.execute("select kernel_name, counter_name, value from counters_collection"):
+        agg[short_name(name)][ctr].append(val)
+    return {k: {ctr: sum(v) / len(v) for ctr, v in d.items()} for k, d in agg.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("db")
+    ap.add_argument("--counters", action="store_true")
+    args = ap.parse_args()
+    if args.counters:
+        for k, d in sorted(counter_stats(args.db).items()):
+            print(f"{k}")
+            print("    " + "  ".join(f"{ctr}={v:.6g}" for ctr, v in sorted(d.items())))
+        return
+    print(f"{'kernel':90s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s} "
+          f"{'threads':>8s} {'wg':>4s} {'vgpr':>4s} {'lds':>6s}")
+    for k, n, avg, mn, mx, pct, g, w, v, l in kernel_stats(args.db):
+        print(f"{k:90s} {n:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f} {pct:6.2f} {g:8d} {w:4d} {v:4d} {l:6d}")
+
+
+if __name__ == "__main__":
+    main()

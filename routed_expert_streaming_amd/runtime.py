@@ -182,6 +182,12 @@ class MoEStack:
                          self.shared[l] if (self.has_shared and shared) else None, mask, self.y, self.ffn_ws,
                          self.ffn_ws_bytes, self.path, self.stream)
 
+    def ffn_combine(self, x: torch.Tensor, l: int, out: torch.Tensor):
+        """Gate/up, down and the weighted combine of layer l (every needed expert resident)."""
+        L.moe_expert_ffn_combine(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.w[l], self.k,
+                                 self.table[l], self.shared[l] if self.has_shared else None, out[l], self.ffn_ws,
+                                 self.ffn_ws_bytes, self.path, self.stream)
+
     def combine(self, l: int, out: torch.Tensor):
         L.moe_combine(self.y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l], self.stream)
 
@@ -213,8 +219,7 @@ class MoEStack:
             self.route(x, l)
         if not self.streaming:
             for l in range(self.L):
-                self.ffn(x, l)
-                self.combine(l, out)
+                self.ffn_combine(x, l, out)
             return st
         # one small D2H per step, then the host plans every layer
         idx_host = np.frombuffer(self._idx_host.array, dtype=np.int32, count=self.L * self.T * self.k)
@@ -232,10 +237,15 @@ class MoEStack:
                     mh[l, wv, experts] = 1
             self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
         for l, waves in enumerate(plans):
+            if len(waves) == 1:
+                st.copies += L.moe_cache_prefetch(self.cache, l, waves[0], self.stream)
+                self.ffn_combine(x, l, out)
+                L.moe_cache_release(self.cache, l, self.stream)
+                st.waves += 1
+                continue
             for wv, experts in enumerate(waves):
                 st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
-                mask = self.masks[l, wv] if len(waves) > 1 else None
-                self.ffn(x, l, mask=mask, shared=(wv == 0))
+                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0))
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
             self.combine(l, out)

@@ -123,11 +123,16 @@ def test_router_ties_and_degenerate_cases():
     assert (w == 1.0).all()
 
 
-def test_router_workspace_ticket_is_left_zero():
+def test_router_workspace_contents_do_not_matter():
     x = synth.x_bf16(3, 0, 0, 2, 256)
     Wr = synth.router_w(3, 0, 16, 256)
-    _, _, _, ws = run_router(x, Wr, None, 2)
-    assert int(ws[:256].sum().item()) == 0
+    idx, w, _, ws = run_router(x, Wr, None, 2)
+    ws.fill_(0xFF)
+    L.moe_router_topk(bf16_dev(x), 2, 256, torch.from_numpy(Wr).cuda(), None, 16, 2,
+                      idx2 := torch.empty((2, 2), dtype=torch.int32, device="cuda"),
+                      w2 := torch.empty((2, 2), dtype=torch.float32, device="cuda"), ws, ws.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), idx) and np.array_equal(w2.cpu().numpy(), w)
 
 
 # ---------------------------------------------------------------------------- dequant
@@ -187,6 +192,12 @@ class Layer:
         L.moe_expert_ffn(x, T, H, I, E, idx, k, self.table, self.shared_dev, mask, y, fws, fb, path)
         out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         L.moe_combine(y, w, T, k, H, self.shared is not None, out)
+        self.fused = None
+        if mask is None:
+            fused = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+            L.moe_expert_ffn_combine(x, T, H, I, E, idx, w, k, self.table, self.shared_dev, fused, fws, fb, path)
+            torch.cuda.synchronize()
+            self.fused = fused.view(torch.int16).cpu().numpy().view(np.uint16)
         torch.cuda.synchronize()
         return idx.cpu().numpy(), y.cpu().numpy(), out.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -216,6 +227,8 @@ def test_layer_parity_all_paths(name, T, H, I, E, k, shared, bias, rows):
         assert np.array_equal(idx, ref["idx"])
         sel = slice(None) if rows is None else rows
         ratio = check_close(out[sel], ref["out64"][sel], f"{name} path {path}")
+        # the one-call FFN + combine gives exactly the two-call result
+        assert np.array_equal(lay.fused, out)
         results[path] = (y, out, ratio)
     # both kernel groupings compute each (token, expert) pair with the same arithmetic
     assert np.array_equal(results[paths[0]][0], results[paths[1]][0])
