@@ -31,6 +31,14 @@ int decode_gate_up(const FfnArgs &a, hipStream_t s);
 // out == nullptr: write y; otherwise apply the weighted combine into out [T, H].
 int decode_down(const FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s);
 
+// MFMA grouped GEMM (prefill): needs the expert grouping and H, I multiples of 128.
+bool mfma_supported(const FfnArgs &a);
+int mfma_gate_up(const FfnArgs &a, hipStream_t s);
+int mfma_down(const FfnArgs &a, hipStream_t s);
+
+// Tokens from which the automatic choice uses the MFMA kernels.
+constexpr int kMfmaMinTokens = 128;
+
 // Counting sort of pairs by expert (see moe_permute).
 int permute_launch(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
                    int32_t *pair_of_row, hipStream_t s);

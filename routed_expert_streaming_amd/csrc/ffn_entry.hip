@@ -166,7 +166,6 @@ int validate_ffn(const void *act, int T, int H, int I, int E, const int32_t *top
     if (H > 16384 || I > 16384) return moe::fail(MOE_E_SHAPE, "%s: H=%d I=%d above 16384", who, H, I);
     if (E < 1 || E > kPermMaxE || k < 1 || k > E) return moe::fail(MOE_E_SHAPE, "%s: E=%d k=%d", who, E, k);
     if (path < MOE_FFN_AUTO || path > MOE_FFN_MFMA) return moe::fail(MOE_E_ARG, "%s: path=%d", who, path);
-    if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_STATE, "%s: the MFMA path is not built in this library", who);
     return MOE_OK;
 }
 
@@ -178,8 +177,9 @@ int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, 
     const bool have_perm = count && offset && pair_of_row;
     if ((count || offset || pair_of_row) && !have_perm)
         return moe::fail(MOE_E_ARG, "%s: count, offset and pair_of_row go together", who);
-    if (path == MOE_FFN_GROUPED && !have_perm) return moe::fail(MOE_E_ARG, "%s: grouped path needs a permutation", who);
-    const bool grouped = (path == MOE_FFN_GROUPED) || (path == MOE_FFN_AUTO && have_perm);
+    if ((path == MOE_FFN_GROUPED || path == MOE_FFN_MFMA) && !have_perm)
+        return moe::fail(MOE_E_ARG, "%s: grouped and MFMA paths need a permutation", who);
+    const bool grouped = (path == MOE_FFN_GROUPED) || (path == MOE_FFN_MFMA) || (path == MOE_FFN_AUTO && have_perm);
     a = moe::FfnArgs{};
     a.x = x;
     a.h = h;
@@ -202,6 +202,18 @@ int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, 
     return MOE_OK;
 }
 
+// Kernel family for a grouped call: MFMA when forced, or automatically for many tokens.
+bool use_mfma(const moe::FfnArgs &a, int path) {
+    if (!moe::mfma_supported(a)) return false;
+    return path == MOE_FFN_MFMA || (path == MOE_FFN_AUTO && a.T >= moe::kMfmaMinTokens);
+}
+
+// Automatic path of the one-call entry points.
+int auto_path(int T, int k) {
+    if ((long long)T * k <= 64) return MOE_FFN_PAIRS;
+    return T >= moe::kMfmaMinTokens ? MOE_FFN_MFMA : MOE_FFN_GROUPED;
+}
+
 }  // namespace
 
 extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
@@ -217,6 +229,8 @@ extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E,
     rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
                    expert_mask, path, &max_m, "expert_gate_up");
     if (rc != MOE_OK) return rc;
+    if (use_mfma(a, path)) return moe::mfma_gate_up(a, (hipStream_t)stream);
+    if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_gate_up: MFMA path needs H, I multiples of 128");
     if (moe::decode_supported(a)) return moe::decode_gate_up(a, (hipStream_t)stream);
     return moe::ffn_gemv_gate_up(a, max_m, (hipStream_t)stream);
 }
@@ -234,6 +248,8 @@ extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, co
     rc = make_args(a, nullptr, const_cast<uint16_t *>(h), y, T, H, I, E, topk_idx, k, count, offset, pair_of_row,
                    expert_table, shared_slab, expert_mask, path, &max_m, "expert_down");
     if (rc != MOE_OK) return rc;
+    if (use_mfma(a, path)) return moe::mfma_down(a, (hipStream_t)stream);
+    if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_down: MFMA path needs H, I multiples of 128");
     if (moe::decode_supported(a)) return moe::decode_down(a, nullptr, nullptr, (hipStream_t)stream);
     return moe::ffn_gemv_down(a, max_m, (hipStream_t)stream);
 }
@@ -250,14 +266,17 @@ extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, con
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "expert_ffn: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
-    if (path == MOE_FFN_AUTO) path = ((long long)T * k <= 64) ? MOE_FFN_PAIRS : MOE_FFN_GROUPED;
-    if (path == MOE_FFN_GROUPED && (long long)T * k > kPermMaxPairs)
-        return moe::fail(MOE_E_SHAPE, "expert_ffn: grouped path needs T*k <= %d", kPermMaxPairs);
+    if (path == MOE_FFN_AUTO) {
+        path = auto_path(T, k);
+        if (path == MOE_FFN_MFMA && (H % 128 || I % 128)) path = MOE_FFN_GROUPED;
+    }
+    if (path != MOE_FFN_PAIRS && (long long)T * k > kPermMaxPairs)
+        return moe::fail(MOE_E_SHAPE, "expert_ffn: grouped paths need T*k <= %d", kPermMaxPairs);
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     uint16_t *h = (uint16_t *)(ws + Ly.h);
     int32_t *count = nullptr, *offset = nullptr, *pairs = nullptr;
-    if (path == MOE_FFN_GROUPED) {
+    if (path == MOE_FFN_GROUPED || path == MOE_FFN_MFMA) {
         count = (int32_t *)(ws + Ly.count);
         offset = (int32_t *)(ws + Ly.offset);
         pairs = (int32_t *)(ws + Ly.pairs);
@@ -284,7 +303,7 @@ extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, in
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "expert_ffn_combine: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
-    if (path == MOE_FFN_AUTO) path = ((long long)T * k <= 64) ? MOE_FFN_PAIRS : MOE_FFN_GROUPED;
+    if (path == MOE_FFN_AUTO) path = auto_path(T, k);
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     uint16_t *h = (uint16_t *)(ws + Ly.h);

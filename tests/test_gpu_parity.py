@@ -222,7 +222,8 @@ def test_layer_parity_all_paths(name, T, H, I, E, k, shared, bias, rows):
     ref = lay.oracle(rows)
     results = {}
     paths = [L.MOE_FFN_PAIRS, L.MOE_FFN_GROUPED]
-    for path in paths:
+    mfma_ok = H % 128 == 0 and I % 128 == 0
+    for path in paths + ([L.MOE_FFN_MFMA] if mfma_ok else []):
         idx, y, out = lay.run(path)
         assert np.array_equal(idx, ref["idx"])
         sel = slice(None) if rows is None else rows
@@ -230,10 +231,41 @@ def test_layer_parity_all_paths(name, T, H, I, E, k, shared, bias, rows):
         # the one-call FFN + combine gives exactly the two-call result
         assert np.array_equal(lay.fused, out)
         results[path] = (y, out, ratio)
-    # both kernel groupings compute each (token, expert) pair with the same arithmetic
+    if not mfma_ok:
+        with pytest.raises(L.MoEError) as ei:
+            lay.run(L.MOE_FFN_MFMA)
+        assert ei.value.status == L.MOE_E_SHAPE
+    else:  # MFMA run twice gives the same bits
+        assert np.array_equal(lay.run(L.MOE_FFN_MFMA)[2], results[L.MOE_FFN_MFMA][1])
+    # both GEMV kernel groupings compute each (token, expert) pair with the same arithmetic
     assert np.array_equal(results[paths[0]][0], results[paths[1]][0])
     assert np.array_equal(results[paths[0]][1], results[paths[1]][1])
     print(f"{name}: max err / max|ref| = {results[paths[0]][2]:.2e}")
+
+
+PREFILL_CASES = [
+    # name, T, H, I, E, k, shared, hot expert (gets a large bias), oracle rows
+    ("prefill2048", 2048, 6144, 2048, 256, 8, False, None, [0, 1, 777, 2047]),
+    ("hot_expert", 300, 512, 256, 16, 4, True, 3, [0, 150, 299]),
+    ("tiny_prefill", 129, 256, 128, 16, 2, False, None, None),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,shared,hot,rows", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_mfma_parity(name, T, H, I, E, k, shared, hot, rows):
+    lay = Layer(T, H, I, E, k, shared, None, seed=zlib.crc32(name.encode()) % 1000 + 5)
+    if hot is not None:
+        lay.bias = np.zeros(E, np.float32)
+        lay.bias[hot] = 10.0  # every token routes to this expert: more than one 128-token chunk
+    ref = lay.oracle(rows)
+    idx, y, out = lay.run(L.MOE_FFN_AUTO)  # T >= 128 selects the MFMA kernels
+    assert np.array_equal(idx, ref["idx"])
+    sel = slice(None) if rows is None else rows
+    ratio = check_close(out[sel], ref["out64"][sel], f"{name} mfma")
+    assert np.array_equal(lay.fused, out)
+    _, _, out_g = lay.run(L.MOE_FFN_GROUPED)
+    check_close(out_g[sel], ref["out64"][sel], f"{name} grouped")
+    print(f"{name}: mfma max err / max|ref| = {ratio:.2e}")
 
 
 def test_mask_computes_only_admitted_experts():
