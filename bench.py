@@ -44,7 +44,83 @@ def parse():
     ap.add_argument("--kernel-iters", type=int, default=50, help="iterations of the per-kernel event timing")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streamed-decode (PCIe) leg")
+    ap.add_argument("--stream-workload", default="decode1_stream")
+    ap.add_argument("--stream-steps", type=int, default=256)
+    ap.add_argument("--stream-warmup", type=int, default=64)
     return ap.parse_args()
+
+
+def link_peak(torch, slab_bytes: int):
+    """Pinned host -> HBM copy rate on a side stream: best of 1 GiB copies, and
+    back-to-back slab-sized copies (the cache's copy pattern)."""
+    nbytes = 1 << 30
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    host.fill_(1)
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    best = 0.0
+    with torch.cuda.stream(side):
+        for _ in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(side)
+            dev.copy_(host, non_blocking=True)
+            b.record(side)
+            b.synchronize()
+            best = max(best, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+        n = nbytes // slab_bytes
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(side)
+        for i in range(n):
+            dev[i * slab_bytes:(i + 1) * slab_bytes].copy_(host[i * slab_bytes:(i + 1) * slab_bytes],
+                                                           non_blocking=True)
+        b.record(side)
+        b.synchronize()
+        slabs = n * slab_bytes / (a.elapsed_time(b) * 1e-3) / 1e9
+    del host, dev
+    return best, slabs
+
+
+def streaming_leg(torch, args, resident_ms_per_step: float):
+    """The streamed decode workload: expert cache capped per layer, misses copied
+    from pinned host RAM over PCIe on a copy stream while earlier layers compute."""
+    import synth
+    from routed_expert_streaming_amd.runtime import MoEStack
+
+    cfg = synth.get(args.stream_workload)
+    log(f"streaming leg: {cfg.description}")
+    st = MoEStack(cfg)
+    peak, slab_rate = link_peak(torch, st.slab)
+    log(f"pinned H2D: {peak:.1f} GB/s (1 GiB copies), {slab_rate:.1f} GB/s (back-to-back {st.slab} B slabs)")
+    n_in = 32
+    xs = [st.make_inputs(s) for s in range(n_in)]
+    out = st.new_output()
+    for s in range(args.stream_warmup):  # cold start happens here
+        st.forward(xs[s % n_in], out)
+    torch.cuda.synchronize()
+    h0, m0, b0 = st.stats()
+    t0 = time.perf_counter()
+    for s in range(args.stream_steps):
+        st.forward(xs[s % n_in], out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    h1, m1, b1 = st.stats()
+    st.close()
+    hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
+    ms_step = wall / args.stream_steps * 1e3
+    copy_ms = nbytes / args.stream_steps / (slab_rate * 1e9) * 1e3  # copy-stream busy time at the slab copy rate
+    h2d = nbytes / wall / 1e9
+    res = {"workload": cfg.name, "layers": cfg.layers, "cache_slots_per_layer": st.C,
+           "tokens_per_s": round(args.stream_steps * cfg.tokens / wall, 2), "ms_per_step": round(ms_step, 3),
+           "hit_rate": round(hits / max(hits + misses, 1), 4), "h2d_bytes_per_step": nbytes // args.stream_steps,
+           "h2d_GBps": round(h2d, 2), "link_peak_GBps": round(peak, 2), "slab_copy_GBps": round(slab_rate, 2),
+           "h2d_frac_of_link_peak": round(h2d / peak, 4),
+           "copy_busy_ms_per_step": round(copy_ms, 3), "resident_ms_per_step": round(resident_ms_per_step, 3),
+           "wall_over_copy_busy": round(ms_step / copy_ms, 4) if copy_ms > 0 else None,
+           "exposed_ms_per_step": round(ms_step - copy_ms, 3),
+           "steps": args.stream_steps, "warmup": args.stream_warmup}
+    log(f"streaming: {res}")
+    return res
 
 
 def gate_up_bytes(stack) -> int:
@@ -214,6 +290,10 @@ def main():
                                             f"fp64 plain-C oracle, {cpu_s:.1f} s"}
         log(f"cpu baseline: {result['cpu_baseline']}")
     stack.close()
+    del stack, graphs, xs, outs
+    torch.cuda.empty_cache()
+    if not args.no_stream:
+        result["streaming"] = streaming_leg(torch, args, ms_per_step)
     print(json.dumps(result), flush=True)
 
 
