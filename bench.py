@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--stream-workload", default="decode1_stream")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="also run 4 plain 256 MiB device copies (reference for HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -121,6 +123,26 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
            "steps": args.stream_steps, "warmup": args.stream_warmup}
     log(f"streaming: {res}")
     return res
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch measured with FETCH_SIZE/WRITE_SIZE (scaled by a plain
+    copy of known size), from the committed profile summary; None if the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode1_gate_up_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json:"):
+            info = json.loads(line.split(":", 1)[1])
+            if info.get("kernel") != kernel:
+                return None
+            h = hashlib.sha1()
+            for src in info["sources"]:
+                h.update(open(os.path.join(ROOT, src), "rb").read())
+            return info["traffic_bytes_per_launch"] if h.hexdigest() == info["sources_sha1"] else None
+    return None
 
 
 def gate_up_bytes(stack) -> int:
@@ -214,6 +236,15 @@ def main():
     log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s (events {gpu_ms:.2f} ms, "
         f"wall {wall * 1e3:.2f} ms)")
 
+    if args.traffic_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(3)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---------------- dominant kernel, timed live with events on its stream
     h = torch.empty((cfg.tokens * cfg.top_k + cfg.tokens * cfg.shared, cfg.inter), dtype=torch.bfloat16,
                     device="cuda")
@@ -261,7 +292,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "decode_gate_up_kernel (dequant + gate/up + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("decode_gate_up_kernel"),
                      "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},
         "ffn": {"bytes_per_step": ffn_bytes_step, "kernel_us_per_step": round(ffn_us_step, 2),
                 "achieved_GBps": round(ffn_bytes_step / (ffn_us_step * 1e-6) / 1e9, 1),
