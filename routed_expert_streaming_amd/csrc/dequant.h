@@ -15,17 +15,18 @@
 
 // The bf16 exponent pattern 0x4300 in both halves, held in a VGPR: gfx9 VOP3
 // instructions read at most one scalar/constant operand, so keeping this one in
-// a vector register lets (w & mask) | magic compile to a single v_and_or_b32.
+// a vector register (the mask goes in an SGPR) lets the extraction below compile
+// to a single bitfield insert per word.
 __device__ __forceinline__ uint32_t moe_magic_vgpr() {
     uint32_t m;
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
     return m;
 }
 
+// (a & mask) | magic, written as a bitfield select (magic has no bits inside the
+// mask) so that it becomes one v_bfi_b32 that the compiler can schedule freely.
 __device__ __forceinline__ uint32_t moe_and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-    return r;
+    return (a & mask) | (magic & ~mask);
 }
 
 // sum over one block of (128 + q) * x; two interleaved accumulators shorten the

@@ -29,13 +29,31 @@ namespace {
 #define MOE_DECODE_D_GU 5  // gate/up units in flight per lane group (H = 4096)
 #endif
 #ifndef MOE_DECODE_D_DN
-#define MOE_DECODE_D_DN 8  // down units in flight per lane group (I = 1536)
+#define MOE_DECODE_D_DN 4  // down units in flight per lane group (I = 1536)
 #endif
 
 constexpr int kMaxTok = 4;      // tokens per launch on this path
 constexpr int kMaxGroups = 64;  // T*k + 1
 
-
+// Permute one 32-column activation block (4 x 16 B of bf16, natural order) into
+// the dot2 pair order of dequant.h and return its fp32 sum (in index order).
+__device__ __forceinline__ float block_pairs(const uint4 (&d)[4], uint4 (&X)[4]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        X[j].x = (d[j].x & 0xFFFFu) | (d[j].z << 16);
+        X[j].y = (d[j].x >> 16) | (d[j].z & 0xFFFF0000u);
+        X[j].z = (d[j].y & 0xFFFFu) | (d[j].w << 16);
+        X[j].w = (d[j].y >> 16) | (d[j].w & 0xFFFF0000u);
+        const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s += bf16_bits_to_f32(v[q] & 0xFFFFu);
+            s += bf16_bits_to_f32(v[q] >> 16);
+        }
+    }
+    return s;
+}
 
 // Stage n activation rows (K columns, bf16) into LDS in dot2 pair order plus
 // the fp32 block sums (same layout as the general kernels).
@@ -44,26 +62,12 @@ __device__ __forceinline__ void stage_all(const uint16_t *__restrict__ act, int 
     for (int id = threadIdx.x; id < n * nblk; id += blockDim.x) {
         const int m = id / nblk, b = id - m * nblk;
         const uint4 *src = reinterpret_cast<const uint4 *>(act + (size_t)m * K + 32 * b);
-        uint4 d[4];
+        uint4 d[4], p[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) d[j] = src[j];  // the whole block in one round trip
-        float s = 0.0f;
+        S[m * nblk + b] = block_pairs(d, p);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint4 p;
-            p.x = (d[j].x & 0xFFFFu) | (d[j].z << 16);
-            p.y = (d[j].x >> 16) | (d[j].z & 0xFFFF0000u);
-            p.z = (d[j].y & 0xFFFFu) | (d[j].w << 16);
-            p.w = (d[j].y >> 16) | (d[j].w & 0xFFFF0000u);
-            X[(m * 4 + j) * nblk + b] = p;
-            const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                s += bf16_bits_to_f32(v[q] & 0xFFFFu);
-                s += bf16_bits_to_f32(v[q] >> 16);
-            }
-        }
-        S[m * nblk + b] = s;
+        for (int j = 0; j < 4; ++j) X[(m * 4 + j) * nblk + b] = p[j];
     }
 }
 
@@ -80,19 +84,29 @@ __device__ __forceinline__ void load_group_slabs(const moe::FfnArgs &a, const ui
     }
 }
 
+// The weight loads of the register ring are issued unconditionally (tail units
+// and masked groups re-read a valid row and skip the compute), so the compiler
+// can count outstanding loads exactly and wait only for the oldest unit instead
+// of draining the whole ring.
 // ---------------------------------------------------------------- gate/up
-template <int LPR, int BPL, int D>
+template <int LPR, int BPL, int D, bool XREG>
 __global__ __launch_bounds__(256) void decode_gate_up_kernel(moe::FfnArgs a, int units_per_sg) {
     constexpr int RPW = 64 / LPR;
     const int H = a.H, I = a.I, T = a.T, nblk = H >> 5;
     const int G = a.n_routed_groups + (a.shared ? 1 : 0);
     const long long Q = (long long)G * I;
     extern __shared__ uint4 lds[];
-    uint4 *X = lds;
-    float *S = reinterpret_cast<float *>(lds + (size_t)T * 4 * nblk);
+    uint4 *Xs = lds;
+    float *Ss = reinterpret_cast<float *>(lds + (size_t)T * 4 * nblk);
     __shared__ const uint8_t *gslab[kMaxGroups];
+    __shared__ const uint8_t *any_slab;
     load_group_slabs(a, gslab, G);
     __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint8_t *p = nullptr;
+        for (int g = 0; g < G && !p; ++g) p = gslab[g];
+        any_slab = p;
+    }
 
     const uint32_t magic = moe_magic_vgpr();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -103,23 +117,33 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(moe::FfnArgs a, int
     const size_t m13 = (size_t)I * H * 5 / 8;
     const size_t cbytes = (size_t)I * H / 2;
 
+    // one token: the lane's activation blocks go straight to registers
+    uint4 xd[XREG ? BPL : 1][4];
+    if (XREG) {
+#pragma unroll
+        for (int b = 0; b < BPL; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xd[b][j] = load_global_u4(a.x + 32 * (c + b * LPR) + 8 * j);
+    }
+    __syncthreads();  // any_slab
+    const uint8_t *fallback = any_slab;
+    if (!fallback) return;  // every group masked off
+
     uint4 c0[D][BPL], c1[D][BPL];
     uint32_t p0[D][BPL], p1[D][BPL];
     // issue cursor (unit index, group, row) walks ahead of the compute cursor
     int ui = 0, gi = (int)(q0 / I), ri = (int)(q0 - (long long)gi * I);
     auto issue = [&](int j) {
-        if (ui < n) {
-            const uint8_t *slab = gslab[gi];
-            if (slab) {
+        const uint8_t *slab = (ui < n) ? gslab[gi] : nullptr;
+        const size_t row = slab ? (size_t)ri : 0;
+        if (!slab) slab = fallback;
 #pragma unroll
-                for (int b = 0; b < BPL; ++b) {
-                    const int blk = c + b * LPR;
-                    c0[j][b] = load_stream_u4(slab + (size_t)ri * (H / 2) + 16 * blk);
-                    p0[j][b] = load_stream_u32(slab + cbytes + ((size_t)ri * nblk + blk) * 4);
-                    c1[j][b] = load_stream_u4(slab + m13 + (size_t)ri * (H / 2) + 16 * blk);
-                    p1[j][b] = load_stream_u32(slab + m13 + cbytes + ((size_t)ri * nblk + blk) * 4);
-                }
-            }
+        for (int b = 0; b < BPL; ++b) {
+            const int blk = c + b * LPR;
+            c0[j][b] = load_stream_u4(slab + row * (H / 2) + 16 * blk);
+            p0[j][b] = load_stream_u32(slab + cbytes + (row * nblk + blk) * 4);
+            c1[j][b] = load_stream_u4(slab + m13 + row * (H / 2) + 16 * blk);
+            p1[j][b] = load_stream_u32(slab + m13 + cbytes + (row * nblk + blk) * 4);
         }
         ++ui;
         if (++ri == I) {
@@ -129,8 +153,16 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(moe::FfnArgs a, int
     };
 #pragma unroll
     for (int j = 0; j < D; ++j) issue(j);
-    stage_all(a.x, H, T, X, S);
-    __syncthreads();
+
+    uint4 Xr[XREG ? BPL : 1][4];
+    float Sr[XREG ? BPL : 1];
+    if (XREG) {
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) Sr[b] = block_pairs(xd[b], Xr[b]);
+    } else {
+        stage_all(a.x, H, T, Xs, Ss);
+        __syncthreads();
+    }
 
     int g = (int)(q0 / I), r = (int)(q0 - (long long)g * I);  // compute cursor
     for (int base = 0; base < n; base += D) {
@@ -145,10 +177,15 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(moe::FfnArgs a, int
 #pragma unroll
                     for (int b = 0; b < BPL; ++b) {
                         const int blk = c + b * LPR;
-                        const uint4 *xb = X + (size_t)(t * 4) * nblk + blk;
-                        const float Sb = S[t * nblk + blk];
-                        v0 += moe_block_value(p0[j][b], moe_block_dot(c0[j][b], xb, nblk, magic), Sb);
-                        v1 += moe_block_value(p1[j][b], moe_block_dot(c1[j][b], xb, nblk, magic), Sb);
+                        if (XREG) {
+                            v0 += moe_block_value(p0[j][b], moe_block_dot(c0[j][b], Xr[b], 1, magic), Sr[b]);
+                            v1 += moe_block_value(p1[j][b], moe_block_dot(c1[j][b], Xr[b], 1, magic), Sr[b]);
+                        } else {
+                            const uint4 *xb = Xs + (size_t)(t * 4) * nblk + blk;
+                            const float Sb = Ss[t * nblk + blk];
+                            v0 += moe_block_value(p0[j][b], moe_block_dot(c0[j][b], xb, nblk, magic), Sb);
+                            v1 += moe_block_value(p1[j][b], moe_block_dot(c1[j][b], xb, nblk, magic), Sb);
+                        }
                     }
                     v0 = moe_group_sum<LPR>(v0);
                     v1 = moe_group_sum<LPR>(v1);
@@ -167,11 +204,132 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(moe::FfnArgs a, int
     }
 }
 
+// ---------------------------------------------------------------- gate/up, one token
+// A 64-bit pointer that is the same in every lane, moved to scalar registers so
+// that address arithmetic on it runs on the scalar unit.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(((uint64_t)hi << 32) | lo);
+}
+
+// One token, H = 64*32*BPL: a whole wave covers one weight row (lane l owns
+// blocks l, l+64, ...), so the unit cursor is wave-uniform and every weight load
+// is a scalar row base plus the lane's fixed offset.  Units (group, row) are
+// dealt to the waves round-robin (wave w takes units w, w+W, w+2W, ...), so the
+// loads in flight across the chip at any moment cover one contiguous window of
+// each weight matrix, which keeps HBM pages open, instead of one scattered run
+// per wave.  The token's activation blocks stay in registers for the whole
+// launch; there is no LDS staging.
+template <int BPL, int D>
+__global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, int n_waves) {
+    const int H = a.H, I = a.I, nblk = H >> 5;
+    const int G = a.n_routed_groups + (a.shared ? 1 : 0);
+    const int Q = G * I;
+    __shared__ const uint8_t *gslab[kMaxGroups];
+    load_group_slabs(a, gslab, G);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint4 xd[BPL][4];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xd[b][j] = load_global_u4(a.x + 32 * (lane + 64 * b) + 8 * j);
+    __syncthreads();
+
+    // tail units and masked groups re-read row 0 of the first present slab
+    const uint8_t *mine = lane < G ? gslab[lane] : nullptr;
+    const uint64_t present = __ballot(mine != nullptr);
+    if (present == 0) return;  // every group masked off
+    const int first = __ffsll((long long)present) - 1;
+    const uint64_t fv = (uint64_t)mine;
+    const uint8_t *fallback = (const uint8_t *)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(fv >> 32), first) << 32) |
+                                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)fv, first));
+
+    const uint32_t magic = moe_magic_vgpr();
+    const int w0 = blockIdx.x * 4 + wave;
+    const int n = w0 < Q ? (Q - w0 + n_waves - 1) / n_waves : 0;  // units of this wave
+    const int dg = n_waves / I, dr = n_waves - dg * I;              // cursor step in (group, row)
+    const size_t m13 = (size_t)I * H * 5 / 8;
+    const size_t cbytes = (size_t)I * H / 2;
+    const uint32_t code_off = 16u * lane, rec_off = 4u * lane;
+
+    uint4 c0[D][BPL], c1[D][BPL];
+    uint32_t p0[D][BPL], p1[D][BPL];
+    int ui = 0, gi = w0 / I, ri = w0 - gi * I;  // issue cursor, D units ahead
+    auto issue = [&](int j) {
+        const uint8_t *slab = fallback;
+        int row = 0;
+        if (ui < n) {
+            const uint8_t *p = uniform_ptr(gslab[gi]);
+            if (p) {
+                slab = p;
+                row = ri;
+            }
+        }
+        const uint8_t *w1 = slab + (size_t)row * (H / 2);
+        const uint8_t *r1 = slab + cbytes + (size_t)row * nblk * 4;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            c0[j][b] = load_stream_u4(w1 + (code_off + 1024u * b));
+            p0[j][b] = load_stream_u32(r1 + (rec_off + 256u * b));
+            c1[j][b] = load_stream_u4(w1 + m13 + (code_off + 1024u * b));
+            p1[j][b] = load_stream_u32(r1 + m13 + (rec_off + 256u * b));
+        }
+        ++ui;
+        gi += dg;
+        ri += dr;
+        if (ri >= I) {
+            ri -= I;
+            ++gi;
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) issue(j);
+
+    uint4 X[BPL][4];
+    float S[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) S[b] = block_pairs(xd[b], X[b]);
+
+    int g = w0 / I, r = w0 - g * I;  // compute cursor
+    for (int base = 0; base < n; base += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            if (base + j >= n) break;
+            if (uniform_ptr(gslab[g])) {
+                float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    v0 += moe_block_value(p0[j][b], moe_block_dot(c0[j][b], X[b], 1, magic), S[b]);
+                    v1 += moe_block_value(p1[j][b], moe_block_dot(c1[j][b], X[b], 1, magic), S[b]);
+                }
+                v0 = moe_group_sum<64>(v0);
+                v1 = moe_group_sum<64>(v1);
+                if (lane == 63) {
+                    const int row = g < a.n_routed_groups ? g : a.k;  // pair g, or the shared row
+                    a.h[(size_t)row * I + r] = (uint16_t)f32_to_bf16_bits(v0 / (1.0f + expf(-v0)) * v1);
+                }
+            }
+            issue(j);  // slot j is free again: request the unit D ahead
+            g += dg;
+            r += dr;
+            if (r >= I) {
+                r -= I;
+                ++g;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- down (+ combine)
 template <int LPR, int BPL, int D, bool COMBINE>
 __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const float *__restrict__ topk_w,
-                                                          uint16_t *__restrict__ out, int rows_per_sg) {
+                                                          uint16_t *__restrict__ out, int n_sg) {
     constexpr int RPW = 64 / LPR;
+    constexpr int kStagePerThread = 2;  // (row, block) items of h requested ahead of the ring
     const int H = a.H, I = a.I, T = a.T, k = a.k, nblk = I >> 5;
     const int G = a.n_routed_groups + (a.shared ? 1 : 0);
     const int P = T * k + (a.shared ? T : 0);
@@ -180,46 +338,90 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
     float *S = reinterpret_cast<float *>(lds + (size_t)P * 4 * nblk);
     __shared__ const uint8_t *gslab[kMaxGroups];
     __shared__ float wts[kMaxGroups];
+    __shared__ const uint8_t *any_slab;
     load_group_slabs(a, gslab, G);
     if (COMBINE)
         for (int i = threadIdx.x; i < T * k; i += blockDim.x) wts[i] = topk_w[i];
     __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint8_t *p = nullptr;
+        for (int g = 0; g < G && !p; ++g) p = gslab[g];
+        any_slab = p;
+    }
 
     const uint32_t magic = moe_magic_vgpr();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane / LPR, c = lane % LPR;
     const long long sg = ((long long)blockIdx.x * 4 + wave) * RPW + sub;
-    const int r_first = (int)min<long long>(sg * rows_per_sg, H);
-    const int r_last = (int)min<long long>((long long)r_first + rows_per_sg, H);
-    const int n_units = (r_last - r_first) * G;  // (row, pair) units, pairs innermost
+    // rows are dealt round-robin (lane group s takes rows s, s+n_sg, ...) so that
+    // the loads in flight cover one contiguous window of every expert's W2
+    const int r_first = (int)sg;
+    const int n_rows = r_first < H ? (H - r_first + n_sg - 1) / n_sg : 0;
+    const int n_units = n_rows * G;  // (row, pair) units, pairs innermost
     const size_t m2 = 2 * ((size_t)I * H * 5 / 8);
     const size_t cbytes = (size_t)H * I / 2;
+
+    // h blocks to stage: issued before the weight ring so that waiting for them
+    // does not wait for the ring (items past the end re-read item 0)
+    const int n_items = P * nblk;
+    uint4 hd[kStagePerThread][4];
+#pragma unroll
+    for (int i = 0; i < kStagePerThread; ++i) {
+        int item = threadIdx.x + i * 256;
+        if (item >= n_items) item = 0;
+        const int m = item / nblk, b = item - m * nblk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hd[i][j] = load_global_u4(a.h + (size_t)m * I + 32 * b + 8 * j);
+    }
+    __syncthreads();  // any_slab
+    const uint8_t *fallback = any_slab;
 
     uint4 cw[D][BPL];
     uint32_t pw[D][BPL];
     int ui = 0, ri = r_first, gi = 0;
     auto issue = [&](int j) {
-        if (ui < n_units) {
-            const uint8_t *slab = gslab[gi];
-            if (slab) {
+        const uint8_t *slab = (ui < n_units) ? gslab[gi] : nullptr;
+        const size_t row = slab ? (size_t)ri : 0;
+        if (!slab) slab = fallback;
 #pragma unroll
-                for (int b = 0; b < BPL; ++b) {
-                    const int blk = c + b * LPR;
-                    cw[j][b] = load_stream_u4(slab + m2 + (size_t)ri * (I / 2) + 16 * blk);
-                    pw[j][b] = load_stream_u32(slab + m2 + cbytes + ((size_t)ri * nblk + blk) * 4);
-                }
-            }
+        for (int b = 0; b < BPL; ++b) {
+            const int blk = c + b * LPR;
+            cw[j][b] = load_stream_u4(slab + m2 + row * (I / 2) + 16 * blk);
+            pw[j][b] = load_stream_u32(slab + m2 + cbytes + (row * nblk + blk) * 4);
         }
         ++ui;
         if (++gi == G) {
             gi = 0;
-            ++ri;
+            ri += n_sg;
         }
     };
+    if (fallback) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) issue(j);
-    stage_all(a.h, I, P, X, S);
+        for (int j = 0; j < D; ++j) issue(j);
+    }
+#pragma unroll
+    for (int i = 0; i < kStagePerThread; ++i) {
+        const int item = threadIdx.x + i * 256;
+        if (item < n_items) {
+            const int m = item / nblk, b = item - m * nblk;
+            uint4 Xb[4];
+            S[m * nblk + b] = block_pairs(hd[i], Xb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[(m * 4 + j) * nblk + b] = Xb[j];
+        }
+    }
+    // larger P: the remaining items the plain way (this wait also covers the ring)
+    for (int item = threadIdx.x + kStagePerThread * 256; item < n_items; item += 256) {
+        const int m = item / nblk, b = item - m * nblk;
+        uint4 d[4], Xb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = load_global_u4(a.h + (size_t)m * I + 32 * b + 8 * j);
+        S[m * nblk + b] = block_pairs(d, Xb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[(m * 4 + j) * nblk + b] = Xb[j];
+    }
     __syncthreads();
+    if (!fallback) return;
 
     float acc[kMaxTok];
 #pragma unroll
@@ -264,7 +466,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
             }
             if (++g == G) {
                 g = 0;
-                ++rr;
+                rr += n_sg;
             }
         }
     }
@@ -300,11 +502,30 @@ int launch_gate_up(const moe::FfnArgs &a, hipStream_t s) {
     const int ups = (int)std::max<long long>(1, (Q + target_sg - 1) / target_sg);
     const long long nsg = (Q + ups - 1) / ups;
     const int grid = (int)((nsg + 4 * RPW - 1) / (4 * RPW));
-    const size_t lds = (size_t)a.T * (a.H >> 5) * (4 * 16 + 4);
-    int rc = raise_lds(decode_gate_up_kernel<LPR, BPL, D>, lds);
-    if (rc != MOE_OK) return rc;
-    hipLaunchKernelGGL((decode_gate_up_kernel<LPR, BPL, D>), dim3(grid), dim3(256), lds, s, a, ups);
+    if (a.T == 1) {
+        hipLaunchKernelGGL((decode_gate_up_kernel<LPR, BPL, D, true>), dim3(grid), dim3(256), 0, s, a, ups);
+    } else {
+        const size_t lds = (size_t)a.T * (a.H >> 5) * (4 * 16 + 4);
+        int rc = raise_lds(decode_gate_up_kernel<LPR, BPL, D, false>, lds);
+        if (rc != MOE_OK) return rc;
+        hipLaunchKernelGGL((decode_gate_up_kernel<LPR, BPL, D, false>), dim3(grid), dim3(256), lds, s, a, ups);
+    }
     MOE_LAUNCH_CHECK("decode_gate_up_kernel");
+    return MOE_OK;
+}
+
+#ifndef MOE_DECODE1_WG_PER_CU
+#define MOE_DECODE1_WG_PER_CU 2  // workgroups per CU for the one-token gate/up kernel
+#endif
+
+template <int BPL, int D>
+int launch_gate_up1(const moe::FfnArgs &a, hipStream_t s) {
+    const int G = a.n_routed_groups + (a.shared ? 1 : 0);
+    const long long Q = (long long)G * a.I;
+    const long long target = (long long)MOE_DECODE1_WG_PER_CU * num_cus() * 4;
+    const int grid = (int)((std::min(Q, target) + 3) / 4);
+    hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D>), dim3(grid), dim3(256), 0, s, a, grid * 4);
+    MOE_LAUNCH_CHECK("decode1_gate_up_kernel");
     return MOE_OK;
 }
 
@@ -312,21 +533,20 @@ template <int LPR, int BPL, int D>
 int launch_down(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s) {
     constexpr int RPW = 64 / LPR;
     const long long target_sg = (long long)MOE_DECODE_WG_PER_CU * num_cus() * 4 * RPW;
-    const int rps = (int)std::max<long long>(1, (a.H + target_sg - 1) / target_sg);
-    const long long nsg = (a.H + rps - 1) / rps;
-    const int grid = (int)((nsg + 4 * RPW - 1) / (4 * RPW));
+    const int grid = (int)((std::min<long long>(a.H, target_sg) + 4 * RPW - 1) / (4 * RPW));
+    const int n_sg = grid * 4 * RPW;
     const int P = a.T * a.k + (a.shared ? a.T : 0);
     const size_t lds = (size_t)P * (a.I >> 5) * (4 * 16 + 4);
     if (out) {
         int rc = raise_lds(decode_down_kernel<LPR, BPL, D, true>, lds);
         if (rc != MOE_OK) return rc;
         hipLaunchKernelGGL((decode_down_kernel<LPR, BPL, D, true>), dim3(grid), dim3(256), lds, s, a, topk_w, out,
-                           rps);
+                           n_sg);
     } else {
         int rc = raise_lds(decode_down_kernel<LPR, BPL, D, false>, lds);
         if (rc != MOE_OK) return rc;
         hipLaunchKernelGGL((decode_down_kernel<LPR, BPL, D, false>), dim3(grid), dim3(256), lds, s, a, topk_w,
-                           out, rps);
+                           out, n_sg);
     }
     MOE_LAUNCH_CHECK("decode_down_kernel");
     return MOE_OK;
@@ -347,7 +567,19 @@ bool decode_supported(const FfnArgs &a) {
     return gu && dn;
 }
 
+#ifndef MOE_DECODE1_D
+#define MOE_DECODE1_D 4  // units in flight per wave, one-token gate/up
+#endif
+
 int decode_gate_up(const FfnArgs &a, hipStream_t s) {
+    if (a.T == 1) {
+        switch (a.H >> 5) {
+            case 128: return launch_gate_up1<2, MOE_DECODE1_D>(a, s);
+            case 192: return launch_gate_up1<3, 3>(a, s);
+            case 64: return launch_gate_up1<1, 6>(a, s);
+            default: break;
+        }
+    }
     switch (a.H >> 5) {
         case 128: return launch_gate_up<64, 2, MOE_DECODE_D_GU>(a, s);
         case 192: return launch_gate_up<64, 3, 3>(a, s);
