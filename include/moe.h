@@ -209,6 +209,20 @@ int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const 
                            const float *topk_w, int k, const void *const *expert_table, const void *shared_slab,
                            uint16_t *out, void *workspace, size_t workspace_bytes, int path, void *stream);
 
+/* The whole routed-expert step of one layer in one call: router (as
+ * moe_router_topk) then gate/up + SwiGLU, down projection and weighted combine
+ * (as moe_expert_ffn_combine), with the same arithmetic and roundings, so
+ * topk_idx, topk_w and out are bit-identical to those two calls.  For one
+ * token (decode) the router's last step runs inside the gate/up kernel
+ * instead of a kernel of its own: three launches per layer.  Every routed
+ * expert must be resident.  Arguments as in the two calls; topk_idx [T,k] and
+ * topk_w [T,k] are outputs.  workspace: moe_route_ffn_combine_workspace_bytes
+ * (contents don't care; calls sharing it must not overlap in time). */
+size_t moe_route_ffn_combine_workspace_bytes(int T, int H, int I, int E, int k, int has_shared);
+int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias, int E,
+                          int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
+                          float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ debug
  * Dequantise matrix `which` (0 = W1, 1 = W3, 2 = W2) of a device slab into out
  * (fp32, row-major [rows x cols]); exact, for round-trip tests of the format. */

@@ -20,6 +20,17 @@ struct FfnArgs {
     float *y;                   // [T*k + T*shared, H] fp32 expert outputs
 };
 
+// Router finish fused into the one-token gate/up kernel: the per-slice fp64
+// partial logits of the token and where to publish the routing.
+struct RouteArgs {
+    const double *partial;  // [E][kMaxSlices] partial logits of the token
+    const float *bias;      // [E] or nullptr
+    int E, nslices;
+    float *logits;          // [E] fp32 logits (written by workgroup 0)
+    int32_t *idx_out;       // [k] selected experts
+    float *w_out;           // [k] their renormalised weights
+};
+
 // Gate/up + SwiGLU (x -> h) and down projection (h -> y) with the dequant-GEMV
 // kernels.  max_m: largest number of tokens any group can have.
 int ffn_gemv_gate_up(const FfnArgs &a, int max_m, hipStream_t s);
@@ -30,6 +41,10 @@ bool decode_supported(const FfnArgs &a);
 int decode_gate_up(const FfnArgs &a, hipStream_t s);
 // out == nullptr: write y; otherwise apply the weighted combine into out [T, H].
 int decode_down(const FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s);
+// One token with the router finished inside gate/up (a.topk_idx unused; the
+// down kernel must then read ra.idx_out / ra.w_out).
+bool decode1_routed_supported(const FfnArgs &a, int E);
+int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s);
 
 // MFMA grouped GEMM (prefill): needs the expert grouping and H, I multiples of 128.
 bool mfma_supported(const FfnArgs &a);

@@ -17,6 +17,8 @@
 
 #include "common.h"
 #include "dequant.h"
+#include "router.h"
+#include "topk.h"
 #include "ffn.h"
 
 namespace {
@@ -219,17 +221,20 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 // is a scalar row base plus the lane's fixed offset.  Units (group, row) are
 // dealt to the waves round-robin (wave w takes units w, w+W, w+2W, ...), so the
 // loads in flight across the chip at any moment cover one contiguous window of
-// each weight matrix, which keeps HBM pages open, instead of one scattered run
-// per wave.  The token's activation blocks stay in registers for the whole
-// launch; there is no LDS staging.
-template <int BPL, int D>
-__global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, int n_waves) {
-    const int H = a.H, I = a.I, nblk = H >> 5;
-    const int G = a.n_routed_groups + (a.shared ? 1 : 0);
+// each weight matrix instead of one scattered run per wave.  The token's
+// activation blocks stay in registers for the whole launch.
+//
+// Routing: with PER = 0 the k slots come from a.topk_idx; with PER > 0 every
+// wave finishes the router itself from the per-slice fp64 partial logits
+// (same fp32 logits, same top-k and softmax as the router entry point) and
+// workgroup 0 publishes idx / weights / logits for the down kernel and the
+// caller.  Lane g holds the slab of group g (slot g, then the shared expert);
+// a group's slab is read with v_readlane, so there is no LDS and no barrier.
+template <int BPL, int D, int PER>
+__global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, moe::RouteArgs ra, int n_waves) {
+    const int H = a.H, I = a.I, nblk = H >> 5, k = a.k;
+    const int G = k + (a.shared ? 1 : 0);
     const int Q = G * I;
-    __shared__ const uint8_t *gslab[kMaxGroups];
-    load_group_slabs(a, gslab, G);
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint4 xd[BPL][4];
@@ -237,16 +242,47 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, in
     for (int b = 0; b < BPL; ++b)
 #pragma unroll
         for (int j = 0; j < 4; ++j) xd[b][j] = load_global_u4(a.x + 32 * (lane + 64 * b) + 8 * j);
-    __syncthreads();
 
+    int slot_e;
+    if constexpr (PER > 0) {
+        const bool publish = blockIdx.x == 0 && wave == 0;
+        uint32_t ord[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int e = lane + 64 * j;
+            ord[j] = 0u;
+            if (e < ra.E) {
+                const float l = moe::router_logit(ra.partial, ra.nslices, ra.bias, e);
+                if (publish) ra.logits[e] = l;
+                ord[j] = moe::topk_ord(l);
+            }
+        }
+        float slot_logit;
+        moe::topk_select(ord, k, slot_logit, slot_e);
+        const float w = moe::topk_softmax(slot_logit, k);
+        if (publish && lane < k) {
+            ra.idx_out[lane] = slot_e;
+            ra.w_out[lane] = w;
+        }
+    } else {
+        slot_e = lane < k ? a.topk_idx[lane] : 0;
+    }
+    const uint8_t *mine = nullptr;
+    if (lane < k) {
+        if (!a.mask || a.mask[slot_e]) mine = (const uint8_t *)a.table[slot_e];
+    } else if (lane == k) {
+        mine = (const uint8_t *)a.shared;
+    }
+    const uint64_t mv = (uint64_t)mine;
+    const int mlo = (int)(uint32_t)mv, mhi = (int)(uint32_t)(mv >> 32);
+    auto group_slab = [&](int g) {
+        return (const uint8_t *)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(mhi, g) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane(mlo, g));
+    };
     // tail units and masked groups re-read row 0 of the first present slab
-    const uint8_t *mine = lane < G ? gslab[lane] : nullptr;
     const uint64_t present = __ballot(mine != nullptr);
     if (present == 0) return;  // every group masked off
-    const int first = __ffsll((long long)present) - 1;
-    const uint64_t fv = (uint64_t)mine;
-    const uint8_t *fallback = (const uint8_t *)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(fv >> 32), first) << 32) |
-                                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)fv, first));
+    const uint8_t *fallback = group_slab(__ffsll((long long)present) - 1);
 
     const uint32_t magic = moe_magic_vgpr();
     const int w0 = blockIdx.x * 4 + wave;
@@ -263,7 +299,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, in
         const uint8_t *slab = fallback;
         int row = 0;
         if (ui < n) {
-            const uint8_t *p = uniform_ptr(gslab[gi]);
+            const uint8_t *p = group_slab(gi);
             if (p) {
                 slab = p;
                 row = ri;
@@ -299,7 +335,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, in
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             if (base + j >= n) break;
-            if (uniform_ptr(gslab[g])) {
+            if (group_slab(g)) {
                 float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
                 for (int b = 0; b < BPL; ++b) {
@@ -308,10 +344,8 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, in
                 }
                 v0 = moe_group_sum<64>(v0);
                 v1 = moe_group_sum<64>(v1);
-                if (lane == 63) {
-                    const int row = g < a.n_routed_groups ? g : a.k;  // pair g, or the shared row
-                    a.h[(size_t)row * I + r] = (uint16_t)f32_to_bf16_bits(v0 / (1.0f + expf(-v0)) * v1);
-                }
+                if (lane == 63)  // h row: slot g, or the shared row k
+                    a.h[(size_t)g * I + r] = (uint16_t)f32_to_bf16_bits(v0 / (1.0f + expf(-v0)) * v1);
             }
             issue(j);  // slot j is free again: request the unit D ahead
             g += dg;
@@ -472,6 +506,105 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
     }
 }
 
+// ---------------------------------------------------------------- down (+ combine), one token
+// One token, I = 16*32*BPL: wave p of a workgroup owns pair p of the token
+// (routed slots 0..k-1, then the shared expert) and keeps that pair's h row in
+// registers; its four 16-lane groups take rows r0+s, r0+s+4, ... of the
+// workgroup's row range in W2 of the pair's expert.  Per-(row, pair) results
+// meet in LDS and one thread per row combines them in slot order (fmaf with
+// the routing weight, then + shared), so the fused output matches the
+// two-kernel path bit for bit.  Every SIMD gets several independent waves
+// instead of one wave walking all pairs of a row.
+constexpr int kDown1MaxRows = 64;  // rows per workgroup
+constexpr int kDown1MaxPairs = 16;
+
+template <int BPL, int D, bool COMBINE>
+__global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, const float *__restrict__ topk_w,
+                                                            uint16_t *__restrict__ out, int rows_per_wg) {
+    const int H = a.H, I = a.I, k = a.k;
+    const int P = k + (a.shared ? 1 : 0);
+    __shared__ float part[kDown1MaxRows][kDown1MaxPairs + 1];
+    __shared__ int present[kDown1MaxPairs];
+    const int lane = threadIdx.x & 63, sub = lane >> 4, c = lane & 15;
+    const int p = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r0 = blockIdx.x * rows_per_wg;
+    const int U = rows_per_wg >> 2;  // rows per 16-lane group
+
+    uint4 hd[BPL][4];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hd[b][j] = load_global_u4(a.h + (size_t)p * I + 32 * (c + 16 * b) + 8 * j);
+
+    const uint8_t *slab = nullptr;
+    if (p < k) {
+        const int e = a.topk_idx[p];
+        if (!a.mask || a.mask[e]) slab = (const uint8_t *)a.table[e];
+    } else {
+        slab = (const uint8_t *)a.shared;
+    }
+    slab = uniform_ptr(slab);
+    if (lane == 0) present[p] = slab != nullptr;
+
+    if (slab) {
+        const uint32_t magic = moe_magic_vgpr();
+        const size_t m2 = 2 * ((size_t)I * H * 5 / 8);
+        const uint8_t *w2 = slab + m2, *r2 = slab + m2 + (size_t)H * I / 2;
+        const uint32_t code_off = 16u * c, rec_off = 4u * c;
+        uint4 cw[D][BPL];
+        uint32_t pw[D][BPL];
+        int ui = 0;
+        auto issue = [&](int j) {
+            int row = r0 + sub + 4 * ui;
+            if (ui >= U || row >= H) row = r0;  // past the end: re-read a valid row
+            const uint32_t crow = (uint32_t)row * (uint32_t)(I / 2), rrow = (uint32_t)row * (uint32_t)(I / 8);
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                cw[j][b] = load_stream_u4(w2 + (crow + code_off + 256u * b));
+                pw[j][b] = load_stream_u32(r2 + (rrow + rec_off + 64u * b));
+            }
+            ++ui;
+        };
+#pragma unroll
+        for (int j = 0; j < D; ++j) issue(j);
+
+        uint4 X[BPL][4];
+        float S[BPL];
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) S[b] = block_pairs(hd[b], X[b]);
+
+        for (int base = 0; base < U; base += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if (base + j >= U) break;
+                const int rl = sub + 4 * (base + j), row = r0 + rl;
+                float v = 0.0f;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b)
+                    v += moe_block_value(pw[j][b], moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
+                v = moe_group_sum<16>(v);
+                if (c == 15 && row < H) {
+                    if (COMBINE)
+                        part[rl][p] = v;
+                    else
+                        a.y[(size_t)p * H + row] = v;
+                }
+                issue(j);
+            }
+        }
+    }
+    if (COMBINE) {
+        __syncthreads();
+        const int t = threadIdx.x, row = r0 + t;
+        if (t < rows_per_wg && row < H) {
+            float acc = 0.0f;
+            for (int g = 0; g < P; ++g)
+                if (present[g]) acc = g < k ? fmaf(topk_w[g], part[t][g], acc) : acc + part[t][g];
+            out[row] = (uint16_t)f32_to_bf16_bits(acc);
+        }
+    }
+}
+
 int g_num_cus = 0;
 
 int num_cus() {
@@ -519,12 +652,20 @@ int launch_gate_up(const moe::FfnArgs &a, hipStream_t s) {
 #endif
 
 template <int BPL, int D>
-int launch_gate_up1(const moe::FfnArgs &a, hipStream_t s) {
+int launch_gate_up1(const moe::FfnArgs &a, const moe::RouteArgs *ra, hipStream_t s) {
     const int G = a.n_routed_groups + (a.shared ? 1 : 0);
     const long long Q = (long long)G * a.I;
     const long long target = (long long)MOE_DECODE1_WG_PER_CU * num_cus() * 4;
     const int grid = (int)((std::min(Q, target) + 3) / 4);
-    hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D>), dim3(grid), dim3(256), 0, s, a, grid * 4);
+    const moe::RouteArgs none{};
+    if (!ra)
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 0>), dim3(grid), dim3(256), 0, s, a, none, grid * 4);
+    else if (ra->E <= 64)
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 1>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
+    else if (ra->E <= 128)
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 2>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
+    else
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 4>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
     MOE_LAUNCH_CHECK("decode1_gate_up_kernel");
     return MOE_OK;
 }
@@ -552,6 +693,28 @@ int launch_down(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipSt
     return MOE_OK;
 }
 
+#ifndef MOE_DOWN1_ROWS
+#define MOE_DOWN1_ROWS 16 // rows per workgroup, one-token down kernel
+#endif
+#ifndef MOE_DOWN1_D
+#define MOE_DOWN1_D 2  // units in flight per lane group, one-token down kernel
+#endif
+
+template <int BPL>
+int launch_down1(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s) {
+    static_assert(MOE_DOWN1_ROWS % 4 == 0 && MOE_DOWN1_ROWS <= kDown1MaxRows, "rows per workgroup");
+    const int P = a.k + (a.shared ? 1 : 0);
+    const int grid = (a.H + MOE_DOWN1_ROWS - 1) / MOE_DOWN1_ROWS;
+    if (out)
+        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, true>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
+                           out, MOE_DOWN1_ROWS);
+    else
+        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, false>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
+                           out, MOE_DOWN1_ROWS);
+    MOE_LAUNCH_CHECK("decode1_down_kernel");
+    return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -571,12 +734,27 @@ bool decode_supported(const FfnArgs &a) {
 #define MOE_DECODE1_D 4  // units in flight per wave, one-token gate/up
 #endif
 
+bool decode1_routed_supported(const FfnArgs &a, int E) {
+    const int nh = a.H >> 5;
+    return a.T == 1 && !a.grouped && a.k + (a.shared ? 1 : 0) <= kMaxGroups && E <= 256 &&
+           (nh == 128 || nh == 192 || nh == 64) && decode_supported(a);
+}
+
+int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s) {
+    switch (a.H >> 5) {
+        case 128: return launch_gate_up1<2, MOE_DECODE1_D>(a, &ra, s);
+        case 192: return launch_gate_up1<3, 3>(a, &ra, s);
+        case 64: return launch_gate_up1<1, 6>(a, &ra, s);
+        default: return fail(MOE_E_SHAPE, "routed gate/up: H=%d not supported", a.H);
+    }
+}
+
 int decode_gate_up(const FfnArgs &a, hipStream_t s) {
     if (a.T == 1) {
         switch (a.H >> 5) {
-            case 128: return launch_gate_up1<2, MOE_DECODE1_D>(a, s);
-            case 192: return launch_gate_up1<3, 3>(a, s);
-            case 64: return launch_gate_up1<1, 6>(a, s);
+            case 128: return launch_gate_up1<2, MOE_DECODE1_D>(a, nullptr, s);
+            case 192: return launch_gate_up1<3, 3>(a, nullptr, s);
+            case 64: return launch_gate_up1<1, 6>(a, nullptr, s);
             default: break;
         }
     }
@@ -590,6 +768,13 @@ int decode_gate_up(const FfnArgs &a, hipStream_t s) {
 }
 
 int decode_down(const FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s) {
+    if (a.T == 1 && a.k + (a.shared ? 1 : 0) <= kDown1MaxPairs) {
+        switch (a.I >> 5) {
+            case 48: return launch_down1<3>(a, topk_w, out, s);
+            case 64: return launch_down1<4>(a, topk_w, out, s);
+            default: break;
+        }
+    }
     switch (a.I >> 5) {
         case 48: return launch_down<16, 3, MOE_DECODE_D_DN>(a, topk_w, out, s);
         case 64: return launch_down<64, 1, 8>(a, topk_w, out, s);

@@ -2,6 +2,8 @@
 // dispatcher, the weighted combine and the dequantisation debug hook.
 #include "common.h"
 #include "ffn.h"
+#include "router.h"
+#include "topk.h"
 
 namespace {
 
@@ -324,6 +326,51 @@ extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, in
                         workspace_bytes, path, stream);
     if (rc != MOE_OK) return rc;
     return moe_combine(y, topk_w, T, k, H, has_shared, out, stream);
+}
+
+extern "C" size_t moe_route_ffn_combine_workspace_bytes(int T, int H, int I, int E, int k, int has_shared) {
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
+    return moe::align_up(moe_router_workspace_bytes(T, E), 256) + ffn_layout(T, H, I, E, k, has_shared).total;
+}
+
+extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias,
+                                     int E, int k, const void *const *expert_table, const void *shared_slab,
+                                     int32_t *topk_idx, float *topk_w, uint16_t *out, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    const char *who = "route_ffn_combine";
+    if (T < 0) return moe::fail(MOE_E_ARG, "%s: T=%d < 0", who, T);
+    if (T == 0) return MOE_OK;
+    if (!workspace || !w_router || !topk_w) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, MOE_FFN_AUTO, who);
+    if (rc != MOE_OK) return rc;
+    const int has_shared = shared_slab != nullptr;
+    const size_t need = moe_route_ffn_combine_workspace_bytes(T, H, I, E, k, has_shared);
+    if (workspace_bytes < need) return moe::fail(MOE_E_NOMEM, "%s: workspace %zu < %zu bytes", who, workspace_bytes, need);
+    const size_t rbytes = moe::align_up(moe_router_workspace_bytes(T, E), 256);
+    char *rws = (char *)workspace;
+    char *fws = rws + rbytes;
+    hipStream_t s = (hipStream_t)stream;
+
+    moe::FfnArgs a;
+    int max_m = 1;
+    const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
+    rc = make_args(a, x, (uint16_t *)(fws + Ly.h), nullptr, T, H, I, E, topk_idx, k, nullptr, nullptr, nullptr,
+                   expert_table, shared_slab, nullptr, MOE_FFN_PAIRS, &max_m, who);
+    if (rc != MOE_OK) return rc;
+    if (k <= moe::kTopkMaxK && H <= moe::kSlice * moe::kMaxSlices && moe::decode1_routed_supported(a, E)) {
+        double *partial = moe::router_partials_buf(rws, T, E);
+        rc = moe::router_partials(x, T, H, w_router, E, partial, s);
+        if (rc != MOE_OK) return rc;
+        const moe::RouteArgs ra{partial, bias, E, (H + moe::kSlice - 1) / moe::kSlice, moe::router_logits(rws),
+                                topk_idx, topk_w};
+        rc = moe::decode1_routed_gate_up(a, ra, s);
+        if (rc != MOE_OK) return rc;
+        return moe::decode_down(a, topk_w, out, s);
+    }
+    rc = moe_router_topk(x, T, H, w_router, bias, E, k, topk_idx, topk_w, rws, rbytes, stream);
+    if (rc != MOE_OK) return rc;
+    return moe_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, fws,
+                                  workspace_bytes - rbytes, MOE_FFN_AUTO, stream);
 }
 
 extern "C" int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,

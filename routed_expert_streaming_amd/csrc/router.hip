@@ -14,76 +14,27 @@
 //  * large T (prefill): 64x64 register-tiled fp64 product through LDS, then a
 //    top-k kernel with one wavefront per token.
 #include "common.h"
+#include "router.h"
+#include "topk.h"
 
 namespace {
 
-constexpr int kTopkMaxK = 64;
-constexpr int kMaxE = 1024;
+using moe::kTopkMaxK;
+constexpr int kMaxE = moe::kTopkMaxE;
+constexpr int kPer = moe::kTopkPer;
 
-// Order-preserving key: larger logit first, then lower index.  Key 0 never
-// occurs for finite logits, so it marks taken/empty entries.
-__device__ __forceinline__ unsigned long long topk_key(float l, int e) {
-    if (l == 0.0f) l = 0.0f;  // -0 and +0 compare equal: same key
-    uint32_t u = __float_as_uint(l);
-    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_logit(unsigned long long key) {
-    uint32_t ord = (uint32_t)(key >> 32);
-    uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-    return __uint_as_float(u);
-}
-
-__device__ __forceinline__ int key_index(unsigned long long key) {
-    return (int)(0xFFFFFFFFu - (uint32_t)key);
-}
-
-constexpr int kPer = kMaxE / 64;  // logits per lane at most
-
-// One wavefront: top-k over keys held in registers (lane l holds experts
-// l, l+64, ...), then the renormalised softmax over the selected k.
+// One wavefront: top-k of the codes in registers, softmax, write slot i from lane i.
 template <int PER>
-__device__ void wave_topk_keys(unsigned long long (&keys)[PER], int k, int32_t *idx_out, float *w_out) {
+__device__ __forceinline__ void wave_topk_write(uint32_t (&ord)[PER], int k, int32_t *idx_out, float *w_out) {
+    float slot_logit;
+    int slot_index;
+    moe::topk_select(ord, k, slot_logit, slot_index);
+    const float w = moe::topk_softmax(slot_logit, k);
     const int lane = threadIdx.x & 63;
-    float my_logit = 0.0f;
-    int my_index = 0;
-    for (int i = 0; i < k; ++i) {
-        unsigned long long best = 0;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) best = keys[j] > best ? keys[j] : best;
-        best = wave_max_u64(best);
-        const int e = key_index(best);
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (lane + 64 * j == e) keys[j] = 0ull;  // owner drops the winner
-        if (lane == i) {
-            my_logit = key_logit(best);
-            my_index = e;
-        }
-    }
-    // softmax over the k selected, max is slot 0
-    const float top = __shfl(my_logit, 0, 64);
-    const float ex = (lane < k) ? expf(my_logit - top) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
     if (lane < k) {
-        idx_out[lane] = my_index;
-        w_out[lane] = ex / sum;
+        idx_out[lane] = slot_index;
+        w_out[lane] = w;
     }
-}
-
-// Top-k of one token's E logits stored in memory.
-__device__ void wave_topk(const float *lg, int E, int k, int32_t *idx_out, float *w_out) {
-    const int lane = threadIdx.x & 63;
-    unsigned long long keys[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int e = lane + 64 * j;
-        keys[j] = (e < E) ? topk_key(lg[e], e) : 0ull;
-    }
-    wave_topk_keys(keys, k, idx_out, w_out);
 }
 
 // ---------------------------------------------------------------- small T
@@ -93,8 +44,8 @@ __device__ void wave_topk(const float *lg, int E, int k, int32_t *idx_out, float
 // the partials of each logit in slice order plus the bias, rounds once to fp32
 // and runs the top-k.  (A single kernel with a last-workgroup ticket would need
 // an agent-scope fence per workgroup, which costs more than the second launch.)
-constexpr int kSlice = 1024;
-constexpr int kMaxSlices = 16;  // H <= 16384
+using moe::kSlice;
+using moe::kMaxSlices;
 constexpr int kSmallT = 32;
 
 template <int TMAX>
@@ -144,21 +95,18 @@ __global__ __launch_bounds__(256) void router_finalize_kernel(const double *__re
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int nslices = (H + kSlice - 1) / kSlice;
-    unsigned long long keys[PER];
+    uint32_t ord[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = lane + 64 * j;
-        keys[j] = 0ull;
+        ord[j] = 0u;
         if (e < E) {
-            const double *p = partial + ((size_t)t * E + e) * kMaxSlices;
-            double s = 0.0;
-            for (int q = 0; q < nslices; ++q) s += p[q];
-            const float l = (float)(s + (bias ? (double)bias[e] : 0.0));
+            const float l = moe::router_logit(partial + (size_t)t * E * kMaxSlices, nslices, bias, e);
             logits[(size_t)t * E + e] = l;  // kept for inspection; the top-k reads registers
-            keys[j] = topk_key(l, e);
+            ord[j] = moe::topk_ord(l);
         }
     }
-    wave_topk_keys(keys, k, idx + (size_t)t * k, w + (size_t)t * k);
+    wave_topk_write(ord, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
 // ---------------------------------------------------------------- large T
@@ -218,18 +166,50 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
                                                           int32_t *__restrict__ idx, float *__restrict__ w) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    wave_topk(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+    const int lane = threadIdx.x & 63;
+    uint32_t ord[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = lane + 64 * j;
+        ord[j] = (e < E) ? moe::topk_ord(logits[(size_t)t * E + e]) : 0u;
+    }
+    wave_topk_write(ord, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
-constexpr size_t kTicketBytes = 256;  // reserved header before the logits
+constexpr size_t kHeaderBytes = 256;  // reserved header before the logits
 
 }  // namespace
+
+namespace moe {
+
+float *router_logits(void *workspace) { return (float *)((char *)workspace + kHeaderBytes); }
+
+double *router_partials_buf(void *workspace, int T, int E) {
+    return (double *)((char *)workspace + kHeaderBytes + align_up((size_t)T * (size_t)E * sizeof(float), 256));
+}
+
+int router_partials(const uint16_t *x, int T, int H, const float *w_router, int E, double *partial, hipStream_t s) {
+    const int nslices = (H + kSlice - 1) / kSlice;
+    const dim3 grid((E * nslices + 3) / 4), block(256);
+    if (T == 1)
+        hipLaunchKernelGGL(router_partial_kernel<1>, grid, block, 0, s, x, T, H, w_router, E, partial);
+    else if (T <= 4)
+        hipLaunchKernelGGL(router_partial_kernel<4>, grid, block, 0, s, x, T, H, w_router, E, partial);
+    else if (T <= 8)
+        hipLaunchKernelGGL(router_partial_kernel<8>, grid, block, 0, s, x, T, H, w_router, E, partial);
+    else
+        hipLaunchKernelGGL(router_partial_kernel<32>, grid, block, 0, s, x, T, H, w_router, E, partial);
+    MOE_LAUNCH_CHECK("router_partial_kernel");
+    return MOE_OK;
+}
+
+}  // namespace moe
 
 extern "C" size_t moe_router_workspace_bytes(int T, int E) {
     if (T < 0 || E <= 0) return 0;
     const size_t logits = moe::align_up((size_t)T * (size_t)E * sizeof(float), 256);
     const size_t partial = T <= kSmallT ? (size_t)T * (size_t)E * kMaxSlices * sizeof(double) : 0;
-    return kTicketBytes + logits + partial;
+    return kHeaderBytes + logits + partial;
 }
 
 extern "C" int moe_router_topk(const uint16_t *x, int T, int H, const float *w_router, const float *bias, int E,
@@ -246,22 +226,12 @@ extern "C" int moe_router_topk(const uint16_t *x, int T, int H, const float *w_r
                          moe_router_workspace_bytes(T, E));
     if (H > kSlice * kMaxSlices) return moe::fail(MOE_E_SHAPE, "router: H=%d above %d", H, kSlice * kMaxSlices);
     hipStream_t s = (hipStream_t)stream;
-    float *logits = (float *)((char *)workspace + kTicketBytes);
-    double *partial =
-        (double *)((char *)workspace + kTicketBytes + moe::align_up((size_t)T * (size_t)E * sizeof(float), 256));
+    float *logits = moe::router_logits(workspace);
+    double *partial = moe::router_partials_buf(workspace, T, E);
     const dim3 block(256);
     if (T <= kSmallT) {
-        const int nslices = (H + kSlice - 1) / kSlice;
-        const dim3 grid_p((E * nslices + 3) / 4);
-        if (T == 1)
-            hipLaunchKernelGGL(router_partial_kernel<1>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
-        else if (T <= 4)
-            hipLaunchKernelGGL(router_partial_kernel<4>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
-        else if (T <= 8)
-            hipLaunchKernelGGL(router_partial_kernel<8>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
-        else
-            hipLaunchKernelGGL(router_partial_kernel<32>, grid_p, block, 0, s, x, T, H, w_router, E, partial);
-        MOE_LAUNCH_CHECK("router_partial_kernel");
+        int rc = moe::router_partials(x, T, H, w_router, E, partial, s);
+        if (rc != MOE_OK) return rc;
         const dim3 grid_f((T + 3) / 4);
         if (E <= 64)
             hipLaunchKernelGGL(router_finalize_kernel<1>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,

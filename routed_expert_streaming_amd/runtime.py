@@ -145,6 +145,8 @@ class MoEStack:
         self.router_ws = torch.zeros(self.router_ws_bytes, dtype=torch.uint8, device=self.dev)
         self.ffn_ws_bytes = L.moe_expert_ffn_workspace_bytes(T, H, I, E, k, self.has_shared)
         self.ffn_ws = torch.empty(self.ffn_ws_bytes, dtype=torch.uint8, device=self.dev)
+        self.layer_ws_bytes = L.moe_route_ffn_combine_workspace_bytes(T, H, I, E, k, self.has_shared)
+        self.layer_ws = torch.empty(self.layer_ws_bytes, dtype=torch.uint8, device=self.dev)
         self.idx = torch.empty((Lyr, T, k), dtype=torch.int32, device=self.dev)
         self.w = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
         P = T * k + (T if self.has_shared else 0)
@@ -188,6 +190,12 @@ class MoEStack:
                                  self.table[l], self.shared[l] if self.has_shared else None, out[l], self.ffn_ws,
                                  self.ffn_ws_bytes, self.path, self.stream)
 
+    def route_ffn_combine(self, x: torch.Tensor, l: int, out: torch.Tensor):
+        """Router, gate/up, down and combine of layer l in one call (every expert resident)."""
+        L.moe_route_ffn_combine(x[l], self.T, self.H, self.I, self.wr[l], None if self.bias is None else self.bias[l],
+                                self.E, self.k, self.table[l], self.shared[l] if self.has_shared else None,
+                                self.idx[l], self.w[l], out[l], self.layer_ws, self.layer_ws_bytes, self.stream)
+
     def combine(self, l: int, out: torch.Tensor):
         L.moe_combine(self.y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l], self.stream)
 
@@ -215,12 +223,12 @@ class MoEStack:
     def forward(self, x: torch.Tensor, out: torch.Tensor) -> StepStats:
         """One step over all layers: x [L,T,H] bf16 -> out [L,T,H] bf16."""
         st = StepStats()
-        for l in range(self.L):
-            self.route(x, l)
         if not self.streaming:
             for l in range(self.L):
-                self.ffn_combine(x, l, out)
+                self.route_ffn_combine(x, l, out)
             return st
+        for l in range(self.L):
+            self.route(x, l)
         # one small D2H per step, then the host plans every layer
         idx_host = np.frombuffer(self._idx_host.array, dtype=np.int32, count=self.L * self.T * self.k)
         torch.from_numpy(idx_host).copy_(self.idx.view(-1), non_blocking=True)

@@ -233,3 +233,19 @@ def test_cache_create_rejects_bad_descriptions():
     for d in (_desc(0, 16, 4), _desc(1, 16, 0), _desc(1, 16, 17), _desc(1, 16, 4, hidden=100)):
         with pytest.raises(L.MoEError):
             L.moe_cache_create_recording(d)
+
+
+def test_route_ffn_combine_validation():
+    ws = L.moe_route_ffn_combine_workspace_bytes(1, 256, 128, 16, 2, 1)
+    assert ws >= L.moe_router_workspace_bytes(1, 16) + L.moe_expert_ffn_workspace_bytes(1, 256, 128, 16, 2, 1)
+    args = [FAKE, 1, 256, 128, FAKE, None, 16, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws]
+    assert _status(L.moe_route_ffn_combine, None, *args[1:]) == L.MOE_E_ARG
+    bad = list(args); bad[4] = None  # router weights
+    assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_ARG
+    bad = list(args); bad[2] = 250
+    assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_SHAPE
+    bad = list(args); bad[7] = 17  # k > E
+    assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_SHAPE
+    bad = list(args); bad[14] = ws - 1
+    assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_NOMEM
+    L.moe_route_ffn_combine(None, 0, 256, 128, None, None, 16, 2, None, None, None, None, None, None, 0)

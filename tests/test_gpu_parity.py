@@ -204,6 +204,21 @@ class Layer:
     def oracle(self, rows=None):
         return oracle.moe_layer(self.x, self.Wr, self.bias, self.k, self.slabs, self.shared, self.I, rows=rows)
 
+    def run_routed(self):
+        """Router + FFN + combine through the one-call entry point."""
+        T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
+        x = bf16_dev(self.x)
+        wr = torch.from_numpy(self.Wr).cuda()
+        b = None if self.bias is None else torch.from_numpy(self.bias).cuda()
+        idx = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+        w = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        nb = L.moe_route_ffn_combine_workspace_bytes(T, H, I, E, k, self.shared is not None)
+        ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+        L.moe_route_ffn_combine(x, T, H, I, wr, b, E, k, self.table, self.shared_dev, idx, w, out, ws, nb)
+        torch.cuda.synchronize()
+        return idx.cpu().numpy(), w.cpu().numpy(), out.view(torch.int16).cpu().numpy().view(np.uint16)
+
 
 LAYER_CASES = [
     # name, T, H, I, E, k, shared, bias, oracle rows
@@ -241,6 +256,37 @@ def test_layer_parity_all_paths(name, T, H, I, E, k, shared, bias, rows):
     assert np.array_equal(results[paths[0]][0], results[paths[1]][0])
     assert np.array_equal(results[paths[0]][1], results[paths[1]][1])
     print(f"{name}: max err / max|ref| = {results[paths[0]][2]:.2e}")
+
+
+ROUTED_CASES = [
+    # name, T, H, I, E, k, shared, bias, zero router (all logits tie)
+    ("decode1", 1, 4096, 1536, 128, 8, True, None, False),
+    ("wide_e256", 1, 6144, 2048, 256, 8, True, "zipf", False),
+    ("e64_no_shared", 1, 2048, 1536, 64, 4, False, None, False),
+    ("all_ties", 1, 4096, 1536, 128, 8, True, None, True),
+    ("tiny_fallback", 4, 256, 128, 16, 2, False, None, False),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,shared,bias,zero", ROUTED_CASES, ids=[c[0] for c in ROUTED_CASES])
+def test_route_ffn_combine_matches_separate_calls(name, T, H, I, E, k, shared, bias, zero):
+    """The one-call layer (router finished inside gate/up for one token) gives
+    the indices, weights and output of router + FFN + combine bit for bit."""
+    lay = Layer(T, H, I, E, k, shared, bias, seed=zlib.crc32(name.encode()) % 1000 + 29)
+    if zero:
+        lay.Wr[:] = 0.0
+    idx_f, w_f, out_f = lay.run_routed()
+    idx_s, _, out_s = lay.run(L.MOE_FFN_AUTO)
+    _, w_s, _, _ = run_router(lay.x, lay.Wr, lay.bias, k)
+    assert np.array_equal(idx_f, idx_s)
+    assert np.array_equal(w_f.view(np.uint32), w_s.view(np.uint32))
+    assert np.array_equal(out_f, out_s)
+    if zero:  # every logit equal: the lowest indices win, equal weights
+        assert np.array_equal(idx_f, np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+        assert np.allclose(w_f, 1.0 / k, rtol=0, atol=1e-7)
+    ref = lay.oracle()
+    assert np.array_equal(idx_f, ref["idx"])
+    check_close(out_f, ref["out64"], name)
 
 
 PREFILL_CASES = [
