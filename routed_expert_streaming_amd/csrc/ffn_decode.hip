@@ -34,6 +34,15 @@ namespace {
 #define MOE_DECODE_D_DN 4  // down units in flight per lane group (I = 1536)
 #endif
 
+// s_waitcnt immediate that waits until at most n vector-memory loads are in
+// flight (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their no-wait maxima)
+constexpr int kWaitVm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+
+#ifndef MOE_DECODE1_EARLY
+#define MOE_DECODE1_EARLY 1  // one-token gate/up: request a shared-expert unit before routing
+#endif
+
 constexpr int kMaxTok = 4;      // tokens per launch on this path
 constexpr int kMaxGroups = 64;  // T*k + 1
 
@@ -228,12 +237,19 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 // wave finishes the router itself from the per-slice fp64 partial logits
 // (same fp32 logits, same top-k and softmax as the router entry point) and
 // workgroup 0 publishes idx / weights / logits for the down kernel and the
-// caller.  Lane g holds the slab of group g (slot g, then the shared expert);
-// a group's slab is read with v_readlane, so there is no LDS and no barrier.
+// caller.  The expert table is loaded alongside the partials, so resolving a
+// slot's slab is a lane shuffle rather than another trip to memory.
+//
+// Groups: the shared expert (when present) is group 0 and slot s is group
+// s+1, so most waves start on the shared expert, whose slab is known before
+// routing: they request their first unit before the top-k.  Lane g holds the
+// slab of group g and a group's slab is read with v_readlane (no LDS, no
+// barrier).
 template <int BPL, int D, int PER>
 __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, moe::RouteArgs ra, int n_waves) {
     const int H = a.H, I = a.I, nblk = H >> 5, k = a.k;
-    const int G = k + (a.shared ? 1 : 0);
+    const int hs = a.shared ? 1 : 0;
+    const int G = k + hs;
     const int Q = G * I;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -243,19 +259,83 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
 #pragma unroll
         for (int j = 0; j < 4; ++j) xd[b][j] = load_global_u4(a.x + 32 * (lane + 64 * b) + 8 * j);
 
-    int slot_e;
+    const uint8_t *shared_slab = (const uint8_t *)a.shared;
+    const uint32_t magic = moe_magic_vgpr();
+    const int w0 = blockIdx.x * 4 + wave;
+    const int n = w0 < Q ? (Q - w0 + n_waves - 1) / n_waves : 0;  // units of this wave
+    const int dg = n_waves / I, dr = n_waves - dg * I;              // cursor step in (group, row)
+    const size_t m13 = (size_t)I * H * 5 / 8;
+    const size_t cbytes = (size_t)I * H / 2;
+    const uint32_t code_off = 16u * lane, rec_off = 4u * lane;
+
+    uint4 c0[D][BPL], c1[D][BPL];
+    uint32_t p0[D][BPL], p1[D][BPL];
+    int ui = 0, gi = w0 / I, ri = w0 - gi * I;  // issue cursor, D units ahead
+    auto load_unit = [&](int j, const uint8_t *slab, int row) {
+        const uint8_t *w1 = slab + (size_t)row * (H / 2);
+        const uint8_t *r1 = slab + cbytes + (size_t)row * nblk * 4;
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            c0[j][b] = load_stream_u4(w1 + (code_off + 1024u * b));
+            p0[j][b] = load_stream_u32(r1 + (rec_off + 256u * b));
+            c1[j][b] = load_stream_u4(w1 + m13 + (code_off + 1024u * b));
+            p1[j][b] = load_stream_u32(r1 + m13 + (rec_off + 256u * b));
+        }
+    };
+    auto advance_issue = [&]() {
+        ++ui;
+        gi += dg;
+        ri += dr;
+        if (ri >= I) {
+            ri -= I;
+            ++gi;
+        }
+    };
+    // routing loads first (branch-free, indices clamped into range), so that
+    // waiting for them never waits for weight loads issued after them
+    int slot_e;  // lane s < k: expert of slot s
+    uint64_t tab[PER > 0 ? PER : 1];
+    moe_u32x4 pv[PER > 0 ? PER : 1][2];
+    float bv[PER > 0 ? PER : 1];
     if constexpr (PER > 0) {
+        typedef __attribute__((address_space(1))) const moe_u32x4 gvec;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int ec = min(lane + 64 * j, ra.E - 1);
+            const double *pp = ra.partial + (size_t)ec * moe::kMaxSlices;
+            pv[j][0] = *(gvec *)pp;
+            pv[j][1] = *(gvec *)(pp + 2);
+            tab[j] = (uint64_t)a.table[ec];
+            // no branch around the load: without a bias read any valid float and drop it
+            const float braw = (ra.bias ? ra.bias : (const float *)ra.partial)[ec];
+            bv[j] = ra.bias ? braw : 0.0f;
+        }
+    } else {
+        slot_e = lane < k ? a.topk_idx[lane] : 0;
+    }
+    // the first unit of a wave that starts on the shared expert goes out now
+    const bool early = MOE_DECODE1_EARLY && hs && n > 0 && gi == 0;
+    if (early) {
+        load_unit(0, shared_slab, ri);
+        advance_issue();
+    }
+    if constexpr (PER > 0) {
+        // wait for the routing loads only: the early unit's 4*BPL loads are younger
+        // (explicit counts, since the two paths leave different loads in flight)
+        if (early)
+            __builtin_amdgcn_s_waitcnt(kWaitVm(4 * BPL));
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitVm(0));
         const bool publish = blockIdx.x == 0 && wave == 0;
         uint32_t ord[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int e = lane + 64 * j;
-            ord[j] = 0u;
-            if (e < ra.E) {
-                const float l = moe::router_logit(ra.partial, ra.nslices, ra.bias, e);
-                if (publish) ra.logits[e] = l;
-                ord[j] = moe::topk_ord(l);
-            }
+            const double q[4] = {__hiloint2double(pv[j][0].y, pv[j][0].x), __hiloint2double(pv[j][0].w, pv[j][0].z),
+                                 __hiloint2double(pv[j][1].y, pv[j][1].x), __hiloint2double(pv[j][1].w, pv[j][1].z)};
+            const float l = moe::router_logit4(q, ra.nslices, bv[j]);
+            ord[j] = e < ra.E ? moe::topk_ord(l) : 0u;
+            if (publish && e < ra.E) ra.logits[e] = l;
         }
         float slot_logit;
         moe::topk_select(ord, k, slot_logit, slot_e);
@@ -264,14 +344,29 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
             ra.idx_out[lane] = slot_e;
             ra.w_out[lane] = w;
         }
-    } else {
-        slot_e = lane < k ? a.topk_idx[lane] : 0;
+    }
+    // lane g: the slab of group g
+    // (shuffles read only active lanes, so they run before any lane diverges)
+    const int src = min(max(lane - hs, 0), 63);
+    const int ge = __shfl(slot_e, src, 64);  // expert of group g (g >= hs)
+    uint64_t ge_slab = 0;
+    if constexpr (PER > 0) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)tab[j], ge & 63, 64);
+            const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(tab[j] >> 32), ge & 63, 64);
+            if ((ge >> 6) == j) ge_slab = ((uint64_t)hi << 32) | lo;
+        }
     }
     const uint8_t *mine = nullptr;
-    if (lane < k) {
-        if (!a.mask || a.mask[slot_e]) mine = (const uint8_t *)a.table[slot_e];
-    } else if (lane == k) {
-        mine = (const uint8_t *)a.shared;
+    if (lane < hs) {
+        mine = shared_slab;
+    } else if (lane < G) {
+        if constexpr (PER > 0) {
+            mine = (const uint8_t *)ge_slab;
+        } else {
+            if (!a.mask || a.mask[ge]) mine = (const uint8_t *)a.table[ge];
+        }
     }
     const uint64_t mv = (uint64_t)mine;
     const int mlo = (int)(uint32_t)mv, mhi = (int)(uint32_t)(mv >> 32);
@@ -284,17 +379,6 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
     if (present == 0) return;  // every group masked off
     const uint8_t *fallback = group_slab(__ffsll((long long)present) - 1);
 
-    const uint32_t magic = moe_magic_vgpr();
-    const int w0 = blockIdx.x * 4 + wave;
-    const int n = w0 < Q ? (Q - w0 + n_waves - 1) / n_waves : 0;  // units of this wave
-    const int dg = n_waves / I, dr = n_waves - dg * I;              // cursor step in (group, row)
-    const size_t m13 = (size_t)I * H * 5 / 8;
-    const size_t cbytes = (size_t)I * H / 2;
-    const uint32_t code_off = 16u * lane, rec_off = 4u * lane;
-
-    uint4 c0[D][BPL], c1[D][BPL];
-    uint32_t p0[D][BPL], p1[D][BPL];
-    int ui = 0, gi = w0 / I, ri = w0 - gi * I;  // issue cursor, D units ahead
     auto issue = [&](int j) {
         const uint8_t *slab = fallback;
         int row = 0;
@@ -305,25 +389,12 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
                 row = ri;
             }
         }
-        const uint8_t *w1 = slab + (size_t)row * (H / 2);
-        const uint8_t *r1 = slab + cbytes + (size_t)row * nblk * 4;
-#pragma unroll
-        for (int b = 0; b < BPL; ++b) {
-            c0[j][b] = load_stream_u4(w1 + (code_off + 1024u * b));
-            p0[j][b] = load_stream_u32(r1 + (rec_off + 256u * b));
-            c1[j][b] = load_stream_u4(w1 + m13 + (code_off + 1024u * b));
-            p1[j][b] = load_stream_u32(r1 + m13 + (rec_off + 256u * b));
-        }
-        ++ui;
-        gi += dg;
-        ri += dr;
-        if (ri >= I) {
-            ri -= I;
-            ++gi;
-        }
+        load_unit(j, slab, row);
+        advance_issue();
     };
+    if (!early) issue(0);
 #pragma unroll
-    for (int j = 0; j < D; ++j) issue(j);
+    for (int j = 1; j < D; ++j) issue(j);
 
     uint4 X[BPL][4];
     float S[BPL];
@@ -344,8 +415,10 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
                 }
                 v0 = moe_group_sum<64>(v0);
                 v1 = moe_group_sum<64>(v1);
-                if (lane == 63)  // h row: slot g, or the shared row k
-                    a.h[(size_t)g * I + r] = (uint16_t)f32_to_bf16_bits(v0 / (1.0f + expf(-v0)) * v1);
+                if (lane == 63) {  // h row: slot g - hs, or the shared row k
+                    const int hrow = g < hs ? k : g - hs;
+                    a.h[(size_t)hrow * I + r] = (uint16_t)f32_to_bf16_bits(v0 / (1.0f + expf(-v0)) * v1);
+                }
             }
             issue(j);  // slot j is free again: request the unit D ahead
             g += dg;
@@ -736,14 +809,15 @@ bool decode_supported(const FfnArgs &a) {
 
 bool decode1_routed_supported(const FfnArgs &a, int E) {
     const int nh = a.H >> 5;
-    return a.T == 1 && !a.grouped && a.k + (a.shared ? 1 : 0) <= kMaxGroups && E <= 256 &&
-           (nh == 128 || nh == 192 || nh == 64) && decode_supported(a);
+    // H <= 4096: at most four router slices, read in one go by the fused prologue
+    return a.T == 1 && !a.grouped && a.k + (a.shared ? 1 : 0) <= kMaxGroups && E <= 256 && a.H <= 4 * kSlice &&
+           (nh == 128 || nh == 64) && decode_supported(a);
 }
 
 int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s) {
+    if (ra.nslices > 4) return fail(MOE_E_SHAPE, "routed gate/up: H=%d above 4096", a.H);
     switch (a.H >> 5) {
         case 128: return launch_gate_up1<2, MOE_DECODE1_D>(a, &ra, s);
-        case 192: return launch_gate_up1<3, 3>(a, &ra, s);
         case 64: return launch_gate_up1<1, 6>(a, &ra, s);
         default: return fail(MOE_E_SHAPE, "routed gate/up: H=%d not supported", a.H);
     }

@@ -15,8 +15,17 @@ constexpr int kMaxSlices = 16;  // H <= 16384
 __device__ __forceinline__ float router_logit(const double *partial_t, int nslices, const float *bias, int e) {
     const double *p = partial_t + (size_t)e * kMaxSlices;
     double s = 0.0;
-    for (int q = 0; q < nslices; ++q) s += p[q];
+    for (int i = 0; i < nslices; ++i) s += p[i];
     return (float)(s + (bias ? (double)bias[e] : 0.0));
+}
+
+// The same rule for nslices <= 4 with the partials already loaded.
+__device__ __forceinline__ float router_logit4(const double (&q)[4], int nslices, float bias) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (i < nslices) s += q[i];
+    return (float)(s + (double)bias);
 }
 
 // Workspace layout of the router: 256-byte header, fp32 logits [T][E], then the

@@ -4,9 +4,9 @@
 //
 // Selection order: larger fp32 logit first, ties to the lower expert index
 // (-0 and +0 are equal).  Each logit is mapped to an order-preserving 32-bit
-// code; the wave maximum of the codes and then the minimum index among the
-// lanes holding that maximum are found with DPP row shifts and broadcasts, so a
-// selection round costs a few dozen VALU instructions and no LDS traffic.
+// code; the wave maximum of the codes is found with DPP row shifts and
+// broadcasts, and the lowest index holding it with a ballot, so a selection
+// round costs a few dozen instructions and no LDS traffic.
 #pragma once
 #include "common.h"
 
@@ -28,8 +28,8 @@ __device__ __forceinline__ float topk_logit(uint32_t ord) {
     return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
-// Wave-wide max / min of an unsigned value, returned in every lane (inclusive
-// scans inside 16-lane rows, then row broadcasts; lane 63 ends with the total).
+// Wave-wide max of an unsigned value, returned in every lane (inclusive scans
+// inside 16-lane rows, then row broadcasts; lane 63 ends with the total).
 __device__ __forceinline__ uint32_t topk_wave_max(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
@@ -37,17 +37,6 @@ __device__ __forceinline__ uint32_t topk_wave_max(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-__device__ __forceinline__ uint32_t topk_wave_min(uint32_t v) {
-    const int id = -1;  // 0xFFFFFFFF
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
@@ -69,7 +58,17 @@ __device__ __forceinline__ void topk_select(uint32_t (&ord)[PER], int k, float &
                 best_j = j;
             }
         const uint32_t top = topk_wave_max(best);
-        const uint32_t e = topk_wave_min(best == top ? (uint32_t)(lane + 64 * best_j) : 0xFFFFFFFFu);
+        // lowest index holding the maximum: lanes whose best sits in register j
+        // hold indices 64j + lane, so the first j with a match, then its lowest lane
+        uint32_t e = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const uint64_t m = __ballot(best == top && best_j == j);
+            if (m) {
+                e = 64u * j + (uint32_t)(__ffsll((long long)m) - 1);
+                break;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < PER; ++j)
             if ((uint32_t)(lane + 64 * j) == e) ord[j] = 0u;  // the owner drops the winner
