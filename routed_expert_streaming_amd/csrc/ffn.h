@@ -18,6 +18,8 @@ struct FfnArgs {
     const int32_t *pair_of_row; // [T*k]   (grouped)
     uint16_t *h;                // [T*k + T*shared, I] bf16 SwiGLU output
     float *y;                   // [T*k + T*shared, H] fp32 expert outputs
+    const uint8_t **pair_slab;  // [T*k + T*shared] or nullptr: slab of each pair (nullptr = masked),
+                                // written by the one-token gate/up kernel, read by the down kernel
 };
 
 // Router finish fused into the one-token gate/up kernel: the per-slice fp64
@@ -44,6 +46,8 @@ int decode_down(const FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_
 // One token with the router finished inside gate/up (a.topk_idx unused; the
 // down kernel must then read ra.idx_out / ra.w_out).
 bool decode1_routed_supported(const FfnArgs &a, int E);
+// True if decode_gate_up runs the one-token kernel, which fills a.pair_slab.
+bool decode1_publishes_slabs(const FfnArgs &a);
 int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s);
 
 // MFMA grouped GEMM (prefill): needs the expert grouping and H, I multiples of 128.

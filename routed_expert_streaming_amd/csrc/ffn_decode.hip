@@ -374,6 +374,8 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
         return (const uint8_t *)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(mhi, g) << 32) |
                                  (uint32_t)__builtin_amdgcn_readlane(mlo, g));
     };
+    if (a.pair_slab && blockIdx.x == 0 && wave == 0 && lane < G)  // pair order: slots, then shared
+        a.pair_slab[lane < hs ? k : lane - hs] = mine;
     // tail units and masked groups re-read row 0 of the first present slab
     const uint64_t present = __ballot(mine != nullptr);
     if (present == 0) return;  // every group masked off
@@ -395,6 +397,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
     if (!early) issue(0);
 #pragma unroll
     for (int j = 1; j < D; ++j) issue(j);
+    __builtin_amdgcn_sched_barrier(0);  // the ring requests go out before waiting for x
 
     uint4 X[BPL][4];
     float S[BPL];
@@ -598,10 +601,13 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
     const int P = k + (a.shared ? 1 : 0);
     __shared__ float part[kDown1MaxRows][kDown1MaxPairs + 1];
     __shared__ int present[kDown1MaxPairs];
+    __shared__ float wts[kDown1MaxPairs];
     const int lane = threadIdx.x & 63, sub = lane >> 4, c = lane & 15;
     const int p = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r0 = blockIdx.x * rows_per_wg;
     const int U = rows_per_wg >> 2;  // rows per 16-lane group
+    // routing weights requested now, stored to LDS just before the barrier
+    const float my_w = (COMBINE && lane < k) ? topk_w[lane] : 0.0f;
 
     uint4 hd[BPL][4];
 #pragma unroll
@@ -609,12 +615,16 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
 #pragma unroll
         for (int j = 0; j < 4; ++j) hd[b][j] = load_global_u4(a.h + (size_t)p * I + 32 * (c + 16 * b) + 8 * j);
 
+    // the pair's slab: the shared expert is known up front; a routed slot's slab
+    // was published by the gate/up kernel, else it is looked up
     const uint8_t *slab = nullptr;
-    if (p < k) {
-        const int e = a.topk_idx[p];
-        if (!a.mask || a.mask[e]) slab = (const uint8_t *)a.table[e];
-    } else {
+    if (p >= k) {
         slab = (const uint8_t *)a.shared;
+    } else if (a.pair_slab) {
+        slab = a.pair_slab[p];
+    } else {
+        const int e = a.topk_idx[p];
+        if (COMBINE || !a.mask || a.mask[e]) slab = (const uint8_t *)a.table[e];  // combine: no mask
     }
     slab = uniform_ptr(slab);
     if (lane == 0) present[p] = slab != nullptr;
@@ -640,6 +650,7 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
         };
 #pragma unroll
         for (int j = 0; j < D; ++j) issue(j);
+        __builtin_amdgcn_sched_barrier(0);  // the weight requests go out before waiting for h
 
         uint4 X[BPL][4];
         float S[BPL];
@@ -667,12 +678,13 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
         }
     }
     if (COMBINE) {
+        if (p == 0 && lane < k) wts[lane] = my_w;
         __syncthreads();
         const int t = threadIdx.x, row = r0 + t;
         if (t < rows_per_wg && row < H) {
             float acc = 0.0f;
             for (int g = 0; g < P; ++g)
-                if (present[g]) acc = g < k ? fmaf(topk_w[g], part[t][g], acc) : acc + part[t][g];
+                if (present[g]) acc = g < k ? fmaf(wts[g], part[t][g], acc) : acc + part[t][g];
             out[row] = (uint16_t)f32_to_bf16_bits(acc);
         }
     }
@@ -812,6 +824,11 @@ bool decode1_routed_supported(const FfnArgs &a, int E) {
     // H <= 4096: at most four router slices, read in one go by the fused prologue
     return a.T == 1 && !a.grouped && a.k + (a.shared ? 1 : 0) <= kMaxGroups && E <= 256 && a.H <= 4 * kSlice &&
            (nh == 128 || nh == 64) && decode_supported(a);
+}
+
+bool decode1_publishes_slabs(const FfnArgs &a) {
+    const int nh = a.H >> 5;
+    return a.T == 1 && !a.grouped && (nh == 128 || nh == 192 || nh == 64) && decode_supported(a);
 }
 
 int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s) {

@@ -130,7 +130,7 @@ extern "C" int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t
 namespace {
 
 struct FfnLayout {
-    size_t h, count, offset, pairs, y, total;
+    size_t h, count, offset, pairs, y, slabs, total;
 };
 
 FfnLayout ffn_layout(int T, int H, int I, int E, int k, int has_shared) {
@@ -147,6 +147,8 @@ FfnLayout ffn_layout(int T, int H, int I, int E, int k, int has_shared) {
     o += moe::align_up((size_t)T * k * sizeof(int32_t), 256);
     L.y = o;
     o += moe::align_up(P * H * sizeof(float), 256);
+    L.slabs = o;
+    o += moe::align_up(P * sizeof(void *), 256);
     L.total = o;
     return L;
 }
@@ -316,6 +318,7 @@ extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, in
                        shared_slab, nullptr, MOE_FFN_PAIRS, &max_m, "expert_ffn_combine");
         if (rc != MOE_OK) return rc;
         if (moe::decode_supported(a)) {
+            if (moe::decode1_publishes_slabs(a)) a.pair_slab = (const uint8_t **)(ws + Ly.slabs);
             rc = moe::decode_gate_up(a, s);
             if (rc != MOE_OK) return rc;
             return moe::decode_down(a, topk_w, out, s);
@@ -363,6 +366,7 @@ extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, con
         if (rc != MOE_OK) return rc;
         const moe::RouteArgs ra{partial, bias, E, (H + moe::kSlice - 1) / moe::kSlice, moe::router_logits(rws),
                                 topk_idx, topk_w};
+        a.pair_slab = (const uint8_t **)(fws + Ly.slabs);
         rc = moe::decode1_routed_gate_up(a, ra, s);
         if (rc != MOE_OK) return rc;
         return moe::decode_down(a, topk_w, out, s);
