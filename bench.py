@@ -4,7 +4,8 @@ Default workload: batch-1 decode through 8 routed-MoE layers (hidden 4096, 128
 experts + 1 shared, intermediate 1536, top-8, 4-bit 32-column blocks), every
 expert resident in HBM.  One step = router + top-k, expert lookup (device
 pointer table), fused dequant + gate/up + SwiGLU, dequant + down, weighted
-combine, for all 8 layers, on one token.
+combine, for all 8 layers, on one token: one moe_route_ffn_combine call per
+layer (three kernels), replayed from HIP graphs.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode1]
 
@@ -290,9 +291,12 @@ def main():
                    "hidden": cfg.hidden, "inter": cfg.inter, "experts": cfg.experts, "shared": cfg.shared,
                    "top_k": cfg.top_k, "resident": True, "graph": graphs is not None,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "decode_gate_up_kernel (dequant + gate/up + SwiGLU)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode1_gate_up_kernel<2, 4, 0> (dequant + gate/up + SwiGLU, launched alone "
+                               "through moe_expert_gate_up; in the step the same kernel also finishes the top-k)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("decode_gate_up_kernel"),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("decode1_gate_up_kernel<2, 4, 0>"),
                      "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},
         "ffn": {"bytes_per_step": ffn_bytes_step, "kernel_us_per_step": round(ffn_us_step, 2),
                 "achieved_GBps": round(ffn_bytes_step / (ffn_us_step * 1e-6) / 1e9, 1),

@@ -1,10 +1,13 @@
 """Summarise a rocprofv3 result database (rocpd SQLite) as plain text.
 
-  python -m routed_expert_streaming_amd.rocprof_summary RESULTS.db [--counters]
+  python -m routed_expert_streaming_amd.rocprof_summary RESULTS.db [--counters | --timeline]
 
 Prints one line per kernel: dispatches, average / min / max duration, share of
 GPU time, grid, workgroup size and VGPRs; with --counters, the average of every
-PMC counter per kernel (as collected by ``rocprofv3 --pmc ...``).
+PMC counter per kernel (as collected by ``rocprofv3 --pmc ...``); with
+--timeline, per kernel the average duration and the average idle gap between
+the end of the previous dispatch and its start (over the last two thirds of the
+trace, gaps under 20 us, so set-up and host pauses are left out).
 """
 from __future__ import annotations
 
@@ -47,11 +50,33 @@ def counter_stats(db: str):
     return {k: {ctr: sum(v) / len(v) for ctr, v in d.items()} for k, d in agg.items()}
 
 
+def timeline_stats(db: str):
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, start, end from kernels order by start").fetchall()
+    dur = collections.defaultdict(list)
+    gap = collections.defaultdict(list)
+    prev_end = None
+    for name, start, end in rows[len(rows) // 3:]:
+        k = short_name(name)
+        dur[k].append(end - start)
+        if prev_end is not None and 0 <= start - prev_end < 20000:
+            gap[k].append(start - prev_end)
+        prev_end = end
+    return [(k, len(d), sum(d) / len(d) / 1e3, (sum(gap[k]) / len(gap[k]) / 1e3) if gap[k] else 0.0)
+            for k, d in dur.items()]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("db")
     ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--timeline", action="store_true")
     args = ap.parse_args()
+    if args.timeline:
+        print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'gap_before_us':>14s}")
+        for k, n, d, g in timeline_stats(args.db):
+            print(f"{k[:60]:60s} {n:6d} {d:9.3f} {g:14.3f}")
+        return
     if args.counters:
         for k, d in sorted(counter_stats(args.db).items()):
             print(f"{k}")
