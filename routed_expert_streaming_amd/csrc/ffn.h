@@ -28,7 +28,7 @@ struct RouteArgs {
     const double *partial;  // [E][kMaxSlices] partial logits of the token
     const float *bias;      // [E] or nullptr
     int E, nslices;
-    float *logits;          // [E] fp32 logits (written by workgroup 0)
+    float *logits;          // [E] fp32 logits (written by one wave of the kernel)
     int32_t *idx_out;       // [k] selected experts
     float *w_out;           // [k] their renormalised weights
 };

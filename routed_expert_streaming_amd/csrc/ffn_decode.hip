@@ -236,7 +236,7 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 // Routing: with PER = 0 the k slots come from a.topk_idx; with PER > 0 every
 // wave finishes the router itself from the per-slice fp64 partial logits
 // (same fp32 logits, same top-k and softmax as the router entry point) and
-// workgroup 0 publishes idx / weights / logits for the down kernel and the
+// one wave publishes idx / weights / logits for the down kernel and the
 // caller.  The expert table is loaded alongside the partials, so resolving a
 // slot's slab is a lane shuffle rather than another trip to memory.
 //
@@ -326,7 +326,9 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
             __builtin_amdgcn_s_waitcnt(kWaitVm(4 * BPL));
         else
             __builtin_amdgcn_s_waitcnt(kWaitVm(0));
-        const bool publish = blockIdx.x == 0 && wave == 0;
+        // the grid's last wave (one of those with the fewest units) publishes the
+        // routing; only it needs the softmax
+        const bool publish = w0 == n_waves - 1;
         uint32_t ord[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -339,10 +341,12 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
         }
         float slot_logit;
         moe::topk_select(ord, k, slot_logit, slot_e);
-        const float w = moe::topk_softmax(slot_logit, k);
-        if (publish && lane < k) {
-            ra.idx_out[lane] = slot_e;
-            ra.w_out[lane] = w;
+        if (publish) {
+            const float w = moe::topk_softmax(slot_logit, k);
+            if (lane < k) {
+                ra.idx_out[lane] = slot_e;
+                ra.w_out[lane] = w;
+            }
         }
     }
     // lane g: the slab of group g
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
         return (const uint8_t *)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(mhi, g) << 32) |
                                  (uint32_t)__builtin_amdgcn_readlane(mlo, g));
     };
-    if (a.pair_slab && blockIdx.x == 0 && wave == 0 && lane < G)  // pair order: slots, then shared
+    if (a.pair_slab && w0 == n_waves - 1 && lane < G)  // pair order: slots, then shared
         a.pair_slab[lane < hs ? k : lane - hs] = mine;
     // tail units and masked groups re-read row 0 of the first present slab
     const uint64_t present = __ballot(mine != nullptr);
@@ -782,7 +786,7 @@ int launch_down(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipSt
 #define MOE_DOWN1_ROWS 16 // rows per workgroup, one-token down kernel
 #endif
 #ifndef MOE_DOWN1_D
-#define MOE_DOWN1_D 2  // units in flight per lane group, one-token down kernel
+#define MOE_DOWN1_D 1  // units in flight per lane group, one-token down kernel
 #endif
 
 template <int BPL>
@@ -816,7 +820,7 @@ bool decode_supported(const FfnArgs &a) {
 }
 
 #ifndef MOE_DECODE1_D
-#define MOE_DECODE1_D 4  // units in flight per wave, one-token gate/up
+#define MOE_DECODE1_D 2  // units in flight per wave, one-token gate/up (H = 4096)
 #endif
 
 bool decode1_routed_supported(const FfnArgs &a, int E) {
