@@ -5,7 +5,8 @@ experts + 1 shared, intermediate 1536, top-8, 4-bit 32-column blocks), every
 expert resident in HBM.  One step = router + top-k, expert lookup (device
 pointer table), fused dequant + gate/up + SwiGLU, dequant + down, weighted
 combine, for all 8 layers, on one token: one moe_route_ffn_combine call per
-layer (three kernels), replayed from HIP graphs.
+layer (three kernels), launched eagerly (the host stays ahead of the GPU; with
+--graph, one HIP graph per step is replayed instead).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode1]
 
@@ -41,7 +42,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode1")
     ap.add_argument("--inputs", type=int, default=8, help="distinct resident input steps cycled through")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one HIP graph per step instead of launching eagerly (each replay boundary leaves "
+                         "the GPU idle ~8 us, more than the eager launches cost)")
     ap.add_argument("--kernel-iters", type=int, default=50, help="iterations of the per-kernel event timing")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,12 +201,12 @@ def main():
     log(f"built in {time.time() - t0:.1f}s")
     dev_stream = torch.cuda.current_stream()
 
-    # warm-up (eager), then capture one graph per resident input
+    # warm-up (eager); with --graph, capture one graph per resident input
     for i in range(max(args.warmup, 1)):
         stack.forward(xs[i % args.inputs], outs[i % args.inputs])
     torch.cuda.synchronize()
     graphs = None
-    if not args.no_graph:
+    if args.graph:
         graphs = []
         for i in range(args.inputs):
             g = torch.cuda.CUDAGraph()
