@@ -408,11 +408,21 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
 #pragma unroll
     for (int b = 0; b < BPL; ++b) S[b] = block_pairs(xd[b], X[b]);
 
+    // Each unit's two sums go to lane (unit index mod 64); SiLU, rounding and the
+    // store then run once for up to 64 units in parallel instead of once per unit
+    // in a single lane (same arithmetic, so the same bits).
+    float sg = 0.0f, su = 0.0f;
+    int hoff = -1;  // h element of this lane's pending unit, -1: none
+    auto flush = [&]() {
+        if (hoff >= 0) a.h[hoff] = (uint16_t)f32_to_bf16_bits(sg / (1.0f + expf(-sg)) * su);
+        hoff = -1;
+    };
     int g = w0 / I, r = w0 - g * I;  // compute cursor
     for (int base = 0; base < n; base += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            if (base + j >= n) break;
+            const int u = base + j;
+            if (u >= n) break;
             if (group_slab(g)) {
                 float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
@@ -422,12 +432,16 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
                 }
                 v0 = moe_group_sum<64>(v0);
                 v1 = moe_group_sum<64>(v1);
-                if (lane == 63) {  // h row: slot g - hs, or the shared row k
-                    const int hrow = g < hs ? k : g - hs;
-                    a.h[(size_t)hrow * I + r] = (uint16_t)f32_to_bf16_bits(v0 / (1.0f + expf(-v0)) * v1);
+                const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v0), 63));
+                const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v1), 63));
+                if (lane == (u & 63)) {  // h row: slot g - hs, or the shared row k
+                    sg = t0;
+                    su = t1;
+                    hoff = (g < hs ? k : g - hs) * I + r;
                 }
             }
             issue(j);  // slot j is free again: request the unit D ahead
+            if ((u & 63) == 63) flush();
             g += dg;
             r += dr;
             if (r >= I) {
@@ -436,6 +450,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
             }
         }
     }
+    flush();
 }
 
 // ---------------------------------------------------------------- down (+ combine)
