@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 
 
 def log(msg):
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--stream-workload", default="decode1_stream")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
+    ap.add_argument("--no-layer-legs", action="store_true",
+                    help="skip the one-resident-layer measurements of the 32-token decode and 2048-token prefill shapes")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run 4 plain 256 MiB device copies (reference for HBM traffic counters)")
     return ap.parse_args()
@@ -126,6 +129,69 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
            "exposed_ms_per_step": round(ms_step - copy_ms, 3),
            "steps": args.stream_steps, "warmup": args.stream_warmup}
     log(f"streaming: {res}")
+    return res
+
+
+def layer_leg(torch, name: str, path: int, iters: int):
+    """One resident layer of a multi-token configuration (every expert in HBM, no
+    PCIe): each kernel of the layer timed alone with events over `iters` launches.
+    Algorithmic bytes = the slabs of the experts the tokens use (+ shared) plus
+    activations; flops = 2·3·H·I per (token, expert) pair."""
+    import synth
+    from routed_expert_streaming_amd import _lib as L
+    from routed_expert_streaming_amd.runtime import MoEStack
+
+    cfg = synth.get(name)
+    st = MoEStack(cfg, cap=1.0, layers=1)
+    T, H, I, E, k = cfg.tokens, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
+    x = st.make_inputs(0)
+    out = st.new_output()
+    st.route(x, 0)
+    P = T * k + (T if st.has_shared else 0)
+    h = torch.empty((P, I), dtype=torch.bfloat16, device="cuda")
+    cnt = torch.empty(E, dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    por = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    shared = st.shared[0] if st.has_shared else None
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    res = {"workload": f"{name}, one resident layer", "tokens": T, "path": {L.MOE_FFN_MFMA: "mfma",
+                                                                              L.MOE_FFN_GROUPED: "grouped"}[path]}
+    res["router_ms"] = timed(lambda: st.route(x, 0))
+    res["permute_ms"] = timed(lambda: L.moe_permute(st.idx[0], T, k, E, cnt, off, por))
+    res["gate_up_ms"] = timed(lambda: L.moe_expert_gate_up(x[0], T, H, I, E, st.idx[0], k, cnt, off, por,
+                                                           st.table[0], shared, None, h, path))
+    res["down_ms"] = timed(lambda: L.moe_expert_down(h, T, H, I, E, st.idx[0], k, cnt, off, por, st.table[0],
+                                                     shared, None, st.y, path))
+    res["combine_ms"] = timed(lambda: st.combine(0, out))
+    res["layer_ms"] = timed(lambda: (st.route(x, 0), st.ffn_combine(x, 0, out)))
+    idx = st.idx[0].cpu().numpy()
+    n_exp = len(set(int(e) for e in idx.ravel())) + (1 if st.has_shared else 0)
+    w_bytes = n_exp * st.slab
+    flops = 2 * 3 * H * I * P
+    ffn_ms = res["gate_up_ms"] + res["down_ms"]
+    res.update({"experts_used": n_exp, "weight_bytes": w_bytes, "ffn_flops": flops,
+                "ffn_weights_GBps": round(w_bytes / (ffn_ms * 1e-3) / 1e9, 1),
+                "ffn_TFLOPs": round(flops / (ffn_ms * 1e-3) / 1e12, 2),
+                "hbm_frac": round(w_bytes / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "bf16_mfma_frac": round(flops / (ffn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)})
+    for key in list(res):
+        if key.endswith("_ms"):
+            res[key] = round(res[key], 4)
+    st.close()
+    del st, x, out, h
+    torch.cuda.empty_cache()
+    log(f"layer leg: {res}")
     return res
 
 
@@ -332,6 +398,10 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_stream:
         result["streaming"] = streaming_leg(torch, args, ms_per_step)
+    if not args.no_layer_legs:
+        from routed_expert_streaming_amd import _lib as L
+        result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_GROUPED, 20)
+        result["layer_prefill2048"] = layer_leg(torch, "prefill2048_stream", L.MOE_FFN_MFMA, 3)
     print(json.dumps(result), flush=True)
 
 
