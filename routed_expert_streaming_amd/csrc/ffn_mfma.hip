@@ -39,11 +39,11 @@ constexpr int kXcds = 8;       // workgroups are dealt to the XCDs round-robin
 static_assert(kMC * (kKC * 2 / 16) % 256 == 0, "activation tile loads must divide over the workgroup");
 
 struct MfmaBuf {
-    uint8_t x[kMC * kXStride];    // activation tile, bf16, natural column order
+    __attribute__((aligned(16))) uint8_t x[kMC * kXStride];  // activation tile, bf16, natural column order
     uint8_t w[2][kNT * kWStride]; // code tiles (W1, W3) or (W2, -)
     uint2 p[2][kNT];              // (scale, min) records of the chunk's 2 blocks per row
 };
-struct MfmaLds {
+struct __attribute__((aligned(16))) MfmaLds {  // 16-byte aligned: A operands load with ds_read_b128
     MfmaBuf buf[2];
     int src[kMC];                 // activation row of each M row (-1 = padding)
     int dst[kMC];                 // output row of each M row

@@ -11,8 +11,8 @@
 //  * small T (decode, T <= 32): one wavefront per (expert, H slice) streams
 //    that piece of the router row once for every token, then one wavefront per
 //    token sums the slices in order and runs the top-k;
-//  * large T (prefill): 64x64 register-tiled fp64 product through LDS, then a
-//    top-k kernel with one wavefront per token.
+//  * large T (prefill): the product on the fp64 matrix cores (32 x 32 tiles),
+//    then a top-k kernel with one wavefront per token.
 #include "common.h"
 #include "router.h"
 #include "topk.h"
@@ -110,54 +110,74 @@ __global__ __launch_bounds__(256) void router_finalize_kernel(const double *__re
 }
 
 // ---------------------------------------------------------------- large T
-constexpr int kTT = 64, kTE = 64, kTK = 16;
+// Prefill router on the fp64 matrix cores: logits[t][e] = sum_h x[t][h] Wr[e][h]
+// + bias[e] with every product exact in fp64 (v_mfma_f64_16x16x4_f64), summed in
+// fp64 and rounded once to fp32.  A workgroup owns 32 tokens x 32 experts; each
+// wave one 16 x 16 tile.  K streams in chunks of 64 columns through two LDS
+// buffers (x and Wr converted to fp64 on the way in, exact); the next chunk's
+// loads are in flight in registers while the current one is multiplied.
+// Lane layout of v_mfma_f64_16x16x4_f64 (checked on gfx950): lane l holds
+// A[l%16][l/16], B[l/16][l%16], and C[4*j + l/16][l%16] for j < 4.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRT = 32, kRE = 32, kRK = 64, kRStride = kRK + 1;  // fp64 LDS rows padded by one
 
-__global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__restrict__ x, int T, int H,
-                                                           const float *__restrict__ wr,
-                                                           const float *__restrict__ bias, int E,
-                                                           float *__restrict__ logits) {
-    __shared__ double xs[kTK][kTT];
-    __shared__ double ws[kTK][kTE];
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
-    const int t0 = blockIdx.x * kTT, e0 = blockIdx.y * kTE;
-    double acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int k0 = 0; k0 < H; k0 += kTK) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int id = tid + 256 * r;
-            int row = id >> 4, kk = id & 15;
-            int t = t0 + row, e = e0 + row;
-            xs[kk][row] = (t < T) ? (double)bf16_bits_to_f32(x[(size_t)t * H + k0 + kk]) : 0.0;
-            ws[kk][row] = (e < E) ? (double)wr[(size_t)e * H + k0 + kk] : 0.0;
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__restrict__ x, int T, int H,
+                                                          const float *__restrict__ wr,
+                                                          const float *__restrict__ bias, int E,
+                                                          float *__restrict__ logits) {
+    __shared__ double xs[2][kRT * kRStride];
+    __shared__ double ws[2][kRE * kRStride];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
+    const int nchunks = (H + kRK - 1) / kRK;
+    // one chunk per thread: 8 bf16 of x (row tid/8, cols 8*(tid%8)..) and 8 fp32 of Wr
+    const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+    uint4 xv, wv0, wv1;
+    auto load = [&](int c) {
+        const int k = c * kRK + lcol, t = t0 + lrow, e = e0 + lrow;
+        xv = (t < T && k < H) ? *reinterpret_cast<const uint4 *>(x + (size_t)t * H + k) : make_uint4(0u, 0u, 0u, 0u);
+        if (e < E && k < H) {
+            wv0 = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + k);
+            wv1 = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + k + 4);
+        } else {
+            wv0 = wv1 = make_uint4(0u, 0u, 0u, 0u);
         }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < kTK; ++kk) {
-            double a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int t = t0 + ty * 4 + i;
-        if (t >= T) continue;
+    };
+    auto store = [&](int b) {
+        double *xr = &xs[b][lrow * kRStride + lcol];
+        double *wq = &ws[b][lrow * kRStride + lcol];
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            int e = e0 + tx * 4 + j;
-            if (e < E) logits[(size_t)t * E + e] = (float)(acc[i][j] + (bias ? (double)bias[e] : 0.0));
+            xr[2 * j] = (double)bf16_bits_to_f32(xw[j] & 0xFFFFu);
+            xr[2 * j + 1] = (double)bf16_bits_to_f32(xw[j] >> 16);
+        }
+        const uint32_t ww[8] = {wv0.x, wv0.y, wv0.z, wv0.w, wv1.x, wv1.y, wv1.z, wv1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wq[j] = (double)__uint_as_float(ww[j]);
+    };
+    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nchunks) load(c + 1);
+        const double *xa = &xs[b][(wm * 16 + (lane & 15)) * kRStride + (lane >> 4)];
+        const double *wb = &ws[b][(wn * 16 + (lane & 15)) * kRStride + (lane >> 4)];
+#pragma unroll
+        for (int kk = 0; kk < kRK / 4; ++kk) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[4 * kk], wb[4 * kk], acc, 0, 0, 0);
+        if (c + 1 < nchunks) store(b ^ 1);
+        __syncthreads();
+    }
+    const int e = e0 + wn * 16 + (lane & 15);
+    if (e < E) {
+        const double bb = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = t0 + wm * 16 + 4 * j + (lane >> 4);
+            if (t < T) logits[(size_t)t * E + e] = (float)(acc[j] + bb);
         }
     }
 }
@@ -248,9 +268,9 @@ extern "C" int moe_router_topk(const uint16_t *x, int T, int H, const float *w_r
         MOE_LAUNCH_CHECK("router_finalize_kernel");
         return MOE_OK;
     }
-    dim3 grid((T + kTT - 1) / kTT, (E + kTE - 1) / kTE);
-    hipLaunchKernelGGL(router_tiled_kernel, grid, block, 0, s, x, T, H, w_router, bias, E, logits);
-    MOE_LAUNCH_CHECK("router_tiled_kernel");
+    dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
+    hipLaunchKernelGGL(router_mfma_kernel, grid, block, 0, s, x, T, H, w_router, bias, E, logits);
+    MOE_LAUNCH_CHECK("router_mfma_kernel");
     hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), block, 0, s, logits, T, E, k, topk_idx, topk_w);
     MOE_LAUNCH_CHECK("router_topk_kernel");
     return MOE_OK;
