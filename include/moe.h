@@ -102,7 +102,8 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *count, in
  * compute).  Per layer there are `slots_per_layer` slots of moe_expert_bytes(H,I)
  * bytes in `slot_pool` (layer l's slots start at l * slots * slab bytes).
  * expert_table: device array [n_layers * n_experts] of slab pointers the library
- * keeps current on the copy stream (NULL = not resident); kernels read layer l's
+ * keeps current on the compute stream of each prefetch, after that layer's copies
+ * (NULL = not resident); kernels read layer l's
  * entries at expert_table + l * n_experts.  experts_host: host array
  * [n_layers * n_experts] of pinned host slab pointers.  The caller owns the
  * pool, the table and the host slabs, which must outlive the cache.
@@ -129,8 +130,9 @@ int moe_cache_lookup(moe_cache *cache, int layer, const int32_t *experts_host, i
                      int *n_hits);
 /* Acquire n distinct experts of `layer` (n <= slots, else MOE_E_CAPACITY): touch
    hits, pick victims, enqueue on the copy stream each victim's wait for its last
-   release, the H2D copy of each missed slab and the table update, then make
-   `compute_stream` wait for them.  *n_copies (may be NULL) = misses streamed.
+   release and the H2D copy of each missed slab, make `compute_stream` wait for
+   them, then enqueue the table update on `compute_stream` (the copy stream carries
+   DMA copies and event records only).  *n_copies (may be NULL) = misses streamed.
    The acquired slots stay held until moe_cache_release(layer).  On a HIP failure
    the slots being filled are left empty (their experts are misses again). */
 int moe_cache_prefetch(moe_cache *cache, int layer, const int32_t *experts_host, int n,

@@ -50,6 +50,12 @@ struct Engine {
     virtual int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
                       const std::vector<int> &slots) = 0;
     virtual int ready(int layer, void *compute_stream) = 0;
+    // Table writes that must land now, on the copy stream (a prefetch that failed
+    // part-way keeps the table equal to what is resident, without a ready()).
+    virtual int table_now(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
+                          const std::vector<int> &slots) {
+        return table(layer, experts, ptrs, slots);
+    }
     virtual int release(int layer, long long release_id, int n_slots, void *compute_stream) = 0;
     virtual int sync() = 0;
     virtual int clear_table() = 0;
@@ -61,6 +67,9 @@ struct HipEngine final : Engine {
     const void **tbl = nullptr;
     std::vector<hipEvent_t> ready_ev;    // [L]
     std::vector<hipEvent_t> release_ev;  // [L * kReleaseRing]
+    int pending_layer = -1;              // table writes waiting for ready()
+    std::vector<int> pending_experts;
+    std::vector<const void *> pending_ptrs;
 
     int init(int layers, int experts, hipStream_t cs, void **table_dev) {
         L = layers;
@@ -88,8 +97,11 @@ struct HipEngine final : Engine {
         MOE_TRY_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, copy_stream));
         return MOE_OK;
     }
-    int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
-              const std::vector<int> &) override {
+    // Table writes wait for the layer's copies and run on the compute stream just
+    // before the layer's kernels, so the copy stream carries only DMA copies and
+    // event records (a kernel between two copies would stall the copy engine).
+    int launch_updates(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
+                       hipStream_t st) {
         for (size_t i = 0; i < experts.size(); i += kTableBatch) {
             TableUpdate u{};
             u.n = (int)std::min<size_t>(kTableBatch, experts.size() - i);
@@ -97,16 +109,35 @@ struct HipEngine final : Engine {
                 u.experts[j] = experts[i + j];
                 u.ptrs[j] = ptrs[i + j];
             }
-            hipLaunchKernelGGL(table_update_kernel, dim3(1), dim3(kTableBatch), 0, copy_stream,
-                               tbl + (size_t)layer * E, u);
+            hipLaunchKernelGGL(table_update_kernel, dim3(1), dim3(kTableBatch), 0, st, tbl + (size_t)layer * E, u);
             MOE_LAUNCH_CHECK("table_update_kernel");
         }
         return MOE_OK;
     }
-    int ready(int layer, void *compute_stream) override {
-        MOE_TRY_HIP(hipEventRecord(ready_ev[layer], copy_stream));
-        MOE_TRY_HIP(hipStreamWaitEvent((hipStream_t)compute_stream, ready_ev[layer], 0));
+    int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
+              const std::vector<int> &) override {
+        pending_layer = layer;
+        pending_experts = experts;
+        pending_ptrs = ptrs;
         return MOE_OK;
+    }
+    int table_now(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
+                  const std::vector<int> &) override {
+        pending_layer = -1;
+        pending_experts.clear();
+        pending_ptrs.clear();
+        return launch_updates(layer, experts, ptrs, copy_stream);
+    }
+    int ready(int layer, void *compute_stream) override {
+        hipStream_t cs = (hipStream_t)compute_stream;
+        MOE_TRY_HIP(hipEventRecord(ready_ev[layer], copy_stream));
+        MOE_TRY_HIP(hipStreamWaitEvent(cs, ready_ev[layer], 0));
+        int rc = MOE_OK;
+        if (pending_layer == layer) rc = launch_updates(layer, pending_experts, pending_ptrs, cs);
+        pending_layer = -1;
+        pending_experts.clear();
+        pending_ptrs.clear();
+        return rc;
     }
     int release(int layer, long long id, int, void *compute_stream) override {
         MOE_TRY_HIP(hipEventRecord(release_ev[(size_t)layer * kReleaseRing + id % kReleaseRing],
@@ -383,7 +414,7 @@ extern "C" int moe_cache_prefetch(moe_cache *c, int layer, const int32_t *expert
     }
     if (rc != MOE_OK) {
         // keep the table consistent with what is resident, then un-hold this request
-        (void)c->engine->table(layer, t_exp, t_ptr, t_slot);
+        (void)c->engine->table_now(layer, t_exp, t_ptr, t_slot);
         for (int s : acquired) held[s] = 0;
         return rc;
     }
