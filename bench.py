@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+# the one-token gate/up kernel as launched alone (units per lane, ring depth, no routing)
+GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 2, 0>"
 
 
 def log(msg):
@@ -361,11 +363,11 @@ def main():
                    "top_k": cfg.top_k, "resident": True, "graph": graphs is not None,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
-                     "kernel": "decode1_gate_up_kernel<2, 4, 0> (dequant + gate/up + SwiGLU, launched alone "
+                     "kernel": f"{GATE_UP_KERNEL} (dequant + gate/up + SwiGLU, launched alone "
                                "through moe_expert_gate_up; in the step the same kernel also finishes the top-k)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic("decode1_gate_up_kernel<2, 4, 0>"),
+                     "traffic": counter_traffic(GATE_UP_KERNEL),
                      "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},
         "ffn": {"bytes_per_step": ffn_bytes_step, "kernel_us_per_step": round(ffn_us_step, 2),
                 "achieved_GBps": round(ffn_bytes_step / (ffn_us_step * 1e-6) / 1e9, 1),

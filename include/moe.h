@@ -86,6 +86,19 @@ size_t moe_router_workspace_bytes(int T, int E);
 int moe_router_topk(const uint16_t *x, int T, int H, const float *w_router, const float *bias, int E,
                     int k, int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes,
                     void *stream);
+/* The same router for n_layers independent layers in one call (a streamed step
+   routes every layer first, then plans its copies; LayerStoRm README "TL;DR":
+   the router output decides what is streamed).  Layer l reads x + l*T*H,
+   w_router + l*E*H, bias + l*E (bias NULL = none for every layer) and writes
+   topk_idx / topk_w + l*T*k; each layer's result is bit-identical to
+   moe_router_topk on that layer.  Workspace: moe_router_layers_workspace_bytes
+   (n_layers, T, E) bytes; layer l's fp32 logits start at byte
+   l * align_up(moe_router_workspace_bytes(T, E), 256) + 256.  n_layers <= 65535;
+   n_layers == 0 or T == 0 enqueues nothing. */
+size_t moe_router_layers_workspace_bytes(int n_layers, int T, int E);
+int moe_router_topk_layers(const uint16_t *x, int n_layers, int T, int H, const float *w_router,
+                           const float *bias, int E, int k, int32_t *topk_idx, float *topk_w, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ dispatch
  * Token -> expert permutation of the T*k (token, slot) pairs p = t*k + i:
@@ -101,10 +114,10 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *count, in
  * set is pinned in host RAM, GPU memory is used as a cache, streaming overlaps
  * compute).  Per layer there are `slots_per_layer` slots of moe_expert_bytes(H,I)
  * bytes in `slot_pool` (layer l's slots start at l * slots * slab bytes).
- * expert_table: device array [n_layers * n_experts] of slab pointers the library
- * keeps current on the compute stream of each prefetch, after that layer's copies
- * (NULL = not resident); kernels read layer l's
- * entries at expert_table + l * n_experts.  experts_host: host array
+ * expert_table: device array [n_layers * n_experts] of slab pointers (NULL = not
+ * resident) the library keeps current: a layer's entries are written on the
+ * compute stream by moe_cache_wait, after that layer's copies; kernels read layer
+ * l's entries at expert_table + l * n_experts.  experts_host: host array
  * [n_layers * n_experts] of pinned host slab pointers.  The caller owns the
  * pool, the table and the host slabs, which must outlive the cache.
  * LRU rule per layer: a request touches its hits first (ascending expert id),
@@ -128,17 +141,26 @@ int moe_cache_create(const moe_cache_desc *desc, const void *const *experts_host
 /* Query only: slot_host[i] = slot of experts_host[i] or -1, *n_hits = number resident. */
 int moe_cache_lookup(moe_cache *cache, int layer, const int32_t *experts_host, int n, int32_t *slot_host,
                      int *n_hits);
-/* Acquire n distinct experts of `layer` (n <= slots, else MOE_E_CAPACITY): touch
-   hits, pick victims, enqueue on the copy stream each victim's wait for its last
-   release and the H2D copy of each missed slab, make `compute_stream` wait for
-   them, then enqueue the table update on `compute_stream` (the copy stream carries
-   DMA copies and event records only).  *n_copies (may be NULL) = misses streamed.
-   The acquired slots stay held until moe_cache_release(layer).  On a HIP failure
-   the slots being filled are left empty (their experts are misses again). */
+/* Copy half of a prefetch.  Acquire n distinct experts of `layer` (n <= slots,
+   else MOE_E_CAPACITY): touch hits, pick victims, enqueue on the copy stream each
+   victim's wait for its last release and the H2D copy of each missed slab, and
+   keep the layer's table writes for moe_cache_wait.  The copy stream carries only
+   DMA copies and event records, so copies of several layers can be queued ahead
+   of their kernels.  *n_copies (may be NULL) = misses streamed.  The acquired
+   slots stay held until moe_cache_release(layer).  On a HIP failure the slots
+   being filled are left empty (their experts are misses again) and the table
+   writes made so far are enqueued on the copy stream at once. */
+int moe_cache_prefetch_async(moe_cache *cache, int layer, const int32_t *experts_host, int n, int *n_copies);
+/* Compute half: makes `compute_stream` wait for every copy of `layer` enqueued so
+   far, then enqueues the layer's pending table writes on it.  A no-op when
+   nothing is pending.  Call it before the kernels that read the layer's table. */
+int moe_cache_wait(moe_cache *cache, int layer, void *compute_stream);
+/* moe_cache_prefetch_async followed by moe_cache_wait. */
 int moe_cache_prefetch(moe_cache *cache, int layer, const int32_t *experts_host, int n,
                        void *compute_stream, int *n_copies);
 /* Records on `compute_stream` that every slot held by `layer` may be overwritten
-   once the work enqueued so far on that stream is done, and un-holds them. */
+   once the work enqueued so far on that stream is done, and un-holds them.
+   MOE_E_STATE if the layer has copies that no moe_cache_wait has covered. */
 int moe_cache_release(moe_cache *cache, int layer, void *compute_stream);
 /* Cumulative hit / miss counts (per requested expert) and H2D bytes streamed. */
 int moe_cache_stats(const moe_cache *cache, uint64_t *hits, uint64_t *misses, uint64_t *h2d_bytes);
@@ -154,7 +176,7 @@ int moe_cache_create_recording(const moe_cache_desc *desc, uintptr_t slot_pool, 
                                moe_cache **out);
 /* Recorded commands of a recording cache, 4 int64 per command:
    (kind, a, b, c) with kind 1 = wait(slot, release_id, -), 2 = copy(layer, expert, slot),
-   3 = table(layer, expert, slot or -1), 4 = ready(layer, -, -), 5 = release(layer, id, n_slots).
+   3 = table(layer, expert, slot or -1), 4 = wait(layer, -, -), 5 = release(layer, id, n_slots).
    Returns the total number of commands; writes at most max_cmds of them. */
 int64_t moe_cache_trace(const moe_cache *cache, int64_t *cmds, int64_t max_cmds);
 

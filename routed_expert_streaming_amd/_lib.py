@@ -55,6 +55,8 @@ def lib():
             "moe_expert_bytes": ([i, i], sz),
             "moe_router_workspace_bytes": ([i, i], sz),
             "moe_router_topk": ([vp, i, i, vp, vp, i, i, vp, vp, vp, sz, vp], i),
+            "moe_router_layers_workspace_bytes": ([i, i, i], sz),
+            "moe_router_topk_layers": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, sz, vp], i),
             "moe_permute": ([vp, i, i, i, vp, vp, vp, vp], i),
             "moe_cache_create": ([ctypes.POINTER(moe_cache_desc), vp, vp, vp, vp, ctypes.POINTER(vp)], i),
             "moe_cache_create_recording": ([ctypes.POINTER(moe_cache_desc), ctypes.c_uint64, i,
@@ -62,6 +64,8 @@ def lib():
             "moe_cache_trace": ([vp, vp, ctypes.c_int64], ctypes.c_int64),
             "moe_cache_lookup": ([vp, i, vp, i, vp, ctypes.POINTER(i)], i),
             "moe_cache_prefetch": ([vp, i, vp, i, vp, ctypes.POINTER(i)], i),
+            "moe_cache_prefetch_async": ([vp, i, vp, i, ctypes.POINTER(i)], i),
+            "moe_cache_wait": ([vp, i, vp], i),
             "moe_cache_release": ([vp, i, vp], i),
             "moe_cache_stats": ([vp, u64p, u64p, u64p], i),
             "moe_cache_reset": ([vp], i),
@@ -156,6 +160,17 @@ def moe_router_topk(x, T, H, w_router, bias, E, k, topk_idx, topk_w, workspace, 
                                  _ptr(workspace), workspace_bytes, _stream(stream)), "moe_router_topk")
 
 
+def moe_router_layers_workspace_bytes(n_layers: int, T: int, E: int) -> int:
+    return lib().moe_router_layers_workspace_bytes(n_layers, T, E)
+
+
+def moe_router_topk_layers(x, n_layers, T, H, w_router, bias, E, k, topk_idx, topk_w, workspace, workspace_bytes,
+                           stream=None):
+    _check(lib().moe_router_topk_layers(_ptr(x), n_layers, T, H, _ptr(w_router), _ptr(bias), E, k, _ptr(topk_idx),
+                                        _ptr(topk_w), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "moe_router_topk_layers")
+
+
 def moe_permute(topk_idx, T, k, E, count, offset, pair_of_row, stream=None):
     _check(lib().moe_permute(_ptr(topk_idx), T, k, E, _ptr(count), _ptr(offset), _ptr(pair_of_row),
                              _stream(stream)), "moe_permute")
@@ -207,6 +222,18 @@ def moe_cache_prefetch(cache: int, layer: int, experts, compute_stream=None) -> 
     _check(lib().moe_cache_prefetch(cache, layer, arr, len(experts), _stream(compute_stream), ctypes.byref(n)),
            "moe_cache_prefetch")
     return n.value
+
+
+def moe_cache_prefetch_async(cache: int, layer: int, experts) -> int:
+    arr = _i32_array(experts)
+    n = ctypes.c_int()
+    _check(lib().moe_cache_prefetch_async(cache, layer, arr, len(experts), ctypes.byref(n)),
+           "moe_cache_prefetch_async")
+    return n.value
+
+
+def moe_cache_wait(cache: int, layer: int, compute_stream=None):
+    _check(lib().moe_cache_wait(cache, layer, _stream(compute_stream)), "moe_cache_wait")
 
 
 def moe_cache_release(cache: int, layer: int, compute_stream=None):

@@ -11,9 +11,13 @@
 //
 // Ordering, per layer:
 //   copy stream   : [wait release of victim slot] -> H2D slab copy -> ... ->
-//                   table update kernel -> record ready
-//   compute stream: wait ready -> FFN kernels -> moe_cache_release records the
-//                   release event that the next copy into those slots waits for.
+//                   record ready
+//   compute stream: wait ready -> table update kernel -> FFN kernels ->
+//                   moe_cache_release records the release event that the next
+//                   copy into those slots waits for.
+// The copy half (moe_cache_prefetch_async) and the compute half (moe_cache_wait)
+// can be issued apart, so the copies of later layers are queued before the
+// kernels of earlier ones.
 #include <algorithm>
 #include <cstring>
 #include <memory>
@@ -47,15 +51,17 @@ struct Engine {
     virtual ~Engine() = default;
     virtual int wait_release(int layer, int slot, long long release_id) = 0;
     virtual int copy(int layer, int expert, int slot, void *dst, const void *src, size_t bytes) = 0;
+    // table writes of a prefetch: applied by the layer's next wait()
     virtual int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
                       const std::vector<int> &slots) = 0;
-    virtual int ready(int layer, void *compute_stream) = 0;
-    // Table writes that must land now, on the copy stream (a prefetch that failed
-    // part-way keeps the table equal to what is resident, without a ready()).
+    // table writes that must land now (a prefetch that failed part-way keeps the
+    // table equal to what is resident)
     virtual int table_now(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
                           const std::vector<int> &slots) {
         return table(layer, experts, ptrs, slots);
     }
+    virtual int copies_done(int layer) = 0;                // after the layer's copies, on the copy stream
+    virtual int wait(int layer, void *compute_stream) = 0;  // compute waits for them, then the table writes
     virtual int release(int layer, long long release_id, int n_slots, void *compute_stream) = 0;
     virtual int sync() = 0;
     virtual int clear_table() = 0;
@@ -67,9 +73,9 @@ struct HipEngine final : Engine {
     const void **tbl = nullptr;
     std::vector<hipEvent_t> ready_ev;    // [L]
     std::vector<hipEvent_t> release_ev;  // [L * kReleaseRing]
-    int pending_layer = -1;              // table writes waiting for ready()
-    std::vector<int> pending_experts;
-    std::vector<const void *> pending_ptrs;
+    // table writes waiting for wait(), per layer; one entry per expert (the latest)
+    std::vector<std::vector<int>> pend_exp;
+    std::vector<std::vector<const void *>> pend_ptr;
 
     int init(int layers, int experts, hipStream_t cs, void **table_dev) {
         L = layers;
@@ -78,6 +84,8 @@ struct HipEngine final : Engine {
         tbl = (const void **)table_dev;
         ready_ev.assign(L, nullptr);
         release_ev.assign((size_t)L * kReleaseRing, nullptr);
+        pend_exp.assign(L, {});
+        pend_ptr.assign(L, {});
         for (auto &e : ready_ev) MOE_TRY_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
         for (auto &e : release_ev) MOE_TRY_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
         return MOE_OK;
@@ -89,17 +97,26 @@ struct HipEngine final : Engine {
         for (auto e : release_ev)
             if (e) (void)hipEventDestroy(e);
     }
+    // A release that has already completed needs no barrier on the copy stream
+    // (a barrier ahead of each copy costs the copy engine tens of microseconds).
+    // The ring slot may hold a later release of the layer; that one completing
+    // implies this one did.
     int wait_release(int layer, int, long long id) override {
-        MOE_TRY_HIP(hipStreamWaitEvent(copy_stream, release_ev[(size_t)layer * kReleaseRing + id % kReleaseRing], 0));
+        hipEvent_t ev = release_ev[(size_t)layer * kReleaseRing + id % kReleaseRing];
+        const hipError_t q = hipEventQuery(ev);
+        if (q == hipSuccess) return MOE_OK;
+        if (q != hipErrorNotReady) return moe::fail_hip(q, "hipEventQuery(release)");
+        MOE_TRY_HIP(hipStreamWaitEvent(copy_stream, ev, 0));
         return MOE_OK;
     }
     int copy(int, int, int, void *dst, const void *src, size_t bytes) override {
         MOE_TRY_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, copy_stream));
         return MOE_OK;
     }
-    // Table writes wait for the layer's copies and run on the compute stream just
-    // before the layer's kernels, so the copy stream carries only DMA copies and
-    // event records (a kernel between two copies would stall the copy engine).
+    // Table writes run on the compute stream after it waits for the layer's
+    // copies, so the copy stream carries only DMA copies and event records (a
+    // kernel between two copies would stall the copy engine).  One launch writes
+    // up to 64 entries; an expert appears at most once per launch.
     int launch_updates(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
                        hipStream_t st) {
         for (size_t i = 0; i < experts.size(); i += kTableBatch) {
@@ -116,27 +133,39 @@ struct HipEngine final : Engine {
     }
     int table(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
               const std::vector<int> &) override {
-        pending_layer = layer;
-        pending_experts = experts;
-        pending_ptrs = ptrs;
+        auto &pe = pend_exp[layer];
+        auto &pp = pend_ptr[layer];
+        for (size_t i = 0; i < experts.size(); ++i) {
+            const auto it = std::find(pe.begin(), pe.end(), experts[i]);
+            if (it != pe.end()) {
+                pp[it - pe.begin()] = ptrs[i];
+            } else {
+                pe.push_back(experts[i]);
+                pp.push_back(ptrs[i]);
+            }
+        }
         return MOE_OK;
     }
     int table_now(int layer, const std::vector<int> &experts, const std::vector<const void *> &ptrs,
-                  const std::vector<int> &) override {
-        pending_layer = -1;
-        pending_experts.clear();
-        pending_ptrs.clear();
-        return launch_updates(layer, experts, ptrs, copy_stream);
+                  const std::vector<int> &slots) override {
+        // earlier pending writes of the layer land first, in the same stream order
+        int rc = table(layer, experts, ptrs, slots);
+        if (rc != MOE_OK) return rc;
+        rc = launch_updates(layer, pend_exp[layer], pend_ptr[layer], copy_stream);
+        pend_exp[layer].clear();
+        pend_ptr[layer].clear();
+        return rc;
     }
-    int ready(int layer, void *compute_stream) override {
-        hipStream_t cs = (hipStream_t)compute_stream;
+    int copies_done(int layer) override {
         MOE_TRY_HIP(hipEventRecord(ready_ev[layer], copy_stream));
+        return MOE_OK;
+    }
+    int wait(int layer, void *compute_stream) override {
+        hipStream_t cs = (hipStream_t)compute_stream;
         MOE_TRY_HIP(hipStreamWaitEvent(cs, ready_ev[layer], 0));
-        int rc = MOE_OK;
-        if (pending_layer == layer) rc = launch_updates(layer, pending_experts, pending_ptrs, cs);
-        pending_layer = -1;
-        pending_experts.clear();
-        pending_ptrs.clear();
+        const int rc = launch_updates(layer, pend_exp[layer], pend_ptr[layer], cs);
+        pend_exp[layer].clear();
+        pend_ptr[layer].clear();
         return rc;
     }
     int release(int layer, long long id, int, void *compute_stream) override {
@@ -149,6 +178,10 @@ struct HipEngine final : Engine {
         return MOE_OK;
     }
     int clear_table() override {
+        for (int l = 0; l < L; ++l) {
+            pend_exp[l].clear();
+            pend_ptr[l].clear();
+        }
         const size_t n = (size_t)L * E;
         hipLaunchKernelGGL(table_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, copy_stream, tbl, n);
         MOE_LAUNCH_CHECK("table_clear_kernel");
@@ -183,7 +216,8 @@ struct RecordingEngine final : Engine {
         for (size_t i = 0; i < experts.size(); ++i) put(3, layer, experts[i], slots[i]);
         return MOE_OK;
     }
-    int ready(int layer, void *) override {
+    int copies_done(int) override { return MOE_OK; }
+    int wait(int layer, void *) override {
         put(4, layer, -1, -1);
         return MOE_OK;
     }
@@ -211,6 +245,7 @@ struct moe_cache {
     std::vector<char> held;              // [L * C]
     std::vector<long long> last_release; // [L * C], -1 = never released
     std::vector<long long> next_release; // [L]
+    std::vector<char> unwaited;          // [L], copies or table writes not yet waited for
     unsigned long long clock = 0;
     uint64_t hits = 0, misses = 0, bytes = 0;
 
@@ -226,6 +261,7 @@ struct moe_cache {
         held.assign(L * Cs, 0);
         last_release.assign(L * Cs, -1);
         next_release.assign(L, 0);
+        unwaited.assign(L, 0);
         clock = 0;
         hits = misses = bytes = 0;
     }
@@ -343,8 +379,7 @@ extern "C" int moe_cache_lookup(moe_cache *c, int layer, const int32_t *experts,
     return MOE_OK;
 }
 
-extern "C" int moe_cache_prefetch(moe_cache *c, int layer, const int32_t *experts, int n, void *compute_stream,
-                                  int *n_copies) {
+extern "C" int moe_cache_prefetch_async(moe_cache *c, int layer, const int32_t *experts, int n, int *n_copies) {
     int rc = check_request(c, layer, experts, n);
     if (rc != MOE_OK) return rc;
     const int Cs = c->C(), E = c->d.n_experts;
@@ -423,8 +458,9 @@ extern "C" int moe_cache_prefetch(moe_cache *c, int layer, const int32_t *expert
         if (rc != MOE_OK) return rc;
     }
     if (copies > 0 || !t_exp.empty()) {
-        rc = c->engine->ready(layer, compute_stream);
+        rc = c->engine->copies_done(layer);
         if (rc != MOE_OK) return rc;
+        c->unwaited[layer] = 1;
     }
     c->hits += hit_list.size();
     c->misses += miss_list.size();
@@ -433,9 +469,28 @@ extern "C" int moe_cache_prefetch(moe_cache *c, int layer, const int32_t *expert
     return MOE_OK;
 }
 
+extern "C" int moe_cache_wait(moe_cache *c, int layer, void *compute_stream) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache_wait: NULL cache");
+    if (layer < 0 || layer >= c->d.n_layers) return moe::fail(MOE_E_ARG, "cache_wait: layer %d", layer);
+    if (!c->unwaited[layer]) return MOE_OK;
+    const int rc = c->engine->wait(layer, compute_stream);
+    if (rc != MOE_OK) return rc;
+    c->unwaited[layer] = 0;
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_prefetch(moe_cache *c, int layer, const int32_t *experts, int n, void *compute_stream,
+                                  int *n_copies) {
+    const int rc = moe_cache_prefetch_async(c, layer, experts, n, n_copies);
+    if (rc != MOE_OK) return rc;
+    return moe_cache_wait(c, layer, compute_stream);
+}
+
 extern "C" int moe_cache_release(moe_cache *c, int layer, void *compute_stream) {
     if (!c) return moe::fail(MOE_E_ARG, "cache_release: NULL cache");
     if (layer < 0 || layer >= c->d.n_layers) return moe::fail(MOE_E_ARG, "cache_release: layer %d", layer);
+    if (c->unwaited[layer])
+        return moe::fail(MOE_E_STATE, "cache_release: layer %d has copies not yet waited for (moe_cache_wait)", layer);
     const int Cs = c->C();
     char *held = &c->held[(size_t)layer * Cs];
     int n_held = 0;

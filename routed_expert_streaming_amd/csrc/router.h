@@ -33,7 +33,9 @@ __device__ __forceinline__ float router_logit4(const double (&q)[4], int nslices
 float *router_logits(void *workspace);
 double *router_partials_buf(void *workspace, int T, int E);
 
-// Launch the partial-logit kernel for T <= 32 tokens.
-int router_partials(const uint16_t *x, int T, int H, const float *w_router, int E, double *partial, hipStream_t s);
+// Launch the partial-logit kernel for T <= 32 tokens; with layers > 1, layer l
+// reads x + l*T*H and w_router + l*E*H and writes partial + l*ws_stride bytes.
+int router_partials(const uint16_t *x, int T, int H, const float *w_router, int E, double *partial, hipStream_t s,
+                    int layers = 1, size_t ws_stride = 0);
 
 }  // namespace moe

@@ -48,11 +48,17 @@ using moe::kSlice;
 using moe::kMaxSlices;
 constexpr int kSmallT = 32;
 
+// Both kernels take grid.y = layers: layer y reads x + y*T*H, the router rows
+// + y*E*H and the bias + y*E, and writes its partials and logits in its own
+// workspace slice (ws_stride bytes apart) and its top-k at + y*T*k.
 template <int TMAX>
 __global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t *__restrict__ x, int T, int H,
                                                              const float *__restrict__ wr, int E,
-                                                             double *__restrict__ partial) {
+                                                             double *__restrict__ partial, size_t ws_stride) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    x += (size_t)blockIdx.y * T * H;
+    wr += (size_t)blockIdx.y * E * H;
+    partial = (double *)((char *)partial + blockIdx.y * ws_stride);
     const int nslices = (H + kSlice - 1) / kSlice;
     const int item = blockIdx.x * 4 + wave;  // (expert, slice)
     const int e = item / nslices, sl = item - e * nslices;
@@ -90,10 +96,15 @@ template <int PER>
 __global__ __launch_bounds__(256) void router_finalize_kernel(const double *__restrict__ partial, int T, int H,
                                                               const float *__restrict__ bias, int E, int k,
                                                               float *__restrict__ logits, int32_t *__restrict__ idx,
-                                                              float *__restrict__ w) {
+                                                              float *__restrict__ w, size_t ws_stride) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
+    partial = (const double *)((const char *)partial + blockIdx.y * ws_stride);
+    logits = (float *)((char *)logits + blockIdx.y * ws_stride);
+    if (bias) bias += (size_t)blockIdx.y * E;
+    idx += (size_t)blockIdx.y * T * k;
+    w += (size_t)blockIdx.y * T * k;
     const int nslices = (H + kSlice - 1) / kSlice;
     uint32_t ord[PER];
 #pragma unroll
@@ -208,17 +219,18 @@ double *router_partials_buf(void *workspace, int T, int E) {
     return (double *)((char *)workspace + kHeaderBytes + align_up((size_t)T * (size_t)E * sizeof(float), 256));
 }
 
-int router_partials(const uint16_t *x, int T, int H, const float *w_router, int E, double *partial, hipStream_t s) {
+int router_partials(const uint16_t *x, int T, int H, const float *w_router, int E, double *partial, hipStream_t s,
+                    int layers, size_t ws_stride) {
     const int nslices = (H + kSlice - 1) / kSlice;
-    const dim3 grid((E * nslices + 3) / 4), block(256);
+    const dim3 grid((E * nslices + 3) / 4, layers), block(256);
     if (T == 1)
-        hipLaunchKernelGGL(router_partial_kernel<1>, grid, block, 0, s, x, T, H, w_router, E, partial);
+        hipLaunchKernelGGL(router_partial_kernel<1>, grid, block, 0, s, x, T, H, w_router, E, partial, ws_stride);
     else if (T <= 4)
-        hipLaunchKernelGGL(router_partial_kernel<4>, grid, block, 0, s, x, T, H, w_router, E, partial);
+        hipLaunchKernelGGL(router_partial_kernel<4>, grid, block, 0, s, x, T, H, w_router, E, partial, ws_stride);
     else if (T <= 8)
-        hipLaunchKernelGGL(router_partial_kernel<8>, grid, block, 0, s, x, T, H, w_router, E, partial);
+        hipLaunchKernelGGL(router_partial_kernel<8>, grid, block, 0, s, x, T, H, w_router, E, partial, ws_stride);
     else
-        hipLaunchKernelGGL(router_partial_kernel<32>, grid, block, 0, s, x, T, H, w_router, E, partial);
+        hipLaunchKernelGGL(router_partial_kernel<32>, grid, block, 0, s, x, T, H, w_router, E, partial, ws_stride);
     MOE_LAUNCH_CHECK("router_partial_kernel");
     return MOE_OK;
 }
@@ -232,46 +244,82 @@ extern "C" size_t moe_router_workspace_bytes(int T, int E) {
     return kHeaderBytes + logits + partial;
 }
 
-extern "C" int moe_router_topk(const uint16_t *x, int T, int H, const float *w_router, const float *bias, int E,
-                               int k, int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes,
-                               void *stream) {
-    if (T < 0) return moe::fail(MOE_E_ARG, "router: T=%d < 0", T);
-    if (T == 0) return MOE_OK;
-    if (!x || !w_router || !topk_idx || !topk_w || !workspace) return moe::fail(MOE_E_ARG, "router: NULL pointer");
-    if (H <= 0 || H % 32 != 0) return moe::fail(MOE_E_SHAPE, "router: H=%d must be a positive multiple of 32", H);
-    if (E <= 0 || E > kMaxE) return moe::fail(MOE_E_SHAPE, "router: E=%d outside 1..%d", E, kMaxE);
-    if (k < 1 || k > E || k > kTopkMaxK) return moe::fail(MOE_E_SHAPE, "router: k=%d outside 1..min(E,64)", k);
-    if (workspace_bytes < moe_router_workspace_bytes(T, E))
-        return moe::fail(MOE_E_NOMEM, "router: workspace %zu < %zu bytes", workspace_bytes,
-                         moe_router_workspace_bytes(T, E));
-    if (H > kSlice * kMaxSlices) return moe::fail(MOE_E_SHAPE, "router: H=%d above %d", H, kSlice * kMaxSlices);
+extern "C" size_t moe_router_layers_workspace_bytes(int n_layers, int T, int E);
+
+namespace {
+
+// Bytes between the workspace slices of consecutive layers.
+size_t layer_stride(int T, int E) { return moe::align_up(moe_router_workspace_bytes(T, E), 256); }
+
+// Shared body of the single-layer and layer-batched entry points: `layers`
+// independent routers, layer l using workspace slice l (ws_stride bytes apart).
+int router_run(const uint16_t *x, int layers, int T, int H, const float *w_router, const float *bias, int E, int k,
+               int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes, void *stream,
+               const char *who) {
+    if (T < 0 || layers < 0) return moe::fail(MOE_E_ARG, "%s: T=%d, layers=%d must be >= 0", who, T, layers);
+    if (T == 0 || layers == 0) return MOE_OK;
+    if (!x || !w_router || !topk_idx || !topk_w || !workspace) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
+    if (H <= 0 || H % 32 != 0) return moe::fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 32", who, H);
+    if (E <= 0 || E > kMaxE) return moe::fail(MOE_E_SHAPE, "%s: E=%d outside 1..%d", who, E, kMaxE);
+    if (k < 1 || k > E || k > kTopkMaxK) return moe::fail(MOE_E_SHAPE, "%s: k=%d outside 1..min(E,64)", who, k);
+    if (layers > 65535) return moe::fail(MOE_E_SHAPE, "%s: layers=%d above 65535", who, layers);
+    const size_t per = layer_stride(T, E), need = moe_router_layers_workspace_bytes(layers, T, E);
+    if (workspace_bytes < need) return moe::fail(MOE_E_NOMEM, "%s: workspace %zu < %zu bytes", who, workspace_bytes, need);
+    if (H > kSlice * kMaxSlices) return moe::fail(MOE_E_SHAPE, "%s: H=%d above %d", who, H, kSlice * kMaxSlices);
     hipStream_t s = (hipStream_t)stream;
-    float *logits = moe::router_logits(workspace);
-    double *partial = moe::router_partials_buf(workspace, T, E);
     const dim3 block(256);
     if (T <= kSmallT) {
-        int rc = moe::router_partials(x, T, H, w_router, E, partial, s);
+        float *logits = moe::router_logits(workspace);
+        double *partial = moe::router_partials_buf(workspace, T, E);
+        int rc = moe::router_partials(x, T, H, w_router, E, partial, s, layers, per);
         if (rc != MOE_OK) return rc;
-        const dim3 grid_f((T + 3) / 4);
+        const dim3 grid_f((T + 3) / 4, layers);
         if (E <= 64)
             hipLaunchKernelGGL(router_finalize_kernel<1>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
-                               topk_idx, topk_w);
+                               topk_idx, topk_w, per);
         else if (E <= 128)
             hipLaunchKernelGGL(router_finalize_kernel<2>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
-                               topk_idx, topk_w);
+                               topk_idx, topk_w, per);
         else if (E <= 256)
             hipLaunchKernelGGL(router_finalize_kernel<4>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
-                               topk_idx, topk_w);
+                               topk_idx, topk_w, per);
         else
             hipLaunchKernelGGL(router_finalize_kernel<kPer>, grid_f, block, 0, s, partial, T, H, bias, E, k, logits,
-                               topk_idx, topk_w);
+                               topk_idx, topk_w, per);
         MOE_LAUNCH_CHECK("router_finalize_kernel");
         return MOE_OK;
     }
-    dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
-    hipLaunchKernelGGL(router_mfma_kernel, grid, block, 0, s, x, T, H, w_router, bias, E, logits);
-    MOE_LAUNCH_CHECK("router_mfma_kernel");
-    hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), block, 0, s, logits, T, E, k, topk_idx, topk_w);
-    MOE_LAUNCH_CHECK("router_topk_kernel");
+    for (int l = 0; l < layers; ++l) {
+        const size_t xo = (size_t)l * T * H, wo = (size_t)l * E * H, io = (size_t)l * T * k;
+        float *logits = moe::router_logits((char *)workspace + (size_t)l * per);
+        dim3 grid((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
+        hipLaunchKernelGGL(router_mfma_kernel, grid, block, 0, s, x + xo, T, H, w_router + wo,
+                           bias ? bias + (size_t)l * E : nullptr, E, logits);
+        MOE_LAUNCH_CHECK("router_mfma_kernel");
+        hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), block, 0, s, logits, T, E, k, topk_idx + io,
+                           topk_w + io);
+        MOE_LAUNCH_CHECK("router_topk_kernel");
+    }
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_router_topk(const uint16_t *x, int T, int H, const float *w_router, const float *bias, int E,
+                               int k, int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    return router_run(x, 1, T, H, w_router, bias, E, k, topk_idx, topk_w, workspace, workspace_bytes, stream,
+                      "router");
+}
+
+extern "C" size_t moe_router_layers_workspace_bytes(int n_layers, int T, int E) {
+    if (n_layers <= 0 || moe_router_workspace_bytes(T, E) == 0) return 0;
+    return (size_t)(n_layers - 1) * layer_stride(T, E) + moe_router_workspace_bytes(T, E);
+}
+
+extern "C" int moe_router_topk_layers(const uint16_t *x, int n_layers, int T, int H, const float *w_router,
+                                      const float *bias, int E, int k, int32_t *topk_idx, float *topk_w,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    return router_run(x, n_layers, T, H, w_router, bias, E, k, topk_idx, topk_w, workspace, workspace_bytes, stream,
+                      "router_layers");
 }

@@ -1,13 +1,17 @@
 """Summarise a rocprofv3 result database (rocpd SQLite) as plain text.
 
-  python -m routed_expert_streaming_amd.rocprof_summary RESULTS.db [--counters | --timeline]
+  python -m routed_expert_streaming_amd.rocprof_summary RESULTS.db [--counters | --timeline | --copies]
 
 Prints one line per kernel: dispatches, average / min / max duration, share of
 GPU time, grid, workgroup size and VGPRs; with --counters, the average of every
 PMC counter per kernel (as collected by ``rocprofv3 --pmc ...``); with
 --timeline, per kernel the average duration and the average idle gap between
 the end of the previous dispatch and its start (over the last two thirds of the
-trace, gaps under 20 us, so set-up and host pauses are left out).
+trace, gaps under 20 us, so set-up and host pauses are left out); with --copies
+(a trace taken with --memory-copy-trace), per copy direction the number of
+copies, their average size, duration and rate, and over the last two thirds of
+the trace the average idle gap between consecutive copies (gaps under 1 ms) and
+the share of that span the copies were running.
 """
 from __future__ import annotations
 
@@ -66,12 +70,40 @@ def timeline_stats(db: str):
             for k, d in dur.items()]
 
 
+def copy_stats(db: str):
+    c = sqlite3.connect(db)
+    rows = c.execute("select src_agent_type, dst_agent_type, size, start, end from memory_copies "
+                     "order by start").fetchall()
+    by_dir = collections.defaultdict(list)
+    for src, dst, size, start, end in rows:
+        by_dir[f"{src}->{dst}"].append((start, end, size))
+    out = []
+    for d, cps in by_dir.items():
+        tail = cps[len(cps) // 3:]
+        gaps = [b[0] - a[1] for a, b in zip(tail, tail[1:]) if 0 <= b[0] - a[1] < 1_000_000]
+        span = (tail[-1][1] - tail[0][0]) if tail else 0
+        busy = sum(e - s0 for s0, e, _ in tail)
+        n = len(cps)
+        avg_size = sum(x[2] for x in cps) / n
+        avg_dur = sum(x[1] - x[0] for x in cps) / n
+        out.append((d, n, avg_size, avg_dur / 1e3, avg_size / avg_dur if avg_dur else 0.0,
+                    (sum(gaps) / len(gaps) / 1e3) if gaps else 0.0, busy / span if span else 0.0))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("db")
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--timeline", action="store_true")
+    ap.add_argument("--copies", action="store_true")
     args = ap.parse_args()
+    if args.copies:
+        print(f"{'direction':14s} {'copies':>7s} {'avg_bytes':>11s} {'avg_us':>9s} {'GB/s':>7s} "
+              f"{'gap_us':>8s} {'busy':>6s}")
+        for d, n, sz, us, rate, gap, busy in copy_stats(args.db):
+            print(f"{d:14s} {n:7d} {sz:11.0f} {us:9.2f} {rate:7.2f} {gap:8.2f} {busy:6.3f}")
+        return
     if args.timeline:
         print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'gap_before_us':>14s}")
         for k, n, d, g in timeline_stats(args.db):

@@ -4,17 +4,18 @@ Device memory and streams come from torch; pinned host memory comes from the
 HIP runtime torch already loaded.  Every arithmetic step runs in libmoe.so's
 kernels; this module only allocates, fills inputs and orders the calls:
 
-  step:  router(l) for every layer            (compute stream)
-         [streaming] one D2H of the top-k ids + host wait, then per layer:
-             prefetch(l)   -> copy stream streams the misses, compute waits
-             expert_ffn(l) -> gate/up + SwiGLU, down
-             release(l)    -> slots may be overwritten after this point
-         combine(l)
+  step:  [resident] per layer: router + gate/up + SwiGLU + down + combine
+         [streaming] the routers of every layer (one call, compute stream), one
+         D2H of the top-k ids + host wait, then
+             prefetch_async(l) for every layer -> the copy stream queues the misses
+             per layer: wait(l)  -> compute waits for layer l's copies
+                        expert_ffn + combine(l)
+                        release(l) -> slots may be overwritten after this point
 
 The routing of every layer is known at the start of a step because each
-(step, layer) gets its own synthetic hidden states; the prefetch of layer l+1
-therefore overlaps the FFN of layer l (LayerStoRm README "TL;DR": streaming is
-overlapped with compute).  When a layer needs more distinct experts than it has
+(step, layer) gets its own synthetic hidden states; the copies of later layers
+therefore overlap the FFN of earlier ones (LayerStoRm README "TL;DR": streaming
+is overlapped with compute).  When a layer needs more distinct experts than it has
 slots, it runs in waves: hits plus as many misses as fit first, then the
 remaining misses into slots released by the finished wave.
 """
@@ -141,7 +142,7 @@ class MoEStack:
             self.cache = L.moe_cache_create(desc, ctypes.addressof(self._host_ptrs), self.pool, self.table,
                                             self.copy_stream)
         # workspaces and outputs
-        self.router_ws_bytes = L.moe_router_workspace_bytes(T, E)
+        self.router_ws_bytes = L.moe_router_layers_workspace_bytes(Lyr, T, E)
         self.router_ws = torch.zeros(self.router_ws_bytes, dtype=torch.uint8, device=self.dev)
         self.ffn_ws_bytes = L.moe_expert_ffn_workspace_bytes(T, H, I, E, k, self.has_shared)
         self.ffn_ws = torch.empty(self.ffn_ws_bytes, dtype=torch.uint8, device=self.dev)
@@ -178,6 +179,11 @@ class MoEStack:
     def route(self, x: torch.Tensor, l: int):
         L.moe_router_topk(x[l], self.T, self.H, self.wr[l], None if self.bias is None else self.bias[l], self.E,
                           self.k, self.idx[l], self.w[l], self.router_ws, self.router_ws_bytes, self.stream)
+
+    def route_all(self, x: torch.Tensor):
+        """Routers of every layer in one call."""
+        L.moe_router_topk_layers(x, self.L, self.T, self.H, self.wr, self.bias, self.E, self.k, self.idx, self.w,
+                                 self.router_ws, self.router_ws_bytes, self.stream)
 
     def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True):
         L.moe_expert_ffn(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l],
@@ -227,14 +233,16 @@ class MoEStack:
             for l in range(self.L):
                 self.route_ffn_combine(x, l, out)
             return st
-        for l in range(self.L):
-            self.route(x, l)
+        self.route_all(x)
         # one small D2H per step, then the host plans every layer
         idx_host = np.frombuffer(self._idx_host.array, dtype=np.int32, count=self.L * self.T * self.k)
         torch.from_numpy(idx_host).copy_(self.idx.view(-1), non_blocking=True)
         self.stream.synchronize()
-        idx_host = idx_host.reshape(self.L, self.T, self.k)
-        plans = [self.plan_waves(l, sorted(set(int(e) for e in idx_host[l].ravel()))) for l in range(self.L)]
+        plans = []
+        for l, row in enumerate(idx_host.reshape(self.L, -1).tolist()):
+            needed = sorted(set(row))
+            # up to C experts always fit in one wave, whatever is resident
+            plans.append([needed] if len(needed) <= self.C else self.plan_waves(l, needed))
         need_masks = any(len(p) > 1 for p in plans)
         if need_masks:
             mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
@@ -244,9 +252,17 @@ class MoEStack:
                 for wv, experts in enumerate(waves):
                     mh[l, wv, experts] = 1
             self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
+        # single-wave layers: every copy is queued before the first FFN launch, so
+        # the copy engine starts as soon as the plan is known (each layer evicts
+        # only its own slots, released in the previous step); the compute stream
+        # waits for a layer's copies just before that layer's kernels
+        single = [len(waves) == 1 for waves in plans]
         for l, waves in enumerate(plans):
-            if len(waves) == 1:
-                st.copies += L.moe_cache_prefetch(self.cache, l, waves[0], self.stream)
+            if single[l]:
+                st.copies += L.moe_cache_prefetch_async(self.cache, l, waves[0])
+        for l, waves in enumerate(plans):
+            if single[l]:
+                L.moe_cache_wait(self.cache, l, self.stream)
                 self.ffn_combine(x, l, out)
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1

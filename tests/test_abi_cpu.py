@@ -59,6 +59,20 @@ def test_router_validation():
     L.moe_router_topk(None, 0, 256, None, None, 16, 2, None, None, None, 0)  # T = 0 is a no-op
 
 
+def test_router_layers_validation():
+    one = L.moe_router_workspace_bytes(4, 16)
+    ws = L.moe_router_layers_workspace_bytes(3, 4, 16)
+    assert L.moe_router_layers_workspace_bytes(1, 4, 16) == one
+    assert ws == 2 * ((one + 255) // 256 * 256) + one
+    assert L.moe_router_layers_workspace_bytes(0, 4, 16) == 0
+    args = (FAKE, 3, 4, 256, FAKE, None, 16, 2, FAKE, FAKE, FAKE)
+    assert _status(L.moe_router_topk_layers, *args, ws - 1) == L.MOE_E_NOMEM
+    assert _status(L.moe_router_topk_layers, FAKE, -1, 4, 256, FAKE, None, 16, 2, FAKE, FAKE, FAKE, ws) == L.MOE_E_ARG
+    assert _status(L.moe_router_topk_layers, FAKE, 3, 4, 256, FAKE, None, 16, 0, FAKE, FAKE, FAKE, ws) == L.MOE_E_SHAPE
+    assert _status(L.moe_router_topk_layers, FAKE, 3, 4, 256, None, None, 16, 2, FAKE, FAKE, FAKE, ws) == L.MOE_E_ARG
+    L.moe_router_topk_layers(None, 0, 4, 256, None, None, 16, 2, None, None, None, 0)  # no layers: no-op
+
+
 def test_ffn_combine_permute_validation():
     ws = L.moe_expert_ffn_workspace_bytes(4, 256, 128, 16, 2, 0)
     args = [FAKE, 4, 256, 128, 16, FAKE, 2, FAKE, None, None, FAKE, FAKE, ws]
@@ -226,6 +240,39 @@ def test_cache_copy_failure_leaves_slot_empty():
     # the request was un-held: a full-size request still fits and re-streams the failed ones
     assert L.moe_cache_prefetch(cache, 0, [4, 7, 9, 11, 12, 13]) == 4
     assert L.moe_cache_lookup(cache, 0, [9, 11])[1] == 2
+    L.moe_cache_destroy(cache)
+
+
+def test_cache_async_prefetch_and_wait():
+    cache = L.moe_cache_create_recording(_desc(3, 16, 4), 1 << 40)
+    # copies of layers 0 and 2 queued before either layer's wait
+    assert L.moe_cache_prefetch_async(cache, 0, [5, 1]) == 2
+    assert L.moe_cache_prefetch_async(cache, 2, [3]) == 1
+    trace = L.moe_cache_trace(cache)
+    assert [c[0] for c in trace] == [2, 2, 3, 3, 2, 3]  # copies and table writes only, no wait yet
+    assert trace[0] == (2, 0, 1, 0) and trace[1] == (2, 0, 5, 1) and trace[4] == (2, 2, 3, 0)
+    # release before the wait is refused; the slots stay held
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_cache_release(cache, 0)
+    assert ei.value.status == L.MOE_E_STATE
+    L.moe_cache_wait(cache, 0)
+    L.moe_cache_wait(cache, 0)  # nothing pending: no command
+    L.moe_cache_wait(cache, 1)  # never prefetched: no command
+    L.moe_cache_release(cache, 0)
+    L.moe_cache_wait(cache, 2)
+    L.moe_cache_release(cache, 2)
+    trace = L.moe_cache_trace(cache)
+    assert trace[6:] == [(4, 0, -1, -1), (5, 0, 0, 2), (4, 2, -1, -1), (5, 2, 0, 1)]
+    # an all-hit request has nothing to wait for
+    assert L.moe_cache_prefetch_async(cache, 0, [1]) == 0
+    L.moe_cache_release(cache, 0)
+    assert len(L.moe_cache_trace(cache)) == 11
+    # the combined call equals async + wait
+    assert L.moe_cache_prefetch(cache, 1, [7]) == 1
+    assert L.moe_cache_trace(cache)[-1] == (4, 1, -1, -1)
+    L.moe_cache_release(cache, 1)
+    with pytest.raises(L.MoEError):
+        L.moe_cache_wait(cache, 3)
     L.moe_cache_destroy(cache)
 
 

@@ -135,6 +135,33 @@ def test_router_workspace_contents_do_not_matter():
     assert np.array_equal(idx2.cpu().numpy(), idx) and np.array_equal(w2.cpu().numpy(), w)
 
 
+@pytest.mark.parametrize("layers,T,H,E,k,bias", [(8, 1, 4096, 128, 8, True), (3, 5, 512, 64, 6, False),
+                                                   (2, 40, 256, 40, 5, True)])
+def test_router_layers_matches_per_layer_calls(layers, T, H, E, k, bias):
+    """The layer-batched router gives each layer exactly the single-layer result,
+    which the oracle pins (same indices, weights within 1e-6)."""
+    seed = 77 + layers + T
+    xs = np.stack([synth.x_bf16(seed, 0, l, T, H) for l in range(layers)])
+    Wr = np.stack([synth.router_w(seed, l, E, H) for l in range(layers)])
+    b = np.random.default_rng(seed).standard_normal((layers, E)).astype(np.float32) if bias else None
+    nb = L.moe_router_layers_workspace_bytes(layers, T, E)
+    ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((layers, T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((layers, T, k), dtype=torch.float32, device="cuda")
+    L.moe_router_topk_layers(bf16_dev(xs.reshape(layers * T, H)), layers, T, H, torch.from_numpy(Wr).cuda(),
+                             None if b is None else torch.from_numpy(b).cuda(), E, k, idx, w, ws, nb)
+    torch.cuda.synchronize()
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    stride = (L.moe_router_workspace_bytes(T, E) + 255) // 256 * 256
+    for l in range(layers):
+        i1, w1, lg1, _ = run_router(xs[l], Wr[l], None if b is None else b[l], k)
+        assert np.array_equal(idx[l], i1) and np.array_equal(w[l], w1)
+        lg = ws[l * stride + 256:l * stride + 256 + T * E * 4].view(torch.float32).view(T, E).cpu().numpy()
+        assert np.array_equal(lg, lg1)
+        _, ref_idx, ref_w = oracle.router(xs[l], Wr[l], None if b is None else b[l], k)
+        assert np.array_equal(idx[l], ref_idx) and np.max(np.abs(w[l] - ref_w)) <= 1e-6
+
+
 # ---------------------------------------------------------------------------- dequant
 def test_debug_dequant_round_trip_exact():
     H, I = 64, 32
