@@ -322,17 +322,26 @@ def main():
                     device="cuda")
     stack.forward(xs[0], outs[0])  # routing of input 0 for every layer
     # back-to-back launches of one kernel between two events: the average launch
-    # duration on the stream the kernel runs on
+    # duration on the stream the kernel runs on.  The launches are captured in one
+    # HIP graph and replayed on that stream, so host launch cost (which a profiler
+    # inflates) does not show up as idle time between them.
     def time_launches(fn, iters):
         for l in range(stack.L):
             fn(l)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(iters):
+                for l in range(stack.L):
+                    fn(l)
+        g.replay()
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(dev_stream)
-        for _ in range(iters):
-            for l in range(stack.L):
-                fn(l)
+        g.replay()
         b.record(dev_stream)
         torch.cuda.synchronize()
+        del g
         return a.elapsed_time(b) * 1e3 / (iters * stack.L)
 
     gu_us = time_launches(lambda l: stack.gate_up_only(xs[0], l, h), args.kernel_iters)

@@ -11,7 +11,9 @@ trace, gaps under 20 us, so set-up and host pauses are left out); with --copies
 (a trace taken with --memory-copy-trace), per copy direction the number of
 copies, their average size, duration and rate, and over the last two thirds of
 the trace the average idle gap between consecutive copies (gaps under 1 ms) and
-the share of that span the copies were running.
+the share of that span the copies were running; with --events N AT, N kernels
+and copies in start order from the AT-th dispatch of the router partial kernel
+counted from the end (1 = the last), times in microseconds from the first one.
 """
 from __future__ import annotations
 
@@ -91,13 +93,34 @@ def copy_stats(db: str):
     return out
 
 
+def events(db: str, n: int, at: int, anchor: str = "router_partial_kernel"):
+    c = sqlite3.connect(db)
+    ev = [(s, e, "K " + short_name(name)[:60]) for name, s, e in c.execute("select name, start, end from kernels")]
+    tabs = {r[0] for r in c.execute("select name from sqlite_master where type in ('table', 'view')")}
+    if "memory_copies" in tabs:
+        ev += [(s, e, f"C {size}") for s, e, size in c.execute("select start, end, size from memory_copies")]
+    ev.sort()
+    starts = [i for i, x in enumerate(ev) if anchor in x[2]]
+    if not starts:
+        return []
+    i0 = starts[-min(at, len(starts))]
+    t0 = ev[i0][0]
+    return [((s - t0) / 1e3, (e - t0) / 1e3, (e - s) / 1e3, name) for s, e, name in ev[i0:i0 + n]]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("db")
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--timeline", action="store_true")
     ap.add_argument("--copies", action="store_true")
+    ap.add_argument("--events", nargs=2, type=int, metavar=("N", "AT"))
     args = ap.parse_args()
+    if args.events:
+        print(f"{'start_us':>9s} {'end_us':>9s} {'dur_us':>8s}  event")
+        for s0, e, d, name in events(args.db, *args.events):
+            print(f"{s0:9.2f} {e:9.2f} {d:8.2f}  {name}")
+        return
     if args.copies:
         print(f"{'direction':14s} {'copies':>7s} {'avg_bytes':>11s} {'avg_us':>9s} {'GB/s':>7s} "
               f"{'gap_us':>8s} {'busy':>6s}")
