@@ -8,15 +8,21 @@
 // the expert's tokens in M chunks of up to 96, so at prefill sizes (about 64
 // tokens per expert) every weight byte is read from HBM once.
 //
-// The K dimension streams in chunks of 64 columns through two LDS buffers: the
-// next chunk's global loads (gathered activations, weight codes, (scale, min)
-// records) are in flight in registers while the current chunk is multiplied,
-// then land in the other buffer behind one barrier per chunk.  Each wave owns
-// 32 N columns (of W1 and of W3 for gate/up): it dequantises its B operand from
-// LDS into bf16 registers (scale*q + min in fp32, rounded to bf16) and
-// accumulates v_mfma_f32_16x16x32_bf16 products in fp32.  Workgroups are
-// numbered so that every tile of one expert runs on the same XCD, where the
-// expert's gathered activation rows are shared through that XCD's L2.
+// The K dimension streams in chunks of 64 columns through a ring of kStages
+// LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4 for
+// activations and weight codes, _dword for the (scale, min) records), so the
+// loads of the next kStages-1 chunks are in flight while the current chunk is
+// multiplied and no registers hold data on its way to LDS.  Each wave loads its
+// own 32 weight rows; the activation tile is shared and XOR-swizzled in 16-byte
+// units so that the A-operand reads hit distinct banks.  One barrier per chunk:
+// each wave first waits (exact vmcnt) for its own loads of the chunk, the
+// barrier then makes every wave's loads visible and frees the buffer that the
+// chunk loads issued next will overwrite.  Each wave owns 32 N columns (of W1
+// and of W3 for gate/up): it dequantises its B operand from LDS into bf16
+// registers (scale*q + min in fp32, rounded to bf16) and accumulates
+// v_mfma_f32_16x16x32_bf16 products in fp32.  Workgroups are numbered so that
+// every tile of one expert runs on the same XCD, where the expert's gathered
+// activation rows are shared through that XCD's L2.
 //
 // Lane layout of v_mfma_f32_16x16x32_bf16 (checked on gfx950): lane l holds
 // A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16] for j < 8, and C[4*(l/16)+j][l%16]
@@ -30,24 +36,59 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kNT = 128;       // weight rows (N) per workgroup
-constexpr int kKC = 64;        // columns (K) per LDS chunk
-constexpr int kMaxMT = 6;      // 16-row M tiles per chunk
+constexpr int kKC = 64;        // columns (K) per chunk
+constexpr int kMaxMT = 6;      // 16-row M tiles per pass
 constexpr int kMC = 16 * kMaxMT;
-constexpr int kXStride = 144;  // bytes per staged activation row (128 + 16 pad)
-constexpr int kWStride = 40;   // bytes per staged code row (32 + 8 pad: conflict-free B reads)
+constexpr int kXRow = kKC * 2; // bytes of one activation row of a chunk (8 units of 16 B)
 constexpr int kXcds = 8;       // workgroups are dealt to the XCDs round-robin
-static_assert(kMC * (kKC * 2 / 16) % 256 == 0, "activation tile loads must divide over the workgroup");
+#ifndef MOE_MFMA_STAGES_GU
+#define MOE_MFMA_STAGES_GU 3
+#endif
+#ifndef MOE_MFMA_STAGES_DN
+#define MOE_MFMA_STAGES_DN 4
+#endif
+constexpr int kStagesGateUp = MOE_MFMA_STAGES_GU;  // ring depth: 3 x 22 KB of LDS, two workgroups per CU
+constexpr int kStagesDown = MOE_MFMA_STAGES_DN;    // 4 x 17 KB
 
-struct MfmaBuf {
-    __attribute__((aligned(16))) uint8_t x[kMC * kXStride];  // activation tile, bf16, natural column order
-    uint8_t w[2][kNT * kWStride]; // code tiles (W1, W3) or (W2, -)
-    uint2 p[2][kNT];              // (scale, min) records of the chunk's 2 blocks per row
+// One ring stage: the chunk's activation tile (row r, 16-byte unit u stored at
+// unit position u ^ (r & 7)), and per matrix the codes and records of the 128
+// rows, wave w's 32 rows in its own 1 KB (codes: unit (row, half) at position
+// half*32 + row) and 256 B (records: row-major, 2 per row).
+template <int NMAT>
+struct __attribute__((aligned(16))) Stage {
+    uint8_t x[kMC * kXRow];
+    uint8_t w[NMAT][kNT * 32];
+    uint32_t p[NMAT][kNT * 2];
 };
-struct __attribute__((aligned(16))) MfmaLds {  // 16-byte aligned: A operands load with ds_read_b128
-    MfmaBuf buf[2];
-    int src[kMC];                 // activation row of each M row (-1 = padding)
-    int dst[kMC];                 // output row of each M row
-};
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct global->LDS loads: lane l's 16 (or 4) bytes from g land at LDS byte
+// lds + 16*l (4*l); lds must be the same in every lane.  Written as inline asm
+// because the compiler, when it sees these loads, makes every later LDS read
+// wait for all of them (it cannot tell the ring's stages apart), which would
+// drain the ring each chunk; completion is tracked with explicit vmcnt waits
+// instead (the instructions have no register results).
+__device__ __forceinline__ uint32_t lds_addr(const void *lds) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8 *)lds);
+}
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds));
+}
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds));
+}
+
+constexpr int kWaitVm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+
+// Workgroup barrier without a memory fence (a fence would wait for every load
+// in flight); the asm clobbers keep the compiler from moving memory accesses
+// across it, and this wave's LDS reads are complete before it arrives.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // 8 consecutive weights of one row (codes dword, its block record) -> bf16x8.
 // (w >> 4s) & 0x000F000F | 0x64006400 holds the fp16 values 1024 + q of columns
@@ -86,10 +127,11 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, uint3
     return v;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int S>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_ffn_kernel(moe::FfnArgs a, int ntiles,
                                                                                            int n_groups) {
     constexpr int NMAT = GATEUP ? 2 : 1;
+    static_assert(S >= 2, "the ring needs two stages at least");
     const int K = GATEUP ? a.H : a.I;   // reduction length
     const int R = GATEUP ? a.I : a.H;   // weight rows (output columns)
     const int nblk = K >> 5;
@@ -118,78 +160,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const size_t cbytes = (size_t)R * K / 2;
     const uint16_t *act = GATEUP ? a.x : a.h;
 
-    __shared__ MfmaLds s;
+    // separate variables, not an array: the compiler then sees that a chunk's
+    // LDS reads cannot alias the loads in flight into the other stages, and
+    // does not wait for those before reading
+    __shared__ Stage<NMAT> st0, st1, st2, st3;
+    static_assert(S <= 4, "at most four stages");
+    const uint32_t a0 = lds_addr(&st0), a1 = lds_addr(&st1), a2 = S > 2 ? lds_addr(&st2) : 0u,
+                   a3 = S > 3 ? lds_addr(&st3) : 0u;
+    __shared__ int s_src[kMC];  // activation row of each M row
+    __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
     const uint32_t magic = fp16_magic_vgpr();
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;  // MFMA row-in-tile and k-quarter
     const int nchunks = K / kKC;
 
-    // per-thread share of one chunk's global loads
-    constexpr int kXLoads = kMC * (kKC * 2 / 16) / 256;  // 16-byte activation loads per thread
-    uint4 xr[kXLoads], wr[NMAT];
-    uint2 pr = make_uint2(0u, 0u);
-    auto load_chunk = [&](int c) {
-        const int k0 = c * kKC;
+    // this lane's global sources, fixed over a pass: weight rows of its wave
+    const int wrow = n0 + 32 * wave + (lane & 31);           // codes: lanes 0-31 half 0, 32-63 half 1
+    const int rrow = n0 + 32 * wave + (lane >> 1);           // records: 2 lanes per row
+    const uint8_t *wsrc[NMAT], *rsrc[NMAT];
 #pragma unroll
-        for (int q = 0; q < kXLoads; ++q) {  // activations: kMC rows x 128 B, 16 B per load
-            const int idx = tid + 256 * q, row = idx >> 3, ch = idx & 7;
-            const int src = s.src[row];
-            xr[q] = src >= 0 ? load_global_u4(act + (size_t)src * K + k0 + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int q = 0; q < NMAT; ++q) {  // codes: 128 rows x 32 B per matrix
-            const int row = tid >> 1, ch = tid & 1, n = n0 + row;
-            wr[q] = n < R ? load_stream_u4(mat[q] + (size_t)n * (K / 2) + k0 / 2 + ch * 16) : make_uint4(0u, 0u, 0u, 0u);
-        }
-        if (tid < NMAT * kNT) {  // records: 2 blocks x 4 B per row
-            const int q = tid / kNT, row = tid - q * kNT, n = n0 + row;
-            if (n < R) {
-                const uint8_t *rp = mat[q] + cbytes + ((size_t)n * nblk + (k0 >> 5)) * 4;
-                pr = make_uint2(load_stream_u32(rp), load_stream_u32(rp + 4));
-            } else {
-                pr = make_uint2(0u, 0u);
-            }
-        }
-    };
-    auto store_chunk = [&](int b) {
-        MfmaBuf &B = s.buf[b];
-#pragma unroll
-        for (int q = 0; q < kXLoads; ++q) {
-            const int idx = tid + 256 * q, row = idx >> 3, ch = idx & 7;
-            *reinterpret_cast<uint4 *>(&B.x[row * kXStride + ch * 16]) = xr[q];
-        }
-#pragma unroll
-        for (int q = 0; q < NMAT; ++q) {
-            const int row = tid >> 1, ch = tid & 1;
-            *reinterpret_cast<uint4 *>(&B.w[q][row * kWStride + ch * 16]) = wr[q];
-        }
-        if (tid < NMAT * kNT) {
-            const int q = tid / kNT, row = tid - q * kNT;
-            B.p[q][row] = pr;
-        }
-    };
+    for (int q = 0; q < NMAT; ++q) {
+        wsrc[q] = mat[q] + (size_t)wrow * (K / 2) + (lane >> 5) * 16;
+        rsrc[q] = mat[q] + cbytes + ((size_t)rrow * nblk + (lane & 1)) * 4;
+    }
 
     for (int m0 = 0; m0 < M; m0 += kMC) {
         const int mc = min(kMC, M - m0);
         const int mtiles = (mc + 15) >> 4;
-        __syncthreads();  // previous chunk done with s.src / s.dst and the buffers
+        __syncthreads();  // the previous pass is done with s_src / s_dst and the ring
         if (tid < kMC) {
             int src = -1, dst = -1;
-            if (tid < mc) {
-                const int m = m0 + tid;
-                if (routed) {
-                    const int p = a.pair_of_row[base + m];
-                    dst = p;
-                    src = GATEUP ? p / a.k : p;
-                } else {
-                    dst = a.T * a.k + m;
-                    src = GATEUP ? m : dst;
-                }
+            const int m = m0 + (tid < mc ? tid : 0);  // padding rows repeat the first row
+            if (routed) {
+                const int p = a.pair_of_row[base + m];
+                src = GATEUP ? p / a.k : p;
+                dst = p;
+            } else {
+                dst = a.T * a.k + m;
+                src = GATEUP ? m : dst;
             }
-            s.src[tid] = src;
-            s.dst[tid] = dst;
+            s_src[tid] = src;
+            s_dst[tid] = tid < mc ? dst : -1;
         }
         __syncthreads();
+        // activation loads of this wave: tile units wave + 4j (8 rows each).  All
+        // 96 rows are loaded whatever mtiles is (rows past the tokens repeat the
+        // first row and are never read), so every wave issues the same number
+        // of loads per chunk and the compiler can count them statically.
+        const uint16_t *xsrc[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int r = 8 * (wave + 4 * j) + (lane >> 3), pos = lane & 7;
+            xsrc[j] = act + (size_t)s_src[r] * K + 8 * (pos ^ (r & 7));
+        }
+        constexpr int per_stage = 3 + 2 * NMAT;  // loads each wave issues per chunk
+
+        // LDS byte address of stage st (uniform), then constant offsets
+        auto issue = [&](uint32_t st, int c) {
+            const int k0 = c * kKC;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) dma16(xsrc[j] + k0, st + (uint32_t)((wave + 4 * j) * 1024));
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q) {
+                dma16(wsrc[q] + k0 / 2, st + (uint32_t)(offsetof(Stage<NMAT>, w) + q * kNT * 32 + wave * 1024));
+                dma4(rsrc[q] + (k0 >> 5) * 4, st + (uint32_t)(offsetof(Stage<NMAT>, p) + q * kNT * 8 + wave * 256));
+            }
+        };
+
         f32x4_t acc[NMAT][kMaxMT][2];
 #pragma unroll
         for (int q = 0; q < NMAT; ++q)
@@ -198,13 +236,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) acc[q][mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        load_chunk(0);
-        store_chunk(0);
-        __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-            const int cur = c & 1;
-            if (c + 1 < nchunks) load_chunk(c + 1);  // in flight during this chunk's products
-            const MfmaBuf &B = s.buf[cur];
+        // Byte offsets of matrix q's codes and records in a stage, hidden from the
+        // optimiser: otherwise it pairs the reads of the two matrices into one
+        // ds_read2st64, whose merged memory operand no longer shows which stage it
+        // reads, and then waits for every load in flight before it.
+        int wq[NMAT], pq[NMAT];
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+            wq[q] = (int)(offsetof(Stage<NMAT>, w) + q * kNT * 32) + wave * 1024 + lq * 4;
+            pq[q] = (int)(offsetof(Stage<NMAT>, p) + q * kNT * 8) + wave * 256;
+            asm volatile("" : "+v"(wq[q]), "+v"(pq[q]));
+        }
+        auto compute = [&](const Stage<NMAT> &st) {
+            const uint8_t *sb = reinterpret_cast<const uint8_t *>(&st);
 #pragma unroll
             for (int kb = 0; kb < kKC / 32; ++kb) {
                 // B operands: this wave's 2 N tiles of each matrix
@@ -213,17 +257,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                 for (int q = 0; q < NMAT; ++q)
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
-                        const int row = wave * 32 + nt * 16 + lr;
-                        const uint32_t codes =
-                            *reinterpret_cast<const uint32_t *>(&B.w[q][row * kWStride + kb * 16 + lq * 4]);
-                        const uint2 rec2 = B.p[q][row];
-                        bo[q][nt] = dequant8(codes, kb == 0 ? rec2.x : rec2.y, magic);
+                        const int rl = nt * 16 + lr;  // row within the wave's 32
+                        const uint32_t codes = *reinterpret_cast<const uint32_t *>(sb + wq[q] + (kb * 32 + rl) * 16);
+                        const uint32_t rec = *reinterpret_cast<const uint32_t *>(sb + pq[q] + (rl * 2 + kb) * 4);
+                        bo[q][nt] = dequant8(codes, rec, magic);
                     }
 #pragma unroll
                 for (int mt = 0; mt < kMaxMT; ++mt) {
                     if (mt < mtiles) {
-                        const uint4 av =
-                            *reinterpret_cast<const uint4 *>(&B.x[(mt * 16 + lr) * kXStride + kb * 64 + lq * 16]);
+                        const int r = mt * 16 + lr;
+                        const uint4 av = *reinterpret_cast<const uint4 *>(
+                            &st.x[r * kXRow + (((kb * 4 + lq) ^ (r & 7)) * 16)]);
                         const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
                         for (int q = 0; q < NMAT; ++q)
@@ -234,9 +278,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                     }
                 }
             }
-            if (c + 1 < nchunks) store_chunk(cur ^ 1);
-            __syncthreads();
+        };
+
+        // One chunk: wait for its loads, barrier, refill the buffer freed by the
+        // previous chunk with chunk c + S - 1, multiply.  Every step issues one
+        // stage (past the last chunk it re-loads the last chunk into a buffer
+        // that is not read again), so exactly S - 2 stages are in flight behind
+        // the one being waited for, and the loop carries a fixed load count.
+        auto step = [&](const Stage<NMAT> &cur, uint32_t refill, int c) {
+            __builtin_amdgcn_s_waitcnt(kWaitVm((S - 2) * per_stage));
+            ring_barrier();
+            issue(refill, min(c + S - 1, nchunks - 1));
+            compute(cur);
+        };
+
+        issue(a0, 0);
+        if constexpr (S > 2) issue(a1, min(1, nchunks - 1));
+        if constexpr (S > 3) issue(a2, min(2, nchunks - 1));
+        for (int c0 = 0; c0 < nchunks; c0 += S) {
+            if constexpr (S == 2) {
+                step(st0, a1, c0);
+                if (c0 + 1 < nchunks) step(st1, a0, c0 + 1);
+            } else if constexpr (S == 3) {
+                step(st0, a2, c0);
+                if (c0 + 1 < nchunks) step(st1, a0, c0 + 1);
+                if (c0 + 2 < nchunks) step(st2, a1, c0 + 2);
+            } else {
+                step(st0, a3, c0);
+                if (c0 + 1 < nchunks) step(st1, a0, c0 + 1);
+                if (c0 + 2 < nchunks) step(st2, a1, c0 + 2);
+                if (c0 + 3 < nchunks) step(st3, a2, c0 + 3);
+            }
         }
+
+        // no load may still be writing LDS when the workgroup moves on or exits
+        __builtin_amdgcn_s_waitcnt(kWaitVm(0));
+
         // epilogue
 #pragma unroll
         for (int mt = 0; mt < kMaxMT; ++mt) {
@@ -248,7 +325,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                 for (int j = 0; j < 4; ++j) {
                     const int m = mt * 16 + lq * 4 + j;
                     if (m >= mc || n >= R) continue;
-                    const int row = s.dst[m];
+                    const int row = s_dst[m];
                     if (GATEUP) {
                         const float gv = acc[0][mt][nt][j], uv = acc[NMAT - 1][mt][nt][j];
                         a.h[(size_t)row * a.I + n] = (uint16_t)f32_to_bf16_bits(gv / (1.0f + expf(-gv)) * uv);
@@ -274,7 +351,8 @@ int mfma_gate_up(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     const int ntiles = (a.I + kNT - 1) / kNT;
     const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(mfma_ffn_kernel<true>, dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles, n_groups);
+    hipLaunchKernelGGL((mfma_ffn_kernel<true, kStagesGateUp>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
+                       n_groups);
     MOE_LAUNCH_CHECK("mfma_ffn_kernel<gate_up>");
     return MOE_OK;
 }
@@ -283,7 +361,8 @@ int mfma_down(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     const int ntiles = (a.H + kNT - 1) / kNT;
     const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(mfma_ffn_kernel<false>, dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles, n_groups);
+    hipLaunchKernelGGL((mfma_ffn_kernel<false, kStagesDown>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
+                       n_groups);
     MOE_LAUNCH_CHECK("mfma_ffn_kernel<down>");
     return MOE_OK;
 }
