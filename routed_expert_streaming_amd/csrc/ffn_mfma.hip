@@ -91,40 +91,69 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // 8 consecutive weights of one row (codes dword, its block record) -> bf16x8.
-// (w >> 4s) & 0x000F000F | 0x64006400 holds the fp16 values 1024 + q of columns
-// s and s+4; v_fma_mix_f32 widens each half and computes
-// scale*(1024+q) + (min - 1024*scale) in fp32 with one rounding, which equals
-// fmaf(scale, q, min) whenever min - 1024*scale is exact in fp32 (scale and min
+// Byte b of the dword holds column 2b in bits 0-3 and 2b+1 in bits 4-7.  OR-ing
+// a nibble into the mantissa of an fp16 constant gives an exact fp16 number:
+//   bits 0-3 into 0x6400 (1024, ulp 1)    -> 1024 + q
+//   bits 4-7 into 0x5400 (64, ulp 1/16)   ->   64 + q
+// so w & 0x000F000F | 0x64006400 holds columns 0 and 4, w & 0x00F000F0 |
+// 0x54005400 columns 1 and 5, and the same on w >> 8 columns 2, 6 and 3, 7:
+// four extractions for one shift.  v_fma_mix_f32 widens each half and computes
+// scale*(base + q) + (min - base*scale) in fp32 with one rounding, which equals
+// fmaf(scale, q, min) whenever min - base*scale is exact in fp32 (scale and min
 // within 2^12 of each other's magnitude); then round to bf16 in natural order.
 __device__ __forceinline__ float fma_half(uint32_t pair, int hi, float sc, float c) {
     const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(hi ? pair >> 16 : pair & 0xFFFFu));
     return fmaf((float)h, sc, c);
 }
 
-// The fp16 exponent pattern 0x6400 in both halves, held in a VGPR so that
-// (w & mask) | magic is one v_and_or_b32 (the mask goes in an SGPR).
-__device__ __forceinline__ uint32_t fp16_magic_vgpr() {
-    uint32_t m;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
-    return m;
+// Constants of the extraction: masks in SGPRs and the fp16 exponent patterns in
+// VGPRs, so that (w & mask) | pattern is one v_and_or_b32 (a VOP3 instruction
+// reads at most one scalar operand, and a literal not at all).
+struct Dequant {
+    uint32_t mask_lo, mask_hi;    // SGPR: 0x000F000F, 0x00F000F0
+    uint32_t magic_lo, magic_hi;  // VGPR: 0x64006400, 0x54005400
+};
+
+__device__ __forceinline__ Dequant dequant_consts() {
+    Dequant d;
+    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(d.mask_lo));
+    asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(d.mask_hi));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(d.magic_lo));
+    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(d.magic_hi));
+    return d;
 }
 
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, uint32_t magic) {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> bf16 pair (round to nearest even), lo in bits 0-15
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){lo, hi},
+                                                                bf16x2_t));
+}
+
+// (a & mask) | pattern as one instruction (the compiler splits it into two)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t pattern) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(pattern));
+    return r;
+}
+
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, const Dequant &d) {
     const float sc = fp16_bits_to_f32(rec & 0xFFFFu);
     const float mn = fp16_bits_to_f32(rec >> 16);
-    const float c = fmaf(-1024.0f, sc, mn);
-    const uint32_t mask = 0x000F000Fu;
-    float f[8];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const uint32_t p = ((codes >> (4 * s)) & mask) | (magic & ~mask);
-        f[s] = fma_half(p, 0, sc, c);
-        f[s + 4] = fma_half(p, 1, sc, c);
-    }
-    bf16x8_t v;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (__bf16)f[j];
-    return v;
+    const float c_lo = fmaf(-1024.0f, sc, mn);
+    const float c_hi = fmaf(-64.0f, sc, mn);
+    const uint32_t c8 = codes >> 8;
+    const uint32_t p0 = and_or(codes, d.mask_lo, d.magic_lo);  // columns 0, 4
+    const uint32_t p1 = and_or(codes, d.mask_hi, d.magic_hi);  // columns 1, 5
+    const uint32_t p2 = and_or(c8, d.mask_lo, d.magic_lo);     // columns 2, 6
+    const uint32_t p3 = and_or(c8, d.mask_hi, d.magic_hi);     // columns 3, 7
+    // columns (0,1) (2,3) (4,5) (6,7), each pair rounded to bf16 by one v_cvt_pk_bf16_f32
+    const uint32_t w01 = pack_bf16(fma_half(p0, 0, sc, c_lo), fma_half(p1, 0, sc, c_hi));
+    const uint32_t w23 = pack_bf16(fma_half(p2, 0, sc, c_lo), fma_half(p3, 0, sc, c_hi));
+    const uint32_t w45 = pack_bf16(fma_half(p0, 1, sc, c_lo), fma_half(p1, 1, sc, c_hi));
+    const uint32_t w67 = pack_bf16(fma_half(p2, 1, sc, c_lo), fma_half(p3, 1, sc, c_hi));
+    return __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, w45, w67));
 }
 
 template <bool GATEUP, int S>
@@ -169,7 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                    a3 = S > 3 ? lds_addr(&st3) : 0u;
     __shared__ int s_src[kMC];  // activation row of each M row
     __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
-    const uint32_t magic = fp16_magic_vgpr();
+    const Dequant dq = dequant_consts();
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;  // MFMA row-in-tile and k-quarter
@@ -260,15 +289,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                         const int rl = nt * 16 + lr;  // row within the wave's 32
                         const uint32_t codes = *reinterpret_cast<const uint32_t *>(sb + wq[q] + (kb * 32 + rl) * 16);
                         const uint32_t rec = *reinterpret_cast<const uint32_t *>(sb + pq[q] + (rl * 2 + kb) * 4);
-                        bo[q][nt] = dequant8(codes, rec, magic);
+                        bo[q][nt] = dequant8(codes, rec, dq);
                     }
+                // A operands of every M tile read at once (rows past the tokens hold
+                // valid data), so the LDS latency is paid once per 32 columns
+                uint4 av[kMaxMT];
+#pragma unroll
+                for (int mt = 0; mt < kMaxMT; ++mt) {
+                    const int r = mt * 16 + lr;
+                    av[mt] = *reinterpret_cast<const uint4 *>(&st.x[r * kXRow + (((kb * 4 + lq) ^ (r & 7)) * 16)]);
+                }
 #pragma unroll
                 for (int mt = 0; mt < kMaxMT; ++mt) {
                     if (mt < mtiles) {
-                        const int r = mt * 16 + lr;
-                        const uint4 av = *reinterpret_cast<const uint4 *>(
-                            &st.x[r * kXRow + (((kb * 4 + lq) ^ (r & 7)) * 16)]);
-                        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
+                        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[mt]);
 #pragma unroll
                         for (int q = 0; q < NMAT; ++q)
 #pragma unroll
