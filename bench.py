@@ -168,7 +168,8 @@ def layer_leg(torch, name: str, path: int, iters: int):
         return a.elapsed_time(b) / iters
 
     res = {"workload": f"{name}, one resident layer", "tokens": T, "path": {L.MOE_FFN_MFMA: "mfma",
-                                                                              L.MOE_FFN_GROUPED: "grouped"}[path]}
+                                                                              L.MOE_FFN_GROUPED: "grouped",
+                                                                              L.MOE_FFN_SPLIT: "split"}[path]}
     res["router_ms"] = timed(lambda: st.route(x, 0))
     res["permute_ms"] = timed(lambda: L.moe_permute(st.idx[0], T, k, E, cnt, off, por))
     res["gate_up_ms"] = timed(lambda: L.moe_expert_gate_up(x[0], T, H, I, E, st.idx[0], k, cnt, off, por,
@@ -411,7 +412,7 @@ def main():
         result["streaming"] = streaming_leg(torch, args, ms_per_step)
     if not args.no_layer_legs:
         from routed_expert_streaming_amd import _lib as L
-        result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_GROUPED, 20)
+        result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_SPLIT, 20)
         result["layer_prefill2048"] = layer_leg(torch, "prefill2048_stream", L.MOE_FFN_MFMA, 3)
     print(json.dumps(result), flush=True)
 

@@ -190,9 +190,18 @@ int64_t moe_cache_trace(const moe_cache *cache, int64_t *cmds, int64_t max_cmds)
  * (nonzero = compute this expert's pairs) or NULL for all.
  * y: [T*k + (shared ? T : 0), H] fp32; row t*k+i is pair (t, i), row T*k+t is the
  * shared expert for token t.  Rows of masked-off pairs are left untouched.
- * path: MOE_FFN_AUTO picks by T*k; the others force a kernel family (for tests).
+ * path: MOE_FFN_AUTO picks by T and k (pairs for T*k <= 64, MFMA for T >= 128,
+ * split in between when H and I are multiples of 128, else grouped); the others
+ * force a kernel family:
+ *   MOE_FFN_PAIRS   dequant-GEMV, one group per (token, slot) pair;
+ *   MOE_FFN_GROUPED dequant-GEMV, one group per expert (bit-identical to PAIRS);
+ *   MOE_FFN_MFMA    grouped bf16 matrix-core kernels (weights rounded to bf16;
+ *                   H and I multiples of 128);
+ *   MOE_FFN_SPLIT   one group per expert: experts with up to 4 tokens on the
+ *                   dequant-GEMV, the others on the MFMA kernels (H and I
+ *                   multiples of 128, else as GROUPED).
  * workspace: moe_expert_ffn_workspace_bytes(...) bytes, contents don't care. */
-enum { MOE_FFN_AUTO = 0, MOE_FFN_PAIRS = 1, MOE_FFN_GROUPED = 2, MOE_FFN_MFMA = 3 };
+enum { MOE_FFN_AUTO = 0, MOE_FFN_PAIRS = 1, MOE_FFN_GROUPED = 2, MOE_FFN_MFMA = 3, MOE_FFN_SPLIT = 4 };
 size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int has_shared);
 int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
                    const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
@@ -206,7 +215,8 @@ int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t 
  * count/offset/pair_of_row: a permutation from moe_permute on the same topk_idx
  * (one kernel group per expert, weights read once per expert), or all three NULL
  * (one group per (token, slot) pair).  path: MOE_FFN_AUTO follows the presence
- * of the permutation; MOE_FFN_GROUPED requires it. */
+ * of the permutation (with it: MFMA for T >= 128, else split); MOE_FFN_GROUPED,
+ * MOE_FFN_MFMA and MOE_FFN_SPLIT require it. */
 int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
                        const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
                        const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,

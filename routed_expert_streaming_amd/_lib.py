@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_E_ARG, MOE_E_SHAPE, MOE_E_NOT_PINNED, MOE_E_NOMEM, MOE_E_CAPACITY, MOE_E_HIP, MOE_E_STATE = \
     0, -1, -2, -3, -4, -5, -6, -7
-MOE_FFN_AUTO, MOE_FFN_PAIRS, MOE_FFN_GROUPED, MOE_FFN_MFMA = 0, 1, 2, 3
+MOE_FFN_AUTO, MOE_FFN_PAIRS, MOE_FFN_GROUPED, MOE_FFN_MFMA, MOE_FFN_SPLIT = 0, 1, 2, 3, 4
 
 _lib = None
 

@@ -20,6 +20,7 @@ struct FfnArgs {
     float *y;                   // [T*k + T*shared, H] fp32 expert outputs
     const uint8_t **pair_slab;  // [T*k + T*shared] or nullptr: slab of each pair (nullptr = masked),
                                 // written by the one-token gate/up kernel, read by the down kernel
+    int min_m, max_m;           // grouped kernels skip groups with fewer / more tokens than these
 };
 
 // Router finish fused into the one-token gate/up kernel: the per-slice fp64
@@ -57,6 +58,9 @@ int mfma_down(const FfnArgs &a, hipStream_t s);
 
 // Tokens from which the automatic choice uses the MFMA kernels.
 constexpr int kMfmaMinTokens = 128;
+// Tokens of a group that one grouped-GEMV pass stages (LDS for the activations);
+// larger groups go to the MFMA kernels when their shapes allow.
+constexpr int kGemvOnePass = 4;
 
 // Counting sort of pairs by expert (see moe_permute).
 int permute_launch(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,

@@ -169,7 +169,7 @@ int validate_ffn(const void *act, int T, int H, int I, int E, const int32_t *top
         return moe::fail(MOE_E_SHAPE, "%s: H=%d and I=%d must be positive multiples of 32", who, H, I);
     if (H > 16384 || I > 16384) return moe::fail(MOE_E_SHAPE, "%s: H=%d I=%d above 16384", who, H, I);
     if (E < 1 || E > kPermMaxE || k < 1 || k > E) return moe::fail(MOE_E_SHAPE, "%s: E=%d k=%d", who, E, k);
-    if (path < MOE_FFN_AUTO || path > MOE_FFN_MFMA) return moe::fail(MOE_E_ARG, "%s: path=%d", who, path);
+    if (path < MOE_FFN_AUTO || path > MOE_FFN_SPLIT) return moe::fail(MOE_E_ARG, "%s: path=%d", who, path);
     return MOE_OK;
 }
 
@@ -181,9 +181,10 @@ int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, 
     const bool have_perm = count && offset && pair_of_row;
     if ((count || offset || pair_of_row) && !have_perm)
         return moe::fail(MOE_E_ARG, "%s: count, offset and pair_of_row go together", who);
-    if ((path == MOE_FFN_GROUPED || path == MOE_FFN_MFMA) && !have_perm)
-        return moe::fail(MOE_E_ARG, "%s: grouped and MFMA paths need a permutation", who);
-    const bool grouped = (path == MOE_FFN_GROUPED) || (path == MOE_FFN_MFMA) || (path == MOE_FFN_AUTO && have_perm);
+    if ((path == MOE_FFN_GROUPED || path == MOE_FFN_MFMA || path == MOE_FFN_SPLIT) && !have_perm)
+        return moe::fail(MOE_E_ARG, "%s: grouped, MFMA and split paths need a permutation", who);
+    const bool grouped = (path == MOE_FFN_GROUPED) || (path == MOE_FFN_MFMA) || (path == MOE_FFN_SPLIT) ||
+                         (path == MOE_FFN_AUTO && have_perm);
     a = moe::FfnArgs{};
     a.x = x;
     a.h = h;
@@ -202,8 +203,28 @@ int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, 
     a.count = count;
     a.offset = offset;
     a.pair_of_row = pair_of_row;
+    a.min_m = 0;
+    a.max_m = 1 << 30;
     *max_m = grouped ? T : (shared ? T : 1);
     return MOE_OK;
+}
+
+// Grouped dequant-GEMV call.  With split (when the shapes allow the MFMA
+// kernels and some group may hold more tokens than one GEMV pass stages) the
+// GEMV takes the groups of up to kGemvOnePass tokens (each weight read once,
+// dotted with every token) and the MFMA kernel the larger ones (each weight
+// dequantised once for all its tokens) -- rather than re-reading weights or
+// re-staging activations for every pass.
+template <bool GATEUP>
+int grouped_gemv(moe::FfnArgs a, int max_m, bool split, hipStream_t s) {
+    if (!split || !a.grouped || !moe::mfma_supported(a) || max_m <= moe::kGemvOnePass)
+        return GATEUP ? moe::ffn_gemv_gate_up(a, max_m, s) : moe::ffn_gemv_down(a, max_m, s);
+    a.max_m = moe::kGemvOnePass;
+    int rc = GATEUP ? moe::ffn_gemv_gate_up(a, moe::kGemvOnePass, s) : moe::ffn_gemv_down(a, moe::kGemvOnePass, s);
+    if (rc != MOE_OK) return rc;
+    a.min_m = moe::kGemvOnePass + 1;
+    a.max_m = 1 << 30;
+    return GATEUP ? moe::mfma_gate_up(a, s) : moe::mfma_down(a, s);
 }
 
 // Kernel family for a grouped call: MFMA when forced, or automatically for many tokens.
@@ -215,7 +236,12 @@ bool use_mfma(const moe::FfnArgs &a, int path) {
 // Automatic path of the one-call entry points.
 int auto_path(int T, int k) {
     if ((long long)T * k <= 64) return MOE_FFN_PAIRS;
-    return T >= moe::kMfmaMinTokens ? MOE_FFN_MFMA : MOE_FFN_GROUPED;
+    return T >= moe::kMfmaMinTokens ? MOE_FFN_MFMA : MOE_FFN_SPLIT;
+}
+
+// Split grouped dispatch for an explicit split path, or automatic with a permutation.
+bool use_split(const moe::FfnArgs &a, int path) {
+    return a.grouped && (path == MOE_FFN_SPLIT || path == MOE_FFN_AUTO);
 }
 
 }  // namespace
@@ -236,7 +262,7 @@ extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E,
     if (use_mfma(a, path)) return moe::mfma_gate_up(a, (hipStream_t)stream);
     if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_gate_up: MFMA path needs H, I multiples of 128");
     if (moe::decode_supported(a)) return moe::decode_gate_up(a, (hipStream_t)stream);
-    return moe::ffn_gemv_gate_up(a, max_m, (hipStream_t)stream);
+    return grouped_gemv<true>(a, max_m, use_split(a, path), (hipStream_t)stream);
 }
 
 extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k,
@@ -255,7 +281,7 @@ extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, co
     if (use_mfma(a, path)) return moe::mfma_down(a, (hipStream_t)stream);
     if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_down: MFMA path needs H, I multiples of 128");
     if (moe::decode_supported(a)) return moe::decode_down(a, nullptr, nullptr, (hipStream_t)stream);
-    return moe::ffn_gemv_down(a, max_m, (hipStream_t)stream);
+    return grouped_gemv<false>(a, max_m, use_split(a, path), (hipStream_t)stream);
 }
 
 extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
@@ -272,7 +298,7 @@ extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, con
         return moe::fail(MOE_E_NOMEM, "expert_ffn: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
     if (path == MOE_FFN_AUTO) {
         path = auto_path(T, k);
-        if (path == MOE_FFN_MFMA && (H % 128 || I % 128)) path = MOE_FFN_GROUPED;
+        if ((path == MOE_FFN_MFMA || path == MOE_FFN_SPLIT) && (H % 128 || I % 128)) path = MOE_FFN_GROUPED;
     }
     if (path != MOE_FFN_PAIRS && (long long)T * k > kPermMaxPairs)
         return moe::fail(MOE_E_SHAPE, "expert_ffn: grouped paths need T*k <= %d", kPermMaxPairs);
@@ -280,7 +306,7 @@ extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, con
     char *ws = (char *)workspace;
     uint16_t *h = (uint16_t *)(ws + Ly.h);
     int32_t *count = nullptr, *offset = nullptr, *pairs = nullptr;
-    if (path == MOE_FFN_GROUPED || path == MOE_FFN_MFMA) {
+    if (path == MOE_FFN_GROUPED || path == MOE_FFN_MFMA || path == MOE_FFN_SPLIT) {
         count = (int32_t *)(ws + Ly.count);
         offset = (int32_t *)(ws + Ly.offset);
         pairs = (int32_t *)(ws + Ly.pairs);

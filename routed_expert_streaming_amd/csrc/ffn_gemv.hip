@@ -27,6 +27,7 @@
 namespace {
 
 constexpr int kMT = 4;  // tokens staged per pass
+static_assert(kMT >= moe::kGemvOnePass, "a one-pass group must fit one staging pass");
 
 
 struct Group {
@@ -47,11 +48,11 @@ __device__ __forceinline__ Group resolve_group(const moe::FfnArgs &a, int g) {
             e = a.topk_idx[g];
             M = 1;
         }
-        if (M == 0 || (a.mask && a.mask[e] == 0)) return out;
+        if (M == 0 || M < a.min_m || M > a.max_m || (a.mask && a.mask[e] == 0)) return out;
         out.slab = (const uint8_t *)a.table[e];
         out.M = M;
         out.routed = g;
-    } else if (a.shared) {
+    } else if (a.shared && a.T >= a.min_m && a.T <= a.max_m) {
         out.slab = (const uint8_t *)a.shared;
         out.M = a.T;
     }
@@ -98,23 +99,35 @@ __device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ act, int
     }
 }
 
-// RIT rows per lane-group; the weights of all of them are requested before the
-// activations are staged, so each wave keeps RIT*BPL*(2 or 1)*16 bytes per lane
-// in flight while the workgroup waits for the staging barrier.
+// One workgroup owns one group (expert) and `iters` row steps of ROWS_PER_STEP
+// rows (RPW rows per wave per step): it stages the group's activation rows in
+// LDS once per pass of up to mt_cap tokens and walks its steps with the weights
+// of the next D steps in flight in registers (a ring of D slots, the loop
+// unrolled by D so every slot is a fixed set of registers).  The weights of a
+// row are dotted with every staged token before the slot is refilled.
 #ifndef MOE_GEMV_WAVES_PER_EU
 #define MOE_GEMV_WAVES_PER_EU 2
 #endif
-template <int LPR, int BPL, int RIT, bool GATEUP>
+template <int BPL, bool GATEUP>
+struct GemvSlot {
+    uint4 c0[BPL], c1[GATEUP ? BPL : 1];
+    uint32_t p0[BPL], p1[GATEUP ? BPL : 1];
+};
+
+template <int LPR, int BPL, int D, bool GATEUP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_GEMV_WAVES_PER_EU)))
-void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap) {
-    constexpr int RPW = 64 / LPR;                // rows per wave at a time
-    constexpr int ROWS_PER_WG = 4 * RPW * RIT;   // rows per workgroup
+void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
+    constexpr int RPW = 64 / LPR;              // rows per wave per step
+    constexpr int ROWS_PER_STEP = 4 * RPW;     // rows per workgroup per step
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
     const int nblk = K >> 5;
     const int g = blockIdx.x / tiles, tile = blockIdx.x - g * tiles;
     const Group gr = resolve_group(a, g);
     if (gr.M == 0) return;
+    const int row0 = tile * iters * ROWS_PER_STEP;
+    if (row0 >= R) return;
+    const int nsteps = min(iters, (R - row0 + ROWS_PER_STEP - 1) / ROWS_PER_STEP);
 
     const size_t m13 = (size_t)a.I * a.H * 5 / 8;  // bytes of W1 (= W3)
     const uint8_t *mat0 = gr.slab + (GATEUP ? 0 : 2 * m13);
@@ -131,29 +144,55 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap) {
     const uint32_t magic = moe_magic_vgpr();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane / LPR, c = lane % LPR;
-    const int r0 = tile * ROWS_PER_WG + wave * RPW + sub;
+    const int rbase = row0 + wave * RPW + sub;  // this lane group's row in step 0
 
-    uint4 c0[RIT][BPL], c1[RIT][BPL];
-    uint32_t p0[RIT][BPL], p1[RIT][BPL];
-#pragma unroll
-    for (int i = 0; i < RIT; ++i) {
-        const int r = r0 + i * 4 * RPW;
+    // rows past R re-read row R-1 (valid memory) and are not stored
+    auto load = [&](GemvSlot<BPL, GATEUP> &sl, int step) {
+        const int r = min(rbase + step * ROWS_PER_STEP, R - 1);
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
-            const int blk = c + b * LPR;
-            if (r < R && blk < nblk) {
-                c0[i][b] = load_stream_u4(mat0 + (size_t)r * (K / 2) + 16 * blk);
-                p0[i][b] = load_stream_u32(par0 + ((size_t)r * nblk + blk) * 4);
-                if (GATEUP) {
-                    c1[i][b] = load_stream_u4(mat1 + (size_t)r * (K / 2) + 16 * blk);
-                    p1[i][b] = load_stream_u32(par1 + ((size_t)r * nblk + blk) * 4);
+            const int blk = min(c + b * LPR, nblk - 1);
+            sl.c0[b] = load_stream_u4(mat0 + (size_t)r * (K / 2) + 16 * blk);
+            sl.p0[b] = load_stream_u32(par0 + ((size_t)r * nblk + blk) * 4);
+            if constexpr (GATEUP) {
+                sl.c1[b] = load_stream_u4(mat1 + (size_t)r * (K / 2) + 16 * blk);
+                sl.p1[b] = load_stream_u32(par1 + ((size_t)r * nblk + blk) * 4);
+            }
+        }
+    };
+    auto compute = [&](const GemvSlot<BPL, GATEUP> &sl, int step, int mcount) {
+        const int r = rbase + step * ROWS_PER_STEP;
+        for (int m = 0; m < mcount; ++m) {
+            float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                const int blk = c + b * LPR;
+                if (blk < nblk) {
+                    const uint4 *xb = X + (size_t)(m * 4) * nblk + blk;
+                    const float Sb = S[m * nblk + blk];
+                    v0 += moe_block_value(sl.p0[b], moe_block_dot(sl.c0[b], xb, nblk, magic), Sb);
+                    if constexpr (GATEUP) v1 += moe_block_value(sl.p1[b], moe_block_dot(sl.c1[b], xb, nblk, magic), Sb);
+                }
+            }
+            v0 = moe_group_sum<LPR>(v0);
+            if constexpr (GATEUP) v1 = moe_group_sum<LPR>(v1);
+            if (moe_group_sum_owner<LPR>(c) && r < R) {
+                if constexpr (GATEUP) {
+                    const float hval = v0 / (1.0f + expf(-v0)) * v1;
+                    a.h[(size_t)out_rows[m] * a.I + r] = (uint16_t)f32_to_bf16_bits(hval);
+                } else {
+                    a.y[(size_t)out_rows[m] * a.H + r] = v0;
                 }
             }
         }
-    }
+    };
 
+    GemvSlot<BPL, GATEUP> slot[D];
     for (int pass = 0; pass < gr.M; pass += mt_cap) {
         const int mcount = min(mt_cap, gr.M - pass);
+        // the first D steps' weights are requested before the activations are staged
+#pragma unroll
+        for (int d = 0; d < D; ++d) load(slot[d], d);
         if (threadIdx.x < mcount) {
             const int row = group_row(a, gr, pass + threadIdx.x);
             out_rows[threadIdx.x] = row;
@@ -162,69 +201,54 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap) {
         __syncthreads();
         stage_rows(GATEUP ? a.x : a.h, K, src_rows, mcount, X, S);
         __syncthreads();
-
+        for (int i0 = 0; i0 < nsteps; i0 += D) {
 #pragma unroll
-        for (int i = 0; i < RIT; ++i) {
-            const int r = r0 + i * 4 * RPW;
-            if (r >= R) break;  // uniform within a lane group
-            for (int m = 0; m < mcount; ++m) {
-                float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-                for (int b = 0; b < BPL; ++b) {
-                    const int blk = c + b * LPR;
-                    if (blk < nblk) {
-                        const uint4 *xb = X + (size_t)(m * 4) * nblk + blk;
-                        const float Sb = S[m * nblk + blk];
-                        v0 += moe_block_value(p0[i][b], moe_block_dot(c0[i][b], xb, nblk, magic), Sb);
-                        if (GATEUP) v1 += moe_block_value(p1[i][b], moe_block_dot(c1[i][b], xb, nblk, magic), Sb);
-                    }
-                }
-                v0 = moe_group_sum<LPR>(v0);
-                if (GATEUP) v1 = moe_group_sum<LPR>(v1);
-                if (moe_group_sum_owner<LPR>(c)) {
-                    if (GATEUP) {
-                        const float hval = v0 / (1.0f + expf(-v0)) * v1;
-                        a.h[(size_t)out_rows[m] * a.I + r] = (uint16_t)f32_to_bf16_bits(hval);
-                    } else {
-                        a.y[(size_t)out_rows[m] * a.H + r] = v0;
-                    }
+            for (int d = 0; d < D; ++d) {
+                const int i = i0 + d;
+                if (i < nsteps) {
+                    compute(slot[d], i, mcount);
+                    if (i + D < nsteps) load(slot[d], i + D);
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();  // the next pass restages X and the row tables
     }
 }
 
-// rows requested up front per lane group: about MOE_GEMV_BLOCKS_IN_FLIGHT
-// 16-byte blocks per lane (at least one row)
+// rows of one row step in flight per wave: D steps of (GATEUP ? 2 : 1) * BPL
+// 16-byte blocks per lane, about MOE_GEMV_BLOCKS_IN_FLIGHT blocks
 #ifndef MOE_GEMV_BLOCKS_IN_FLIGHT
-#define MOE_GEMV_BLOCKS_IN_FLIGHT 4
+#define MOE_GEMV_BLOCKS_IN_FLIGHT 6
 #endif
 template <int BPL, bool GATEUP>
-constexpr int rows_in_flight() {
-    return ((GATEUP ? 2 : 1) * BPL >= MOE_GEMV_BLOCKS_IN_FLIGHT) ? 1
-                                                                 : MOE_GEMV_BLOCKS_IN_FLIGHT / ((GATEUP ? 2 : 1) * BPL);
+constexpr int steps_in_flight() {
+    constexpr int per = (GATEUP ? 2 : 1) * BPL;
+    return per >= MOE_GEMV_BLOCKS_IN_FLIGHT ? 1 : (MOE_GEMV_BLOCKS_IN_FLIGHT + per - 1) / per;
 }
+#ifndef MOE_GEMV_ITERS
+#define MOE_GEMV_ITERS 8
+#endif
 
 template <int LPR, int BPL, bool GATEUP>
 int launch_one(const moe::FfnArgs &a, int R, int K, int n_groups, int max_m, hipStream_t s) {
-    constexpr int RIT = rows_in_flight<BPL, GATEUP>();
-    constexpr int ROWS_PER_WG = 4 * (64 / LPR) * RIT;
-    const int tiles = (R + ROWS_PER_WG - 1) / ROWS_PER_WG;
+    constexpr int D = steps_in_flight<BPL, GATEUP>();
+    constexpr int ROWS_PER_STEP = 4 * (64 / LPR);
+    const int iters = MOE_GEMV_ITERS;
+    const int tiles = (R + ROWS_PER_STEP * iters - 1) / (ROWS_PER_STEP * iters);
     const int nblk = K / 32;
     const int mt_cap = max_m < kMT ? max_m : kMT;
     const size_t lds_bytes = (size_t)mt_cap * nblk * (4 * 16 + 4);
     if (lds_bytes > 64 * 1024) {
         static bool raised = false;
         if (!raised) {
-            hipError_t e = hipFuncSetAttribute((const void *)ffn_gemv_kernel<LPR, BPL, RIT, GATEUP>,
+            hipError_t e = hipFuncSetAttribute((const void *)ffn_gemv_kernel<LPR, BPL, D, GATEUP>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
             if (e != hipSuccess) return moe::fail_hip(e, "hipFuncSetAttribute(ffn_gemv_kernel)");
             raised = true;
         }
     }
-    hipLaunchKernelGGL((ffn_gemv_kernel<LPR, BPL, RIT, GATEUP>), dim3((unsigned)n_groups * tiles), dim3(256), lds_bytes, s,
-                       a, tiles, mt_cap);
+    hipLaunchKernelGGL((ffn_gemv_kernel<LPR, BPL, D, GATEUP>), dim3((unsigned)n_groups * tiles), dim3(256), lds_bytes,
+                       s, a, tiles, mt_cap, iters);
     MOE_LAUNCH_CHECK("ffn_gemv_kernel");
     return MOE_OK;
 }

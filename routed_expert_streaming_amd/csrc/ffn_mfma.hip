@@ -176,11 +176,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const bool routed = g < a.n_routed_groups;
     if (routed) {
         M = __builtin_amdgcn_readfirstlane(a.count[g]);  // uniform: M-tile checks become scalar branches
-        if (M == 0 || (a.mask && a.mask[g] == 0)) return;
+        if (M == 0 || M < a.min_m || M > a.max_m || (a.mask && a.mask[g] == 0)) return;
         slab = (const uint8_t *)a.table[g];
         base = a.offset[g];
     } else {
-        if (!a.shared) return;
+        if (!a.shared || a.T < a.min_m || a.T > a.max_m) return;
         slab = (const uint8_t *)a.shared;
         M = a.T;
     }

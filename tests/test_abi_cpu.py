@@ -86,6 +86,11 @@ def test_ffn_combine_permute_validation():
     bad = list(args); bad[12] = ws - 1
     assert _status(L.moe_expert_ffn, *bad) == L.MOE_E_NOMEM
     assert _status(L.moe_expert_ffn, *args, 7) == L.MOE_E_ARG
+    assert _status(L.moe_expert_ffn, *args, L.MOE_FFN_SPLIT + 1) == L.MOE_E_ARG
+    # grouped, MFMA and split kernels need the permutation
+    for path in (L.MOE_FFN_GROUPED, L.MOE_FFN_MFMA, L.MOE_FFN_SPLIT):
+        assert _status(L.moe_expert_gate_up, FAKE, 4, 256, 128, 16, FAKE, 2, None, None, None, FAKE, None, None,
+                       FAKE, path) == L.MOE_E_ARG
     assert _status(L.moe_combine, None, FAKE, 4, 2, 256, 0, FAKE) == L.MOE_E_ARG
     assert _status(L.moe_combine, FAKE, FAKE, 4, 2, 254, 0, FAKE) == L.MOE_E_SHAPE
     assert _status(L.moe_permute, FAKE, 4096, 8, 256, FAKE, FAKE, FAKE) == L.MOE_E_SHAPE

@@ -265,7 +265,7 @@ def test_layer_parity_all_paths(name, T, H, I, E, k, shared, bias, rows):
     results = {}
     paths = [L.MOE_FFN_PAIRS, L.MOE_FFN_GROUPED]
     mfma_ok = H % 128 == 0 and I % 128 == 0
-    for path in paths + ([L.MOE_FFN_MFMA] if mfma_ok else []):
+    for path in paths + ([L.MOE_FFN_MFMA, L.MOE_FFN_SPLIT] if mfma_ok else []):
         idx, y, out = lay.run(path)
         assert np.array_equal(idx, ref["idx"])
         sel = slice(None) if rows is None else rows
@@ -279,6 +279,17 @@ def test_layer_parity_all_paths(name, T, H, I, E, k, shared, bias, rows):
         assert ei.value.status == L.MOE_E_SHAPE
     else:  # MFMA run twice gives the same bits
         assert np.array_equal(lay.run(L.MOE_FFN_MFMA)[2], results[L.MOE_FFN_MFMA][1])
+        # split: experts with up to 4 tokens on the GEMV (their rows equal the grouped
+        # path's bit for bit), the others on MFMA (their rows equal the MFMA path's)
+        y_s = results[L.MOE_FFN_SPLIT][0]
+        counts = np.bincount(ref["idx"].ravel(), minlength=E)
+        pair_counts = counts[ref["idx"]].ravel()  # tokens of the expert of each (token, slot) pair
+        small = pair_counts <= 4
+        assert np.array_equal(y_s[:T * k][small], results[L.MOE_FFN_GROUPED][0][:T * k][small])
+        assert np.array_equal(y_s[:T * k][~small], results[L.MOE_FFN_MFMA][0][:T * k][~small])
+        if shared:
+            src = L.MOE_FFN_GROUPED if T <= 4 else L.MOE_FFN_MFMA
+            assert np.array_equal(y_s[T * k:], results[src][0][T * k:])
     # both GEMV kernel groupings compute each (token, expert) pair with the same arithmetic
     assert np.array_equal(results[paths[0]][0], results[paths[1]][0])
     assert np.array_equal(results[paths[0]][1], results[paths[1]][1])
