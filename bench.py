@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the streamed-decode (PCIe) leg")
     ap.add_argument("--stream-workload", default="decode1_stream")
+    ap.add_argument("--stream-layers", type=int, default=0,
+                    help="layers of the streamed leg (0 = the configuration's; fewer when its host pool exceeds what "
+                         "the machine lets one process pin)")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
     ap.add_argument("--no-layer-legs", action="store_true",
@@ -92,15 +95,46 @@ def link_peak(torch, slab_bytes: int):
     return best, slabs
 
 
+def resident_step_ms(torch, cfg, layers: int, steps: int = 8) -> float:
+    """Per-step time of a streamed configuration with every expert resident (the
+    compute the copies have to hide), on the same synthetic inputs."""
+    from routed_expert_streaming_amd.runtime import MoEStack
+
+    st = MoEStack(cfg, cap=1.0, layers=layers)
+    xs = [st.make_inputs(s) for s in range(4)]
+    out = st.new_output()
+    for s in range(2):
+        st.forward(xs[s % 4], out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(steps):
+        st.forward(xs[s % 4], out)
+    b.record()
+    torch.cuda.synchronize()
+    st.close()
+    del st, xs, out
+    torch.cuda.empty_cache()
+    return a.elapsed_time(b) / steps
+
+
 def streaming_leg(torch, args, resident_ms_per_step: float):
     """The streamed decode workload: expert cache capped per layer, misses copied
-    from pinned host RAM over PCIe on a copy stream while earlier layers compute."""
+    from pinned host RAM over PCIe on a copy stream while earlier layers compute.
+    resident_ms_per_step: the same shapes with every expert resident (measured
+    here when the streamed configuration's shapes differ from the timed one's)."""
     import synth
     from routed_expert_streaming_amd.runtime import MoEStack
 
     cfg = synth.get(args.stream_workload)
-    log(f"streaming leg: {cfg.description}")
-    st = MoEStack(cfg)
+    main = synth.get(args.workload)
+    layers = args.stream_layers or cfg.layers
+    shape = lambda c, n: (n, c.tokens, c.hidden, c.inter, c.experts, c.shared, c.top_k)
+    if shape(cfg, layers) != shape(main, main.layers):
+        resident_ms_per_step = resident_step_ms(torch, cfg, layers)
+        log(f"{cfg.name} ({layers} layers) with every expert resident: {resident_ms_per_step:.3f} ms/step")
+    log(f"streaming leg: {cfg.description}" + (f", {layers} of its {cfg.layers} layers" if layers != cfg.layers else ""))
+    st = MoEStack(cfg, layers=layers)
     peak, slab_rate = link_peak(torch, st.slab)
     log(f"pinned H2D: {peak:.1f} GB/s (1 GiB copies), {slab_rate:.1f} GB/s (back-to-back {st.slab} B slabs)")
     n_in = 32
@@ -121,7 +155,7 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     ms_step = wall / args.stream_steps * 1e3
     copy_ms = nbytes / args.stream_steps / (slab_rate * 1e9) * 1e3  # copy-stream busy time at the slab copy rate
     h2d = nbytes / wall / 1e9
-    res = {"workload": cfg.name, "layers": cfg.layers, "cache_slots_per_layer": st.C,
+    res = {"workload": cfg.name, "layers": layers, "cache_slots_per_layer": st.C,
            "tokens_per_s": round(args.stream_steps * cfg.tokens / wall, 2), "ms_per_step": round(ms_step, 3),
            "hit_rate": round(hits / max(hits + misses, 1), 4), "h2d_bytes_per_step": nbytes // args.stream_steps,
            "h2d_GBps": round(h2d, 2), "link_peak_GBps": round(peak, 2), "slab_copy_GBps": round(slab_rate, 2),
@@ -129,6 +163,9 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
            "copy_busy_ms_per_step": round(copy_ms, 3), "resident_ms_per_step": round(resident_ms_per_step, 3),
            "wall_over_copy_busy": round(ms_step / copy_ms, 4) if copy_ms > 0 else None,
            "exposed_ms_per_step": round(ms_step - copy_ms, 3),
+           # share of the shorter of copy and compute hidden under the other
+           "overlap_frac": (round((copy_ms + resident_ms_per_step - ms_step) / min(copy_ms, resident_ms_per_step), 4)
+                            if copy_ms > 0 and resident_ms_per_step > 0 else None),
            "steps": args.stream_steps, "warmup": args.stream_warmup}
     log(f"streaming: {res}")
     return res

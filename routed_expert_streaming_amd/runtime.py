@@ -129,14 +129,16 @@ class MoEStack:
             ptrs = np.array([base + i * self.slab for i in range(Lyr * E)], dtype=np.int64).reshape(Lyr, E)
             self.table = torch.from_numpy(ptrs).to(self.dev)
         else:
-            self.host = PinnedHost(Lyr * E * self.slab)
+            # one pinned allocation per layer (very large single pinned allocations
+            # can be refused where the total would still be granted)
+            self.host = [PinnedHost(E * self.slab) for _ in range(Lyr)]
             for l in range(Lyr):
                 synth.fill_slabs(cfg.seed, l, list(range(E)), H, I,
-                                 [self.host.ptr + (l * E + e) * self.slab for e in range(E)], threads)
+                                 [self.host[l].ptr + e * self.slab for e in range(E)], threads)
             self.pool = torch.empty((Lyr * self.C, self.slab), dtype=torch.uint8, device=self.dev)
             self.table = torch.zeros((Lyr, E), dtype=torch.int64, device=self.dev)
             self._host_ptrs = (ctypes.c_void_p * (Lyr * E))(
-                *[self.host.ptr + i * self.slab for i in range(Lyr * E)])
+                *[self.host[l].ptr + e * self.slab for l in range(Lyr) for e in range(E)])
             desc = L.moe_cache_desc(Lyr, E, H, I, self.C)
             torch.cuda.synchronize(self.dev)
             self.cache = L.moe_cache_create(desc, ctypes.addressof(self._host_ptrs), self.pool, self.table,
@@ -288,7 +290,8 @@ class MoEStack:
             L.moe_cache_destroy(self.cache)
             self.cache = None
         if self.host is not None:
-            self.host.free()
+            for buf in self.host:
+                buf.free()
             self.host = None
         for attr in ("_idx_host", "_mask_host"):
             buf = getattr(self, attr, None)
