@@ -16,8 +16,9 @@ The routing of every layer is known at the start of a step because each
 (step, layer) gets its own synthetic hidden states; the copies of later layers
 therefore overlap the FFN of earlier ones (LayerStoRm README "TL;DR": streaming
 is overlapped with compute).  When a layer needs more distinct experts than it has
-slots, it runs in waves: hits plus as many misses as fit first, then the
-remaining misses into slots released by the finished wave.
+slots, it runs in waves of half its slots, hits first: each wave's misses go
+into slots that the wave before last released, so they stream while the
+previous wave computes.
 """
 from __future__ import annotations
 
@@ -154,7 +155,8 @@ class MoEStack:
         self.w = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
         P = T * k + (T if self.has_shared else 0)
         self.y = torch.empty((P, H), dtype=torch.float32, device=self.dev)
-        self.max_waves = (E + self.C - 1) // self.C + 1
+        half = max(1, self.C // 2)
+        self.max_waves = (E + half - 1) // half + 1
         self.masks = torch.zeros((Lyr, self.max_waves, E), dtype=torch.uint8, device=self.dev)
         self._idx_host = PinnedHost(Lyr * T * k * 4) if self.streaming else None
         self._mask_host = PinnedHost(Lyr * self.max_waves * E) if self.streaming else None
@@ -219,14 +221,21 @@ class MoEStack:
                           self.table[l], self.shared[l] if self.has_shared else None, None, self.y,
                           L.MOE_FFN_PAIRS, self.stream)
 
+    def wave_size(self, n_needed: int) -> int:
+        """C when a layer's experts fit its slots, else half of them: then the next
+        wave's copies go to the slots the wave before last released while the
+        current wave computes, and the copy stream never waits on a wave's compute."""
+        return self.C if n_needed <= self.C else max(1, self.C // 2)
+
     def plan_waves(self, l: int, needed):
-        """Split a layer's sorted needed experts into waves of at most C experts,
+        """Split a layer's sorted needed experts into waves (wave_size each),
         resident ones (hits) first."""
         slots, _ = L.moe_cache_lookup(self.cache, l, needed)
         hits = [e for e, s in zip(needed, slots) if s >= 0]
         misses = [e for e, s in zip(needed, slots) if s < 0]
         order = hits + misses
-        return [sorted(order[i:i + self.C]) for i in range(0, len(order), self.C)]
+        w = self.wave_size(len(order))
+        return [sorted(order[i:i + w]) for i in range(0, len(order), w)]
 
     def forward(self, x: torch.Tensor, out: torch.Tensor) -> StepStats:
         """One step over all layers: x [L,T,H] bf16 -> out [L,T,H] bf16."""

@@ -426,8 +426,9 @@ def lru_replay(idx_steps, L_, C):
             needed = sorted(set(int(e) for e in idx[l].ravel()))
             resident = [e for e in needed if e in model.slot_of[l]]
             order = resident + [e for e in needed if e not in model.slot_of[l]]
-            for i in range(0, len(order), C):
-                status, _ = model.prefetch(l, sorted(order[i:i + C]))
+            w = C if len(order) <= C else max(1, C // 2)  # waves of half the slots when they overflow
+            for i in range(0, len(order), w):
+                status, _ = model.prefetch(l, sorted(order[i:i + w]))
                 assert status == "ok"
                 model.release(l)
     return model.hits, model.misses
