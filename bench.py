@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 # the one-token gate/up kernel as launched alone (units per lane, ring depth, no routing)
-GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 2, 0>"
+GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 1, 0>"
 
 
 def log(msg):

@@ -27,11 +27,15 @@
  * Expert slab format (one contiguous slab per expert, hidden H, intermediate I,
  * H % 32 == 0, I % 32 == 0):
  *   matrix 0 = W1 (gate) [I rows x H cols], 1 = W3 (up) [I x H], 2 = W2 (down) [H x I].
- *   Each matrix with R rows and K columns is R*K/2 code bytes (row-major; byte b
- *   of a row holds column 2b in bits 0-3 and column 2b+1 in bits 4-7), followed by
- *   R*(K/32) 4-byte records (row-major over (row, 32-column block)): fp16 scale,
- *   then fp16 min.  Weight value = scale * code + min (exact in fp32).
- *   Slab = W1 | W3 | W2, moe_expert_bytes(H, I) = 1.875 * H * I bytes.
+ *   A row of a matrix with K columns is K/2 code bytes (byte b holds column 2b
+ *   in bits 0-3 and column 2b+1 in bits 4-7), then K/32 4-byte records, one per
+ *   32-column block: fp16 scale, then fp16 min; then zero padding to a multiple
+ *   of 16 bytes (none when K % 128 == 0).  Weight value = scale * code + min
+ *   (exact in fp32).
+ *   Slab = for r = 0..I-1 the row pair (W1 row r, W3 row r), then the H rows of
+ *   W2; moe_expert_bytes(H, I) bytes (1.875 * H * I for H, I multiples of 128).
+ *   Every row a kernel streams -- a gate/up pair, or a down row -- is one
+ *   contiguous stretch.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -63,8 +67,8 @@ const char *moe_last_error_message(void);
 /* Library version, e.g. 100 for 1.0.0. */
 int moe_version(void);
 
-/* Bytes of one expert slab: 1.875 * hidden * inter (format above).  0 if the
-   sizes are not positive multiples of 32. */
+/* Bytes of one expert slab (format above; 1.875 * hidden * inter when both are
+   multiples of 128).  0 if the sizes are not positive multiples of 32. */
 size_t moe_expert_bytes(int hidden, int inter);
 
 /* ------------------------------------------------------------------ router

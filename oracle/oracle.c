@@ -75,19 +75,24 @@ uint16_t oracle_double_to_bf16(double v) {
 }
 
 /* ---------------- slab decoding ---------------- */
-static int64_t matrix_bytes(int64_t rows, int64_t cols) { return rows * cols / 2 + rows * (cols / 32) * 4; }
+/* A row of K columns: K/2 code bytes, K/32 records of 4 bytes, zero padding to a multiple of 16. */
+static int64_t row_bytes(int64_t cols) { return (cols / 2 + (cols / 32) * 4 + 15) / 16 * 16; }
+static int64_t matrix_bytes(int64_t rows, int64_t cols) { return rows * row_bytes(cols); }
 
 int64_t oracle_slab_bytes(int64_t H, int64_t I) { return 2 * matrix_bytes(I, H) + matrix_bytes(H, I); }
 
-/* Start of matrix `which` (0 = W1 gate [I x H], 1 = W3 up [I x H], 2 = W2 down [H x I]). */
-static const uint8_t *matrix_at(const uint8_t *slab, int64_t H, int64_t I, int which) {
-    return slab + (int64_t)which * matrix_bytes(I, H);
+/* Row r of matrix `which` (0 = W1 gate [I x H], 1 = W3 up [I x H], 2 = W2 down
+   [H x I]); the slab holds the I row pairs (W1 row, W3 row), then the H rows of W2. */
+static const uint8_t *matrix_row(const uint8_t *slab, int64_t H, int64_t I, int which, int64_t r) {
+    const int64_t gate_row = row_bytes(H), down_row = row_bytes(I);
+    if (which < 2) return slab + r * 2 * gate_row + (which == 1 ? gate_row : 0);
+    return slab + I * 2 * gate_row + r * down_row;
 }
 
-/* Dequantise row r of a [rows x cols] matrix into out[cols]. */
-static void dequant_row(const uint8_t *mat, int64_t rows, int64_t cols, int64_t r, double *out) {
-    const uint8_t *codes = mat + r * (cols / 2);
-    const uint8_t *params = mat + rows * cols / 2 + r * (cols / 32) * 4;
+/* Dequantise one row (K = cols columns, starting at `row`) into out[cols]. */
+static void dequant_row(const uint8_t *row, int64_t cols, double *out) {
+    const uint8_t *codes = row;
+    const uint8_t *params = row + cols / 2;
     for (int64_t c = 0; c < cols; ++c) {
         uint8_t byte = codes[c / 2];
         int q = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
@@ -101,8 +106,7 @@ static void dequant_row(const uint8_t *mat, int64_t rows, int64_t cols, int64_t 
 /* Full dequantised matrix `which` of a slab, row-major. */
 void oracle_dequant(const uint8_t *slab, int64_t H, int64_t I, int which, double *out) {
     int64_t rows = (which < 2) ? I : H, cols = (which < 2) ? H : I;
-    const uint8_t *mat = matrix_at(slab, H, I, which);
-    for (int64_t r = 0; r < rows; ++r) dequant_row(mat, rows, cols, r, out + r * cols);
+    for (int64_t r = 0; r < rows; ++r) dequant_row(matrix_row(slab, H, I, which, r), cols, out + r * cols);
 }
 
 /* ---------------- expert FFN ---------------- */
@@ -113,23 +117,20 @@ void oracle_expert_ffn(const uint8_t *slab, int64_t H, int64_t I, const double *
     double *g = g_out ? g_out : (double *)malloc(sizeof(double) * (size_t)I);
     double *u = u_out ? u_out : (double *)malloc(sizeof(double) * (size_t)I);
     double *h = h_out ? h_out : (double *)malloc(sizeof(double) * (size_t)I);
-    const uint8_t *w1 = matrix_at(slab, H, I, 0);
-    const uint8_t *w3 = matrix_at(slab, H, I, 1);
-    const uint8_t *w2 = matrix_at(slab, H, I, 2);
     for (int64_t r = 0; r < I; ++r) {
         double acc = 0.0;
-        dequant_row(w1, I, H, r, row);
+        dequant_row(matrix_row(slab, H, I, 0, r), H, row);
         for (int64_t c = 0; c < H; ++c) acc += row[c] * x[c];
         g[r] = acc;
         acc = 0.0;
-        dequant_row(w3, I, H, r, row);
+        dequant_row(matrix_row(slab, H, I, 1, r), H, row);
         for (int64_t c = 0; c < H; ++c) acc += row[c] * x[c];
         u[r] = acc;
         h[r] = g[r] / (1.0 + exp(-g[r])) * u[r];
     }
     for (int64_t r = 0; r < H; ++r) {
         double acc = 0.0;
-        dequant_row(w2, H, I, r, row);
+        dequant_row(matrix_row(slab, H, I, 2, r), I, row);
         for (int64_t c = 0; c < I; ++c) acc += row[c] * h[c];
         y[r] = acc;
     }
@@ -142,10 +143,9 @@ void oracle_expert_ffn(const uint8_t *slab, int64_t H, int64_t I, const double *
 /* Down projection alone: y = W2 h (h has I entries, y has H). */
 void oracle_expert_down(const uint8_t *slab, int64_t H, int64_t I, const double *h, double *y) {
     double *row = (double *)malloc(sizeof(double) * (size_t)I);
-    const uint8_t *w2 = matrix_at(slab, H, I, 2);
     for (int64_t r = 0; r < H; ++r) {
         double acc = 0.0;
-        dequant_row(w2, H, I, r, row);
+        dequant_row(matrix_row(slab, H, I, 2, r), I, row);
         for (int64_t c = 0; c < I; ++c) acc += row[c] * h[c];
         y[r] = acc;
     }

@@ -5,6 +5,7 @@
 #include <cstdio>
 
 #include "moe.h"
+#include "dequant.h"
 
 namespace {
 thread_local int g_last_hip = 0;
@@ -51,6 +52,8 @@ extern "C" int moe_version(void) { return 100; }
 
 extern "C" size_t moe_expert_bytes(int hidden, int inter) {
     if (hidden <= 0 || inter <= 0 || hidden % 32 || inter % 32) return 0;
-    // three matrices of hidden*inter 4-bit codes plus one 4-byte record per 32 codes
-    return (size_t)3 * hidden * inter * 5 / 8;
+    // 2*inter gate/up rows of `hidden` columns and `hidden` down rows of `inter`
+    // columns; a row holds K/2 code bytes and K/32 4-byte records, padded to 16
+    // bytes (1.875 * hidden * inter when both are multiples of 128)
+    return (size_t)2 * inter * moe::slab_row_bytes(hidden) + (size_t)hidden * moe::slab_row_bytes(inter);
 }

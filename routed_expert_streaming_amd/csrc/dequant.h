@@ -13,6 +13,32 @@
 #pragma once
 #include "common.h"
 
+// Expert slab layout.  A row of a matrix with K columns is K/2 code bytes followed
+// by the K/32 four-byte records of its 32-column blocks (then zero padding to a
+// multiple of 16 bytes); the slab holds, for each
+// r < I, the pair (W1 row r, W3 row r), then the H rows of W2.  So every (expert,
+// row) unit of a kernel -- the gate and up rows together, or one down row -- is
+// one contiguous stretch of memory.
+namespace moe {
+// codes and records of a K-column row, padded to a multiple of 16 bytes (no
+// padding when K % 128 == 0), so every row starts 16-byte aligned
+__host__ __device__ constexpr size_t slab_row_bytes(int K) { return ((size_t)K / 2 + (size_t)K / 8 + 15) / 16 * 16; }
+
+// Rows of one matrix of a slab: row r starts at row0 + r * stride (codes), its
+// records at + K/2.
+struct MatRows {
+    const uint8_t *row0;
+    size_t stride;
+};
+__device__ __forceinline__ MatRows slab_w1(const uint8_t *slab, int H, int) { return {slab, 2 * slab_row_bytes(H)}; }
+__device__ __forceinline__ MatRows slab_w3(const uint8_t *slab, int H, int) {
+    return {slab + slab_row_bytes(H), 2 * slab_row_bytes(H)};
+}
+__device__ __forceinline__ MatRows slab_w2(const uint8_t *slab, int H, int I) {
+    return {slab + (size_t)I * 2 * slab_row_bytes(H), slab_row_bytes(I)};
+}
+}  // namespace moe
+
 // The bf16 exponent pattern 0x4300 in both halves, held in a VGPR: gfx9 VOP3
 // instructions read at most one scalar/constant operand, so keeping this one in
 // a vector register (the mask goes in an SGPR) lets the extraction below compile

@@ -125,8 +125,7 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(moe::FfnArgs a, int
     const long long sg = ((long long)blockIdx.x * 4 + wave) * RPW + sub;
     const long long q0 = sg * units_per_sg;
     const int n = (int)max(0LL, min(q0 + units_per_sg, Q) - q0);  // units of this lane group
-    const size_t m13 = (size_t)I * H * 5 / 8;
-    const size_t cbytes = (size_t)I * H / 2;
+    const size_t rs = moe::slab_row_bytes(H);  // W1 row r at slab + 2*rs*r, W3 row r right after it
 
     // one token: the lane's activation blocks go straight to registers
     uint4 xd[XREG ? BPL : 1][4];
@@ -148,13 +147,14 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(moe::FfnArgs a, int
         const uint8_t *slab = (ui < n) ? gslab[gi] : nullptr;
         const size_t row = slab ? (size_t)ri : 0;
         if (!slab) slab = fallback;
+        const uint8_t *w1 = slab + 2 * rs * row, *w3 = w1 + rs;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             const int blk = c + b * LPR;
-            c0[j][b] = load_stream_u4(slab + row * (H / 2) + 16 * blk);
-            p0[j][b] = load_stream_u32(slab + cbytes + (row * nblk + blk) * 4);
-            c1[j][b] = load_stream_u4(slab + m13 + row * (H / 2) + 16 * blk);
-            p1[j][b] = load_stream_u32(slab + m13 + cbytes + (row * nblk + blk) * 4);
+            c0[j][b] = load_stream_u4(w1 + 16 * blk);
+            p0[j][b] = load_stream_u32(w1 + H / 2 + 4 * blk);
+            c1[j][b] = load_stream_u4(w3 + 16 * blk);
+            p1[j][b] = load_stream_u32(w3 + H / 2 + 4 * blk);
         }
         ++ui;
         if (++ri == I) {
@@ -264,22 +264,20 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
     const int w0 = blockIdx.x * 4 + wave;
     const int n = w0 < Q ? (Q - w0 + n_waves - 1) / n_waves : 0;  // units of this wave
     const int dg = n_waves / I, dr = n_waves - dg * I;              // cursor step in (group, row)
-    const size_t m13 = (size_t)I * H * 5 / 8;
-    const size_t cbytes = (size_t)I * H / 2;
-    const uint32_t code_off = 16u * lane, rec_off = 4u * lane;
+    const uint32_t rs = (uint32_t)moe::slab_row_bytes(H);  // W1 row r at slab + 2*rs*r, W3 row r right after it
+    const uint32_t code_off = 16u * lane, rec_off = (uint32_t)(H / 2) + 4u * lane;
 
     uint4 c0[D][BPL], c1[D][BPL];
     uint32_t p0[D][BPL], p1[D][BPL];
     int ui = 0, gi = w0 / I, ri = w0 - gi * I;  // issue cursor, D units ahead
     auto load_unit = [&](int j, const uint8_t *slab, int row) {
-        const uint8_t *w1 = slab + (size_t)row * (H / 2);
-        const uint8_t *r1 = slab + cbytes + (size_t)row * nblk * 4;
+        const uint8_t *w1 = slab + (size_t)row * (2 * rs);
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             c0[j][b] = load_stream_u4(w1 + (code_off + 1024u * b));
-            p0[j][b] = load_stream_u32(r1 + (rec_off + 256u * b));
-            c1[j][b] = load_stream_u4(w1 + m13 + (code_off + 1024u * b));
-            p1[j][b] = load_stream_u32(r1 + m13 + (rec_off + 256u * b));
+            p0[j][b] = load_stream_u32(w1 + (rec_off + 256u * b));
+            c1[j][b] = load_stream_u4(w1 + (rs + code_off + 1024u * b));
+            p1[j][b] = load_stream_u32(w1 + (rs + rec_off + 256u * b));
         }
     };
     auto advance_issue = [&]() {
@@ -487,8 +485,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
     const int r_first = (int)sg;
     const int n_rows = r_first < H ? (H - r_first + n_sg - 1) / n_sg : 0;
     const int n_units = n_rows * G;  // (row, pair) units, pairs innermost
-    const size_t m2 = 2 * ((size_t)I * H * 5 / 8);
-    const size_t cbytes = (size_t)H * I / 2;
+    const size_t w2off = (size_t)I * 2 * moe::slab_row_bytes(H), rs2 = moe::slab_row_bytes(I);  // W2 row r
 
     // h blocks to stage: issued before the weight ring so that waiting for them
     // does not wait for the ring (items past the end re-read item 0)
@@ -512,11 +509,12 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
         const uint8_t *slab = (ui < n_units) ? gslab[gi] : nullptr;
         const size_t row = slab ? (size_t)ri : 0;
         if (!slab) slab = fallback;
+        const uint8_t *w2 = slab + w2off + row * rs2;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             const int blk = c + b * LPR;
-            cw[j][b] = load_stream_u4(slab + m2 + row * (I / 2) + 16 * blk);
-            pw[j][b] = load_stream_u32(slab + m2 + cbytes + (row * nblk + blk) * 4);
+            cw[j][b] = load_stream_u4(w2 + 16 * blk);
+            pw[j][b] = load_stream_u32(w2 + I / 2 + 4 * blk);
         }
         ++ui;
         if (++gi == G) {
@@ -650,20 +648,20 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
 
     if (slab) {
         const uint32_t magic = moe_magic_vgpr();
-        const size_t m2 = 2 * ((size_t)I * H * 5 / 8);
-        const uint8_t *w2 = slab + m2, *r2 = slab + m2 + (size_t)H * I / 2;
-        const uint32_t code_off = 16u * c, rec_off = 4u * c;
+        const uint8_t *w2 = slab + (size_t)I * 2 * moe::slab_row_bytes(H);  // W2 row 0
+        const uint32_t rs2 = (uint32_t)moe::slab_row_bytes(I);
+        const uint32_t code_off = 16u * c, rec_off = (uint32_t)(I / 2) + 4u * c;
         uint4 cw[D][BPL];
         uint32_t pw[D][BPL];
         int ui = 0;
         auto issue = [&](int j) {
             int row = r0 + sub + 4 * ui;
             if (ui >= U || row >= H) row = r0;  // past the end: re-read a valid row
-            const uint32_t crow = (uint32_t)row * (uint32_t)(I / 2), rrow = (uint32_t)row * (uint32_t)(I / 8);
+            const uint32_t rrow = (uint32_t)row * rs2;
 #pragma unroll
             for (int b = 0; b < BPL; ++b) {
-                cw[j][b] = load_stream_u4(w2 + (crow + code_off + 256u * b));
-                pw[j][b] = load_stream_u32(r2 + (rrow + rec_off + 64u * b));
+                cw[j][b] = load_stream_u4(w2 + (rrow + code_off + 256u * b));
+                pw[j][b] = load_stream_u32(w2 + (rrow + rec_off + 64u * b));
             }
             ++ui;
         };
@@ -835,7 +833,7 @@ bool decode_supported(const FfnArgs &a) {
 }
 
 #ifndef MOE_DECODE1_D
-#define MOE_DECODE1_D 2  // units in flight per wave, one-token gate/up (H = 4096)
+#define MOE_DECODE1_D 1  // units in flight per wave, one-token gate/up (H = 4096)
 #endif
 
 bool decode1_routed_supported(const FfnArgs &a, int E) {

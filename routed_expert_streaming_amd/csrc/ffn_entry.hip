@@ -1,6 +1,7 @@
 // Entry points around the expert FFN: token->expert permutation, the FFN
 // dispatcher, the weighted combine and the dequantisation debug hook.
 #include "common.h"
+#include "dequant.h"
 #include "ffn.h"
 #include "router.h"
 #include "topk.h"
@@ -84,14 +85,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     *reinterpret_cast<uint2 *>(out + (size_t)t * H + j) = o;
 }
 
-__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ mat, int R, int K,
+// row r of the matrix starts at row0 + r * stride: K/2 code bytes, then the records
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ row0, size_t stride, int R, int K,
                                                       float *__restrict__ out) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (size_t)R * K) return;
     const size_t r = i / K, col = i - r * K;
-    const uint8_t byte = mat[r * (K / 2) + col / 2];
+    const uint8_t *row = row0 + r * stride;
+    const uint8_t byte = row[col / 2];
     const uint32_t q = (col & 1) ? (byte >> 4) : (byte & 0xF);
-    const uint32_t rec = *reinterpret_cast<const uint32_t *>(mat + (size_t)R * K / 2 + (r * (K / 32) + col / 32) * 4);
+    const uint32_t rec = *reinterpret_cast<const uint32_t *>(row + K / 2 + (col / 32) * 4);
     out[i] = fmaf(fp16_bits_to_f32(rec & 0xFFFFu), (float)q, fp16_bits_to_f32(rec >> 16));
 }
 
@@ -420,10 +423,12 @@ extern "C" int moe_debug_dequant(const void *slab, int H, int I, int which, floa
     if (H <= 0 || I <= 0 || H % 32 || I % 32) return moe::fail(MOE_E_SHAPE, "debug_dequant: H=%d I=%d", H, I);
     if (which < 0 || which > 2) return moe::fail(MOE_E_ARG, "debug_dequant: which=%d", which);
     const int R = which < 2 ? I : H, K = which < 2 ? H : I;
-    const uint8_t *mat = (const uint8_t *)slab + (size_t)which * ((size_t)I * H * 5 / 8);
+    const size_t gate_row = moe::slab_row_bytes(H);
+    const uint8_t *row0 = (const uint8_t *)slab + (which == 0 ? 0 : which == 1 ? gate_row : (size_t)I * 2 * gate_row);
+    const size_t stride = which < 2 ? 2 * gate_row : moe::slab_row_bytes(I);
     const size_t n = (size_t)R * K;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, mat, R,
-                       K, out);
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, row0,
+                       stride, R, K, out);
     MOE_LAUNCH_CHECK("dequant_kernel");
     return MOE_OK;
 }

@@ -129,11 +129,9 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
     if (row0 >= R) return;
     const int nsteps = min(iters, (R - row0 + ROWS_PER_STEP - 1) / ROWS_PER_STEP);
 
-    const size_t m13 = (size_t)a.I * a.H * 5 / 8;  // bytes of W1 (= W3)
-    const uint8_t *mat0 = gr.slab + (GATEUP ? 0 : 2 * m13);
-    const uint8_t *mat1 = gr.slab + m13;
-    const uint8_t *par0 = mat0 + (size_t)R * K / 2;
-    const uint8_t *par1 = mat1 + (size_t)R * K / 2;
+    // matrix rows: W1 and W3 (gate/up) or W2 (down); codes, then records at + K/2
+    const moe::MatRows m0 = GATEUP ? moe::slab_w1(gr.slab, a.H, a.I) : moe::slab_w2(gr.slab, a.H, a.I);
+    const moe::MatRows m1 = moe::slab_w3(gr.slab, a.H, a.I);
 
     extern __shared__ uint4 lds[];
     uint4 *X = lds;
@@ -149,14 +147,15 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
     // rows past R re-read row R-1 (valid memory) and are not stored
     auto load = [&](GemvSlot<BPL, GATEUP> &sl, int step) {
         const int r = min(rbase + step * ROWS_PER_STEP, R - 1);
+        const uint8_t *row0 = m0.row0 + (size_t)r * m0.stride, *row1 = m1.row0 + (size_t)r * m1.stride;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             const int blk = min(c + b * LPR, nblk - 1);
-            sl.c0[b] = load_stream_u4(mat0 + (size_t)r * (K / 2) + 16 * blk);
-            sl.p0[b] = load_stream_u32(par0 + ((size_t)r * nblk + blk) * 4);
+            sl.c0[b] = load_stream_u4(row0 + 16 * blk);
+            sl.p0[b] = load_stream_u32(row0 + K / 2 + 4 * blk);
             if constexpr (GATEUP) {
-                sl.c1[b] = load_stream_u4(mat1 + (size_t)r * (K / 2) + 16 * blk);
-                sl.p1[b] = load_stream_u32(par1 + ((size_t)r * nblk + blk) * 4);
+                sl.c1[b] = load_stream_u4(row1 + 16 * blk);
+                sl.p1[b] = load_stream_u32(row1 + K / 2 + 4 * blk);
             }
         }
     };

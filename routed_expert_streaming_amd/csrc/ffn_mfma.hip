@@ -28,6 +28,7 @@
 // A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16] for j < 8, and C[4*(l/16)+j][l%16]
 // for j < 4.
 #include "common.h"
+#include "dequant.h"
 #include "ffn.h"
 
 namespace {
@@ -184,9 +185,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         slab = (const uint8_t *)a.shared;
         M = a.T;
     }
-    const size_t m13 = (size_t)a.I * a.H * 5 / 8;
-    const uint8_t *mat[2] = {slab + (GATEUP ? 0 : 2 * m13), slab + m13};
-    const size_t cbytes = (size_t)R * K / 2;
+    const moe::MatRows mat[2] = {GATEUP ? moe::slab_w1(slab, a.H, a.I) : moe::slab_w2(slab, a.H, a.I),
+                                 moe::slab_w3(slab, a.H, a.I)};
     const uint16_t *act = GATEUP ? a.x : a.h;
 
     // separate variables, not an array: the compiler then sees that a chunk's
@@ -210,8 +210,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const uint8_t *wsrc[NMAT], *rsrc[NMAT];
 #pragma unroll
     for (int q = 0; q < NMAT; ++q) {
-        wsrc[q] = mat[q] + (size_t)wrow * (K / 2) + (lane >> 5) * 16;
-        rsrc[q] = mat[q] + cbytes + ((size_t)rrow * nblk + (lane & 1)) * 4;
+        wsrc[q] = mat[q].row0 + (size_t)wrow * mat[q].stride + (lane >> 5) * 16;
+        rsrc[q] = mat[q].row0 + (size_t)rrow * mat[q].stride + K / 2 + (lane & 1) * 4;
     }
 
     for (int m0 = 0; m0 < M; m0 += kMC) {

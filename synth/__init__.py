@@ -120,11 +120,12 @@ def get(name: str, **overrides) -> Config:
 
 # --------------------------------------------------------------------------- generators
 def matrix_bytes(rows: int, cols: int) -> int:
-    return rows * cols // 2 + rows * (cols // 32) * 4
+    """Bytes of a matrix's rows (each row's codes and records padded to 16 bytes)."""
+    return int(lib().synth_matrix_bytes(rows, cols))
 
 
 def slab_bytes(hidden: int, inter: int) -> int:
-    return 2 * matrix_bytes(inter, hidden) + matrix_bytes(hidden, inter)
+    return int(lib().synth_slab_bytes(hidden, inter))
 
 
 def philox(ctr, key) -> np.ndarray:

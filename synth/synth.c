@@ -14,12 +14,13 @@
  *
  * Expert slab byte layout (one contiguous slab per expert):
  *   matrix 0 = W1 (gate) [I rows x H cols], matrix 1 = W3 (up) [I x H],
- *   matrix 2 = W2 (down) [H rows x I cols]; each matrix with R rows and K cols:
- *     codes : R*K/2 bytes, row-major; byte b of a row holds column 2b in bits
- *             0-3 and column 2b+1 in bits 4-7 (codes are 0..15)
- *     params: R*(K/32) records of 4 bytes, row-major over (row, block);
- *             record = fp16 scale (bytes 0-1) then fp16 min (bytes 2-3)
- *   matrix bytes = 0.625*R*K, slab = W1 | W3 | W2.
+ *   matrix 2 = W2 (down) [H rows x I cols].  A row of a matrix with K cols is
+ *   K/2 code bytes (byte b holds column 2b in bits 0-3 and column 2b+1 in bits
+ *   4-7; codes are 0..15), then K/32 records of 4 bytes, one per 32-column
+ *   block: fp16 scale (bytes 0-1) then fp16 min (bytes 2-3); 0.625*K bytes,
+ *   padded with zeros to a multiple of 16 (no padding when K % 128 == 0).
+ *   slab = I row pairs [W1 row r | W3 row r], then the H rows of W2; for H and I
+ *   multiples of 128 that is 1.875*H*I bytes.
  * Value distributions: x ~ N(0,1) rounded to bf16; router W ~ N(0, 0.02^2)
  * rounded to fp32; codes uniform on 0..15; scale = fp16(|N(0, 0.02^2)|);
  * min = -8*scale (exact in fp16).  The scale of block b is drawn from Philox
@@ -188,8 +189,19 @@ void synth_zipf_bias(uint64_t seed, uint32_t layer, int64_t E, double s, float *
     free(rank);
 }
 
-int64_t synth_matrix_bytes(int64_t rows, int64_t cols) { return rows * cols / 2 + rows * (cols / 32) * 4; }
+/* Bytes of one row of a matrix with `cols` columns: codes and records, rounded up
+   to 16 so that every row starts on a 16-byte boundary. */
+static int64_t row_bytes(int64_t cols) { return (cols / 2 + (cols / 32) * 4 + 15) / 16 * 16; }
+int64_t synth_matrix_bytes(int64_t rows, int64_t cols) { return rows * row_bytes(cols); }
 int64_t synth_slab_bytes(int64_t H, int64_t I) { return 2 * synth_matrix_bytes(I, H) + synth_matrix_bytes(H, I); }
+
+/* Where row r of matrix m starts in a slab, and the distance between its rows. */
+static int64_t matrix_start(int64_t H, int64_t I, uint32_t m) {
+    return m == 0 ? 0 : m == 1 ? row_bytes(H) : 2 * I * row_bytes(H);
+}
+static int64_t matrix_row_stride(int64_t H, int64_t I, uint32_t m) {
+    return m < 2 ? 2 * row_bytes(H) : row_bytes(I);
+}
 
 static inline void write_params(double z, uint8_t *rec) {
     uint16_t sc = synth_double_to_fp16(fabs(0.02 * z));
@@ -203,34 +215,44 @@ static inline void write_params(double z, uint8_t *rec) {
     rec[3] = (uint8_t)(mn >> 8);
 }
 
+/* Record of global block B (row-major over (row, block)) of a matrix. */
+static inline uint8_t *record_at(uint8_t *base, int64_t stride, int64_t cols, int64_t B) {
+    int64_t nblk = cols / 32, row = B / nblk, blk = B - row * nblk;
+    return base + row * stride + cols / 2 + 4 * blk;
+}
+
 /* Scale of block b comes from Philox call b/2: the cosine branch for even b, the
-   sine branch for odd b. */
+   sine branch for odd b (b counts the matrix's blocks row-major). */
 static inline void params_for_pair(uint64_t seed, uint32_t layer, uint32_t expert, uint32_t m,
-                                   int64_t pair, int64_t nblocks, uint8_t *params) {
+                                   int64_t pair, int64_t nblocks, uint8_t *base, int64_t stride, int64_t cols) {
     uint32_t r[4];
     double z0, z1;
     draw(seed, KIND_PARAMS, 0, layer, expert, m, (uint32_t)pair, r);
     normal_pair_from(r[0], r[1], &z0, &z1);
-    write_params(z0, params + 8 * pair);
-    if (2 * pair + 1 < nblocks) write_params(z1, params + 8 * pair + 4);
+    write_params(z0, record_at(base, stride, cols, 2 * pair));
+    if (2 * pair + 1 < nblocks) write_params(z1, record_at(base, stride, cols, 2 * pair + 1));
 }
 
-/* Fill part `part` of `nparts` of one matrix (codes then params). */
+/* Fill part `part` of `nparts` of one matrix: its 16-byte code chunks c (row-major,
+   K/32 per row) and its records; base = the matrix's row 0, stride = between rows. */
 static void fill_matrix_part(uint64_t seed, uint32_t layer, uint32_t expert, uint32_t m,
-                             int64_t rows, int64_t cols, uint8_t *base, int64_t part, int64_t nparts) {
-    int64_t code_bytes = rows * cols / 2;
-    int64_t nchunks = code_bytes / 16;
+                             int64_t rows, int64_t cols, uint8_t *base, int64_t stride, int64_t part,
+                             int64_t nparts) {
+    int64_t chunks_per_row = cols / 32;
+    int64_t nchunks = rows * chunks_per_row;
     int64_t nblocks = rows * (cols / 32);
     int64_t c0 = nchunks * part / nparts, c1 = nchunks * (part + 1) / nparts;
+    const int64_t used = cols / 2 + (cols / 32) * 4, pad = row_bytes(cols) - used;
     for (int64_t c = c0; c < c1; ++c) {
         uint32_t r[4];
+        int64_t row = c / chunks_per_row, ch = c - row * chunks_per_row;
         draw(seed, KIND_CODES, 0, layer, expert, m, (uint32_t)c, r);
-        memcpy(base + 16 * c, r, 16);
+        memcpy(base + row * stride + 16 * ch, r, 16);
+        if (ch == 0 && pad > 0) memset(base + row * stride + used, 0, (size_t)pad);  /* row padding */
     }
-    uint8_t *params = base + code_bytes;
     int64_t npairs = (nblocks + 1) / 2;
     int64_t b0 = npairs * part / nparts, b1 = npairs * (part + 1) / nparts;
-    for (int64_t b = b0; b < b1; ++b) params_for_pair(seed, layer, expert, m, b, nblocks, params);
+    for (int64_t b = b0; b < b1; ++b) params_for_pair(seed, layer, expert, m, b, nblocks, base, stride, cols);
 }
 
 /* Many slabs in parallel: outs[i] receives expert experts[i] of `layer`.  Expert
@@ -240,7 +262,6 @@ void synth_expert_slabs(uint64_t seed, uint32_t layer, const uint32_t *experts, 
     nthreads = clamp_threads(nthreads);
     /* Split every matrix into parts so a handful of slabs still keeps all threads busy. */
     const int64_t nparts = 16;
-    int64_t m13 = synth_matrix_bytes(I, H);
     int64_t njobs = n * 3 * nparts;
     #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
     for (int64_t job = 0; job < njobs; ++job) {
@@ -248,7 +269,8 @@ void synth_expert_slabs(uint64_t seed, uint32_t layer, const uint32_t *experts, 
         uint32_t m = (uint32_t)((job / nparts) % 3);
         int64_t part = job % nparts;
         int64_t rows = (m < 2) ? I : H, cols = (m < 2) ? H : I;
-        fill_matrix_part(seed, layer, experts[i], m, rows, cols, outs[i] + m * m13, part, nparts);
+        fill_matrix_part(seed, layer, experts[i], m, rows, cols, outs[i] + matrix_start(H, I, m),
+                         matrix_row_stride(H, I, m), part, nparts);
     }
 }
 

@@ -340,9 +340,7 @@ def test_generator_params_are_scale_and_minus_eight_scale():
     H, I = cfg.hidden, cfg.inter
     slab = synth.expert_slab(cfg.seed, 0, 3, H, I)
     for which in range(3):
-        rows, cols = (I, H) if which < 2 else (H, I)
-        off = which * synth.matrix_bytes(I, H) + rows * cols // 2
-        rec = slab[off:off + rows * cols // 32 * 4].view(np.uint16).reshape(-1, 2)
+        rec = sk.records_of(slab, H, I, which).reshape(-1, 2)
         sc = rec[:, 0].view(np.float16).astype(np.float64)
         mn = rec[:, 1].view(np.float16).astype(np.float64)
         assert np.all(np.isfinite(sc)) and np.all(sc >= 0) and np.array_equal(mn, -8 * sc)
