@@ -411,7 +411,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
                      "kernel": f"{GATE_UP_KERNEL} (dequant + gate/up + SwiGLU, launched alone "
-                               "through moe_expert_gate_up; in the step the same kernel also finishes the top-k)",
+                               "through moe_expert_gate_up; in the step the same kernel, with a two-deep load "
+                               "ring, also finishes the top-k)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic(GATE_UP_KERNEL),
