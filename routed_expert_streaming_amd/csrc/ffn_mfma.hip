@@ -189,13 +189,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                                  moe::slab_w3(slab, a.H, a.I)};
     const uint16_t *act = GATEUP ? a.x : a.h;
 
-    // separate variables, not an array: the compiler then sees that a chunk's
-    // LDS reads cannot alias the loads in flight into the other stages, and
-    // does not wait for those before reading
-    __shared__ Stage<NMAT> st0, st1, st2, st3;
-    static_assert(S <= 4, "at most four stages");
-    const uint32_t a0 = lds_addr(&st0), a1 = lds_addr(&st1), a2 = S > 2 ? lds_addr(&st2) : 0u,
-                   a3 = S > 3 ? lds_addr(&st3) : 0u;
+    __shared__ Stage<NMAT> ring[S];
+    const uint32_t ring_lds = lds_addr(&ring[0]);
+    auto stage_addr = [&](int b) { return ring_lds + (uint32_t)(b * sizeof(Stage<NMAT>)); };
     __shared__ int s_src[kMC];  // activation row of each M row
     __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
     const Dequant dq = dequant_consts();
@@ -326,23 +322,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             compute(cur);
         };
 
-        issue(a0, 0);
-        if constexpr (S > 2) issue(a1, min(1, nchunks - 1));
-        if constexpr (S > 3) issue(a2, min(2, nchunks - 1));
+        // stage b of the ring holds chunks b, b + S, ...; the loop is unrolled by S
+        // so that every step names its stages with constants
+#pragma unroll
+        for (int b = 0; b < S - 1; ++b) issue(stage_addr(b), min(b, nchunks - 1));
         for (int c0 = 0; c0 < nchunks; c0 += S) {
-            if constexpr (S == 2) {
-                step(st0, a1, c0);
-                if (c0 + 1 < nchunks) step(st1, a0, c0 + 1);
-            } else if constexpr (S == 3) {
-                step(st0, a2, c0);
-                if (c0 + 1 < nchunks) step(st1, a0, c0 + 1);
-                if (c0 + 2 < nchunks) step(st2, a1, c0 + 2);
-            } else {
-                step(st0, a3, c0);
-                if (c0 + 1 < nchunks) step(st1, a0, c0 + 1);
-                if (c0 + 2 < nchunks) step(st2, a1, c0 + 2);
-                if (c0 + 3 < nchunks) step(st3, a2, c0 + 3);
-            }
+#pragma unroll
+            for (int b = 0; b < S; ++b)
+                if (c0 + b < nchunks) step(ring[b], stage_addr((b + S - 1) % S), c0 + b);
         }
 
         // no load may still be writing LDS when the workgroup moves on or exits
@@ -381,24 +368,19 @@ bool mfma_supported(const FfnArgs &a) { return a.grouped && a.H % 128 == 0 && a.
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-int mfma_gate_up(const FfnArgs &a, hipStream_t s) {
+template <bool GATEUP, int S>
+int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
-    const int ntiles = (a.I + kNT - 1) / kNT;
+    const int ntiles = ((GATEUP ? a.I : a.H) + kNT - 1) / kNT;
     const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((mfma_ffn_kernel<true, kStagesGateUp>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
                        n_groups);
-    MOE_LAUNCH_CHECK("mfma_ffn_kernel<gate_up>");
+    MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
 
-int mfma_down(const FfnArgs &a, hipStream_t s) {
-    const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
-    const int ntiles = (a.H + kNT - 1) / kNT;
-    const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((mfma_ffn_kernel<false, kStagesDown>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
-                       n_groups);
-    MOE_LAUNCH_CHECK("mfma_ffn_kernel<down>");
-    return MOE_OK;
-}
+int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true, kStagesGateUp>(a, s); }
+
+int mfma_down(const FfnArgs &a, hipStream_t s) { return launch_mfma<false, kStagesDown>(a, s); }
 
 }  // namespace moe
