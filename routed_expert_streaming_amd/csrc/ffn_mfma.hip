@@ -8,11 +8,13 @@
 // the expert's tokens in M chunks of up to 96, so at prefill sizes (about 64
 // tokens per expert) every weight byte is read from HBM once.
 //
-// The K dimension streams in chunks of 64 columns through a ring of kStages
-// LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4 for
-// activations and weight codes, _dword for the (scale, min) records), so the
-// loads of the next kStages-1 chunks are in flight while the current chunk is
-// multiplied and no registers hold data on its way to LDS.  Each wave loads its
+// The K dimension streams in chunks of 64 columns through a ring of S LDS
+// buffers filled by direct global->LDS loads (global_load_lds_dwordx4), so the
+// loads of the next S-1 chunks are in flight while the current chunk is
+// multiplied and no registers hold data on its way to LDS.  The (scale, min)
+// records come through a ring of their own, RC chunks per load (16 or 32 bytes
+// per row): fetched with the codes, 8 bytes per row and chunk, they cost as
+// much load bandwidth as the codes, since every row is a separate fetch.  Each wave loads its
 // own 32 weight rows; the activation tile is shared and XOR-swizzled in 16-byte
 // units so that the A-operand reads hit distinct banks.  One barrier per chunk:
 // each wave first waits (exact vmcnt) for its own loads of the chunk, the
@@ -52,15 +54,56 @@ constexpr int kStagesGateUp = MOE_MFMA_STAGES_GU;  // ring depth: 3 x 22 KB of L
 constexpr int kStagesDown = MOE_MFMA_STAGES_DN;    // 4 x 17 KB
 
 // One ring stage: the chunk's activation tile (row r, 16-byte unit u stored at
-// unit position u ^ (r & 7)), and per matrix the codes and records of the 128
-// rows, wave w's 32 rows in its own 1 KB (codes: unit (row, half) at position
-// half*32 + row) and 256 B (records: row-major, 2 per row).
+// unit position u ^ (r & 7)), and per matrix the codes of the 128 rows, wave
+// w's 32 rows in its own 1 KB (unit (row, half) at position half*32 + row).
 template <int NMAT>
 struct __attribute__((aligned(16))) Stage {
     uint8_t x[kMC * kXRow];
     uint8_t w[NMAT][kNT * 32];
-    uint32_t p[NMAT][kNT * 2];
 };
+
+// Record buffer: per wave 1 KB, the records of RC chunks (2*RC blocks, 8*RC
+// bytes) of its 32 rows of each matrix, matrix-major then row-major.  One
+// 64-lane 16-byte load fills it (lanes beyond NMAT*RC*16 repeat the first ones
+// into the unused rest).
+constexpr int kRecWave = 1024;
+
+// Number of multiples of m in [lo, hi].
+constexpr int multiples(int lo, int hi, int m) {
+    return hi < lo ? 0 : (lo > 0 ? hi / m - (lo - 1) / m : hi / m + 1);
+}
+
+// Loads a wave may still have in flight when step c waits, such that chunk c's
+// stage and the records of its group are complete.  Issue order: the records of
+// group 0, then stages 0 .. S-2; step j issues stage j+S-1 (P loads) and, when
+// RC divides j, the records of group j/RC + 1 (NR loads).  The count is the
+// number of loads issued after the later of the two.
+constexpr int newer_loads(int S, int RC, int P, int NR, int c) {
+    const int after_stage = P * (S - 2) + NR * multiples(c - S + 1 > 0 ? c - S + 1 : 0, c - 1, RC);
+    const int grp = c / RC;
+    const int after_rec = grp == 0 ? (S - 1 + c) * P + NR * multiples(0, c - 1, RC)
+                                   : (c - 1 - RC * (grp - 1)) * P + NR * multiples(RC * (grp - 1) + 1, c - 1, RC);
+    return after_stage < after_rec ? after_stage : after_rec;
+}
+// The same for every step at position b of a loop unrolled by U (the pattern
+// repeats with period U after the first U steps).
+constexpr int vm_allow(int S, int RC, int P, int NR, int U, int b) {
+    int m = newer_loads(S, RC, P, NR, b);
+    for (int r = 1; r < 4; ++r) {
+        const int v = newer_loads(S, RC, P, NR, b + r * U);
+        m = v < m ? v : m;
+    }
+    return m;
+}
+constexpr int lcm(int a, int b) {
+    int x = a, y = b;
+    while (y) {
+        const int t = x % y;
+        x = y;
+        y = t;
+    }
+    return a / x * b;
+}
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -126,6 +169,20 @@ __device__ __forceinline__ Dequant dequant_consts() {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
+// f(IntC<B>{}), f(IntC<B + 1>{}), ..., f(IntC<E - 1>{})
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(IntC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // two floats -> bf16 pair (round to nearest even), lo in bits 0-15
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){lo, hi},
@@ -157,14 +214,16 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, const
     return __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, w45, w67));
 }
 
-template <bool GATEUP, int S>
+template <bool GATEUP, int S, int RC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_ffn_kernel(moe::FfnArgs a, int ntiles,
                                                                                            int n_groups) {
     constexpr int NMAT = GATEUP ? 2 : 1;
     static_assert(S >= 2, "the ring needs two stages at least");
-    const int K = GATEUP ? a.H : a.I;   // reduction length
+    static_assert((RC == 2 || RC == 4) && NMAT * RC <= 4, "one 16-byte load per lane fills a record buffer");
+    constexpr int U = lcm(S, RC);       // steps per unrolled loop body
+    constexpr int LPR = RC / 2;         // lanes per row of a record load
+    const int K = GATEUP ? a.H : a.I;   // reduction length (a multiple of 64 * RC)
     const int R = GATEUP ? a.I : a.H;   // weight rows (output columns)
-    const int nblk = K >> 5;
     // every tile of one expert on the same XCD
     const int xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
     const int g = (i / ntiles) * kXcds + xcd, tile = i % ntiles;
@@ -192,6 +251,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     __shared__ Stage<NMAT> ring[S];
     const uint32_t ring_lds = lds_addr(&ring[0]);
     auto stage_addr = [&](int b) { return ring_lds + (uint32_t)(b * sizeof(Stage<NMAT>)); };
+    __shared__ __attribute__((aligned(16))) uint8_t recs_lds[2][4 * kRecWave];
+    const uint32_t rec_lds = lds_addr(&recs_lds[0][0]);
     __shared__ int s_src[kMC];  // activation row of each M row
     __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
     const Dequant dq = dequant_consts();
@@ -202,12 +263,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 
     // this lane's global sources, fixed over a pass: weight rows of its wave
     const int wrow = n0 + 32 * wave + (lane & 31);           // codes: lanes 0-31 half 0, 32-63 half 1
-    const int rrow = n0 + 32 * wave + (lane >> 1);           // records: 2 lanes per row
-    const uint8_t *wsrc[NMAT], *rsrc[NMAT];
+    const uint8_t *wsrc[NMAT];
 #pragma unroll
-    for (int q = 0; q < NMAT; ++q) {
-        wsrc[q] = mat[q].row0 + (size_t)wrow * mat[q].stride + (lane >> 5) * 16;
-        rsrc[q] = mat[q].row0 + (size_t)rrow * mat[q].stride + K / 2 + (lane & 1) * 4;
+    for (int q = 0; q < NMAT; ++q) wsrc[q] = mat[q].row0 + (size_t)wrow * mat[q].stride + (lane >> 5) * 16;
+    // records: lane (q, row, part) of the NMAT * 32 * LPR used lanes takes bytes
+    // 16*part .. 16*part+15 of the row's records of a group of RC chunks
+    const uint8_t *rsrc;
+    {
+        const int ll = lane % (NMAT * 32 * LPR);
+        const int q = ll / (32 * LPR), r = (ll % (32 * LPR)) / LPR, part = ll % LPR;
+        const moe::MatRows &m = q ? mat[1] : mat[0];
+        rsrc = m.row0 + (size_t)(n0 + 32 * wave + r) * m.stride + K / 2 + part * 16;
     }
 
     for (int m0 = 0; m0 < M; m0 += kMC) {
@@ -229,28 +295,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             s_dst[tid] = tid < mc ? dst : -1;
         }
         __syncthreads();
-        // activation loads of this wave: tile units wave + 4j (8 rows each).  All
-        // 96 rows are loaded whatever mtiles is (rows past the tokens repeat the
-        // first row and are never read), so every wave issues the same number
-        // of loads per chunk and the compiler can count them statically.
+        // activation loads of this wave: tile units wave + 4j (8 rows each), for
+        // j < (MT + 1) / 2 with MT M tiles, so that every wave issues the same
+        // number of loads per chunk (rows past the tokens repeat the first row;
+        // rows past 16 * MT are loaded for that reason only and never read).
         const uint16_t *xsrc[3];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int r = 8 * (wave + 4 * j) + (lane >> 3), pos = lane & 7;
             xsrc[j] = act + (size_t)s_src[r] * K + 8 * (pos ^ (r & 7));
         }
-        constexpr int per_stage = 3 + 2 * NMAT;  // loads each wave issues per chunk
 
         // LDS byte address of stage st (uniform), then constant offsets
-        auto issue = [&](uint32_t st, int c) {
+        auto issue = [&](uint32_t st, int c, auto mt_count) {
+            constexpr int XJ = (decltype(mt_count)::value + 1) / 2;
             const int k0 = c * kKC;
 #pragma unroll
-            for (int j = 0; j < 3; ++j) dma16(xsrc[j] + k0, st + (uint32_t)((wave + 4 * j) * 1024));
+            for (int j = 0; j < XJ; ++j) dma16(xsrc[j] + k0, st + (uint32_t)((wave + 4 * j) * 1024));
 #pragma unroll
-            for (int q = 0; q < NMAT; ++q) {
+            for (int q = 0; q < NMAT; ++q)
                 dma16(wsrc[q] + k0 / 2, st + (uint32_t)(offsetof(Stage<NMAT>, w) + q * kNT * 32 + wave * 1024));
-                dma4(rsrc[q] + (k0 >> 5) * 4, st + (uint32_t)(offsetof(Stage<NMAT>, p) + q * kNT * 8 + wave * 256));
-            }
+        };
+        // the records of chunk group grp into record buffer buf (one load per wave)
+        auto issue_rec = [&](int grp, int buf) {
+            dma16(rsrc + grp * RC * 8, rec_lds + (uint32_t)(buf * 4 * kRecWave + wave * kRecWave));
         };
 
         f32x4_t acc[NMAT][kMaxMT][2];
@@ -269,68 +337,96 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
         for (int q = 0; q < NMAT; ++q) {
             wq[q] = (int)(offsetof(Stage<NMAT>, w) + q * kNT * 32) + wave * 1024 + lq * 4;
-            pq[q] = (int)(offsetof(Stage<NMAT>, p) + q * kNT * 8) + wave * 256;
+            pq[q] = q * 32 * LPR * 16 + wave * kRecWave;
             asm volatile("" : "+v"(wq[q]), "+v"(pq[q]));
         }
-        auto compute = [&](const Stage<NMAT> &st) {
+        // One chunk of MT M tiles: every LDS read of the chunk is issued first (the
+        // B codes of both 32-column halves, their records as one 8-byte read per
+        // row from rb, the chunk's place in its record buffer, the A tiles), then
+        // each half is dequantised and multiplied.
+        auto compute = [&](const Stage<NMAT> &st, const uint8_t *rb, auto mt_count) {
+            constexpr int MT = decltype(mt_count)::value;
             const uint8_t *sb = reinterpret_cast<const uint8_t *>(&st);
+            uint32_t codes[2][NMAT][2];
+            uint64_t recs[NMAT][2];
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int rl = nt * 16 + lr;  // row within the wave's 32
+                    recs[q][nt] = *reinterpret_cast<const uint64_t *>(rb + pq[q] + rl * RC * 8);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+                        codes[kb][q][nt] = *reinterpret_cast<const uint32_t *>(sb + wq[q] + (kb * 32 + rl) * 16);
+                }
+            uint4 av[2][MT];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int r = mt * 16 + lr;
+                    av[kb][mt] = *reinterpret_cast<const uint4 *>(&st.x[r * kXRow + (((kb * 4 + lq) ^ (r & 7)) * 16)]);
+                }
 #pragma unroll
             for (int kb = 0; kb < kKC / 32; ++kb) {
-                // B operands: this wave's 2 N tiles of each matrix
                 bf16x8_t bo[NMAT][2];
 #pragma unroll
                 for (int q = 0; q < NMAT; ++q)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const int rl = nt * 16 + lr;  // row within the wave's 32
-                        const uint32_t codes = *reinterpret_cast<const uint32_t *>(sb + wq[q] + (kb * 32 + rl) * 16);
-                        const uint32_t rec = *reinterpret_cast<const uint32_t *>(sb + pq[q] + (rl * 2 + kb) * 4);
-                        bo[q][nt] = dequant8(codes, rec, dq);
-                    }
-                // A operands of every M tile read at once (rows past the tokens hold
-                // valid data), so the LDS latency is paid once per 32 columns
-                uint4 av[kMaxMT];
+                    for (int nt = 0; nt < 2; ++nt)
+                        bo[q][nt] = dequant8(codes[kb][q][nt], (uint32_t)(recs[q][nt] >> (32 * kb)), dq);
 #pragma unroll
-                for (int mt = 0; mt < kMaxMT; ++mt) {
-                    const int r = mt * 16 + lr;
-                    av[mt] = *reinterpret_cast<const uint4 *>(&st.x[r * kXRow + (((kb * 4 + lq) ^ (r & 7)) * 16)]);
-                }
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[kb][mt]);
 #pragma unroll
-                for (int mt = 0; mt < kMaxMT; ++mt) {
-                    if (mt < mtiles) {
-                        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[mt]);
+                    for (int q = 0; q < NMAT; ++q)
 #pragma unroll
-                        for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-                            for (int nt = 0; nt < 2; ++nt)
-                                acc[q][mt][nt] =
-                                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bo[q][nt], acc[q][mt][nt], 0, 0, 0);
-                    }
+                        for (int nt = 0; nt < 2; ++nt)
+                            acc[q][mt][nt] =
+                                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bo[q][nt], acc[q][mt][nt], 0, 0, 0);
                 }
             }
         };
 
-        // One chunk: wait for its loads, barrier, refill the buffer freed by the
-        // previous chunk with chunk c + S - 1, multiply.  Every step issues one
-        // stage (past the last chunk it re-loads the last chunk into a buffer
-        // that is not read again), so exactly S - 2 stages are in flight behind
-        // the one being waited for, and the loop carries a fixed load count.
-        auto step = [&](const Stage<NMAT> &cur, uint32_t refill, int c) {
-            __builtin_amdgcn_s_waitcnt(kWaitVm((S - 2) * per_stage));
+        // Step c (at position b of the unrolled loop): wait until chunk c's stage
+        // and its records have landed (exact vmcnt, from the fixed issue order),
+        // barrier, refill the stage buffer freed by chunk c - 1 with chunk c + S - 1
+        // and, at the start of a record group, the record buffer freed by the
+        // previous group with the next group's records, then multiply.  Past the
+        // last chunk (group) a step re-loads the last one into a buffer that is
+        // not read again, so every step issues a fixed number of loads.
+        const int ngroups = nchunks / RC;
+        auto step = [&](int c, auto b_const, auto mt_count) {
+            constexpr int b = decltype(b_const)::value;
+            constexpr int P = (decltype(mt_count)::value + 1) / 2 + NMAT;  // loads of one stage
+            __builtin_amdgcn_s_waitcnt(kWaitVm(vm_allow(S, RC, P, 1, U, b)));
             ring_barrier();
-            issue(refill, min(c + S - 1, nchunks - 1));
-            compute(cur);
+            issue(stage_addr((b + S - 1) % S), min(c + S - 1, nchunks - 1), mt_count);
+            if (b % RC == 0) issue_rec(min(c / RC + 1, ngroups - 1), (c / RC + 1) & 1);
+            compute(ring[b % S], &recs_lds[(c / RC) & 1][(b % RC) * 8], mt_count);
         };
 
-        // stage b of the ring holds chunks b, b + S, ...; the loop is unrolled by S
-        // so that every step names its stages with constants
+        // The K loop, specialised on the pass's M tile count so that the chunk
+        // body has no branches, and unrolled by U so that every step names its
+        // buffers with constants.
+        auto k_loop = [&](auto mt_count) {
+            issue_rec(0, 0);
 #pragma unroll
-        for (int b = 0; b < S - 1; ++b) issue(stage_addr(b), min(b, nchunks - 1));
-        for (int c0 = 0; c0 < nchunks; c0 += S) {
-#pragma unroll
-            for (int b = 0; b < S; ++b)
-                if (c0 + b < nchunks) step(ring[b], stage_addr((b + S - 1) % S), c0 + b);
+            for (int b = 0; b < S - 1; ++b) issue(stage_addr(b), min(b, nchunks - 1), mt_count);
+            for (int c0 = 0; c0 < nchunks; c0 += U)
+                static_for<0, U>([&](auto b_const) {
+                    if (c0 + decltype(b_const)::value < nchunks) step(c0 + decltype(b_const)::value, b_const, mt_count);
+                });
+        };
+        switch (mtiles) {
+            case 1: k_loop(IntC<1>{}); break;
+            case 2: k_loop(IntC<2>{}); break;
+            case 3: k_loop(IntC<3>{}); break;
+            case 4: k_loop(IntC<4>{}); break;
+            case 5: k_loop(IntC<5>{}); break;
+            default: k_loop(IntC<6>{}); break;
         }
+        static_assert(kMaxMT == 6, "one k_loop case per M tile count");
 
         // no load may still be writing LDS when the workgroup moves on or exits
         __builtin_amdgcn_s_waitcnt(kWaitVm(0));
@@ -368,19 +464,23 @@ bool mfma_supported(const FfnArgs &a) { return a.grouped && a.H % 128 == 0 && a.
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-template <bool GATEUP, int S>
+template <bool GATEUP, int S, int RC>
 int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     const int ntiles = ((GATEUP ? a.I : a.H) + kNT - 1) / kNT;
     const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, RC>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
                        n_groups);
     MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
 
-int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true, kStagesGateUp>(a, s); }
+// Record groups: 2 chunks (128 columns) for gate/up, whose H is a multiple of
+// 128; 4 chunks for the down projection when I is a multiple of 256, else 2.
+int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true, kStagesGateUp, 2>(a, s); }
 
-int mfma_down(const FfnArgs &a, hipStream_t s) { return launch_mfma<false, kStagesDown>(a, s); }
+int mfma_down(const FfnArgs &a, hipStream_t s) {
+    return a.I % 256 == 0 ? launch_mfma<false, kStagesDown, 4>(a, s) : launch_mfma<false, kStagesDown, 2>(a, s);
+}
 
 }  // namespace moe
