@@ -8,13 +8,14 @@
 // the expert's tokens in M chunks of up to 96, so at prefill sizes (about 64
 // tokens per expert) every weight byte is read from HBM once.
 //
-// The K dimension streams in chunks of 64 columns through a ring of S LDS
-// buffers filled by direct global->LDS loads (global_load_lds_dwordx4), so the
-// loads of the next S-1 chunks are in flight while the current chunk is
-// multiplied and no registers hold data on its way to LDS.  The (scale, min)
-// records come through a ring of their own, RC chunks per load (16 or 32 bytes
-// per row): fetched with the codes, 8 bytes per row and chunk, they cost as
-// much load bandwidth as the codes, since every row is a separate fetch.  Each wave loads its
+// The K dimension streams in chunks of 64 columns.  Direct global->LDS loads
+// (global_load_lds_dwordx4) fill two rings: the activation tiles, one chunk per
+// stage, S stages deep; and the weights (codes and (scale, min) records), G
+// chunks per buffer, two buffers, so that each row's codes come as one G*32-byte
+// piece and its records as one G*8-byte piece (every row is a separate access,
+// and small per-row pieces bound the kernel well before HBM does).  While a
+// chunk is multiplied the next S-1 activation chunks and the next weight group
+// are in flight, and no registers hold data on its way to LDS.  Each wave loads its
 // own 32 weight rows; the activation tile is shared and XOR-swizzled in 16-byte
 // units so that the A-operand reads hit distinct banks.  One barrier per chunk:
 // each wave first waits (exact vmcnt) for its own loads of the chunk, the
@@ -48,25 +49,41 @@ constexpr int kXcds = 8;       // workgroups are dealt to the XCDs round-robin
 #define MOE_MFMA_STAGES_GU 3
 #endif
 #ifndef MOE_MFMA_STAGES_DN
-#define MOE_MFMA_STAGES_DN 4
+#define MOE_MFMA_STAGES_DN 3
 #endif
-constexpr int kStagesGateUp = MOE_MFMA_STAGES_GU;  // ring depth: 3 x 22 KB of LDS, two workgroups per CU
-constexpr int kStagesDown = MOE_MFMA_STAGES_DN;    // 4 x 17 KB
+// activation ring depths (12 KB stages); with the weight ring (40 KB) two
+// workgroups fit a CU
+constexpr int kStagesGateUp = MOE_MFMA_STAGES_GU;
+constexpr int kStagesDown = MOE_MFMA_STAGES_DN;
 
-// One ring stage: the chunk's activation tile (row r, 16-byte unit u stored at
-// unit position u ^ (r & 7)), and per matrix the codes of the 128 rows, wave
-// w's 32 rows in its own 1 KB (unit (row, half) at position half*32 + row).
-template <int NMAT>
-struct __attribute__((aligned(16))) Stage {
+// Activation ring stage: one chunk's tile, row r's 16-byte unit u stored at unit
+// position u ^ (r & 7).
+struct __attribute__((aligned(16))) XStage {
     uint8_t x[kMC * kXRow];
-    uint8_t w[NMAT][kNT * 32];
 };
 
-// Record buffer: per wave 1 KB, the records of RC chunks (2*RC blocks, 8*RC
-// bytes) of its 32 rows of each matrix, matrix-major then row-major.  One
-// 64-lane 16-byte load fills it (lanes beyond NMAT*RC*16 repeat the first ones
-// into the unused rest).
-constexpr int kRecWave = 1024;
+// Weight ring buffer: the codes and records of G chunks (one group) of the
+// workgroup's 128 rows, per wave (32 rows) a block of wave_bytes:
+//   codes  [NMAT][32 rows][G*32 B]: row r's 16-byte unit u at unit position
+//          u ^ swz(r), so that the B-operand reads of 16 rows hit distinct banks
+//   records[NMAT][32 rows][G*8 B], padded to 1 KB: one 64-lane 16-byte load
+//          fills it (lanes beyond NMAT*G*16 repeat the first ones into the pad)
+// A row's G*32 code bytes are fetched by 2G adjacent lanes: fetched per chunk,
+// 32 bytes per row by lanes far apart, the codes cost a separate access per
+// row and lane quad, which bounds the kernel before HBM does.
+template <int NMAT, int G>
+struct WLayout {
+    static constexpr int row_code = G * 32;                 // code bytes of one row and group
+    static constexpr int codes = NMAT * 32 * row_code;       // per wave
+    static constexpr int wave_bytes = codes + 1024;
+    static constexpr int buffer = 4 * wave_bytes;
+    static constexpr int code_loads = codes / 1024;          // 16-byte loads per wave and group
+    static constexpr int loads = code_loads + 1;             // with the records
+    // unit swizzle of row r (2G units per row): for any one unit, 16 rows that
+    // start at a multiple of 16 land in 16 distinct 16-byte slots of a 256-byte
+    // bank window
+    __device__ static int swz(int r) { return (r >> (G == 2 ? 2 : 1)) & (2 * G - 1); }
+};
 
 // Number of multiples of m in [lo, hi].
 constexpr int multiples(int lo, int hi, int m) {
@@ -107,8 +124,8 @@ constexpr int lcm(int a, int b) {
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// Direct global->LDS loads: lane l's 16 (or 4) bytes from g land at LDS byte
-// lds + 16*l (4*l); lds must be the same in every lane.  Written as inline asm
+// Direct global->LDS load: lane l's 16 bytes from g land at LDS byte lds + 16*l;
+// lds must be the same in every lane.  Written as inline asm
 // because the compiler, when it sees these loads, makes every later LDS read
 // wait for all of them (it cannot tell the ring's stages apart), which would
 // drain the ring each chunk; completion is tracked with explicit vmcnt waits
@@ -118,9 +135,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *lds) {
 }
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds));
-}
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
-    asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds));
 }
 
 constexpr int kWaitVm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
@@ -214,15 +228,17 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, const
     return __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, w45, w67));
 }
 
-template <bool GATEUP, int S, int RC>
+template <bool GATEUP, int S, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_ffn_kernel(moe::FfnArgs a, int ntiles,
                                                                                            int n_groups) {
     constexpr int NMAT = GATEUP ? 2 : 1;
-    static_assert(S >= 2, "the ring needs two stages at least");
-    static_assert((RC == 2 || RC == 4) && NMAT * RC <= 4, "one 16-byte load per lane fills a record buffer");
-    constexpr int U = lcm(S, RC);       // steps per unrolled loop body
-    constexpr int LPR = RC / 2;         // lanes per row of a record load
-    const int K = GATEUP ? a.H : a.I;   // reduction length (a multiple of 64 * RC)
+    using WL = WLayout<NMAT, G>;
+    static_assert(S >= 2, "the activation ring needs two stages at least");
+    static_assert((G == 2 || G == 4) && NMAT * G <= 4, "one 16-byte load per lane fills a record block");
+    static_assert(S * sizeof(XStage) + 2 * WL::buffer + 2 * kMC * sizeof(int) <= 80 * 1024,
+                  "two workgroups per CU");
+    constexpr int U = lcm(S, G);        // steps per unrolled loop body
+    const int K = GATEUP ? a.H : a.I;   // reduction length (a multiple of 64 * G)
     const int R = GATEUP ? a.I : a.H;   // weight rows (output columns)
     // every tile of one expert on the same XCD
     const int xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
@@ -248,38 +264,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                                  moe::slab_w3(slab, a.H, a.I)};
     const uint16_t *act = GATEUP ? a.x : a.h;
 
-    __shared__ Stage<NMAT> ring[S];
+    __shared__ XStage ring[S];
+    __shared__ __attribute__((aligned(16))) uint8_t wring[2][WL::buffer];
     const uint32_t ring_lds = lds_addr(&ring[0]);
-    auto stage_addr = [&](int b) { return ring_lds + (uint32_t)(b * sizeof(Stage<NMAT>)); };
-    __shared__ __attribute__((aligned(16))) uint8_t recs_lds[2][4 * kRecWave];
-    const uint32_t rec_lds = lds_addr(&recs_lds[0][0]);
+    const uint32_t wring_lds = lds_addr(&wring[0][0]);
+    auto stage_addr = [&](int b) { return ring_lds + (uint32_t)(b * sizeof(XStage)); };
     __shared__ int s_src[kMC];  // activation row of each M row
     __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
     const Dequant dq = dequant_consts();
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;  // MFMA row-in-tile and k-quarter
-    const int nchunks = K / kKC;
+    const int nchunks = K / kKC, ngroups = nchunks / G;
+    const int wrow0 = n0 + 32 * wave;  // first weight row of this wave
 
-    // this lane's global sources, fixed over a pass: weight rows of its wave
-    const int wrow = n0 + 32 * wave + (lane & 31);           // codes: lanes 0-31 half 0, 32-63 half 1
-    const uint8_t *wsrc[NMAT];
+    // This lane's weight sources, fixed over the kernel (a group adds grp*G*32
+    // to the codes, grp*G*8 to the records).  Code load j = q*G + h covers rows
+    // h*32/G .. of matrix q: lane l takes row h*32/G + l/(2G), unit (l % 2G) ^ swz.
+    const uint8_t *csrc[NMAT * G];
 #pragma unroll
-    for (int q = 0; q < NMAT; ++q) wsrc[q] = mat[q].row0 + (size_t)wrow * mat[q].stride + (lane >> 5) * 16;
-    // records: lane (q, row, part) of the NMAT * 32 * LPR used lanes takes bytes
-    // 16*part .. 16*part+15 of the row's records of a group of RC chunks
+    for (int j = 0; j < NMAT * G; ++j) {
+        const int q = j / G, h = j % G;
+        const int r = h * (32 / G) + lane / (2 * G), u = (lane % (2 * G)) ^ WL::swz(r);
+        csrc[j] = mat[q].row0 + (size_t)(wrow0 + r) * mat[q].stride + u * 16;
+    }
+    // records: lane (q, row, part) of the NMAT*G*16 used lanes takes bytes
+    // 16*part .. 16*part+15 of the row's G*8 record bytes of a group
     const uint8_t *rsrc;
     {
+        constexpr int LPR = G / 2;  // lanes per row
         const int ll = lane % (NMAT * 32 * LPR);
         const int q = ll / (32 * LPR), r = (ll % (32 * LPR)) / LPR, part = ll % LPR;
         const moe::MatRows &m = q ? mat[1] : mat[0];
-        rsrc = m.row0 + (size_t)(n0 + 32 * wave + r) * m.stride + K / 2 + part * 16;
+        rsrc = m.row0 + (size_t)(wrow0 + r) * m.stride + K / 2 + part * 16;
+    }
+    // the group grp's codes and records into weight buffer buf (NMAT*G + 1 loads)
+    auto issue_w = [&](int grp, int buf) {
+        const uint32_t wb = wring_lds + (uint32_t)(buf * WL::buffer + wave * WL::wave_bytes);
+#pragma unroll
+        for (int j = 0; j < NMAT * G; ++j) dma16(csrc[j] + grp * G * 32, wb + (uint32_t)(j * 1024));
+        dma16(rsrc + grp * G * 8, wb + (uint32_t)WL::codes);
+    };
+
+    // B-operand read offsets in a wave block: row rl = nt*16 + lr of matrix q,
+    // the k-quarter's dword; the unit position is XORed with swz(rl) per read
+    int cq[NMAT][2], swz16[2], rq[NMAT][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int rl = nt * 16 + lr;
+        swz16[nt] = WL::swz(rl) * 16;
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+            cq[q][nt] = wave * WL::wave_bytes + q * 32 * WL::row_code + rl * WL::row_code + lq * 4;
+            rq[q][nt] = wave * WL::wave_bytes + WL::codes + q * 32 * G * 8 + rl * G * 8;
+        }
     }
 
     for (int m0 = 0; m0 < M; m0 += kMC) {
         const int mc = min(kMC, M - m0);
         const int mtiles = (mc + 15) >> 4;
-        __syncthreads();  // the previous pass is done with s_src / s_dst and the ring
+        __syncthreads();  // the previous pass is done with s_src / s_dst and the rings
         if (tid < kMC) {
             int src = -1, dst = -1;
             const int m = m0 + (tid < mc ? tid : 0);  // padding rows repeat the first row
@@ -305,20 +349,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             const int r = 8 * (wave + 4 * j) + (lane >> 3), pos = lane & 7;
             xsrc[j] = act + (size_t)s_src[r] * K + 8 * (pos ^ (r & 7));
         }
-
-        // LDS byte address of stage st (uniform), then constant offsets
-        auto issue = [&](uint32_t st, int c, auto mt_count) {
+        // chunk c's activation tile into the stage at LDS address st
+        auto issue_x = [&](uint32_t st, int c, auto mt_count) {
             constexpr int XJ = (decltype(mt_count)::value + 1) / 2;
             const int k0 = c * kKC;
 #pragma unroll
             for (int j = 0; j < XJ; ++j) dma16(xsrc[j] + k0, st + (uint32_t)((wave + 4 * j) * 1024));
-#pragma unroll
-            for (int q = 0; q < NMAT; ++q)
-                dma16(wsrc[q] + k0 / 2, st + (uint32_t)(offsetof(Stage<NMAT>, w) + q * kNT * 32 + wave * 1024));
-        };
-        // the records of chunk group grp into record buffer buf (one load per wave)
-        auto issue_rec = [&](int grp, int buf) {
-            dma16(rsrc + grp * RC * 8, rec_lds + (uint32_t)(buf * 4 * kRecWave + wave * kRecWave));
         };
 
         f32x4_t acc[NMAT][kMaxMT][2];
@@ -329,35 +365,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) acc[q][mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // Byte offsets of matrix q's codes and records in a stage, hidden from the
-        // optimiser: otherwise it pairs the reads of the two matrices into one
-        // ds_read2st64, whose merged memory operand no longer shows which stage it
-        // reads, and then waits for every load in flight before it.
-        int wq[NMAT], pq[NMAT];
-#pragma unroll
-        for (int q = 0; q < NMAT; ++q) {
-            wq[q] = (int)(offsetof(Stage<NMAT>, w) + q * kNT * 32) + wave * 1024 + lq * 4;
-            pq[q] = q * 32 * LPR * 16 + wave * kRecWave;
-            asm volatile("" : "+v"(wq[q]), "+v"(pq[q]));
-        }
-        // One chunk of MT M tiles: every LDS read of the chunk is issued first (the
-        // B codes of both 32-column halves, their records as one 8-byte read per
-        // row from rb, the chunk's place in its record buffer, the A tiles), then
-        // each half is dequantised and multiplied.
-        auto compute = [&](const Stage<NMAT> &st, const uint8_t *rb, auto mt_count) {
+        // One chunk (chunk cg of its group, weight buffer wb) of MT M tiles: every
+        // LDS read of the chunk is issued first (the B codes of both 32-column
+        // halves, their records as one 8-byte read per row, the A tiles), then each
+        // half is dequantised and multiplied.
+        auto compute = [&](const XStage &st, const uint8_t *wb, auto cg_const, auto mt_count) {
             constexpr int MT = decltype(mt_count)::value;
-            const uint8_t *sb = reinterpret_cast<const uint8_t *>(&st);
+            constexpr int cg = decltype(cg_const)::value;
             uint32_t codes[2][NMAT][2];
             uint64_t recs[NMAT][2];
 #pragma unroll
             for (int q = 0; q < NMAT; ++q)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    const int rl = nt * 16 + lr;  // row within the wave's 32
-                    recs[q][nt] = *reinterpret_cast<const uint64_t *>(rb + pq[q] + rl * RC * 8);
+                    recs[q][nt] = *reinterpret_cast<const uint64_t *>(wb + rq[q][nt] + cg * 8);
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
-                        codes[kb][q][nt] = *reinterpret_cast<const uint32_t *>(sb + wq[q] + (kb * 32 + rl) * 16);
+                        codes[kb][q][nt] =
+                            *reinterpret_cast<const uint32_t *>(wb + cq[q][nt] + (((2 * cg + kb) * 16) ^ swz16[nt]));
                 }
             uint4 av[2][MT];
 #pragma unroll
@@ -388,31 +413,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             }
         };
 
-        // Step c (at position b of the unrolled loop): wait until chunk c's stage
-        // and its records have landed (exact vmcnt, from the fixed issue order),
-        // barrier, refill the stage buffer freed by chunk c - 1 with chunk c + S - 1
-        // and, at the start of a record group, the record buffer freed by the
-        // previous group with the next group's records, then multiply.  Past the
-        // last chunk (group) a step re-loads the last one into a buffer that is
-        // not read again, so every step issues a fixed number of loads.
-        const int ngroups = nchunks / RC;
+        // Step c (at position b of the unrolled loop): wait until chunk c's
+        // activations and its group's weights have landed (exact vmcnt, from the
+        // fixed issue order), barrier, refill the stage freed by chunk c - 1 with
+        // chunk c + S - 1 and, at the start of a group, the weight buffer freed by
+        // the previous group with the next group, then multiply.  Past the last
+        // chunk (group) a step re-loads the last one into a buffer that is not
+        // read again, so every step issues a fixed number of loads.
         auto step = [&](int c, auto b_const, auto mt_count) {
             constexpr int b = decltype(b_const)::value;
-            constexpr int P = (decltype(mt_count)::value + 1) / 2 + NMAT;  // loads of one stage
-            __builtin_amdgcn_s_waitcnt(kWaitVm(vm_allow(S, RC, P, 1, U, b)));
+            constexpr int P = (decltype(mt_count)::value + 1) / 2;  // activation loads of one stage
+            __builtin_amdgcn_s_waitcnt(kWaitVm(vm_allow(S, G, P, WL::loads, U, b)));
             ring_barrier();
-            issue(stage_addr((b + S - 1) % S), min(c + S - 1, nchunks - 1), mt_count);
-            if (b % RC == 0) issue_rec(min(c / RC + 1, ngroups - 1), (c / RC + 1) & 1);
-            compute(ring[b % S], &recs_lds[(c / RC) & 1][(b % RC) * 8], mt_count);
+            issue_x(stage_addr((b + S - 1) % S), min(c + S - 1, nchunks - 1), mt_count);
+            if (b % G == 0) issue_w(min(c / G + 1, ngroups - 1), (c / G + 1) & 1);
+            compute(ring[b % S], &wring[(c / G) & 1][0], IntC<b % G>{}, mt_count);
         };
 
         // The K loop, specialised on the pass's M tile count so that the chunk
         // body has no branches, and unrolled by U so that every step names its
         // buffers with constants.
         auto k_loop = [&](auto mt_count) {
-            issue_rec(0, 0);
+            issue_w(0, 0);
 #pragma unroll
-            for (int b = 0; b < S - 1; ++b) issue(stage_addr(b), min(b, nchunks - 1), mt_count);
+            for (int b = 0; b < S - 1; ++b) issue_x(stage_addr(b), min(b, nchunks - 1), mt_count);
             for (int c0 = 0; c0 < nchunks; c0 += U)
                 static_for<0, U>([&](auto b_const) {
                     if (c0 + decltype(b_const)::value < nchunks) step(c0 + decltype(b_const)::value, b_const, mt_count);
@@ -464,19 +488,20 @@ bool mfma_supported(const FfnArgs &a) { return a.grouped && a.H % 128 == 0 && a.
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-template <bool GATEUP, int S, int RC>
+template <bool GATEUP, int S, int G>
 int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     const int ntiles = ((GATEUP ? a.I : a.H) + kNT - 1) / kNT;
     const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, RC>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, G>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
                        n_groups);
     MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
 
-// Record groups: 2 chunks (128 columns) for gate/up, whose H is a multiple of
-// 128; 4 chunks for the down projection when I is a multiple of 256, else 2.
+// Weight groups: 2 chunks (128 columns, 64 code bytes per row) for gate/up,
+// whose H is a multiple of 128; 4 chunks (a 128-byte line of codes per row) for
+// the down projection when I is a multiple of 256, else 2.
 int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true, kStagesGateUp, 2>(a, s); }
 
 int mfma_down(const FfnArgs &a, hipStream_t s) {
