@@ -39,7 +39,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kNT = 128;       // weight rows (N) per workgroup
+constexpr int kNT = 128;       // weight rows (N) of each matrix per workgroup
 constexpr int kKC = 64;        // columns (K) per chunk
 constexpr int kMaxMT = 6;      // 16-row M tiles per pass
 constexpr int kMC = 16 * kMaxMT;
@@ -228,10 +228,14 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, const
     return __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, w45, w67));
 }
 
-template <bool GATEUP, int S, int G>
+// NMAT weight matrices of 128 rows per workgroup: W1 and W3 for gate/up; for
+// the down projection two 128-row tiles of W2 (PAIR, H a multiple of 256, so
+// that every activation tile loaded serves 256 weight rows) or one.
+template <bool GATEUP, int S, int G, bool PAIR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_ffn_kernel(moe::FfnArgs a, int ntiles,
                                                                                            int n_groups) {
-    constexpr int NMAT = GATEUP ? 2 : 1;
+    constexpr int NMAT = GATEUP || PAIR ? 2 : 1;
+    constexpr int kTileN = GATEUP ? kNT : NMAT * kNT;  // output columns per workgroup
     using WL = WLayout<NMAT, G>;
     static_assert(S >= 2, "the activation ring needs two stages at least");
     static_assert((G == 2 || G == 4) && NMAT * G <= 4, "one 16-byte load per lane fills a record block");
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
     const int g = (i / ntiles) * kXcds + xcd, tile = i % ntiles;
     if (g >= n_groups) return;
-    const int n0 = tile * kNT;
+    const int n0 = tile * kTileN;
 
     // resolve the group: routed expert g (grouped), or the shared expert
     const uint8_t *slab;
@@ -260,8 +264,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         slab = (const uint8_t *)a.shared;
         M = a.T;
     }
-    const moe::MatRows mat[2] = {GATEUP ? moe::slab_w1(slab, a.H, a.I) : moe::slab_w2(slab, a.H, a.I),
-                                 moe::slab_w3(slab, a.H, a.I)};
+    moe::MatRows mat[2] = {GATEUP ? moe::slab_w1(slab, a.H, a.I) : moe::slab_w2(slab, a.H, a.I),
+                           moe::slab_w3(slab, a.H, a.I)};
+    if (!GATEUP) {  // matrix 1 of a pair: the W2 rows 128 further on
+        mat[1] = mat[0];
+        mat[1].row0 += (size_t)kNT * mat[0].stride;
+    }
     const uint16_t *act = GATEUP ? a.x : a.h;
 
     __shared__ XStage ring[S];
@@ -468,10 +476,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                     if (m >= mc || n >= R) continue;
                     const int row = s_dst[m];
                     if (GATEUP) {
-                        const float gv = acc[0][mt][nt][j], uv = acc[NMAT - 1][mt][nt][j];
+                        const float gv = acc[0][mt][nt][j], uv = acc[1][mt][nt][j];
                         a.h[(size_t)row * a.I + n] = (uint16_t)f32_to_bf16_bits(gv / (1.0f + expf(-gv)) * uv);
                     } else {
-                        a.y[(size_t)row * a.H + n] = acc[0][mt][nt][j];
+#pragma unroll
+                        for (int q = 0; q < NMAT; ++q) a.y[(size_t)row * a.H + n + q * kNT] = acc[q][mt][nt][j];
                     }
                 }
             }
@@ -488,23 +497,25 @@ bool mfma_supported(const FfnArgs &a) { return a.grouped && a.H % 128 == 0 && a.
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-template <bool GATEUP, int S, int G>
+template <bool GATEUP, int S, int G, bool PAIR = false>
 int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
-    const int ntiles = ((GATEUP ? a.I : a.H) + kNT - 1) / kNT;
+    const int ntiles = GATEUP ? a.I / kNT : a.H / (PAIR ? 2 * kNT : kNT);
     const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, G>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a, ntiles,
-                       n_groups);
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, G, PAIR>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a,
+                       ntiles, n_groups);
     MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
 
-// Weight groups: 2 chunks (128 columns, 64 code bytes per row) for gate/up,
-// whose H is a multiple of 128; 4 chunks (a 128-byte line of codes per row) for
-// the down projection when I is a multiple of 256, else 2.
+// Weight groups: 2 chunks (128 columns, 64 code bytes per row) with two
+// matrices per workgroup (gate/up, and the down projection when H is a multiple
+// of 256); with one matrix, 4 chunks (a 128-byte line of codes per row) when
+// the reduction length is a multiple of 256, else 2.
 int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true, kStagesGateUp, 2>(a, s); }
 
 int mfma_down(const FfnArgs &a, hipStream_t s) {
+    if (a.H % (2 * kNT) == 0) return launch_mfma<false, kStagesDown, 2, true>(a, s);
     return a.I % 256 == 0 ? launch_mfma<false, kStagesDown, 4>(a, s) : launch_mfma<false, kStagesDown, 2>(a, s);
 }
 

@@ -332,6 +332,10 @@ PREFILL_CASES = [
     ("prefill2048", 2048, 6144, 2048, 256, 8, False, None, [0, 1, 777, 2047]),
     ("hot_expert", 300, 512, 256, 16, 4, True, 3, [0, 150, 299]),
     ("tiny_prefill", 129, 256, 128, 16, 2, False, None, None),
+    # H not a multiple of 256: the down projection takes one 128-row W2 tile per
+    # workgroup, with weight groups of 2 chunks (I = 128) and of 4 (I = 256)
+    ("odd_hidden_i128", 160, 384, 128, 8, 2, False, None, None),
+    ("odd_hidden_i256", 200, 640, 256, 8, 2, True, None, None),
 ]
 
 
