@@ -33,6 +33,9 @@
 #include "common.h"
 #include "dequant.h"
 #include "ffn.h"
+#ifndef MOE_EXP_SCHED
+#define MOE_EXP_SCHED 0
+#endif
 
 namespace {
 
@@ -45,16 +48,18 @@ constexpr int kMaxMT = 6;      // 16-row M tiles per pass
 constexpr int kMC = 16 * kMaxMT;
 constexpr int kXRow = kKC * 2; // bytes of one activation row of a chunk (8 units of 16 B)
 constexpr int kXcds = 8;       // workgroups are dealt to the XCDs round-robin
-#ifndef MOE_MFMA_STAGES_GU
-#define MOE_MFMA_STAGES_GU 3
+#ifndef MOE_MFMA_STAGES
+#define MOE_MFMA_STAGES 2
 #endif
-#ifndef MOE_MFMA_STAGES_DN
-#define MOE_MFMA_STAGES_DN 3
+#ifndef MOE_MFMA_REC_GROUP
+#define MOE_MFMA_REC_GROUP 4
 #endif
-// activation ring depths (12 KB stages); with the weight ring (40 KB) two
-// workgroups fit a CU
-constexpr int kStagesGateUp = MOE_MFMA_STAGES_GU;
-constexpr int kStagesDown = MOE_MFMA_STAGES_DN;
+// Activation ring depth (12 KB stages; the tiles are L2 hits, shared by all
+// tiles of an expert, so one chunk of lead hides them) and the record group of
+// two-matrix workgroups; with the weight rings two workgroups fit a CU.
+constexpr int kStagesGateUp = MOE_MFMA_STAGES;
+constexpr int kStagesDown = MOE_MFMA_STAGES;
+constexpr int kRecGroup = MOE_MFMA_REC_GROUP;
 
 // Activation ring stage: one chunk's tile, row r's 16-byte unit u stored at unit
 // position u ^ (r & 7).
@@ -62,52 +67,67 @@ struct __attribute__((aligned(16))) XStage {
     uint8_t x[kMC * kXRow];
 };
 
-// Weight ring buffer: the codes and records of G chunks (one group) of the
-// workgroup's 128 rows, per wave (32 rows) a block of wave_bytes:
-//   codes  [NMAT][32 rows][G*32 B]: row r's 16-byte unit u at unit position
-//          u ^ swz(r), so that the B-operand reads of 16 rows hit distinct banks
-//   records[NMAT][32 rows][G*8 B], padded to 1 KB: one 64-lane 16-byte load
-//          fills it (lanes beyond NMAT*G*16 repeat the first ones into the pad)
-// A row's G*32 code bytes are fetched by 2G adjacent lanes: fetched per chunk,
-// 32 bytes per row by lanes far apart, the codes cost a separate access per
-// row and lane quad, which bounds the kernel before HBM does.
-template <int NMAT, int G>
+// Weight rings, per wave (32 rows of each of NMAT matrices) a block in each:
+//   codes   [NMAT][32 rows][G*32 B], one group of G chunks per buffer: row r's
+//           16-byte unit u at unit position u ^ swz(r), so that the B-operand
+//           reads of 16 rows hit distinct banks
+//   records [NMAT][32 rows][R*8 B], one group of R chunks per buffer, at least
+//           1 KB: every 64-lane 16-byte load fills 1 KB (with one matrix and
+//           R = 2, lanes beyond 32 repeat the first ones into the rest)
+// A row's G*32 code bytes (R*8 record bytes) are fetched by adjacent lanes as
+// one piece: the memory pipeline tracks a bounded number of requests per CU, and
+// a request carries one row's piece of at most 64 bytes, so bytes per row and
+// fetch set the kernel's load bandwidth well below HBM's.
+template <int NMAT, int G, int R>
 struct WLayout {
-    static constexpr int row_code = G * 32;                 // code bytes of one row and group
-    static constexpr int codes = NMAT * 32 * row_code;       // per wave
-    static constexpr int wave_bytes = codes + 1024;
-    static constexpr int buffer = 4 * wave_bytes;
-    static constexpr int code_loads = codes / 1024;          // 16-byte loads per wave and group
-    static constexpr int loads = code_loads + 1;             // with the records
+    static constexpr int row_code = G * 32;                  // code bytes of one row and group
+    static constexpr int codes = NMAT * 32 * row_code;        // per wave
+    static constexpr int code_loads = codes / 1024;           // 16-byte loads per wave and group
+    static constexpr int row_rec = R * 8;                     // record bytes of one row and group
+    static constexpr int recs = NMAT * 32 * row_rec < 1024 ? 1024 : NMAT * 32 * row_rec;
+    static constexpr int rec_loads = recs / 1024;
+    static constexpr int rec_lanes = NMAT * 32 * row_rec / 16;  // lanes with distinct data
     // unit swizzle of row r (2G units per row): for any one unit, 16 rows that
     // start at a multiple of 16 land in 16 distinct 16-byte slots of a 256-byte
     // bank window
     __device__ static int swz(int r) { return (r >> (G == 2 ? 2 : 1)) & (2 * G - 1); }
 };
 
-// Number of multiples of m in [lo, hi].
-constexpr int multiples(int lo, int hi, int m) {
-    return hi < lo ? 0 : (lo > 0 ? hi / m - (lo - 1) / m : hi / m + 1);
-}
-
 // Loads a wave may still have in flight when step c waits, such that chunk c's
-// stage and the records of its group are complete.  Issue order: the records of
-// group 0, then stages 0 .. S-2; step j issues stage j+S-1 (P loads) and, when
-// RC divides j, the records of group j/RC + 1 (NR loads).  The count is the
-// number of loads issued after the later of the two.
-constexpr int newer_loads(int S, int RC, int P, int NR, int c) {
-    const int after_stage = P * (S - 2) + NR * multiples(c - S + 1 > 0 ? c - S + 1 : 0, c - 1, RC);
-    const int grp = c / RC;
-    const int after_rec = grp == 0 ? (S - 1 + c) * P + NR * multiples(0, c - 1, RC)
-                                   : (c - 1 - RC * (grp - 1)) * P + NR * multiples(RC * (grp - 1) + 1, c - 1, RC);
-    return after_stage < after_rec ? after_stage : after_rec;
+// activations, its code group and its record group have all landed (vmcnt
+// counts a wave's loads in issue order).  Issue order: records of group 0 (NR
+// loads), codes of group 0 (NC), activation stages 0 .. S-2 (P each); then step
+// j issues stage j+S-1, the codes of group j/G + 1 when G divides j and the
+// records of group j/R + 1 when R divides j.  The count is the number of loads
+// issued, before step c, after the last of the three it needs.
+constexpr int newer_loads(int S, int P, int G, int NC, int R, int NR, int c) {
+    int total = NR + NC, pos_x = 0, pos_code = NR + NC, pos_rec = NR;
+    for (int b = 0; b < S - 1; ++b) {
+        total += P;
+        if (b == c) pos_x = total;
+    }
+    for (int j = 0; j < c; ++j) {
+        total += P;
+        if (j + S - 1 == c) pos_x = total;
+        if (j % G == 0) {
+            total += NC;
+            if (j / G + 1 == c / G) pos_code = total;
+        }
+        if (j % R == 0) {
+            total += NR;
+            if (j / R + 1 == c / R) pos_rec = total;
+        }
+    }
+    int need = pos_x > pos_code ? pos_x : pos_code;
+    need = need > pos_rec ? need : pos_rec;
+    return total - need;
 }
-// The same for every step at position b of a loop unrolled by U (the pattern
-// repeats with period U after the first U steps).
-constexpr int vm_allow(int S, int RC, int P, int NR, int U, int b) {
-    int m = newer_loads(S, RC, P, NR, b);
+// The same for every step at position b of a loop unrolled by U (a multiple of
+// S, G and R: the pattern repeats with period U after the first U steps).
+constexpr int vm_allow(int S, int P, int G, int NC, int R, int NR, int U, int b) {
+    int m = newer_loads(S, P, G, NC, R, NR, b);
     for (int r = 1; r < 4; ++r) {
-        const int v = newer_loads(S, RC, P, NR, b + r * U);
+        const int v = newer_loads(S, P, G, NC, R, NR, b + r * U);
         m = v < m ? v : m;
     }
     return m;
@@ -231,19 +251,19 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, const
 // NMAT weight matrices of 128 rows per workgroup: W1 and W3 for gate/up; for
 // the down projection two 128-row tiles of W2 (PAIR, H a multiple of 256, so
 // that every activation tile loaded serves 256 weight rows) or one.
-template <bool GATEUP, int S, int G, bool PAIR>
+template <bool GATEUP, int S, int G, int R, bool PAIR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_ffn_kernel(moe::FfnArgs a, int ntiles,
                                                                                            int n_groups) {
     constexpr int NMAT = GATEUP || PAIR ? 2 : 1;
     constexpr int kTileN = GATEUP ? kNT : NMAT * kNT;  // output columns per workgroup
-    using WL = WLayout<NMAT, G>;
+    using WL = WLayout<NMAT, G, R>;
     static_assert(S >= 2, "the activation ring needs two stages at least");
-    static_assert((G == 2 || G == 4) && NMAT * G <= 4, "one 16-byte load per lane fills a record block");
-    static_assert(S * sizeof(XStage) + 2 * WL::buffer + 2 * kMC * sizeof(int) <= 80 * 1024,
+    static_assert((G == 2 || G == 4) && (R == 2 || R == 4 || R == 8), "weight group sizes");
+    static_assert(S * sizeof(XStage) + 2 * 4 * (WL::codes + WL::recs) + 2 * kMC * sizeof(int) <= 80 * 1024,
                   "two workgroups per CU");
-    constexpr int U = lcm(S, G);        // steps per unrolled loop body
-    const int K = GATEUP ? a.H : a.I;   // reduction length (a multiple of 64 * G)
-    const int R = GATEUP ? a.I : a.H;   // weight rows (output columns)
+    constexpr int U = lcm(lcm(S, G), R);  // steps per unrolled loop body
+    const int K = GATEUP ? a.H : a.I;   // reduction length (a multiple of 64 * G and 64 * R)
+    const int nrows = GATEUP ? a.I : a.H;  // weight rows (output columns)
     // every tile of one expert on the same XCD
     const int xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
     const int g = (i / ntiles) * kXcds + xcd, tile = i % ntiles;
@@ -273,9 +293,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const uint16_t *act = GATEUP ? a.x : a.h;
 
     __shared__ XStage ring[S];
-    __shared__ __attribute__((aligned(16))) uint8_t wring[2][WL::buffer];
+    __shared__ __attribute__((aligned(16))) uint8_t cring[2][4 * WL::codes];
+    __shared__ __attribute__((aligned(16))) uint8_t rring[2][4 * WL::recs];
     const uint32_t ring_lds = lds_addr(&ring[0]);
-    const uint32_t wring_lds = lds_addr(&wring[0][0]);
+    const uint32_t cring_lds = lds_addr(&cring[0][0]), rring_lds = lds_addr(&rring[0][0]);
     auto stage_addr = [&](int b) { return ring_lds + (uint32_t)(b * sizeof(XStage)); };
     __shared__ int s_src[kMC];  // activation row of each M row
     __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
@@ -283,7 +304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;  // MFMA row-in-tile and k-quarter
-    const int nchunks = K / kKC, ngroups = nchunks / G;
+    const int nchunks = K / kKC, ncgroups = nchunks / G, nrgroups = nchunks / R;
     const int wrow0 = n0 + 32 * wave;  // first weight row of this wave
 
     // This lane's weight sources, fixed over the kernel (a group adds grp*G*32
@@ -296,22 +317,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         const int r = h * (32 / G) + lane / (2 * G), u = (lane % (2 * G)) ^ WL::swz(r);
         csrc[j] = mat[q].row0 + (size_t)(wrow0 + r) * mat[q].stride + u * 16;
     }
-    // records: lane (q, row, part) of the NMAT*G*16 used lanes takes bytes
-    // 16*part .. 16*part+15 of the row's G*8 record bytes of a group
-    const uint8_t *rsrc;
-    {
-        constexpr int LPR = G / 2;  // lanes per row
-        const int ll = lane % (NMAT * 32 * LPR);
-        const int q = ll / (32 * LPR), r = (ll % (32 * LPR)) / LPR, part = ll % LPR;
-        const moe::MatRows &m = q ? mat[1] : mat[0];
-        rsrc = m.row0 + (size_t)(wrow0 + r) * m.stride + K / 2 + part * 16;
-    }
-    // the group grp's codes and records into weight buffer buf (NMAT*G + 1 loads)
-    auto issue_w = [&](int grp, int buf) {
-        const uint32_t wb = wring_lds + (uint32_t)(buf * WL::buffer + wave * WL::wave_bytes);
+    // records: load j, lane l takes piece f = (64j + l) mod rec_lanes, 16 bytes
+    // (part f % LPR) of row (f / LPR) % 32 of matrix f / (32 LPR)
+    const uint8_t *rsrc[WL::rec_loads];
 #pragma unroll
-        for (int j = 0; j < NMAT * G; ++j) dma16(csrc[j] + grp * G * 32, wb + (uint32_t)(j * 1024));
-        dma16(rsrc + grp * G * 8, wb + (uint32_t)WL::codes);
+    for (int j = 0; j < WL::rec_loads; ++j) {
+        constexpr int LPR = R / 2;  // lanes per row
+        const int f = (64 * j + lane) % WL::rec_lanes;
+        const int q = f / (32 * LPR), r = (f % (32 * LPR)) / LPR, part = f % LPR;
+        const moe::MatRows &m = q ? mat[1] : mat[0];
+        rsrc[j] = m.row0 + (size_t)(wrow0 + r) * m.stride + K / 2 + part * 16;
+    }
+    // code group grp into code buffer buf, record group grp into record buffer buf
+    auto issue_c = [&](int grp, int buf) {
+        const uint32_t wb = cring_lds + (uint32_t)(buf * 4 * WL::codes + wave * WL::codes);
+#pragma unroll
+        for (int j = 0; j < WL::code_loads; ++j) dma16(csrc[j] + grp * G * 32, wb + (uint32_t)(j * 1024));
+    };
+    auto issue_r = [&](int grp, int buf) {
+        const uint32_t wb = rring_lds + (uint32_t)(buf * 4 * WL::recs + wave * WL::recs);
+#pragma unroll
+        for (int j = 0; j < WL::rec_loads; ++j) dma16(rsrc[j] + grp * R * 8, wb + (uint32_t)(j * 1024));
     };
 
     // B-operand read offsets in a wave block: row rl = nt*16 + lr of matrix q,
@@ -323,8 +349,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         swz16[nt] = WL::swz(rl) * 16;
 #pragma unroll
         for (int q = 0; q < NMAT; ++q) {
-            cq[q][nt] = wave * WL::wave_bytes + q * 32 * WL::row_code + rl * WL::row_code + lq * 4;
-            rq[q][nt] = wave * WL::wave_bytes + WL::codes + q * 32 * G * 8 + rl * G * 8;
+            cq[q][nt] = wave * WL::codes + q * 32 * WL::row_code + rl * WL::row_code + lq * 4;
+            rq[q][nt] = wave * WL::recs + q * 32 * WL::row_rec + rl * WL::row_rec;
         }
     }
 
@@ -373,24 +399,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) acc[q][mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // One chunk (chunk cg of its group, weight buffer wb) of MT M tiles: every
-        // LDS read of the chunk is issued first (the B codes of both 32-column
-        // halves, their records as one 8-byte read per row, the A tiles), then each
-        // half is dequantised and multiplied.
-        auto compute = [&](const XStage &st, const uint8_t *wb, auto cg_const, auto mt_count) {
+        // One chunk (chunk cg of its code group in code buffer cb, chunk cr of its
+        // record group in record buffer rb) of MT M tiles: every LDS read of the
+        // chunk is issued first (the B codes of both 32-column halves, their
+        // records as one 8-byte read per row, the A tiles), then each half is
+        // dequantised and multiplied.
+        auto compute = [&](const XStage &st, const uint8_t *cb, auto cg_const, const uint8_t *rb, auto cr_const,
+                           auto mt_count) {
             constexpr int MT = decltype(mt_count)::value;
-            constexpr int cg = decltype(cg_const)::value;
+            constexpr int cg = decltype(cg_const)::value, cr = decltype(cr_const)::value;
             uint32_t codes[2][NMAT][2];
             uint64_t recs[NMAT][2];
 #pragma unroll
             for (int q = 0; q < NMAT; ++q)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    recs[q][nt] = *reinterpret_cast<const uint64_t *>(wb + rq[q][nt] + cg * 8);
+                    recs[q][nt] = *reinterpret_cast<const uint64_t *>(rb + rq[q][nt] + cr * 8);
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
                         codes[kb][q][nt] =
-                            *reinterpret_cast<const uint32_t *>(wb + cq[q][nt] + (((2 * cg + kb) * 16) ^ swz16[nt]));
+                            *reinterpret_cast<const uint32_t *>(cb + cq[q][nt] + (((2 * cg + kb) * 16) ^ swz16[nt]));
                 }
             uint4 av[2][MT];
 #pragma unroll
@@ -400,6 +428,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                     const int r = mt * 16 + lr;
                     av[kb][mt] = *reinterpret_cast<const uint4 *>(&st.x[r * kXRow + (((kb * 4 + lq) ^ (r & 7)) * 16)]);
                 }
+#if MOE_EXP_SCHED
+            // one B tile at a time: its dequantisation, then its MT products, so
+            // that the products of one tile run while the next is dequantised
+#pragma unroll
+            for (int kb = 0; kb < kKC / 32; ++kb)
+#pragma unroll
+                for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const bf16x8_t B = dequant8(codes[kb][q][nt], (uint32_t)(recs[q][nt] >> (32 * kb)), dq);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            acc[q][mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, av[kb][mt]), B, acc[q][mt][nt], 0, 0, 0);
+#if MOE_EXP_SCHED == 2
+                        __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+#endif
+                    }
+#else
 #pragma unroll
             for (int kb = 0; kb < kKC / 32; ++kb) {
                 bf16x8_t bo[NMAT][2];
@@ -419,30 +467,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bo[q][nt], acc[q][mt][nt], 0, 0, 0);
                 }
             }
+#endif
         };
 
         // Step c (at position b of the unrolled loop): wait until chunk c's
-        // activations and its group's weights have landed (exact vmcnt, from the
-        // fixed issue order), barrier, refill the stage freed by chunk c - 1 with
-        // chunk c + S - 1 and, at the start of a group, the weight buffer freed by
+        // activations, codes and records have landed (exact vmcnt, from the fixed
+        // issue order), barrier, refill the stage freed by chunk c - 1 with chunk
+        // c + S - 1 and, at the start of a code (record) group, the buffer freed by
         // the previous group with the next group, then multiply.  Past the last
         // chunk (group) a step re-loads the last one into a buffer that is not
         // read again, so every step issues a fixed number of loads.
         auto step = [&](int c, auto b_const, auto mt_count) {
             constexpr int b = decltype(b_const)::value;
             constexpr int P = (decltype(mt_count)::value + 1) / 2;  // activation loads of one stage
-            __builtin_amdgcn_s_waitcnt(kWaitVm(vm_allow(S, G, P, WL::loads, U, b)));
+            __builtin_amdgcn_s_waitcnt(
+                kWaitVm(vm_allow(S, P, G, WL::code_loads, R, WL::rec_loads, U, b)));
             ring_barrier();
             issue_x(stage_addr((b + S - 1) % S), min(c + S - 1, nchunks - 1), mt_count);
-            if (b % G == 0) issue_w(min(c / G + 1, ngroups - 1), (c / G + 1) & 1);
-            compute(ring[b % S], &wring[(c / G) & 1][0], IntC<b % G>{}, mt_count);
+            if (b % G == 0) issue_c(min(c / G + 1, ncgroups - 1), (c / G + 1) & 1);
+            if (b % R == 0) issue_r(min(c / R + 1, nrgroups - 1), (c / R + 1) & 1);
+            compute(ring[b % S], &cring[(c / G) & 1][0], IntC<b % G>{}, &rring[(c / R) & 1][0], IntC<b % R>{},
+                    mt_count);
         };
 
         // The K loop, specialised on the pass's M tile count so that the chunk
         // body has no branches, and unrolled by U so that every step names its
         // buffers with constants.
         auto k_loop = [&](auto mt_count) {
-            issue_w(0, 0);
+            issue_r(0, 0);
+            issue_c(0, 0);
 #pragma unroll
             for (int b = 0; b < S - 1; ++b) issue_x(stage_addr(b), min(b, nchunks - 1), mt_count);
             for (int c0 = 0; c0 < nchunks; c0 += U)
@@ -473,7 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int m = mt * 16 + lq * 4 + j;
-                    if (m >= mc || n >= R) continue;
+                    if (m >= mc || n >= nrows) continue;
                     const int row = s_dst[m];
                     if (GATEUP) {
                         const float gv = acc[0][mt][nt][j], uv = acc[1][mt][nt][j];
@@ -497,26 +550,32 @@ bool mfma_supported(const FfnArgs &a) { return a.grouped && a.H % 128 == 0 && a.
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-template <bool GATEUP, int S, int G, bool PAIR = false>
+template <bool GATEUP, int S, int G, int R, bool PAIR = false>
 int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     const int ntiles = GATEUP ? a.I / kNT : a.H / (PAIR ? 2 * kNT : kNT);
     const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, G, PAIR>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, G, R, PAIR>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a,
                        ntiles, n_groups);
     MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
 
-// Weight groups: 2 chunks (128 columns, 64 code bytes per row) with two
-// matrices per workgroup (gate/up, and the down projection when H is a multiple
-// of 256); with one matrix, 4 chunks (a 128-byte line of codes per row) when
-// the reduction length is a multiple of 256, else 2.
-int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true, kStagesGateUp, 2>(a, s); }
+// Two matrices per workgroup (gate/up, and the down projection when H is a
+// multiple of 256): code groups of 2 chunks (64 bytes per row), record groups
+// of 4 chunks (32 bytes per row) when the reduction length is a multiple of 256,
+// else 2.  One matrix: code and record groups of 4 chunks (a 128-byte line of
+// codes per row) when I is a multiple of 256, else 2.
+int mfma_gate_up(const FfnArgs &a, hipStream_t s) {
+    return a.H % 256 == 0 ? launch_mfma<true, kStagesGateUp, 2, kRecGroup>(a, s)
+                          : launch_mfma<true, kStagesGateUp, 2, 2>(a, s);
+}
 
 int mfma_down(const FfnArgs &a, hipStream_t s) {
-    if (a.H % (2 * kNT) == 0) return launch_mfma<false, kStagesDown, 2, true>(a, s);
-    return a.I % 256 == 0 ? launch_mfma<false, kStagesDown, 4>(a, s) : launch_mfma<false, kStagesDown, 2>(a, s);
+    if (a.H % (2 * kNT) == 0)
+        return a.I % 256 == 0 ? launch_mfma<false, kStagesDown, 2, kRecGroup, true>(a, s)
+                              : launch_mfma<false, kStagesDown, 2, 2, true>(a, s);
+    return a.I % 256 == 0 ? launch_mfma<false, kStagesDown, 4, 4>(a, s) : launch_mfma<false, kStagesDown, 2, 2>(a, s);
 }
 
 }  // namespace moe
