@@ -1,9 +1,11 @@
 """Summarise a rocprofv3 result database (rocpd SQLite) as plain text.
 
-  python -m routed_expert_streaming_amd.rocprof_summary RESULTS.db [--counters | --timeline | --copies]
+  python -m routed_expert_streaming_amd.rocprof_summary RESULTS.db [--by-grid | --counters | --timeline | --copies]
 
 Prints one line per kernel: dispatches, average / min / max duration, share of
-GPU time, grid, workgroup size and VGPRs; with --counters, the average of every
+GPU time, grid, workgroup size and VGPRs (with --by-grid, one line per kernel
+and grid size, which tells launches of one kernel on different shapes apart);
+with --counters, the average of every
 PMC counter per kernel (as collected by ``rocprofv3 --pmc ...``); with
 --timeline, per kernel the average duration and the average idle gap between
 the end of the previous dispatch and its start (over the last two thirds of the
@@ -29,7 +31,7 @@ def short_name(name: str) -> str:
     return (m.group(1) if m else s)[:90]
 
 
-def kernel_stats(db: str):
+def kernel_stats(db: str, by_grid: bool = False):
     c = sqlite3.connect(db)
     rows = c.execute("select name, duration, grid_x, grid_y, grid_z, workgroup_x, vgpr_count, lds_size "
                      "from kernels").fetchall()
@@ -37,6 +39,8 @@ def kernel_stats(db: str):
     meta = {}
     for name, dur, gx, gy, gz, wx, vgpr, lds in rows:
         k = short_name(name)
+        if by_grid:
+            k = f"{k[:70]} [{gx * gy * gz}]"
         agg[k].append(dur)
         meta[k] = (gx * gy * gz, wx, vgpr, lds)
     total = sum(sum(v) for v in agg.values()) or 1
@@ -111,6 +115,7 @@ def events(db: str, n: int, at: int, anchor: str = "router_partial_kernel"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("db")
+    ap.add_argument("--by-grid", action="store_true")
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--timeline", action="store_true")
     ap.add_argument("--copies", action="store_true")
@@ -139,7 +144,7 @@ def main():
         return
     print(f"{'kernel':90s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s} "
           f"{'threads':>8s} {'wg':>4s} {'vgpr':>4s} {'lds':>6s}")
-    for k, n, avg, mn, mx, pct, g, w, v, l in kernel_stats(args.db):
+    for k, n, avg, mn, mx, pct, g, w, v, l in kernel_stats(args.db, args.by_grid):
         print(f"{k:90s} {n:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f} {pct:6.2f} {g:8d} {w:4d} {v:4d} {l:6d}")
 
 
