@@ -58,6 +58,9 @@ def parse():
                          "the machine lets one process pin)")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
+    ap.add_argument("--chain-steps", type=int, default=128,
+                    help="timed steps of each chained-layer run of the streamed leg (0 skips them)")
+    ap.add_argument("--chain-warmup", type=int, default=32)
     ap.add_argument("--no-layer-legs", action="store_true",
                     help="skip the one-resident-layer measurements of the 32-token decode and 2048-token prefill shapes")
     ap.add_argument("--traffic-calibration", action="store_true",
@@ -150,6 +153,7 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     h1, m1, b1 = st.stats()
+    chained = chained_runs(torch, st, args, xs) if args.chain_steps > 0 else None
     st.close()
     hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
     ms_step = wall / args.stream_steps * 1e3
@@ -167,7 +171,72 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
            "overlap_frac": (round((copy_ms + resident_ms_per_step - ms_step) / min(copy_ms, resident_ms_per_step), 4)
                             if copy_ms > 0 and resident_ms_per_step > 0 else None),
            "steps": args.stream_steps, "warmup": args.stream_warmup}
+    if chained:
+        res["chained"] = chained
     log(f"streaming: {res}")
+    return res
+
+
+def chained_runs(torch, st, args, xs):
+    """The streamed workload with chained layers (layer l+1's input computed from
+    layer l's output through a residual stream), so each layer is routed only
+    when the one before it is done: without lookahead every miss is exposed;
+    with lookahead the next layer's router is applied to the current layer's
+    input and the experts it ranks highest are prefetched (gating lookahead);
+    the bound is an exact predictor of the same routing."""
+    cfg = st.cfg
+    resid, hs = st.chain_buffers()
+    out = st.new_output()
+    n_in = len(xs)
+    res = {"model": "pre-norm residual stream between layers (moe_residual_norm, eps 1e-6)",
+           "steps": args.chain_steps, "warmup": args.chain_warmup}
+    k = cfg.top_k
+    for name, la in [("no_lookahead", 0)] + [(f"lookahead_{m}", m) for m in sorted({1, 2, k // 2, k}) if 0 < m <= k]:
+        st.reset_cache()
+        for s in range(args.chain_warmup):
+            st.forward_chained(xs[s % n_in][0], hs, resid, out, lookahead=la)
+        torch.cuda.synchronize()
+        h0, m0, b0 = st.stats()
+        tot = None
+        t0 = time.perf_counter()
+        for s in range(args.chain_steps):
+            c = st.forward_chained(xs[s % n_in][0], hs, resid, out, lookahead=la)
+            tot = c if tot is None else type(c)(*[a + b for a, b in zip(vars(tot).values(), vars(c).values())])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        h1, m1, b1 = st.stats()
+        n = args.chain_steps
+        r = {"tokens_per_s": round(n * cfg.tokens / wall, 2), "ms_per_step": round(wall / n * 1e3, 3),
+             "hit_rate": round((h1 - h0) / max(h1 - h0 + m1 - m0, 1), 4), "h2d_bytes_per_step": (b1 - b0) // n,
+             "exposed_copies_per_step": round(tot.copies / n, 3)}
+        if la:
+            r.update({"named_recall": round(tot.predicted / max(tot.routed, 1), 4),
+                      "ahead_copies_per_step": round(tot.ahead_copies / n, 3),
+                      "ahead_unused_per_step": round(tot.ahead_unused / n, 3)})
+        res[name] = r
+        log(f"chained, {name}: {r}")
+    # exact-predictor bound on the same routing: the chained layer inputs of
+    # every step input, recorded, then run with every layer routed up front
+    rec = []
+    for s in range(n_in):
+        st.forward_chained(xs[s][0], hs, resid, out, lookahead=0)
+        rec.append(hs.clone())
+    st.reset_cache()
+    for s in range(args.chain_warmup):
+        st.forward(rec[s % n_in], out)
+    torch.cuda.synchronize()
+    h0, m0, b0 = st.stats()
+    t0 = time.perf_counter()
+    for s in range(args.chain_steps):
+        st.forward(rec[s % n_in], out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    h1, m1, b1 = st.stats()
+    n = args.chain_steps
+    res["exact_predictor"] = {"tokens_per_s": round(n * cfg.tokens / wall, 2), "ms_per_step": round(wall / n * 1e3, 3),
+                              "hit_rate": round((h1 - h0) / max(h1 - h0 + m1 - m0, 1), 4),
+                              "h2d_bytes_per_step": (b1 - b0) // n}
+    log(f"chained, exact predictor: {res['exact_predictor']}")
     return res
 
 

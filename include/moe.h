@@ -261,6 +261,22 @@ int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w
                           int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
                           float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------ chained layers
+ * Residual stream between chained layers (LayerStoRm README, "Status and
+ * limitations": predictive expert prefetching; "References": gating lookahead
+ * behind the expert prefetch predictor; both need layer l+1's input to depend
+ * on layer l's output).  The pages name no block around the MoE layers; this is
+ * the plainest pre-norm residual step with the attention half left out and no
+ * learned norm weight, per token row t:
+ *   resid[t,:] += float(add[t,:])                    (skipped when add is NULL)
+ *   x_next[t,:] = bf16_rne( resid[t,:] / sqrt(mean(resid[t,:]^2) + eps) )
+ * add [T,H] bf16 (a layer's combined output) or NULL; resid [T,H] fp32, updated
+ * in place; x_next [T,H] bf16, the next layer's input (must not alias add).  The
+ * sum of squares is fp32 in a fixed order (reproducible run to run).  All device
+ * pointers, caller-owned.  MOE_E_ARG for T < 0, H <= 0, eps outside [0, 1] or a
+ * NULL resid / x_next (T = 0 is a no-op). */
+int moe_residual_norm(const uint16_t *add, float *resid, int T, int H, float eps, uint16_t *x_next, void *stream);
+
 /* ------------------------------------------------------------------ debug
  * Dequantise matrix `which` (0 = W1, 1 = W3, 2 = W2) of a device slab into out
  * (fp32, row-major [rows x cols]); exact, for round-trip tests of the format. */

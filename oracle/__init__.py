@@ -15,6 +15,9 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
   expert FFN     -- constant-code experts give a closed form for y
   combine        -- zero routed experts leave the shared expert; k=1 gives y;
                     expert relabelling leaves the output unchanged
+  residual norm  -- a constant row normalises to +-1; a row that is sqrt(H) times
+                    a unit vector is returned unchanged; positive scaling leaves
+                    the output unchanged; the fp32 update equals numpy's fp32 add
 The end-to-end values on random inputs have no printed worked example to pin
 them; they rest on the pins above.
 """
@@ -62,6 +65,7 @@ def lib():
         L.oracle_router.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, i32]
         L.oracle_moe_layer.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, i64, i32,
                                        vp, vp, vp, vp]
+        L.oracle_residual_norm.argtypes = [vp, vp, i64, i64, ctypes.c_double, vp]
         _lib = L
     return _lib
 
@@ -154,3 +158,17 @@ def moe_layer(x_bf16: np.ndarray, Wr: np.ndarray, bias, k: int, slabs, shared, I
                            None if shared is None else _p(shared), _p(r), nr, threads,
                            _p(idx), _p(w), _p(out64), _p(outb))
     return {"idx": idx, "w": w, "out64": out64, "out_bf16": outb}
+
+
+def residual_norm(add, resid: np.ndarray, eps: float):
+    """Residual update and RMS normalisation of chained layers (see oracle.c).
+
+    add: [T,H] bf16 bits (uint16) or None; resid: [T,H] float32, updated in place.
+    Returns x_next [T,H] bf16 bits.
+    """
+    assert resid.dtype == np.float32 and resid.flags["C_CONTIGUOUS"]
+    T, H = resid.shape
+    a = None if add is None else np.ascontiguousarray(add, dtype=np.uint16)
+    out = np.empty((T, H), np.uint16)
+    lib().oracle_residual_norm(_p(a), _p(resid), T, H, ctypes.c_double(eps), _p(out))
+    return out

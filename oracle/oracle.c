@@ -254,3 +254,24 @@ void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_
     }
     free(y);
 }
+
+/* ---------------- residual stream between chained layers ----------------
+ * The pages describe no block around the MoE layers; when layers are chained
+ * (layer l+1's input depends on layer l's output, which predictive expert
+ * prefetching needs: LayerStoRm README, "Status and limitations" and
+ * "References", gating lookahead) the plainest pre-norm residual step stands in
+ * for the rest of the block, per token row:
+ *   resid += add            (fp32 values; the sum taken exactly, rounded once to fp32)
+ *   x_next = bf16( resid / sqrt(mean(resid^2) + eps) )   in fp64, rounded once
+ * add may be NULL (resid unchanged). */
+void oracle_residual_norm(const uint16_t *add, float *resid, int64_t T, int64_t H, double eps, uint16_t *x_next) {
+    for (int64_t t = 0; t < T; ++t) {
+        float *r = resid + t * H;
+        if (add)
+            for (int64_t h = 0; h < H; ++h) r[h] = (float)((double)r[h] + oracle_bf16_to_double(add[t * H + h]));
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; ++h) ss += (double)r[h] * (double)r[h];
+        const double den = sqrt(ss / (double)H + eps);
+        for (int64_t h = 0; h < H; ++h) x_next[t * H + h] = oracle_double_to_bf16((double)r[h] / den);
+    }
+}

@@ -78,6 +78,7 @@ def lib():
             "moe_route_ffn_combine_workspace_bytes": ([i, i, i, i, i, i], sz),
             "moe_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp], i),
             "moe_combine": ([vp, vp, i, i, i, i, vp, vp], i),
+            "moe_residual_norm": ([vp, vp, i, i, ctypes.c_float, vp, vp], i),
             "moe_debug_dequant": ([vp, i, i, i, vp, vp], i),
         }
         for name, (args, res) in sig.items():
@@ -301,6 +302,11 @@ def moe_route_ffn_combine(x, T, H, I, w_router, bias, E, k, expert_table, shared
 def moe_combine(y, topk_w, T, k, H, has_shared, out, stream=None):
     _check(lib().moe_combine(_ptr(y), _ptr(topk_w), T, k, H, int(bool(has_shared)), _ptr(out), _stream(stream)),
            "moe_combine")
+
+
+def moe_residual_norm(add, resid, T, H, eps, x_next, stream=None):
+    _check(lib().moe_residual_norm(_ptr(add) if add is not None else None, _ptr(resid), T, H, float(eps),
+                                   _ptr(x_next), _stream(stream)), "moe_residual_norm")
 
 
 def moe_debug_dequant(slab, H, I, which, out, stream=None):

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "router.hip", "ffn_gemv.hip", "ffn_decode.hip", "ffn_mfma.hip", "ffn_entry.hip", "cache.hip"]
+SOURCES = ["abi.cpp", "router.hip", "ffn_gemv.hip", "ffn_decode.hip", "ffn_mfma.hip", "ffn_entry.hip", "cache.hip", "residual.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", f"--offload-arch={ARCH}",

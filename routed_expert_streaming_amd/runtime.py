@@ -12,7 +12,13 @@ kernels; this module only allocates, fills inputs and orders the calls:
                         expert_ffn + combine(l)
                         release(l) -> slots may be overwritten after this point
 
-The routing of every layer is known at the start of a step because each
+Chained steps (forward_chained): layer l+1's input is computed from layer l's
+output (a residual stream, moe_residual_norm), so each layer is routed only when
+the one before it is done; optionally the next layer's experts are predicted by
+applying its router to the current layer's input and prefetched (gating
+lookahead).
+
+In forward, the routing of every layer is known at the start of a step because each
 (step, layer) gets its own synthetic hidden states; the copies of later layers
 therefore overlap the FFN of earlier ones (LayerStoRm README "TL;DR": streaming
 is overlapped with compute).  When a layer needs more distinct experts than it has
@@ -68,6 +74,19 @@ def _bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
 class StepStats:
     waves: int = 0
     copies: int = 0
+
+
+@dataclass
+class ChainStats:
+    """Expert copies of one chained step (see MoEStack.forward_chained)."""
+    copies: int = 0        # streamed for the layers' own routing (exposed: the layer waits for them)
+    ahead_copies: int = 0  # streamed ahead from the predictions (overlap the layer before)
+    ahead_unused: int = 0  # of those, experts the layer's own routing did not select
+    routed: int = 0        # distinct routed experts of the predicted layers (1 .. L-1)
+    predicted: int = 0     # of those, experts the prediction had named
+
+
+RMS_EPS = 1e-6  # eps of the residual stream's RMS normalisation between chained layers
 
 
 class MoEStack:
@@ -158,7 +177,9 @@ class MoEStack:
         half = max(1, self.C // 2)
         self.max_waves = (E + half - 1) // half + 1
         self.masks = torch.zeros((Lyr, self.max_waves, E), dtype=torch.uint8, device=self.dev)
-        self._idx_host = PinnedHost(Lyr * T * k * 4) if self.streaming else None
+        self.pidx = torch.empty((Lyr, T, k), dtype=torch.int32, device=self.dev)  # predicted experts
+        self.pw = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
+        self._idx_host = PinnedHost(max(Lyr, 2) * T * k * 4) if self.streaming else None
         self._mask_host = PinnedHost(Lyr * self.max_waves * E) if self.streaming else None
         torch.cuda.synchronize(self.dev)
 
@@ -183,6 +204,11 @@ class MoEStack:
     def route(self, x: torch.Tensor, l: int):
         L.moe_router_topk(x[l], self.T, self.H, self.wr[l], None if self.bias is None else self.bias[l], self.E,
                           self.k, self.idx[l], self.w[l], self.router_ws, self.router_ws_bytes, self.stream)
+
+    def route_with(self, x_l: torch.Tensor, l: int, idx: torch.Tensor, w: torch.Tensor):
+        """Router of layer l applied to the hidden states x_l [T,H] (any layer's)."""
+        L.moe_router_topk(x_l, self.T, self.H, self.wr[l], None if self.bias is None else self.bias[l], self.E,
+                          self.k, idx, w, self.router_ws, self.router_ws_bytes, self.stream)
 
     def route_all(self, x: torch.Tensor):
         """Routers of every layer in one call."""
@@ -284,6 +310,70 @@ class MoEStack:
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
             self.combine(l, out)
+        return st
+
+    # ------------------------------------------------------------------ chained layers
+    def chain_buffers(self):
+        """Device buffers of a chained step: the residual stream [T,H] fp32 and
+        the layer inputs [L,T,H] bf16."""
+        resid = torch.empty((self.T, self.H), dtype=torch.float32, device=self.dev)
+        xs = torch.empty((self.L, self.T, self.H), dtype=torch.bfloat16, device=self.dev)
+        return resid, xs
+
+    def forward_chained(self, h0: torch.Tensor, xs: torch.Tensor, resid: torch.Tensor, out: torch.Tensor,
+                        lookahead: int = 0) -> ChainStats:
+        """One step with chained layers: h0 [T,H] bf16 starts the residual stream,
+        layer l's input xs[l] is the stream RMS-normalised after every earlier
+        layer's output was added (moe_residual_norm), out[l] is layer l's output.
+
+        Streamed, a layer's routing is known only when the layer before it is
+        done, so the copies for its own routing are exposed.  With lookahead = m
+        > 0, layer l+1's router is also applied to layer l's input (gating
+        lookahead) and, per token, the m experts it ranks highest are prefetched
+        while layer l computes (m = k: every predicted expert); they stay held
+        until layer l+1 has run.  Needs T*(k+m) <= C: a layer's own experts fit
+        beside the predicted ones."""
+        st = ChainStats()
+        T, H, k = self.T, self.H, self.k
+        resid.zero_()
+        L.moe_residual_norm(h0, resid, T, H, RMS_EPS, xs[0], self.stream)
+        m = max(0, min(int(lookahead), k))
+        if self.streaming and T * (k + m) > self.C:
+            raise ValueError(f"chained streaming needs {T * (k + m)} <= {self.C} slots")
+        pred = {}  # layer -> (predicted set, set copied ahead)
+        for l in range(self.L):
+            if not self.streaming:
+                self.route_ffn_combine(xs, l, out)
+            else:
+                ahead = m > 0 and l + 1 < self.L
+                self.route(xs, l)
+                if ahead:
+                    self.route_with(xs[l], l + 1, self.pidx[l + 1], self.pw[l + 1])
+                # one small D2H of the ids and a host wait per layer, then the host plans
+                hv = np.frombuffer(self._idx_host.array, dtype=np.int32, count=2 * T * k)
+                torch.from_numpy(hv[:T * k]).copy_(self.idx[l].view(-1), non_blocking=True)
+                if ahead:
+                    torch.from_numpy(hv[T * k:]).copy_(self.pidx[l + 1].view(-1), non_blocking=True)
+                self.stream.synchronize()
+                needed = sorted(set(hv[:T * k].tolist()))
+                st.copies += L.moe_cache_prefetch_async(self.cache, l, needed)
+                if l in pred:
+                    named, copied = pred.pop(l)
+                    st.routed += len(needed)
+                    st.predicted += len(named.intersection(needed))
+                    st.ahead_unused += len(copied.difference(needed))
+                if ahead:
+                    # the predicted ids come per token in order of descending logit
+                    nxt = sorted(set(hv[T * k:].reshape(T, k)[:, :m].ravel().tolist()))
+                    slots, _ = L.moe_cache_lookup(self.cache, l + 1, nxt)
+                    copied = {e for e, s in zip(nxt, slots) if s < 0}
+                    st.ahead_copies += L.moe_cache_prefetch_async(self.cache, l + 1, nxt)
+                    pred[l + 1] = (set(nxt), copied)
+                L.moe_cache_wait(self.cache, l, self.stream)
+                self.ffn_combine(xs, l, out)
+                L.moe_cache_release(self.cache, l, self.stream)
+            if l + 1 < self.L:
+                L.moe_residual_norm(out[l], resid, T, H, RMS_EPS, xs[l + 1], self.stream)
         return st
 
     def stats(self):

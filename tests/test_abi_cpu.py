@@ -301,3 +301,13 @@ def test_route_ffn_combine_validation():
     bad = list(args); bad[14] = ws - 1
     assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_NOMEM
     L.moe_route_ffn_combine(None, 0, 256, 128, None, None, 16, 2, None, None, None, None, None, None, 0)
+
+
+def test_residual_norm_validation():
+    assert _status(L.moe_residual_norm, FAKE, FAKE, -1, 256, 1e-6, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_residual_norm, FAKE, FAKE, 4, 0, 1e-6, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_residual_norm, FAKE, FAKE, 4, 256, -1.0, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_residual_norm, FAKE, FAKE, 4, 256, float("nan"), FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_residual_norm, FAKE, None, 4, 256, 1e-6, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_residual_norm, None, FAKE, 4, 256, 1e-6, None) == L.MOE_E_ARG
+    L.moe_residual_norm(None, None, 0, 256, 1e-6, None)  # no rows: nothing to do

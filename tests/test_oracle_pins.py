@@ -345,3 +345,48 @@ def test_generator_params_are_scale_and_minus_eight_scale():
         mn = rec[:, 1].view(np.float16).astype(np.float64)
         assert np.all(np.isfinite(sc)) and np.all(sc >= 0) and np.array_equal(mn, -8 * sc)
         assert 0.012 < np.sqrt(np.mean(sc ** 2)) < 0.028
+
+
+# ---------------------------------------------------------------- residual stream of chained layers
+def test_residual_norm_closed_forms():
+    H = 64
+    bf = lambda v: oracle.double_to_bf16(v)
+    # a constant row c normalises to sign(c) (eps small against c^2); rows of
+    # different magnitudes in one call, so each row must use its own mean square
+    cs = (3.0, -0.25, 1024.0, -7.5)
+    r = np.array([np.full(H, c) for c in cs], np.float32)
+    x = oracle.residual_norm(None, r, 1e-6)
+    for t, c in enumerate(cs):
+        assert (x[t] == bf(math.copysign(1.0, c))).all(), c
+    # sqrt(H) * e_j has mean square 1, so it comes back unchanged (one row per j)
+    r = np.zeros((3, H), np.float32)
+    for t, j in enumerate((0, 17, 63)):
+        r[t, j] = 8.0 * (-1) ** t
+    x = oracle.residual_norm(None, r, 0.0)
+    for t, j in enumerate((0, 17, 63)):
+        want = np.zeros(H, np.uint16)
+        want[j] = bf(8.0 * (-1) ** t)
+        assert (x[t] == want).all()
+    # eps inside the square root: a constant row with c^2 = eps gives 1/sqrt(2)
+    r = np.full((1, H), 1e-3, np.float32)
+    eps = float(np.float32(1e-3)) ** 2
+    x = oracle.residual_norm(None, r, eps)
+    assert (x == bf(1.0 / math.sqrt(2.0))).all()
+    # the input row is left as it is when nothing is added
+    assert (r == np.float32(1e-3)).all()
+
+
+def test_residual_norm_scale_invariance_and_fp32_update():
+    rng = np.random.default_rng(7)
+    T, H = 4, 96
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    base = oracle.residual_norm(None, r.copy(), 0.0)
+    for m in (-6, 3, 20):  # power-of-two scalings are exact in fp32
+        assert (oracle.residual_norm(None, r * np.float32(2.0 ** m), 0.0) == base).all(), m
+    # the update is the fp32 sum of the residual and the bf16 output
+    add = np.array([[oracle.double_to_bf16(float(v)) for v in row] for row in rng.standard_normal((T, H)) * 30.0],
+                   np.uint16)
+    upd = r.copy()
+    oracle.residual_norm(add, upd, 1e-6)
+    add_f = np.array([[oracle.bf16_to_double(int(b)) for b in row] for row in add], np.float32)
+    assert (upd == r + add_f).all()
