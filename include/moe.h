@@ -159,6 +159,15 @@ int moe_cache_prefetch_async(moe_cache *cache, int layer, const int32_t *experts
    far, then enqueues the layer's pending table writes on it.  A no-op when
    nothing is pending.  Call it before the kernels that read the layer's table. */
 int moe_cache_wait(moe_cache *cache, int layer, void *compute_stream);
+/* Splits every later slab copy into two halves, the second on
+   second_copy_stream (caller-owned, default priority, same device), so that two
+   DMA engines share the PCIe link: back-to-back slab-sized copies on one stream
+   reach ~4% less than one large copy, two streams reach it.  The readiness and
+   release ordering of moe_cache_prefetch_async / moe_cache_wait /
+   moe_cache_release covers both streams.  NULL returns to one stream.
+   MOE_E_STATE while a layer has copies no moe_cache_wait has covered.  A no-op
+   on a recording cache. */
+int moe_cache_split_copies(moe_cache *cache, void *second_copy_stream);
 /* moe_cache_prefetch_async followed by moe_cache_wait. */
 int moe_cache_prefetch(moe_cache *cache, int layer, const int32_t *experts_host, int n,
                        void *compute_stream, int *n_copies);

@@ -66,6 +66,7 @@ def lib():
             "moe_cache_prefetch": ([vp, i, vp, i, vp, ctypes.POINTER(i)], i),
             "moe_cache_prefetch_async": ([vp, i, vp, i, ctypes.POINTER(i)], i),
             "moe_cache_wait": ([vp, i, vp], i),
+            "moe_cache_split_copies": ([vp, vp], i),
             "moe_cache_release": ([vp, i, vp], i),
             "moe_cache_stats": ([vp, u64p, u64p, u64p], i),
             "moe_cache_reset": ([vp], i),
@@ -231,6 +232,10 @@ def moe_cache_prefetch_async(cache: int, layer: int, experts) -> int:
     _check(lib().moe_cache_prefetch_async(cache, layer, arr, len(experts), ctypes.byref(n)),
            "moe_cache_prefetch_async")
     return n.value
+
+
+def moe_cache_split_copies(cache, second_copy_stream=None):
+    _check(lib().moe_cache_split_copies(cache, _stream(second_copy_stream)), "moe_cache_split_copies")
 
 
 def moe_cache_wait(cache: int, layer: int, compute_stream=None):

@@ -94,10 +94,12 @@ class MoEStack:
 
     cap: fraction of experts per layer held in HBM (None = the configuration's).
     layers: number of layers to build (None = the configuration's).
+    split_copies: streamed stacks copy each slab in two halves on two copy
+    streams (moe_cache_split_copies).
     """
 
     def __init__(self, cfg: synth.Config, *, layers: int | None = None, cap: float | None = None,
-                 device: int = 0, threads: int = 0, path: int = L.MOE_FFN_AUTO):
+                 device: int = 0, threads: int = 0, path: int = L.MOE_FFN_AUTO, split_copies: bool = True):
         L.lib()
         self.cfg = cfg
         self.L = layers or cfg.layers
@@ -110,6 +112,7 @@ class MoEStack:
         self.dev = torch.device("cuda", device)
         torch.cuda.set_device(self.dev)
         self.copy_stream = torch.cuda.Stream(self.dev)  # default priority
+        self.copy_stream2 = torch.cuda.Stream(self.dev) if split_copies else None
         self.slab = L.moe_expert_bytes(self.H, self.I)
         assert self.slab == synth.slab_bytes(self.H, self.I)
         Lyr, T, H, I, E, k = self.L, self.T, self.H, self.I, self.E, self.k
@@ -163,6 +166,8 @@ class MoEStack:
             torch.cuda.synchronize(self.dev)
             self.cache = L.moe_cache_create(desc, ctypes.addressof(self._host_ptrs), self.pool, self.table,
                                             self.copy_stream)
+            if self.copy_stream2 is not None:
+                L.moe_cache_split_copies(self.cache, self.copy_stream2)
         # workspaces and outputs
         self.router_ws_bytes = L.moe_router_layers_workspace_bytes(Lyr, T, E)
         self.router_ws = torch.zeros(self.router_ws_bytes, dtype=torch.uint8, device=self.dev)

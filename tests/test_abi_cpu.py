@@ -311,3 +311,17 @@ def test_residual_norm_validation():
     assert _status(L.moe_residual_norm, FAKE, None, 4, 256, 1e-6, FAKE) == L.MOE_E_ARG
     assert _status(L.moe_residual_norm, None, FAKE, 4, 256, 1e-6, None) == L.MOE_E_ARG
     L.moe_residual_norm(None, None, 0, 256, 1e-6, None)  # no rows: nothing to do
+
+
+def test_split_copies_validation_and_state():
+    assert _status(L.moe_cache_split_copies, None, FAKE) == L.MOE_E_ARG
+    desc = L.moe_cache_desc(2, 8, 256, 128, 4)
+    c = L.moe_cache_create_recording(desc, 0x10000)
+    try:
+        L.moe_cache_split_copies(c, FAKE)  # a recording cache ignores the stream
+        L.moe_cache_prefetch_async(c, 0, [1, 2])
+        assert _status(L.moe_cache_split_copies, c, None) == L.MOE_E_STATE  # layer 0 not waited for
+        L.moe_cache_wait(c, 0)
+        L.moe_cache_split_copies(c, None)
+    finally:
+        L.moe_cache_destroy(c)
