@@ -176,7 +176,9 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     h1, m1, b1 = st.stats()
-    chained = chained_runs(torch, st, args, xs) if args.chain_steps > 0 else None
+    # chained layers with the deepest lookahead need 2*T*k slots per layer
+    chained = (chained_runs(torch, st, args, xs)
+               if args.chain_steps > 0 and 2 * cfg.tokens * cfg.top_k <= st.C else None)
     st.close()
     hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
     ms_step = wall / args.stream_steps * 1e3
