@@ -6,6 +6,7 @@ Bars: expert indices bit-exact; gate weights within 1e-6; outputs within
 max|err| <= 2e-2 * max|ref| per (step, layer) tensor (bf16 activations, fp32
 accumulation); dequantisation exact.
 """
+import ctypes
 import zlib
 
 import numpy as np
@@ -467,3 +468,48 @@ def test_streaming_equals_resident_and_lru_replay(name, layers, steps):
         sel = slice(None) if rows is None else rows
         check_close(out_r[0][l][sel], ref[l]["out64"][sel], f"{name} layer {l}")
     resident.close()
+
+
+def test_empty_inputs_are_no_ops():
+    """Zero tokens (and an empty cache request): every call succeeds, the outputs
+    keep their sentinel contents, and the permutation of no pairs is all zero."""
+    T1, H, I, E, k = 1, 256, 128, 16, 2
+    x = torch.zeros((T1, H), dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros((E, H), dtype=torch.float32, device="cuda")
+    slab = torch.zeros(L.moe_expert_bytes(H, I), dtype=torch.uint8, device="cuda")
+    table = torch.full((E,), slab.data_ptr(), dtype=torch.int64, device="cuda")
+    idx = torch.full((T1, k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((T1, k), -3.0, dtype=torch.float32, device="cuda")
+    out = torch.full((T1, H), 5.0, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((T1 * k + T1, H), 9.0, dtype=torch.float32, device="cuda")
+    nb = L.moe_route_ffn_combine_workspace_bytes(T1, H, I, E, k, True)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    L.moe_router_topk(x, 0, H, wr, None, E, k, idx, w, ws, nb)
+    L.moe_expert_ffn(x, 0, H, I, E, idx, k, table, slab, None, y, ws, nb)
+    L.moe_expert_ffn_combine(x, 0, H, I, E, idx, w, k, table, slab, out, ws, nb)
+    L.moe_route_ffn_combine(x, 0, H, I, wr, None, E, k, table, slab, idx, w, out, ws, nb)
+    L.moe_combine(y, w, 0, k, H, True, out)
+    resid = torch.full((T1, H), 2.0, dtype=torch.float32, device="cuda")
+    L.moe_residual_norm(out, resid, 0, H, 1e-6, x)
+    count = torch.full((E,), 11, dtype=torch.int32, device="cuda")
+    offset = torch.full((E + 1,), 11, dtype=torch.int32, device="cuda")
+    L.moe_permute(idx, 0, k, E, count, offset, None)
+    torch.cuda.synchronize()
+    assert (idx == -7).all() and (w == -3.0).all()
+    assert (out == 5.0).all() and (y == 9.0).all() and (resid == 2.0).all() and (x == 0).all()
+    assert (count == 0).all() and (offset == 0).all()
+    # an empty cache request copies nothing and holds nothing
+    desc = L.moe_cache_desc(1, E, H, I, 4)
+    host_slab = torch.zeros(L.moe_expert_bytes(H, I), dtype=torch.uint8, pin_memory=True)
+    ptrs = (ctypes.c_void_p * E)(*([host_slab.data_ptr()] * E))
+    pool = torch.zeros((4, L.moe_expert_bytes(H, I)), dtype=torch.uint8, device="cuda")
+    tab = torch.zeros((1, E), dtype=torch.int64, device="cuda")
+    cs = torch.cuda.Stream()
+    c = L.moe_cache_create(desc, ctypes.addressof(ptrs), pool, tab, cs)
+    try:
+        assert L.moe_cache_prefetch(c, 0, [], torch.cuda.current_stream()) == 0
+        L.moe_cache_release(c, 0, torch.cuda.current_stream())
+        assert L.moe_cache_stats(c) == (0, 0, 0)
+    finally:
+        torch.cuda.synchronize()
+        L.moe_cache_destroy(c)
