@@ -264,11 +264,21 @@ int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const 
  * instead of a kernel of its own: three launches per layer.  Every routed
  * expert must be resident.  Arguments as in the two calls; topk_idx [T,k] and
  * topk_w [T,k] are outputs.  workspace: moe_route_ffn_combine_workspace_bytes
- * (contents don't care; calls sharing it must not overlap in time). */
+ * (contents don't care; calls sharing it must not overlap in time).
+ * prefetch / prefetch_bytes: an optional hint, device bytes that the caller's
+ * next call reads cold (e.g. the next layer's router weights, which do not
+ * depend on that layer's input); for one token the down kernel reads them
+ * alongside its first weight loads and discards them, so the next call finds
+ * them in the device caches: 16 KB unit u is read on XCD u % 8, where the
+ * router kernel's workgroup u (one expert's 16 KB of weights when H = 4096)
+ * runs; as much of the hint as the kernel has waves for (1 KB per wave).
+ * Results do not depend on it.  NULL and 0 for
+ * none; MOE_E_ARG for a NULL pointer with a non-zero size. */
 size_t moe_route_ffn_combine_workspace_bytes(int T, int H, int I, int E, int k, int has_shared);
 int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias, int E,
                           int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
-                          float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+                          float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes,
+                          const void *prefetch, size_t prefetch_bytes, void *stream);
 
 /* ------------------------------------------------------------------ chained layers
  * Residual stream between chained layers (LayerStoRm README, "Status and

@@ -77,7 +77,7 @@ def lib():
             "moe_expert_down": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, vp], i),
             "moe_expert_ffn_combine": ([vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, i, vp], i),
             "moe_route_ffn_combine_workspace_bytes": ([i, i, i, i, i, i], sz),
-            "moe_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp], i),
+            "moe_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp], i),
             "moe_combine": ([vp, vp, i, i, i, i, vp, vp], i),
             "moe_residual_norm": ([vp, vp, i, i, ctypes.c_float, vp, vp], i),
             "moe_debug_dequant": ([vp, i, i, i, vp, vp], i),
@@ -298,10 +298,11 @@ def moe_route_ffn_combine_workspace_bytes(T, H, I, E, k, has_shared) -> int:
 
 
 def moe_route_ffn_combine(x, T, H, I, w_router, bias, E, k, expert_table, shared_slab, topk_idx, topk_w, out,
-                          workspace, workspace_bytes, stream=None):
+                          workspace, workspace_bytes, stream=None, prefetch=None, prefetch_bytes=0):
     _check(lib().moe_route_ffn_combine(_ptr(x), T, H, I, _ptr(w_router), _ptr(bias), E, k, _ptr(expert_table),
                                        _ptr(shared_slab), _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(workspace),
-                                       workspace_bytes, _stream(stream)), "moe_route_ffn_combine")
+                                       workspace_bytes, _ptr(prefetch), prefetch_bytes, _stream(stream)),
+           "moe_route_ffn_combine")
 
 
 def moe_combine(y, topk_w, T, k, H, has_shared, out, stream=None):

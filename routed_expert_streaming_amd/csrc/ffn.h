@@ -21,6 +21,8 @@ struct FfnArgs {
     const uint8_t **pair_slab;  // [T*k + T*shared] or nullptr: slab of each pair (nullptr = masked),
                                 // written by the one-token gate/up kernel, read by the down kernel
     int min_m, max_m;           // grouped kernels skip groups with fewer / more tokens than these
+    const uint8_t *prefetch;    // or nullptr: bytes the one-token down kernel reads into the device caches
+    size_t prefetch_bytes;      // for the caller's next call (read and discarded, 1 KB per wave)
 };
 
 // Router finish fused into the one-token gate/up kernel: the per-slice fp64

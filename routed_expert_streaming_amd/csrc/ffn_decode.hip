@@ -631,6 +631,19 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
     for (int b = 0; b < BPL; ++b)
 #pragma unroll
         for (int j = 0; j < 4; ++j) hd[b][j] = load_global_u4(a.h + (size_t)p * I + 32 * (c + 16 * b) + 8 * j);
+    // the prefetch hint: 1 KB per wave, requested with the loads of the wave's
+    // last batch of rows (so that it is still in the L2 when the next call reads
+    // it; with a single batch, with the first loads) and looked at only after
+    // the rows are done, so nothing waits for it.  The
+    // hint is read in 16 KB units, unit u on XCD u % 8 (workgroups are dealt to
+    // the XCDs round-robin, and XCD x's waves take units x, x + 8, ...): the
+    // router kernel's workgroup u, which reads one 16 KB slice of weights, then
+    // finds it in its own XCD's L2.
+    const int pf_x = blockIdx.x % 8, pf_j = (blockIdx.x / 8) * P + p;
+    const size_t pf_off = ((size_t)(pf_x + 8 * (pf_j >> 4)) * 16 + (pf_j & 15)) * 1024 + 16 * lane;
+    const bool pf = a.prefetch && pf_off + 16 <= a.prefetch_bytes;
+    uint4 pfv = make_uint4(0, 0, 0, 0);
+    if (pf && U < 2) pfv = load_global_u4(a.prefetch + pf_off);
 
     // the pair's slab: the shared expert is known up front; a routed slot's slab
     // was published by the gate/up kernel, else it is looked up
@@ -691,9 +704,13 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
                         a.y[(size_t)p * H + row] = v;
                 }
                 issue(j);
+                if (pf && base + j == U - 2) pfv = load_global_u4(a.prefetch + pf_off);
             }
         }
     }
+    // keeps the prefetch loads (their values are never needed)
+    if (pf && pfv.x == 0x2545F491u && pfv.y == 0x9E3779B9u && pfv.z == 0x7F4A7C15u && pfv.w == 0xF39CC060u)
+        asm volatile("" ::"v"(pfv.x));
     if (COMBINE) {
         if (p == 0 && lane < k) wts[lane] = my_w;
         __syncthreads();

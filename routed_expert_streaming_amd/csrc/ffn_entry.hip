@@ -368,9 +368,11 @@ extern "C" size_t moe_route_ffn_combine_workspace_bytes(int T, int H, int I, int
 extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias,
                                      int E, int k, const void *const *expert_table, const void *shared_slab,
                                      int32_t *topk_idx, float *topk_w, uint16_t *out, void *workspace,
-                                     size_t workspace_bytes, void *stream) {
+                                     size_t workspace_bytes, const void *prefetch, size_t prefetch_bytes,
+                                     void *stream) {
     const char *who = "route_ffn_combine";
     if (T < 0) return moe::fail(MOE_E_ARG, "%s: T=%d < 0", who, T);
+    if (!prefetch && prefetch_bytes) return moe::fail(MOE_E_ARG, "%s: %zu prefetch bytes at NULL", who, prefetch_bytes);
     if (T == 0) return MOE_OK;
     if (!workspace || !w_router || !topk_w) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
     int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, MOE_FFN_AUTO, who);
@@ -398,6 +400,8 @@ extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, con
         a.pair_slab = (const uint8_t **)(fws + Ly.slabs);
         rc = moe::decode1_routed_gate_up(a, ra, s);
         if (rc != MOE_OK) return rc;
+        a.prefetch = (const uint8_t *)prefetch;
+        a.prefetch_bytes = prefetch_bytes;
         return moe::decode_down(a, topk_w, out, s);
     }
     rc = moe_router_topk(x, T, H, w_router, bias, E, k, topk_idx, topk_w, rws, rbytes, stream);

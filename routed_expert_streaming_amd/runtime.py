@@ -232,10 +232,15 @@ class MoEStack:
                                  self.ffn_ws_bytes, self.path, self.stream)
 
     def route_ffn_combine(self, x: torch.Tensor, l: int, out: torch.Tensor):
-        """Router, gate/up, down and combine of layer l in one call (every expert resident)."""
+        """Router, gate/up, down and combine of layer l in one call (every expert resident).
+        The call reads the router weights of the layer that runs next (the first
+        after the last) into the device caches while it runs: they are static, so
+        this does not depend on the next layer's input."""
+        nxt = self.wr[(l + 1) % self.L]
         L.moe_route_ffn_combine(x[l], self.T, self.H, self.I, self.wr[l], None if self.bias is None else self.bias[l],
                                 self.E, self.k, self.table[l], self.shared[l] if self.has_shared else None,
-                                self.idx[l], self.w[l], out[l], self.layer_ws, self.layer_ws_bytes, self.stream)
+                                self.idx[l], self.w[l], out[l], self.layer_ws, self.layer_ws_bytes, self.stream,
+                                prefetch=nxt, prefetch_bytes=nxt.numel() * 4)
 
     def combine(self, l: int, out: torch.Tensor):
         L.moe_combine(self.y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l], self.stream)

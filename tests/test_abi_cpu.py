@@ -298,6 +298,8 @@ def test_route_ffn_combine_validation():
     assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_SHAPE
     bad = list(args); bad[7] = 17  # k > E
     assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_SHAPE
+    # a prefetch size without a pointer
+    assert _status(L.moe_route_ffn_combine, *args, None, None, 4096) == L.MOE_E_ARG
     bad = list(args); bad[14] = ws - 1
     assert _status(L.moe_route_ffn_combine, *bad) == L.MOE_E_NOMEM
     L.moe_route_ffn_combine(None, 0, 256, 128, None, None, 16, 2, None, None, None, None, None, None, 0)

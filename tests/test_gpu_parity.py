@@ -232,8 +232,9 @@ class Layer:
     def oracle(self, rows=None):
         return oracle.moe_layer(self.x, self.Wr, self.bias, self.k, self.slabs, self.shared, self.I, rows=rows)
 
-    def run_routed(self):
-        """Router + FFN + combine through the one-call entry point."""
+    def run_routed(self, prefetch=None):
+        """Router + FFN + combine through the one-call entry point (with an
+        optional prefetch hint: a device byte tensor)."""
         T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
         x = bf16_dev(self.x)
         wr = torch.from_numpy(self.Wr).cuda()
@@ -243,7 +244,8 @@ class Layer:
         out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         nb = L.moe_route_ffn_combine_workspace_bytes(T, H, I, E, k, self.shared is not None)
         ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
-        L.moe_route_ffn_combine(x, T, H, I, wr, b, E, k, self.table, self.shared_dev, idx, w, out, ws, nb)
+        L.moe_route_ffn_combine(x, T, H, I, wr, b, E, k, self.table, self.shared_dev, idx, w, out, ws, nb,
+                                prefetch=prefetch, prefetch_bytes=0 if prefetch is None else prefetch.numel())
         torch.cuda.synchronize()
         return idx.cpu().numpy(), w.cpu().numpy(), out.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -315,6 +317,11 @@ def test_route_ffn_combine_matches_separate_calls(name, T, H, I, E, k, shared, b
     if zero:
         lay.Wr[:] = 0.0
     idx_f, w_f, out_f = lay.run_routed()
+    # a prefetch hint (a size that is no multiple of the 1 KB a wave reads) changes nothing
+    hint = torch.randint(0, 256, ((3 << 20) + 100,), dtype=torch.uint8, device="cuda")
+    idx_p, w_p, out_p = lay.run_routed(prefetch=hint)
+    assert np.array_equal(idx_p, idx_f) and np.array_equal(w_p.view(np.uint32), w_f.view(np.uint32))
+    assert np.array_equal(out_p, out_f)
     idx_s, _, out_s = lay.run(L.MOE_FFN_AUTO)
     _, w_s, _, _ = run_router(lay.x, lay.Wr, lay.bias, k)
     assert np.array_equal(idx_f, idx_s)
