@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--chain-steps", type=int, default=128,
                     help="timed steps of each chained-layer run of the streamed leg (0 skips them)")
     ap.add_argument("--chain-warmup", type=int, default=32)
+    ap.add_argument("--cpu-lane-threads", type=int, default=12,
+                    help="worker threads of the streamed leg's CPU-lane run (0 skips it)")
     ap.add_argument("--no-layer-legs", action="store_true",
                     help="skip the one-resident-layer measurements of the 32-token decode and 2048-token prefill shapes")
     ap.add_argument("--traffic-calibration", action="store_true",
@@ -179,6 +181,8 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     # chained layers with the deepest lookahead need 2*T*k slots per layer
     chained = (chained_runs(torch, st, args, xs)
                if args.chain_steps > 0 and 2 * cfg.tokens * cfg.top_k <= st.C else None)
+    lane = (cpu_lane_run(torch, st, args, xs, args.stream_steps * cfg.tokens / wall)
+            if args.cpu_lane_threads > 0 and st.T * st.k <= st.C else None)
     st.close()
     hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
     ms_step = wall / args.stream_steps * 1e3
@@ -199,7 +203,45 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
            "steps": args.stream_steps, "warmup": args.stream_warmup}
     if chained:
         res["chained"] = chained
+    if lane:
+        res["cpu_lane"] = lane
     log(f"streaming: {res}")
+    return res
+
+
+def cpu_lane_run(torch, st, args, xs, streamed_tokens_per_s: float):
+    """The same streamed steps with a CPU lane: each step's misses split between
+    the copy engine and host cores computing them from the pinned pool, by the
+    earliest-finish cost model (runtime.assign_lanes)."""
+    from routed_expert_streaming_amd import _lib as L
+    st.enable_cpu_lane(args.cpu_lane_threads)
+    out = st.new_output()
+    n_in = len(xs)
+    for s in range(args.stream_warmup):
+        st.forward(xs[s % n_in], out)
+    torch.cuda.synchronize()
+    h0, m0, b0 = st.stats()
+    cpu_e = cpu_p = 0
+    t0 = time.perf_counter()
+    for s in range(args.stream_steps):
+        r = st.forward(xs[s % n_in], out)
+        cpu_e += r.cpu_experts
+        cpu_p += r.cpu_pairs
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    h1, m1, b1 = st.stats()
+    n = args.stream_steps
+    tps = n * st.T / wall
+    res = {"threads": st.lane_threads, "isa_bits": L.moe_cpu_lane_isa(),
+           "t_cpu_expert_ms": {"1_token": round(st.t_cpu1 * 1e3, 3), "8_tokens": round(st.t_cpu8 * 1e3, 3)},
+           "t_copy_expert_ms": round(st.slab / (st.link_GBps * 1e9) * 1e3, 3), "link_GBps_assumed": st.link_GBps,
+           "tokens_per_s": round(tps, 2), "ms_per_step": round(wall / n * 1e3, 3),
+           "speedup_vs_streaming": round(tps / streamed_tokens_per_s, 4),
+           "cpu_experts_per_step": round(cpu_e / n, 3), "cpu_pairs_per_step": round(cpu_p / n, 3),
+           "streamed_experts_per_step": round((m1 - m0) / n, 3),
+           "hit_rate_of_gpu_requests": round((h1 - h0) / max(h1 - h0 + m1 - m0, 1), 4),
+           "h2d_GBps": round((b1 - b0) / wall / 1e9, 2), "steps": n, "warmup": args.stream_warmup}
+    log(f"cpu lane: {res}")
     return res
 
 

@@ -296,6 +296,47 @@ int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w
  * NULL resid / x_next (T = 0 is a no-op). */
 int moe_residual_norm(const uint16_t *add, float *resid, int T, int H, float eps, uint16_t *x_next, void *stream);
 
+/* ------------------------------------------------------------------ CPU lane
+ * Routed experts computed on host cores from the pinned host expert pool while
+ * the GPU computes the others (LayerStoRm README, "Status and limitations": CPU
+ * hybrid decode; glm-flash-lite page, "How it works": a GPU lane for the experts
+ * in VRAM and a CPU lane for those in system RAM, side by side).  A caller sends
+ * some cache misses here instead of streaming them and uploads the returned rows
+ * into the y rows of their (token, expert) pairs before moe_combine.
+ *
+ * Per token x and expert slab: g = W1 x, u = W3 x (fp32, each 32-column block
+ * as s * sum(q x) + m * sum(x), the 16 lanes of a block -- even column 2j and odd
+ * column 2j+1 in lane j -- accumulated with fma across blocks and summed in a
+ * fixed tree), h = bf16_rne(g / (1 + exp(-g)) * u), y = W2 h the same way (fp32).
+ * Every row is computed by one thread in that fixed order: results are the same
+ * for any thread count and instruction set (AVX-512, AVX2 or scalar).
+ *
+ * A lane owns `threads` worker threads (1..256) that run the submitted jobs in
+ * order, all workers on one job at a time.  Thread-safe; the handle is the
+ * caller's until moe_cpu_lane_destroy. */
+typedef struct moe_cpu_lane moe_cpu_lane;
+int moe_cpu_lane_create(int threads, moe_cpu_lane **out);
+/* Queue one expert: slab (host memory, H, I positive multiples of 32, MOE_E_SHAPE
+ * otherwise) for M tokens; x_rows[t] points at token t's H bf16 values, y_rows[t]
+ * at H fp32 values the lane writes.  The lane reads the slab and the x rows until
+ * the job completes (x rows are copied at submission; the slab and y rows must
+ * stay valid and untouched until then).  *ticket receives the job's number;
+ * M = 0 queues nothing and gives the last job's ticket.  MOE_E_ARG for a NULL
+ * lane, ticket, slab or row pointer or M < 0. */
+int moe_cpu_lane_submit(moe_cpu_lane *lane, const void *slab, int H, int I, int M, const uint16_t *const *x_rows,
+                        float *const *y_rows, uint64_t *ticket);
+/* Block until the job with this ticket and every earlier one have completed
+ * (MOE_E_ARG for a ticket not yet issued). */
+int moe_cpu_lane_wait(moe_cpu_lane *lane, uint64_t ticket);
+/* Finish every queued job, stop the workers and free the lane (NULL: no-op). */
+int moe_cpu_lane_destroy(moe_cpu_lane *lane);
+/* Widest vector version this CPU runs: 512 (AVX-512), 256 (AVX2, FMA, F16C) or 0 (scalar). */
+int moe_cpu_lane_isa(void);
+/* Tests: run the lane with the given version (0, 256 or 512, at most
+ * moe_cpu_lane_isa(); MOE_E_ARG otherwise), only with no job in flight
+ * (MOE_E_STATE). */
+int moe_cpu_lane_force_isa(moe_cpu_lane *lane, int isa);
+
 /* ------------------------------------------------------------------ debug
  * Dequantise matrix `which` (0 = W1, 1 = W3, 2 = W2) of a device slab into out
  * (fp32, row-major [rows x cols]); exact, for round-trip tests of the format. */

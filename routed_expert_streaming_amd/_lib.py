@@ -81,6 +81,12 @@ def lib():
             "moe_combine": ([vp, vp, i, i, i, i, vp, vp], i),
             "moe_residual_norm": ([vp, vp, i, i, ctypes.c_float, vp, vp], i),
             "moe_debug_dequant": ([vp, i, i, i, vp, vp], i),
+            "moe_cpu_lane_create": ([i, ctypes.POINTER(vp)], i),
+            "moe_cpu_lane_submit": ([vp, vp, i, i, i, vp, vp, u64p], i),
+            "moe_cpu_lane_wait": ([vp, ctypes.c_uint64], i),
+            "moe_cpu_lane_destroy": ([vp], i),
+            "moe_cpu_lane_isa": ([], i),
+            "moe_cpu_lane_force_isa": ([vp, i], i),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -317,3 +323,36 @@ def moe_residual_norm(add, resid, T, H, eps, x_next, stream=None):
 
 def moe_debug_dequant(slab, H, I, which, out, stream=None):
     _check(lib().moe_debug_dequant(_ptr(slab), H, I, which, _ptr(out), _stream(stream)), "moe_debug_dequant")
+
+
+# ----------------------------------------------------------------------- CPU lane
+def moe_cpu_lane_create(threads: int) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().moe_cpu_lane_create(int(threads), ctypes.byref(out)), "moe_cpu_lane_create")
+    return out.value
+
+
+def moe_cpu_lane_submit(lane, slab, H, I, M, x_rows, y_rows) -> int:
+    """x_rows / y_rows: sequences of M host addresses (bf16 rows in, fp32 rows out).
+    Returns the job's ticket."""
+    xs = (ctypes.c_void_p * max(M, 1))(*[int(a) for a in x_rows])
+    ys = (ctypes.c_void_p * max(M, 1))(*[int(a) for a in y_rows])
+    t = ctypes.c_uint64()
+    _check(lib().moe_cpu_lane_submit(lane, _ptr(slab), H, I, M, xs, ys, ctypes.byref(t)), "moe_cpu_lane_submit")
+    return t.value
+
+
+def moe_cpu_lane_wait(lane, ticket: int):
+    _check(lib().moe_cpu_lane_wait(lane, ticket), "moe_cpu_lane_wait")
+
+
+def moe_cpu_lane_destroy(lane):
+    _check(lib().moe_cpu_lane_destroy(lane), "moe_cpu_lane_destroy")
+
+
+def moe_cpu_lane_isa() -> int:
+    return lib().moe_cpu_lane_isa()
+
+
+def moe_cpu_lane_force_isa(lane, isa: int):
+    _check(lib().moe_cpu_lane_force_isa(lane, isa), "moe_cpu_lane_force_isa")

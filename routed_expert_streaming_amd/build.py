@@ -20,9 +20,13 @@ LIB = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "router.hip", "ffn_gemv.hip", "ffn_decode.hip", "ffn_mfma.hip", "ffn_entry.hip", "cache.hip", "residual.hip"]
+SOURCES = ["abi.cpp", "router.hip", "ffn_gemv.hip", "ffn_decode.hip", "ffn_mfma.hip", "ffn_entry.hip", "cache.hip", "residual.hip",
+           "cpu_lane.cpp"]
+# host-only C++ (no HIP), built with the host compiler: the CPU lane
+HOST_SOURCES = {"cpu_lane.cpp"}
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+CXX = shutil.which("g++") or "g++"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument"]
@@ -32,6 +36,13 @@ COMMON += [f"-D{d}" for d in os.environ.get("MOE_EXTRA_DEFINES", "").split() if 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    if src in HOST_SOURCES:
+        cmd = [CXX, "-O3", "-std=c++17", "-fPIC", "-pthread", "-ffp-contract=off", "-Wall", f"-I{INCLUDE}",
+               "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{CXX} failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,7 +61,7 @@ def build(verbose: bool = False, out: str | None = None) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = target + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

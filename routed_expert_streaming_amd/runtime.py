@@ -74,6 +74,27 @@ def _bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
 class StepStats:
     waves: int = 0
     copies: int = 0
+    cpu_experts: int = 0  # misses computed by the CPU lane instead of streamed
+    cpu_pairs: int = 0    # (token, expert) pairs among them
+
+
+def assign_lanes(misses, t_copy: float, t_cpu, copy_busy: float = 0.0, cpu_busy: float = 0.0):
+    """Cost model of the CPU lane: misses = [(layer, expert, tokens)] in the order
+    both lanes work through them (layer by layer).  Each miss goes to the lane
+    that would finish it first -- the copy engine (t_copy per expert, then the
+    GPU computes it) or the CPU lane (t_cpu(tokens) per expert) -- ties to the
+    copy engine, which also leaves the expert cached.  Returns one bool per miss
+    (True = CPU lane) and the two lanes' busy times."""
+    to_cpu = []
+    for _, _, tokens in misses:
+        fc, fp = copy_busy + t_copy, cpu_busy + t_cpu(tokens)
+        if fp < fc:
+            cpu_busy = fp
+            to_cpu.append(True)
+        else:
+            copy_busy = fc
+            to_cpu.append(False)
+    return to_cpu, copy_busy, cpu_busy
 
 
 @dataclass
@@ -96,10 +117,16 @@ class MoEStack:
     layers: number of layers to build (None = the configuration's).
     split_copies: streamed stacks copy each slab in two halves on two copy
     streams (moe_cache_split_copies).
+    cpu_lane: worker threads of a CPU lane (0 = none): in streamed steps whose
+    layers fit their slots, cache misses are split between the copy engine and
+    host cores computing them from the pinned pool (assign_lanes; lane_pick, if
+    set, overrides the choice: lane_pick(layer, misses) -> experts for the CPU).
+    link_GBps: host-to-device rate the cost model assumes for a streamed expert.
     """
 
     def __init__(self, cfg: synth.Config, *, layers: int | None = None, cap: float | None = None,
-                 device: int = 0, threads: int = 0, path: int = L.MOE_FFN_AUTO, split_copies: bool = True):
+                 device: int = 0, threads: int = 0, path: int = L.MOE_FFN_AUTO, split_copies: bool = True,
+                 cpu_lane: int = 0, link_GBps: float = 55.0):
         L.lib()
         self.cfg = cfg
         self.L = layers or cfg.layers
@@ -186,6 +213,12 @@ class MoEStack:
         self.pw = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
         self._idx_host = PinnedHost(max(Lyr, 2) * T * k * 4) if self.streaming else None
         self._mask_host = PinnedHost(Lyr * self.max_waves * E) if self.streaming else None
+        # CPU lane: host copies of the layer inputs and the rows it returns
+        self.lane = None
+        self.lane_pick = None
+        self.link_GBps = link_GBps
+        if cpu_lane and self.streaming:
+            self.enable_cpu_lane(cpu_lane)
         torch.cuda.synchronize(self.dev)
 
     # ------------------------------------------------------------------ inputs
@@ -273,6 +306,81 @@ class MoEStack:
         w = self.wave_size(len(order))
         return [sorted(order[i:i + w]) for i in range(0, len(order), w)]
 
+    # ------------------------------------------------------------------ CPU lane
+    def enable_cpu_lane(self, threads: int):
+        """Start a CPU lane of `threads` workers (streamed stacks only) and calibrate it."""
+        assert self.streaming and self.lane is None
+        P = self.T * self.k + (self.T if self.has_shared else 0)
+        self.lane = L.moe_cpu_lane_create(threads)
+        self.lane_threads = threads
+        self._x_host = torch.empty((self.L, self.T, self.H), dtype=torch.bfloat16, pin_memory=True)
+        self._y_host = torch.empty((self.L, P, self.H), dtype=torch.float32, pin_memory=True)
+        self.t_cpu1, self.t_cpu8 = self.calibrate_lane()
+
+    def t_cpu(self, tokens: int) -> float:
+        """CPU lane seconds for one expert and `tokens` tokens (calibrated at 1 and 8)."""
+        return self.t_cpu1 + (tokens - 1) * (self.t_cpu8 - self.t_cpu1) / 7.0
+
+    def calibrate_lane(self, reps: int = 3):
+        """Time the lane on layer 0's first slabs (1 and 8 tokens), best of reps."""
+        import time
+        ys = torch.empty((8, self.H), dtype=torch.float32)
+        xs = torch.zeros((8, self.H), dtype=torch.bfloat16)
+        out = []
+        for M in (1, 8):
+            best = float("inf")
+            for r in range(reps + 1):
+                slab = self.host[0].ptr + (r % self.E) * self.slab
+                t0 = time.perf_counter()
+                t = L.moe_cpu_lane_submit(self.lane, slab, self.H, self.I, M,
+                                          [xs[i].data_ptr() for i in range(M)], [ys[i].data_ptr() for i in range(M)])
+                L.moe_cpu_lane_wait(self.lane, t)
+                if r:  # the first run warms the threads
+                    best = min(best, time.perf_counter() - t0)
+            out.append(best)
+        return out[0], out[1]
+
+    def plan_cpu_lane(self, needed_by_layer, idx_host):
+        """Experts of each layer that the CPU lane computes this step."""
+        misses = []
+        for l, needed in enumerate(needed_by_layer):
+            slots, _ = L.moe_cache_lookup(self.cache, l, needed)
+            tok = np.bincount(idx_host[l].ravel(), minlength=self.E)
+            misses += [(l, e, int(tok[e])) for e, s in zip(needed, slots) if s < 0]
+        cpu = [set() for _ in needed_by_layer]
+        if self.lane_pick is not None:
+            for l in range(len(needed_by_layer)):
+                cpu[l] = set(self.lane_pick(l, [e for ll, e, _ in misses if ll == l]))
+            return cpu
+        to_cpu, _, _ = assign_lanes(misses, self.slab / (self.link_GBps * 1e9), self.t_cpu)
+        for (l, e, _), c in zip(misses, to_cpu):
+            if c:
+                cpu[l].add(e)
+        return cpu
+
+    def submit_cpu_lane(self, l: int, experts, idx_l: np.ndarray):
+        """Queue layer l's CPU-lane experts; returns (last ticket, sorted pair rows)."""
+        ticket, rows = 0, []
+        for e in sorted(experts):
+            ts, iis = np.nonzero(idx_l == e)
+            pairs = [int(t) * self.k + int(i) for t, i in zip(ts, iis)]
+            ticket = L.moe_cpu_lane_submit(self.lane, self.host[l].ptr + e * self.slab, self.H, self.I, len(pairs),
+                                           [self._x_host[l, int(t)].data_ptr() for t in ts],
+                                           [self._y_host[l, p].data_ptr() for p in pairs])
+            rows += pairs
+        return ticket, sorted(rows)
+
+    def upload_cpu_rows(self, l: int, rows):
+        """Copy the CPU lane's rows of layer l into y (runs of adjacent rows as one copy)."""
+        i = 0
+        while i < len(rows):
+            j = i
+            while j + 1 < len(rows) and rows[j + 1] == rows[j] + 1:
+                j += 1
+            self.y[rows[i]:rows[j] + 1].copy_(self._y_host[l, rows[i]:rows[j] + 1], non_blocking=True)
+            i = j + 1
+
+    # ------------------------------------------------------------------ steps
     def forward(self, x: torch.Tensor, out: torch.Tensor) -> StepStats:
         """One step over all layers: x [L,T,H] bf16 -> out [L,T,H] bf16."""
         st = StepStats()
@@ -284,13 +392,27 @@ class MoEStack:
         # one small D2H per step, then the host plans every layer
         idx_host = np.frombuffer(self._idx_host.array, dtype=np.int32, count=self.L * self.T * self.k)
         torch.from_numpy(idx_host).copy_(self.idx.view(-1), non_blocking=True)
+        if self.lane is not None:
+            self._x_host.copy_(x, non_blocking=True)
         self.stream.synchronize()
         plans = []
         for l, row in enumerate(idx_host.reshape(self.L, -1).tolist()):
             needed = sorted(set(row))
             # up to C experts always fit in one wave, whatever is resident
             plans.append([needed] if len(needed) <= self.C else self.plan_waves(l, needed))
-        need_masks = any(len(p) > 1 for p in plans)
+        # CPU lane (single-wave steps): some misses are computed on the host
+        cpu_sets, lane_jobs = [set() for _ in plans], {}
+        self.last_cpu_sets = cpu_sets
+        if self.lane is not None and all(len(p) == 1 for p in plans):
+            idx3 = idx_host.reshape(self.L, self.T, self.k)
+            cpu_sets = self.last_cpu_sets = self.plan_cpu_lane([p[0] for p in plans], idx3)
+            for l, cs in enumerate(cpu_sets):
+                if cs:
+                    plans[l] = [[e for e in plans[l][0] if e not in cs]]
+                    lane_jobs[l] = self.submit_cpu_lane(l, cs, idx3[l])
+                    st.cpu_experts += len(cs)
+                    st.cpu_pairs += len(lane_jobs[l][1])
+        need_masks = any(len(p) > 1 for p in plans) or bool(lane_jobs)
         if need_masks:
             mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
                                count=self.L * self.max_waves * self.E).reshape(self.L, self.max_waves, self.E)
@@ -308,6 +430,18 @@ class MoEStack:
             if single[l]:
                 st.copies += L.moe_cache_prefetch_async(self.cache, l, waves[0])
         for l, waves in enumerate(plans):
+            if single[l] and l in lane_jobs:
+                # GPU lane: the layer's hits and streamed misses (masked call), then
+                # the CPU lane's rows, then the combine of all of them
+                L.moe_cache_wait(self.cache, l, self.stream)
+                self.ffn(x, l, mask=self.masks[l, 0], shared=True)
+                L.moe_cache_release(self.cache, l, self.stream)
+                ticket, rows = lane_jobs[l]
+                L.moe_cpu_lane_wait(self.lane, ticket)
+                self.upload_cpu_rows(l, rows)
+                self.combine(l, out)
+                st.waves += 1
+                continue
             if single[l]:
                 L.moe_cache_wait(self.cache, l, self.stream)
                 self.ffn_combine(x, l, out)
@@ -394,6 +528,9 @@ class MoEStack:
             L.moe_cache_reset(self.cache)
 
     def close(self):
+        if getattr(self, "lane", None):
+            L.moe_cpu_lane_destroy(self.lane)
+            self.lane = None
         if self.cache:
             torch.cuda.synchronize(self.dev)
             L.moe_cache_destroy(self.cache)

@@ -1,0 +1,121 @@
+"""GPU parity of streamed steps with a CPU lane: some cache misses computed on
+host cores from the pinned pool while the GPU computes the rest.
+
+Bars: expert indices bit-exact against the oracle router; every layer's output
+within 2e-2 * max|ref| of the oracle (the CPU lane's rows and the GPU's combined
+as usual); the cache's hits and misses equal to a brute-force LRU replay of the
+requests the GPU lane made (the CPU lane's experts bypass the cache); with
+nothing sent to the CPU lane the step is bit-identical to a stack without one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from routed_expert_streaming_amd import _lib as L
+from routed_expert_streaming_amd.runtime import MoEStack
+from tests.test_abi_cpu import LRUModel
+from tests.test_gpu_parity import check_close
+
+
+def pool_slabs(st: MoEStack, l: int):
+    """Layer l's routed slabs as views of the pinned host pool the lanes read."""
+    return [st.host[l].array[e * st.slab:(e + 1) * st.slab] for e in range(st.E)]
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.lib()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name,layers,steps,rows", [
+    ("decode1_stream", 3, 4, None),
+    ("decode32_stream", 2, 2, list(range(0, 32, 3))),
+])
+def test_streamed_with_cpu_lane_against_oracle(name, layers, steps, rows):
+    cfg = synth.get(name)
+    st = MoEStack(cfg, layers=layers, cpu_lane=4)
+    k = cfg.top_k
+    try:
+        assert st.streaming and st.lane
+        # every other miss of each layer to the CPU lane, so both lanes always work
+        st.lane_pick = lambda l, misses: misses[::2]
+        wr = [st.wr[l].cpu().numpy() for l in range(layers)]
+        bias = [None if st.bias is None else st.bias[l].cpu().numpy() for l in range(layers)]
+        model = LRUModel(layers, 10 ** 6, st.C)
+        out = st.new_output()
+        n_cpu = 0
+        for s in range(steps):
+            x = st.make_inputs(s)
+            r = st.forward(x, out)
+            torch.cuda.synchronize()
+            n_cpu += r.cpu_experts
+            xb, ob, idx = bits(x), bits(out), st.idx.cpu().numpy()
+            for l in range(layers):
+                needed = sorted(set(int(e) for e in idx[l].ravel()))
+                gpu_side = [e for e in needed if e not in st.last_cpu_sets[l]]
+                assert model.prefetch(l, gpu_side)[0] == "ok"
+                model.release(l)
+                o = oracle.moe_layer(xb[l], wr[l], bias[l], k, pool_slabs(st, l), st.host_shared(l), cfg.inter,
+                                     rows=rows)
+                sel = slice(None) if rows is None else rows
+                assert (o["idx"][sel] == idx[l][sel]).all(), (name, s, l)
+                ratio = check_close(ob[l][sel], o["out64"][sel], f"{name} step {s} layer {l}")
+                print(f"{name} step {s} layer {l}: CPU lane {sorted(st.last_cpu_sets[l])}, "
+                      f"max err / max|ref| = {ratio:.2e}")
+        hits, misses, nbytes = st.stats()
+        assert (hits, misses) == (model.hits, model.misses)
+        assert nbytes == misses * st.slab
+        assert n_cpu > 0
+    finally:
+        st.close()
+
+
+def test_cpu_lane_cost_model_run_and_empty_pick_is_identical():
+    cfg = synth.get("decode1_stream")
+    layers, steps = 2, 3
+    plain = MoEStack(cfg, layers=layers)
+    ref = []
+    out = plain.new_output()
+    for s in range(steps):
+        plain.forward(plain.make_inputs(s), out)
+        torch.cuda.synchronize()
+        ref.append(bits(out))
+    plain.close()
+    st = MoEStack(cfg, layers=layers, cpu_lane=4)
+    try:
+        assert st.t_cpu1 > 0 and st.t_cpu8 >= 0
+        st.lane_pick = lambda l, misses: []
+        out = st.new_output()
+        for s in range(steps):
+            r = st.forward(st.make_inputs(s), out)
+            torch.cuda.synchronize()
+            assert r.cpu_experts == 0
+            assert (bits(out) == ref[s]).all()
+        # the cost model itself, a few steps: outputs stay within the bar
+        st.lane_pick = None
+        wr = [st.wr[l].cpu().numpy() for l in range(layers)]
+        bias = [st.bias[l].cpu().numpy() for l in range(layers)]
+        for s in range(steps, steps + 3):
+            x = st.make_inputs(s)
+            r = st.forward(x, out)
+            torch.cuda.synchronize()
+            xb, ob = bits(x), bits(out)
+            for l in range(layers):
+                o = oracle.moe_layer(xb[l], wr[l], bias[l], cfg.top_k, pool_slabs(st, l), st.host_shared(l), cfg.inter)
+                check_close(ob[l], o["out64"], f"cost model step {s} layer {l}")
+            print(f"step {s}: {r.cpu_experts} experts on the CPU lane (t_cpu 1 token {st.t_cpu1 * 1e3:.3f} ms)")
+    finally:
+        st.close()
