@@ -61,8 +61,8 @@ def parse():
     ap.add_argument("--chain-steps", type=int, default=128,
                     help="timed steps of each chained-layer run of the streamed leg (0 skips them)")
     ap.add_argument("--chain-warmup", type=int, default=32)
-    ap.add_argument("--cpu-lane-threads", type=int, default=12,
-                    help="worker threads of the streamed leg's CPU-lane run (0 skips it)")
+    ap.add_argument("--cpu-lane-threads", type=int, default=14,
+                    help="worker threads of the streamed leg's CPU-lane run (0 skips it; decode workloads only)")
     ap.add_argument("--no-layer-legs", action="store_true",
                     help="skip the one-resident-layer measurements of the 32-token decode and 2048-token prefill shapes")
     ap.add_argument("--traffic-calibration", action="store_true",
@@ -182,7 +182,7 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     chained = (chained_runs(torch, st, args, xs)
                if args.chain_steps > 0 and 2 * cfg.tokens * cfg.top_k <= st.C else None)
     lane = (cpu_lane_run(torch, st, args, xs, args.stream_steps * cfg.tokens / wall)
-            if args.cpu_lane_threads > 0 and st.T * st.k <= st.C else None)
+            if args.cpu_lane_threads > 0 and st.T <= 64 else None)
     st.close()
     hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
     ms_step = wall / args.stream_steps * 1e3

@@ -395,23 +395,27 @@ class MoEStack:
         if self.lane is not None:
             self._x_host.copy_(x, non_blocking=True)
         self.stream.synchronize()
+        needed_by_layer = [sorted(set(row)) for row in idx_host.reshape(self.L, -1).tolist()]
+        # CPU lane: some misses are computed on the host; a layer uses it when the
+        # rest of its experts fit its slots (one wave)
+        cpu_sets, lane_jobs = [set() for _ in needed_by_layer], {}
+        idx3 = idx_host.reshape(self.L, self.T, self.k)
+        if self.lane is not None:
+            cpu_sets = self.plan_cpu_lane(needed_by_layer, idx3)
         plans = []
-        for l, row in enumerate(idx_host.reshape(self.L, -1).tolist()):
-            needed = sorted(set(row))
+        for l, needed in enumerate(needed_by_layer):
+            if cpu_sets[l]:
+                gpu_side = [e for e in needed if e not in cpu_sets[l]]
+                if len(gpu_side) <= self.C:
+                    plans.append([gpu_side])
+                    lane_jobs[l] = self.submit_cpu_lane(l, cpu_sets[l], idx3[l])
+                    st.cpu_experts += len(cpu_sets[l])
+                    st.cpu_pairs += len(lane_jobs[l][1])
+                    continue
+                cpu_sets[l] = set()
             # up to C experts always fit in one wave, whatever is resident
             plans.append([needed] if len(needed) <= self.C else self.plan_waves(l, needed))
-        # CPU lane (single-wave steps): some misses are computed on the host
-        cpu_sets, lane_jobs = [set() for _ in plans], {}
         self.last_cpu_sets = cpu_sets
-        if self.lane is not None and all(len(p) == 1 for p in plans):
-            idx3 = idx_host.reshape(self.L, self.T, self.k)
-            cpu_sets = self.last_cpu_sets = self.plan_cpu_lane([p[0] for p in plans], idx3)
-            for l, cs in enumerate(cpu_sets):
-                if cs:
-                    plans[l] = [[e for e in plans[l][0] if e not in cs]]
-                    lane_jobs[l] = self.submit_cpu_lane(l, cs, idx3[l])
-                    st.cpu_experts += len(cs)
-                    st.cpu_pairs += len(lane_jobs[l][1])
         need_masks = any(len(p) > 1 for p in plans) or bool(lane_jobs)
         if need_masks:
             mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
