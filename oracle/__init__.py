@@ -66,6 +66,16 @@ def lib():
         L.oracle_moe_layer.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, i64, i32,
                                        vp, vp, vp, vp]
         L.oracle_residual_norm.argtypes = [vp, vp, i64, i64, ctypes.c_double, vp]
+        L.oracle_slab_bytes_fmt.argtypes = [i64, i64, i32]
+        L.oracle_slab_bytes_fmt.restype = i64
+        L.oracle_e2m1_to_double.argtypes = [i32]
+        L.oracle_e2m1_to_double.restype = ctypes.c_double
+        L.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_to_double.restype = ctypes.c_double
+        L.oracle_dequant_fmt.argtypes = [vp, i64, i64, i32, vp, i32]
+        L.oracle_expert_ffn_fmt.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i32]
+        L.oracle_moe_layer_fmt.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, i64, i32,
+                                           vp, vp, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -89,23 +99,31 @@ def double_to_bf16(v: float) -> int:
     return int(lib().oracle_double_to_bf16(float(v)))
 
 
-def slab_bytes(H: int, I: int) -> int:
-    return int(lib().oracle_slab_bytes(H, I))
+def slab_bytes(H: int, I: int, fmt: int = 0) -> int:
+    return int(lib().oracle_slab_bytes_fmt(H, I, fmt))
 
 
-def dequant(slab: np.ndarray, H: int, I: int, which: int) -> np.ndarray:
+def e2m1_to_double(q: int) -> float:
+    return lib().oracle_e2m1_to_double(q)
+
+
+def e8m0_to_double(v: int) -> float:
+    return lib().oracle_e8m0_to_double(v)
+
+
+def dequant(slab: np.ndarray, H: int, I: int, which: int, fmt: int = 0) -> np.ndarray:
     rows, cols = (I, H) if which < 2 else (H, I)
     out = np.empty((rows, cols), dtype=np.float64)
-    lib().oracle_dequant(_p(slab), H, I, which, _p(out))
+    lib().oracle_dequant_fmt(_p(slab), H, I, which, _p(out), fmt)
     return out
 
 
-def expert_ffn(slab: np.ndarray, H: int, I: int, x: np.ndarray):
+def expert_ffn(slab: np.ndarray, H: int, I: int, x: np.ndarray, fmt: int = 0):
     """One token (x: float64 [H]) through one expert -> (g, u, h, y)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     g, u, h = (np.empty(I, np.float64) for _ in range(3))
     y = np.empty(H, np.float64)
-    lib().oracle_expert_ffn(_p(slab), H, I, _p(x), _p(g), _p(u), _p(h), _p(y))
+    lib().oracle_expert_ffn_fmt(_p(slab), H, I, _p(x), _p(g), _p(u), _p(h), _p(y), fmt)
     return g, u, h, y
 
 
@@ -132,7 +150,7 @@ def router(x_bf16: np.ndarray, Wr: np.ndarray, bias, k: int, threads: int = 0):
 
 
 def moe_layer(x_bf16: np.ndarray, Wr: np.ndarray, bias, k: int, slabs, shared, I: int,
-              rows=None, threads: int = 0):
+              rows=None, threads: int = 0, fmt: int = 0):
     """One MoE layer.  slabs: list of E uint8 arrays; shared: uint8 array or None.
 
     rows: optional list of token indices to compute (others are left zero).
@@ -143,7 +161,7 @@ def moe_layer(x_bf16: np.ndarray, Wr: np.ndarray, bias, k: int, slabs, shared, I
     T, H = x_bf16.shape
     E = Wr.shape[0]
     assert len(slabs) == E
-    sb = slab_bytes(H, I)
+    sb = slab_bytes(H, I, fmt)
     for s in slabs:
         assert s.dtype == np.uint8 and s.size == sb and s.flags["C_CONTIGUOUS"]
     ptrs = np.array([s.ctypes.data for s in slabs], dtype=np.uint64)
@@ -154,9 +172,9 @@ def moe_layer(x_bf16: np.ndarray, Wr: np.ndarray, bias, k: int, slabs, shared, I
     w = np.empty((T, k), np.float64)
     out64 = np.zeros((T, H), np.float64)
     outb = np.zeros((T, H), np.uint16)
-    lib().oracle_moe_layer(_p(x_bf16), T, H, I, E, k, _p(Wr), _p(b), _p(ptrs),
-                           None if shared is None else _p(shared), _p(r), nr, threads,
-                           _p(idx), _p(w), _p(out64), _p(outb))
+    lib().oracle_moe_layer_fmt(_p(x_bf16), T, H, I, E, k, _p(Wr), _p(b), _p(ptrs),
+                               None if shared is None else _p(shared), _p(r), nr, threads,
+                               _p(idx), _p(w), _p(out64), _p(outb), fmt)
     return {"idx": idx, "w": w, "out64": out64, "out_bf16": outb}
 
 

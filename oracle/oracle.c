@@ -21,6 +21,15 @@
  *      then the shared expert with weight 1; reported in fp64 and rounded to bf16.
  * Slab layout: see the header of the input generator (synth/synth.c); this file
  * decodes it on its own from that description.
+ *
+ * Weight format 1, MXFP4 (the pages name MXFP4 decode paths among the sources
+ * of their kernels: LayerStoRm README, "License and attributions"; the element
+ * and scale encodings are those of the OCP Microscaling Formats specification
+ * v1.0): per 32-column block one E8M0 scale byte v (2^(v-127), v = 255 NaN) and
+ * 32 E2M1 codes q (sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0;
+ * exponent 0 is subnormal: 0 or 0.5), W = E2M1(q) * 2^(v-127).  A K-column row
+ * is K/2 code bytes (same nibble order) then K/32 scale bytes, padded to 16.
+ * The *_fmt functions take the format; the others are format 0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -76,10 +85,25 @@ uint16_t oracle_double_to_bf16(double v) {
 
 /* ---------------- slab decoding ---------------- */
 /* A row of K columns: K/2 code bytes, K/32 records of 4 bytes, zero padding to a multiple of 16. */
-static int64_t row_bytes(int64_t cols) { return (cols / 2 + (cols / 32) * 4 + 15) / 16 * 16; }
-static int64_t matrix_bytes(int64_t rows, int64_t cols) { return rows * row_bytes(cols); }
+static int g_fmt = 0; /* weight format of the call in progress (set by the *_fmt entry points) */
+static int64_t row_bytes_f(int64_t cols, int fmt) {
+    return fmt == 1 ? (cols / 2 + cols / 32 + 15) / 16 * 16 : (cols / 2 + (cols / 32) * 4 + 15) / 16 * 16;
+}
+static int64_t row_bytes(int64_t cols) { return row_bytes_f(cols, g_fmt); }
 
-int64_t oracle_slab_bytes(int64_t H, int64_t I) { return 2 * matrix_bytes(I, H) + matrix_bytes(H, I); }
+int64_t oracle_slab_bytes(int64_t H, int64_t I) { return 2 * I * row_bytes_f(H, 0) + H * row_bytes_f(I, 0); }
+int64_t oracle_slab_bytes_fmt(int64_t H, int64_t I, int fmt) {
+    return 2 * I * row_bytes_f(H, fmt) + H * row_bytes_f(I, fmt);
+}
+
+/* OCP MX v1.0 FP4 (E2M1) element value. */
+double oracle_e2m1_to_double(int q) {
+    const int sign = (q >> 3) & 1, e = (q >> 1) & 3, m = q & 1;
+    const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -mag : mag;
+}
+/* OCP MX v1.0 E8M0 scale value. */
+double oracle_e8m0_to_double(uint8_t v) { return v == 255 ? NAN : ldexp(1.0, (int)v - 127); }
 
 /* Row r of matrix `which` (0 = W1 gate [I x H], 1 = W3 up [I x H], 2 = W2 down
    [H x I]); the slab holds the I row pairs (W1 row, W3 row), then the H rows of W2. */
@@ -91,6 +115,14 @@ static const uint8_t *matrix_row(const uint8_t *slab, int64_t H, int64_t I, int 
 
 /* Dequantise one row (K = cols columns, starting at `row`) into out[cols]. */
 static void dequant_row(const uint8_t *row, int64_t cols, double *out) {
+    if (g_fmt == 1) {
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t byte = row[c / 2];
+            int q = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+            out[c] = oracle_e2m1_to_double(q) * oracle_e8m0_to_double(row[cols / 2 + c / 32]);
+        }
+        return;
+    }
     const uint8_t *codes = row;
     const uint8_t *params = row + cols / 2;
     for (int64_t c = 0; c < cols; ++c) {
@@ -274,4 +306,27 @@ void oracle_residual_norm(const uint16_t *add, float *resid, int64_t T, int64_t 
         const double den = sqrt(ss / (double)H + eps);
         for (int64_t h = 0; h < H; ++h) x_next[t * H + h] = oracle_double_to_bf16((double)r[h] / den);
     }
+}
+
+/* ---------------- weight format selection ----------------
+ * The same computations for a slab of weight format `fmt` (0 or 1).  Not
+ * reentrant across formats: callers run one format at a time. */
+void oracle_dequant_fmt(const uint8_t *slab, int64_t H, int64_t I, int which, double *out, int fmt) {
+    g_fmt = fmt;
+    oracle_dequant(slab, H, I, which, out);
+    g_fmt = 0;
+}
+void oracle_expert_ffn_fmt(const uint8_t *slab, int64_t H, int64_t I, const double *x, double *g, double *u,
+                           double *h, double *y, int fmt) {
+    g_fmt = fmt;
+    oracle_expert_ffn(slab, H, I, x, g, u, h, y);
+    g_fmt = 0;
+}
+void oracle_moe_layer_fmt(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_t E, int k, const float *Wr,
+                          const float *bias, const uint8_t *const *slabs, const uint8_t *shared, const int32_t *rows,
+                          int64_t n_rows, int nthreads, int32_t *idx, double *w, double *out64, uint16_t *out_bf16,
+                          int fmt) {
+    g_fmt = fmt;
+    oracle_moe_layer(x, T, H, I, E, k, Wr, bias, slabs, shared, rows, n_rows, nthreads, idx, w, out64, out_bf16);
+    g_fmt = 0;
 }

@@ -53,6 +53,9 @@ def lib():
         L.synth_slab_bytes.restype = i64
         L.synth_expert_slab.argtypes = [u64, u32, u32, i64, i64, vp]
         L.synth_expert_slabs.argtypes = [u64, u32, vp, i64, i64, i64, vp, i32]
+        L.synth_expert_slabs_fmt.argtypes = [u64, u32, vp, i64, i64, i64, vp, i32, i32]
+        L.synth_slab_bytes_fmt.argtypes = [i64, i64, i32]
+        L.synth_slab_bytes_fmt.restype = i64
         L.synth_double_to_bf16.argtypes = [ctypes.c_double]
         L.synth_double_to_bf16.restype = ctypes.c_uint16
         L.synth_double_to_fp16.argtypes = [ctypes.c_double]
@@ -82,6 +85,8 @@ class Config:
     zipf_s: float
     seed: int
     description: str
+    fmt: int = 0      # expert weight format: 0 = 4-bit codes with fp16 scale/min per 32; 1 = MXFP4
+
 
     @property
     def slots(self) -> int:
@@ -94,7 +99,7 @@ class Config:
 
     @property
     def slab_bytes(self) -> int:
-        return slab_bytes(self.hidden, self.inter)
+        return slab_bytes(self.hidden, self.inter, self.fmt)
 
 
 CONFIGS = {
@@ -110,6 +115,12 @@ CONFIGS = {
     "prefill2048_stream": Config("prefill2048_stream", 16, 2048, 6144, 2048, 256, 0, 8, 0.40, "none", 0.0,
                                  20261208, "prefill chunk 2048 tokens: 16 layers, H6144, 256 experts, I2048, "
                                  "top-8, uniform routing, cap 40%"),
+    "decode1_mx": Config("decode1_mx", 8, 1, 4096, 1536, 128, 1, 8, 1.0, "none", 0.0, 20261210,
+                         "decode batch 1 with MXFP4 expert weights: 8 layers, H4096, 128 experts + 1 shared, "
+                         "I1536, top-8, resident", 1),
+    "decode1_mx_stream": Config("decode1_mx_stream", 8, 1, 4096, 1536, 128, 1, 8, 0.25, "zipf", 1.1, 20261211,
+                                "decode batch 1 with MXFP4 expert weights, cache cap 25% per layer, Zipf(1.1) "
+                                "router bias, streamed misses", 1),
 }
 ORDER = ["tiny", "decode1", "decode1_stream", "decode32_stream", "prefill2048_stream"]
 
@@ -124,8 +135,8 @@ def matrix_bytes(rows: int, cols: int) -> int:
     return int(lib().synth_matrix_bytes(rows, cols))
 
 
-def slab_bytes(hidden: int, inter: int) -> int:
-    return int(lib().synth_slab_bytes(hidden, inter))
+def slab_bytes(hidden: int, inter: int, fmt: int = 0) -> int:
+    return int(lib().synth_slab_bytes_fmt(hidden, inter, fmt))
 
 
 def philox(ctr, key) -> np.ndarray:
@@ -164,18 +175,21 @@ def router_bias(cfg: Config, layer: int):
     return out
 
 
-def expert_slab(seed: int, layer: int, expert: int, H: int, I: int) -> np.ndarray:
-    out = np.empty(slab_bytes(H, I), dtype=np.uint8)
-    lib().synth_expert_slab(seed, layer, expert, H, I, _ptr(out))
+def expert_slab(seed: int, layer: int, expert: int, H: int, I: int, fmt: int = 0) -> np.ndarray:
+    out = np.empty(slab_bytes(H, I, fmt), dtype=np.uint8)
+    if fmt == 0:
+        lib().synth_expert_slab(seed, layer, expert, H, I, _ptr(out))
+    else:
+        fill_slabs(seed, layer, [expert], H, I, [out.ctypes.data], 1, fmt)
     return out
 
 
-def fill_slabs(seed: int, layer: int, experts, H: int, I: int, dst_ptrs, threads: int = 0) -> None:
+def fill_slabs(seed: int, layer: int, experts, H: int, I: int, dst_ptrs, threads: int = 0, fmt: int = 0) -> None:
     """Write the slabs of `experts` of `layer` to the host addresses `dst_ptrs`."""
     ex = np.ascontiguousarray(np.asarray(experts, dtype=np.uint32))
     ptrs = np.ascontiguousarray(np.asarray(dst_ptrs, dtype=np.uint64))
     assert ex.shape == ptrs.shape
-    lib().synth_expert_slabs(seed, layer, _ptr(ex), len(ex), H, I, _ptr(ptrs), threads)
+    lib().synth_expert_slabs_fmt(seed, layer, _ptr(ex), len(ex), H, I, _ptr(ptrs), threads, fmt)
 
 
 def shared_expert_id(cfg: Config, j: int = 0) -> int:

@@ -25,6 +25,13 @@
  * rounded to fp32; codes uniform on 0..15; scale = fp16(|N(0, 0.02^2)|);
  * min = -8*scale (exact in fp16).  The scale of block b is drawn from Philox
  * call b/2 (cosine branch for even b, sine branch for odd b).
+ *
+ * Weight format 1 (MXFP4, the *_fmt functions): the same slab arrangement, a
+ * K-column row being K/2 code bytes (same nibble order; a code is an E2M1
+ * value: sign bit 3, exponent bits 2-1, mantissa bit 0) then K/32 one-byte
+ * E8M0 block scales, zero-padded to a multiple of 16 bytes (17/32 byte per
+ * weight when K % 512 == 0).  Codes uniform on 0..15; scale byte of block b =
+ * 120 + (byte b%16 of Philox call b/16) mod 3, i.e. 2^-7, 2^-6 or 2^-5.
  */
 #include <math.h>
 #include <stdint.h>
@@ -34,7 +41,7 @@
 #include <omp.h>
 #endif
 
-enum { KIND_X = 1, KIND_WR = 2, KIND_BIAS = 3, KIND_CODES = 4, KIND_PARAMS = 5 };
+enum { KIND_X = 1, KIND_WR = 2, KIND_BIAS = 3, KIND_CODES = 4, KIND_PARAMS = 5, KIND_MX_CODES = 6, KIND_MX_SCALES = 7 };
 
 /* ---------------- Philox4x32-10 ---------------- */
 static inline void mulhilo32(uint32_t a, uint32_t b, uint32_t *hi, uint32_t *lo) {
@@ -277,4 +284,55 @@ void synth_expert_slabs(uint64_t seed, uint32_t layer, const uint32_t *experts, 
 void synth_expert_slab(uint64_t seed, uint32_t layer, uint32_t expert, int64_t H, int64_t I, uint8_t *out) {
     uint8_t *outs[1] = { out };
     synth_expert_slabs(seed, layer, &expert, 1, H, I, outs, 1);
+}
+
+/* ---------------- weight format 1: MXFP4 ---------------- */
+static int64_t row_bytes_fmt(int64_t cols, int fmt) {
+    return fmt == 1 ? (cols / 2 + cols / 32 + 15) / 16 * 16 : row_bytes(cols);
+}
+int64_t synth_slab_bytes_fmt(int64_t H, int64_t I, int fmt) {
+    return 2 * I * row_bytes_fmt(H, fmt) + H * row_bytes_fmt(I, fmt);
+}
+
+static void fill_matrix_part_mx(uint64_t seed, uint32_t layer, uint32_t expert, uint32_t m, int64_t rows,
+                                int64_t cols, uint8_t *base, int64_t stride, int64_t part, int64_t nparts) {
+    const int64_t cpr = cols / 32, used = cols / 2 + cols / 32, pad = row_bytes_fmt(cols, 1) - used;
+    const int64_t r0 = rows * part / nparts, r1 = rows * (part + 1) / nparts;
+    for (int64_t row = r0; row < r1; ++row) {
+        uint8_t *rp = base + row * stride;
+        for (int64_t ch = 0; ch < cpr; ++ch) {
+            uint32_t r[4];
+            draw(seed, KIND_MX_CODES, 0, layer, expert, m, (uint32_t)(row * cpr + ch), r);
+            memcpy(rp + 16 * ch, r, 16);
+        }
+        for (int64_t b = 0; b < cpr; ++b) {
+            int64_t B = row * cpr + b;
+            uint32_t r[4];
+            draw(seed, KIND_MX_SCALES, 0, layer, expert, m, (uint32_t)(B / 16), r);
+            uint8_t bytes[16];
+            memcpy(bytes, r, 16);
+            rp[cols / 2 + b] = (uint8_t)(120 + bytes[B % 16] % 3);
+        }
+        if (pad > 0) memset(rp + used, 0, (size_t)pad);
+    }
+}
+
+void synth_expert_slabs_fmt(uint64_t seed, uint32_t layer, const uint32_t *experts, int64_t n, int64_t H,
+                            int64_t I, uint8_t *const *outs, int nthreads, int fmt) {
+    if (fmt != 1) {
+        synth_expert_slabs(seed, layer, experts, n, H, I, outs, nthreads);
+        return;
+    }
+    nthreads = clamp_threads(nthreads);
+    const int64_t nparts = 16, njobs = n * 3 * nparts;
+    const int64_t rh = row_bytes_fmt(H, 1), ri = row_bytes_fmt(I, 1);
+    #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t job = 0; job < njobs; ++job) {
+        int64_t i = job / (3 * nparts);
+        uint32_t m = (uint32_t)((job / nparts) % 3);
+        int64_t part = job % nparts;
+        int64_t rows = (m < 2) ? I : H, cols = (m < 2) ? H : I;
+        int64_t start = m == 0 ? 0 : m == 1 ? rh : 2 * I * rh, stride = m < 2 ? 2 * rh : ri;
+        fill_matrix_part_mx(seed, layer, experts[i], m, rows, cols, outs[i] + start, stride, part, nparts);
+    }
 }

@@ -390,3 +390,79 @@ def test_residual_norm_scale_invariance_and_fp32_update():
     oracle.residual_norm(add, upd, 1e-6)
     add_f = np.array([[oracle.bf16_to_double(int(b)) for b in row] for row in add], np.float32)
     assert (upd == r + add_f).all()
+
+
+# ---------------------------------------------------------------- weight format 1 (MXFP4)
+# OCP Microscaling Formats v1.0: FP4 E2M1 element values by code (sign bit 3),
+# E8M0 scale = 2^(v - 127) with v = 255 NaN.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def mx_row(q, v):
+    """One MXFP4 row from codes q [K] and scale bytes v [K/32], written from the
+    layout description (byte b: column 2b low nibble, 2b+1 high), padded to 16."""
+    q = np.asarray(q, np.uint8)
+    body = bytes((q[0::2] | (q[1::2] << 4)).astype(np.uint8)) + bytes(np.asarray(v, np.uint8))
+    return body + bytes((-len(body)) % 16)
+
+
+def mx_slab(H, I, q1, v1, q3, v3, q2, v2):
+    blob = b"".join(mx_row(q1[r], v1[r]) + mx_row(q3[r], v3[r]) for r in range(I))
+    blob += b"".join(mx_row(q2[r], v2[r]) for r in range(H))
+    return np.frombuffer(blob, np.uint8).copy()
+
+
+def test_mx_element_and_scale_values():
+    for q, ref in enumerate(E2M1_TABLE):
+        got = oracle.e2m1_to_double(q)
+        assert got == ref and np.signbit(got) == np.signbit(ref), q
+    assert oracle.e8m0_to_double(127) == 1.0
+    assert oracle.e8m0_to_double(120) == 2.0 ** -7
+    assert oracle.e8m0_to_double(0) == 2.0 ** -127
+    assert oracle.e8m0_to_double(254) == 2.0 ** 127
+    assert np.isnan(oracle.e8m0_to_double(255))
+
+
+@pytest.mark.parametrize("H,I", [(64, 32), (96, 64)])
+def test_mx_dequant_matches_layout(H, I):
+    rng = np.random.default_rng(H + I)
+    q1, q3 = rng.integers(0, 16, (I, H)), rng.integers(0, 16, (I, H))
+    q2 = rng.integers(0, 16, (H, I))
+    v1, v3 = rng.integers(100, 140, (I, H // 32)), rng.integers(100, 140, (I, H // 32))
+    v2 = rng.integers(100, 140, (H, I // 32))
+    slab = mx_slab(H, I, q1, v1, q3, v3, q2, v2)
+    assert slab.size == oracle.slab_bytes(H, I, 1) == synth.slab_bytes(H, I, 1)
+    tab = np.array(E2M1_TABLE)
+    for which, (q, v) in enumerate([(q1, v1), (q3, v3), (q2, v2)]):
+        ref = tab[q] * np.ldexp(1.0, np.repeat(v, 32, axis=1) - 127)
+        np.testing.assert_array_equal(oracle.dequant(slab, H, I, which, fmt=1), ref)
+
+
+def test_mx_expert_ffn_closed_form():
+    """All weights 1.5 * 2^-6 (code 3, scale byte 121): g = u = w * sum(x),
+    h = silu(g) * u, y = w * I * h in every row."""
+    H, I = 64, 32
+    w = 1.5 * 2.0 ** -6
+    c = lambda R, K: (np.full((R, K), 3), np.full((R, K // 32), 121))
+    slab = mx_slab(H, I, *c(I, H), *c(I, H), *c(H, I))
+    x = np.linspace(0.1, 1.0, H)
+    g, u, h, y = oracle.expert_ffn(slab, H, I, x, fmt=1)
+    gs = w * x.sum()
+    np.testing.assert_allclose(g, gs, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(h, gs / (1 + np.exp(-gs)) * gs, rtol=1e-13)
+    np.testing.assert_allclose(y, w * I * h[0], rtol=1e-13)
+
+
+def test_mx_synth_slabs_follow_the_recipe():
+    H, I = 96, 64
+    slab = synth.expert_slab(5, 1, 3, H, I, fmt=1)
+    rb = lambda K: (K // 2 + K // 32 + 15) // 16 * 16
+    for r in range(I):
+        for off, K in ((2 * r * rb(H), H), (2 * r * rb(H) + rb(H), H)):
+            row = slab[off:off + rb(K)]
+            assert set(row[K // 2:K // 2 + K // 32].tolist()) <= {120, 121, 122}
+            assert not row[K // 2 + K // 32:].any()  # padding
+    vals = oracle.dequant(slab, H, I, 2, fmt=1)
+    assert np.isfinite(vals).all() and np.abs(vals).max() <= 6 * 2.0 ** -5
+    assert (synth.expert_slab(5, 1, 3, H, I, fmt=1) == slab).all()
+    assert not (synth.expert_slab(5, 1, 4, H, I, fmt=1) == slab).all()
