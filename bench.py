@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 # the one-token gate/up kernel as launched alone (units per lane, ring depth, no routing)
-GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 1, 0>"
+GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 1, 0, 0>"
 
 
 def log(msg):
@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--chain-warmup", type=int, default=32)
     ap.add_argument("--cpu-lane-threads", type=int, default=14,
                     help="worker threads of the streamed leg's CPU-lane run (0 skips it; decode workloads only)")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 decode leg (resident and streamed)")
     ap.add_argument("--no-layer-legs", action="store_true",
                     help="skip the one-resident-layer measurements of the 32-token decode and 2048-token prefill shapes")
     ap.add_argument("--traffic-calibration", action="store_true",
@@ -144,6 +145,64 @@ def resident_step_ms(torch, cfg, layers: int, steps: int = 8) -> float:
     return a.elapsed_time(b) / steps
 
 
+def mx_leg(torch, args, fmt0_ms_per_step: float, fmt0_streaming):
+    """The one-token decode with MXFP4 expert slabs (E2M1 codes, one E8M0 scale
+    per 32 weights: 17/32 byte per weight against 20/32): resident, one call per
+    layer, then streamed at the same cache cap and router bias as the format-0
+    streamed leg.  Only the MXFP4 entry points run on these slabs."""
+    import synth
+    from routed_expert_streaming_amd.runtime import MoEStack
+
+    cfg = synth.get("decode1_mx")
+    st = MoEStack(cfg)
+    xs = [st.make_inputs(s) for s in range(args.inputs)]
+    out = st.new_output()
+    for s in range(args.warmup):
+        st.forward(xs[s % len(xs)], out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(args.steps):
+        st.forward(xs[s % len(xs)], out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    nbytes = step_bytes(st)
+    res = {"workload": cfg.name, "layers": cfg.layers, "slab_bytes": st.slab, "tokens_per_s": round(1e3 / ms, 2),
+           "ms_per_step": round(ms, 4), "speedup_vs_format0": round(fmt0_ms_per_step / ms, 4),
+           "step_bytes": nbytes, "step_GBps": round(nbytes / ms / 1e6, 1), "steps": args.steps}
+    st.close()
+    del st, xs, out
+    torch.cuda.empty_cache()
+    if not args.no_stream:
+        scfg = synth.get("decode1_mx_stream")
+        ss = MoEStack(scfg)
+        sx = [ss.make_inputs(s) for s in range(32)]
+        so = ss.new_output()
+        for s in range(args.stream_warmup):
+            ss.forward(sx[s % 32], so)
+        torch.cuda.synchronize()
+        h0, m0, b0 = ss.stats()
+        t0 = time.perf_counter()
+        for s in range(args.stream_steps):
+            ss.forward(sx[s % 32], so)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        h1, m1, b1 = ss.stats()
+        tps = args.stream_steps / wall
+        res["streaming"] = {"workload": scfg.name, "tokens_per_s": round(tps, 2),
+                            "ms_per_step": round(wall / args.stream_steps * 1e3, 3),
+                            "hit_rate": round((h1 - h0) / max(h1 - h0 + m1 - m0, 1), 4),
+                            "h2d_bytes_per_step": (b1 - b0) // args.stream_steps,
+                            "h2d_GBps": round((b1 - b0) / wall / 1e9, 2),
+                            "speedup_vs_format0": (round(tps / fmt0_streaming["tokens_per_s"], 4)
+                                                   if fmt0_streaming else None),
+                            "steps": args.stream_steps, "warmup": args.stream_warmup}
+        ss.close()
+    log(f"mx: {res}")
+    return res
+
+
 def streaming_leg(torch, args, resident_ms_per_step: float):
     """The streamed decode workload: expert cache capped per layer, misses copied
     from pinned host RAM over PCIe on a copy stream while earlier layers compute.
@@ -182,7 +241,7 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     chained = (chained_runs(torch, st, args, xs)
                if args.chain_steps > 0 and 2 * cfg.tokens * cfg.top_k <= st.C else None)
     lane = (cpu_lane_run(torch, st, args, xs, args.stream_steps * cfg.tokens / wall)
-            if args.cpu_lane_threads > 0 and st.T <= 64 else None)
+            if args.cpu_lane_threads > 0 and st.T <= 64 and st.fmt == 0 else None)
     st.close()
     hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
     ms_step = wall / args.stream_steps * 1e3
@@ -392,11 +451,17 @@ def counter_traffic(kernel: str):
     return None
 
 
+def bytes_per_32(stack) -> int:
+    """Weight bytes per 32 weights: 16 code bytes plus a 4-byte (fp16 scale, fp16
+    min) record, or plus a 1-byte E8M0 scale for MXFP4."""
+    return 17 if stack.fmt == 1 else 20
+
+
 def gate_up_bytes(stack) -> int:
     """Algorithmic bytes of one gate/up launch: W1+W3 of every distinct expert the
     step uses, the activations read and h written."""
     idx = stack.idx.cpu().numpy()
-    per_expert = 2 * (stack.I * stack.H * 5 // 8)
+    per_expert = 2 * (stack.I * stack.H * bytes_per_32(stack) // 32)
     experts = [len(set(int(e) for e in idx[l].ravel())) for l in range(stack.L)]
     P = stack.T * stack.k + (stack.T if stack.has_shared else 0)
     n = np.mean(experts) + (1 if stack.has_shared else 0)
@@ -405,7 +470,7 @@ def gate_up_bytes(stack) -> int:
 
 def down_bytes(stack) -> int:
     idx = stack.idx.cpu().numpy()
-    per_expert = stack.I * stack.H * 5 // 8
+    per_expert = stack.I * stack.H * bytes_per_32(stack) // 32
     experts = [len(set(int(e) for e in idx[l].ravel())) for l in range(stack.L)]
     P = stack.T * stack.k + (stack.T if stack.has_shared else 0)
     n = np.mean(experts) + (1 if stack.has_shared else 0)
@@ -436,6 +501,8 @@ def main():
     cfg = synth.get(args.workload)
     if cfg.streaming:
         raise SystemExit("the timed workload must be resident; streamed configurations run in the tests")
+    if cfg.fmt != 0:
+        raise SystemExit("MXFP4 workloads are measured by the run's mx leg (the per-kernel legs use format-0 calls)")
     t0 = time.time()
     log(f"building {cfg.name}: {cfg.description}")
     stack = MoEStack(cfg)
@@ -585,6 +652,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_stream:
         result["streaming"] = streaming_leg(torch, args, ms_per_step)
+    if not args.no_mx:
+        result["mx"] = mx_leg(torch, args, ms_per_step, result.get("streaming"))
     if not args.no_layer_legs:
         from routed_expert_streaming_amd import _lib as L
         result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_SPLIT, 20)

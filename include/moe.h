@@ -70,6 +70,8 @@ int moe_version(void);
 /* Bytes of one expert slab (format above; 1.875 * hidden * inter when both are
    multiples of 128).  0 if the sizes are not positive multiples of 32. */
 size_t moe_expert_bytes(int hidden, int inter);
+/* Bytes of one MXFP4 expert slab (see "MXFP4 weights" below), 0 for invalid sizes. */
+size_t moe_expert_bytes_mx(int hidden, int inter);
 
 /* ------------------------------------------------------------------ router
  * Router logits, top-k selection and renormalised gate weights (LayerStoRm
@@ -135,6 +137,7 @@ typedef struct moe_cache_desc {
     int hidden;
     int inter;
     int slots_per_layer;
+    int format; /* slab format: 0 = moe_expert_bytes slabs, 1 = MXFP4 (moe_expert_bytes_mx) */
 } moe_cache_desc;
 
 /* Validates the description (slots <= experts), checks every host slab is pinned
@@ -295,6 +298,31 @@ int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w
  * pointers, caller-owned.  MOE_E_ARG for T < 0, H <= 0, eps outside [0, 1] or a
  * NULL resid / x_next (T = 0 is a no-op). */
 int moe_residual_norm(const uint16_t *add, float *resid, int T, int H, float eps, uint16_t *x_next, void *stream);
+
+/* ------------------------------------------------------------------ MXFP4 weights
+ * A second expert weight format (the pages name MXFP4 decode paths among their
+ * kernels' sources: LayerStoRm README, "License and attributions"; encodings per
+ * the OCP Microscaling Formats v1.0 spec): per 32-column block 32 E2M1 codes and
+ * one E8M0 scale byte v, W = E2M1(q) * 2^(v-127) (v = 255 gives NaN).  A row of K
+ * columns is K/2 code bytes (byte b: column 2b in bits 0-3, 2b+1 in bits 4-7)
+ * then K/32 scale bytes, zero-padded to 16 bytes; the slab holds the I row pairs
+ * (W1 row r, W3 row r) then the H rows of W2, moe_expert_bytes_mx(H, I) bytes
+ * (17/32 byte per weight for H, I multiples of 512).  The kernels dequantise with
+ * gfx950's scaled FP4-to-bf16 convert (exact) and compute as for format 0: fp32
+ * sums, h rounded once to bf16, fixed-order combine.
+ *
+ * One token only (T = 1; T = 0 is a no-op; MOE_E_SHAPE for T > 1 or other
+ * shapes: H in {2048, 4096, 6144} (routed variant: 2048, 4096), I in {1536, 2048},
+ * k + shared <= 16).  Arguments, workspace and errors otherwise as
+ * moe_expert_ffn_combine (no path argument) and moe_route_ffn_combine.  A cache
+ * of MXFP4 slabs sets format = 1 in its descriptor. */
+int moe_mx_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
+                              const float *topk_w, int k, const void *const *expert_table, const void *shared_slab,
+                              uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+int moe_mx_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias, int E,
+                             int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
+                             float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes,
+                             const void *prefetch, size_t prefetch_bytes, void *stream);
 
 /* ------------------------------------------------------------------ CPU lane
  * Routed experts computed on host cores from the pinned host expert pool while

@@ -30,7 +30,7 @@ class MoEError(RuntimeError):
 
 class moe_cache_desc(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int), ("n_experts", ctypes.c_int), ("hidden", ctypes.c_int),
-                ("inter", ctypes.c_int), ("slots_per_layer", ctypes.c_int)]
+                ("inter", ctypes.c_int), ("slots_per_layer", ctypes.c_int), ("format", ctypes.c_int)]
 
 
 def lib():
@@ -81,6 +81,9 @@ def lib():
             "moe_combine": ([vp, vp, i, i, i, i, vp, vp], i),
             "moe_residual_norm": ([vp, vp, i, i, ctypes.c_float, vp, vp], i),
             "moe_debug_dequant": ([vp, i, i, i, vp, vp], i),
+            "moe_expert_bytes_mx": ([i, i], sz),
+            "moe_mx_expert_ffn_combine": ([vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, vp], i),
+            "moe_mx_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp], i),
             "moe_cpu_lane_create": ([i, ctypes.POINTER(vp)], i),
             "moe_cpu_lane_submit": ([vp, vp, i, i, i, vp, vp, u64p], i),
             "moe_cpu_lane_wait": ([vp, ctypes.c_uint64], i),
@@ -356,3 +359,23 @@ def moe_cpu_lane_isa() -> int:
 
 def moe_cpu_lane_force_isa(lane, isa: int):
     _check(lib().moe_cpu_lane_force_isa(lane, isa), "moe_cpu_lane_force_isa")
+
+
+# ----------------------------------------------------------------------- MXFP4 weights
+def moe_expert_bytes_mx(H: int, I: int) -> int:
+    return lib().moe_expert_bytes_mx(H, I)
+
+
+def moe_mx_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, workspace,
+                              workspace_bytes, stream=None):
+    _check(lib().moe_mx_expert_ffn_combine(_ptr(x), T, H, I, E, _ptr(topk_idx), _ptr(topk_w), k, _ptr(expert_table),
+                                           _ptr(shared_slab), _ptr(out), _ptr(workspace), workspace_bytes,
+                                           _stream(stream)), "moe_mx_expert_ffn_combine")
+
+
+def moe_mx_route_ffn_combine(x, T, H, I, w_router, bias, E, k, expert_table, shared_slab, topk_idx, topk_w, out,
+                             workspace, workspace_bytes, stream=None, prefetch=None, prefetch_bytes=0):
+    _check(lib().moe_mx_route_ffn_combine(_ptr(x), T, H, I, _ptr(w_router), _ptr(bias), E, k, _ptr(expert_table),
+                                          _ptr(shared_slab), _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(workspace),
+                                          workspace_bytes, _ptr(prefetch), prefetch_bytes, _stream(stream)),
+           "moe_mx_route_ffn_combine")

@@ -66,6 +66,15 @@ __device__ __forceinline__ uint32_t load_stream_u32(const void *p) {
     return *g;
 #endif
 }
+__device__ __forceinline__ uint32_t load_stream_u8(const void *p) {
+    typedef __attribute__((address_space(1))) const uint8_t moe_gu8;
+    const moe_gu8 *g = (const moe_gu8 *)p;
+#if MOE_STREAM_NT
+    return __builtin_nontemporal_load(g);
+#else
+    return *g;
+#endif
+}
 // Plain global loads of small operands (activations, tables).
 __device__ __forceinline__ uint4 load_global_u4(const void *p) {
     const moe_u32x4 v = *(const moe_gu32x4 *)p;

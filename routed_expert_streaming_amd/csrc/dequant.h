@@ -30,6 +30,12 @@ struct MatRows {
     const uint8_t *row0;
     size_t stride;
 };
+// MXFP4 rows (weight format 1): K/2 E2M1 code bytes then K/32 E8M0 scale bytes,
+// padded to a multiple of 16 bytes; same slab arrangement.
+__host__ __device__ constexpr size_t mx_row_bytes(int K) { return ((size_t)K / 2 + (size_t)K / 32 + 15) / 16 * 16; }
+template <int FMT>
+__host__ __device__ constexpr size_t row_bytes_fmt(int K) { return FMT == 1 ? mx_row_bytes(K) : slab_row_bytes(K); }
+
 __device__ __forceinline__ MatRows slab_w1(const uint8_t *slab, int H, int) { return {slab, 2 * slab_row_bytes(H)}; }
 __device__ __forceinline__ MatRows slab_w3(const uint8_t *slab, int H, int) {
     return {slab + slab_row_bytes(H), 2 * slab_row_bytes(H)};
@@ -109,4 +115,30 @@ __device__ __forceinline__ float moe_group_sum(float v) {
 template <int W>
 __device__ __forceinline__ bool moe_group_sum_owner(int lane_in_group) {
     return (W == 16 || W == 64) ? lane_in_group == W - 1 : lane_in_group == 0;
+}
+
+// MXFP4 block: sum over 32 columns of E2M1(q) * x, with x in natural column
+// order (xb[j] holds columns 8j .. 8j+7 as bf16 pairs).  Each code byte becomes
+// two bf16 values (low nibble first) through gfx950's scaled FP4 convert with
+// scale 1 (exact: an E2M1 value has two significant bits), then
+// v_dot2_f32_bf16; two interleaved accumulators as in moe_block_dot.
+__device__ __forceinline__ float moe_mx_block_dot(const uint4 c, const uint4 *xb) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 X = xb[j];
+        float a = acc[j & 1];
+        a = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 0)), X.x, a);
+        a = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 1)), X.y, a);
+        a = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 2)), X.z, a);
+        a = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 3)), X.w, a);
+        acc[j & 1] = a;
+    }
+    return acc[0] + acc[1];
+}
+
+// block value from the E8M0 scale byte v: acc * 2^(v - 127) (v = 255: NaN)
+__device__ __forceinline__ float moe_mx_block_value(uint32_t v, float acc) {
+    return v == 255u ? __builtin_nanf("") : ldexpf(acc, (int)v - 127);
 }

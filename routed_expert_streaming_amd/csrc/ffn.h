@@ -20,6 +20,7 @@ struct FfnArgs {
     float *y;                   // [T*k + T*shared, H] fp32 expert outputs
     const uint8_t **pair_slab;  // [T*k + T*shared] or nullptr: slab of each pair (nullptr = masked),
                                 // written by the one-token gate/up kernel, read by the down kernel
+    int fmt;                    // expert weight format: 0 = fp16 scale/min blocks, 1 = MXFP4 (one-token decode only)
     int min_m, max_m;           // grouped kernels skip groups with fewer / more tokens than these
     const uint8_t *prefetch;    // or nullptr: bytes the one-token down kernel reads into the device caches
     size_t prefetch_bytes;      // for the caller's next call (read and discarded, 1 KB per wave)

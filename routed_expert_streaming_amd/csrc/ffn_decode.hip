@@ -245,7 +245,7 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 // routing: they request their first unit before the top-k.  Lane g holds the
 // slab of group g and a group's slab is read with v_readlane (no LDS, no
 // barrier).
-template <int BPL, int D, int PER>
+template <int BPL, int D, int PER, int FMT = 0>
 __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, moe::RouteArgs ra, int n_waves) {
     const int H = a.H, I = a.I, nblk = H >> 5, k = a.k;
     const int hs = a.shared ? 1 : 0;
@@ -264,8 +264,11 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
     const int w0 = blockIdx.x * 4 + wave;
     const int n = w0 < Q ? (Q - w0 + n_waves - 1) / n_waves : 0;  // units of this wave
     const int dg = n_waves / I, dr = n_waves - dg * I;              // cursor step in (group, row)
-    const uint32_t rs = (uint32_t)moe::slab_row_bytes(H);  // W1 row r at slab + 2*rs*r, W3 row r right after it
-    const uint32_t code_off = 16u * lane, rec_off = (uint32_t)(H / 2) + 4u * lane;
+    const uint32_t rs = (uint32_t)moe::row_bytes_fmt<FMT>(H);  // W1 row r at slab + 2*rs*r, W3 row r right after it
+    // block lane + 64b: its codes at 16 bytes per block, its record (4 bytes; an
+    // MXFP4 scale: 1 byte) after the row's codes
+    constexpr uint32_t RB = FMT == 1 ? 1u : 4u;
+    const uint32_t code_off = 16u * lane, rec_off = (uint32_t)(H / 2) + RB * lane;
 
     uint4 c0[D][BPL], c1[D][BPL];
     uint32_t p0[D][BPL], p1[D][BPL];
@@ -275,9 +278,14 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             c0[j][b] = load_stream_u4(w1 + (code_off + 1024u * b));
-            p0[j][b] = load_stream_u32(w1 + (rec_off + 256u * b));
             c1[j][b] = load_stream_u4(w1 + (rs + code_off + 1024u * b));
-            p1[j][b] = load_stream_u32(w1 + (rs + rec_off + 256u * b));
+            if constexpr (FMT == 1) {
+                p0[j][b] = load_stream_u8(w1 + (rec_off + 64u * b));
+                p1[j][b] = load_stream_u8(w1 + (rs + rec_off + 64u * b));
+            } else {
+                p0[j][b] = load_stream_u32(w1 + (rec_off + 256u * b));
+                p1[j][b] = load_stream_u32(w1 + (rs + rec_off + 256u * b));
+            }
         }
     };
     auto advance_issue = [&]() {
@@ -404,7 +412,15 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
     uint4 X[BPL][4];
     float S[BPL];
 #pragma unroll
-    for (int b = 0; b < BPL; ++b) S[b] = block_pairs(xd[b], X[b]);
+    for (int b = 0; b < BPL; ++b) {
+        if constexpr (FMT == 1) {  // natural column order, no block sums
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[b][j] = xd[b][j];
+            S[b] = 0.0f;
+        } else {
+            S[b] = block_pairs(xd[b], X[b]);
+        }
+    }
 
     // Each unit's two sums go to lane (unit index mod 64); SiLU, rounding and the
     // store then run once for up to 64 units in parallel instead of once per unit
@@ -425,8 +441,13 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
                 float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
                 for (int b = 0; b < BPL; ++b) {
-                    v0 += moe_block_value(p0[j][b], moe_block_dot(c0[j][b], X[b], 1, magic), S[b]);
-                    v1 += moe_block_value(p1[j][b], moe_block_dot(c1[j][b], X[b], 1, magic), S[b]);
+                    if constexpr (FMT == 1) {
+                        v0 += moe_mx_block_value(p0[j][b], moe_mx_block_dot(c0[j][b], X[b]));
+                        v1 += moe_mx_block_value(p1[j][b], moe_mx_block_dot(c1[j][b], X[b]));
+                    } else {
+                        v0 += moe_block_value(p0[j][b], moe_block_dot(c0[j][b], X[b], 1, magic), S[b]);
+                        v1 += moe_block_value(p1[j][b], moe_block_dot(c1[j][b], X[b], 1, magic), S[b]);
+                    }
                 }
                 v0 = moe_group_sum<64>(v0);
                 v1 = moe_group_sum<64>(v1);
@@ -611,7 +632,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
 constexpr int kDown1MaxRows = 64;  // rows per workgroup
 constexpr int kDown1MaxPairs = 16;
 
-template <int BPL, int D, bool COMBINE>
+template <int BPL, int D, bool COMBINE, int FMT = 0>
 __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, const float *__restrict__ topk_w,
                                                             uint16_t *__restrict__ out, int rows_per_wg) {
     const int H = a.H, I = a.I, k = a.k;
@@ -661,9 +682,10 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
 
     if (slab) {
         const uint32_t magic = moe_magic_vgpr();
-        const uint8_t *w2 = slab + (size_t)I * 2 * moe::slab_row_bytes(H);  // W2 row 0
-        const uint32_t rs2 = (uint32_t)moe::slab_row_bytes(I);
-        const uint32_t code_off = 16u * c, rec_off = (uint32_t)(I / 2) + 4u * c;
+        const uint8_t *w2 = slab + (size_t)I * 2 * moe::row_bytes_fmt<FMT>(H);  // W2 row 0
+        const uint32_t rs2 = (uint32_t)moe::row_bytes_fmt<FMT>(I);
+        constexpr uint32_t RB = FMT == 1 ? 1u : 4u;  // record bytes per block
+        const uint32_t code_off = 16u * c, rec_off = (uint32_t)(I / 2) + RB * c;
         uint4 cw[D][BPL];
         uint32_t pw[D][BPL];
         int ui = 0;
@@ -674,7 +696,10 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
 #pragma unroll
             for (int b = 0; b < BPL; ++b) {
                 cw[j][b] = load_stream_u4(w2 + (rrow + code_off + 256u * b));
-                pw[j][b] = load_stream_u32(w2 + (rrow + rec_off + 64u * b));
+                if constexpr (FMT == 1)
+                    pw[j][b] = load_stream_u8(w2 + (rrow + rec_off + 16u * b));
+                else
+                    pw[j][b] = load_stream_u32(w2 + (rrow + rec_off + 64u * b));
             }
             ++ui;
         };
@@ -685,7 +710,15 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
         uint4 X[BPL][4];
         float S[BPL];
 #pragma unroll
-        for (int b = 0; b < BPL; ++b) S[b] = block_pairs(hd[b], X[b]);
+        for (int b = 0; b < BPL; ++b) {
+            if constexpr (FMT == 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) X[b][j] = hd[b][j];
+                S[b] = 0.0f;
+            } else {
+                S[b] = block_pairs(hd[b], X[b]);
+            }
+        }
 
         for (int base = 0; base < U; base += D) {
 #pragma unroll
@@ -694,8 +727,12 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
                 const int rl = sub + 4 * (base + j), row = r0 + rl;
                 float v = 0.0f;
 #pragma unroll
-                for (int b = 0; b < BPL; ++b)
-                    v += moe_block_value(pw[j][b], moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
+                for (int b = 0; b < BPL; ++b) {
+                    if constexpr (FMT == 1)
+                        v += moe_mx_block_value(pw[j][b], moe_mx_block_dot(cw[j][b], X[b]));
+                    else
+                        v += moe_block_value(pw[j][b], moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
+                }
                 v = moe_group_sum<16>(v);
                 if (c == 15 && row < H) {
                     if (COMBINE)
@@ -770,7 +807,7 @@ int launch_gate_up(const moe::FfnArgs &a, hipStream_t s) {
 #define MOE_DECODE1_WG_PER_CU 2  // workgroups per CU for the one-token gate/up kernel
 #endif
 
-template <int BPL, int D>
+template <int BPL, int D, int FMT = 0>
 int launch_gate_up1(const moe::FfnArgs &a, const moe::RouteArgs *ra, hipStream_t s) {
     const int G = a.n_routed_groups + (a.shared ? 1 : 0);
     const long long Q = (long long)G * a.I;
@@ -778,13 +815,13 @@ int launch_gate_up1(const moe::FfnArgs &a, const moe::RouteArgs *ra, hipStream_t
     const int grid = (int)((std::min(Q, target) + 3) / 4);
     const moe::RouteArgs none{};
     if (!ra)
-        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 0>), dim3(grid), dim3(256), 0, s, a, none, grid * 4);
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 0, FMT>), dim3(grid), dim3(256), 0, s, a, none, grid * 4);
     else if (ra->E <= 64)
-        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 1>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 1, FMT>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
     else if (ra->E <= 128)
-        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 2>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 2, FMT>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
     else
-        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 4>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
+        hipLaunchKernelGGL((decode1_gate_up_kernel<BPL, D, 4, FMT>), dim3(grid), dim3(256), 0, s, a, *ra, grid * 4);
     MOE_LAUNCH_CHECK("decode1_gate_up_kernel");
     return MOE_OK;
 }
@@ -819,16 +856,16 @@ int launch_down(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipSt
 #define MOE_DOWN1_D 1  // units in flight per lane group, one-token down kernel
 #endif
 
-template <int BPL>
+template <int BPL, int FMT = 0>
 int launch_down1(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s) {
     static_assert(MOE_DOWN1_ROWS % 4 == 0 && MOE_DOWN1_ROWS <= kDown1MaxRows, "rows per workgroup");
     const int P = a.k + (a.shared ? 1 : 0);
     const int grid = (a.H + MOE_DOWN1_ROWS - 1) / MOE_DOWN1_ROWS;
     if (out)
-        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, true>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
+        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, true, FMT>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
                            out, MOE_DOWN1_ROWS);
     else
-        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, false>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
+        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, false, FMT>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
                            out, MOE_DOWN1_ROWS);
     MOE_LAUNCH_CHECK("decode1_down_kernel");
     return MOE_OK;
@@ -873,6 +910,13 @@ bool decode1_publishes_slabs(const FfnArgs &a) {
 
 int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s) {
     if (ra.nslices > 4) return fail(MOE_E_SHAPE, "routed gate/up: H=%d above 4096", a.H);
+    if (a.fmt == 1) {
+        switch (a.H >> 5) {
+            case 128: return launch_gate_up1<2, MOE_DECODE1_D_ROUTED, 1>(a, &ra, s);
+            case 64: return launch_gate_up1<1, 6, 1>(a, &ra, s);
+            default: return fail(MOE_E_SHAPE, "routed gate/up (MXFP4): H=%d not supported", a.H);
+        }
+    }
     switch (a.H >> 5) {
         case 128: return launch_gate_up1<2, MOE_DECODE1_D_ROUTED>(a, &ra, s);
         case 64: return launch_gate_up1<1, 6>(a, &ra, s);
@@ -881,6 +925,15 @@ int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s)
 }
 
 int decode_gate_up(const FfnArgs &a, hipStream_t s) {
+    if (a.fmt == 1) {
+        if (a.T == 1)
+            switch (a.H >> 5) {
+                case 128: return launch_gate_up1<2, MOE_DECODE1_D, 1>(a, nullptr, s);
+                case 192: return launch_gate_up1<3, 3, 1>(a, nullptr, s);
+                case 64: return launch_gate_up1<1, 6, 1>(a, nullptr, s);
+            }
+        return fail(MOE_E_SHAPE, "gate/up (MXFP4): one token with H 2048, 4096 or 6144 only (T=%d, H=%d)", a.T, a.H);
+    }
     if (a.T == 1) {
         switch (a.H >> 5) {
             case 128: return launch_gate_up1<2, MOE_DECODE1_D>(a, nullptr, s);
@@ -899,6 +952,14 @@ int decode_gate_up(const FfnArgs &a, hipStream_t s) {
 }
 
 int decode_down(const FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s) {
+    if (a.fmt == 1) {
+        if (a.T == 1 && !a.grouped && a.k + (a.shared ? 1 : 0) <= kDown1MaxPairs)
+            switch (a.I >> 5) {
+                case 48: return launch_down1<3, 1>(a, topk_w, out, s);
+                case 64: return launch_down1<4, 1>(a, topk_w, out, s);
+            }
+        return fail(MOE_E_SHAPE, "down (MXFP4): one token with I 1536 or 2048 only (T=%d, I=%d)", a.T, a.I);
+    }
     if (a.T == 1 && a.k + (a.shared ? 1 : 0) <= kDown1MaxPairs) {
         switch (a.I >> 5) {
             case 48: return launch_down1<3>(a, topk_w, out, s);

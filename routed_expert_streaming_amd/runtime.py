@@ -140,8 +140,11 @@ class MoEStack:
         torch.cuda.set_device(self.dev)
         self.copy_stream = torch.cuda.Stream(self.dev)  # default priority
         self.copy_stream2 = torch.cuda.Stream(self.dev) if split_copies else None
-        self.slab = L.moe_expert_bytes(self.H, self.I)
-        assert self.slab == synth.slab_bytes(self.H, self.I)
+        self.fmt = cfg.fmt  # 0: fp16 scale/min blocks; 1: MXFP4 (one-token decode entry points)
+        if self.fmt == 1 and cfg.tokens != 1:
+            raise ValueError("MXFP4 stacks run the one-token decode entry points only (tokens = 1)")
+        self.slab = L.moe_expert_bytes_mx(self.H, self.I) if self.fmt else L.moe_expert_bytes(self.H, self.I)
+        assert self.slab == synth.slab_bytes(self.H, self.I, self.fmt)
         Lyr, T, H, I, E, k = self.L, self.T, self.H, self.I, self.E, self.k
 
         # router weights and bias
@@ -156,10 +159,9 @@ class MoEStack:
         self.shared = None
         if self.has_shared:
             stage = PinnedHost(Lyr * self.slab)
-            synth.fill_slabs(cfg.seed, 0, [synth.shared_expert_id(cfg)], H, I, [stage.ptr], threads)
-            for l in range(1, Lyr):
+            for l in range(Lyr):
                 synth.fill_slabs(cfg.seed, l, [synth.shared_expert_id(cfg)], H, I, [stage.ptr + l * self.slab],
-                                 threads)
+                                 threads, self.fmt)
             self.shared = torch.empty((Lyr, self.slab), dtype=torch.uint8, device=self.dev)
             self.shared.view(-1).copy_(torch.from_numpy(stage.array[:Lyr * self.slab]), non_blocking=False)
             stage.free()
@@ -172,7 +174,7 @@ class MoEStack:
             stage = PinnedHost(E * self.slab)
             for l in range(Lyr):
                 synth.fill_slabs(cfg.seed, l, list(range(E)), H, I,
-                                 [stage.ptr + e * self.slab for e in range(E)], threads)
+                                 [stage.ptr + e * self.slab for e in range(E)], threads, self.fmt)
                 self.pool[l * E:(l + 1) * E].view(-1).copy_(torch.from_numpy(stage.array[:E * self.slab]))
             stage.free()
             base = self.pool.data_ptr()
@@ -184,12 +186,12 @@ class MoEStack:
             self.host = [PinnedHost(E * self.slab) for _ in range(Lyr)]
             for l in range(Lyr):
                 synth.fill_slabs(cfg.seed, l, list(range(E)), H, I,
-                                 [self.host[l].ptr + e * self.slab for e in range(E)], threads)
+                                 [self.host[l].ptr + e * self.slab for e in range(E)], threads, self.fmt)
             self.pool = torch.empty((Lyr * self.C, self.slab), dtype=torch.uint8, device=self.dev)
             self.table = torch.zeros((Lyr, E), dtype=torch.int64, device=self.dev)
             self._host_ptrs = (ctypes.c_void_p * (Lyr * E))(
                 *[self.host[l].ptr + e * self.slab for l in range(Lyr) for e in range(E)])
-            desc = L.moe_cache_desc(Lyr, E, H, I, self.C)
+            desc = L.moe_cache_desc(Lyr, E, H, I, self.C, self.fmt)
             torch.cuda.synchronize(self.dev)
             self.cache = L.moe_cache_create(desc, ctypes.addressof(self._host_ptrs), self.pool, self.table,
                                             self.copy_stream)
@@ -254,12 +256,18 @@ class MoEStack:
                                  self.router_ws, self.router_ws_bytes, self.stream)
 
     def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True):
+        self._format0_only("ffn (masked FFN into y)")
         L.moe_expert_ffn(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l],
                          self.shared[l] if (self.has_shared and shared) else None, mask, self.y, self.ffn_ws,
                          self.ffn_ws_bytes, self.path, self.stream)
 
     def ffn_combine(self, x: torch.Tensor, l: int, out: torch.Tensor):
         """Gate/up, down and the weighted combine of layer l (every needed expert resident)."""
+        if self.fmt:
+            L.moe_mx_expert_ffn_combine(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.w[l], self.k,
+                                        self.table[l], self.shared[l] if self.has_shared else None, out[l],
+                                        self.ffn_ws, self.ffn_ws_bytes, self.stream)
+            return
         L.moe_expert_ffn_combine(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.w[l], self.k,
                                  self.table[l], self.shared[l] if self.has_shared else None, out[l], self.ffn_ws,
                                  self.ffn_ws_bytes, self.path, self.stream)
@@ -270,7 +278,8 @@ class MoEStack:
         after the last) into the device caches while it runs: they are static, so
         this does not depend on the next layer's input."""
         nxt = self.wr[(l + 1) % self.L]
-        L.moe_route_ffn_combine(x[l], self.T, self.H, self.I, self.wr[l], None if self.bias is None else self.bias[l],
+        call = L.moe_mx_route_ffn_combine if self.fmt else L.moe_route_ffn_combine
+        call(x[l], self.T, self.H, self.I, self.wr[l], None if self.bias is None else self.bias[l],
                                 self.E, self.k, self.table[l], self.shared[l] if self.has_shared else None,
                                 self.idx[l], self.w[l], out[l], self.layer_ws, self.layer_ws_bytes, self.stream,
                                 prefetch=nxt, prefetch_bytes=nxt.numel() * 4)
@@ -278,14 +287,22 @@ class MoEStack:
     def combine(self, l: int, out: torch.Tensor):
         L.moe_combine(self.y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l], self.stream)
 
+    def _format0_only(self, what: str):
+        # the format-0 kernels read format-0 row sizes: on MXFP4 slabs they would
+        # read past the end of each slab
+        if self.fmt != 0:
+            raise ValueError(f"{what} runs format-0 kernels; this stack holds MXFP4 slabs")
+
     def gate_up_only(self, x: torch.Tensor, l: int, h: torch.Tensor):
         """Only the dequant + gate/up + SwiGLU kernel of layer l (pair grouping), for timing it."""
+        self._format0_only("gate_up_only")
         L.moe_expert_gate_up(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
                              self.table[l], self.shared[l] if self.has_shared else None, None, h,
                              L.MOE_FFN_PAIRS, self.stream)
 
     def down_only(self, h: torch.Tensor, l: int):
         """Only the dequant + down-projection kernel of layer l (pair grouping), for timing it."""
+        self._format0_only("down_only")
         L.moe_expert_down(h, self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
                           self.table[l], self.shared[l] if self.has_shared else None, None, self.y,
                           L.MOE_FFN_PAIRS, self.stream)
@@ -309,7 +326,7 @@ class MoEStack:
     # ------------------------------------------------------------------ CPU lane
     def enable_cpu_lane(self, threads: int):
         """Start a CPU lane of `threads` workers (streamed stacks only) and calibrate it."""
-        assert self.streaming and self.lane is None
+        assert self.streaming and self.lane is None and self.fmt == 0
         P = self.T * self.k + (self.T if self.has_shared else 0)
         self.lane = L.moe_cpu_lane_create(threads)
         self.lane_threads = threads
@@ -558,9 +575,9 @@ class MoEStack:
     # ------------------------------------------------------------------ host copies for checking
     def host_slabs(self, l: int):
         """Routed slabs of layer l as host numpy arrays (regenerated from the seed)."""
-        return [synth.expert_slab(self.cfg.seed, l, e, self.H, self.I) for e in range(self.E)]
+        return [synth.expert_slab(self.cfg.seed, l, e, self.H, self.I, self.fmt) for e in range(self.E)]
 
     def host_shared(self, l: int):
         if not self.has_shared:
             return None
-        return synth.expert_slab(self.cfg.seed, l, synth.shared_expert_id(self.cfg), self.H, self.I)
+        return synth.expert_slab(self.cfg.seed, l, synth.shared_expert_id(self.cfg), self.H, self.I, self.fmt)

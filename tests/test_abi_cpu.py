@@ -4,6 +4,8 @@ import os
 import random
 import re
 
+import numpy as np
+
 import pytest
 
 from routed_expert_streaming_amd import _lib as L
@@ -327,3 +329,32 @@ def test_split_copies_validation_and_state():
         L.moe_cache_split_copies(c, None)
     finally:
         L.moe_cache_destroy(c)
+
+
+def test_mx_sizes_and_validation():
+    """MXFP4 slab sizes, and the one-token entry points' checks (no kernel runs)."""
+    assert L.moe_expert_bytes_mx(4096, 1536) == 3 * 4096 * 1536 * 17 // 32
+    assert L.moe_expert_bytes_mx(96, 64) == 2 * 64 * 64 + 96 * 48  # rows of 51 -> 64 and 34 -> 48 bytes
+    assert L.moe_expert_bytes_mx(100, 64) == 0
+    ws = np.zeros(1 << 20, np.uint8)
+    x = np.zeros((2, 4096), np.uint16)
+    idx = np.zeros((2, 8), np.int32)
+    w = np.zeros((2, 8), np.float32)
+    out = np.zeros((2, 4096), np.uint16)
+    table = np.zeros(128, np.int64)
+    # T = 0: no-op; T = 2: MXFP4 slabs need one token
+    L.moe_mx_expert_ffn_combine(x, 0, 4096, 1536, 128, idx, w, 8, table, None, out, ws, ws.size)
+    with pytest.raises(L.MoEError) as e:
+        L.moe_mx_expert_ffn_combine(x, 2, 4096, 1536, 128, idx, w, 8, table, None, out, ws, ws.size)
+    assert e.value.status == L.MOE_E_SHAPE
+    with pytest.raises(L.MoEError) as e:  # I = 1024 has no MXFP4 down kernel
+        L.moe_mx_expert_ffn_combine(x, 1, 4096, 1024, 128, idx, w, 8, table, None, out, ws, ws.size)
+    assert e.value.status == L.MOE_E_SHAPE
+    wr = np.zeros((128, 4096), np.float32)
+    with pytest.raises(L.MoEError) as e:
+        L.moe_mx_route_ffn_combine(x, 2, 4096, 1536, wr, None, 128, 8, table, None, idx, w, out, ws, ws.size)
+    assert e.value.status == L.MOE_E_SHAPE
+    d = L.moe_cache_desc(1, 4, 64, 32, 2, 2)
+    with pytest.raises(L.MoEError) as e:
+        L.moe_cache_create_recording(d)
+    assert e.value.status == L.MOE_E_ARG
