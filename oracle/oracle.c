@@ -29,6 +29,15 @@
  * 32 E2M1 codes q (sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0;
  * exponent 0 is subnormal: 0 or 0.5), W = E2M1(q) * 2^(v-127).  A K-column row
  * is K/2 code bytes (same nibble order) then K/32 scale bytes, padded to 16.
+ *
+ * Weight format 2, k-quant-style super-blocks (the pages' own weights are a
+ * 4-bit k-quant GGUF variant: LayerStoRm README, "TL;DR" and "Serve"): per
+ * 256-column super-block an fp16 d and fp16 dmin and, for each of its eight
+ * 32-column blocks j, a 6-bit scale code s_j and a 6-bit min code m_j;
+ * W = d*s_j*q - dmin*m_j.  A K-column row (K % 256 == 0) is K/2 code bytes then
+ * one 16-byte header per super-block: d, dmin, then the eight s_j (bytes 4-9)
+ * and the eight m_j (bytes 10-15), code j in bits 6j..6j+5 of each 48-bit
+ * little-endian field.
  * The *_fmt functions take the format; the others are format 0.
  */
 #include <math.h>
@@ -87,12 +96,21 @@ uint16_t oracle_double_to_bf16(double v) {
 /* A row of K columns: K/2 code bytes, K/32 records of 4 bytes, zero padding to a multiple of 16. */
 static int g_fmt = 0; /* weight format of the call in progress (set by the *_fmt entry points) */
 static int64_t row_bytes_f(int64_t cols, int fmt) {
+    if (fmt == 2) return cols / 2 + cols / 16;
     return fmt == 1 ? (cols / 2 + cols / 32 + 15) / 16 * 16 : (cols / 2 + (cols / 32) * 4 + 15) / 16 * 16;
+}
+
+/* 6-bit code j of a 48-bit little-endian field. */
+static unsigned field6(const uint8_t *f, int j) {
+    uint64_t v = 0;
+    for (int b = 0; b < 6; ++b) v |= (uint64_t)f[b] << (8 * b);
+    return (unsigned)((v >> (6 * j)) & 63);
 }
 static int64_t row_bytes(int64_t cols) { return row_bytes_f(cols, g_fmt); }
 
 int64_t oracle_slab_bytes(int64_t H, int64_t I) { return 2 * I * row_bytes_f(H, 0) + H * row_bytes_f(I, 0); }
 int64_t oracle_slab_bytes_fmt(int64_t H, int64_t I, int fmt) {
+    if (fmt == 2 && (H % 256 || I % 256)) return 0;
     return 2 * I * row_bytes_f(H, fmt) + H * row_bytes_f(I, fmt);
 }
 
@@ -115,6 +133,18 @@ static const uint8_t *matrix_row(const uint8_t *slab, int64_t H, int64_t I, int 
 
 /* Dequantise one row (K = cols columns, starting at `row`) into out[cols]. */
 static void dequant_row(const uint8_t *row, int64_t cols, double *out) {
+    if (g_fmt == 2) {
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t byte = row[c / 2];
+            int q = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+            const uint8_t *h = row + cols / 2 + 16 * (c / 256);
+            const int j = (int)((c / 32) % 8);
+            double d = oracle_fp16_to_double((uint16_t)(h[0] | (h[1] << 8)));
+            double dmin = oracle_fp16_to_double((uint16_t)(h[2] | (h[3] << 8)));
+            out[c] = d * field6(h + 4, j) * q - dmin * field6(h + 10, j);
+        }
+        return;
+    }
     if (g_fmt == 1) {
         for (int64_t c = 0; c < cols; ++c) {
             uint8_t byte = row[c / 2];

@@ -32,6 +32,14 @@
  * E8M0 block scales, zero-padded to a multiple of 16 bytes (17/32 byte per
  * weight when K % 512 == 0).  Codes uniform on 0..15; scale byte of block b =
  * 120 + (byte b%16 of Philox call b/16) mod 3, i.e. 2^-7, 2^-6 or 2^-5.
+ *
+ * Weight format 2 (super-blocks of 256 columns, k-quant style): a K-column row
+ * (K % 256 == 0) is K/2 code bytes (same nibble order), then one 16-byte header
+ * per 256-column super-block: fp16 d (bytes 0-1), fp16 dmin (bytes 2-3), eight
+ * 6-bit scale codes (bytes 4-9, code j in bits 6j..6j+5 of that little-endian
+ * 48-bit field) and eight 6-bit min codes (bytes 10-15, likewise); 0.5625*K
+ * bytes.  Codes uniform on 0..15; d = fp16(0.0002 * (1 + |N(0,1)|)), dmin =
+ * fp16(4 * d); scale codes uniform on 16..63, min codes uniform on 0..63.
  */
 #include <math.h>
 #include <stdint.h>
@@ -290,7 +298,9 @@ void synth_expert_slab(uint64_t seed, uint32_t layer, uint32_t expert, int64_t H
 static int64_t row_bytes_fmt(int64_t cols, int fmt) {
     return fmt == 1 ? (cols / 2 + cols / 32 + 15) / 16 * 16 : row_bytes(cols);
 }
+int64_t synth_slab_bytes_sb(int64_t H, int64_t I);
 int64_t synth_slab_bytes_fmt(int64_t H, int64_t I, int fmt) {
+    if (fmt == 2) return (H % 256 || I % 256) ? 0 : synth_slab_bytes_sb(H, I);
     return 2 * I * row_bytes_fmt(H, fmt) + H * row_bytes_fmt(I, fmt);
 }
 
@@ -317,15 +327,19 @@ static void fill_matrix_part_mx(uint64_t seed, uint32_t layer, uint32_t expert, 
     }
 }
 
+static void fill_matrix_part_sb(uint64_t, uint32_t, uint32_t, uint32_t, int64_t, int64_t, uint8_t *, int64_t,
+                                int64_t, int64_t);
+static int64_t row_bytes_sb(int64_t cols);
+
 void synth_expert_slabs_fmt(uint64_t seed, uint32_t layer, const uint32_t *experts, int64_t n, int64_t H,
                             int64_t I, uint8_t *const *outs, int nthreads, int fmt) {
-    if (fmt != 1) {
+    if (fmt != 1 && fmt != 2) {
         synth_expert_slabs(seed, layer, experts, n, H, I, outs, nthreads);
         return;
     }
     nthreads = clamp_threads(nthreads);
     const int64_t nparts = 16, njobs = n * 3 * nparts;
-    const int64_t rh = row_bytes_fmt(H, 1), ri = row_bytes_fmt(I, 1);
+    const int64_t rh = fmt == 2 ? row_bytes_sb(H) : row_bytes_fmt(H, 1), ri = fmt == 2 ? row_bytes_sb(I) : row_bytes_fmt(I, 1);
     #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
     for (int64_t job = 0; job < njobs; ++job) {
         int64_t i = job / (3 * nparts);
@@ -333,6 +347,56 @@ void synth_expert_slabs_fmt(uint64_t seed, uint32_t layer, const uint32_t *exper
         int64_t part = job % nparts;
         int64_t rows = (m < 2) ? I : H, cols = (m < 2) ? H : I;
         int64_t start = m == 0 ? 0 : m == 1 ? rh : 2 * I * rh, stride = m < 2 ? 2 * rh : ri;
-        fill_matrix_part_mx(seed, layer, experts[i], m, rows, cols, outs[i] + start, stride, part, nparts);
+        if (fmt == 2)
+            fill_matrix_part_sb(seed, layer, experts[i], m, rows, cols, outs[i] + start, stride, part, nparts);
+        else
+            fill_matrix_part_mx(seed, layer, experts[i], m, rows, cols, outs[i] + start, stride, part, nparts);
+    }
+}
+
+/* ---------------- weight format 2: 256-column super-blocks ---------------- */
+enum { KIND_SB_CODES = 8, KIND_SB_HEAD = 9 };
+static int64_t row_bytes_sb(int64_t cols) { return cols / 2 + cols / 16; }
+int64_t synth_slab_bytes_sb(int64_t H, int64_t I) { return 2 * I * row_bytes_sb(H) + H * row_bytes_sb(I); }
+
+static void put6(uint8_t *field, int j, unsigned v) {   /* 6-bit code j into a 48-bit little-endian field */
+    uint64_t f = 0;
+    for (int b = 0; b < 6; ++b) f |= (uint64_t)field[b] << (8 * b);
+    f = (f & ~((uint64_t)63 << (6 * j))) | ((uint64_t)(v & 63) << (6 * j));
+    for (int b = 0; b < 6; ++b) field[b] = (uint8_t)(f >> (8 * b));
+}
+
+static void fill_matrix_part_sb(uint64_t seed, uint32_t layer, uint32_t expert, uint32_t m, int64_t rows,
+                                int64_t cols, uint8_t *base, int64_t stride, int64_t part, int64_t nparts) {
+    const int64_t cpr = cols / 32, nsb = cols / 256;
+    const int64_t r0 = rows * part / nparts, r1 = rows * (part + 1) / nparts;
+    for (int64_t row = r0; row < r1; ++row) {
+        uint8_t *rp = base + row * stride;
+        for (int64_t ch = 0; ch < cpr; ++ch) {
+            uint32_t r[4];
+            draw(seed, KIND_SB_CODES, 0, layer, expert, m, (uint32_t)(row * cpr + ch), r);
+            memcpy(rp + 16 * ch, r, 16);
+        }
+        for (int64_t sb = 0; sb < nsb; ++sb) {
+            uint32_t r[4], r2[4];
+            draw(seed, KIND_SB_HEAD, 0, layer, expert, m, (uint32_t)(2 * (row * nsb + sb)), r);
+            draw(seed, KIND_SB_HEAD, 0, layer, expert, m, (uint32_t)(2 * (row * nsb + sb) + 1), r2);
+            uint8_t *h = rp + cols / 2 + 16 * sb;
+            memset(h, 0, 16);
+            uint16_t d = synth_double_to_fp16(0.0002 * (1.0 + fabs(normal_from(r[0], r[1]))));
+            uint32_t ex = (d >> 10) & 0x1F, mt = d & 0x3FF;
+            double dv = ex ? ldexp((double)(mt | 0x400), (int)ex - 25) : ldexp((double)mt, -24);
+            uint16_t dmin = synth_double_to_fp16(4.0 * dv);
+            h[0] = (uint8_t)(d & 0xFF);
+            h[1] = (uint8_t)(d >> 8);
+            h[2] = (uint8_t)(dmin & 0xFF);
+            h[3] = (uint8_t)(dmin >> 8);
+            uint8_t bytes[16];
+            memcpy(bytes, r2, 16);
+            for (int j = 0; j < 8; ++j) {
+                put6(h + 4, j, 16u + bytes[j] % 48u);
+                put6(h + 10, j, bytes[8 + j] % 64u);
+            }
+        }
     }
 }

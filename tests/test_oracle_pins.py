@@ -466,3 +466,54 @@ def test_mx_synth_slabs_follow_the_recipe():
     assert np.isfinite(vals).all() and np.abs(vals).max() <= 6 * 2.0 ** -5
     assert (synth.expert_slab(5, 1, 3, H, I, fmt=1) == slab).all()
     assert not (synth.expert_slab(5, 1, 4, H, I, fmt=1) == slab).all()
+
+
+# ---------------------------------------------------------------- weight format 2 (super-blocks)
+def sb_row(q, d, dmin, s, m):
+    """One super-block row from codes q [K], fp16 d/dmin per super-block and
+    6-bit codes s, m [K/256, 8], written from the layout description."""
+    q = np.asarray(q, np.uint8)
+    out = bytes((q[0::2] | (q[1::2] << 4)).astype(np.uint8))
+    for b in range(len(d)):
+        fs = sum(int(s[b][j]) << (6 * j) for j in range(8))
+        fm = sum(int(m[b][j]) << (6 * j) for j in range(8))
+        out += (np.float16(d[b]).tobytes() + np.float16(dmin[b]).tobytes() + fs.to_bytes(6, "little")
+                + fm.to_bytes(6, "little"))
+    return out
+
+
+def test_sb_dequant_matches_layout():
+    H, I = 512, 256
+    rng = np.random.default_rng(11)
+    mats = []
+    for R, K in ((I, H), (I, H), (H, I)):
+        q = rng.integers(0, 16, (R, K))
+        d = rng.uniform(1e-4, 1e-3, (R, K // 256)).astype(np.float16)
+        dmin = rng.uniform(1e-4, 1e-3, (R, K // 256)).astype(np.float16)
+        s, m = rng.integers(0, 64, (R, K // 256, 8)), rng.integers(0, 64, (R, K // 256, 8))
+        mats.append((q, d, dmin, s, m))
+    rows = [[sb_row(*(a[r] for a in mat)) for r in range(len(mat[0]))] for mat in mats]
+    slab = np.frombuffer(b"".join(rows[0][r] + rows[1][r] for r in range(I)) + b"".join(rows[2]), np.uint8).copy()
+    assert slab.size == oracle.slab_bytes(H, I, 2) == synth.slab_bytes(H, I, 2) == 3 * H * I * 9 // 16
+    for which, (q, d, dmin, s, m) in enumerate(mats):
+        R, K = q.shape
+        blk = np.arange(K) // 32
+        sbk, j = blk // 8, blk % 8
+        ref = (d.astype(np.float64)[:, sbk] * s[:, sbk, j] * q - dmin.astype(np.float64)[:, sbk] * m[:, sbk, j])
+        np.testing.assert_array_equal(oracle.dequant(slab, H, I, which, fmt=2), ref)
+    assert oracle.slab_bytes(96, 256, 2) == 0
+
+
+def test_sb_synth_slabs_follow_the_recipe():
+    H, I = 512, 256
+    slab = synth.expert_slab(9, 0, 2, H, I, fmt=2)
+    rb = H // 2 + H // 16
+    for r in (0, I - 1):
+        h = slab[2 * r * rb + H // 2:2 * r * rb + H // 2 + 16]
+        d, dmin = h[0:2].view(np.float16)[0], h[2:4].view(np.float16)[0]
+        assert np.float16(4 * np.float64(d)) == dmin and 0.0002 <= float(d) < 0.002
+        fs = int.from_bytes(bytes(h[4:10]), "little")
+        assert all(16 <= (fs >> (6 * j)) & 63 <= 63 for j in range(8))
+    w = oracle.dequant(slab, H, I, 2, fmt=2)
+    assert np.isfinite(w).all() and 0.01 < np.abs(w).max() < 1.0
+    assert (synth.expert_slab(9, 0, 2, H, I, fmt=2) == slab).all()
