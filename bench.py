@@ -63,7 +63,8 @@ def parse():
     ap.add_argument("--chain-warmup", type=int, default=32)
     ap.add_argument("--cpu-lane-threads", type=int, default=14,
                     help="worker threads of the streamed leg's CPU-lane run (0 skips it; decode workloads only)")
-    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 decode leg (resident and streamed)")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the MXFP4 and super-block decode legs (resident and streamed)")
     ap.add_argument("--no-layer-legs", action="store_true",
                     help="skip the one-resident-layer measurements of the 32-token decode and 2048-token prefill shapes")
     ap.add_argument("--traffic-calibration", action="store_true",
@@ -145,15 +146,16 @@ def resident_step_ms(torch, cfg, layers: int, steps: int = 8) -> float:
     return a.elapsed_time(b) / steps
 
 
-def mx_leg(torch, args, fmt0_ms_per_step: float, fmt0_streaming):
-    """The one-token decode with MXFP4 expert slabs (E2M1 codes, one E8M0 scale
-    per 32 weights: 17/32 byte per weight against 20/32): resident, one call per
-    layer, then streamed at the same cache cap and router bias as the format-0
-    streamed leg.  Only the MXFP4 entry points run on these slabs."""
+def format_leg(torch, args, name: str, stream_name: str, fmt0_ms_per_step: float, fmt0_streaming):
+    """The one-token decode with another expert weight format -- MXFP4 (E2M1
+    codes, one E8M0 scale per 32 weights: 17/32 byte per weight against 20/32) or
+    super-blocks (18/32) -- resident, one call per layer, then streamed at the
+    same cache cap and router bias as the format-0 streamed leg.  Only that
+    format's entry points run on these slabs."""
     import synth
     from routed_expert_streaming_amd.runtime import MoEStack
 
-    cfg = synth.get("decode1_mx")
+    cfg = synth.get(name)
     st = MoEStack(cfg)
     xs = [st.make_inputs(s) for s in range(args.inputs)]
     out = st.new_output()
@@ -175,7 +177,7 @@ def mx_leg(torch, args, fmt0_ms_per_step: float, fmt0_streaming):
     del st, xs, out
     torch.cuda.empty_cache()
     if not args.no_stream:
-        scfg = synth.get("decode1_mx_stream")
+        scfg = synth.get(stream_name)
         ss = MoEStack(scfg)
         sx = [ss.make_inputs(s) for s in range(32)]
         so = ss.new_output()
@@ -199,7 +201,7 @@ def mx_leg(torch, args, fmt0_ms_per_step: float, fmt0_streaming):
                                                    if fmt0_streaming else None),
                             "steps": args.stream_steps, "warmup": args.stream_warmup}
         ss.close()
-    log(f"mx: {res}")
+    log(f"{name}: {res}")
     return res
 
 
@@ -453,8 +455,9 @@ def counter_traffic(kernel: str):
 
 def bytes_per_32(stack) -> int:
     """Weight bytes per 32 weights: 16 code bytes plus a 4-byte (fp16 scale, fp16
-    min) record, or plus a 1-byte E8M0 scale for MXFP4."""
-    return 17 if stack.fmt == 1 else 20
+    min) record, plus a 1-byte E8M0 scale for MXFP4, plus 2 bytes (a 16-byte
+    header per 256) for super-blocks."""
+    return {0: 20, 1: 17, 2: 18}[stack.fmt]
 
 
 def gate_up_bytes(stack) -> int:
@@ -502,7 +505,8 @@ def main():
     if cfg.streaming:
         raise SystemExit("the timed workload must be resident; streamed configurations run in the tests")
     if cfg.fmt != 0:
-        raise SystemExit("MXFP4 workloads are measured by the run's mx leg (the per-kernel legs use format-0 calls)")
+        raise SystemExit("MXFP4 and super-block workloads are measured by the run's mx and superblock legs (the "
+                         "per-kernel legs use format-0 calls)")
     t0 = time.time()
     log(f"building {cfg.name}: {cfg.description}")
     stack = MoEStack(cfg)
@@ -653,7 +657,9 @@ def main():
     if not args.no_stream:
         result["streaming"] = streaming_leg(torch, args, ms_per_step)
     if not args.no_mx:
-        result["mx"] = mx_leg(torch, args, ms_per_step, result.get("streaming"))
+        result["mx"] = format_leg(torch, args, "decode1_mx", "decode1_mx_stream", ms_per_step, result.get("streaming"))
+        result["superblock"] = format_leg(torch, args, "decode1_sb", "decode1_sb_stream", ms_per_step,
+                                          result.get("streaming"))
     if not args.no_layer_legs:
         from routed_expert_streaming_amd import _lib as L
         result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_SPLIT, 20)

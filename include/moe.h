@@ -72,6 +72,9 @@ int moe_version(void);
 size_t moe_expert_bytes(int hidden, int inter);
 /* Bytes of one MXFP4 expert slab (see "MXFP4 weights" below), 0 for invalid sizes. */
 size_t moe_expert_bytes_mx(int hidden, int inter);
+/* Bytes of one super-block expert slab (see "Super-block weights" below); 0 unless
+ * hidden and inter are positive multiples of 256. */
+size_t moe_expert_bytes_sb(int hidden, int inter);
 
 /* ------------------------------------------------------------------ router
  * Router logits, top-k selection and renormalised gate weights (LayerStoRm
@@ -137,7 +140,8 @@ typedef struct moe_cache_desc {
     int hidden;
     int inter;
     int slots_per_layer;
-    int format; /* slab format: 0 = moe_expert_bytes slabs, 1 = MXFP4 (moe_expert_bytes_mx) */
+    int format; /* slab format: 0 = moe_expert_bytes slabs, 1 = MXFP4 (moe_expert_bytes_mx),
+                   2 = super-blocks (moe_expert_bytes_sb) */
 } moe_cache_desc;
 
 /* Validates the description (slots <= experts), checks every host slab is pinned
@@ -320,6 +324,29 @@ int moe_mx_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, con
                               const float *topk_w, int k, const void *const *expert_table, const void *shared_slab,
                               uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
 int moe_mx_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias, int E,
+                             int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
+                             float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes,
+                             const void *prefetch, size_t prefetch_bytes, void *stream);
+
+/* ------------------------------------------------------------------ super-block weights
+ * A k-quant-style format (the pages' own weights are a 4-bit k-quant GGUF
+ * variant: LayerStoRm README, "TL;DR" and "Serve"; this layout is this
+ * library's own): per 256-column super-block an fp16 d and fp16 dmin and, for
+ * each of its eight 32-column blocks j, a 6-bit scale code s_j and a 6-bit min
+ * code m_j; W = d*s_j*q - dmin*m_j for a 4-bit code q.  A K-column row (K a
+ * multiple of 256) is K/2 code bytes (byte b: column 2b in bits 0-3, 2b+1 in bits
+ * 4-7) then one 16-byte header per super-block: d (bytes 0-1), dmin (2-3), the
+ * eight s_j (bytes 4-9) and the eight m_j (bytes 10-15), code j in bits
+ * 6j..6j+5 of each 48-bit little-endian field; 4.5 bits per weight.  Same slab
+ * arrangement as the other formats.  The kernels form scale d*s_j and min
+ * -dmin*m_j per block (exact in fp32) and then compute as for format 0.
+ * One token only, as the MXFP4 entry points (same arguments, shapes and errors,
+ * plus MOE_E_SHAPE unless H and I are multiples of 256).  A cache of such slabs
+ * sets format = 2 in its descriptor. */
+int moe_sb_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
+                              const float *topk_w, int k, const void *const *expert_table, const void *shared_slab,
+                              uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+int moe_sb_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias, int E,
                              int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
                              float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes,
                              const void *prefetch, size_t prefetch_bytes, void *stream);

@@ -82,6 +82,9 @@ def lib():
             "moe_residual_norm": ([vp, vp, i, i, ctypes.c_float, vp, vp], i),
             "moe_debug_dequant": ([vp, i, i, i, vp, vp], i),
             "moe_expert_bytes_mx": ([i, i], sz),
+            "moe_expert_bytes_sb": ([i, i], sz),
+            "moe_sb_expert_ffn_combine": ([vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, vp], i),
+            "moe_sb_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp], i),
             "moe_mx_expert_ffn_combine": ([vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, vp], i),
             "moe_mx_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp], i),
             "moe_cpu_lane_create": ([i, ctypes.POINTER(vp)], i),
@@ -379,3 +382,23 @@ def moe_mx_route_ffn_combine(x, T, H, I, w_router, bias, E, k, expert_table, sha
                                           _ptr(shared_slab), _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(workspace),
                                           workspace_bytes, _ptr(prefetch), prefetch_bytes, _stream(stream)),
            "moe_mx_route_ffn_combine")
+
+
+# ----------------------------------------------------------------------- super-block weights
+def moe_expert_bytes_sb(H: int, I: int) -> int:
+    return lib().moe_expert_bytes_sb(H, I)
+
+
+def moe_sb_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, workspace,
+                              workspace_bytes, stream=None):
+    _check(lib().moe_sb_expert_ffn_combine(_ptr(x), T, H, I, E, _ptr(topk_idx), _ptr(topk_w), k, _ptr(expert_table),
+                                           _ptr(shared_slab), _ptr(out), _ptr(workspace), workspace_bytes,
+                                           _stream(stream)), "moe_sb_expert_ffn_combine")
+
+
+def moe_sb_route_ffn_combine(x, T, H, I, w_router, bias, E, k, expert_table, shared_slab, topk_idx, topk_w, out,
+                             workspace, workspace_bytes, stream=None, prefetch=None, prefetch_bytes=0):
+    _check(lib().moe_sb_route_ffn_combine(_ptr(x), T, H, I, _ptr(w_router), _ptr(bias), E, k, _ptr(expert_table),
+                                          _ptr(shared_slab), _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(workspace),
+                                          workspace_bytes, _ptr(prefetch), prefetch_bytes, _stream(stream)),
+           "moe_sb_route_ffn_combine")

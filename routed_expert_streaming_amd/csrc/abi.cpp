@@ -55,6 +55,11 @@ extern "C" size_t moe_expert_bytes_mx(int hidden, int inter) {
     return (size_t)2 * inter * moe::mx_row_bytes(hidden) + (size_t)hidden * moe::mx_row_bytes(inter);
 }
 
+extern "C" size_t moe_expert_bytes_sb(int hidden, int inter) {
+    if (hidden <= 0 || inter <= 0 || hidden % 256 || inter % 256) return 0;
+    return (size_t)2 * inter * moe::sb_row_bytes(hidden) + (size_t)hidden * moe::sb_row_bytes(inter);
+}
+
 extern "C" size_t moe_expert_bytes(int hidden, int inter) {
     if (hidden <= 0 || inter <= 0 || hidden % 32 || inter % 32) return 0;
     // 2*inter gate/up rows of `hidden` columns and `hidden` down rows of `inter`

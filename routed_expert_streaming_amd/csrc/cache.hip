@@ -313,7 +313,9 @@ int validate_desc(const moe_cache_desc *d) {
                          d->slots_per_layer);
     if (d->slots_per_layer > d->n_experts)
         return moe::fail(MOE_E_SHAPE, "cache: slots %d > experts %d", d->slots_per_layer, d->n_experts);
-    if (d->format != 0 && d->format != 1) return moe::fail(MOE_E_ARG, "cache: format %d", d->format);
+    if (d->format < 0 || d->format > 2) return moe::fail(MOE_E_ARG, "cache: format %d", d->format);
+    if (d->format == 2 && moe_expert_bytes_sb(d->hidden, d->inter) == 0)
+        return moe::fail(MOE_E_SHAPE, "cache: super-block slabs need H, I multiples of 256");
     if (moe_expert_bytes(d->hidden, d->inter) == 0)
         return moe::fail(MOE_E_SHAPE, "cache: hidden=%d inter=%d", d->hidden, d->inter);
     return MOE_OK;
@@ -341,8 +343,9 @@ static int cache_make(const moe_cache_desc *desc, moe_cache **out) {
     if (!out) return moe::fail(MOE_E_ARG, "cache: NULL out");
     auto *c = new moe_cache();
     c->d = *desc;
-    c->slab_bytes = desc->format == 1 ? moe_expert_bytes_mx(desc->hidden, desc->inter)
-                                      : moe_expert_bytes(desc->hidden, desc->inter);
+    c->slab_bytes = desc->format == 1   ? moe_expert_bytes_mx(desc->hidden, desc->inter)
+                    : desc->format == 2 ? moe_expert_bytes_sb(desc->hidden, desc->inter)
+                                        : moe_expert_bytes(desc->hidden, desc->inter);
     c->clear_state();
     *out = c;
     return MOE_OK;

@@ -33,8 +33,14 @@ struct MatRows {
 // MXFP4 rows (weight format 1): K/2 E2M1 code bytes then K/32 E8M0 scale bytes,
 // padded to a multiple of 16 bytes; same slab arrangement.
 __host__ __device__ constexpr size_t mx_row_bytes(int K) { return ((size_t)K / 2 + (size_t)K / 32 + 15) / 16 * 16; }
+// Super-block rows (weight format 2, K % 256 == 0): K/2 code bytes then one
+// 16-byte header per 256 columns (fp16 d, fp16 dmin, eight 6-bit scale codes,
+// eight 6-bit min codes).
+__host__ __device__ constexpr size_t sb_row_bytes(int K) { return (size_t)K / 2 + (size_t)K / 16; }
 template <int FMT>
-__host__ __device__ constexpr size_t row_bytes_fmt(int K) { return FMT == 1 ? mx_row_bytes(K) : slab_row_bytes(K); }
+__host__ __device__ constexpr size_t row_bytes_fmt(int K) {
+    return FMT == 1 ? mx_row_bytes(K) : FMT == 2 ? sb_row_bytes(K) : slab_row_bytes(K);
+}
 
 __device__ __forceinline__ MatRows slab_w1(const uint8_t *slab, int H, int) { return {slab, 2 * slab_row_bytes(H)}; }
 __device__ __forceinline__ MatRows slab_w3(const uint8_t *slab, int H, int) {
@@ -141,4 +147,16 @@ __device__ __forceinline__ float moe_mx_block_dot(const uint4 c, const uint4 *xb
 // block value from the E8M0 scale byte v: acc * 2^(v - 127) (v = 255: NaN)
 __device__ __forceinline__ float moe_mx_block_value(uint32_t v, float acc) {
     return v == 255u ? __builtin_nanf("") : ldexpf(acc, (int)v - 127);
+}
+
+// Super-block value of block j (0..7) of a header: scale d*s_j and min
+// -dmin*m_j (both exact in fp32), then the format-0 identity
+//   sum (scale*q + min) * x = scale * sum((128+q) x) + (min - 128*scale) * sum x.
+__device__ __forceinline__ float moe_sb_block_value(const uint4 hdr, int j, float acc, float S) {
+    const float d = fp16_bits_to_f32(hdr.x & 0xFFFFu), dmin = fp16_bits_to_f32(hdr.x >> 16);
+    const uint64_t fs = (uint64_t)hdr.y | ((uint64_t)(hdr.z & 0xFFFFu) << 32);
+    const uint64_t fm = (uint64_t)(hdr.z >> 16) | ((uint64_t)hdr.w << 16);
+    const float sc = d * (float)(uint32_t)((fs >> (6 * j)) & 63u);
+    const float mn = -dmin * (float)(uint32_t)((fm >> (6 * j)) & 63u);
+    return fmaf(sc, acc, fmaf(-128.0f, sc, mn) * S);
 }

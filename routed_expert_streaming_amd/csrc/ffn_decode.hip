@@ -21,6 +21,8 @@
 #include "topk.h"
 #include "ffn.h"
 
+#include <type_traits>
+
 namespace {
 
 // Build-time tuning knobs (defaults are the tuned values).
@@ -267,11 +269,14 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
     const uint32_t rs = (uint32_t)moe::row_bytes_fmt<FMT>(H);  // W1 row r at slab + 2*rs*r, W3 row r right after it
     // block lane + 64b: its codes at 16 bytes per block, its record (4 bytes; an
     // MXFP4 scale: 1 byte) after the row's codes
+    // (format 2: the 16-byte header of the lane's super-block, block lane % 8 of it)
     constexpr uint32_t RB = FMT == 1 ? 1u : 4u;
-    const uint32_t code_off = 16u * lane, rec_off = (uint32_t)(H / 2) + RB * lane;
+    const uint32_t code_off = 16u * lane,
+                   rec_off = (uint32_t)(H / 2) + (FMT == 2 ? 2u * (uint32_t)(lane & ~7) : RB * lane);
+    using Rec = std::conditional_t<FMT == 2, uint4, uint32_t>;
 
     uint4 c0[D][BPL], c1[D][BPL];
-    uint32_t p0[D][BPL], p1[D][BPL];
+    Rec p0[D][BPL], p1[D][BPL];
     int ui = 0, gi = w0 / I, ri = w0 - gi * I;  // issue cursor, D units ahead
     auto load_unit = [&](int j, const uint8_t *slab, int row) {
         const uint8_t *w1 = slab + (size_t)row * (2 * rs);
@@ -279,7 +284,10 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
         for (int b = 0; b < BPL; ++b) {
             c0[j][b] = load_stream_u4(w1 + (code_off + 1024u * b));
             c1[j][b] = load_stream_u4(w1 + (rs + code_off + 1024u * b));
-            if constexpr (FMT == 1) {
+            if constexpr (FMT == 2) {
+                p0[j][b] = load_stream_u4(w1 + (rec_off + 128u * b));
+                p1[j][b] = load_stream_u4(w1 + (rs + rec_off + 128u * b));
+            } else if constexpr (FMT == 1) {
                 p0[j][b] = load_stream_u8(w1 + (rec_off + 64u * b));
                 p1[j][b] = load_stream_u8(w1 + (rs + rec_off + 64u * b));
             } else {
@@ -441,7 +449,10 @@ __global__ __launch_bounds__(256) void decode1_gate_up_kernel(moe::FfnArgs a, mo
                 float v0 = 0.0f, v1 = 0.0f;
 #pragma unroll
                 for (int b = 0; b < BPL; ++b) {
-                    if constexpr (FMT == 1) {
+                    if constexpr (FMT == 2) {
+                        v0 += moe_sb_block_value(p0[j][b], lane & 7, moe_block_dot(c0[j][b], X[b], 1, magic), S[b]);
+                        v1 += moe_sb_block_value(p1[j][b], lane & 7, moe_block_dot(c1[j][b], X[b], 1, magic), S[b]);
+                    } else if constexpr (FMT == 1) {
                         v0 += moe_mx_block_value(p0[j][b], moe_mx_block_dot(c0[j][b], X[b]));
                         v1 += moe_mx_block_value(p1[j][b], moe_mx_block_dot(c1[j][b], X[b]));
                     } else {
@@ -684,10 +695,11 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
         const uint32_t magic = moe_magic_vgpr();
         const uint8_t *w2 = slab + (size_t)I * 2 * moe::row_bytes_fmt<FMT>(H);  // W2 row 0
         const uint32_t rs2 = (uint32_t)moe::row_bytes_fmt<FMT>(I);
-        constexpr uint32_t RB = FMT == 1 ? 1u : 4u;  // record bytes per block
-        const uint32_t code_off = 16u * c, rec_off = (uint32_t)(I / 2) + RB * c;
+        constexpr uint32_t RB = FMT == 1 ? 1u : 4u;  // record bytes per block (format 2: a 16-byte header)
+        const uint32_t code_off = 16u * c,
+                       rec_off = (uint32_t)(I / 2) + (FMT == 2 ? 2u * (uint32_t)(c & ~7) : RB * c);
         uint4 cw[D][BPL];
-        uint32_t pw[D][BPL];
+        std::conditional_t<FMT == 2, uint4, uint32_t> pw[D][BPL];
         int ui = 0;
         auto issue = [&](int j) {
             int row = r0 + sub + 4 * ui;
@@ -696,7 +708,9 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
 #pragma unroll
             for (int b = 0; b < BPL; ++b) {
                 cw[j][b] = load_stream_u4(w2 + (rrow + code_off + 256u * b));
-                if constexpr (FMT == 1)
+                if constexpr (FMT == 2)
+                    pw[j][b] = load_stream_u4(w2 + (rrow + rec_off + 32u * b));
+                else if constexpr (FMT == 1)
                     pw[j][b] = load_stream_u8(w2 + (rrow + rec_off + 16u * b));
                 else
                     pw[j][b] = load_stream_u32(w2 + (rrow + rec_off + 64u * b));
@@ -728,7 +742,9 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
                 float v = 0.0f;
 #pragma unroll
                 for (int b = 0; b < BPL; ++b) {
-                    if constexpr (FMT == 1)
+                    if constexpr (FMT == 2)
+                        v += moe_sb_block_value(pw[j][b], c & 7, moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
+                    else if constexpr (FMT == 1)
                         v += moe_mx_block_value(pw[j][b], moe_mx_block_dot(cw[j][b], X[b]));
                     else
                         v += moe_block_value(pw[j][b], moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
@@ -917,6 +933,13 @@ int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s)
             default: return fail(MOE_E_SHAPE, "routed gate/up (MXFP4): H=%d not supported", a.H);
         }
     }
+    if (a.fmt == 2) {
+        switch (a.H >> 5) {
+            case 128: return launch_gate_up1<2, MOE_DECODE1_D_ROUTED, 2>(a, &ra, s);
+            case 64: return launch_gate_up1<1, 6, 2>(a, &ra, s);
+            default: return fail(MOE_E_SHAPE, "routed gate/up (super-blocks): H=%d not supported", a.H);
+        }
+    }
     switch (a.H >> 5) {
         case 128: return launch_gate_up1<2, MOE_DECODE1_D_ROUTED>(a, &ra, s);
         case 64: return launch_gate_up1<1, 6>(a, &ra, s);
@@ -933,6 +956,16 @@ int decode_gate_up(const FfnArgs &a, hipStream_t s) {
                 case 64: return launch_gate_up1<1, 6, 1>(a, nullptr, s);
             }
         return fail(MOE_E_SHAPE, "gate/up (MXFP4): one token with H 2048, 4096 or 6144 only (T=%d, H=%d)", a.T, a.H);
+    }
+    if (a.fmt == 2) {
+        if (a.T == 1)
+            switch (a.H >> 5) {
+                case 128: return launch_gate_up1<2, MOE_DECODE1_D, 2>(a, nullptr, s);
+                case 192: return launch_gate_up1<3, 3, 2>(a, nullptr, s);
+                case 64: return launch_gate_up1<1, 6, 2>(a, nullptr, s);
+            }
+        return fail(MOE_E_SHAPE, "gate/up (super-blocks): one token with H 2048, 4096 or 6144 only (T=%d, H=%d)", a.T,
+                    a.H);
     }
     if (a.T == 1) {
         switch (a.H >> 5) {
@@ -959,6 +992,14 @@ int decode_down(const FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_
                 case 64: return launch_down1<4, 1>(a, topk_w, out, s);
             }
         return fail(MOE_E_SHAPE, "down (MXFP4): one token with I 1536 or 2048 only (T=%d, I=%d)", a.T, a.I);
+    }
+    if (a.fmt == 2) {
+        if (a.T == 1 && !a.grouped && a.k + (a.shared ? 1 : 0) <= kDown1MaxPairs)
+            switch (a.I >> 5) {
+                case 48: return launch_down1<3, 2>(a, topk_w, out, s);
+                case 64: return launch_down1<4, 2>(a, topk_w, out, s);
+            }
+        return fail(MOE_E_SHAPE, "down (super-blocks): one token with I 1536 or 2048 only (T=%d, I=%d)", a.T, a.I);
     }
     if (a.T == 1 && a.k + (a.shared ? 1 : 0) <= kDown1MaxPairs) {
         switch (a.I >> 5) {

@@ -410,29 +410,29 @@ extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, con
                                   workspace_bytes - rbytes, MOE_FFN_AUTO, stream);
 }
 
-// ---------------------------------------------------------------- MXFP4 weights
-// One-token decode with MXFP4 expert slabs: the same kernels specialised for
-// the format (pairs path, fused combine).
+// ---------------------------------------------------------------- other weight formats
+// One-token decode with MXFP4 (format 1) or super-block (format 2) expert slabs:
+// the same kernels specialised for the format (pairs path, fused combine).
 namespace {
-int mx_ffn_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx,
-                int k, const void *const *table, const void *shared, const char *who) {
-    if (T != 1) return moe::fail(MOE_E_SHAPE, "%s: MXFP4 slabs need T = 1 (T=%d)", who, T);
+int fmt_ffn_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx,
+                 int k, const void *const *table, const void *shared, const char *who, int fmt) {
+    if (T != 1) return moe::fail(MOE_E_SHAPE, "%s: weight format %d needs T = 1 (T=%d)", who, fmt, T);
+    if (fmt == 2 && (H % 256 || I % 256))
+        return moe::fail(MOE_E_SHAPE, "%s: super-block slabs need H, I multiples of 256 (H=%d I=%d)", who, H, I);
     int max_m = 1;
     int rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, nullptr, nullptr, nullptr, table, shared, nullptr,
                        MOE_FFN_PAIRS, &max_m, who);
     if (rc != MOE_OK) return rc;
-    a.fmt = 1;
+    a.fmt = fmt;
     if (!moe::decode_supported(a) || !moe::decode1_publishes_slabs(a))
-        return moe::fail(MOE_E_SHAPE, "%s: MXFP4 shapes H=%d I=%d k=%d not supported", who, H, I, k);
+        return moe::fail(MOE_E_SHAPE, "%s: shapes H=%d I=%d k=%d not supported for format %d", who, H, I, k, fmt);
     return MOE_OK;
 }
-}  // namespace
 
-extern "C" int moe_mx_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
-                                         const float *topk_w, int k, const void *const *expert_table,
-                                         const void *shared_slab, uint16_t *out, void *workspace,
-                                         size_t workspace_bytes, void *stream) {
-    const char *who = "mx_expert_ffn_combine";
+int fmt_expert_ffn_combine(int fmt, const char *who, const uint16_t *x, int T, int H, int I, int E,
+                           const int32_t *topk_idx, const float *topk_w, int k, const void *const *expert_table,
+                           const void *shared_slab, uint16_t *out, void *workspace, size_t workspace_bytes,
+                           void *stream) {
     if (T < 0) return moe::fail(MOE_E_ARG, "%s: T=%d < 0", who, T);
     if (T == 0) return MOE_OK;
     if (!workspace || !topk_w) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
@@ -443,7 +443,7 @@ extern "C" int moe_mx_expert_ffn_combine(const uint16_t *x, int T, int H, int I,
         return moe::fail(MOE_E_NOMEM, "%s: workspace %zu < %zu bytes", who, workspace_bytes, Ly.total);
     char *ws = (char *)workspace;
     moe::FfnArgs a;
-    rc = mx_ffn_args(a, x, (uint16_t *)(ws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who);
+    rc = fmt_ffn_args(a, x, (uint16_t *)(ws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who, fmt);
     if (rc != MOE_OK) return rc;
     a.pair_slab = (const uint8_t **)(ws + Ly.slabs);
     rc = moe::decode_gate_up(a, (hipStream_t)stream);
@@ -451,12 +451,10 @@ extern "C" int moe_mx_expert_ffn_combine(const uint16_t *x, int T, int H, int I,
     return moe::decode_down(a, topk_w, out, (hipStream_t)stream);
 }
 
-extern "C" int moe_mx_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router,
-                                        const float *bias, int E, int k, const void *const *expert_table,
-                                        const void *shared_slab, int32_t *topk_idx, float *topk_w, uint16_t *out,
-                                        void *workspace, size_t workspace_bytes, const void *prefetch,
-                                        size_t prefetch_bytes, void *stream) {
-    const char *who = "mx_route_ffn_combine";
+int fmt_route_ffn_combine(int fmt, const char *who, const uint16_t *x, int T, int H, int I, const float *w_router,
+                          const float *bias, int E, int k, const void *const *expert_table, const void *shared_slab,
+                          int32_t *topk_idx, float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes,
+                          const void *prefetch, size_t prefetch_bytes, void *stream) {
     if (T < 0) return moe::fail(MOE_E_ARG, "%s: T=%d < 0", who, T);
     if (!prefetch && prefetch_bytes) return moe::fail(MOE_E_ARG, "%s: %zu prefetch bytes at NULL", who, prefetch_bytes);
     if (T == 0) return MOE_OK;
@@ -472,7 +470,7 @@ extern "C" int moe_mx_route_ffn_combine(const uint16_t *x, int T, int H, int I, 
     hipStream_t s = (hipStream_t)stream;
     moe::FfnArgs a;
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
-    rc = mx_ffn_args(a, x, (uint16_t *)(fws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who);
+    rc = fmt_ffn_args(a, x, (uint16_t *)(fws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who, fmt);
     if (rc != MOE_OK) return rc;
     if (k <= moe::kTopkMaxK && H <= moe::kSlice * moe::kMaxSlices && moe::decode1_routed_supported(a, E)) {
         double *partial = moe::router_partials_buf(rws, T, E);
@@ -489,8 +487,45 @@ extern "C" int moe_mx_route_ffn_combine(const uint16_t *x, int T, int H, int I, 
     }
     rc = moe_router_topk(x, T, H, w_router, bias, E, k, topk_idx, topk_w, rws, rbytes, stream);
     if (rc != MOE_OK) return rc;
-    return moe_mx_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, fws,
-                                     workspace_bytes - rbytes, stream);
+    return fmt_expert_ffn_combine(fmt, who, x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, fws,
+                                  workspace_bytes - rbytes, stream);
+}
+}  // namespace
+
+extern "C" int moe_mx_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
+                                         const float *topk_w, int k, const void *const *expert_table,
+                                         const void *shared_slab, uint16_t *out, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    return fmt_expert_ffn_combine(1, "mx_expert_ffn_combine", x, T, H, I, E, topk_idx, topk_w, k, expert_table,
+                                  shared_slab, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int moe_mx_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router,
+                                        const float *bias, int E, int k, const void *const *expert_table,
+                                        const void *shared_slab, int32_t *topk_idx, float *topk_w, uint16_t *out,
+                                        void *workspace, size_t workspace_bytes, const void *prefetch,
+                                        size_t prefetch_bytes, void *stream) {
+    return fmt_route_ffn_combine(1, "mx_route_ffn_combine", x, T, H, I, w_router, bias, E, k, expert_table,
+                                 shared_slab, topk_idx, topk_w, out, workspace, workspace_bytes, prefetch,
+                                 prefetch_bytes, stream);
+}
+
+extern "C" int moe_sb_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
+                                         const float *topk_w, int k, const void *const *expert_table,
+                                         const void *shared_slab, uint16_t *out, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    return fmt_expert_ffn_combine(2, "sb_expert_ffn_combine", x, T, H, I, E, topk_idx, topk_w, k, expert_table,
+                                  shared_slab, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int moe_sb_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router,
+                                        const float *bias, int E, int k, const void *const *expert_table,
+                                        const void *shared_slab, int32_t *topk_idx, float *topk_w, uint16_t *out,
+                                        void *workspace, size_t workspace_bytes, const void *prefetch,
+                                        size_t prefetch_bytes, void *stream) {
+    return fmt_route_ffn_combine(2, "sb_route_ffn_combine", x, T, H, I, w_router, bias, E, k, expert_table,
+                                 shared_slab, topk_idx, topk_w, out, workspace, workspace_bytes, prefetch,
+                                 prefetch_bytes, stream);
 }
 
 extern "C" int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,

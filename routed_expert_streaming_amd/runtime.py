@@ -140,10 +140,11 @@ class MoEStack:
         torch.cuda.set_device(self.dev)
         self.copy_stream = torch.cuda.Stream(self.dev)  # default priority
         self.copy_stream2 = torch.cuda.Stream(self.dev) if split_copies else None
-        self.fmt = cfg.fmt  # 0: fp16 scale/min blocks; 1: MXFP4 (one-token decode entry points)
-        if self.fmt == 1 and cfg.tokens != 1:
-            raise ValueError("MXFP4 stacks run the one-token decode entry points only (tokens = 1)")
-        self.slab = L.moe_expert_bytes_mx(self.H, self.I) if self.fmt else L.moe_expert_bytes(self.H, self.I)
+        # 0: fp16 scale/min blocks; 1: MXFP4; 2: super-blocks (1 and 2: one-token decode entry points)
+        self.fmt = cfg.fmt
+        if self.fmt != 0 and cfg.tokens != 1:
+            raise ValueError("MXFP4 and super-block stacks run the one-token decode entry points only (tokens = 1)")
+        self.slab = [L.moe_expert_bytes, L.moe_expert_bytes_mx, L.moe_expert_bytes_sb][self.fmt](self.H, self.I)
         assert self.slab == synth.slab_bytes(self.H, self.I, self.fmt)
         Lyr, T, H, I, E, k = self.L, self.T, self.H, self.I, self.E, self.k
 
@@ -264,7 +265,7 @@ class MoEStack:
     def ffn_combine(self, x: torch.Tensor, l: int, out: torch.Tensor):
         """Gate/up, down and the weighted combine of layer l (every needed expert resident)."""
         if self.fmt:
-            L.moe_mx_expert_ffn_combine(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.w[l], self.k,
+            (L.moe_mx_expert_ffn_combine if self.fmt == 1 else L.moe_sb_expert_ffn_combine)(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.w[l], self.k,
                                         self.table[l], self.shared[l] if self.has_shared else None, out[l],
                                         self.ffn_ws, self.ffn_ws_bytes, self.stream)
             return
@@ -278,7 +279,7 @@ class MoEStack:
         after the last) into the device caches while it runs: they are static, so
         this does not depend on the next layer's input."""
         nxt = self.wr[(l + 1) % self.L]
-        call = L.moe_mx_route_ffn_combine if self.fmt else L.moe_route_ffn_combine
+        call = [L.moe_route_ffn_combine, L.moe_mx_route_ffn_combine, L.moe_sb_route_ffn_combine][self.fmt]
         call(x[l], self.T, self.H, self.I, self.wr[l], None if self.bias is None else self.bias[l],
                                 self.E, self.k, self.table[l], self.shared[l] if self.has_shared else None,
                                 self.idx[l], self.w[l], out[l], self.layer_ws, self.layer_ws_bytes, self.stream,
@@ -291,7 +292,7 @@ class MoEStack:
         # the format-0 kernels read format-0 row sizes: on MXFP4 slabs they would
         # read past the end of each slab
         if self.fmt != 0:
-            raise ValueError(f"{what} runs format-0 kernels; this stack holds MXFP4 slabs")
+            raise ValueError(f"{what} runs format-0 kernels; this stack holds format-{self.fmt} slabs")
 
     def gate_up_only(self, x: torch.Tensor, l: int, h: torch.Tensor):
         """Only the dequant + gate/up + SwiGLU kernel of layer l (pair grouping), for timing it."""

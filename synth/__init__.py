@@ -85,7 +85,7 @@ class Config:
     zipf_s: float
     seed: int
     description: str
-    fmt: int = 0      # expert weight format: 0 = 4-bit codes with fp16 scale/min per 32; 1 = MXFP4
+    fmt: int = 0      # expert weight format: 0 = 4-bit codes with fp16 scale/min per 32; 1 = MXFP4; 2 = super-blocks
 
 
     @property
@@ -121,6 +121,12 @@ CONFIGS = {
     "decode1_mx_stream": Config("decode1_mx_stream", 8, 1, 4096, 1536, 128, 1, 8, 0.25, "zipf", 1.1, 20261211,
                                 "decode batch 1 with MXFP4 expert weights, cache cap 25% per layer, Zipf(1.1) "
                                 "router bias, streamed misses", 1),
+    "decode1_sb": Config("decode1_sb", 8, 1, 4096, 1536, 128, 1, 8, 1.0, "none", 0.0, 20261212,
+                         "decode batch 1 with super-block expert weights: 8 layers, H4096, 128 experts + 1 shared, "
+                         "I1536, top-8, resident", 2),
+    "decode1_sb_stream": Config("decode1_sb_stream", 8, 1, 4096, 1536, 128, 1, 8, 0.25, "zipf", 1.1, 20261213,
+                                "decode batch 1 with super-block expert weights, cache cap 25% per layer, Zipf(1.1) "
+                                "router bias, streamed misses", 2),
 }
 ORDER = ["tiny", "decode1", "decode1_stream", "decode32_stream", "prefill2048_stream"]
 

@@ -354,7 +354,28 @@ def test_mx_sizes_and_validation():
     with pytest.raises(L.MoEError) as e:
         L.moe_mx_route_ffn_combine(x, 2, 4096, 1536, wr, None, 128, 8, table, None, idx, w, out, ws, ws.size)
     assert e.value.status == L.MOE_E_SHAPE
-    d = L.moe_cache_desc(1, 4, 64, 32, 2, 2)
+    d = L.moe_cache_desc(1, 4, 64, 32, 2, 3)
     with pytest.raises(L.MoEError) as e:
         L.moe_cache_create_recording(d)
+    assert e.value.status == L.MOE_E_ARG
+
+
+def test_superblock_sizes_and_validation():
+    assert L.moe_expert_bytes_sb(4096, 1536) == 3 * 4096 * 1536 * 9 // 16
+    assert L.moe_expert_bytes_sb(4096, 1504) == 0 and L.moe_expert_bytes_sb(96, 256) == 0
+    ws = np.zeros(1 << 20, np.uint8)
+    x = np.zeros((2, 4096), np.uint16)
+    idx = np.zeros((2, 8), np.int32)
+    w = np.zeros((2, 8), np.float32)
+    out = np.zeros((2, 4096), np.uint16)
+    table = np.zeros(128, np.int64)
+    for T, H, I in ((2, 4096, 1536), (1, 4096, 1024 + 32)):
+        with pytest.raises(L.MoEError) as e:
+            L.moe_sb_expert_ffn_combine(x, T, H, I, 128, idx, w, 8, table, None, out, ws, ws.size)
+        assert e.value.status == L.MOE_E_SHAPE, (T, H, I)
+    with pytest.raises(L.MoEError) as e:
+        L.moe_cache_create_recording(L.moe_cache_desc(1, 4, 64, 32, 2, 2))
+    assert e.value.status == L.MOE_E_SHAPE
+    with pytest.raises(L.MoEError) as e:
+        L.moe_cache_create_recording(L.moe_cache_desc(1, 4, 64, 32, 2, 3))
     assert e.value.status == L.MOE_E_ARG

@@ -1,4 +1,5 @@
-"""GPU parity of the MXFP4 weight format (one-token decode) against the oracle.
+"""GPU parity of the MXFP4 (format 1) and super-block (format 2) weight formats
+(one-token decode) against the oracle.
 
 Bars: expert indices bit-exact; outputs within 2e-2 * max|ref| of the fp64
 oracle reading the same MXFP4 slabs; the one-call layer bit-identical to the
@@ -33,18 +34,19 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+@pytest.mark.parametrize("name", ["decode1_mx", "decode1_sb"])
 @pytest.mark.parametrize("over", [
     {},                                                        # H4096 I1536, 128 experts + shared, top-8
     {"hidden": 2048, "inter": 2048, "experts": 32, "layers": 2},  # routed variant with one block per lane
     {"hidden": 6144, "inter": 2048, "experts": 24, "layers": 2},  # H above the fused router's range
     {"experts": 16, "shared": 0, "top_k": 4, "layers": 2},
 ])
-def test_mx_layers_match_oracle_and_split_calls(over):
-    cfg = synth.get("decode1_mx", **over)
+def test_format_layers_match_oracle_and_split_calls(name, over):
+    cfg = synth.get(name, **over)
     layers = min(cfg.layers, 2)
     st = MoEStack(cfg, layers=layers)
     try:
-        assert not st.streaming and st.fmt == 1
+        assert not st.streaming and st.fmt == cfg.fmt
         for s in range(2):
             x = st.make_inputs(s)
             out = st.new_output()
@@ -64,16 +66,17 @@ def test_mx_layers_match_oracle_and_split_calls(over):
                 wr = st.wr[l].cpu().numpy()
                 bias = None if st.bias is None else st.bias[l].cpu().numpy()
                 o = oracle.moe_layer(xb[l], wr, bias, cfg.top_k, st.host_slabs(l), st.host_shared(l), cfg.inter,
-                                     fmt=1)
+                                     fmt=cfg.fmt)
                 assert (o["idx"] == idx1[l]).all()
-                ratio = check_close(ob[l], o["out64"], f"mx {over} step {s} layer {l}")
-                print(f"mx {over} step {s} layer {l}: max err / max|ref| = {ratio:.2e}")
+                ratio = check_close(ob[l], o["out64"], f"{name} {over} step {s} layer {l}")
+                print(f"{name} {over} step {s} layer {l}: max err / max|ref| = {ratio:.2e}")
     finally:
         st.close()
 
 
-def test_mx_streamed_equals_resident_and_lru():
-    cfg = synth.get("decode1_mx_stream")
+@pytest.mark.parametrize("name", ["decode1_mx_stream", "decode1_sb_stream"])
+def test_format_streamed_equals_resident_and_lru(name):
+    cfg = synth.get(name)
     layers, steps = 3, 4
     streamed = MoEStack(cfg, layers=layers)
     resident = MoEStack(cfg, layers=layers, cap=1.0)
@@ -94,7 +97,7 @@ def test_mx_streamed_equals_resident_and_lru():
                 model.release(l)
         hits, misses, nbytes = streamed.stats()
         assert (hits, misses) == (model.hits, model.misses) and nbytes == misses * streamed.slab
-        assert streamed.slab == L.moe_expert_bytes_mx(cfg.hidden, cfg.inter) == 4096 * 1536 * 3 * 17 // 32
+        assert streamed.slab == 4096 * 1536 * 3 * (17 if cfg.fmt == 1 else 18) // 32
     finally:
         streamed.close()
         resident.close()
