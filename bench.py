@@ -302,6 +302,27 @@ def cpu_lane_run(torch, st, args, xs, streamed_tokens_per_s: float):
            "streamed_experts_per_step": round((m1 - m0) / n, 3),
            "hit_rate_of_gpu_requests": round((h1 - h0) / max(h1 - h0 + m1 - m0, 1), 4),
            "h2d_GBps": round((b1 - b0) / wall / 1e9, 2), "steps": n, "warmup": args.stream_warmup}
+    if args.chain_steps > 0 and st.T * st.k <= st.C:
+        # chained layers (no lookahead): each layer's misses split between the
+        # copy engine and the lane as soon as the layer is routed
+        resid, hs = st.chain_buffers()
+        st.reset_cache()
+        for s in range(args.chain_warmup):
+            st.forward_chained(xs[s % n_in][0], hs, resid, out)
+        torch.cuda.synchronize()
+        h0, m0, b0 = st.stats()
+        cpu_e = 0
+        t0 = time.perf_counter()
+        for s in range(args.chain_steps):
+            cpu_e += st.forward_chained(xs[s % n_in][0], hs, resid, out).cpu_experts
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        h1, m1, b1 = st.stats()
+        n = args.chain_steps
+        res["chained_no_lookahead"] = {"tokens_per_s": round(n * st.T / wall, 2), "ms_per_step": round(wall / n * 1e3, 3),
+                                       "cpu_experts_per_step": round(cpu_e / n, 3),
+                                       "streamed_experts_per_step": round((m1 - m0) / n, 3),
+                                       "steps": n, "warmup": args.chain_warmup}
     log(f"cpu lane: {res}")
     return res
 

@@ -105,6 +105,7 @@ class ChainStats:
     ahead_unused: int = 0  # of those, experts the layer's own routing did not select
     routed: int = 0        # distinct routed experts of the predicted layers (1 .. L-1)
     predicted: int = 0     # of those, experts the prediction had named
+    cpu_experts: int = 0   # misses computed by the CPU lane instead of streamed
 
 
 RMS_EPS = 1e-6  # eps of the residual stream's RMS normalisation between chained layers
@@ -358,22 +359,25 @@ class MoEStack:
             out.append(best)
         return out[0], out[1]
 
-    def plan_cpu_lane(self, needed_by_layer, idx_host):
-        """Experts of each layer that the CPU lane computes this step."""
+    def plan_cpu_lane(self, needed_by_layer, idx_host, layers=None, cpu_head: float = 0.0):
+        """Experts of each layer that the CPU lane computes (layers: the layer ids
+        of the lists, default 0, 1, ...; cpu_head: seconds the lane starts behind
+        the copy engine)."""
+        layers = list(range(len(needed_by_layer))) if layers is None else list(layers)
         misses = []
-        for l, needed in enumerate(needed_by_layer):
+        for i, (l, needed) in enumerate(zip(layers, needed_by_layer)):
             slots, _ = L.moe_cache_lookup(self.cache, l, needed)
-            tok = np.bincount(idx_host[l].ravel(), minlength=self.E)
-            misses += [(l, e, int(tok[e])) for e, s in zip(needed, slots) if s < 0]
+            tok = np.bincount(idx_host[i].ravel(), minlength=self.E)
+            misses += [(i, e, int(tok[e])) for e, s in zip(needed, slots) if s < 0]
         cpu = [set() for _ in needed_by_layer]
         if self.lane_pick is not None:
-            for l in range(len(needed_by_layer)):
-                cpu[l] = set(self.lane_pick(l, [e for ll, e, _ in misses if ll == l]))
+            for i, l in enumerate(layers):
+                cpu[i] = set(self.lane_pick(l, [e for ii, e, _ in misses if ii == i]))
             return cpu
-        to_cpu, _, _ = assign_lanes(misses, self.slab / (self.link_GBps * 1e9), self.t_cpu)
-        for (l, e, _), c in zip(misses, to_cpu):
+        to_cpu, _, _ = assign_lanes(misses, self.slab / (self.link_GBps * 1e9), self.t_cpu, cpu_busy=cpu_head)
+        for (i, e, _), c in zip(misses, to_cpu):
             if c:
-                cpu[l].add(e)
+                cpu[i].add(e)
         return cpu
 
     def submit_cpu_lane(self, l: int, experts, idx_l: np.ndarray):
@@ -507,6 +511,7 @@ class MoEStack:
         if self.streaming and T * (k + m) > self.C:
             raise ValueError(f"chained streaming needs {T * (k + m)} <= {self.C} slots")
         pred = {}  # layer -> (predicted set, set copied ahead)
+        self.last_cpu_sets = [set() for _ in range(self.L)]
         for l in range(self.L):
             if not self.streaming:
                 self.route_ffn_combine(xs, l, out)
@@ -520,9 +525,27 @@ class MoEStack:
                 torch.from_numpy(hv[:T * k]).copy_(self.idx[l].view(-1), non_blocking=True)
                 if ahead:
                     torch.from_numpy(hv[T * k:]).copy_(self.pidx[l + 1].view(-1), non_blocking=True)
+                if self.lane is not None:
+                    self._x_host[l].copy_(xs[l], non_blocking=True)
                 self.stream.synchronize()
                 needed = sorted(set(hv[:T * k].tolist()))
-                st.copies += L.moe_cache_prefetch_async(self.cache, l, needed)
+                # CPU lane: some of this layer's misses computed on the host while
+                # the copy engine streams the others
+                cpu, job = set(), None
+                if self.lane is not None:
+                    idx_l = hv[:T * k].reshape(T, k).copy()
+                    # a layer's first miss always streams: it is exposed either way,
+                    # and streamed it is cached for the next step (the lane's
+                    # experts are not); the lane takes later misses when it
+                    # would finish them first
+                    cpu = self.plan_cpu_lane([needed], idx_l[None], layers=[l],
+                                             cpu_head=self.slab / (self.link_GBps * 1e9))[0]
+                    if cpu:
+                        job = self.submit_cpu_lane(l, cpu, idx_l)
+                        st.cpu_experts += len(cpu)
+                        self.last_cpu_sets[l] = cpu
+                gpu_side = [e for e in needed if e not in cpu]
+                st.copies += L.moe_cache_prefetch_async(self.cache, l, gpu_side)
                 if l in pred:
                     named, copied = pred.pop(l)
                     st.routed += len(needed)
@@ -536,8 +559,20 @@ class MoEStack:
                     st.ahead_copies += L.moe_cache_prefetch_async(self.cache, l + 1, nxt)
                     pred[l + 1] = (set(nxt), copied)
                 L.moe_cache_wait(self.cache, l, self.stream)
-                self.ffn_combine(xs, l, out)
-                L.moe_cache_release(self.cache, l, self.stream)
+                if job is None:
+                    self.ffn_combine(xs, l, out)
+                    L.moe_cache_release(self.cache, l, self.stream)
+                else:
+                    mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
+                                       count=self.L * self.max_waves * self.E).reshape(self.L, self.max_waves, self.E)
+                    mh[l, 0] = 0
+                    mh[l, 0, gpu_side] = 1
+                    self.masks[l, 0].copy_(torch.from_numpy(mh[l, 0]), non_blocking=True)
+                    self.ffn(xs, l, mask=self.masks[l, 0], shared=True)
+                    L.moe_cache_release(self.cache, l, self.stream)
+                    L.moe_cpu_lane_wait(self.lane, job[0])
+                    self.upload_cpu_rows(l, job[1])
+                    self.combine(l, out)
             if l + 1 < self.L:
                 L.moe_residual_norm(out[l], resid, T, H, RMS_EPS, xs[l + 1], self.stream)
         return st

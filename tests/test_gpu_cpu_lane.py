@@ -119,3 +119,40 @@ def test_cpu_lane_cost_model_run_and_empty_pick_is_identical():
             print(f"step {s}: {r.cpu_experts} experts on the CPU lane (t_cpu 1 token {st.t_cpu1 * 1e3:.3f} ms)")
     finally:
         st.close()
+
+
+def test_chained_with_cpu_lane_against_oracle():
+    """Chained layers with the lane (every other miss of a layer on the host):
+    layer by layer on the GPU's own inputs, indices bit-exact and outputs within
+    the bar; the residual step reproduces the next layer's input."""
+    from routed_expert_streaming_amd.runtime import RMS_EPS
+    from tests.test_gpu_chained import bf16_ulps
+    cfg = synth.get("decode1_stream")
+    layers, k = 3, cfg.top_k
+    st = MoEStack(cfg, layers=layers, cpu_lane=4)
+    try:
+        st.lane_pick = lambda l, misses: misses[::2]
+        resid, xs = st.chain_buffers()
+        out = st.new_output()
+        wr = [st.wr[l].cpu().numpy() for l in range(layers)]
+        bias = [st.bias[l].cpu().numpy() for l in range(layers)]
+        n_cpu = 0
+        for s in range(3):
+            h0 = st.make_inputs(s)[0]
+            c = st.forward_chained(h0, xs, resid, out)
+            torch.cuda.synchronize()
+            n_cpu += c.cpu_experts
+            xb, ob, idx = bits(xs), bits(out), st.idx.cpu().numpy()
+            ref_resid = np.zeros((cfg.tokens, cfg.hidden), np.float32)
+            x_ref = oracle.residual_norm(bits(h0), ref_resid, RMS_EPS)
+            assert bf16_ulps(xb[0], x_ref).max() <= 1
+            for l in range(layers):
+                o = oracle.moe_layer(xb[l], wr[l], bias[l], k, pool_slabs(st, l), st.host_shared(l), cfg.inter)
+                assert (o["idx"] == idx[l]).all(), (s, l)
+                check_close(ob[l], o["out64"], f"chained lane step {s} layer {l}")
+                if l + 1 < layers:
+                    x_ref = oracle.residual_norm(ob[l], ref_resid, RMS_EPS)
+                    assert bf16_ulps(xb[l + 1], x_ref).max() <= 1
+        assert n_cpu > 0
+    finally:
+        st.close()
