@@ -22,6 +22,7 @@ struct FfnArgs {
                                 // written by the one-token gate/up kernel, read by the down kernel
     int fmt;                    // expert weight format: 0 = fp16 scale/min blocks, 1 = MXFP4 (one-token decode only)
     int min_m, max_m;           // grouped kernels skip groups with fewer / more tokens than these
+    int compact;                // MFMA kernel: workgroups take the active groups in rank order (see the kernel)
     const uint8_t *prefetch;    // or nullptr: bytes the one-token down kernel reads into the device caches
     size_t prefetch_bytes;      // for the caller's next call (read and discarded, 1 KB per wave)
 };

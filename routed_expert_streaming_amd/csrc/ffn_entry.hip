@@ -227,6 +227,7 @@ int grouped_gemv(moe::FfnArgs a, int max_m, bool split, hipStream_t s) {
     if (rc != MOE_OK) return rc;
     a.min_m = moe::kGemvOnePass + 1;
     a.max_m = 1 << 30;
+    a.compact = 1;  // few experts have that many tokens: deal their tiles over all XCDs
     return GATEUP ? moe::mfma_gate_up(a, s) : moe::mfma_down(a, s);
 }
 

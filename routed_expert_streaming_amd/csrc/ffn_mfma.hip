@@ -264,9 +264,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     constexpr int U = lcm(lcm(S, G), R);  // steps per unrolled loop body
     const int K = GATEUP ? a.H : a.I;   // reduction length (a multiple of 64 * G and 64 * R)
     const int nrows = GATEUP ? a.I : a.H;  // weight rows (output columns)
-    // every tile of one expert on the same XCD
-    const int xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
-    const int g = (i / ntiles) * kXcds + xcd, tile = i % ntiles;
+    // Which group and tile: by default every tile of one expert on the same XCD
+    // (its activation tiles are then fetched into one L2).  Compact (a launch
+    // where few groups qualify, the many-token experts of the split path):
+    // workgroup b takes tile b % ntiles of the (b / ntiles)-th qualifying group
+    // in group order, so each expert's tiles are dealt over all XCDs and the
+    // XCDs get equal shares however the qualifying experts are numbered.
+    int g, tile;
+    if (a.compact) {
+        __shared__ int s_g, s_wcnt[4];
+        const int j = blockIdx.x / ntiles;
+        tile = blockIdx.x % ntiles;
+        const int t = threadIdx.x, ln = t & 63, w = t >> 6;
+        if (t == 0) s_g = -1;
+        int before = 0;  // qualifying groups in earlier chunks
+        for (int c0 = 0; c0 < a.n_routed_groups; c0 += 256) {
+            const int gg = c0 + t;
+            bool act = false;
+            if (gg < a.n_routed_groups) {
+                const int M = a.count[gg];
+                act = M > 0 && M >= a.min_m && M <= a.max_m && (!a.mask || a.mask[gg]);
+            }
+            const uint64_t bal = __ballot(act);
+            __syncthreads();  // s_wcnt of the previous chunk has been read
+            if (ln == 0) s_wcnt[w] = __popcll(bal);
+            __syncthreads();
+            int wb = 0;
+            for (int v = 0; v < w; ++v) wb += s_wcnt[v];
+            if (act && before + wb + __popcll(bal & ((1ull << ln) - 1)) == j) s_g = gg;
+            before += s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+        }
+        __syncthreads();
+        g = s_g;
+        if (g < 0) {  // past the routed groups: the shared expert comes last
+            if (!(a.shared && j == before)) return;
+            g = a.n_routed_groups;
+        }
+    } else {
+        const int xcd = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
+        g = (i / ntiles) * kXcds + xcd;
+        tile = i % ntiles;
+    }
     if (g >= n_groups) return;
     const int n0 = tile * kTileN;
 
