@@ -219,7 +219,12 @@ int64_t moe_cache_trace(const moe_cache *cache, int64_t *cmds, int64_t max_cmds)
  *                   H and I multiples of 128);
  *   MOE_FFN_SPLIT   one group per expert: experts with up to 4 tokens on the
  *                   dequant-GEMV, the others on the MFMA kernels (H and I
- *                   multiples of 128, else as GROUPED).
+ *                   multiples of 128, else as GROUPED).  The two parts run
+ *                   side by side: the MFMA part on a helper stream of the
+ *                   library's (one per device, created on first use), forked
+ *                   from and joined back into `stream` with events, so all of
+ *                   the call's work is still ordered after the work before it
+ *                   on `stream` and before the work after it.
  * workspace: moe_expert_ffn_workspace_bytes(...) bytes, contents don't care. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_PAIRS = 1, MOE_FFN_GROUPED = 2, MOE_FFN_MFMA = 3, MOE_FFN_SPLIT = 4 };
 size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int has_shared);

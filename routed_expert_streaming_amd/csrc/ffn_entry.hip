@@ -1,5 +1,7 @@
 // Entry points around the expert FFN: token->expert permutation, the FFN
 // dispatcher, the weighted combine and the dequantisation debug hook.
+#include <mutex>
+
 #include "common.h"
 #include "dequant.h"
 #include "ffn.h"
@@ -218,17 +220,60 @@ int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, 
 // dotted with every token) and the MFMA kernel the larger ones (each weight
 // dequantised once for all its tokens) -- rather than re-reading weights or
 // re-staging activations for every pass.
+// Per-device helper stream of the split path (default priority, non-blocking).
+std::mutex g_aux_mu;
+hipStream_t g_aux[64] = {};
+
+int aux_stream(hipStream_t *out) {
+    int dev = 0;
+    MOE_TRY_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return moe::fail(MOE_E_STATE, "split path: device %d", dev);
+    std::lock_guard<std::mutex> lk(g_aux_mu);
+    if (!g_aux[dev]) MOE_TRY_HIP(hipStreamCreateWithFlags(&g_aux[dev], hipStreamNonBlocking));
+    *out = g_aux[dev];
+    return MOE_OK;
+}
+
 template <bool GATEUP>
 int grouped_gemv(moe::FfnArgs a, int max_m, bool split, hipStream_t s) {
     if (!split || !a.grouped || !moe::mfma_supported(a) || max_m <= moe::kGemvOnePass)
         return GATEUP ? moe::ffn_gemv_gate_up(a, max_m, s) : moe::ffn_gemv_down(a, max_m, s);
-    a.max_m = moe::kGemvOnePass;
-    int rc = GATEUP ? moe::ffn_gemv_gate_up(a, moe::kGemvOnePass, s) : moe::ffn_gemv_down(a, moe::kGemvOnePass, s);
+    // The MFMA part (few experts, few workgroups) runs on a helper stream beside
+    // the GEMV part, forked from and joined back into the caller's stream by
+    // events; the two write disjoint rows of h (y).
+    hipStream_t aux = nullptr;
+    int rc = aux_stream(&aux);
     if (rc != MOE_OK) return rc;
-    a.min_m = moe::kGemvOnePass + 1;
-    a.max_m = 1 << 30;
-    a.compact = 1;  // few experts have that many tokens: deal their tiles over all XCDs
-    return GATEUP ? moe::mfma_gate_up(a, s) : moe::mfma_down(a, s);
+    hipEvent_t fork = nullptr, join = nullptr;
+    MOE_TRY_HIP(hipEventCreateWithFlags(&fork, hipEventDisableTiming));
+    hipError_t e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        (void)hipEventDestroy(fork);
+        return moe::fail_hip(e, "hipEventCreateWithFlags(join)");
+    }
+    moe::FfnArgs b = a;
+    b.min_m = moe::kGemvOnePass + 1;
+    b.max_m = 1 << 30;
+    b.compact = 1;  // few experts have that many tokens: deal their tiles over all XCDs
+    a.max_m = moe::kGemvOnePass;
+    e = hipEventRecord(fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(aux, fork, 0);
+    if (e == hipSuccess) {
+        rc = GATEUP ? moe::mfma_gate_up(b, aux) : moe::mfma_down(b, aux);
+        if (rc == MOE_OK) {
+            e = hipEventRecord(join, aux);
+            if (e == hipSuccess) {
+                rc = GATEUP ? moe::ffn_gemv_gate_up(a, moe::kGemvOnePass, s)
+                            : moe::ffn_gemv_down(a, moe::kGemvOnePass, s);
+                const hipError_t e2 = hipStreamWaitEvent(s, join, 0);  // join even if the GEMV launch failed
+                if (rc == MOE_OK && e2 != hipSuccess) e = e2;
+            }
+        }
+    }
+    (void)hipEventDestroy(fork);
+    (void)hipEventDestroy(join);
+    if (e != hipSuccess) return moe::fail_hip(e, "split path fork/join");
+    return rc;
 }
 
 // Kernel family for a grouped call: MFMA when forced, or automatically for many tokens.
