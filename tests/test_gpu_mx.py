@@ -62,6 +62,9 @@ def test_format_layers_match_oracle_and_split_calls(name, over):
             assert (st.idx.cpu().numpy() == idx1).all()
             assert (bits(out2) == ob).all()
             xb = bits(x)
+            # the format-0 calls refuse these slabs (their row sizes differ)
+            with pytest.raises(ValueError):
+                st.gate_up_only(x, 0, torch.empty((1, cfg.inter), dtype=torch.bfloat16, device="cuda"))
             for l in range(layers):
                 wr = st.wr[l].cpu().numpy()
                 bias = None if st.bias is None else st.bias[l].cpu().numpy()
