@@ -110,10 +110,18 @@ int moe_router_topk_layers(const uint16_t *x, int n_layers, int T, int H, const 
                            size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ dispatch
- * Token -> expert permutation of the T*k (token, slot) pairs p = t*k + i:
- * counting sort by expert, stable in p.  count[e] = pairs routed to e;
+ * Token -> expert permutation of the T*k (token, slot) pairs p = t*k + i
+ * (LayerStoRm README, "TL;DR": each token activates only the few experts the
+ * router names, so a batch of tokens -- a batched decode step or a prefill chunk,
+ * rebasdaily article, section "96 GB of VRAM and 208 GB of RAM behind it" -- is
+ * grouped by expert so that each expert's weights are read once for all of its
+ * tokens): counting sort by expert, stable in p.  count[e] = pairs routed to e;
  * offset[e] = exclusive prefix sum (offset[E] = T*k); pair_of_row[offset[e]+j] =
- * the j-th smallest pair index routed to e.  Requires T*k <= 16384, E <= 1024. */
+ * the j-th smallest pair index routed to e.  topk_idx [T,k] int32 (values in
+ * 0..E-1); count [E], offset [E+1], pair_of_row [T*k] int32 outputs; all device
+ * memory owned by the caller.  Requires T*k <= 16384, E <= 1024, k <= E
+ * (MOE_E_SHAPE otherwise); MOE_E_ARG for a NULL pointer or T < 0; T = 0 writes
+ * zero counts and offsets. */
 int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
                 int32_t *pair_of_row, void *stream);
 
@@ -184,10 +192,30 @@ int moe_cache_prefetch(moe_cache *cache, int layer, const int32_t *experts_host,
 int moe_cache_release(moe_cache *cache, int layer, void *compute_stream);
 /* Cumulative hit / miss counts (per requested expert) and H2D bytes streamed. */
 int moe_cache_stats(const moe_cache *cache, uint64_t *hits, uint64_t *misses, uint64_t *h2d_bytes);
-/* Waits for outstanding copies, empties every slot, clears the table, zeroes stats. */
+/* Waits for outstanding copies and for the work enqueued before every
+   moe_cache_release so far (kernels that read the slots or the table), then
+   empties every slot, clears the table and zeroes the stats.  Blocks. */
 int moe_cache_reset(moe_cache *cache);
-/* Waits for outstanding copies and frees the library's events and the object. */
+/* Waits as moe_cache_reset does, then frees the library's events and the object. */
 void moe_cache_destroy(moe_cache *cache);
+/* Step plan of one layer (LayerStoRm README, "TL;DR": the router's choice
+ * decides what is streamed; rebasdaily article, section "keep the experts in the
+ * warehouse": the host manages the cache and moves the data).  ids_host: the
+ * layer's n_ids top-k expert ids of the step (host memory, repeats allowed).  The
+ * distinct experts are split into waves that each fit the layer's slots: one
+ * wave when there are at most slots_per_layer of them; otherwise waves of
+ * max(1, slots/2), the experts already resident first and then the misses (each
+ * group in ascending id), every wave sorted ascending -- so that each wave's
+ * misses can stream into slots released two waves earlier while the previous
+ * wave computes.  Outputs (host memory): wave_experts_host [number of distinct
+ * experts] the experts wave by wave; wave_start_host [max_waves + 1], wave w
+ * being wave_experts_host[wave_start_host[w] .. wave_start_host[w+1]); masks_host
+ * NULL or [max_waves][n_experts] uint8, set to 1 at each wave's experts and 0
+ * elsewhere (the expert_mask of the wave's FFN call); *n_waves (0 when n_ids is
+ * 0).  Reads the cache state only.  MOE_E_CAPACITY if more than max_waves waves
+ * are needed, MOE_E_ARG for an id out of range or a NULL pointer. */
+int moe_cache_plan(const moe_cache *cache, int layer, const int32_t *ids_host, int n_ids, int32_t *wave_experts_host,
+                   int32_t *wave_start_host, int max_waves, uint8_t *masks_host, int *n_waves);
 
 /* Test hook: a cache whose copy engine only records commands (no HIP calls).
    slot_pool is then just a base address used to form slot pointers.  If
@@ -202,7 +230,10 @@ int64_t moe_cache_trace(const moe_cache *cache, int64_t *cmds, int64_t max_cmds)
 
 /* ------------------------------------------------------------------ expert FFN
  * Fused 4-bit block dequant + SwiGLU expert FFN for every (token, slot) pair
- * whose expert the mask admits, plus an always-on shared expert:
+ * whose expert the mask admits, plus an always-on shared expert (LayerStoRm
+ * README, "TL;DR": only the experts the router picks run for a token; "Serve":
+ * the weights are a 4-bit block-quantised GGUF type; the 4-bit 32-column blocks
+ * with an fp16 scale and min are the slab format above):
  *   g = W1 x_t, u = W3 x_t, h = bf16(silu(g) * u), y = W2 h   (fp32 accumulation)
  * x [T,H] bf16; topk_idx [T,k]; expert_table: device array [E] of this layer's
  * slab pointers (entries of masked-off experts are never read); shared_slab:
@@ -252,9 +283,14 @@ int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t
                     float *y, int path, void *stream);
 
 /* ------------------------------------------------------------------ combine
- * Weighted combine in a fixed order, fp32, rounded once to bf16:
+ * Weighted combine of a token's expert outputs (LayerStoRm README, "TL;DR": the
+ * selected experts' outputs are combined into the layer output; "Serve" notes: a
+ * deterministic combine gives reproducible output), in a fixed order, fp32,
+ * rounded once to bf16:
  *   out[t,:] = bf16( sum_{i=0..k-1} topk_w[t,i] * y[t*k+i,:] + (has_shared ? y[T*k+t,:] : 0) ).
- * y as produced by moe_expert_ffn; out [T,H] bf16. */
+ * y [T*k (+T), H] fp32 as produced by moe_expert_ffn; topk_w [T,k] fp32; out [T,H]
+ * bf16; device memory owned by the caller.  MOE_E_ARG for T < 0, k < 1, H <= 0 or
+ * a NULL pointer, MOE_E_SHAPE unless H % 4 == 0; T = 0 is a no-op. */
 int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,
                 void *stream);
 

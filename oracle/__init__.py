@@ -76,6 +76,7 @@ def lib():
         L.oracle_expert_ffn_fmt.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i32]
         L.oracle_moe_layer_fmt.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, i64, i32,
                                            vp, vp, vp, vp, i32]
+        L.oracle_moe_ffn_routed_fmt.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, i64, i32, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -176,6 +177,33 @@ def moe_layer(x_bf16: np.ndarray, Wr: np.ndarray, bias, k: int, slabs, shared, I
                                None if shared is None else _p(shared), _p(r), nr, threads,
                                _p(idx), _p(w), _p(out64), _p(outb), fmt)
     return {"idx": idx, "w": w, "out64": out64, "out_bf16": outb}
+
+
+def moe_ffn_routed(x_bf16: np.ndarray, idx: np.ndarray, w: np.ndarray, slabs, shared, I: int,
+                   rows=None, threads: int = 0, fmt: int = 0):
+    """Expert FFNs and the combine for a given routing (steps 4-5 of oracle.c):
+    idx [T,k] expert ids, w [T,k] gate weights (taken as given, in fp64).
+    Returns dict(out64 [T,H] float64, out_bf16 [T,H] uint16); rows as moe_layer."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    T, H = x_bf16.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    assert idx.shape == w.shape and idx.shape[0] == T
+    k = idx.shape[1]
+    E = len(slabs)
+    assert idx.min() >= 0 and idx.max() < E
+    sb = slab_bytes(H, I, fmt)
+    for s in slabs:
+        assert s.dtype == np.uint8 and s.size == sb and s.flags["C_CONTIGUOUS"]
+    ptrs = np.array([s.ctypes.data for s in slabs], dtype=np.uint64)
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    nr = 0 if r is None else len(r)
+    out64 = np.zeros((T, H), np.float64)
+    outb = np.zeros((T, H), np.uint16)
+    lib().oracle_moe_ffn_routed_fmt(_p(x_bf16), T, H, I, k, _p(idx), _p(w), _p(ptrs),
+                                    None if shared is None else _p(shared), _p(r), nr, threads,
+                                    _p(out64), _p(outb), fmt)
+    return {"out64": out64, "out_bf16": outb}
 
 
 def residual_norm(add, resid: np.ndarray, eps: float):

@@ -276,17 +276,17 @@ void oracle_router(const uint16_t *x, int64_t T, int64_t H, const float *Wr, con
     }
 }
 
-/* ---------------- one MoE layer ---------------- */
-/* slabs[e] = host slab of routed expert e; shared = host slab of the always-on
-   shared expert or NULL.  Tokens listed in `rows` (n_rows of them; NULL = all T)
-   are the only ones computed; out64/out_bf16 are [T x H] and only those rows are
-   written.  idx/w are computed for every token. */
-void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
-                      const float *Wr, const float *bias, const uint8_t *const *slabs, const uint8_t *shared,
-                      const int32_t *rows, int64_t n_rows, int nthreads,
-                      int32_t *idx, double *w, double *out64, uint16_t *out_bf16) {
+/* ---------------- expert FFNs and combine for a given routing ---------------- */
+/* Steps 4 and 5 above for routing that is already known: token t's slot i runs
+   expert idx[t*k+i] with gate weight w[t*k+i]; then the shared expert (if any)
+   with weight 1.  slabs[e] = host slab of routed expert e; shared = host slab of
+   the always-on shared expert or NULL.  Tokens listed in `rows` (n_rows of them;
+   NULL = all T) are the only ones computed; out64/out_bf16 are [T x H] and only
+   those rows are written. */
+void oracle_moe_ffn_routed(const uint16_t *x, int64_t T, int64_t H, int64_t I, int k, const int32_t *idx,
+                           const double *w, const uint8_t *const *slabs, const uint8_t *shared,
+                           const int32_t *rows, int64_t n_rows, int nthreads, double *out64, uint16_t *out_bf16) {
     nthreads = clamp_threads(nthreads);
-    oracle_router(x, T, H, Wr, bias, E, k, NULL, idx, w, nthreads);
     int64_t nt = rows ? n_rows : T;
     int per = k + (shared ? 1 : 0);
     int64_t npairs = nt * per;
@@ -315,6 +315,18 @@ void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_
         }
     }
     free(y);
+}
+
+/* ---------------- one MoE layer ---------------- */
+/* Steps 1-5: the router for every token (idx/w are computed for all T), then the
+   expert FFNs and the combine for the tokens in `rows` (NULL = all). */
+void oracle_moe_layer(const uint16_t *x, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                      const float *Wr, const float *bias, const uint8_t *const *slabs, const uint8_t *shared,
+                      const int32_t *rows, int64_t n_rows, int nthreads,
+                      int32_t *idx, double *w, double *out64, uint16_t *out_bf16) {
+    nthreads = clamp_threads(nthreads);
+    oracle_router(x, T, H, Wr, bias, E, k, NULL, idx, w, nthreads);
+    oracle_moe_ffn_routed(x, T, H, I, k, idx, w, slabs, shared, rows, n_rows, nthreads, out64, out_bf16);
 }
 
 /* ---------------- residual stream between chained layers ----------------
@@ -358,5 +370,13 @@ void oracle_moe_layer_fmt(const uint16_t *x, int64_t T, int64_t H, int64_t I, in
                           int fmt) {
     g_fmt = fmt;
     oracle_moe_layer(x, T, H, I, E, k, Wr, bias, slabs, shared, rows, n_rows, nthreads, idx, w, out64, out_bf16);
+    g_fmt = 0;
+}
+void oracle_moe_ffn_routed_fmt(const uint16_t *x, int64_t T, int64_t H, int64_t I, int k, const int32_t *idx,
+                               const double *w, const uint8_t *const *slabs, const uint8_t *shared,
+                               const int32_t *rows, int64_t n_rows, int nthreads, double *out64, uint16_t *out_bf16,
+                               int fmt) {
+    g_fmt = fmt;
+    oracle_moe_ffn_routed(x, T, H, I, k, idx, w, slabs, shared, rows, n_rows, nthreads, out64, out_bf16);
     g_fmt = 0;
 }

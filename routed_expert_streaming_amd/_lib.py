@@ -70,6 +70,7 @@ def lib():
             "moe_cache_release": ([vp, i, vp], i),
             "moe_cache_stats": ([vp, u64p, u64p, u64p], i),
             "moe_cache_reset": ([vp], i),
+            "moe_cache_plan": ([vp, i, vp, i, vp, vp, i, vp, ctypes.POINTER(i)], i),
             "moe_cache_destroy": ([vp], None),
             "moe_expert_ffn_workspace_bytes": ([i, i, i, i, i, i], sz),
             "moe_expert_ffn": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, sz, i, vp], i),
@@ -262,6 +263,27 @@ def moe_cache_stats(cache: int):
     h, m, b = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
     _check(lib().moe_cache_stats(cache, ctypes.byref(h), ctypes.byref(m), ctypes.byref(b)), "moe_cache_stats")
     return h.value, m.value, b.value
+
+
+def moe_cache_plan(cache: int, layer: int, ids, max_waves: int = 0, masks=None):
+    """Waves of a layer's experts (see moe.h).  ids: host int32 numpy array (or a
+    sequence) of the layer's top-k ids, repeats allowed; masks: optional host
+    uint8 numpy array [max_waves, E] that the call fills.  Returns the waves as
+    lists of expert ids."""
+    import numpy as np
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
+    n = int(ids.size)
+    if masks is not None:
+        assert masks.dtype == np.uint8 and masks.flags["C_CONTIGUOUS"] and masks.ndim == 2
+        max_waves = masks.shape[0]
+    max_waves = max_waves or max(n, 1)
+    experts = np.empty(max(n, 1), np.int32)
+    starts = np.empty(max_waves + 1, np.int32)
+    nw = ctypes.c_int()
+    _check(lib().moe_cache_plan(cache, layer, ids.ctypes.data if n else None, n, experts.ctypes.data,
+                                starts.ctypes.data, max_waves, None if masks is None else masks.ctypes.data,
+                                ctypes.byref(nw)), "moe_cache_plan")
+    return [experts[starts[v]:starts[v + 1]].tolist() for v in range(nw.value)]
 
 
 def moe_cache_reset(cache: int):

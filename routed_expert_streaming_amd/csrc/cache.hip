@@ -64,6 +64,7 @@ struct Engine {
     virtual int wait(int layer, void *compute_stream) = 0;  // compute waits for them, then the table writes
     virtual int release(int layer, long long release_id, int n_slots, void *compute_stream) = 0;
     virtual int sync() = 0;
+    virtual int drain() { return sync(); }
     virtual int clear_table() = 0;
     // later copies in two halves, the second on stream2 (nullptr: one stream)
     virtual int split_copies(hipStream_t) { return MOE_OK; }
@@ -212,6 +213,15 @@ struct HipEngine final : Engine {
     int sync() override {
         MOE_TRY_HIP(hipStreamSynchronize(copy_stream));
         if (copy_stream2) MOE_TRY_HIP(hipStreamSynchronize(copy_stream2));
+        return MOE_OK;
+    }
+    // Copies done and every recorded release reached: no kernel enqueued before
+    // a moe_cache_release still reads a slot or the table (an event never
+    // recorded counts as complete).
+    int drain() override {
+        int rc = sync();
+        if (rc != MOE_OK) return rc;
+        for (auto e : release_ev) MOE_TRY_HIP(hipEventSynchronize(e));
         return MOE_OK;
     }
     int clear_table() override {
@@ -511,6 +521,47 @@ extern "C" int moe_cache_prefetch_async(moe_cache *c, int layer, const int32_t *
     return MOE_OK;
 }
 
+extern "C" int moe_cache_plan(const moe_cache *c, int layer, const int32_t *ids_host, int n_ids,
+                              int32_t *wave_experts_host, int32_t *wave_start_host, int max_waves,
+                              uint8_t *masks_host, int *n_waves) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache_plan: NULL cache");
+    if (layer < 0 || layer >= c->d.n_layers) return moe::fail(MOE_E_ARG, "cache_plan: layer %d", layer);
+    if (n_ids < 0 || (n_ids > 0 && !ids_host) || !wave_start_host || !n_waves || max_waves < 1 ||
+        (n_ids > 0 && !wave_experts_host))
+        return moe::fail(MOE_E_ARG, "cache_plan: n_ids=%d max_waves=%d or a NULL pointer", n_ids, max_waves);
+    const int E = c->d.n_experts, Cs = c->C();
+    std::vector<char> seen(E, 0);
+    for (int i = 0; i < n_ids; ++i) {
+        const int e = ids_host[i];
+        if (e < 0 || e >= E) return moe::fail(MOE_E_ARG, "cache_plan: expert %d out of range", e);
+        seen[e] = 1;
+    }
+    // distinct experts, hits first then misses, each in ascending id
+    const int *slot_of = &c->slot_of[(size_t)layer * E];
+    std::vector<int> order;
+    for (int e = 0; e < E; ++e)
+        if (seen[e] && slot_of[e] >= 0) order.push_back(e);
+    for (int e = 0; e < E; ++e)
+        if (seen[e] && slot_of[e] < 0) order.push_back(e);
+    const int n = (int)order.size();
+    const int w = n <= Cs ? Cs : std::max(1, Cs / 2);
+    const int waves = (n + w - 1) / w;
+    if (waves > max_waves) return moe::fail(MOE_E_CAPACITY, "cache_plan: %d waves > max_waves %d", waves, max_waves);
+    if (masks_host) std::memset(masks_host, 0, (size_t)max_waves * E);
+    wave_start_host[0] = 0;
+    for (int v = 0; v < waves; ++v) {
+        const int b = v * w, e_ = std::min(n, b + w);
+        std::sort(order.begin() + b, order.begin() + e_);
+        for (int i = b; i < e_; ++i) {
+            wave_experts_host[i] = order[i];
+            if (masks_host) masks_host[(size_t)v * E + order[i]] = 1;
+        }
+        wave_start_host[v + 1] = e_;
+    }
+    *n_waves = waves;
+    return MOE_OK;
+}
+
 extern "C" int moe_cache_split_copies(moe_cache *c, void *second_copy_stream) {
     if (!c) return moe::fail(MOE_E_ARG, "cache_split_copies: NULL cache");
     for (int l = 0; l < c->d.n_layers; ++l)
@@ -568,7 +619,9 @@ extern "C" int moe_cache_stats(const moe_cache *c, uint64_t *hits, uint64_t *mis
 
 extern "C" int moe_cache_reset(moe_cache *c) {
     if (!c) return moe::fail(MOE_E_ARG, "cache_reset: NULL cache");
-    int rc = c->engine->sync();
+    // wait for the copies and for every kernel ordered before a release, so that
+    // nothing still reads a slot or table entry when the table is cleared
+    int rc = c->engine->drain();
     if (rc != MOE_OK) return rc;
     rc = c->engine->clear_table();
     if (rc != MOE_OK) return rc;
@@ -576,4 +629,7 @@ extern "C" int moe_cache_reset(moe_cache *c) {
     return MOE_OK;
 }
 
-extern "C" void moe_cache_destroy(moe_cache *c) { delete c; }
+extern "C" void moe_cache_destroy(moe_cache *c) {
+    if (c && c->engine) (void)c->engine->drain();
+    delete c;
+}

@@ -66,6 +66,13 @@ constexpr int kMfmaMinTokens = 128;
 // larger groups go to the MFMA kernels when their shapes allow.
 constexpr int kGemvOnePass = 4;
 
+// moe_route_ffn_combine; fork = false runs the split path's two parts in order
+// on `stream` (no helper stream, no events: nothing is allocated).
+int route_ffn_combine_impl(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias, int E,
+                           int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
+                           float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes,
+                           const void *prefetch, size_t prefetch_bytes, bool fork, void *stream);
+
 // Counting sort of pairs by expert (see moe_permute).
 int permute_launch(const int32_t *topk_idx, int T, int k, int E, int32_t *count, int32_t *offset,
                    int32_t *pair_of_row, hipStream_t s);

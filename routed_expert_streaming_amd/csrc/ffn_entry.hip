@@ -235,9 +235,19 @@ int aux_stream(hipStream_t *out) {
 }
 
 template <bool GATEUP>
-int grouped_gemv(moe::FfnArgs a, int max_m, bool split, hipStream_t s) {
+int grouped_gemv(moe::FfnArgs a, int max_m, bool split, bool use_fork, hipStream_t s) {
     if (!split || !a.grouped || !moe::mfma_supported(a) || max_m <= moe::kGemvOnePass)
         return GATEUP ? moe::ffn_gemv_gate_up(a, max_m, s) : moe::ffn_gemv_down(a, max_m, s);
+    moe::FfnArgs b = a;
+    b.min_m = moe::kGemvOnePass + 1;
+    b.max_m = 1 << 30;
+    b.compact = 1;  // few experts have that many tokens: deal their tiles over all XCDs
+    a.max_m = moe::kGemvOnePass;
+    if (!use_fork) {  // both parts in order on the caller's stream (no helper stream, no events)
+        int rc = GATEUP ? moe::mfma_gate_up(b, s) : moe::mfma_down(b, s);
+        if (rc != MOE_OK) return rc;
+        return GATEUP ? moe::ffn_gemv_gate_up(a, moe::kGemvOnePass, s) : moe::ffn_gemv_down(a, moe::kGemvOnePass, s);
+    }
     // The MFMA part (few experts, few workgroups) runs on a helper stream beside
     // the GEMV part, forked from and joined back into the caller's stream by
     // events; the two write disjoint rows of h (y).
@@ -251,11 +261,6 @@ int grouped_gemv(moe::FfnArgs a, int max_m, bool split, hipStream_t s) {
         (void)hipEventDestroy(fork);
         return moe::fail_hip(e, "hipEventCreateWithFlags(join)");
     }
-    moe::FfnArgs b = a;
-    b.min_m = moe::kGemvOnePass + 1;
-    b.max_m = 1 << 30;
-    b.compact = 1;  // few experts have that many tokens: deal their tiles over all XCDs
-    a.max_m = moe::kGemvOnePass;
     e = hipEventRecord(fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(aux, fork, 0);
     if (e == hipSuccess) {
@@ -282,9 +287,12 @@ bool use_mfma(const moe::FfnArgs &a, int path) {
     return path == MOE_FFN_MFMA || (path == MOE_FFN_AUTO && a.T >= moe::kMfmaMinTokens);
 }
 
-// Automatic path of the one-call entry points.
-int auto_path(int T, int k) {
+// Automatic path of the one-call entry points: pairs for few (token, slot)
+// pairs, MFMA for many tokens, split in between; the MFMA and split paths need
+// H and I multiples of 128, other shapes take the grouped GEMV.
+int auto_path(int T, int k, int H, int I) {
     if ((long long)T * k <= 64) return MOE_FFN_PAIRS;
+    if (H % 128 || I % 128) return MOE_FFN_GROUPED;
     return T >= moe::kMfmaMinTokens ? MOE_FFN_MFMA : MOE_FFN_SPLIT;
 }
 
@@ -295,10 +303,10 @@ bool use_split(const moe::FfnArgs &a, int path) {
 
 }  // namespace
 
-extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
-                                  const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
-                                  const void *const *expert_table, const void *shared_slab,
-                                  const uint8_t *expert_mask, uint16_t *h, int path, void *stream) {
+namespace {
+int gate_up_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k, const int32_t *count,
+                 const int32_t *offset, const int32_t *pair_of_row, const void *const *expert_table,
+                 const void *shared_slab, const uint8_t *expert_mask, uint16_t *h, int path, bool fork, void *stream) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_gate_up: T=%d < 0", T);
     if (T == 0) return MOE_OK;
     int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, h, path, "expert_gate_up");
@@ -311,13 +319,12 @@ extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E,
     if (use_mfma(a, path)) return moe::mfma_gate_up(a, (hipStream_t)stream);
     if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_gate_up: MFMA path needs H, I multiples of 128");
     if (moe::decode_supported(a)) return moe::decode_gate_up(a, (hipStream_t)stream);
-    return grouped_gemv<true>(a, max_m, use_split(a, path), (hipStream_t)stream);
+    return grouped_gemv<true>(a, max_m, use_split(a, path), fork, (hipStream_t)stream);
 }
 
-extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k,
-                               const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
-                               const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
-                               float *y, int path, void *stream) {
+int down_impl(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k, const int32_t *count,
+              const int32_t *offset, const int32_t *pair_of_row, const void *const *expert_table,
+              const void *shared_slab, const uint8_t *expert_mask, float *y, int path, bool fork, void *stream) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_down: T=%d < 0", T);
     if (T == 0) return MOE_OK;
     int rc = validate_ffn(h, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_down");
@@ -330,12 +337,12 @@ extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, co
     if (use_mfma(a, path)) return moe::mfma_down(a, (hipStream_t)stream);
     if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_down: MFMA path needs H, I multiples of 128");
     if (moe::decode_supported(a)) return moe::decode_down(a, nullptr, nullptr, (hipStream_t)stream);
-    return grouped_gemv<false>(a, max_m, use_split(a, path), (hipStream_t)stream);
+    return grouped_gemv<false>(a, max_m, use_split(a, path), fork, (hipStream_t)stream);
 }
 
-extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
-                              const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
-                              float *y, void *workspace, size_t workspace_bytes, int path, void *stream) {
+int ffn_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+             const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask, float *y,
+             void *workspace, size_t workspace_bytes, int path, bool fork, void *stream) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_ffn: T=%d < 0", T);
     if (T == 0) return MOE_OK;
     if (!workspace) return moe::fail(MOE_E_ARG, "expert_ffn: NULL workspace");
@@ -345,10 +352,7 @@ extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, con
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "expert_ffn: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
-    if (path == MOE_FFN_AUTO) {
-        path = auto_path(T, k);
-        if ((path == MOE_FFN_MFMA || path == MOE_FFN_SPLIT) && (H % 128 || I % 128)) path = MOE_FFN_GROUPED;
-    }
+    if (path == MOE_FFN_AUTO) path = auto_path(T, k, H, I);
     if (path != MOE_FFN_PAIRS && (long long)T * k > kPermMaxPairs)
         return moe::fail(MOE_E_SHAPE, "expert_ffn: grouped paths need T*k <= %d", kPermMaxPairs);
     hipStream_t s = (hipStream_t)stream;
@@ -362,17 +366,16 @@ extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, con
         rc = moe::permute_launch(topk_idx, T, k, E, count, offset, pairs, s);
         if (rc != MOE_OK) return rc;
     }
-    rc = moe_expert_gate_up(x, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask,
-                            h, path, stream);
+    rc = gate_up_impl(x, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask, h, path,
+                      fork, stream);
     if (rc != MOE_OK) return rc;
-    return moe_expert_down(h, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask,
-                           y, path, stream);
+    return down_impl(h, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask, y, path,
+                     fork, stream);
 }
 
-extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
-                                      const float *topk_w, int k, const void *const *expert_table,
-                                      const void *shared_slab, uint16_t *out, void *workspace, size_t workspace_bytes,
-                                      int path, void *stream) {
+int ffn_combine_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, const float *topk_w,
+                     int k, const void *const *expert_table, const void *shared_slab, uint16_t *out, void *workspace,
+                     size_t workspace_bytes, int path, bool fork, void *stream) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_ffn_combine: T=%d < 0", T);
     if (T == 0) return MOE_OK;
     if (!workspace || !topk_w) return moe::fail(MOE_E_ARG, "expert_ffn_combine: NULL pointer");
@@ -382,7 +385,7 @@ extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, in
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "expert_ffn_combine: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
-    if (path == MOE_FFN_AUTO) path = auto_path(T, k);
+    if (path == MOE_FFN_AUTO) path = auto_path(T, k, H, I);
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     uint16_t *h = (uint16_t *)(ws + Ly.h);
@@ -400,10 +403,42 @@ extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, in
         }
     }
     float *y = (float *)(ws + Ly.y);
-    rc = moe_expert_ffn(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, nullptr, y, workspace,
-                        workspace_bytes, path, stream);
+    rc = ffn_impl(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, nullptr, y, workspace, workspace_bytes, path,
+                  fork, stream);
     if (rc != MOE_OK) return rc;
     return moe_combine(y, topk_w, T, k, H, has_shared, out, stream);
+}
+}  // namespace
+
+extern "C" int moe_expert_gate_up(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                                  const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                                  const void *const *expert_table, const void *shared_slab,
+                                  const uint8_t *expert_mask, uint16_t *h, int path, void *stream) {
+    return gate_up_impl(x, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
+                        expert_mask, h, path, true, stream);
+}
+
+extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                               const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                               const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                               float *y, int path, void *stream) {
+    return down_impl(h, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab, expert_mask,
+                     y, path, true, stream);
+}
+
+extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                              const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                              float *y, void *workspace, size_t workspace_bytes, int path, void *stream) {
+    return ffn_impl(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, expert_mask, y, workspace,
+                    workspace_bytes, path, true, stream);
+}
+
+extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
+                                      const float *topk_w, int k, const void *const *expert_table,
+                                      const void *shared_slab, uint16_t *out, void *workspace, size_t workspace_bytes,
+                                      int path, void *stream) {
+    return ffn_combine_impl(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, workspace,
+                            workspace_bytes, path, true, stream);
 }
 
 extern "C" size_t moe_route_ffn_combine_workspace_bytes(int T, int H, int I, int E, int k, int has_shared) {
@@ -411,11 +446,11 @@ extern "C" size_t moe_route_ffn_combine_workspace_bytes(int T, int H, int I, int
     return moe::align_up(moe_router_workspace_bytes(T, E), 256) + ffn_layout(T, H, I, E, k, has_shared).total;
 }
 
-extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias,
-                                     int E, int k, const void *const *expert_table, const void *shared_slab,
-                                     int32_t *topk_idx, float *topk_w, uint16_t *out, void *workspace,
-                                     size_t workspace_bytes, const void *prefetch, size_t prefetch_bytes,
-                                     void *stream) {
+namespace moe {
+int route_ffn_combine_impl(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias, int E,
+                           int k, const void *const *expert_table, const void *shared_slab, int32_t *topk_idx,
+                           float *topk_w, uint16_t *out, void *workspace, size_t workspace_bytes,
+                           const void *prefetch, size_t prefetch_bytes, bool fork, void *stream) {
     const char *who = "route_ffn_combine";
     if (T < 0) return moe::fail(MOE_E_ARG, "%s: T=%d < 0", who, T);
     if (!prefetch && prefetch_bytes) return moe::fail(MOE_E_ARG, "%s: %zu prefetch bytes at NULL", who, prefetch_bytes);
@@ -452,8 +487,18 @@ extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, con
     }
     rc = moe_router_topk(x, T, H, w_router, bias, E, k, topk_idx, topk_w, rws, rbytes, stream);
     if (rc != MOE_OK) return rc;
-    return moe_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, fws,
-                                  workspace_bytes - rbytes, MOE_FFN_AUTO, stream);
+    return ffn_combine_impl(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, fws,
+                            workspace_bytes - rbytes, MOE_FFN_AUTO, fork, stream);
+}
+}  // namespace moe
+
+extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias,
+                                     int E, int k, const void *const *expert_table, const void *shared_slab,
+                                     int32_t *topk_idx, float *topk_w, uint16_t *out, void *workspace,
+                                     size_t workspace_bytes, const void *prefetch, size_t prefetch_bytes,
+                                     void *stream) {
+    return moe::route_ffn_combine_impl(x, T, H, I, w_router, bias, E, k, expert_table, shared_slab, topk_idx, topk_w,
+                                       out, workspace, workspace_bytes, prefetch, prefetch_bytes, true, stream);
 }
 
 // ---------------------------------------------------------------- other weight formats

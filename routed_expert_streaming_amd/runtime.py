@@ -162,8 +162,8 @@ class MoEStack:
         if self.has_shared:
             stage = PinnedHost(Lyr * self.slab)
             for l in range(Lyr):
-                synth.fill_slabs(cfg.seed, l, [synth.shared_expert_id(cfg)], H, I, [stage.ptr + l * self.slab],
-                                 threads, self.fmt)
+                synth.fill_slabs(cfg.seed, cfg.weight_layer(l), [synth.shared_expert_id(cfg)], H, I,
+                                 [stage.ptr + l * self.slab], threads, self.fmt)
             self.shared = torch.empty((Lyr, self.slab), dtype=torch.uint8, device=self.dev)
             self.shared.view(-1).copy_(torch.from_numpy(stage.array[:Lyr * self.slab]), non_blocking=False)
             stage.free()
@@ -175,7 +175,11 @@ class MoEStack:
             self.pool = torch.empty((Lyr * E, self.slab), dtype=torch.uint8, device=self.dev)
             stage = PinnedHost(E * self.slab)
             for l in range(Lyr):
-                synth.fill_slabs(cfg.seed, l, list(range(E)), H, I,
+                wl = cfg.weight_layer(l)
+                if wl != l:  # the same weights as an earlier layer: device-to-device copy
+                    self.pool[l * E:(l + 1) * E].copy_(self.pool[wl * E:(wl + 1) * E])
+                    continue
+                synth.fill_slabs(cfg.seed, wl, list(range(E)), H, I,
                                  [stage.ptr + e * self.slab for e in range(E)], threads, self.fmt)
                 self.pool[l * E:(l + 1) * E].view(-1).copy_(torch.from_numpy(stage.array[:E * self.slab]))
             stage.free()
@@ -183,16 +187,18 @@ class MoEStack:
             ptrs = np.array([base + i * self.slab for i in range(Lyr * E)], dtype=np.int64).reshape(Lyr, E)
             self.table = torch.from_numpy(ptrs).to(self.dev)
         else:
-            # one pinned allocation per layer (very large single pinned allocations
-            # can be refused where the total would still be granted)
-            self.host = [PinnedHost(E * self.slab) for _ in range(Lyr)]
-            for l in range(Lyr):
-                synth.fill_slabs(cfg.seed, l, list(range(E)), H, I,
-                                 [self.host[l].ptr + e * self.slab for e in range(E)], threads, self.fmt)
+            # one pinned allocation per weight set (very large single pinned
+            # allocations can be refused where the total would still be granted);
+            # layers that share a weight set point at the same host slabs
+            n_sets = min(cfg.n_weight_sets, Lyr)
+            self.host = [PinnedHost(E * self.slab) for _ in range(n_sets)]
+            for j in range(n_sets):
+                synth.fill_slabs(cfg.seed, j, list(range(E)), H, I,
+                                 [self.host[j].ptr + e * self.slab for e in range(E)], threads, self.fmt)
             self.pool = torch.empty((Lyr * self.C, self.slab), dtype=torch.uint8, device=self.dev)
             self.table = torch.zeros((Lyr, E), dtype=torch.int64, device=self.dev)
             self._host_ptrs = (ctypes.c_void_p * (Lyr * E))(
-                *[self.host[l].ptr + e * self.slab for l in range(Lyr) for e in range(E)])
+                *[self.host_slab_ptr(l, e) for l in range(Lyr) for e in range(E)])
             desc = L.moe_cache_desc(Lyr, E, H, I, self.C, self.fmt)
             torch.cuda.synchronize(self.dev)
             self.cache = L.moe_cache_create(desc, ctypes.addressof(self._host_ptrs), self.pool, self.table,
@@ -224,6 +230,15 @@ class MoEStack:
         if cpu_lane and self.streaming:
             self.enable_cpu_lane(cpu_lane)
         torch.cuda.synchronize(self.dev)
+
+    def host_slab_ptr(self, l: int, e: int) -> int:
+        """Pinned host address of layer l's routed expert e (streamed stacks)."""
+        return self.host[self.cfg.weight_layer(l)].ptr + e * self.slab
+
+    def host_pool_slabs(self, l: int):
+        """Layer l's routed slabs as views of the pinned host pool the cache streams from."""
+        arr = self.host[self.cfg.weight_layer(l)].array
+        return [arr[e * self.slab:(e + 1) * self.slab] for e in range(self.E)]
 
     # ------------------------------------------------------------------ inputs
     def make_inputs(self, step: int, threads: int = 0) -> torch.Tensor:
@@ -309,21 +324,11 @@ class MoEStack:
                           self.table[l], self.shared[l] if self.has_shared else None, None, self.y,
                           L.MOE_FFN_PAIRS, self.stream)
 
-    def wave_size(self, n_needed: int) -> int:
-        """C when a layer's experts fit its slots, else half of them: then the next
-        wave's copies go to the slots the wave before last released while the
-        current wave computes, and the copy stream never waits on a wave's compute."""
-        return self.C if n_needed <= self.C else max(1, self.C // 2)
-
-    def plan_waves(self, l: int, needed):
-        """Split a layer's sorted needed experts into waves (wave_size each),
-        resident ones (hits) first."""
-        slots, _ = L.moe_cache_lookup(self.cache, l, needed)
-        hits = [e for e, s in zip(needed, slots) if s >= 0]
-        misses = [e for e, s in zip(needed, slots) if s < 0]
-        order = hits + misses
-        w = self.wave_size(len(order))
-        return [sorted(order[i:i + w]) for i in range(0, len(order), w)]
+    def plan_waves(self, l: int, ids, masks=None):
+        """The library's step plan of layer l (moe_cache_plan): its top-k ids split
+        into waves that fit its slots, resident experts first, each wave's expert
+        mask written into masks [max_waves, E] (host) when given."""
+        return L.moe_cache_plan(self.cache, l, ids, max_waves=self.max_waves, masks=masks)
 
     # ------------------------------------------------------------------ CPU lane
     def enable_cpu_lane(self, threads: int):
@@ -349,7 +354,7 @@ class MoEStack:
         for M in (1, 8):
             best = float("inf")
             for r in range(reps + 1):
-                slab = self.host[0].ptr + (r % self.E) * self.slab
+                slab = self.host_slab_ptr(0, r % self.E)
                 t0 = time.perf_counter()
                 t = L.moe_cpu_lane_submit(self.lane, slab, self.H, self.I, M,
                                           [xs[i].data_ptr() for i in range(M)], [ys[i].data_ptr() for i in range(M)])
@@ -386,7 +391,7 @@ class MoEStack:
         for e in sorted(experts):
             ts, iis = np.nonzero(idx_l == e)
             pairs = [int(t) * self.k + int(i) for t, i in zip(ts, iis)]
-            ticket = L.moe_cpu_lane_submit(self.lane, self.host[l].ptr + e * self.slab, self.H, self.I, len(pairs),
+            ticket = L.moe_cpu_lane_submit(self.lane, self.host_slab_ptr(l, e), self.H, self.I, len(pairs),
                                            [self._x_host[l, int(t)].data_ptr() for t in ts],
                                            [self._y_host[l, p].data_ptr() for p in pairs])
             rows += pairs
@@ -416,36 +421,34 @@ class MoEStack:
         torch.from_numpy(idx_host).copy_(self.idx.view(-1), non_blocking=True)
         if self.lane is not None:
             self._x_host.copy_(x, non_blocking=True)
-        self.stream.synchronize()
-        needed_by_layer = [sorted(set(row)) for row in idx_host.reshape(self.L, -1).tolist()]
+        self.stream.synchronize()  # also: the previous step's mask upload has read the host masks
+        idx3 = idx_host.reshape(self.L, self.T, self.k)
+        mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
+                           count=self.L * self.max_waves * self.E).reshape(self.L, self.max_waves, self.E)
         # CPU lane: some misses are computed on the host; a layer uses it when the
         # rest of its experts fit its slots (one wave)
-        cpu_sets, lane_jobs = [set() for _ in needed_by_layer], {}
-        idx3 = idx_host.reshape(self.L, self.T, self.k)
+        cpu_sets, lane_jobs = [set() for _ in range(self.L)], {}
         if self.lane is not None:
+            needed_by_layer = [sorted(set(row)) for row in idx_host.reshape(self.L, -1).tolist()]
             cpu_sets = self.plan_cpu_lane(needed_by_layer, idx3)
         plans = []
-        for l, needed in enumerate(needed_by_layer):
+        for l in range(self.L):
             if cpu_sets[l]:
-                gpu_side = [e for e in needed if e not in cpu_sets[l]]
+                gpu_side = [e for e in needed_by_layer[l] if e not in cpu_sets[l]]
                 if len(gpu_side) <= self.C:
                     plans.append([gpu_side])
+                    mh[l] = 0
+                    mh[l, 0, gpu_side] = 1
                     lane_jobs[l] = self.submit_cpu_lane(l, cpu_sets[l], idx3[l])
                     st.cpu_experts += len(cpu_sets[l])
                     st.cpu_pairs += len(lane_jobs[l][1])
                     continue
                 cpu_sets[l] = set()
-            # up to C experts always fit in one wave, whatever is resident
-            plans.append([needed] if len(needed) <= self.C else self.plan_waves(l, needed))
+            # the library's plan: one wave when the layer's experts fit its slots,
+            # else waves of half the slots, hits first
+            plans.append(self.plan_waves(l, idx3[l], masks=mh[l]))
         self.last_cpu_sets = cpu_sets
-        need_masks = any(len(p) > 1 for p in plans) or bool(lane_jobs)
-        if need_masks:
-            mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
-                               count=self.L * self.max_waves * self.E).reshape(self.L, self.max_waves, self.E)
-            mh[:] = 0
-            for l, waves in enumerate(plans):
-                for wv, experts in enumerate(waves):
-                    mh[l, wv, experts] = 1
+        if any(len(p) > 1 for p in plans) or lane_jobs:
             self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
         # single-wave layers: every copy is queued before the first FFN launch, so
         # the copy engine starts as soon as the plan is known (each layer evicts
@@ -611,9 +614,11 @@ class MoEStack:
     # ------------------------------------------------------------------ host copies for checking
     def host_slabs(self, l: int):
         """Routed slabs of layer l as host numpy arrays (regenerated from the seed)."""
-        return [synth.expert_slab(self.cfg.seed, l, e, self.H, self.I, self.fmt) for e in range(self.E)]
+        wl = self.cfg.weight_layer(l)
+        return [synth.expert_slab(self.cfg.seed, wl, e, self.H, self.I, self.fmt) for e in range(self.E)]
 
     def host_shared(self, l: int):
         if not self.has_shared:
             return None
-        return synth.expert_slab(self.cfg.seed, l, synth.shared_expert_id(self.cfg), self.H, self.I, self.fmt)
+        return synth.expert_slab(self.cfg.seed, self.cfg.weight_layer(l), synth.shared_expert_id(self.cfg), self.H,
+                                 self.I, self.fmt)

@@ -86,7 +86,12 @@ class Config:
     seed: int
     description: str
     fmt: int = 0      # expert weight format: 0 = 4-bit codes with fp16 scale/min per 32; 1 = MXFP4; 2 = super-blocks
-
+    # distinct expert weight sets: 0 = every layer its own; n > 0: layer l's routed
+    # and shared experts hold the weights of layer l % n (the 16-layer configurations'
+    # full host pool, 90 GiB, is more than one process may page-lock on the test
+    # machine; with 8 weight sets 45 GiB is pinned and every layer still has its own
+    # router, inputs, cache slots and misses, so every streamed byte crosses PCIe)
+    weight_layers: int = 0
 
     @property
     def slots(self) -> int:
@@ -101,6 +106,14 @@ class Config:
     def slab_bytes(self) -> int:
         return slab_bytes(self.hidden, self.inter, self.fmt)
 
+    def weight_layer(self, layer: int) -> int:
+        """Generator layer id of layer `layer`'s expert weights."""
+        return layer % self.weight_layers if self.weight_layers else layer
+
+    @property
+    def n_weight_sets(self) -> int:
+        return min(self.weight_layers, self.layers) if self.weight_layers else self.layers
+
 
 CONFIGS = {
     "tiny": Config("tiny", 1, 4, 256, 128, 16, 0, 2, 1.0, "none", 0.0, 20261204,
@@ -111,10 +124,12 @@ CONFIGS = {
                              "decode batch 1, cache cap 25% per layer, Zipf(1.1) router bias, streamed misses"),
     "decode32_stream": Config("decode32_stream", 16, 32, 6144, 2048, 256, 1, 8, 0.40, "zipf", 1.1, 20261207,
                               "decode batch 32: 16 layers, H6144, 256 experts + 1 shared, I2048, top-8, "
-                              "Zipf(1.1), cap 40%"),
+                              "Zipf(1.1), cap 40%; layers 8-15 reuse the expert weights of layers 0-7",
+                              weight_layers=8),
     "prefill2048_stream": Config("prefill2048_stream", 16, 2048, 6144, 2048, 256, 0, 8, 0.40, "none", 0.0,
                                  20261208, "prefill chunk 2048 tokens: 16 layers, H6144, 256 experts, I2048, "
-                                 "top-8, uniform routing, cap 40%"),
+                                 "top-8, uniform routing, cap 40%; layers 8-15 reuse the expert weights of "
+                                 "layers 0-7", weight_layers=8),
     "decode1_mx": Config("decode1_mx", 8, 1, 4096, 1536, 128, 1, 8, 1.0, "none", 0.0, 20261210,
                          "decode batch 1 with MXFP4 expert weights: 8 layers, H4096, 128 experts + 1 shared, "
                          "I1536, top-8, resident", 1),

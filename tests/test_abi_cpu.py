@@ -379,3 +379,52 @@ def test_superblock_sizes_and_validation():
     with pytest.raises(L.MoEError) as e:
         L.moe_cache_create_recording(L.moe_cache_desc(1, 4, 64, 32, 2, 3))
     assert e.value.status == L.MOE_E_ARG
+
+
+@pytest.mark.parametrize("seed,experts,slots,k,tokens", [(11, 16, 4, 2, 6), (12, 64, 25, 8, 8), (13, 256, 102, 8, 64),
+                                                        (14, 32, 1, 2, 3)])
+def test_step_plan_drives_overflowing_layers_through_the_abi(seed, experts, slots, k, tokens):
+    """The step plan of moe_cache_plan, then every wave through the ABI alone
+    (prefetch, wait, release): waves fit the slots, hits come first, every
+    request succeeds, and the recorded commands equal the brute-force LRU model
+    driven by the documented plan."""
+    rng = np.random.default_rng(seed)
+    cache = L.moe_cache_create_recording(_desc(2, experts, slots), 1 << 40)
+    model = LRUModel(2, experts, slots)
+    expected = []
+    half = max(1, slots // 2)
+    max_waves = (experts + half - 1) // half + 1
+    for step in range(40):
+        l = step % 2
+        ids = np.stack([rng.choice(experts, k, replace=False) for _ in range(tokens)]).astype(np.int32)
+        needed = sorted(set(ids.ravel().tolist()))
+        masks = np.full((max_waves, experts), 7, np.uint8)
+        waves = L.moe_cache_plan(cache, l, ids, masks=masks)
+        # the documented plan
+        resident = [e for e in needed if e in model.slot_of[l]]
+        order = resident + [e for e in needed if e not in model.slot_of[l]]
+        w = slots if len(order) <= slots else half
+        assert waves == [sorted(order[i:i + w]) for i in range(0, len(order), w)]
+        assert all(len(v) <= slots for v in waves)
+        for v in range(max_waves):
+            want = np.zeros(experts, np.uint8)
+            if v < len(waves):
+                want[waves[v]] = 1
+            assert np.array_equal(masks[v], want)
+        for wave in waves:
+            status, cmds = model.prefetch(l, wave)
+            assert status == "ok"
+            L.moe_cache_prefetch_async(cache, l, wave)
+            L.moe_cache_wait(cache, l)
+            L.moe_cache_release(cache, l)
+            expected += cmds + model.release(l)
+    assert L.moe_cache_trace(cache) == expected
+    assert L.moe_cache_stats(cache)[:2] == (model.hits, model.misses)
+    # validation: too few waves, an id out of range, NULL outputs
+    if slots < experts:
+        big = np.arange(experts, dtype=np.int32)
+        assert _status(L.moe_cache_plan, cache, 0, big, 1) == L.MOE_E_CAPACITY
+    assert _status(L.moe_cache_plan, cache, 0, [experts], 4) == L.MOE_E_ARG
+    assert _status(L.moe_cache_plan, cache, 2, [0], 4) == L.MOE_E_ARG
+    assert L.moe_cache_plan(cache, 0, [], 4) == []
+    L.moe_cache_destroy(cache)

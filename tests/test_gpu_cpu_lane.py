@@ -21,7 +21,7 @@ from tests.test_gpu_parity import check_close
 
 def pool_slabs(st: MoEStack, l: int):
     """Layer l's routed slabs as views of the pinned host pool the lanes read."""
-    return [st.host[l].array[e * st.slab:(e + 1) * st.slab] for e in range(st.E)]
+    return st.host_pool_slabs(l)
 
 pytestmark = pytest.mark.gpu
 

@@ -338,12 +338,19 @@ def test_route_ffn_combine_matches_separate_calls(name, T, H, I, E, k, shared, b
 PREFILL_CASES = [
     # name, T, H, I, E, k, shared, hot expert (gets a large bias), oracle rows
     ("prefill2048", 2048, 6144, 2048, 256, 8, False, None, [0, 1, 777, 2047]),
-    ("hot_expert", 300, 512, 256, 16, 4, True, 3, [0, 150, 299]),
+    # every token routes to one expert: 300 rows in four passes of up to 96 (and
+    # the 300-token shared expert), every row compared
+    ("hot_expert", 300, 512, 256, 16, 4, True, 3, None),
     ("tiny_prefill", 129, 256, 128, 16, 2, False, None, None),
     # H not a multiple of 256: the down projection takes one 128-row W2 tile per
     # workgroup, with weight groups of 2 chunks (I = 128) and of 4 (I = 256)
     ("odd_hidden_i128", 160, 384, 128, 8, 2, False, None, None),
     ("odd_hidden_i256", 200, 640, 256, 8, 2, True, None, None),
+    # H, I not multiples of 128: the automatic choice falls back to the grouped
+    # GEMV for the one-call FFN + combine as for the FFN call (prefill and the
+    # mid-size batches that would otherwise take the split path)
+    ("odd_auto_t129", 129, 160, 96, 8, 2, True, None, None),
+    ("odd_auto_t40", 40, 160, 96, 16, 4, True, None, None),
 ]
 
 
@@ -354,7 +361,7 @@ def test_prefill_mfma_parity(name, T, H, I, E, k, shared, hot, rows):
         lay.bias = np.zeros(E, np.float32)
         lay.bias[hot] = 10.0  # every token routes to this expert: more than one 128-token chunk
     ref = lay.oracle(rows)
-    idx, y, out = lay.run(L.MOE_FFN_AUTO)  # T >= 128 selects the MFMA kernels
+    idx, y, out = lay.run(L.MOE_FFN_AUTO)  # T >= 128 selects the MFMA kernels when H, I allow them
     assert np.array_equal(idx, ref["idx"])
     sel = slice(None) if rows is None else rows
     ratio = check_close(out[sel], ref["out64"][sel], f"{name} mfma")

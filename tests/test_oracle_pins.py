@@ -295,6 +295,33 @@ def test_combine_closed_form_two_experts_and_shared():
         np.testing.assert_allclose(res["out64"][t], expect, rtol=1e-12)
 
 
+def test_ffn_with_given_routing_closed_form():
+    """Steps 4-5 with routing taken as given (arbitrary slot order, weights that
+    do not sum to 1, an expert used by many tokens): out = sum_i w_i y(idx_i) +
+    shared, from the constant-expert closed form; rows restricts the output."""
+    H, I, E, k, T = 64, 32, 5, 3, 7
+    xb = synth.x_bf16(8, 0, 0, T, H)
+    params = [(2.0 ** -6, 9 + e, 2.0 ** -5) for e in range(E)]
+    slabs = [_const_expert(H, I, *p) for p in params]
+    shared_p = (2.0 ** -7, 5, 2.0 ** -4)
+    idx = np.array([[4, 0, 2], [1, 4, 3], [0, 1, 2], [3, 2, 4], [4, 3, 0], [2, 0, 1], [1, 3, 4]], np.int32)
+    w = rng.uniform(-0.5, 1.5, (T, k))
+    res = oracle.moe_ffn_routed(xb, idx, w, slabs, _const_expert(H, I, *shared_p), I)
+    for t in range(T):
+        x = np.array([oracle.bf16_to_double(int(v)) for v in xb[t]])
+        expect = sum(w[t, i] * _const_expert_output(x, I, *params[idx[t, i]]) for i in range(k))
+        expect += _const_expert_output(x, I, *shared_p)
+        np.testing.assert_allclose(res["out64"][t], expect, rtol=1e-12)
+    sub = oracle.moe_ffn_routed(xb, idx, w, slabs, None, I, rows=[5, 1])
+    for t in range(T):
+        if t in (1, 5):
+            x = np.array([oracle.bf16_to_double(int(v)) for v in xb[t]])
+            expect = sum(w[t, i] * _const_expert_output(x, I, *params[idx[t, i]]) for i in range(k))
+            np.testing.assert_allclose(sub["out64"][t], expect, rtol=1e-12)
+        else:
+            assert np.all(sub["out64"][t] == 0.0)
+
+
 def test_zero_routed_experts_leave_shared_and_k1_gives_expert():
     H, I, E, T = 64, 32, 4, 2
     xb = synth.x_bf16(6, 0, 0, T, H)
