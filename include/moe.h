@@ -433,6 +433,27 @@ int moe_cpu_lane_isa(void);
  * (MOE_E_STATE). */
 int moe_cpu_lane_force_isa(moe_cpu_lane *lane, int isa);
 
+/* ------------------------------------------------------------------ no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): moe_route_ffn_combine
+ * with its workspace in a fixed scratch array of the library instead of a
+ * caller's buffer.  Same arguments (minus the workspace), arithmetic, kernels and
+ * results (bit-identical), except that the split path's two parts run one after
+ * the other on `stream` (no helper stream, no events).  The scratch holds
+ * moe_noalloc_scratch_bytes() bytes (16 MiB) on each device, kept until the
+ * process ends: calls needing a larger workspace
+ * (moe_route_ffn_combine_workspace_bytes) return MOE_E_NOMEM before enqueuing
+ * anything -- 32 tokens at hidden 6144, intermediate 2048, 256 experts, top-8
+ * and a shared expert fit; a 2048-token chunk does not.  The call allocates
+ * nothing; the first call on a device looks the array's address up.  Every call
+ * on a device shares that device's array: calls that overlap in time on one
+ * device (on different streams, or from different threads) race. */
+size_t moe_noalloc_scratch_bytes(void);
+int moe_route_ffn_combine_noalloc(const uint16_t *x, int T, int H, int I, const float *w_router, const float *bias,
+                                  int E, int k, const void *const *expert_table, const void *shared_slab,
+                                  int32_t *topk_idx, float *topk_w, uint16_t *out, const void *prefetch,
+                                  size_t prefetch_bytes, void *stream);
+
 /* ------------------------------------------------------------------ debug
  * Dequantise matrix `which` (0 = W1, 1 = W3, 2 = W2) of a device slab into out
  * (fp32, row-major [rows x cols]); exact, for round-trip tests of the format. */

@@ -80,6 +80,8 @@ def lib():
             "moe_route_ffn_combine_workspace_bytes": ([i, i, i, i, i, i], sz),
             "moe_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp], i),
             "moe_combine": ([vp, vp, i, i, i, i, vp, vp], i),
+            "moe_noalloc_scratch_bytes": ([], sz),
+            "moe_route_ffn_combine_noalloc": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp], i),
             "moe_residual_norm": ([vp, vp, i, i, ctypes.c_float, vp, vp], i),
             "moe_debug_dequant": ([vp, i, i, i, vp, vp], i),
             "moe_expert_bytes_mx": ([i, i], sz),
@@ -337,6 +339,18 @@ def moe_route_ffn_combine(x, T, H, I, w_router, bias, E, k, expert_table, shared
                                        _ptr(shared_slab), _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(workspace),
                                        workspace_bytes, _ptr(prefetch), prefetch_bytes, _stream(stream)),
            "moe_route_ffn_combine")
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return lib().moe_noalloc_scratch_bytes()
+
+
+def moe_route_ffn_combine_noalloc(x, T, H, I, w_router, bias, E, k, expert_table, shared_slab, topk_idx, topk_w,
+                                  out, stream=None, prefetch=None, prefetch_bytes=0):
+    _check(lib().moe_route_ffn_combine_noalloc(_ptr(x), T, H, I, _ptr(w_router), _ptr(bias), E, k,
+                                               _ptr(expert_table), _ptr(shared_slab), _ptr(topk_idx), _ptr(topk_w),
+                                               _ptr(out), _ptr(prefetch), prefetch_bytes, _stream(stream)),
+           "moe_route_ffn_combine_noalloc")
 
 
 def moe_combine(y, topk_w, T, k, H, has_shared, out, stream=None):

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "router.hip", "ffn_gemv.hip", "ffn_decode.hip", "ffn_mfma.hip", "ffn_entry.hip", "cache.hip",
-           "residual.hip", "cpu_lane.cpp"]
+           "residual.hip", "noalloc.hip", "cpu_lane.cpp"]
 # host-only C++ (no HIP), built with the host compiler: the CPU lane
 HOST_SOURCES = {"cpu_lane.cpp"}
 
