@@ -1,18 +1,25 @@
 """Benchmark of the routed-expert FFN step on one MI355X.
 
-Default workload: batch-1 decode through 8 routed-MoE layers (hidden 4096, 128
-experts + 1 shared, intermediate 1536, top-8, 4-bit 32-column blocks), every
-expert resident in HBM.  One step = router + top-k, expert lookup (device
-pointer table), fused dequant + gate/up + SwiGLU, dequant + down, weighted
-combine, for all 8 layers, on one token: one moe_route_ffn_combine call per
-layer (three kernels), launched eagerly (the host stays ahead of the GPU; with
---graph, one HIP graph per step is replayed instead).
+Default workload: a 2048-token prefill chunk through 16 streamed routed-MoE
+layers (hidden 6144, 256 experts, intermediate 2048, top-8, 4-bit 32-column
+blocks, bias-free routing), the expert cache capped at 102 of 256 experts per
+layer and the full expert set in pinned host RAM (layers 8-15 reuse the expert
+weights of layers 0-7).  One step = the routers of all 16 layers, one D2H of the
+top-k ids, the library's per-layer plan (waves of half the slots, hits first),
+then per wave: its misses streamed over PCIe on two copy streams, the wait, the
+MFMA grouped-GEMM FFN of its experts (dequant + gate/up + SwiGLU, dequant +
+down), the release; and per layer the weighted combine.  Inputs of every timed
+step are resident in HBM before the timed region.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode1]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill2048_stream]
 
-Prints ONE JSON line: tokens/s through all layers, the roofline of the dominant
-kernel (dequant + gate/up + SwiGLU GEMV, timed live with HIP events on the
-stream it runs on), and the CPU oracle timed on a bounded sample.
+Prints ONE JSON line: tokens/s through all layers; `roofline` = the dominant
+kernel (the MFMA gate/up grouped GEMM, each launch of the timed steps bracketed
+by HIP events on the stream it runs on) against the HBM peak, with its MFMA
+fraction and the PCIe link's (H2D bytes over the measured copy-busy time against
+the measured pinned link peak); the CPU oracle timed on a bounded sample; and
+extra legs: the resident batch-1 decode, the streamed batch-1 decode, the tiny
+one-layer case, the other weight formats and single resident layers.
 """
 from __future__ import annotations
 
@@ -30,8 +37,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+METRIC = "routed-MoE layer tokens/s at 1 GPU; achieved HBM GB/s and PCIe H2D GB/s vs peak"
 # the one-token gate/up kernel as launched alone (units per lane, ring depth, no routing)
 GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 1, 0, 0>"
+# the prefill gate/up kernel at hidden 6144 (stages, code group, record group, pair)
+MFMA_GATE_UP_KERNEL = "mfma_ffn_kernel<true, 2, 2, 4, false>"
 
 
 def log(msg):
@@ -41,28 +51,29 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode1")
-    ap.add_argument("--inputs", type=int, default=8, help="distinct resident input steps cycled through")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay one HIP graph per step instead of launching eagerly (each replay boundary leaves "
-                         "the GPU idle ~8 us, more than the eager launches cost)")
-    ap.add_argument("--kernel-iters", type=int, default=50, help="iterations of the per-kernel event timing")
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle CPU-baseline sample")
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill2048_stream",
+                    help="streamed headline configuration (prefill2048_stream, decode32_stream, decode1_stream)")
+    ap.add_argument("--layers", type=int, default=0, help="layers of the headline stack (0 = the configuration's)")
+    ap.add_argument("--inputs", type=int, default=4, help="distinct resident input steps cycled through")
+    ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens in the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-stream", action="store_true", help="skip the streamed-decode (PCIe) leg")
+    ap.add_argument("--no-legs", action="store_true", help="only the headline (no extra legs)")
+    ap.add_argument("--decode-steps", type=int, default=400, help="timed steps of the resident batch-1 decode leg")
+    ap.add_argument("--decode-warmup", type=int, default=40)
+    ap.add_argument("--graph", action="store_true",
+                    help="resident decode leg: replay one HIP graph per step instead of launching eagerly")
+    ap.add_argument("--kernel-iters", type=int, default=50, help="iterations of the per-kernel event timing")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streamed batch-1 decode (PCIe) leg")
     ap.add_argument("--stream-workload", default="decode1_stream")
-    ap.add_argument("--stream-layers", type=int, default=0,
-                    help="layers of the streamed leg (0 = the configuration's; fewer when its host pool exceeds what "
-                         "the machine lets one process pin)")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
     ap.add_argument("--chain-steps", type=int, default=128,
-                    help="timed steps of each chained-layer run of the streamed leg (0 skips them)")
+                    help="timed steps of each chained-layer run of the streamed decode leg (0 skips them)")
     ap.add_argument("--chain-warmup", type=int, default=32)
     ap.add_argument("--cpu-lane-threads", type=int, default=14,
-                    help="worker threads of the streamed leg's CPU-lane run (0 skips it; decode workloads only)")
+                    help="worker threads of the streamed decode leg's CPU-lane run (0 skips it)")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the MXFP4 and super-block decode legs (resident and streamed)")
     ap.add_argument("--no-layer-legs", action="store_true",
@@ -70,6 +81,16 @@ def parse():
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="also run 4 plain 256 MiB device copies (reference for HBM traffic counters)")
     return ap.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def link_peak(torch, slab_bytes: int):
@@ -123,29 +144,6 @@ def link_peak(torch, slab_bytes: int):
     return best, slabs, split
 
 
-def resident_step_ms(torch, cfg, layers: int, steps: int = 8) -> float:
-    """Per-step time of a streamed configuration with every expert resident (the
-    compute the copies have to hide), on the same synthetic inputs."""
-    from routed_expert_streaming_amd.runtime import MoEStack
-
-    st = MoEStack(cfg, cap=1.0, layers=layers)
-    xs = [st.make_inputs(s) for s in range(4)]
-    out = st.new_output()
-    for s in range(2):
-        st.forward(xs[s % 4], out)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for s in range(steps):
-        st.forward(xs[s % 4], out)
-    b.record()
-    torch.cuda.synchronize()
-    st.close()
-    del st, xs, out
-    torch.cuda.empty_cache()
-    return a.elapsed_time(b) / steps
-
-
 def format_leg(torch, args, name: str, stream_name: str, fmt0_ms_per_step: float, fmt0_streaming):
     """The one-token decode with another expert weight format -- MXFP4 (E2M1
     codes, one E8M0 scale per 32 weights: 17/32 byte per weight against 20/32) or
@@ -157,22 +155,22 @@ def format_leg(torch, args, name: str, stream_name: str, fmt0_ms_per_step: float
 
     cfg = synth.get(name)
     st = MoEStack(cfg)
-    xs = [st.make_inputs(s) for s in range(args.inputs)]
+    xs = [st.make_inputs(s) for s in range(8)]
     out = st.new_output()
-    for s in range(args.warmup):
+    for s in range(args.decode_warmup):
         st.forward(xs[s % len(xs)], out)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for s in range(args.steps):
+    for s in range(args.decode_steps):
         st.forward(xs[s % len(xs)], out)
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / args.steps
+    ms = a.elapsed_time(b) / args.decode_steps
     nbytes = step_bytes(st)
     res = {"workload": cfg.name, "layers": cfg.layers, "slab_bytes": st.slab, "tokens_per_s": round(1e3 / ms, 2),
            "ms_per_step": round(ms, 4), "speedup_vs_format0": round(fmt0_ms_per_step / ms, 4),
-           "step_bytes": nbytes, "step_GBps": round(nbytes / ms / 1e6, 1), "steps": args.steps}
+           "step_bytes": nbytes, "step_GBps": round(nbytes / ms / 1e6, 1), "steps": args.decode_steps}
     st.close()
     del st, xs, out
     torch.cuda.empty_cache()
@@ -205,27 +203,47 @@ def format_leg(torch, args, name: str, stream_name: str, fmt0_ms_per_step: float
     return res
 
 
+def copy_timing_summary(torch, st, nbytes: int, steps: int, ms_step: float, link: tuple, compute_ms_step: float):
+    """PCIe figures of a streamed run from the library's copy timing: H2D bytes
+    over the measured copy-busy time (the union of the timed copy intervals on
+    both copy streams, over `steps` steps that streamed `nbytes`) against the
+    measured link peak, the step time ms_step over the busy time per step, and
+    the overlap of copies and compute."""
+    from routed_expert_streaming_amd import _lib as L
+    busy_ms, span_ms, n_timed = L.moe_cache_copy_busy(st.cache)
+    peak, one_rate, split_rate = link
+    busy_step = busy_ms / steps
+    over_busy = nbytes / (busy_ms * 1e-3) / 1e9 if busy_ms > 0 else None
+    res = {"h2d_bytes_per_step": nbytes // steps, "h2d_GBps_over_wall": round(nbytes / steps / ms_step / 1e6, 2),
+           "copy_busy_ms_per_step": round(busy_step, 3), "copies_timed": n_timed,
+           "h2d_GBps_over_copy_busy": round(over_busy, 2) if over_busy else None,
+           "link_peak_GBps": round(peak, 2), "slab_copy_one_stream_GBps": round(one_rate, 2),
+           "slab_copy_split_GBps": round(split_rate, 2), "split_copies": st.copy_stream2 is not None,
+           "frac_of_link_peak": round(over_busy / peak, 4) if over_busy else None,
+           "wall_over_copy_busy": round(ms_step / busy_step, 4) if busy_step > 0 else None,
+           "exposed_ms_per_step": round(ms_step - busy_step, 3)}
+    if compute_ms_step is not None and busy_step > 0 and compute_ms_step > 0:
+        res["compute_ms_per_step"] = round(compute_ms_step, 3)
+        # share of the shorter of copy and compute hidden under the other
+        res["overlap_frac"] = round((busy_step + compute_ms_step - ms_step) / min(busy_step, compute_ms_step), 4)
+    return res
+
+
 def streaming_leg(torch, args, resident_ms_per_step: float):
-    """The streamed decode workload: expert cache capped per layer, misses copied
-    from pinned host RAM over PCIe on a copy stream while earlier layers compute.
-    resident_ms_per_step: the same shapes with every expert resident (measured
-    here when the streamed configuration's shapes differ from the timed one's)."""
+    """The streamed batch-1 decode: expert cache capped per layer, misses copied
+    from pinned host RAM over PCIe on two copy streams while earlier layers
+    compute.  resident_ms_per_step: the same shapes with every expert resident
+    (the compute the copies have to hide)."""
     import synth
+    from routed_expert_streaming_amd import _lib as L
     from routed_expert_streaming_amd.runtime import MoEStack
 
     cfg = synth.get(args.stream_workload)
-    main = synth.get(args.workload)
-    layers = args.stream_layers or cfg.layers
-    shape = lambda c, n: (n, c.tokens, c.hidden, c.inter, c.experts, c.shared, c.top_k)
-    if shape(cfg, layers) != shape(main, main.layers):
-        resident_ms_per_step = resident_step_ms(torch, cfg, layers)
-        log(f"{cfg.name} ({layers} layers) with every expert resident: {resident_ms_per_step:.3f} ms/step")
-    log(f"streaming leg: {cfg.description}" + (f", {layers} of its {cfg.layers} layers" if layers != cfg.layers else ""))
-    st = MoEStack(cfg, layers=layers)
-    peak, one_rate, split_rate = link_peak(torch, st.slab)
-    slab_rate = split_rate if st.copy_stream2 is not None else one_rate
-    log(f"pinned H2D: {peak:.1f} GB/s (1 GiB copies), {one_rate:.1f} GB/s (back-to-back {st.slab} B slabs), "
-        f"{split_rate:.1f} GB/s (slabs split over two streams)")
+    log(f"streaming leg: {cfg.description}")
+    st = MoEStack(cfg)
+    link = link_peak(torch, st.slab)
+    log(f"pinned H2D: {link[0]:.1f} GB/s (1 GiB copies), {link[1]:.1f} GB/s (back-to-back {st.slab} B slabs), "
+        f"{link[2]:.1f} GB/s (slabs split over two streams)")
     n_in = 32
     xs = [st.make_inputs(s) for s in range(n_in)]
     out = st.new_output()
@@ -239,29 +257,32 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     h1, m1, b1 = st.stats()
+    # copy-busy time from a second run with the copies timed (timing events
+    # between copies of 11 MB slab halves lengthen these short steps, so the
+    # step time above comes from the run without them)
+    tsteps = min(args.stream_steps, 64)
+    L.moe_cache_copy_timing(st.cache, True)
+    _, _, c0 = st.stats()
+    for s in range(tsteps):
+        st.forward(xs[s % n_in], out)
+    torch.cuda.synchronize()
+    _, _, c1 = st.stats()
+    pcie = copy_timing_summary(torch, st, c1 - c0, tsteps, wall / args.stream_steps * 1e3, link,
+                               resident_ms_per_step)
+    L.moe_cache_copy_timing(st.cache, False)
+    pcie["copy_timed_steps"] = tsteps
     # chained layers with the deepest lookahead need 2*T*k slots per layer
     chained = (chained_runs(torch, st, args, xs)
                if args.chain_steps > 0 and 2 * cfg.tokens * cfg.top_k <= st.C else None)
     lane = (cpu_lane_run(torch, st, args, xs, args.stream_steps * cfg.tokens / wall)
             if args.cpu_lane_threads > 0 and st.T <= 64 and st.fmt == 0 else None)
     st.close()
-    hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
-    ms_step = wall / args.stream_steps * 1e3
-    copy_ms = nbytes / args.stream_steps / (slab_rate * 1e9) * 1e3  # copy-stream busy time at the slab copy rate
-    h2d = nbytes / wall / 1e9
-    res = {"workload": cfg.name, "layers": layers, "cache_slots_per_layer": st.C,
-           "tokens_per_s": round(args.stream_steps * cfg.tokens / wall, 2), "ms_per_step": round(ms_step, 3),
-           "hit_rate": round(hits / max(hits + misses, 1), 4), "h2d_bytes_per_step": nbytes // args.stream_steps,
-           "h2d_GBps": round(h2d, 2), "link_peak_GBps": round(peak, 2), "slab_copy_GBps": round(slab_rate, 2),
-           "slab_copy_one_stream_GBps": round(one_rate, 2), "split_copies": st.copy_stream2 is not None,
-           "h2d_frac_of_link_peak": round(h2d / peak, 4),
-           "copy_busy_ms_per_step": round(copy_ms, 3), "resident_ms_per_step": round(resident_ms_per_step, 3),
-           "wall_over_copy_busy": round(ms_step / copy_ms, 4) if copy_ms > 0 else None,
-           "exposed_ms_per_step": round(ms_step - copy_ms, 3),
-           # share of the shorter of copy and compute hidden under the other
-           "overlap_frac": (round((copy_ms + resident_ms_per_step - ms_step) / min(copy_ms, resident_ms_per_step), 4)
-                            if copy_ms > 0 and resident_ms_per_step > 0 else None),
-           "steps": args.stream_steps, "warmup": args.stream_warmup}
+    hits, misses = h1 - h0, m1 - m0
+    res = {"workload": cfg.name, "layers": st.L, "cache_slots_per_layer": st.C,
+           "tokens_per_s": round(args.stream_steps * cfg.tokens / wall, 2),
+           "ms_per_step": round(wall / args.stream_steps * 1e3, 3),
+           "hit_rate": round(hits / max(hits + misses, 1), 4), "resident_ms_per_step": round(resident_ms_per_step, 3),
+           "pcie": pcie, "steps": args.stream_steps, "warmup": args.stream_warmup}
     if chained:
         res["chained"] = chained
     if lane:
@@ -454,12 +475,12 @@ def layer_leg(torch, name: str, path: int, iters: int):
     return res
 
 
-def counter_traffic(kernel: str):
+def counter_traffic(kernel: str, profile: str):
     """HBM bytes per launch measured with FETCH_SIZE/WRITE_SIZE (scaled by a plain
-    copy of known size), from the committed profile summary; None if the kernel's
+    copy of known size), from a committed profile summary; None if the kernel's
     sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "decode1_gate_up_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     for line in open(path):
@@ -511,47 +532,50 @@ def step_bytes(stack) -> int:
     return total
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
+def oracle_sample(torch, cfg, layers: int, x_layers, wr, bias, slabs_of, shared_of, rows, threads: int):
+    """The oracle on a bounded sample: the tokens `rows` of one step through every
+    layer (router, expert FFNs, combine), input fetching outside the timed calls.
+    Returns seconds."""
+    import oracle
+    cpu_s = 0.0
+    for l in range(layers):
+        x = np.ascontiguousarray(x_layers[l][rows])
+        slabs, shared = slabs_of(l), shared_of(l)
+        t1 = time.perf_counter()
+        oracle.moe_layer(x, wr[l], bias[l], cfg.top_k, slabs, shared, cfg.inter, threads=threads)
+        cpu_s += time.perf_counter() - t1
+    return cpu_s
 
+
+def headline(torch, args, cfg):
+    """The streamed configuration through all its layers: tokens/s, the MFMA
+    gate/up kernel's roofline from the timed steps, the PCIe link's fraction."""
     import synth
+    from routed_expert_streaming_amd import _lib as L
     from routed_expert_streaming_amd.runtime import MoEStack
 
-    cfg = synth.get(args.workload)
-    if cfg.streaming:
-        raise SystemExit("the timed workload must be resident; streamed configurations run in the tests")
-    if cfg.fmt != 0:
-        raise SystemExit("MXFP4 and super-block workloads are measured by the run's mx and superblock legs (the "
-                         "per-kernel legs use format-0 calls)")
     t0 = time.time()
-    log(f"building {cfg.name}: {cfg.description}")
-    stack = MoEStack(cfg)
-    xs = [stack.make_inputs(s) for s in range(args.inputs)]
-    outs = [stack.new_output() for _ in range(args.inputs)]
-    log(f"built in {time.time() - t0:.1f}s")
+    layers = args.layers or cfg.layers
+    log(f"building {cfg.name} ({layers} layers): {cfg.description}")
+    st = MoEStack(cfg, layers=layers)
+    log(f"built in {time.time() - t0:.1f}s: {st.C} slots per layer, {len(st.host)} host weight sets of "
+        f"{st.E} x {st.slab} B pinned")
+    link = link_peak(torch, st.slab)
+    log(f"pinned H2D: {link[0]:.1f} GB/s (1 GiB copies), {link[1]:.1f} GB/s (back-to-back slabs), "
+        f"{link[2]:.1f} GB/s (slabs split over two streams)")
+    n_in = max(1, min(args.inputs, args.steps + args.warmup))
+    xs = [st.make_inputs(s) for s in range(n_in)]
+    out = st.new_output()
     dev_stream = torch.cuda.current_stream()
-
-    # warm-up (eager); with --graph, capture one graph per resident input
-    for i in range(max(args.warmup, 1)):
-        stack.forward(xs[i % args.inputs], outs[i % args.inputs])
+    for s in range(args.warmup):  # the cold start happens here
+        st.forward(xs[s % n_in], out)
     torch.cuda.synchronize()
-    graphs = None
-    if args.graph:
-        graphs = []
-        for i in range(args.inputs):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                stack.forward(xs[i], outs[i])
-            graphs.append(g)
-        for i in range(args.inputs):
-            graphs[i].replay()
-        torch.cuda.synchronize()
     log("warm-up done")
+    mfma = st.T >= 128 and st.H % 128 == 0 and st.I % 128 == 0
+    h0, m0, b0 = st.stats()
+    L.moe_cache_copy_timing(st.cache, True)
+    st.kernel_log = [] if mfma else None
+    idx_steps, marks = [], []
 
     # ---------------- timed region: K steps
     torch.cuda.synchronize()
@@ -559,7 +583,166 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(dev_stream)
     for s in range(args.steps):
-        i = s % args.inputs
+        marks.append(len(st.kernel_log) if mfma else 0)
+        st.forward(xs[s % n_in], out)
+        idx_steps.append(st.last_routing())
+    ev1.record(dev_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed = max(wall, gpu_ms / 1e3)
+    value = args.steps * st.T / elapsed
+    ms_per_step = elapsed / args.steps * 1e3
+    h1, m1, b1 = st.stats()
+    log(f"{args.steps} steps: {ms_per_step:.2f} ms/step, {value:.1f} tokens/s (events {gpu_ms:.1f} ms, "
+        f"wall {wall * 1e3:.1f} ms)")
+
+    # ---------------- the dominant kernel, from the events around each launch
+    kern = None
+    compute_ms_step = None
+    if mfma:
+        marks.append(len(st.kernel_log))
+        row = st.H // 2 + st.H // 32 * 4  # a W1 (W3) row of the slab: codes and records
+        gu_w = 2 * st.I * row
+        tot_b = tot_f = 0
+        tot_gu = tot_ffn = 0.0
+        n = 0
+        for s in range(args.steps):
+            for a, b, c, l, experts, sh in st.kernel_log[marks[s]:marks[s + 1]]:
+                sel = np.isin(idx_steps[s][l], experts)
+                pairs = int(sel.sum()) + (st.T if sh else 0)
+                toks = st.T if sh else int(sel.any(axis=1).sum())
+                tot_b += (len(experts) + (1 if sh else 0)) * gu_w + toks * st.H * 2 + pairs * st.I * 2
+                tot_f += 4 * st.H * st.I * pairs
+                tot_gu += a.elapsed_time(b)
+                tot_ffn += a.elapsed_time(c)
+                n += 1
+        compute_ms_step = tot_ffn / args.steps
+        gbps = tot_b / (tot_gu * 1e-3) / 1e9
+        tflops = tot_f / (tot_gu * 1e-3) / 1e12
+        kern = {"launches": n, "bytes_per_launch": tot_b // n, "us_per_launch": round(tot_gu * 1e3 / n, 2),
+                "flops_per_launch": tot_f // n, "GBps": gbps, "TFLOPs": tflops,
+                "ffn_ms_per_step": round(compute_ms_step, 3),
+                "gate_up_ms_per_step": round(tot_gu / args.steps, 3)}
+        log(f"gate/up: {n} launches, {kern['us_per_launch']} us and {tot_b // n} B each -> {gbps:.0f} GB/s, "
+            f"{tflops:.1f} TFLOP/s; FFN {compute_ms_step:.2f} ms/step")
+    st.kernel_log = None
+    if args.traffic_calibration:  # plain device copies of known size, the reference of the HBM counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(3)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    pcie = copy_timing_summary(torch, st, b1 - b0, args.steps, ms_per_step, link, compute_ms_step)
+    L.moe_cache_copy_timing(st.cache, False)
+    # control: a few steps with neither copy timing nor kernel events
+    ctrl = min(3, args.steps)
+    if ctrl:
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for s in range(ctrl):
+            st.forward(xs[s % n_in], out)
+        torch.cuda.synchronize()
+        pcie["control_ms_per_step_untimed"] = round((time.perf_counter() - t1) / ctrl * 1e3, 3)
+    log(f"pcie: {pcie}")
+
+    hits, misses = h1 - h0, m1 - m0
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations x 4-bit block weights (bf16 on the matrix cores), fp32 accumulation",
+        "data": "synthetic (seeded Philox inputs and random 4-bit expert weights)",
+        "config": {"workload": cfg.name, "layers": layers, "tokens_per_step": st.T, "hidden": st.H,
+                   "inter": st.I, "experts": st.E, "shared": cfg.shared, "top_k": st.k,
+                   "cache_slots_per_layer": st.C, "streamed": True, "expert_weight_sets": len(st.host),
+                   "host_pool_bytes": len(st.host) * st.E * st.slab, "router_bias": cfg.bias,
+                   "parallelism": "single GPU"},
+    }
+    if kern:
+        result["roofline"] = {
+            "bound": "hbm", "kernel": f"{MFMA_GATE_UP_KERNEL} (dequant + gate/up + SwiGLU grouped GEMM on the "
+                                      "matrix cores, one launch per wave of a layer's experts; every launch of the "
+                                      "timed steps bracketed by HIP events on its stream)",
+            "achieved": round(kern["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kern["GBps"] / HBM_PEAK_GBS, 4),
+            "traffic": counter_traffic(MFMA_GATE_UP_KERNEL, "prefill2048_mfma_counters.md"),
+            "bytes_per_launch": kern["bytes_per_launch"], "us_per_launch": kern["us_per_launch"],
+            "launches": kern["launches"],
+            "mfma": {"achieved": round(kern["TFLOPs"], 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kern["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "flops_per_launch": kern["flops_per_launch"]},
+            "pcie": {"bound": "pcie", "achieved": pcie["h2d_GBps_over_copy_busy"], "peak": pcie["link_peak_GBps"],
+                     "unit": "GB/s", "frac": pcie["frac_of_link_peak"],
+                     "wall_over_copy_busy": pcie["wall_over_copy_busy"]},
+        }
+        result["ffn"] = {"gate_up_ms_per_step": kern["gate_up_ms_per_step"], "ffn_ms_per_step": kern["ffn_ms_per_step"]}
+    result["streaming"] = {"hit_rate": round(hits / max(hits + misses, 1), 4), **pcie}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample
+    if not args.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        n = max(1, args.cpu_tokens)
+        rows = [int(r) for r in np.linspace(0, st.T - 1, n).round()]
+        xb = xs[0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        wr = [st.wr[l].cpu().numpy() for l in range(layers)]
+        bias = [None if st.bias is None else st.bias[l].cpu().numpy() for l in range(layers)]
+        cpu_s = oracle_sample(torch, cfg, layers, xb, wr, bias, st.host_pool_slabs, st.host_shared, rows, threads)
+        result["cpu_baseline"] = {"value": round(n / cpu_s, 5), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "cpu_model": cpu_model(),
+                                  "sample": f"{n} token(s) of step 0 (rows {rows}) through all {layers} layers "
+                                            f"(router, 8 expert FFNs, combine), fp64 plain-C oracle, {threads} "
+                                            f"OpenMP threads, {cpu_s:.1f} s"}
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    st.close()
+    del st, xs, out
+    torch.cuda.empty_cache()
+    return result
+
+
+def decode_leg(torch, args):
+    """Batch-1 decode through 8 resident layers (hidden 4096, 128 experts + 1
+    shared, intermediate 1536, top-8): one moe_route_ffn_combine call per layer
+    (router partials, gate/up finishing the top-k, down + combine)."""
+    import synth
+    from routed_expert_streaming_amd.runtime import MoEStack
+
+    cfg = synth.get("decode1")
+    stack = MoEStack(cfg)
+    n_in = 8
+    xs = [stack.make_inputs(s) for s in range(n_in)]
+    outs = [stack.new_output() for _ in range(n_in)]
+    dev_stream = torch.cuda.current_stream()
+    for i in range(max(args.decode_warmup, 1)):
+        stack.forward(xs[i % n_in], outs[i % n_in])
+    torch.cuda.synchronize()
+    graphs = None
+    if args.graph:
+        graphs = []
+        for i in range(n_in):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                stack.forward(xs[i], outs[i])
+            graphs.append(g)
+        for i in range(n_in):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+    steps = args.decode_steps
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(dev_stream)
+    for s in range(steps):
+        i = s % n_in
         if graphs is not None:
             graphs[i].replay()
         else:
@@ -569,29 +752,16 @@ def main():
     wall = time.perf_counter() - t_start
     gpu_ms = ev0.elapsed_time(ev1)
     elapsed = max(wall, gpu_ms / 1e3)
-    tokens = args.steps * cfg.tokens
-    value = tokens / elapsed
-    ms_per_step = elapsed / args.steps * 1e3
-    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s (events {gpu_ms:.2f} ms, "
-        f"wall {wall * 1e3:.2f} ms)")
+    ms_per_step = elapsed / steps * 1e3
+    log(f"decode leg: {steps} steps, {ms_per_step * 1e3:.1f} us/step, {steps / elapsed:.1f} tokens/s")
 
-    if args.traffic_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(3)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # ---------------- dominant kernel, timed live with events on its stream
+    # the gate/up and down kernels launched alone, timed with events on their stream
     h = torch.empty((cfg.tokens * cfg.top_k + cfg.tokens * cfg.shared, cfg.inter), dtype=torch.bfloat16,
                     device="cuda")
     stack.forward(xs[0], outs[0])  # routing of input 0 for every layer
-    # back-to-back launches of one kernel between two events: the average launch
-    # duration on the stream the kernel runs on.  The launches are captured in one
-    # HIP graph and replayed on that stream, so host launch cost (which a profiler
-    # inflates) does not show up as idle time between them.
+
+    # back-to-back launches of one kernel between two events, captured in one HIP
+    # graph and replayed, so host launch cost does not show up as idle time
     def time_launches(fn, iters):
         for l in range(stack.L):
             fn(l)
@@ -614,77 +784,108 @@ def main():
     gu_us = time_launches(lambda l: stack.gate_up_only(xs[0], l, h), args.kernel_iters)
     dn_us = time_launches(lambda l: stack.down_only(h, l), args.kernel_iters)
     gu_b, dn_b = gate_up_bytes(stack), down_bytes(stack)
-    achieved = gu_b / (gu_us * 1e-6) / 1e9
-    log(f"gate/up kernel: {gu_us:.2f} us/launch, {gu_b} B -> {achieved:.0f} GB/s; "
-        f"down kernel: {dn_us:.2f} us, {dn_b} B -> {dn_b / (dn_us * 1e-6) / 1e9:.0f} GB/s")
     sb = step_bytes(stack)
-    ffn_bytes_step = (gu_b + dn_b) * stack.L
-    ffn_us_step = (gu_us + dn_us) * stack.L
-
-    result = {
-        "metric": "routed-MoE layer tokens/s at 1 GPU (decode, all layers); achieved HBM GB/s vs peak",
-        "value": round(value, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16 activations x 4-bit block weights, fp32 accumulation",
-        "data": "synthetic (seeded Philox inputs and random 4-bit expert weights)",
-        "config": {"workload": cfg.name, "layers": cfg.layers, "tokens_per_step": cfg.tokens,
-                   "hidden": cfg.hidden, "inter": cfg.inter, "experts": cfg.experts, "shared": cfg.shared,
-                   "top_k": cfg.top_k, "resident": True, "graph": graphs is not None,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm",
-                     "kernel": f"{GATE_UP_KERNEL} (dequant + gate/up + SwiGLU, launched alone "
-                               "through moe_expert_gate_up; in the step the same kernel, with a two-deep load "
-                               "ring, also finishes the top-k)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic(GATE_UP_KERNEL),
-                     "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},
-        "ffn": {"bytes_per_step": ffn_bytes_step, "kernel_us_per_step": round(ffn_us_step, 2),
-                "achieved_GBps": round(ffn_bytes_step / (ffn_us_step * 1e-6) / 1e9, 1),
-                "down_us_per_launch": round(dn_us, 3), "down_bytes_per_launch": dn_b},
-        "step_hbm_bytes": sb,
-        "step_hbm_GBps": round(sb / (ms_per_step * 1e-3) / 1e9, 1),
-    }
-
-    # ---------------- CPU baseline: the oracle on a bounded sample
+    res = {"workload": cfg.name, "layers": cfg.layers, "resident": True, "graph": graphs is not None,
+           "tokens_per_s": round(steps / elapsed, 2), "ms_per_step": round(ms_per_step, 4), "steps": steps,
+           "warmup": args.decode_warmup,
+           "gate_up_alone": {"kernel": GATE_UP_KERNEL, "us_per_launch": round(gu_us, 3), "bytes_per_launch": gu_b,
+                             "GBps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
+                             "frac": round(gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": counter_traffic(GATE_UP_KERNEL, "decode1_gate_up_hbm_traffic.md")},
+           "down_alone": {"us_per_launch": round(dn_us, 3), "bytes_per_launch": dn_b,
+                          "GBps": round(dn_b / (dn_us * 1e-6) / 1e9, 1)},
+           "step_hbm_bytes": sb, "step_hbm_GBps": round(sb / (ms_per_step * 1e-3) / 1e9, 1)}
     if not args.no_cpu_baseline:
-        import oracle
         threads = len(os.sched_getaffinity(0))
-        n = args.cpu_tokens
-        cpu_s = 0.0
-        for l in range(stack.L):
-            x = np.concatenate([synth.x_bf16(cfg.seed, s, l, cfg.tokens, cfg.hidden) for s in range(n)])
-            slabs = stack.host_slabs(l)
-            wr = synth.router_w(cfg.seed, l, cfg.experts, cfg.hidden)
-            bias, shared = synth.router_bias(cfg, l), stack.host_shared(l)
-            t1 = time.perf_counter()  # input generation stays outside the timed calls
-            oracle.moe_layer(x, wr, bias, cfg.top_k, slabs, shared, cfg.inter, threads=threads)
-            cpu_s += time.perf_counter() - t1
-        result["cpu_baseline"] = {"value": round(n * cfg.tokens / cpu_s, 4), "unit": "tokens/s", "cores": threads,
-                                  "kind": "oracle",
-                                  "sample": f"{n} decode tokens (steps 0..{n - 1}) through all {stack.L} layers, "
-                                            f"fp64 plain-C oracle, {cpu_s:.1f} s"}
-        log(f"cpu baseline: {result['cpu_baseline']}")
+        x_layers = [np.concatenate([synth.x_bf16(cfg.seed, s, l, 1, cfg.hidden) for s in range(8)])
+                    for l in range(stack.L)]
+        wr = [synth.router_w(cfg.seed, l, cfg.experts, cfg.hidden) for l in range(stack.L)]
+        bias = [synth.router_bias(cfg, l) for l in range(stack.L)]
+        slabs = {l: stack.host_slabs(l) for l in range(stack.L)}
+        shared = {l: stack.host_shared(l) for l in range(stack.L)}
+        t_all = oracle_sample(torch, cfg, stack.L, x_layers, wr, bias, slabs.get, shared.get, list(range(8)), threads)
+        t_one = oracle_sample(torch, cfg, stack.L, x_layers, wr, bias, slabs.get, shared.get, [0], 1)
+        res["cpu_baseline"] = {"tokens_per_s": round(8 / t_all, 4), "threads": threads, "cpu_model": cpu_model(),
+                               "sample": f"8 decode tokens (steps 0..7) through all {stack.L} layers, {t_all:.1f} s",
+                               "one_thread_tokens_per_s": round(1 / t_one, 4),
+                               "one_thread_sample": f"1 decode token through all {stack.L} layers, {t_one:.1f} s"}
     stack.close()
     del stack, graphs, xs, outs
     torch.cuda.empty_cache()
-    if not args.no_stream:
-        result["streaming"] = streaming_leg(torch, args, ms_per_step)
-    if not args.no_mx:
-        result["mx"] = format_leg(torch, args, "decode1_mx", "decode1_mx_stream", ms_per_step, result.get("streaming"))
-        result["superblock"] = format_leg(torch, args, "decode1_sb", "decode1_sb_stream", ms_per_step,
-                                          result.get("streaming"))
-    if not args.no_layer_legs:
-        from routed_expert_streaming_amd import _lib as L
-        result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_SPLIT, 20)
-        result["layer_prefill2048"] = layer_leg(torch, "prefill2048_stream", L.MOE_FFN_MFMA, 3)
+    log(f"decode leg: {res}")
+    return res
+
+
+def tiny_leg(torch, args):
+    """The one-layer case (hidden 256, 16 experts, intermediate 128, top-2, 4
+    tokens, resident): microseconds per layer forward (one moe_route_ffn_combine
+    call), and the oracle on the same layer with one thread."""
+    import synth
+    from routed_expert_streaming_amd.runtime import MoEStack
+
+    cfg = synth.get("tiny")
+    st = MoEStack(cfg)
+    xs = [st.make_inputs(s) for s in range(8)]
+    out = st.new_output()
+    for s in range(50):
+        st.forward(xs[s % 8], out)
+    torch.cuda.synchronize()
+    reps = 1000
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for s in range(reps):
+        st.forward(xs[s % 8], out)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = max(a.elapsed_time(b) * 1e3, wall * 1e6) / reps
+    res = {"workload": cfg.name, "us_per_layer": round(us, 2), "tokens_per_s": round(cfg.tokens * 1e6 / us, 1),
+           "reps": reps}
+    if not args.no_cpu_baseline:
+        x = [synth.x_bf16(cfg.seed, 0, 0, cfg.tokens, cfg.hidden)]
+        wr = [synth.router_w(cfg.seed, 0, cfg.experts, cfg.hidden)]
+        slabs = st.host_slabs(0)
+        n = 20
+        t = sum(oracle_sample(torch, cfg, 1, x, wr, [None], lambda l: slabs, lambda l: None,
+                              list(range(cfg.tokens)), 1) for _ in range(n)) / n
+        res["cpu_one_thread_us_per_layer"] = round(t * 1e6, 1)
+    st.close()
+    log(f"tiny leg: {res}")
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+
+    cfg = synth.get(args.workload)
+    if not cfg.streaming:
+        raise SystemExit("the headline workload is a streamed configuration; the resident decode is an extra leg")
+    if cfg.fmt != 0:
+        raise SystemExit("MXFP4 and super-block workloads are measured by the mx and superblock legs")
+    result = headline(torch, args, cfg)
+    if not args.no_legs:
+        decode = decode_leg(torch, args)
+        result["decode1"] = decode
+        if not args.no_stream:
+            result["decode1_stream"] = streaming_leg(torch, args, decode["ms_per_step"])
+        result["tiny"] = tiny_leg(torch, args)
+        if not args.no_mx:
+            result["mx"] = format_leg(torch, args, "decode1_mx", "decode1_mx_stream", decode["ms_per_step"],
+                                      result.get("decode1_stream"))
+            result["superblock"] = format_leg(torch, args, "decode1_sb", "decode1_sb_stream", decode["ms_per_step"],
+                                              result.get("decode1_stream"))
+        if not args.no_layer_legs:
+            from routed_expert_streaming_amd import _lib as L
+            result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_SPLIT, 20)
+            result["layer_prefill2048"] = layer_leg(torch, "prefill2048_stream", L.MOE_FFN_MFMA, 3)
     print(json.dumps(result), flush=True)
 
 

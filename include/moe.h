@@ -183,6 +183,18 @@ int moe_cache_wait(moe_cache *cache, int layer, void *compute_stream);
    MOE_E_STATE while a layer has copies no moe_cache_wait has covered.  A no-op
    on a recording cache. */
 int moe_cache_split_copies(moe_cache *cache, void *second_copy_stream);
+/* Copy timing, for measuring the link: with timing on, every later slab copy
+   (each half of a split copy) is bracketed on its copy stream by two timing
+   events, the first after the copy's waits for slot releases, so a copy's
+   interval is the time its DMA took.  Turning timing on or off waits for the
+   copies in flight and discards what was measured so far.  A no-op on a
+   recording cache. */
+int moe_cache_copy_timing(moe_cache *cache, int enable);
+/* Waits for the copies issued so far, then reports, over the copies issued since
+   timing was turned on: *busy_ms = length of the union of their intervals on
+   both copy streams (the time the link was busy), *span_ms = from the first
+   start to the last end, *n_copies = copies (halves) timed.  Blocks. */
+int moe_cache_copy_busy(moe_cache *cache, double *busy_ms, double *span_ms, uint64_t *n_copies);
 /* moe_cache_prefetch_async followed by moe_cache_wait. */
 int moe_cache_prefetch(moe_cache *cache, int layer, const int32_t *experts_host, int n,
                        void *compute_stream, int *n_copies);
@@ -203,11 +215,12 @@ void moe_cache_destroy(moe_cache *cache);
  * warehouse": the host manages the cache and moves the data).  ids_host: the
  * layer's n_ids top-k expert ids of the step (host memory, repeats allowed).  The
  * distinct experts are split into waves that each fit the layer's slots: one
- * wave when there are at most slots_per_layer of them; otherwise waves of
- * max(1, slots/2), the experts already resident first and then the misses (each
- * group in ascending id), every wave sorted ascending -- so that each wave's
- * misses can stream into slots released two waves earlier while the previous
- * wave computes.  Outputs (host memory): wave_experts_host [number of distinct
+ * wave when there are at most slots_per_layer of them; otherwise the fewest
+ * waves of at most max(1, slots/2) experts, sizes differing by at most one (the
+ * first ones larger), taking the experts already resident first and then the
+ * misses (each group in ascending id), every wave sorted ascending -- so that
+ * each wave's misses can stream into slots released two waves earlier while
+ * the previous wave computes.  Outputs (host memory): wave_experts_host [number of distinct
  * experts] the experts wave by wave; wave_start_host [max_waves + 1], wave w
  * being wave_experts_host[wave_start_host[w] .. wave_start_host[w+1]); masks_host
  * NULL or [max_waves][n_experts] uint8, set to 1 at each wave's experts and 0
@@ -216,6 +229,17 @@ void moe_cache_destroy(moe_cache *cache);
  * are needed, MOE_E_ARG for an id out of range or a NULL pointer. */
 int moe_cache_plan(const moe_cache *cache, int layer, const int32_t *ids_host, int n_ids, int32_t *wave_experts_host,
                    int32_t *wave_start_host, int max_waves, uint8_t *masks_host, int *n_waves);
+/* moe_cache_plan for every layer of a step in one call: ids_host [n_layers]
+ * [ids_per_layer] (each layer's top-k ids); layer l's outputs at
+ * wave_experts_host + l*ids_per_layer, wave_start_host + l*(max_waves+1),
+ * masks_host + l*max_waves*n_experts (or NULL), n_waves_host[l].  With
+ * issue_single, every layer whose experts fit its slots (one wave) is also
+ * prefetched at once (moe_cache_prefetch_async of its wave), in layer order, so
+ * the copy stream starts right after the plan; *n_copies (may be NULL) = the
+ * misses so streamed.  Layers with several waves are left to the caller. */
+int moe_cache_plan_step(moe_cache *cache, const int32_t *ids_host, int ids_per_layer, int32_t *wave_experts_host,
+                        int32_t *wave_start_host, int max_waves, uint8_t *masks_host, int32_t *n_waves_host,
+                        int issue_single, int *n_copies);
 
 /* Test hook: a cache whose copy engine only records commands (no HIP calls).
    slot_pool is then just a base address used to form slot pointers.  If

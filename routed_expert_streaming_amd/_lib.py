@@ -70,7 +70,10 @@ def lib():
             "moe_cache_release": ([vp, i, vp], i),
             "moe_cache_stats": ([vp, u64p, u64p, u64p], i),
             "moe_cache_reset": ([vp], i),
+            "moe_cache_copy_timing": ([vp, i], i),
+            "moe_cache_copy_busy": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), u64p], i),
             "moe_cache_plan": ([vp, i, vp, i, vp, vp, i, vp, ctypes.POINTER(i)], i),
+            "moe_cache_plan_step": ([vp, vp, i, vp, vp, i, vp, vp, i, ctypes.POINTER(i)], i),
             "moe_cache_destroy": ([vp], None),
             "moe_expert_ffn_workspace_bytes": ([i, i, i, i, i, i], sz),
             "moe_expert_ffn": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, sz, i, vp], i),
@@ -233,11 +236,22 @@ def moe_cache_lookup(cache: int, layer: int, experts):
     return [slots[j] for j in range(len(experts))], hits.value
 
 
+def _i32_arg(values):
+    """(pointer, count) of int32 expert ids: numpy int32 arrays pass through, other sequences are copied."""
+    try:
+        import numpy as np
+        if isinstance(values, np.ndarray) and values.dtype == np.int32 and values.flags["C_CONTIGUOUS"]:
+            return values, int(values.size)
+    except ImportError:
+        pass
+    return _i32_array(values), len(values)
+
+
 def moe_cache_prefetch(cache: int, layer: int, experts, compute_stream=None) -> int:
-    arr = _i32_array(experts)
+    arr, n_e = _i32_arg(experts)
     n = ctypes.c_int()
-    _check(lib().moe_cache_prefetch(cache, layer, arr, len(experts), _stream(compute_stream), ctypes.byref(n)),
-           "moe_cache_prefetch")
+    _check(lib().moe_cache_prefetch(cache, layer, _ptr(arr) if hasattr(arr, "ctypes") else arr, n_e,
+                                    _stream(compute_stream), ctypes.byref(n)), "moe_cache_prefetch")
     return n.value
 
 
@@ -286,6 +300,30 @@ def moe_cache_plan(cache: int, layer: int, ids, max_waves: int = 0, masks=None):
                                 starts.ctypes.data, max_waves, None if masks is None else masks.ctypes.data,
                                 ctypes.byref(nw)), "moe_cache_plan")
     return [experts[starts[v]:starts[v + 1]].tolist() for v in range(nw.value)]
+
+
+def moe_cache_copy_timing(cache: int, enable: bool):
+    _check(lib().moe_cache_copy_timing(cache, int(bool(enable))), "moe_cache_copy_timing")
+
+
+def moe_cache_copy_busy(cache: int):
+    """-> (busy_ms, span_ms, n_copies) over the copies timed so far (blocks)."""
+    b, sp, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_uint64()
+    _check(lib().moe_cache_copy_busy(cache, ctypes.byref(b), ctypes.byref(sp), ctypes.byref(n)),
+           "moe_cache_copy_busy")
+    return b.value, sp.value, n.value
+
+
+def moe_cache_plan_step(cache: int, ids, ids_per_layer: int, wave_experts, wave_start, max_waves: int, masks,
+                        n_waves, issue_single: bool = True) -> int:
+    """moe_cache_plan for every layer (see moe.h); all arrays are caller-owned host
+    numpy arrays (ids and outputs int32, masks uint8 or None).  Returns the number
+    of misses streamed for single-wave layers."""
+    nc = ctypes.c_int()
+    _check(lib().moe_cache_plan_step(cache, _ptr(ids), ids_per_layer, _ptr(wave_experts), _ptr(wave_start),
+                                     max_waves, _ptr(masks), _ptr(n_waves), int(bool(issue_single)),
+                                     ctypes.byref(nc)), "moe_cache_plan_step")
+    return nc.value
 
 
 def moe_cache_reset(cache: int):

@@ -20,7 +20,9 @@
 // kernels of earlier ones.
 #include <algorithm>
 #include <cstring>
+#include <deque>
 #include <memory>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -68,6 +70,13 @@ struct Engine {
     virtual int clear_table() = 0;
     // later copies in two halves, the second on stream2 (nullptr: one stream)
     virtual int split_copies(hipStream_t) { return MOE_OK; }
+    // copy timing (see HipEngine)
+    virtual int set_timing(bool) { return MOE_OK; }
+    virtual int copy_busy(double *busy_ms, double *span_ms, uint64_t *n) {
+        *busy_ms = *span_ms = 0.0;
+        *n = 0;
+        return MOE_OK;
+    }
 };
 
 struct HipEngine final : Engine {
@@ -99,6 +108,12 @@ struct HipEngine final : Engine {
     ~HipEngine() override {
         if (copy_stream) (void)hipStreamSynchronize(copy_stream);
         if (copy_stream2) (void)hipStreamSynchronize(copy_stream2);
+        for (auto &p : ev_pend) {
+            (void)hipEventDestroy(p.first);
+            (void)hipEventDestroy(p.second);
+        }
+        for (auto e : ev_pool) (void)hipEventDestroy(e);
+        if (t_ref) (void)hipEventDestroy(t_ref);
         for (auto e : ready_ev)
             if (e) (void)hipEventDestroy(e);
         for (auto e : ready_ev2)
@@ -124,14 +139,108 @@ struct HipEngine final : Engine {
     // on the second, so two DMA engines share the link (back-to-back slab copies
     // on one stream leave it ~4% below what one large copy reaches).
     int copy(int, int, int, void *dst, const void *src, size_t bytes) override {
-        if (!copy_stream2 || bytes < 8192) {
-            MOE_TRY_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, copy_stream));
+        if (!copy_stream2 || bytes < 8192) return timed_copy(dst, src, bytes, copy_stream);
+        const size_t h = (bytes / 2) & ~(size_t)4095;
+        int rc = timed_copy(dst, src, h, copy_stream);
+        if (rc != MOE_OK) return rc;
+        return timed_copy((char *)dst + h, (const char *)src + h, bytes - h, copy_stream2);
+    }
+
+    // ---- copy timing: with timing on, each copy is bracketed by two timing
+    // events on its stream (the first after the copy's release waits), and the
+    // completed pairs become intervals relative to a reference event; the busy
+    // time of the link is the length of the union of the intervals of both
+    // streams.
+    bool timing = false;
+    hipEvent_t t_ref = nullptr;
+    std::vector<hipEvent_t> ev_pool;
+    std::deque<std::pair<hipEvent_t, hipEvent_t>> ev_pend;
+    std::vector<std::pair<double, double>> spans;  // ms after t_ref
+
+    int take_event(hipEvent_t *e) {
+        if (!ev_pool.empty()) {
+            *e = ev_pool.back();
+            ev_pool.pop_back();
             return MOE_OK;
         }
-        const size_t h = (bytes / 2) & ~(size_t)4095;
-        MOE_TRY_HIP(hipMemcpyAsync(dst, src, h, hipMemcpyHostToDevice, copy_stream));
-        MOE_TRY_HIP(hipMemcpyAsync((char *)dst + h, (const char *)src + h, bytes - h, hipMemcpyHostToDevice,
-                                   copy_stream2));
+        MOE_TRY_HIP(hipEventCreate(e));  // timing events
+        return MOE_OK;
+    }
+    // completed pairs -> spans (pairs complete in order per stream; the queue
+    // mixes both streams, so stop at the first one not done)
+    int harvest(bool all) {
+        while (!ev_pend.empty()) {
+            auto [a, b] = ev_pend.front();
+            if (all) {
+                MOE_TRY_HIP(hipEventSynchronize(b));
+            } else {
+                const hipError_t q = hipEventQuery(b);
+                if (q == hipErrorNotReady) break;
+                if (q != hipSuccess) return moe::fail_hip(q, "hipEventQuery(copy timing)");
+            }
+            float t0 = 0.f, t1 = 0.f;
+            MOE_TRY_HIP(hipEventElapsedTime(&t0, t_ref, a));
+            MOE_TRY_HIP(hipEventElapsedTime(&t1, t_ref, b));
+            spans.emplace_back(t0, t1);
+            ev_pool.push_back(a);
+            ev_pool.push_back(b);
+            ev_pend.pop_front();
+        }
+        return MOE_OK;
+    }
+    int timed_copy(void *dst, const void *src, size_t bytes, hipStream_t st) {
+        if (!timing) {
+            MOE_TRY_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, st));
+            return MOE_OK;
+        }
+        int rc = ev_pend.size() >= 64 ? harvest(false) : MOE_OK;
+        if (rc != MOE_OK) return rc;
+        hipEvent_t a = nullptr, b = nullptr;
+        rc = take_event(&a);
+        if (rc == MOE_OK) rc = take_event(&b);
+        if (rc != MOE_OK) return rc;
+        MOE_TRY_HIP(hipEventRecord(a, st));
+        MOE_TRY_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, st));
+        MOE_TRY_HIP(hipEventRecord(b, st));
+        ev_pend.emplace_back(a, b);
+        return MOE_OK;
+    }
+    int set_timing(bool on) override {
+        int rc = sync();
+        if (rc == MOE_OK) rc = harvest(true);
+        if (rc != MOE_OK) return rc;
+        spans.clear();
+        timing = on;
+        if (on) {
+            if (!t_ref) MOE_TRY_HIP(hipEventCreate(&t_ref));
+            MOE_TRY_HIP(hipEventRecord(t_ref, copy_stream));
+        }
+        return MOE_OK;
+    }
+    int copy_busy(double *busy_ms, double *span_ms, uint64_t *n) override {
+        int rc = sync();
+        if (rc == MOE_OK) rc = harvest(true);
+        if (rc != MOE_OK) return rc;
+        std::vector<std::pair<double, double>> v(spans);
+        std::sort(v.begin(), v.end());
+        double busy = 0.0, cur0 = 0.0, cur1 = 0.0;
+        bool open = false;
+        for (const auto &iv : v) {
+            if (open && iv.first <= cur1) {
+                cur1 = std::max(cur1, iv.second);
+                continue;
+            }
+            if (open) busy += cur1 - cur0;
+            cur0 = iv.first;
+            cur1 = iv.second;
+            open = true;
+        }
+        if (open) busy += cur1 - cur0;
+        *busy_ms = busy;
+        *span_ms = v.empty() ? 0.0 : std::max_element(v.begin(), v.end(), [](auto &x, auto &y) {
+                                         return x.second < y.second;
+                                     })->second - v.front().first;
+        *n = v.size();
         return MOE_OK;
     }
     int split_copies(hipStream_t s2) override {
@@ -544,22 +653,66 @@ extern "C" int moe_cache_plan(const moe_cache *c, int layer, const int32_t *ids_
     for (int e = 0; e < E; ++e)
         if (seen[e] && slot_of[e] < 0) order.push_back(e);
     const int n = (int)order.size();
-    const int w = n <= Cs ? Cs : std::max(1, Cs / 2);
-    const int waves = (n + w - 1) / w;
+    // one wave if they fit; else the fewest waves of at most half the slots,
+    // their sizes differing by at most one (the first n % waves one larger)
+    const int half = std::max(1, Cs / 2);
+    const int waves = n == 0 ? 0 : n <= Cs ? 1 : (n + half - 1) / half;
     if (waves > max_waves) return moe::fail(MOE_E_CAPACITY, "cache_plan: %d waves > max_waves %d", waves, max_waves);
     if (masks_host) std::memset(masks_host, 0, (size_t)max_waves * E);
     wave_start_host[0] = 0;
+    int b = 0;
     for (int v = 0; v < waves; ++v) {
-        const int b = v * w, e_ = std::min(n, b + w);
+        const int e_ = b + n / waves + (v < n % waves ? 1 : 0);
         std::sort(order.begin() + b, order.begin() + e_);
         for (int i = b; i < e_; ++i) {
             wave_experts_host[i] = order[i];
             if (masks_host) masks_host[(size_t)v * E + order[i]] = 1;
         }
         wave_start_host[v + 1] = e_;
+        b = e_;
     }
     *n_waves = waves;
     return MOE_OK;
+}
+
+extern "C" int moe_cache_plan_step(moe_cache *c, const int32_t *ids_host, int ids_per_layer,
+                                   int32_t *wave_experts_host, int32_t *wave_start_host, int max_waves,
+                                   uint8_t *masks_host, int32_t *n_waves_host, int issue_single, int *n_copies) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache_plan_step: NULL cache");
+    if (ids_per_layer < 0 || (ids_per_layer > 0 && !ids_host) || !wave_experts_host || !wave_start_host ||
+        !n_waves_host || max_waves < 1)
+        return moe::fail(MOE_E_ARG, "cache_plan_step: ids_per_layer=%d max_waves=%d or a NULL pointer", ids_per_layer,
+                         max_waves);
+    const int Ln = c->d.n_layers, E = c->d.n_experts;
+    const size_t per = (size_t)std::max(ids_per_layer, 1);
+    int copies = 0;
+    for (int l = 0; l < Ln; ++l) {
+        int32_t *we = wave_experts_host + (size_t)l * per;
+        int32_t *ws = wave_start_host + (size_t)l * (max_waves + 1);
+        int nw = 0;
+        int rc = moe_cache_plan(c, l, ids_host + (size_t)l * ids_per_layer, ids_per_layer, we, ws, max_waves,
+                                masks_host ? masks_host + (size_t)l * max_waves * E : nullptr, &nw);
+        if (rc != MOE_OK) return rc;
+        n_waves_host[l] = nw;
+        if (issue_single && nw == 1) {
+            int nc = 0;
+            rc = moe_cache_prefetch_async(c, l, we, ws[1], &nc);
+            if (rc != MOE_OK) return rc;
+            copies += nc;
+        }
+    }
+    if (n_copies) *n_copies = copies;
+    return MOE_OK;
+}
+
+extern "C" int moe_cache_copy_timing(moe_cache *c, int enable) {
+    if (!c) return moe::fail(MOE_E_ARG, "cache_copy_timing: NULL cache");
+    return c->engine->set_timing(enable != 0);
+}
+
+extern "C" int moe_cache_copy_busy(moe_cache *c, double *busy_ms, double *span_ms, uint64_t *n_copies) {
+    if (!c || !busy_ms || !span_ms || !n_copies) return moe::fail(MOE_E_ARG, "cache_copy_busy: NULL pointer");
+    return c->engine->copy_busy(busy_ms, span_ms, n_copies);
 }
 
 extern "C" int moe_cache_split_copies(moe_cache *c, void *second_copy_stream) {

@@ -1,167 +1,147 @@
 // Expert FFN for many tokens per expert (prefill): grouped GEMM on MFMA with
-// the 4-bit weight tiles dequantised in the kernel.
+// the 4-bit weights dequantised in registers.
 //
 // The multi-token case is a dense contraction per expert: the tokens routed to
-// expert e (gathered through the token->expert permutation) form an M_e x H
-// activation matrix that meets the expert's W1/W3 (H -> I) and then W2 (I -> H).
-// A workgroup owns one expert and one 128-row N tile of the weights and covers
-// the expert's tokens in M chunks of up to 96, so at prefill sizes (about 64
-// tokens per expert) every weight byte is read from HBM once.
+// expert e (gathered through the token->expert permutation) form an M_e x K
+// activation matrix that meets the expert's W1/W3 (K = H -> I) and then W2
+// (K = I -> H).  A workgroup (8 waves) owns one expert and 256 rows of W1 and
+// of W3 (gate/up) or 512 rows of W2 (down) and covers the expert's tokens in
+// passes of up to 96, so at prefill sizes (about 64 tokens per expert) every
+// weight byte is read from HBM once and every activation tile read from L2
+// serves 512 weight rows.
 //
-// The K dimension streams in chunks of 64 columns.  Direct global->LDS loads
-// (global_load_lds_dwordx4) fill two rings: the activation tiles, one chunk per
-// stage, S stages deep; and the weights (codes and (scale, min) records), G
-// chunks per buffer, two buffers, so that each row's codes come as one G*32-byte
-// piece and its records as one G*8-byte piece (every row is a separate access,
-// and small per-row pieces bound the kernel well before HBM does).  While a
-// chunk is multiplied the next S-1 activation chunks and the next weight group
-// are in flight, and no registers hold data on its way to LDS.  Each wave loads its
-// own 32 weight rows; the activation tile is shared and XOR-swizzled in 16-byte
-// units so that the A-operand reads hit distinct banks.  One barrier per chunk:
-// each wave first waits (exact vmcnt) for its own loads of the chunk, the
-// barrier then makes every wave's loads visible and frees the buffer that the
-// chunk loads issued next will overwrite.  Each wave owns 32 N columns (of W1
-// and of W3 for gate/up): it dequantises its B operand from LDS into bf16
-// registers (scale*q + min in fp32, rounded to bf16) and accumulates
-// v_mfma_f32_16x16x32_bf16 products in fp32.  Workgroups are numbered so that
-// every tile of one expert runs on the same XCD, where the expert's gathered
-// activation rows are shared through that XCD's L2.
-//
-// Lane layout of v_mfma_f32_16x16x32_bf16 (checked on gfx950): lane l holds
+// Weights go from HBM straight into registers, already in the lane order of
+// the MFMA B operand, so they need neither LDS nor any synchronisation between
+// waves.  v_mfma_f32_16x16x32_bf16 (checked on gfx950: lane l holds
 // A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16] for j < 8, and C[4*(l/16)+j][l%16]
-// for j < 4.
+// for j < 4) is fed with the K dimension permuted inside each 128-column group
+// (four 32-column blocks): lane quarter q = l/16 owns block q of the group, and
+// MFMA step s (of 4) takes the block's columns 8s..8s+7.  So a lane loads the 16
+// code bytes of one block of its weight row (one 16-row tile: 16 rows x 64
+// contiguous bytes per load instruction), and each of the block's four 8-column
+// words is one B operand.  A sum over K is the same in any order of K, and the
+// activations (A operand) are read in the same permuted order from LDS.
+// The (scale, min) records of 16 blocks (four groups) come in one 16-byte load
+// per lane (64 contiguous bytes per row per instruction), lane quarter q taking
+// blocks 4q..4q+3, straight into a per-wave LDS area in lane order, where the
+// record each lane needs in each of the four groups (that of the block it owns)
+// is one 4-byte read away.  Codes run 2 groups ahead in a register ring,
+// records one 4-group step ahead.
+//
+// Activations: the workgroup copies each group's tile (the pass's token rows x
+// 128 columns, bf16) into an LDS ring of 3 stages with direct global->LDS loads
+// (global_load_lds_dwordx4), 2 groups ahead; row m's 16-byte unit u sits at
+// unit position u ^ (m % 16), so that the 16 rows an A-operand read touches hit
+// distinct banks.  One barrier per group: each wave first waits (exact vmcnt,
+// from the fixed issue order) until its own part of the next group's tile has
+// landed; the barrier then makes every wave's part visible and frees the stage
+// the next copy overwrites.  Weights are dequantised per 8-column word (scale*q
+// + min in fp32, rounded to bf16) and the products accumulate in fp32.
+// Workgroups are numbered so that every tile of one expert runs on the same
+// XCD, where the expert's gathered activation rows are shared through the L2.
+//
+// Every load a wave issues in the K loop is SGPR base + 32-bit lane offset, and
+// the code ring slot of group g is g % 2, a constant of the 4-group unrolled
+// body: no 64-bit per-lane pointers and no register copies of loads in flight,
+// either of which made the compiler drain every load in flight once per group.
+// Measured at the 2048-token prefill shape (one layer, all 256 experts): the
+// weight stream alone runs at 5.7 TB/s in this pattern, the kernel at about
+// 2.5 TB/s; counters put the matrix cores at about 22% of SIMD time and the
+// dequantisation (about 5 VALU instructions per MFMA) at about 31%, rarely
+// co-executing -- the compute issue, not HBM, bounds it.
 #include "common.h"
 #include "dequant.h"
 #include "ffn.h"
-#ifndef MOE_EXP_SCHED
-#define MOE_EXP_SCHED 0
-#endif
 
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kNT = 128;       // weight rows (N) of each matrix per workgroup
-constexpr int kKC = 64;        // columns (K) per chunk
-constexpr int kMaxMT = 6;      // 16-row M tiles per pass
-constexpr int kMC = 16 * kMaxMT;
-constexpr int kXRow = kKC * 2; // bytes of one activation row of a chunk (8 units of 16 B)
-constexpr int kXcds = 8;       // workgroups are dealt to the XCDs round-robin
-#ifndef MOE_MFMA_STAGES
-#define MOE_MFMA_STAGES 2
+#ifndef MOE_MFMA_SCHED_BARRIER
+#define MOE_MFMA_SCHED_BARRIER 0
 #endif
-#ifndef MOE_MFMA_REC_GROUP
-#define MOE_MFMA_REC_GROUP 4
+#ifndef MOE_MFMA_MAX_MT
+#define MOE_MFMA_MAX_MT 6
 #endif
-// Activation ring depth (12 KB stages; the tiles are L2 hits, shared by all
-// tiles of an expert, so one chunk of lead hides them) and the record group of
-// two-matrix workgroups; with the weight rings two workgroups fit a CU.
-constexpr int kStagesGateUp = MOE_MFMA_STAGES;
-constexpr int kStagesDown = MOE_MFMA_STAGES;
-constexpr int kRecGroup = MOE_MFMA_REC_GROUP;
+#ifndef MOE_MFMA_CODE_AHEAD
+#define MOE_MFMA_CODE_AHEAD 2
+#endif
+#ifndef MOE_MFMA_WAVES
+#define MOE_MFMA_WAVES 8
+#endif
+constexpr int kWaves = MOE_MFMA_WAVES;   // waves per workgroup (4, 8 or 16: one, two or four per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTM = 32 / kWaves;         // 16-row weight tiles per wave (512 rows per workgroup)
+constexpr int kRowsGateUp = 256;         // rows of W1 (and of W3) per workgroup
+constexpr int kRowsDown = 512;           // rows of W2 per workgroup
+constexpr int kGK = 128;                 // columns per group (4 blocks of 32)
+constexpr int kMaxMT = MOE_MFMA_MAX_MT;  // 16-row M tiles per pass
+constexpr int kMC = 16 * kMaxMT;         // tokens per pass
+constexpr int kXRow = kGK * 2;           // bytes of one activation row of a group (16 units of 16 B)
+constexpr int kStages = 3;               // activation ring stages
+constexpr int kAhead = 2;                // activation groups copied ahead (kStages - 1)
+constexpr int kCodeAhead = MOE_MFMA_CODE_AHEAD;  // code groups in the register ring
+constexpr int kXcds = 8;                 // workgroups are dealt to the XCDs round-robin
+static_assert(kAhead == kStages - 1, "the stage a copy overwrites is the one read a step earlier");
+static_assert(kCodeAhead == 2 || kCodeAhead == 4, "code ring slots are addressed by the step index mod 4");
+static_assert(kWaves == 4 || kWaves == 8 || kWaves == 16, "workgroup of 4, 8 or 16 waves");
 
-// Activation ring stage: one chunk's tile, row r's 16-byte unit u stored at unit
-// position u ^ (r & 7).
 struct __attribute__((aligned(16))) XStage {
     uint8_t x[kMC * kXRow];
 };
 
-// Weight rings, per wave (32 rows of each of NMAT matrices) a block in each:
-//   codes   [NMAT][32 rows][G*32 B], one group of G chunks per buffer: row r's
-//           16-byte unit u at unit position u ^ swz(r), so that the B-operand
-//           reads of 16 rows hit distinct banks
-//   records [NMAT][32 rows][R*8 B], one group of R chunks per buffer, at least
-//           1 KB: every 64-lane 16-byte load fills 1 KB (with one matrix and
-//           R = 2, lanes beyond 32 repeat the first ones into the rest)
-// A row's G*32 code bytes (R*8 record bytes) are fetched by adjacent lanes as
-// one piece: the memory pipeline tracks a bounded number of requests per CU, and
-// a request carries one row's piece of at most 64 bytes, so bytes per row and
-// fetch set the kernel's load bandwidth well below HBM's.
-template <int NMAT, int G, int R>
-struct WLayout {
-    static constexpr int row_code = G * 32;                  // code bytes of one row and group
-    static constexpr int codes = NMAT * 32 * row_code;        // per wave
-    static constexpr int code_loads = codes / 1024;           // 16-byte loads per wave and group
-    static constexpr int row_rec = R * 8;                     // record bytes of one row and group
-    static constexpr int recs = NMAT * 32 * row_rec < 1024 ? 1024 : NMAT * 32 * row_rec;
-    static constexpr int rec_loads = recs / 1024;
-    static constexpr int rec_lanes = NMAT * 32 * row_rec / 16;  // lanes with distinct data
-    // unit swizzle of row r (2G units per row): for any one unit, 16 rows that
-    // start at a multiple of 16 land in 16 distinct 16-byte slots of a 256-byte
-    // bank window
-    __device__ static int swz(int r) { return (r >> (G == 2 ? 2 : 1)) & (2 * G - 1); }
-};
-
-// Loads a wave may still have in flight when step c waits, such that chunk c's
-// activations, its code group and its record group have all landed (vmcnt
-// counts a wave's loads in issue order).  Issue order: records of group 0 (NR
-// loads), codes of group 0 (NC), activation stages 0 .. S-2 (P each); then step
-// j issues stage j+S-1, the codes of group j/G + 1 when G divides j and the
-// records of group j/R + 1 when R divides j.  The count is the number of loads
-// issued, before step c, after the last of the three it needs.
-constexpr int newer_loads(int S, int P, int G, int NC, int R, int NR, int c) {
-    int total = NR + NC, pos_x = 0, pos_code = NR + NC, pos_rec = NR;
-    for (int b = 0; b < S - 1; ++b) {
-        total += P;
-        if (b == c) pos_x = total;
-    }
-    for (int j = 0; j < c; ++j) {
-        total += P;
-        if (j + S - 1 == c) pos_x = total;
-        if (j % G == 0) {
-            total += NC;
-            if (j / G + 1 == c / G) pos_code = total;
-        }
-        if (j % R == 0) {
-            total += NR;
-            if (j / R + 1 == c / R) pos_rec = total;
-        }
-    }
-    int need = pos_x > pos_code ? pos_x : pos_code;
-    need = need > pos_rec ? need : pos_rec;
-    return total - need;
-}
-// The same for every step at position b of a loop unrolled by U (a multiple of
-// S, G and R: the pattern repeats with period U after the first U steps).
-constexpr int vm_allow(int S, int P, int G, int NC, int R, int NR, int U, int b) {
-    int m = newer_loads(S, P, G, NC, R, NR, b);
-    for (int r = 1; r < 4; ++r) {
-        const int v = newer_loads(S, P, G, NC, R, NR, b + r * U);
-        m = v < m ? v : m;
-    }
-    return m;
-}
-constexpr int lcm(int a, int b) {
-    int x = a, y = b;
-    while (y) {
-        const int t = x % y;
-        x = y;
-        y = t;
-    }
-    return a / x * b;
-}
-
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(1))) const moe_u32x4 gu32x4;
 
-// Direct global->LDS load: lane l's 16 bytes from g land at LDS byte lds + 16*l;
-// lds must be the same in every lane.  Written as inline asm
-// because the compiler, when it sees these loads, makes every later LDS read
-// wait for all of them (it cannot tell the ring's stages apart), which would
-// drain the ring each chunk; completion is tracked with explicit vmcnt waits
-// instead (the instructions have no register results).
 __device__ __forceinline__ uint32_t lds_addr(const void *lds) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8 *)lds);
 }
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds));
+// Direct global->LDS load: lane l's 16 bytes from g land at LDS byte lds + 16*l
+// (lds uniform).  Written as inline asm because the compiler, seeing these
+// loads, would make every later LDS read wait for all of them (it cannot tell
+// the ring's stages apart); completion is tracked with explicit vmcnt waits
+// instead.  The memory clobber keeps the compiler's own loads in program order
+// around it, which the wait counts rely on.
+// base (uniform, in SGPRs) + off (this lane's 32-bit byte offset)
+__device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 constexpr int kWaitVm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
 
+// Loads a wave may still have in flight at the end of step gstep such that the
+// activation tile gstep + 1 has landed (vmcnt counts a wave's loads in issue
+// order).  Issue order: the records of step 0 (TM loads); for c < A: tile c (P
+// loads) and, for c < D, the codes of group c (TM loads); then per step s:
+// [records of step s/4 + 1 when s % 4 == 0], tile s + A, codes of group s + D.
+// gstep < 0: the wait before step 0, for tile 0.
+constexpr int loads_after_tile(int A, int D, int P, int TM, int gstep) {
+    const int t = gstep + 1;
+    int count = 0;
+    bool seen = false;
+    for (int c = 0; c < A; ++c) {
+        if (seen) count += P;
+        if (c == t) seen = true;
+        if (c < D && seen) count += TM;
+    }
+    for (int s = 0; s <= gstep; ++s) {
+        if (s % 4 == 0 && seen) count += TM;
+        if (seen) count += P;
+        if (s + A == t) seen = true;
+        if (seen) count += TM;
+    }
+    return count;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt %0" ::"n"(kWaitVm(N)) : "memory");
+}
+
 // Workgroup barrier without a memory fence (a fence would wait for every load
-// in flight); the asm clobbers keep the compiler from moving memory accesses
-// across it, and this wave's LDS reads are complete before it arrives.
+// in flight); this wave's LDS reads are complete before it arrives.
 __device__ __forceinline__ void ring_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -175,8 +155,8 @@ __device__ __forceinline__ void ring_barrier() {
 //   bits 4-7 into 0x5400 (64, ulp 1/16)   ->   64 + q
 // so w & 0x000F000F | 0x64006400 holds columns 0 and 4, w & 0x00F000F0 |
 // 0x54005400 columns 1 and 5, and the same on w >> 8 columns 2, 6 and 3, 7:
-// four extractions for one shift.  v_fma_mix_f32 widens each half and computes
-// scale*(base + q) + (min - base*scale) in fp32 with one rounding, which equals
+// four extractions for one shift.  Each half is widened and scale*(base + q) +
+// (min - base*scale) computed in fp32 with one rounding, which equals
 // fmaf(scale, q, min) whenever min - base*scale is exact in fp32 (scale and min
 // within 2^12 of each other's magnitude); then round to bf16 in natural order.
 __device__ __forceinline__ float fma_half(uint32_t pair, int hi, float sc, float c) {
@@ -230,11 +210,8 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t p
     return r;
 }
 
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, const Dequant &d) {
-    const float sc = fp16_bits_to_f32(rec & 0xFFFFu);
-    const float mn = fp16_bits_to_f32(rec >> 16);
-    const float c_lo = fmaf(-1024.0f, sc, mn);
-    const float c_hi = fmaf(-64.0f, sc, mn);
+// sc = the block's scale, c_lo = min - 1024*scale, c_hi = min - 64*scale (fp32)
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, float sc, float c_lo, float c_hi, const Dequant &d) {
     const uint32_t c8 = codes >> 8;
     const uint32_t p0 = and_or(codes, d.mask_lo, d.magic_lo);  // columns 0, 4
     const uint32_t p1 = and_or(codes, d.mask_hi, d.magic_hi);  // columns 1, 5
@@ -248,22 +225,28 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, uint32_t rec, const
     return __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, w45, w67));
 }
 
-// NMAT weight matrices of 128 rows per workgroup: W1 and W3 for gate/up; for
-// the down projection two 128-row tiles of W2 (PAIR, H a multiple of 256, so
-// that every activation tile loaded serves 256 weight rows) or one.
-template <bool GATEUP, int S, int G, int R, bool PAIR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_ffn_kernel(moe::FfnArgs a, int ntiles,
-                                                                                           int n_groups) {
-    constexpr int NMAT = GATEUP || PAIR ? 2 : 1;
-    constexpr int kTileN = GATEUP ? kNT : NMAT * kNT;  // output columns per workgroup
-    using WL = WLayout<NMAT, G, R>;
-    static_assert(S >= 2, "the activation ring needs two stages at least");
-    static_assert((G == 2 || G == 4) && (R == 2 || R == 4 || R == 8), "weight group sizes");
-    static_assert(S * sizeof(XStage) + 2 * 4 * (WL::codes + WL::recs) + 2 * kMC * sizeof(int) <= 80 * 1024,
-                  "two workgroups per CU");
-    constexpr int U = lcm(lcm(S, G), R);  // steps per unrolled loop body
-    const int K = GATEUP ? a.H : a.I;   // reduction length (a multiple of 64 * G and 64 * R)
-    const int nrows = GATEUP ? a.I : a.H;  // weight rows (output columns)
+// 16 bytes at base (uniform) + off (this lane's 32-bit byte offset): one load
+// with the base in SGPRs, so a lane keeps only its 32-bit offsets
+__device__ __forceinline__ uint4 load_u4(const uint8_t *base, uint32_t off) {
+    // the empty asm hides that off is loop-invariant: otherwise the compiler
+    // hoists base' + off into a 64-bit per-lane pointer (two VGPRs per load, and
+    // a 64-bit add per step into registers whose previous load may still be in flight)
+    asm volatile("" : "+v"(off));
+    const moe_u32x4 v = *(const gu32x4 *)(base + off);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// GATEUP: W1 and W3 (tiles 0, 1 of each: the wave's 32 rows), h = bf16(silu(g) * u);
+// otherwise W2 (tiles 0..3: the wave's 64 rows), y = W2 h.
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void mfma_ffn_kernel(moe::FfnArgs a,
+                                                                                                   int ntiles,
+                                                                                                   int n_groups) {
+    const int K = GATEUP ? a.H : a.I;        // reduction length (a multiple of 128)
+    const int nrows = GATEUP ? a.I : a.H;    // weight rows (output columns)
+    const int wg_rows = GATEUP ? kRowsGateUp : kRowsDown;
     // Which group and tile: by default every tile of one expert on the same XCD
     // (its activation tiles are then fetched into one L2).  Compact (a launch
     // where few groups qualify, the many-token experts of the split path):
@@ -271,15 +254,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     // in group order, so each expert's tiles are dealt over all XCDs and the
     // XCDs get equal shares however the qualifying experts are numbered.
     int g, tile;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (a.compact) {
-        __shared__ int s_g, s_wcnt[4];
+        __shared__ int s_g, s_wcnt[kThreads / 64];
         const int j = blockIdx.x / ntiles;
         tile = blockIdx.x % ntiles;
-        const int t = threadIdx.x, ln = t & 63, w = t >> 6;
-        if (t == 0) s_g = -1;
+        if (tid == 0) s_g = -1;
         int before = 0;  // qualifying groups in earlier chunks
-        for (int c0 = 0; c0 < a.n_routed_groups; c0 += 256) {
-            const int gg = c0 + t;
+        for (int c0 = 0; c0 < a.n_routed_groups; c0 += kThreads) {
+            const int gg = c0 + tid;
             bool act = false;
             if (gg < a.n_routed_groups) {
                 const int M = a.count[gg];
@@ -287,12 +271,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             }
             const uint64_t bal = __ballot(act);
             __syncthreads();  // s_wcnt of the previous chunk has been read
-            if (ln == 0) s_wcnt[w] = __popcll(bal);
+            if (lane == 0) s_wcnt[wave] = __popcll(bal);
             __syncthreads();
             int wb = 0;
-            for (int v = 0; v < w; ++v) wb += s_wcnt[v];
-            if (act && before + wb + __popcll(bal & ((1ull << ln) - 1)) == j) s_g = gg;
-            before += s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+            for (int v = 0; v < wave; ++v) wb += s_wcnt[v];
+            if (act && before + wb + __popcll(bal & ((1ull << lane) - 1)) == j) s_g = gg;
+            for (int v = 0; v < kThreads / 64; ++v) before += s_wcnt[v];
         }
         __syncthreads();
         g = s_g;
@@ -305,8 +289,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         g = (i / ntiles) * kXcds + xcd;
         tile = i % ntiles;
     }
+    // g and tile are uniform over the workgroup; saying so keeps the slab pointer
+    // in SGPRs, so every weight load is SGPR base + 32-bit lane offset
+    g = __builtin_amdgcn_readfirstlane(g);
+    tile = __builtin_amdgcn_readfirstlane(tile);
     if (g >= n_groups) return;
-    const int n0 = tile * kTileN;
+    const int n0 = tile * wg_rows;
 
     // resolve the group: routed expert g (grouped), or the shared expert
     const uint8_t *slab;
@@ -315,87 +303,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     if (routed) {
         M = __builtin_amdgcn_readfirstlane(a.count[g]);  // uniform: M-tile checks become scalar branches
         if (M == 0 || M < a.min_m || M > a.max_m || (a.mask && a.mask[g] == 0)) return;
-        slab = (const uint8_t *)a.table[g];
-        base = a.offset[g];
+        // (the builtin returns a signed int: widen each half through uint32_t,
+        // or a low half with bit 31 set would sign-extend over the high half)
+        const uint64_t sp = (uint64_t)a.table[g];
+        const uint32_t sp_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sp >> 32));
+        const uint32_t sp_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sp);
+        slab = (const uint8_t *)(((uint64_t)sp_hi << 32) | (uint64_t)sp_lo);
+        base = __builtin_amdgcn_readfirstlane(a.offset[g]);
     } else {
         if (!a.shared || a.T < a.min_m || a.T > a.max_m) return;
         slab = (const uint8_t *)a.shared;
         M = a.T;
     }
-    moe::MatRows mat[2] = {GATEUP ? moe::slab_w1(slab, a.H, a.I) : moe::slab_w2(slab, a.H, a.I),
-                           moe::slab_w3(slab, a.H, a.I)};
-    if (!GATEUP) {  // matrix 1 of a pair: the W2 rows 128 further on
-        mat[1] = mat[0];
-        mat[1].row0 += (size_t)kNT * mat[0].stride;
-    }
     const uint16_t *act = GATEUP ? a.x : a.h;
 
-    __shared__ XStage ring[S];
-    __shared__ __attribute__((aligned(16))) uint8_t cring[2][4 * WL::codes];
-    __shared__ __attribute__((aligned(16))) uint8_t rring[2][4 * WL::recs];
-    const uint32_t ring_lds = lds_addr(&ring[0]);
-    const uint32_t cring_lds = lds_addr(&cring[0][0]), rring_lds = lds_addr(&rring[0][0]);
-    auto stage_addr = [&](int b) { return ring_lds + (uint32_t)(b * sizeof(XStage)); };
+    // This wave's weight tiles: gate/up rows n0 + 8*kTM*wave + 16t of W1 (tm = t)
+    // and of W3 (tm = kTM/2 + t); down rows n0 + 16*kTM*wave + 16*tm of W2.  A wave past
+    // the last row still issues its loads (from rows 0..15) so that every wave's
+    // load counts match the waits below; it skips the products and stores.
+    const int wrow0 = GATEUP ? n0 + 8 * kTM * wave : n0 + 16 * kTM * wave;
+    const bool active = wrow0 < nrows;
+    const int r = lane & 15, q = lane >> 4;
+    const int ng = K / kGK;              // groups
+    const int nh = (ng + 3) / 4;         // record steps (4 groups each)
+    // byte offset in the slab of this lane's row of each tile (< 2^32: a slab is a
+    // few tens of MB), plus 16*q: the lane's code bytes of group gg are block
+    // 4*gg + q, at base + 64*gg; its records of step hh are those of blocks
+    // 16*hh + 4q .. + 3, at base + K/2 + 64*hh (a lane whose blocks lie past the
+    // row's last group reads the step's first ones instead; they go unused)
+    uint32_t woff[kTM];
+#pragma unroll
+    for (int tm = 0; tm < kTM; ++tm) {
+        const moe::MatRows m = GATEUP ? (tm < kTM / 2 ? moe::slab_w1(slab, a.H, a.I) : moe::slab_w3(slab, a.H, a.I))
+                                      : moe::slab_w2(slab, a.H, a.I);
+        const int row = active ? (GATEUP ? wrow0 + 16 * (tm % (kTM / 2)) : wrow0 + 16 * tm) + r : r;
+        woff[tm] = (uint32_t)(m.row0 - slab) + (uint32_t)row * (uint32_t)m.stride + 16 * q;
+    }
+    auto code_base = [&](int gg) { return slab + 64 * min(gg, ng - 1); };
+    auto rec_base = [&](int hh) { return slab + K / 2 + 64 * min(hh, nh - 1); };
+    auto rec_off = [&](int tm, int hh) {  // lanes whose four blocks lie past the last group
+        return 4 * min(hh, nh - 1) + q < ng ? woff[tm] : woff[tm] - 16 * q;
+    };
+
+    __shared__ XStage ring[kStages];
+    // records: [step parity][wave][tile] 1 KB, lane l's 16 bytes at 16*l
+    __shared__ __attribute__((aligned(16))) uint8_t rring[2][kWaves][kTM][1024];
     __shared__ int s_src[kMC];  // activation row of each M row
     __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
+    const uint32_t ring_lds = lds_addr(&ring[0]);
     const Dequant dq = dequant_consts();
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lr = lane & 15, lq = lane >> 4;  // MFMA row-in-tile and k-quarter
-    const int nchunks = K / kKC, ncgroups = nchunks / G, nrgroups = nchunks / R;
-    const int wrow0 = n0 + 32 * wave;  // first weight row of this wave
-
-    // This lane's weight sources, fixed over the kernel (a group adds grp*G*32
-    // to the codes, grp*G*8 to the records).  Code load j = q*G + h covers rows
-    // h*32/G .. of matrix q: lane l takes row h*32/G + l/(2G), unit (l % 2G) ^ swz.
-    const uint8_t *csrc[NMAT * G];
-#pragma unroll
-    for (int j = 0; j < NMAT * G; ++j) {
-        const int q = j / G, h = j % G;
-        const int r = h * (32 / G) + lane / (2 * G), u = (lane % (2 * G)) ^ WL::swz(r);
-        csrc[j] = mat[q].row0 + (size_t)(wrow0 + r) * mat[q].stride + u * 16;
-    }
-    // records: load j, lane l takes piece f = (64j + l) mod rec_lanes, 16 bytes
-    // (part f % LPR) of row (f / LPR) % 32 of matrix f / (32 LPR)
-    const uint8_t *rsrc[WL::rec_loads];
-#pragma unroll
-    for (int j = 0; j < WL::rec_loads; ++j) {
-        constexpr int LPR = R / 2;  // lanes per row
-        const int f = (64 * j + lane) % WL::rec_lanes;
-        const int q = f / (32 * LPR), r = (f % (32 * LPR)) / LPR, part = f % LPR;
-        const moe::MatRows &m = q ? mat[1] : mat[0];
-        rsrc[j] = m.row0 + (size_t)(wrow0 + r) * m.stride + K / 2 + part * 16;
-    }
-    // code group grp into code buffer buf, record group grp into record buffer buf
-    auto issue_c = [&](int grp, int buf) {
-        const uint32_t wb = cring_lds + (uint32_t)(buf * 4 * WL::codes + wave * WL::codes);
-#pragma unroll
-        for (int j = 0; j < WL::code_loads; ++j) dma16(csrc[j] + grp * G * 32, wb + (uint32_t)(j * 1024));
-    };
-    auto issue_r = [&](int grp, int buf) {
-        const uint32_t wb = rring_lds + (uint32_t)(buf * 4 * WL::recs + wave * WL::recs);
-#pragma unroll
-        for (int j = 0; j < WL::rec_loads; ++j) dma16(rsrc[j] + grp * R * 8, wb + (uint32_t)(j * 1024));
-    };
-
-    // B-operand read offsets in a wave block: row rl = nt*16 + lr of matrix q,
-    // the k-quarter's dword; the unit position is XORed with swz(rl) per read
-    int cq[NMAT][2], swz16[2], rq[NMAT][2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int rl = nt * 16 + lr;
-        swz16[nt] = WL::swz(rl) * 16;
-#pragma unroll
-        for (int q = 0; q < NMAT; ++q) {
-            cq[q][nt] = wave * WL::codes + q * 32 * WL::row_code + rl * WL::row_code + lq * 4;
-            rq[q][nt] = wave * WL::recs + q * 32 * WL::row_rec + rl * WL::row_rec;
-        }
-    }
 
     for (int m0 = 0; m0 < M; m0 += kMC) {
         const int mc = min(kMC, M - m0);
         const int mtiles = (mc + 15) >> 4;
-        __syncthreads();  // the previous pass is done with s_src / s_dst and the rings
+        __syncthreads();  // the previous pass is done with s_src / s_dst and the ring
         if (tid < kMC) {
             int src = -1, dst = -1;
             const int m = m0 + (tid < mc ? tid : 0);  // padding rows repeat the first row
@@ -411,171 +372,161 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             s_dst[tid] = tid < mc ? dst : -1;
         }
         __syncthreads();
-        // activation loads of this wave: tile units wave + 4j (8 rows each), for
-        // j < (MT + 1) / 2 with MT M tiles, so that every wave issues the same
-        // number of loads per chunk (rows past the tokens repeat the first row;
-        // rows past 16 * MT are loaded for that reason only and never read).
-        const uint16_t *xsrc[3];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int r = 8 * (wave + 4 * j) + (lane >> 3), pos = lane & 7;
-            xsrc[j] = act + (size_t)s_src[r] * K + 8 * (pos ^ (r & 7));
-        }
-        // chunk c's activation tile into the stage at LDS address st
-        auto issue_x = [&](uint32_t st, int c, auto mt_count) {
-            constexpr int XJ = (decltype(mt_count)::value + 1) / 2;
-            const int k0 = c * kKC;
-#pragma unroll
-            for (int j = 0; j < XJ; ++j) dma16(xsrc[j] + k0, st + (uint32_t)((wave + 4 * j) * 1024));
-        };
 
-        f32x4_t acc[NMAT][kMaxMT][2];
-#pragma unroll
-        for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-            for (int mt = 0; mt < kMaxMT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) acc[q][mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        // One chunk (chunk cg of its code group in code buffer cb, chunk cr of its
-        // record group in record buffer rb) of MT M tiles: every LDS read of the
-        // chunk is issued first (the B codes of both 32-column halves, their
-        // records as one 8-byte read per row, the A tiles), then each half is
-        // dequantised and multiplied.
-        auto compute = [&](const XStage &st, const uint8_t *cb, auto cg_const, const uint8_t *rb, auto cr_const,
-                           auto mt_count) {
+        auto k_loop = [&](auto mt_count) {
             constexpr int MT = decltype(mt_count)::value;
-            constexpr int cg = decltype(cg_const)::value, cr = decltype(cr_const)::value;
-            uint32_t codes[2][NMAT][2];
-            uint64_t recs[NMAT][2];
+            constexpr int RPI = 4 * kWaves;                // rows one copy instruction of every wave covers
+            constexpr int P = (16 * MT + RPI - 1) / RPI;  // activation copy instructions per wave and group
+            // activation copy: instruction j of this wave covers rows RPI*j + 4*wave .. + 3
+            // (when those lie past the stage's kMC rows, the wave copies its rows of
+            // instruction 0 again: the same bytes to the same place, so that every
+            // wave issues the same number of loads); lane l takes row ... + l/16,
+            // unit (l % 16) ^ (row % 16)
+            static_assert(RPI <= kMC, "the first copy instruction stays inside a stage");
+            uint32_t xoff[P], xrow[P];  // byte offsets in the activations (rows of K bf16); LDS row
 #pragma unroll
-            for (int q = 0; q < NMAT; ++q)
+            for (int j = 0; j < P; ++j) {
+                const int r0 = RPI * j + 4 * wave < kMC ? RPI * j + 4 * wave : 4 * wave;
+                const int m = r0 + (lane >> 4);
+                xrow[j] = (uint32_t)r0;
+                xoff[j] = (uint32_t)s_src[m] * (uint32_t)(2 * K) + 16 * ((lane & 15) ^ (m & 15));
+            }
+            auto issue_x = [&](int gg) {  // group gg's tile into its stage
+                const uint8_t *xb = (const uint8_t *)act + 2 * kGK * min(gg, ng - 1);
+                const uint32_t st = ring_lds + (uint32_t)((gg % kStages) * sizeof(XStage));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    recs[q][nt] = *reinterpret_cast<const uint64_t *>(rb + rq[q][nt] + cr * 8);
+                for (int j = 0; j < P; ++j) dma16(xb, xoff[j], st + xrow[j] * kXRow);
+            };
+            f32x4_t acc[kTM][MT];
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-                        codes[kb][q][nt] =
-                            *reinterpret_cast<const uint32_t *>(cb + cq[q][nt] + (((2 * cg + kb) * 16) ^ swz16[nt]));
-                }
-            uint4 av[2][MT];
+            for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int mt = 0; mt < MT; ++mt) acc[tm][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+            // issue order (the waits below count on it): records of step 0; then
+            // tiles 0 .. kAhead-1, each followed (for the first kCodeAhead) by
+            // its group's codes; then per group g: [records of step g/4 + 1 when
+            // g % 4 == 0], tile g + kAhead, products of group g, codes of group
+            // g + kCodeAhead, wait for tile g + 1, barrier.  Group g's codes sit
+            // in ring slot g % kCodeAhead, a constant in the 4-step unrolled body
+            // (no register copies of loads in flight).
+            uint4 cring[kCodeAhead][kTM];
+            // records of step hh (4 groups) into their LDS area
+            auto issue_r = [&](int hh) {
+                const uint8_t *rb = rec_base(hh);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int r = mt * 16 + lr;
-                    av[kb][mt] = *reinterpret_cast<const uint4 *>(&st.x[r * kXRow + (((kb * 4 + lq) ^ (r & 7)) * 16)]);
-                }
-#if MOE_EXP_SCHED
-            // one B tile at a time: its dequantisation, then its MT products, so
-            // that the products of one tile run while the next is dequantised
+                for (int tm = 0; tm < kTM; ++tm) dma16(rb, rec_off(tm, hh), lds_addr(&rring[hh & 1][wave][tm][0]));
+            };
+            issue_r(0);
 #pragma unroll
-            for (int kb = 0; kb < kKC / 32; ++kb)
+            for (int c = 0; c < kAhead; ++c) {
+                issue_x(c);
+                if (c < kCodeAhead)
 #pragma unroll
-                for (int q = 0; q < NMAT; ++q)
+                    for (int tm = 0; tm < kTM; ++tm) cring[c][tm] = load_u4(code_base(c), woff[tm]);
+            }
+            // tile 0 has landed once the loads issued after it are the only ones left
+            wait_vm<loads_after_tile(kAhead, kCodeAhead, P, kTM, -1)>();
+            ring_barrier();
+
+            auto step = [&](int gg, auto b_const) {
+                constexpr int b = decltype(b_const)::value;  // gg % 4
+                // records of this step: loaded 4 groups ago (complete since the
+                // wait for an activation tile issued after them)
+                const uint8_t *rbuf = &rring[(gg / 4) & 1][wave][0][0];
+                if (b == 0) issue_r(gg / 4 + 1);
+                issue_x(gg + kAhead);
+                constexpr int slot = b % kCodeAhead;
+                // loads and waits run in every step of the unrolled body (past the
+                // last group they re-read it), so that the compiler's own load
+                // counts never meet a path that skipped them; only the products
+                // are skipped
+                if (active && gg < ng) {
+                    const uint8_t *st = &ring[gg % kStages].x[0];
+                    // each tile's block record: scale and the two extraction offsets
+                    float sc[kTM], clo[kTM], chi[kTM];
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const bf16x8_t B = dequant8(codes[kb][q][nt], (uint32_t)(recs[q][nt] >> (32 * kb)), dq);
+                    for (int tm = 0; tm < kTM; ++tm) {
+                        // block 16h + 4b + q of this lane's row: lane (row r, quarter b)'s word q
+                        const uint32_t rec = *reinterpret_cast<const uint32_t *>(rbuf + tm * 1024 + (16 * b + r) * 16 + 4 * q);
+                        sc[tm] = fp16_bits_to_f32(rec & 0xFFFFu);
+                        const float mn = fp16_bits_to_f32(rec >> 16);
+                        clo[tm] = fmaf(-1024.0f, sc[tm], mn);
+                        chi[tm] = fmaf(-64.0f, sc[tm], mn);
+                    }
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            acc[q][mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, av[kb][mt]), B, acc[q][mt][nt], 0, 0, 0);
-#if MOE_EXP_SCHED == 2
-                        __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+                    for (int s = 0; s < 4; ++s) {
+                        bf16x8_t bo[kTM];
+#pragma unroll
+                        for (int tm = 0; tm < kTM; ++tm)
+                            bo[tm] = dequant8(word(cring[slot][tm], s), sc[tm], clo[tm], chi[tm], dq);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+                            const int m = 16 * mt + r;
+                            const bf16x8_t av = __builtin_bit_cast(
+                                bf16x8_t, *reinterpret_cast<const uint4 *>(st + m * kXRow + 16 * ((4 * q + s) ^ r)));
+#pragma unroll
+                            for (int tm = 0; tm < kTM; ++tm)
+                                acc[tm][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bo[tm], acc[tm][mt], 0, 0, 0);
+                        }
+#if MOE_MFMA_SCHED_BARRIER
+                        __builtin_amdgcn_sched_barrier(0);
 #endif
                     }
-#else
-#pragma unroll
-            for (int kb = 0; kb < kKC / 32; ++kb) {
-                bf16x8_t bo[NMAT][2];
-#pragma unroll
-                for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        bo[q][nt] = dequant8(codes[kb][q][nt], (uint32_t)(recs[q][nt] >> (32 * kb)), dq);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[kb][mt]);
-#pragma unroll
-                    for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-                        for (int nt = 0; nt < 2; ++nt)
-                            acc[q][mt][nt] =
-                                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bo[q][nt], acc[q][mt][nt], 0, 0, 0);
                 }
-            }
-#endif
-        };
-
-        // Step c (at position b of the unrolled loop): wait until chunk c's
-        // activations, codes and records have landed (exact vmcnt, from the fixed
-        // issue order), barrier, refill the stage freed by chunk c - 1 with chunk
-        // c + S - 1 and, at the start of a code (record) group, the buffer freed by
-        // the previous group with the next group, then multiply.  Past the last
-        // chunk (group) a step re-loads the last one into a buffer that is not
-        // read again, so every step issues a fixed number of loads.
-        auto step = [&](int c, auto b_const, auto mt_count) {
-            constexpr int b = decltype(b_const)::value;
-            constexpr int P = (decltype(mt_count)::value + 1) / 2;  // activation loads of one stage
-            __builtin_amdgcn_s_waitcnt(
-                kWaitVm(vm_allow(S, P, G, WL::code_loads, R, WL::rec_loads, U, b)));
-            ring_barrier();
-            issue_x(stage_addr((b + S - 1) % S), min(c + S - 1, nchunks - 1), mt_count);
-            if (b % G == 0) issue_c(min(c / G + 1, ncgroups - 1), (c / G + 1) & 1);
-            if (b % R == 0) issue_r(min(c / R + 1, nrgroups - 1), (c / R + 1) & 1);
-            compute(ring[b % S], &cring[(c / G) & 1][0], IntC<b % G>{}, &rring[(c / R) & 1][0], IntC<b % R>{},
-                    mt_count);
-        };
-
-        // The K loop, specialised on the pass's M tile count so that the chunk
-        // body has no branches, and unrolled by U so that every step names its
-        // buffers with constants.
-        auto k_loop = [&](auto mt_count) {
-            issue_r(0, 0);
-            issue_c(0, 0);
+                const uint8_t *cb = code_base(gg + kCodeAhead);
 #pragma unroll
-            for (int b = 0; b < S - 1; ++b) issue_x(stage_addr(b), min(b, nchunks - 1), mt_count);
-            for (int c0 = 0; c0 < nchunks; c0 += U)
-                static_for<0, U>([&](auto b_const) {
-                    if (c0 + decltype(b_const)::value < nchunks) step(c0 + decltype(b_const)::value, b_const, mt_count);
-                });
+                for (int tm = 0; tm < kTM; ++tm) cring[slot][tm] = load_u4(cb, woff[tm]);
+                // tile gg + 1 has landed once only the loads issued after it remain
+                // (the first steps follow the prologue's order, later ones repeat
+                // with period 4)
+                if (gg < 4)
+                    wait_vm<loads_after_tile(kAhead, kCodeAhead, P, kTM, b)>();
+                else
+                    wait_vm<loads_after_tile(kAhead, kCodeAhead, P, kTM, 4 + b)>();
+                ring_barrier();
+            };
+            for (int g0 = 0; g0 < ng; g0 += 4)
+                static_for<0, 4>([&](auto b_const) { step(g0 + decltype(b_const)::value, b_const); });
+            // no copy may still be writing LDS when the workgroup moves on or exits
+            wait_vm<0>();
+
+            // epilogue
+            if (active) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int m = 16 * mt + 4 * q + j;
+                        if (m >= mc) continue;
+                        const int row = s_dst[m];
+                        if (GATEUP) {
+#pragma unroll
+                            for (int t = 0; t < kTM / 2; ++t) {
+                                const int n = wrow0 + 16 * t + r;
+                                const float gv = acc[t][mt][j], uv = acc[kTM / 2 + t][mt][j];
+                                a.h[(size_t)row * a.I + n] = (uint16_t)f32_to_bf16_bits(gv / (1.0f + expf(-gv)) * uv);
+                            }
+                        } else {
+#pragma unroll
+                            for (int tm = 0; tm < kTM; ++tm) a.y[(size_t)row * a.H + wrow0 + 16 * tm + r] = acc[tm][mt][j];
+                        }
+                    }
+            }
         };
         switch (mtiles) {
             case 1: k_loop(IntC<1>{}); break;
             case 2: k_loop(IntC<2>{}); break;
             case 3: k_loop(IntC<3>{}); break;
             case 4: k_loop(IntC<4>{}); break;
+#if MOE_MFMA_MAX_MT >= 6
             case 5: k_loop(IntC<5>{}); break;
             default: k_loop(IntC<6>{}); break;
+#else
+            default: k_loop(IntC<5>{}); break;
+#endif
         }
-        static_assert(kMaxMT == 6, "one k_loop case per M tile count");
-
-        // no load may still be writing LDS when the workgroup moves on or exits
-        __builtin_amdgcn_s_waitcnt(kWaitVm(0));
-
-        // epilogue
-#pragma unroll
-        for (int mt = 0; mt < kMaxMT; ++mt) {
-            if (mt >= mtiles) continue;
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int n = n0 + wave * 32 + nt * 16 + lr;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int m = mt * 16 + lq * 4 + j;
-                    if (m >= mc || n >= nrows) continue;
-                    const int row = s_dst[m];
-                    if (GATEUP) {
-                        const float gv = acc[0][mt][nt][j], uv = acc[1][mt][nt][j];
-                        a.h[(size_t)row * a.I + n] = (uint16_t)f32_to_bf16_bits(gv / (1.0f + expf(-gv)) * uv);
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < NMAT; ++q) a.y[(size_t)row * a.H + n + q * kNT] = acc[q][mt][nt][j];
-                    }
-                }
-            }
-        }
+        static_assert(kMaxMT == 5 || kMaxMT == 6, "one k_loop case per M tile count");
     }
 }
 
@@ -588,32 +539,22 @@ bool mfma_supported(const FfnArgs &a) { return a.grouped && a.H % 128 == 0 && a.
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-template <bool GATEUP, int S, int G, int R, bool PAIR = false>
+template <bool GATEUP>
 int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
-    const int ntiles = GATEUP ? a.I / kNT : a.H / (PAIR ? 2 * kNT : kNT);
-    const unsigned slots = (unsigned)((n_groups + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, S, G, R, PAIR>), dim3(slots * kXcds * ntiles), dim3(256), 0, s, a,
-                       ntiles, n_groups);
+    const int rows = GATEUP ? a.I : a.H, per = GATEUP ? kRowsGateUp : kRowsDown;
+    const int ntiles = (rows + per - 1) / per;
+    unsigned grid;
+    if (a.compact)
+        grid = (unsigned)(n_groups * ntiles);
+    else
+        grid = (unsigned)((n_groups + kXcds - 1) / kXcds * kXcds * ntiles);
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP>), dim3(grid), dim3(kThreads), 0, s, a, ntiles, n_groups);
     MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
 
-// Two matrices per workgroup (gate/up, and the down projection when H is a
-// multiple of 256): code groups of 2 chunks (64 bytes per row), record groups
-// of 4 chunks (32 bytes per row) when the reduction length is a multiple of 256,
-// else 2.  One matrix: code and record groups of 4 chunks (a 128-byte line of
-// codes per row) when I is a multiple of 256, else 2.
-int mfma_gate_up(const FfnArgs &a, hipStream_t s) {
-    return a.H % 256 == 0 ? launch_mfma<true, kStagesGateUp, 2, kRecGroup>(a, s)
-                          : launch_mfma<true, kStagesGateUp, 2, 2>(a, s);
-}
-
-int mfma_down(const FfnArgs &a, hipStream_t s) {
-    if (a.H % (2 * kNT) == 0)
-        return a.I % 256 == 0 ? launch_mfma<false, kStagesDown, 2, kRecGroup, true>(a, s)
-                              : launch_mfma<false, kStagesDown, 2, 2, true>(a, s);
-    return a.I % 256 == 0 ? launch_mfma<false, kStagesDown, 4, 4>(a, s) : launch_mfma<false, kStagesDown, 2, 2>(a, s);
-}
+int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true>(a, s); }
+int mfma_down(const FfnArgs &a, hipStream_t s) { return launch_mfma<false>(a, s); }
 
 }  // namespace moe

@@ -219,10 +219,20 @@ class MoEStack:
         half = max(1, self.C // 2)
         self.max_waves = (E + half - 1) // half + 1
         self.masks = torch.zeros((Lyr, self.max_waves, E), dtype=torch.uint8, device=self.dev)
+        # gate/up timing of the MFMA path (see ffn); the permutation and h buffers it uses
+        self.kernel_log = None
+        self._perm = (torch.empty(E, dtype=torch.int32, device=self.dev),
+                      torch.empty(E + 1, dtype=torch.int32, device=self.dev),
+                      torch.empty(T * k, dtype=torch.int32, device=self.dev)) if T >= 128 else None
+        self._h = torch.empty((P, I), dtype=torch.bfloat16, device=self.dev) if T >= 128 else None
         self.pidx = torch.empty((Lyr, T, k), dtype=torch.int32, device=self.dev)  # predicted experts
         self.pw = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
         self._idx_host = PinnedHost(max(Lyr, 2) * T * k * 4) if self.streaming else None
         self._mask_host = PinnedHost(Lyr * self.max_waves * E) if self.streaming else None
+        # host outputs of the library's step plan (moe_cache_plan_step)
+        self._plan_experts = np.empty((Lyr, T * k), np.int32)
+        self._plan_starts = np.empty((Lyr, self.max_waves + 1), np.int32)
+        self._plan_nwaves = np.empty(Lyr, np.int32)
         # CPU lane: host copies of the layer inputs and the rows it returns
         self.lane = None
         self.lane_pick = None
@@ -272,11 +282,31 @@ class MoEStack:
         L.moe_router_topk_layers(x, self.L, self.T, self.H, self.wr, self.bias, self.E, self.k, self.idx, self.w,
                                  self.router_ws, self.router_ws_bytes, self.stream)
 
-    def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True):
+    def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True, experts=None):
+        """Gate/up + SwiGLU and down projection of layer l's pairs whose expert the
+        mask admits (all when None) into y.  With kernel_log set to a list and many
+        tokens (the MFMA kernels), the same kernels run as three calls -- the
+        permutation, gate/up, down -- with timing events before gate/up, between
+        the two and after down, and (the three events, layer, experts, shared
+        expert included) is appended to the log."""
         self._format0_only("ffn (masked FFN into y)")
-        L.moe_expert_ffn(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l],
-                         self.shared[l] if (self.has_shared and shared) else None, mask, self.y, self.ffn_ws,
-                         self.ffn_ws_bytes, self.path, self.stream)
+        sh = self.shared[l] if (self.has_shared and shared) else None
+        if self.kernel_log is None or self.T < 128 or self.path not in (L.MOE_FFN_AUTO, L.MOE_FFN_MFMA):
+            L.moe_expert_ffn(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l], sh, mask,
+                             self.y, self.ffn_ws, self.ffn_ws_bytes, self.path, self.stream)
+            return
+        T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
+        cnt, off, por = self._perm
+        L.moe_permute(self.idx[l], T, k, E, cnt, off, por, self.stream)
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(self.stream)
+        L.moe_expert_gate_up(x[l], T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask, self._h,
+                             self.path, self.stream)
+        b.record(self.stream)
+        L.moe_expert_down(self._h, T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask, self.y,
+                          self.path, self.stream)
+        c.record(self.stream)
+        self.kernel_log.append((a, b, c, l, list(range(E)) if experts is None else list(experts), sh is not None))
 
     def ffn_combine(self, x: torch.Tensor, l: int, out: torch.Tensor):
         """Gate/up, down and the weighted combine of layer l (every needed expert resident)."""
@@ -428,9 +458,10 @@ class MoEStack:
         # CPU lane: some misses are computed on the host; a layer uses it when the
         # rest of its experts fit its slots (one wave)
         cpu_sets, lane_jobs = [set() for _ in range(self.L)], {}
-        if self.lane is not None:
-            needed_by_layer = [sorted(set(row)) for row in idx_host.reshape(self.L, -1).tolist()]
-            cpu_sets = self.plan_cpu_lane(needed_by_layer, idx3)
+        if self.lane is None:
+            return self._forward_planned(x, out, idx_host, mh, st)
+        needed_by_layer = [sorted(set(row)) for row in idx_host.reshape(self.L, -1).tolist()]
+        cpu_sets = self.plan_cpu_lane(needed_by_layer, idx3)
         plans = []
         for l in range(self.L):
             if cpu_sets[l]:
@@ -479,10 +510,40 @@ class MoEStack:
                 continue
             for wv, experts in enumerate(waves):
                 st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
-                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0))
+                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts)
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
             self.combine(l, out)
+        return st
+
+    def _forward_planned(self, x, out, idx_host, mh, st: StepStats) -> StepStats:
+        """The streamed step after routing, without a CPU lane: one library call
+        plans every layer and queues the copies of the layers that fit their slots
+        (the copy engine starts right away); then per layer the wait, the FFN
+        (wave by wave for layers that need more experts than they have slots) and
+        the release."""
+        ne = self._plan_experts
+        starts = self._plan_starts
+        nw = self._plan_nwaves
+        st.copies += L.moe_cache_plan_step(self.cache, idx_host, self.T * self.k, ne, starts, self.max_waves, mh, nw,
+                                           True)
+        if (nw > 1).any():
+            self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
+        for l in range(self.L):
+            if nw[l] == 1:
+                L.moe_cache_wait(self.cache, l, self.stream)
+                self.ffn_combine(x, l, out)
+                L.moe_cache_release(self.cache, l, self.stream)
+                st.waves += 1
+                continue
+            for wv in range(int(nw[l])):
+                experts = ne[l, starts[l, wv]:starts[l, wv + 1]]
+                st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
+                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts)
+                L.moe_cache_release(self.cache, l, self.stream)
+                st.waves += 1
+            self.combine(l, out)
+        self.last_cpu_sets = [set() for _ in range(self.L)]
         return st
 
     # ------------------------------------------------------------------ chained layers
@@ -579,6 +640,11 @@ class MoEStack:
             if l + 1 < self.L:
                 L.moe_residual_norm(out[l], resid, T, H, RMS_EPS, xs[l + 1], self.stream)
         return st
+
+    def last_routing(self) -> np.ndarray:
+        """Host copy [L, T, k] of the expert ids of the last streamed step."""
+        hv = np.frombuffer(self._idx_host.array, dtype=np.int32, count=self.L * self.T * self.k)
+        return hv.reshape(self.L, self.T, self.k).copy()
 
     def stats(self):
         return L.moe_cache_stats(self.cache) if self.cache else (0, 0, 0)

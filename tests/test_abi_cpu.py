@@ -403,8 +403,14 @@ def test_step_plan_drives_overflowing_layers_through_the_abi(seed, experts, slot
         # the documented plan
         resident = [e for e in needed if e in model.slot_of[l]]
         order = resident + [e for e in needed if e not in model.slot_of[l]]
-        w = slots if len(order) <= slots else half
-        assert waves == [sorted(order[i:i + w]) for i in range(0, len(order), w)]
+        if len(order) <= slots:
+            assert waves == [sorted(order)]
+        else:  # the fewest waves of at most half the slots, balanced, resident experts first
+            nw = -(-len(order) // half)
+            sizes = [len(order) // nw + (1 if v < len(order) % nw else 0) for v in range(nw)]
+            assert max(sizes) <= half
+            bounds = np.cumsum([0] + sizes)
+            assert waves == [sorted(order[bounds[v]:bounds[v + 1]]) for v in range(nw)]
         assert all(len(v) <= slots for v in waves)
         for v in range(max_waves):
             want = np.zeros(experts, np.uint8)
@@ -428,3 +434,47 @@ def test_step_plan_drives_overflowing_layers_through_the_abi(seed, experts, slot
     assert _status(L.moe_cache_plan, cache, 2, [0], 4) == L.MOE_E_ARG
     assert L.moe_cache_plan(cache, 0, [], 4) == []
     L.moe_cache_destroy(cache)
+
+
+def test_step_plan_equals_per_layer_plans_and_issues_single_wave_layers():
+    """moe_cache_plan_step plans every layer as moe_cache_plan does and queues
+    the copies of the layers that fit their slots, in layer order."""
+    rng = np.random.default_rng(5)
+    E, C, Ln, n = 64, 20, 4, 24
+    a = L.moe_cache_create_recording(_desc(Ln, E, C), 1 << 40)
+    b = L.moe_cache_create_recording(_desc(Ln, E, C), 1 << 40)
+    half = C // 2
+    mw = (E + half - 1) // half + 1
+    for step in range(6):
+        ids = np.stack([rng.choice(E, n, replace=(l % 2 == 1)) for l in range(Ln)]).astype(np.int32)
+        ids[0, :] = rng.integers(0, 5, n)  # a layer with few distinct experts
+        ne = np.empty((Ln, n), np.int32)
+        st = np.empty((Ln, mw + 1), np.int32)
+        nw = np.empty(Ln, np.int32)
+        masks = np.empty((Ln, mw, E), np.uint8)
+        copies = L.moe_cache_plan_step(a, ids, n, ne, st, mw, masks, nw, True)
+        expect_copies = 0
+        for l in range(Ln):
+            mref = np.empty((mw, E), np.uint8)
+            waves = L.moe_cache_plan(b, l, ids[l], masks=mref)
+            assert nw[l] == len(waves)
+            assert [ne[l, st[l, v]:st[l, v + 1]].tolist() for v in range(nw[l])] == waves
+            assert np.array_equal(masks[l], mref)
+            if len(waves) == 1:
+                expect_copies += L.moe_cache_prefetch_async(b, l, waves[0])
+        assert copies == expect_copies
+        for l in range(Ln):
+            if nw[l] == 1:
+                L.moe_cache_wait(a, l)
+                L.moe_cache_release(a, l)
+                L.moe_cache_wait(b, l)
+                L.moe_cache_release(b, l)
+            else:
+                for v in range(nw[l]):
+                    wave = ne[l, st[l, v]:st[l, v + 1]]
+                    assert L.moe_cache_prefetch(a, l, wave) == L.moe_cache_prefetch(b, l, wave.tolist())
+                    L.moe_cache_release(a, l)
+                    L.moe_cache_release(b, l)
+        assert L.moe_cache_trace(a) == L.moe_cache_trace(b)
+    L.moe_cache_destroy(a)
+    L.moe_cache_destroy(b)

@@ -436,6 +436,23 @@ def test_stack_decode1_full_and_deterministic():
     stack.close()
 
 
+def documented_waves(order, C):
+    """The waves of a layer's experts in the documented order (resident first):
+    one wave if they fit the C slots, else the fewest waves of at most C // 2,
+    sizes differing by at most one, the first ones larger."""
+    n = len(order)
+    if n <= C:
+        return [sorted(order)] if n else []
+    half = max(1, C // 2)
+    nw = (n + half - 1) // half
+    waves, b = [], 0
+    for v in range(nw):
+        e = b + n // nw + (1 if v < n % nw else 0)
+        waves.append(sorted(order[b:e]))
+        b = e
+    return waves
+
+
 def lru_replay(idx_steps, L_, C):
     """Hits/misses of the documented LRU rule replayed on the routing trace."""
     from tests.test_abi_cpu import LRUModel
@@ -445,9 +462,8 @@ def lru_replay(idx_steps, L_, C):
             needed = sorted(set(int(e) for e in idx[l].ravel()))
             resident = [e for e in needed if e in model.slot_of[l]]
             order = resident + [e for e in needed if e not in model.slot_of[l]]
-            w = C if len(order) <= C else max(1, C // 2)  # waves of half the slots when they overflow
-            for i in range(0, len(order), w):
-                status, _ = model.prefetch(l, sorted(order[i:i + w]))
+            for wave in documented_waves(order, C):
+                status, _ = model.prefetch(l, wave)
                 assert status == "ok"
                 model.release(l)
     return model.hits, model.misses
