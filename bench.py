@@ -40,8 +40,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 METRIC = "routed-MoE layer tokens/s at 1 GPU; achieved HBM GB/s and PCIe H2D GB/s vs peak"
 # the one-token gate/up kernel as launched alone (units per lane, ring depth, no routing)
 GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 1, 0, 0>"
-# the prefill gate/up kernel at hidden 6144 (stages, code group, record group, pair)
-MFMA_GATE_UP_KERNEL = "mfma_ffn_kernel<true, 2, 2, 4, false>"
+# the prefill gate/up kernel (matrix cores; W1/W3 rows, SwiGLU epilogue)
+MFMA_GATE_UP_KERNEL = "mfma_ffn_kernel<true>"
 
 
 def log(msg):

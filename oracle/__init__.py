@@ -31,7 +31,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "_oracle.so")
+# MOE_ORACLE_LIB: load another build of oracle.c (the pin-strength test loads
+# copies with a planted mistake this way)
+_LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "_oracle.so")
 _lib = None
 
 

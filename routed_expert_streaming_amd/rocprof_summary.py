@@ -6,7 +6,7 @@ Prints one line per kernel: dispatches, average / min / max duration, share of
 GPU time, grid, workgroup size and VGPRs (with --by-grid, one line per kernel
 and grid size, which tells launches of one kernel on different shapes apart);
 with --counters, the average of every
-PMC counter per kernel (as collected by ``rocprofv3 --pmc ...``); with
+PMC counter per kernel (per kernel and grid size with --by-grid) (as collected by ``rocprofv3 --pmc ...``); with
 --timeline, per kernel the average duration and the average idle gap between
 the end of the previous dispatch and its start (over the last two thirds of the
 trace, gaps under 20 us, so set-up and host pauses are left out); with --copies
@@ -52,12 +52,17 @@ def kernel_stats(db: str, by_grid: bool = False):
     return out
 
 
-def counter_stats(db: str):
+def counter_stats(db: str, by_grid: bool = False):
+    """Per kernel (and grid size, with by_grid): dispatch count and the average of
+    every counter per dispatch."""
     c = sqlite3.connect(db)
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
-    for name, ctr, val in c.execute("select kernel_name, counter_name, value from counters_collection"):
-        agg[short_name(name)][ctr].append(val)
-    return {k: {ctr: sum(v) / len(v) for ctr, v in d.items()} for k, d in agg.items()}
+    for name, grid, ctr, val in c.execute("select kernel_name, grid_size, counter_name, value "
+                                          "from counters_collection"):
+        k = short_name(name)
+        agg[f"{k[:70]} [{grid}]" if by_grid else k][ctr].append(val)
+    return {k: ({ctr: sum(v) / len(v) for ctr, v in d.items()}, max(len(v) for v in d.values()))
+            for k, d in agg.items()}
 
 
 def timeline_stats(db: str):
@@ -138,8 +143,8 @@ def main():
             print(f"{k[:60]:60s} {n:6d} {d:9.3f} {g:14.3f}")
         return
     if args.counters:
-        for k, d in sorted(counter_stats(args.db).items()):
-            print(f"{k}")
+        for k, (d, n) in sorted(counter_stats(args.db, args.by_grid).items()):
+            print(f"{k}  ({n} dispatches)")
             print("    " + "  ".join(f"{ctr}={v:.6g}" for ctr, v in sorted(d.items())))
         return
     print(f"{'kernel':90s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s} "
