@@ -40,8 +40,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 METRIC = "routed-MoE layer tokens/s at 1 GPU; achieved HBM GB/s and PCIe H2D GB/s vs peak"
 # the one-token gate/up kernel as launched alone (units per lane, ring depth, no routing)
 GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 1, 0, 0>"
-# the prefill gate/up kernel (matrix cores; W1/W3 rows, SwiGLU epilogue)
-MFMA_GATE_UP_KERNEL = "mfma_ffn_kernel<true>"
+# the prefill gate/up kernel (matrix cores; W1/W3 rows, SwiGLU epilogue), by weight format
+MFMA_GATE_UP_KERNEL = "mfma_ffn_kernel<true, {fmt}>"
 
 
 def log(msg):
@@ -444,15 +444,16 @@ def layer_leg(torch, name: str, path: int, iters: int):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / iters
 
-    res = {"workload": f"{name}, one resident layer", "tokens": T, "path": {L.MOE_FFN_MFMA: "mfma",
+    res = {"workload": f"{name}, one resident layer", "tokens": T, "format": st.fmt, "slab_bytes": st.slab,
+           "path": {L.MOE_FFN_MFMA: "mfma",
                                                                               L.MOE_FFN_GROUPED: "grouped",
                                                                               L.MOE_FFN_SPLIT: "split"}[path]}
     res["router_ms"] = timed(lambda: st.route(x, 0))
     res["permute_ms"] = timed(lambda: L.moe_permute(st.idx[0], T, k, E, cnt, off, por))
-    res["gate_up_ms"] = timed(lambda: L.moe_expert_gate_up(x[0], T, H, I, E, st.idx[0], k, cnt, off, por,
-                                                           st.table[0], shared, None, h, path))
-    res["down_ms"] = timed(lambda: L.moe_expert_down(h, T, H, I, E, st.idx[0], k, cnt, off, por, st.table[0],
-                                                     shared, None, st.y, path))
+    res["gate_up_ms"] = timed(lambda: L.moe_expert_gate_up_fmt(x[0], T, H, I, E, st.idx[0], k, cnt, off, por,
+                                                               st.table[0], shared, None, h, path, st.fmt))
+    res["down_ms"] = timed(lambda: L.moe_expert_down_fmt(h, T, H, I, E, st.idx[0], k, cnt, off, por, st.table[0],
+                                                         shared, None, st.y, path, st.fmt))
     res["combine_ms"] = timed(lambda: st.combine(0, out))
     res["layer_ms"] = timed(lambda: (st.route(x, 0), st.ffn_combine(x, 0, out)))
     idx = st.idx[0].cpu().numpy()
@@ -493,6 +494,16 @@ def counter_traffic(kernel: str, profile: str):
                 h.update(open(os.path.join(ROOT, src), "rb").read())
             return info["traffic_bytes_per_launch"] if h.hexdigest() == info["sources_sha1"] else None
     return None
+
+
+def row_bytes(K: int, fmt: int) -> int:
+    """Bytes of a K-column weight row: K/2 code bytes plus the block parameters
+    (format 0: 4 bytes per 32 columns, 1: 1 byte per 32, 2: 16 bytes per 256),
+    formats 0 and 1 padded to 16 bytes."""
+    if fmt == 2:
+        return K // 2 + K // 16
+    per = 4 if fmt == 0 else 1
+    return (K // 2 + K // 32 * per + 15) // 16 * 16
 
 
 def bytes_per_32(stack) -> int:
@@ -602,8 +613,7 @@ def headline(torch, args, cfg):
     compute_ms_step = None
     if mfma:
         marks.append(len(st.kernel_log))
-        row = st.H // 2 + st.H // 32 * 4  # a W1 (W3) row of the slab: codes and records
-        gu_w = 2 * st.I * row
+        gu_w = 2 * st.I * row_bytes(st.H, st.fmt)  # W1 and W3 of one expert
         tot_b = tot_f = 0
         tot_gu = tot_ffn = 0.0
         n = 0
@@ -669,13 +679,14 @@ def headline(torch, args, cfg):
                    "parallelism": "single GPU"},
     }
     if kern:
+        kname = MFMA_GATE_UP_KERNEL.format(fmt=st.fmt)
         result["roofline"] = {
-            "bound": "hbm", "kernel": f"{MFMA_GATE_UP_KERNEL} (dequant + gate/up + SwiGLU grouped GEMM on the "
+            "bound": "hbm", "kernel": f"{kname} (dequant + gate/up + SwiGLU grouped GEMM on the "
                                       "matrix cores, one launch per wave of a layer's experts; every launch of the "
                                       "timed steps bracketed by HIP events on its stream)",
             "achieved": round(kern["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kern["GBps"] / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic(MFMA_GATE_UP_KERNEL, "prefill2048_mfma_counters.md"),
+            "traffic": counter_traffic(kname, "prefill2048_mfma_counters.md"),
             "bytes_per_launch": kern["bytes_per_launch"], "us_per_launch": kern["us_per_launch"],
             "launches": kern["launches"],
             "mfma": {"achieved": round(kern["TFLOPs"], 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -868,8 +879,6 @@ def main():
     cfg = synth.get(args.workload)
     if not cfg.streaming:
         raise SystemExit("the headline workload is a streamed configuration; the resident decode is an extra leg")
-    if cfg.fmt != 0:
-        raise SystemExit("MXFP4 and super-block workloads are measured by the mx and superblock legs")
     result = headline(torch, args, cfg)
     if not args.no_legs:
         decode = decode_leg(torch, args)
@@ -886,6 +895,11 @@ def main():
             from routed_expert_streaming_amd import _lib as L
             result["layer_decode32"] = layer_leg(torch, "decode32_stream", L.MOE_FFN_SPLIT, 20)
             result["layer_prefill2048"] = layer_leg(torch, "prefill2048_stream", L.MOE_FFN_MFMA, 3)
+            if not args.no_mx:  # the same layers with MXFP4 and super-block weights
+                for tag in ("mx", "sb"):
+                    result[f"layer_decode32_{tag}"] = layer_leg(torch, f"decode32_{tag}_stream", L.MOE_FFN_SPLIT, 20)
+                    result[f"layer_prefill2048_{tag}"] = layer_leg(torch, f"prefill2048_{tag}_stream",
+                                                                   L.MOE_FFN_MFMA, 3)
     print(json.dumps(result), flush=True)
 
 

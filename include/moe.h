@@ -306,6 +306,31 @@ int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, const int32_t
                     const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
                     float *y, int path, void *stream);
 
+/* moe_expert_ffn, moe_expert_gate_up and moe_expert_down for expert slabs of
+ * weight format `format`: 0 (the fp16 scale/min blocks above; the calls then
+ * equal the ones above), 1 (MXFP4) or 2 (super-blocks), with the slab layouts of
+ * the MXFP4 and super-block sections below (the pages name MXFP4 decode paths
+ * among their kernels' sources: LayerStoRm README, "License and attributions";
+ * their own weights are a 4-bit k-quant GGUF type: README, "Serve").  Every
+ * path reads every format with the arithmetic described there; the pairs path
+ * of formats 1 and 2 is the dequant-GEMV in pair grouping.  The MFMA kernels
+ * form MXFP4 weights in bf16 exactly (gfx950's scaled FP4-to-bf16 convert with
+ * the block's E8M0 scale) and super-block weights as format 0's (scale*q + min
+ * rounded to bf16).  Super-blocks need H and I multiples of 256 (MOE_E_SHAPE);
+ * automatic paths then use MFMA / split only when they are.  MOE_E_ARG for a
+ * format outside 0..2. */
+int moe_expert_ffn_fmt(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                       const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                       float *y, void *workspace, size_t workspace_bytes, int path, int format, void *stream);
+int moe_expert_gate_up_fmt(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                           const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                           const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                           uint16_t *h, int path, int format, void *stream);
+int moe_expert_down_fmt(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                        const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                        const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                        float *y, int path, int format, void *stream);
+
 /* ------------------------------------------------------------------ combine
  * Weighted combine of a token's expert outputs (LayerStoRm README, "TL;DR": the
  * selected experts' outputs are combined into the layer output; "Serve" notes: a
@@ -380,11 +405,13 @@ int moe_residual_norm(const uint16_t *add, float *resid, int T, int H, float eps
  * gfx950's scaled FP4-to-bf16 convert (exact) and compute as for format 0: fp32
  * sums, h rounded once to bf16, fixed-order combine.
  *
- * One token only (T = 1; T = 0 is a no-op; MOE_E_SHAPE for T > 1 or other
- * shapes: H in {2048, 4096, 6144} (routed variant: 2048, 4096), I in {1536, 2048},
- * k + shared <= 16).  Arguments, workspace and errors otherwise as
- * moe_expert_ffn_combine (no path argument) and moe_route_ffn_combine.  A cache
- * of MXFP4 slabs sets format = 1 in its descriptor. */
+ * One token (T = 1) with H in {2048, 4096, 6144}, I in {1536, 2048} and k +
+ * shared <= 16 runs the fused one-token kernels (with the router finished inside
+ * gate/up for H in {2048, 4096}); any other T or shape runs the automatic path of
+ * moe_expert_ffn_fmt (pairs, split or MFMA) and moe_combine.  T = 0 is a no-op.
+ * Arguments, workspace and errors otherwise as moe_expert_ffn_combine (no path
+ * argument) and moe_route_ffn_combine.  A cache of MXFP4 slabs sets format = 1
+ * in its descriptor. */
 int moe_mx_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
                               const float *topk_w, int k, const void *const *expert_table, const void *shared_slab,
                               uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
@@ -405,9 +432,9 @@ int moe_mx_route_ffn_combine(const uint16_t *x, int T, int H, int I, const float
  * 6j..6j+5 of each 48-bit little-endian field; 4.5 bits per weight.  Same slab
  * arrangement as the other formats.  The kernels form scale d*s_j and min
  * -dmin*m_j per block (exact in fp32) and then compute as for format 0.
- * One token only, as the MXFP4 entry points (same arguments, shapes and errors,
- * plus MOE_E_SHAPE unless H and I are multiples of 256).  A cache of such slabs
- * sets format = 2 in its descriptor. */
+ * Tokens, shapes and paths as for the MXFP4 entry points (same arguments and
+ * errors, plus MOE_E_SHAPE unless H and I are multiples of 256).  A cache of
+ * such slabs sets format = 2 in its descriptor. */
 int moe_sb_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
                               const float *topk_w, int k, const void *const *expert_table, const void *shared_slab,
                               uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);

@@ -78,6 +78,9 @@ def lib():
             "moe_expert_ffn_workspace_bytes": ([i, i, i, i, i, i], sz),
             "moe_expert_ffn": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, sz, i, vp], i),
             "moe_expert_gate_up": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, vp], i),
+            "moe_expert_ffn_fmt": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, sz, i, i, vp], i),
+            "moe_expert_gate_up_fmt": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp], i),
+            "moe_expert_down_fmt": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp], i),
             "moe_expert_down": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, vp], i),
             "moe_expert_ffn_combine": ([vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, i, vp], i),
             "moe_route_ffn_combine_workspace_bytes": ([i, i, i, i, i, i], sz),
@@ -358,6 +361,28 @@ def moe_expert_down(h, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expe
     _check(lib().moe_expert_down(_ptr(h), T, H, I, E, _ptr(topk_idx), k, _ptr(count), _ptr(offset),
                                  _ptr(pair_of_row), _ptr(expert_table), _ptr(shared_slab), _ptr(expert_mask),
                                  _ptr(y), path, _stream(stream)), "moe_expert_down")
+
+
+def moe_expert_ffn_fmt(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, expert_mask, y, workspace,
+                       workspace_bytes, path=MOE_FFN_AUTO, format=0, stream=None):
+    _check(lib().moe_expert_ffn_fmt(_ptr(x), T, H, I, E, _ptr(topk_idx), k, _ptr(expert_table), _ptr(shared_slab),
+                                    _ptr(expert_mask), _ptr(y), _ptr(workspace), workspace_bytes, path, format,
+                                    _stream(stream)), "moe_expert_ffn_fmt")
+
+
+def moe_expert_gate_up_fmt(x, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
+                           expert_mask, h, path=MOE_FFN_AUTO, format=0, stream=None):
+    _check(lib().moe_expert_gate_up_fmt(_ptr(x), T, H, I, E, _ptr(topk_idx), k, _ptr(count), _ptr(offset),
+                                        _ptr(pair_of_row), _ptr(expert_table), _ptr(shared_slab),
+                                        _ptr(expert_mask), _ptr(h), path, format, _stream(stream)),
+           "moe_expert_gate_up_fmt")
+
+
+def moe_expert_down_fmt(h, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
+                        expert_mask, y, path=MOE_FFN_AUTO, format=0, stream=None):
+    _check(lib().moe_expert_down_fmt(_ptr(h), T, H, I, E, _ptr(topk_idx), k, _ptr(count), _ptr(offset),
+                                     _ptr(pair_of_row), _ptr(expert_table), _ptr(shared_slab), _ptr(expert_mask),
+                                     _ptr(y), path, format, _stream(stream)), "moe_expert_down_fmt")
 
 
 def moe_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, workspace,

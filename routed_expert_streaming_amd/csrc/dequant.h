@@ -42,12 +42,18 @@ __host__ __device__ constexpr size_t row_bytes_fmt(int K) {
     return FMT == 1 ? mx_row_bytes(K) : FMT == 2 ? sb_row_bytes(K) : slab_row_bytes(K);
 }
 
-__device__ __forceinline__ MatRows slab_w1(const uint8_t *slab, int H, int) { return {slab, 2 * slab_row_bytes(H)}; }
-__device__ __forceinline__ MatRows slab_w3(const uint8_t *slab, int H, int) {
-    return {slab + slab_row_bytes(H), 2 * slab_row_bytes(H)};
+// The three matrices of a slab of weight format FMT.
+template <int FMT = 0>
+__device__ __forceinline__ MatRows slab_w1(const uint8_t *slab, int H, int) {
+    return {slab, 2 * row_bytes_fmt<FMT>(H)};
 }
+template <int FMT = 0>
+__device__ __forceinline__ MatRows slab_w3(const uint8_t *slab, int H, int) {
+    return {slab + row_bytes_fmt<FMT>(H), 2 * row_bytes_fmt<FMT>(H)};
+}
+template <int FMT = 0>
 __device__ __forceinline__ MatRows slab_w2(const uint8_t *slab, int H, int I) {
-    return {slab + (size_t)I * 2 * slab_row_bytes(H), slab_row_bytes(I)};
+    return {slab + (size_t)I * 2 * row_bytes_fmt<FMT>(H), row_bytes_fmt<FMT>(I)};
 }
 }  // namespace moe
 
@@ -128,12 +134,13 @@ __device__ __forceinline__ bool moe_group_sum_owner(int lane_in_group) {
 // two bf16 values (low nibble first) through gfx950's scaled FP4 convert with
 // scale 1 (exact: an E2M1 value has two significant bits), then
 // v_dot2_f32_bf16; two interleaved accumulators as in moe_block_dot.
-__device__ __forceinline__ float moe_mx_block_dot(const uint4 c, const uint4 *xb) {
+// (stride: distance in uint4 between the block's consecutive 8-column words)
+__device__ __forceinline__ float moe_mx_block_dot(const uint4 c, const uint4 *xb, int stride = 1) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     float acc[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint4 X = xb[j];
+        const uint4 X = xb[j * stride];
         float a = acc[j & 1];
         a = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 0)), X.x, a);
         a = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 1)), X.y, a);

@@ -20,7 +20,7 @@ struct FfnArgs {
     float *y;                   // [T*k + T*shared, H] fp32 expert outputs
     const uint8_t **pair_slab;  // [T*k + T*shared] or nullptr: slab of each pair (nullptr = masked),
                                 // written by the one-token gate/up kernel, read by the down kernel
-    int fmt;                    // expert weight format: 0 = fp16 scale/min blocks, 1 = MXFP4 (one-token decode only)
+    int fmt;                    // expert weight format: 0 = fp16 scale/min blocks, 1 = MXFP4, 2 = super-blocks
     int min_m, max_m;           // grouped kernels skip groups with fewer / more tokens than these
     int compact;                // MFMA kernel: workgroups take the active groups in rank order (see the kernel)
     const uint8_t *prefetch;    // or nullptr: bytes the one-token down kernel reads into the device caches
@@ -59,6 +59,9 @@ int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s)
 bool mfma_supported(const FfnArgs &a);
 int mfma_gate_up(const FfnArgs &a, hipStream_t s);
 int mfma_down(const FfnArgs &a, hipStream_t s);
+
+// (token, slot) pairs the one-token down kernel combines (routed slots + shared).
+constexpr int kDown1MaxPairs = 16;
 
 // Tokens from which the automatic choice uses the MFMA kernels.
 constexpr int kMfmaMinTokens = 128;

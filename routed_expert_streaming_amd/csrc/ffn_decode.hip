@@ -641,7 +641,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
 // two-kernel path bit for bit.  Every SIMD gets several independent waves
 // instead of one wave walking all pairs of a row.
 constexpr int kDown1MaxRows = 64;  // rows per workgroup
-constexpr int kDown1MaxPairs = 16;
+constexpr int kDown1MaxPairs = moe::kDown1MaxPairs;
 
 template <int BPL, int D, bool COMBINE, int FMT = 0>
 __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, const float *__restrict__ topk_w,

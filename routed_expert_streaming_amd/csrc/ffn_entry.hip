@@ -29,13 +29,34 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
     __syncthreads();
     for (int p = tid; p < n; p += nt) atomicAdd(&cnt[idx[p]], 1);
     __syncthreads();
-    if (tid == 0) {  // E <= 1024: a serial scan is cheap next to the rest
-        int acc = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = acc;
-            acc += cnt[e];
+    {  // exclusive scan of the counts, one expert per thread (E <= 1024 = blockDim.x):
+       // inclusive scan inside each wave, then over the wave totals
+        __shared__ int wsum[1024 / 64];
+        const int wv = tid >> 6, ln = tid & 63;
+        const int v = tid < E ? cnt[tid] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o, 64);
+            if (ln >= o) incl += u;
         }
-        off[E] = acc;
+        if (ln == 63) wsum[wv] = incl;
+        __syncthreads();
+        if (wv == 0) {
+            const int nw = nt >> 6;
+            const int t0 = ln < nw ? wsum[ln] : 0;
+            int ti = t0;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const int u = __shfl_up(ti, o, 64);
+                if (ln >= o) ti += u;
+            }
+            if (ln < nw) wsum[ln] = ti - t0;  // exclusive over the waves
+        }
+        __syncthreads();
+        const int excl = incl - v + wsum[wv];
+        if (tid < E) off[tid] = excl;
+        if (tid == E - 1) off[E] = excl + v;
     }
     __syncthreads();
     for (int e = tid; e < E; e += nt) {
@@ -168,10 +189,13 @@ extern "C" size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int
 namespace {
 
 int validate_ffn(const void *act, int T, int H, int I, int E, const int32_t *topk_idx, int k,
-                 const void *const *expert_table, const void *out, int path, const char *who) {
+                 const void *const *expert_table, const void *out, int path, const char *who, int fmt = 0) {
     if (!act || !topk_idx || !expert_table || !out) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
+    if (fmt < 0 || fmt > 2) return moe::fail(MOE_E_ARG, "%s: weight format %d (0, 1 or 2)", who, fmt);
     if (H <= 0 || I <= 0 || H % 32 || I % 32)
         return moe::fail(MOE_E_SHAPE, "%s: H=%d and I=%d must be positive multiples of 32", who, H, I);
+    if (fmt == 2 && (H % 256 || I % 256))
+        return moe::fail(MOE_E_SHAPE, "%s: super-block slabs need H, I multiples of 256 (H=%d I=%d)", who, H, I);
     if (H > 16384 || I > 16384) return moe::fail(MOE_E_SHAPE, "%s: H=%d I=%d above 16384", who, H, I);
     if (E < 1 || E > kPermMaxE || k < 1 || k > E) return moe::fail(MOE_E_SHAPE, "%s: E=%d k=%d", who, E, k);
     if (path < MOE_FFN_AUTO || path > MOE_FFN_SPLIT) return moe::fail(MOE_E_ARG, "%s: path=%d", who, path);
@@ -182,7 +206,7 @@ int validate_ffn(const void *act, int T, int H, int I, int E, const int32_t *top
 int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, int H, int I, int E,
               const int32_t *topk_idx, int k, const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
               const void *const *table, const void *shared, const uint8_t *mask, int path, int *max_m,
-              const char *who) {
+              const char *who, int fmt = 0) {
     const bool have_perm = count && offset && pair_of_row;
     if ((count || offset || pair_of_row) && !have_perm)
         return moe::fail(MOE_E_ARG, "%s: count, offset and pair_of_row go together", who);
@@ -208,6 +232,7 @@ int make_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, float *y, int T, 
     a.count = count;
     a.offset = offset;
     a.pair_of_row = pair_of_row;
+    a.fmt = fmt;
     a.min_m = 0;
     a.max_m = 1 << 30;
     *max_m = grouped ? T : (shared ? T : 1);
@@ -290,11 +315,17 @@ bool use_mfma(const moe::FfnArgs &a, int path) {
 // Automatic path of the one-call entry points: pairs for few (token, slot)
 // pairs, MFMA for many tokens, split in between; the MFMA and split paths need
 // H and I multiples of 128, other shapes take the grouped GEMV.
-int auto_path(int T, int k, int H, int I) {
+int auto_path(int T, int k, int H, int I, int fmt = 0) {
     if ((long long)T * k <= 64) return MOE_FFN_PAIRS;
-    if (H % 128 || I % 128) return MOE_FFN_GROUPED;
+    const int mult = fmt == 2 ? 256 : 128;
+    if (H % mult || I % mult) return MOE_FFN_GROUPED;
     return T >= moe::kMfmaMinTokens ? MOE_FFN_MFMA : MOE_FFN_SPLIT;
 }
+
+// The pair-grouped decode kernels as separate gate/up and down calls: format 0
+// (the other formats run them only through their one-call entry points, for
+// one token; here they take the grouped GEMV, which covers every shape).
+bool decode_ok(const moe::FfnArgs &a) { return moe::decode_supported(a) && a.fmt == 0; }
 
 // Split grouped dispatch for an explicit split path, or automatic with a permutation.
 bool use_split(const moe::FfnArgs &a, int path) {
@@ -306,53 +337,57 @@ bool use_split(const moe::FfnArgs &a, int path) {
 namespace {
 int gate_up_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k, const int32_t *count,
                  const int32_t *offset, const int32_t *pair_of_row, const void *const *expert_table,
-                 const void *shared_slab, const uint8_t *expert_mask, uint16_t *h, int path, bool fork, void *stream) {
+                 const void *shared_slab, const uint8_t *expert_mask, uint16_t *h, int path, bool fork, void *stream,
+                 int fmt = 0) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_gate_up: T=%d < 0", T);
     if (T == 0) return MOE_OK;
-    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, h, path, "expert_gate_up");
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, h, path, "expert_gate_up", fmt);
     if (rc != MOE_OK) return rc;
     moe::FfnArgs a;
     int max_m = 1;
     rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
-                   expert_mask, path, &max_m, "expert_gate_up");
+                   expert_mask, path, &max_m, "expert_gate_up", fmt);
     if (rc != MOE_OK) return rc;
     if (use_mfma(a, path)) return moe::mfma_gate_up(a, (hipStream_t)stream);
-    if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_gate_up: MFMA path needs H, I multiples of 128");
-    if (moe::decode_supported(a)) return moe::decode_gate_up(a, (hipStream_t)stream);
+    if (path == MOE_FFN_MFMA)
+        return moe::fail(MOE_E_SHAPE, "expert_gate_up: MFMA path needs H, I multiples of %d", fmt == 2 ? 256 : 128);
+    if (decode_ok(a)) return moe::decode_gate_up(a, (hipStream_t)stream);
     return grouped_gemv<true>(a, max_m, use_split(a, path), fork, (hipStream_t)stream);
 }
 
 int down_impl(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k, const int32_t *count,
               const int32_t *offset, const int32_t *pair_of_row, const void *const *expert_table,
-              const void *shared_slab, const uint8_t *expert_mask, float *y, int path, bool fork, void *stream) {
+              const void *shared_slab, const uint8_t *expert_mask, float *y, int path, bool fork, void *stream,
+              int fmt = 0) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_down: T=%d < 0", T);
     if (T == 0) return MOE_OK;
-    int rc = validate_ffn(h, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_down");
+    int rc = validate_ffn(h, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_down", fmt);
     if (rc != MOE_OK) return rc;
     moe::FfnArgs a;
     int max_m = 1;
     rc = make_args(a, nullptr, const_cast<uint16_t *>(h), y, T, H, I, E, topk_idx, k, count, offset, pair_of_row,
-                   expert_table, shared_slab, expert_mask, path, &max_m, "expert_down");
+                   expert_table, shared_slab, expert_mask, path, &max_m, "expert_down", fmt);
     if (rc != MOE_OK) return rc;
     if (use_mfma(a, path)) return moe::mfma_down(a, (hipStream_t)stream);
-    if (path == MOE_FFN_MFMA) return moe::fail(MOE_E_SHAPE, "expert_down: MFMA path needs H, I multiples of 128");
-    if (moe::decode_supported(a)) return moe::decode_down(a, nullptr, nullptr, (hipStream_t)stream);
+    if (path == MOE_FFN_MFMA)
+        return moe::fail(MOE_E_SHAPE, "expert_down: MFMA path needs H, I multiples of %d", fmt == 2 ? 256 : 128);
+    if (decode_ok(a)) return moe::decode_down(a, nullptr, nullptr, (hipStream_t)stream);
     return grouped_gemv<false>(a, max_m, use_split(a, path), fork, (hipStream_t)stream);
 }
 
 int ffn_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
              const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask, float *y,
-             void *workspace, size_t workspace_bytes, int path, bool fork, void *stream) {
+             void *workspace, size_t workspace_bytes, int path, bool fork, void *stream, int fmt = 0) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_ffn: T=%d < 0", T);
     if (T == 0) return MOE_OK;
     if (!workspace) return moe::fail(MOE_E_ARG, "expert_ffn: NULL workspace");
-    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_ffn");
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, y, path, "expert_ffn", fmt);
     if (rc != MOE_OK) return rc;
     const int has_shared = shared_slab != nullptr;
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "expert_ffn: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
-    if (path == MOE_FFN_AUTO) path = auto_path(T, k, H, I);
+    if (path == MOE_FFN_AUTO) path = auto_path(T, k, H, I, fmt);
     if (path != MOE_FFN_PAIRS && (long long)T * k > kPermMaxPairs)
         return moe::fail(MOE_E_SHAPE, "expert_ffn: grouped paths need T*k <= %d", kPermMaxPairs);
     hipStream_t s = (hipStream_t)stream;
@@ -367,25 +402,25 @@ int ffn_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_
         if (rc != MOE_OK) return rc;
     }
     rc = gate_up_impl(x, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask, h, path,
-                      fork, stream);
+                      fork, stream, fmt);
     if (rc != MOE_OK) return rc;
     return down_impl(h, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask, y, path,
-                     fork, stream);
+                     fork, stream, fmt);
 }
 
 int ffn_combine_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, const float *topk_w,
                      int k, const void *const *expert_table, const void *shared_slab, uint16_t *out, void *workspace,
-                     size_t workspace_bytes, int path, bool fork, void *stream) {
+                     size_t workspace_bytes, int path, bool fork, void *stream, int fmt = 0) {
     if (T < 0) return moe::fail(MOE_E_ARG, "expert_ffn_combine: T=%d < 0", T);
     if (T == 0) return MOE_OK;
     if (!workspace || !topk_w) return moe::fail(MOE_E_ARG, "expert_ffn_combine: NULL pointer");
-    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, path, "expert_ffn_combine");
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, path, "expert_ffn_combine", fmt);
     if (rc != MOE_OK) return rc;
     const int has_shared = shared_slab != nullptr;
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "expert_ffn_combine: workspace %zu < %zu bytes", workspace_bytes, Ly.total);
-    if (path == MOE_FFN_AUTO) path = auto_path(T, k, H, I);
+    if (path == MOE_FFN_AUTO) path = auto_path(T, k, H, I, fmt);
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     uint16_t *h = (uint16_t *)(ws + Ly.h);
@@ -393,9 +428,9 @@ int ffn_combine_impl(const uint16_t *x, int T, int H, int I, int E, const int32_
         moe::FfnArgs a;
         int max_m = 1;
         rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, nullptr, nullptr, nullptr, expert_table,
-                       shared_slab, nullptr, MOE_FFN_PAIRS, &max_m, "expert_ffn_combine");
+                       shared_slab, nullptr, MOE_FFN_PAIRS, &max_m, "expert_ffn_combine", fmt);
         if (rc != MOE_OK) return rc;
-        if (moe::decode_supported(a)) {
+        if (decode_ok(a)) {
             if (moe::decode1_publishes_slabs(a)) a.pair_slab = (const uint8_t **)(ws + Ly.slabs);
             rc = moe::decode_gate_up(a, s);
             if (rc != MOE_OK) return rc;
@@ -404,7 +439,7 @@ int ffn_combine_impl(const uint16_t *x, int T, int H, int I, int E, const int32_
     }
     float *y = (float *)(ws + Ly.y);
     rc = ffn_impl(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, nullptr, y, workspace, workspace_bytes, path,
-                  fork, stream);
+                  fork, stream, fmt);
     if (rc != MOE_OK) return rc;
     return moe_combine(y, topk_w, T, k, H, has_shared, out, stream);
 }
@@ -426,11 +461,35 @@ extern "C" int moe_expert_down(const uint16_t *h, int T, int H, int I, int E, co
                      y, path, true, stream);
 }
 
+extern "C" int moe_expert_gate_up_fmt(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                                      const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                                      const void *const *expert_table, const void *shared_slab,
+                                      const uint8_t *expert_mask, uint16_t *h, int path, int format, void *stream) {
+    return gate_up_impl(x, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab,
+                        expert_mask, h, path, true, stream, format);
+}
+
+extern "C" int moe_expert_down_fmt(const uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                                   const int32_t *count, const int32_t *offset, const int32_t *pair_of_row,
+                                   const void *const *expert_table, const void *shared_slab,
+                                   const uint8_t *expert_mask, float *y, int path, int format, void *stream) {
+    return down_impl(h, T, H, I, E, topk_idx, k, count, offset, pair_of_row, expert_table, shared_slab, expert_mask,
+                     y, path, true, stream, format);
+}
+
 extern "C" int moe_expert_ffn(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
                               const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
                               float *y, void *workspace, size_t workspace_bytes, int path, void *stream) {
     return ffn_impl(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, expert_mask, y, workspace,
                     workspace_bytes, path, true, stream);
+}
+
+extern "C" int moe_expert_ffn_fmt(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx, int k,
+                                  const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
+                                  float *y, void *workspace, size_t workspace_bytes, int path, int format,
+                                  void *stream) {
+    return ffn_impl(x, T, H, I, E, topk_idx, k, expert_table, shared_slab, expert_mask, y, workspace,
+                    workspace_bytes, path, true, stream, format);
 }
 
 extern "C" int moe_expert_ffn_combine(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_idx,
@@ -505,18 +564,18 @@ extern "C" int moe_route_ffn_combine(const uint16_t *x, int T, int H, int I, con
 // One-token decode with MXFP4 (format 1) or super-block (format 2) expert slabs:
 // the same kernels specialised for the format (pairs path, fused combine).
 namespace {
+// One token: the fused one-token kernels when they cover the shape (true in *fused).
 int fmt_ffn_args(moe::FfnArgs &a, const uint16_t *x, uint16_t *h, int T, int H, int I, int E, const int32_t *topk_idx,
-                 int k, const void *const *table, const void *shared, const char *who, int fmt) {
-    if (T != 1) return moe::fail(MOE_E_SHAPE, "%s: weight format %d needs T = 1 (T=%d)", who, fmt, T);
-    if (fmt == 2 && (H % 256 || I % 256))
-        return moe::fail(MOE_E_SHAPE, "%s: super-block slabs need H, I multiples of 256 (H=%d I=%d)", who, H, I);
+                 int k, const void *const *table, const void *shared, const char *who, int fmt, bool *fused) {
+    *fused = false;
+    if (T != 1) return MOE_OK;
     int max_m = 1;
     int rc = make_args(a, x, h, nullptr, T, H, I, E, topk_idx, k, nullptr, nullptr, nullptr, table, shared, nullptr,
-                       MOE_FFN_PAIRS, &max_m, who);
+                       MOE_FFN_PAIRS, &max_m, who, fmt);
     if (rc != MOE_OK) return rc;
-    a.fmt = fmt;
-    if (!moe::decode_supported(a) || !moe::decode1_publishes_slabs(a))
-        return moe::fail(MOE_E_SHAPE, "%s: shapes H=%d I=%d k=%d not supported for format %d", who, H, I, k, fmt);
+    const int ni = I >> 5;
+    *fused = moe::decode_supported(a) && moe::decode1_publishes_slabs(a) && (ni == 48 || ni == 64) &&
+             a.k + (a.shared ? 1 : 0) <= moe::kDown1MaxPairs;
     return MOE_OK;
 }
 
@@ -527,15 +586,20 @@ int fmt_expert_ffn_combine(int fmt, const char *who, const uint16_t *x, int T, i
     if (T < 0) return moe::fail(MOE_E_ARG, "%s: T=%d < 0", who, T);
     if (T == 0) return MOE_OK;
     if (!workspace || !topk_w) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
-    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, MOE_FFN_PAIRS, who);
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, MOE_FFN_AUTO, who, fmt);
     if (rc != MOE_OK) return rc;
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, shared_slab != nullptr);
     if (workspace_bytes < Ly.total)
         return moe::fail(MOE_E_NOMEM, "%s: workspace %zu < %zu bytes", who, workspace_bytes, Ly.total);
     char *ws = (char *)workspace;
     moe::FfnArgs a;
-    rc = fmt_ffn_args(a, x, (uint16_t *)(ws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who, fmt);
+    bool fused = false;
+    rc = fmt_ffn_args(a, x, (uint16_t *)(ws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who, fmt,
+                      &fused);
     if (rc != MOE_OK) return rc;
+    if (!fused)  // several tokens (or a shape the one-token kernels do not cover): the grouped paths
+        return ffn_combine_impl(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, workspace,
+                                workspace_bytes, MOE_FFN_AUTO, true, stream, fmt);
     a.pair_slab = (const uint8_t **)(ws + Ly.slabs);
     rc = moe::decode_gate_up(a, (hipStream_t)stream);
     if (rc != MOE_OK) return rc;
@@ -550,7 +614,7 @@ int fmt_route_ffn_combine(int fmt, const char *who, const uint16_t *x, int T, in
     if (!prefetch && prefetch_bytes) return moe::fail(MOE_E_ARG, "%s: %zu prefetch bytes at NULL", who, prefetch_bytes);
     if (T == 0) return MOE_OK;
     if (!workspace || !w_router || !topk_w) return moe::fail(MOE_E_ARG, "%s: NULL pointer", who);
-    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, MOE_FFN_PAIRS, who);
+    int rc = validate_ffn(x, T, H, I, E, topk_idx, k, expert_table, out, MOE_FFN_AUTO, who, fmt);
     if (rc != MOE_OK) return rc;
     const int has_shared = shared_slab != nullptr;
     const size_t need = moe_route_ffn_combine_workspace_bytes(T, H, I, E, k, has_shared);
@@ -561,9 +625,11 @@ int fmt_route_ffn_combine(int fmt, const char *who, const uint16_t *x, int T, in
     hipStream_t s = (hipStream_t)stream;
     moe::FfnArgs a;
     const FfnLayout Ly = ffn_layout(T, H, I, E, k, has_shared);
-    rc = fmt_ffn_args(a, x, (uint16_t *)(fws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who, fmt);
+    bool fused = false;
+    rc = fmt_ffn_args(a, x, (uint16_t *)(fws + Ly.h), T, H, I, E, topk_idx, k, expert_table, shared_slab, who, fmt,
+                      &fused);
     if (rc != MOE_OK) return rc;
-    if (k <= moe::kTopkMaxK && H <= moe::kSlice * moe::kMaxSlices && moe::decode1_routed_supported(a, E)) {
+    if (fused && k <= moe::kTopkMaxK && H <= moe::kSlice * moe::kMaxSlices && moe::decode1_routed_supported(a, E)) {
         double *partial = moe::router_partials_buf(rws, T, E);
         rc = moe::router_partials(x, T, H, w_router, E, partial, s);
         if (rc != MOE_OK) return rc;

@@ -20,6 +20,13 @@
 //    sum((scale*q + min) * x) exactly in real arithmetic.
 //  * Partial sums of the LPR lanes of a row meet in a fixed butterfly, so the
 //    output is reproducible run to run.
+//  * The other weight formats use the same structure with their own block
+//    terms, the ones the one-token kernels use: MXFP4 blocks through the scaled
+//    FP4-to-bf16 convert (activations staged in column order, scale 2^(v-127)
+//    applied to the block's fp32 sum), super-block headers turned into each
+//    block's scale and min and then the format-0 identity.
+#include <type_traits>
+
 #include "common.h"
 #include "dequant.h"
 #include "ffn.h"
@@ -68,8 +75,10 @@ __device__ __forceinline__ int group_row(const moe::FfnArgs &a, const Group &gr,
 
 // Stage mcount activation rows (bf16, K columns) into LDS:
 //   X[(m*4 + j)*nblk + b] = the 8 values of word j of block b, as bf16 pairs
-//                           (v0,v4), (v1,v5), (v2,v6), (v3,v7)
+//                           (v0,v4), (v1,v5), (v2,v6), (v3,v7) -- for MXFP4
+//                           (NATURAL) in column order (v0,v1) .. (v6,v7)
 //   S[m*nblk + b]         = fp32 sum of the block's 32 values (in index order)
+template <bool NATURAL>
 __device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ act, int K, const int *src_rows, int mcount,
                                            uint4 *X, float *S) {
     const int nblk = K >> 5;
@@ -82,11 +91,13 @@ __device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ act, int
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint4 p;
-            p.x = (d[j].x & 0xFFFFu) | (d[j].z << 16);
-            p.y = (d[j].x >> 16) | (d[j].z & 0xFFFF0000u);
-            p.z = (d[j].y & 0xFFFFu) | (d[j].w << 16);
-            p.w = (d[j].y >> 16) | (d[j].w & 0xFFFF0000u);
+            uint4 p = d[j];
+            if constexpr (!NATURAL) {
+                p.x = (d[j].x & 0xFFFFu) | (d[j].z << 16);
+                p.y = (d[j].x >> 16) | (d[j].z & 0xFFFF0000u);
+                p.z = (d[j].y & 0xFFFFu) | (d[j].w << 16);
+                p.w = (d[j].y >> 16) | (d[j].w & 0xFFFF0000u);
+            }
             X[(m * 4 + j) * nblk + b] = p;
             const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
 #pragma unroll
@@ -105,16 +116,43 @@ __device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ act, int
 // of the next D steps in flight in registers (a ring of D slots, the loop
 // unrolled by D so every slot is a fixed set of registers).  The weights of a
 // row are dotted with every staged token before the slot is refilled.
+// FMT: weight format -- 0: (fp16 scale, fp16 min) record per block; 1: MXFP4,
+// one E8M0 scale byte per block; 2: super-blocks, one 16-byte header per 8
+// blocks (each lane reads the header of each of its blocks).
 #ifndef MOE_GEMV_WAVES_PER_EU
 #define MOE_GEMV_WAVES_PER_EU 2
 #endif
-template <int BPL, bool GATEUP>
+template <int BPL, bool GATEUP, int FMT>
 struct GemvSlot {
+    using Param = std::conditional_t<FMT == 2, uint4, uint32_t>;
     uint4 c0[BPL], c1[GATEUP ? BPL : 1];
-    uint32_t p0[BPL], p1[GATEUP ? BPL : 1];
+    Param p0[BPL], p1[GATEUP ? BPL : 1];
 };
 
-template <int LPR, int BPL, int D, bool GATEUP>
+// the block parameters of block blk of a row (codes at row, parameters at row + K/2)
+template <int FMT>
+__device__ __forceinline__ std::conditional_t<FMT == 2, uint4, uint32_t> load_param(const uint8_t *row, int K, int blk) {
+    if constexpr (FMT == 2)
+        return load_stream_u4(row + K / 2 + 16 * (blk >> 3));
+    else if constexpr (FMT == 1)
+        return load_stream_u8(row + K / 2 + blk);
+    else
+        return load_stream_u32(row + K / 2 + 4 * blk);
+}
+
+// sum over block blk of W * x for one staged token (xb: the block's first word, S: its sum)
+template <int FMT>
+__device__ __forceinline__ float block_term(const uint4 c, std::conditional_t<FMT == 2, uint4, uint32_t> p,
+                                            const uint4 *xb, int stride, float S, int blk, uint32_t magic) {
+    if constexpr (FMT == 1)
+        return moe_mx_block_value(p, moe_mx_block_dot(c, xb, stride));
+    else if constexpr (FMT == 2)
+        return moe_sb_block_value(p, blk & 7, moe_block_dot(c, xb, stride, magic), S);
+    else
+        return moe_block_value(p, moe_block_dot(c, xb, stride, magic), S);
+}
+
+template <int LPR, int BPL, int D, bool GATEUP, int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_GEMV_WAVES_PER_EU)))
 void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
     constexpr int RPW = 64 / LPR;              // rows per wave per step
@@ -130,8 +168,8 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
     const int nsteps = min(iters, (R - row0 + ROWS_PER_STEP - 1) / ROWS_PER_STEP);
 
     // matrix rows: W1 and W3 (gate/up) or W2 (down); codes, then records at + K/2
-    const moe::MatRows m0 = GATEUP ? moe::slab_w1(gr.slab, a.H, a.I) : moe::slab_w2(gr.slab, a.H, a.I);
-    const moe::MatRows m1 = moe::slab_w3(gr.slab, a.H, a.I);
+    const moe::MatRows m0 = GATEUP ? moe::slab_w1<FMT>(gr.slab, a.H, a.I) : moe::slab_w2<FMT>(gr.slab, a.H, a.I);
+    const moe::MatRows m1 = moe::slab_w3<FMT>(gr.slab, a.H, a.I);
 
     extern __shared__ uint4 lds[];
     uint4 *X = lds;
@@ -145,21 +183,21 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
     const int rbase = row0 + wave * RPW + sub;  // this lane group's row in step 0
 
     // rows past R re-read row R-1 (valid memory) and are not stored
-    auto load = [&](GemvSlot<BPL, GATEUP> &sl, int step) {
+    auto load = [&](GemvSlot<BPL, GATEUP, FMT> &sl, int step) {
         const int r = min(rbase + step * ROWS_PER_STEP, R - 1);
         const uint8_t *row0 = m0.row0 + (size_t)r * m0.stride, *row1 = m1.row0 + (size_t)r * m1.stride;
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             const int blk = min(c + b * LPR, nblk - 1);
             sl.c0[b] = load_stream_u4(row0 + 16 * blk);
-            sl.p0[b] = load_stream_u32(row0 + K / 2 + 4 * blk);
+            sl.p0[b] = load_param<FMT>(row0, K, blk);
             if constexpr (GATEUP) {
                 sl.c1[b] = load_stream_u4(row1 + 16 * blk);
-                sl.p1[b] = load_stream_u32(row1 + K / 2 + 4 * blk);
+                sl.p1[b] = load_param<FMT>(row1, K, blk);
             }
         }
     };
-    auto compute = [&](const GemvSlot<BPL, GATEUP> &sl, int step, int mcount) {
+    auto compute = [&](const GemvSlot<BPL, GATEUP, FMT> &sl, int step, int mcount) {
         const int r = rbase + step * ROWS_PER_STEP;
         for (int m = 0; m < mcount; ++m) {
             float v0 = 0.0f, v1 = 0.0f;
@@ -169,8 +207,8 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
                 if (blk < nblk) {
                     const uint4 *xb = X + (size_t)(m * 4) * nblk + blk;
                     const float Sb = S[m * nblk + blk];
-                    v0 += moe_block_value(sl.p0[b], moe_block_dot(sl.c0[b], xb, nblk, magic), Sb);
-                    if constexpr (GATEUP) v1 += moe_block_value(sl.p1[b], moe_block_dot(sl.c1[b], xb, nblk, magic), Sb);
+                    v0 += block_term<FMT>(sl.c0[b], sl.p0[b], xb, nblk, Sb, blk, magic);
+                    if constexpr (GATEUP) v1 += block_term<FMT>(sl.c1[b], sl.p1[b], xb, nblk, Sb, blk, magic);
                 }
             }
             v0 = moe_group_sum<LPR>(v0);
@@ -186,7 +224,7 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
         }
     };
 
-    GemvSlot<BPL, GATEUP> slot[D];
+    GemvSlot<BPL, GATEUP, FMT> slot[D];
     for (int pass = 0; pass < gr.M; pass += mt_cap) {
         const int mcount = min(mt_cap, gr.M - pass);
         // the first D steps' weights are requested before the activations are staged
@@ -198,7 +236,7 @@ void ffn_gemv_kernel(moe::FfnArgs a, int tiles, int mt_cap, int iters) {
             src_rows[threadIdx.x] = GATEUP ? (gr.routed < 0 ? pass + (int)threadIdx.x : row / a.k) : row;
         }
         __syncthreads();
-        stage_rows(GATEUP ? a.x : a.h, K, src_rows, mcount, X, S);
+        stage_rows<FMT == 1>(GATEUP ? a.x : a.h, K, src_rows, mcount, X, S);
         __syncthreads();
         for (int i0 = 0; i0 < nsteps; i0 += D) {
 #pragma unroll
@@ -228,7 +266,7 @@ constexpr int steps_in_flight() {
 #define MOE_GEMV_ITERS 8
 #endif
 
-template <int LPR, int BPL, bool GATEUP>
+template <int LPR, int BPL, bool GATEUP, int FMT>
 int launch_one(const moe::FfnArgs &a, int R, int K, int n_groups, int max_m, hipStream_t s) {
     constexpr int D = steps_in_flight<BPL, GATEUP>();
     constexpr int ROWS_PER_STEP = 4 * (64 / LPR);
@@ -240,34 +278,34 @@ int launch_one(const moe::FfnArgs &a, int R, int K, int n_groups, int max_m, hip
     if (lds_bytes > 64 * 1024) {
         static bool raised = false;
         if (!raised) {
-            hipError_t e = hipFuncSetAttribute((const void *)ffn_gemv_kernel<LPR, BPL, D, GATEUP>,
+            hipError_t e = hipFuncSetAttribute((const void *)ffn_gemv_kernel<LPR, BPL, D, GATEUP, FMT>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
             if (e != hipSuccess) return moe::fail_hip(e, "hipFuncSetAttribute(ffn_gemv_kernel)");
             raised = true;
         }
     }
-    hipLaunchKernelGGL((ffn_gemv_kernel<LPR, BPL, D, GATEUP>), dim3((unsigned)n_groups * tiles), dim3(256), lds_bytes,
+    hipLaunchKernelGGL((ffn_gemv_kernel<LPR, BPL, D, GATEUP, FMT>), dim3((unsigned)n_groups * tiles), dim3(256), lds_bytes,
                        s, a, tiles, mt_cap, iters);
     MOE_LAUNCH_CHECK("ffn_gemv_kernel");
     return MOE_OK;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int FMT>
 int launch_phase(const moe::FfnArgs &a, int n_groups, int max_m, hipStream_t s) {
     const int K = GATEUP ? a.H : a.I;
     const int R = GATEUP ? a.I : a.H;
     const int nblk = K / 32;
 #define MOE_TRY_SHAPE(L, B) \
-    if (nblk == (L) * (B)) return launch_one<L, B, GATEUP>(a, R, K, n_groups, max_m, s);
+    if (nblk == (L) * (B)) return launch_one<L, B, GATEUP, FMT>(a, R, K, n_groups, max_m, s);
     MOE_TRY_SHAPE(64, 1) MOE_TRY_SHAPE(64, 2) MOE_TRY_SHAPE(64, 3) MOE_TRY_SHAPE(64, 4)
     MOE_TRY_SHAPE(16, 1) MOE_TRY_SHAPE(16, 2) MOE_TRY_SHAPE(16, 3) MOE_TRY_SHAPE(16, 4)
     MOE_TRY_SHAPE(8, 1) MOE_TRY_SHAPE(4, 1)
 #undef MOE_TRY_SHAPE
     // other sizes: 64 lanes per row, guarded blocks
-    if (nblk <= 64) return launch_one<64, 1, GATEUP>(a, R, K, n_groups, max_m, s);
-    if (nblk <= 128) return launch_one<64, 2, GATEUP>(a, R, K, n_groups, max_m, s);
-    if (nblk <= 256) return launch_one<64, 4, GATEUP>(a, R, K, n_groups, max_m, s);
-    if (nblk <= 512) return launch_one<64, 8, GATEUP>(a, R, K, n_groups, max_m, s);
+    if (nblk <= 64) return launch_one<64, 1, GATEUP, FMT>(a, R, K, n_groups, max_m, s);
+    if (nblk <= 128) return launch_one<64, 2, GATEUP, FMT>(a, R, K, n_groups, max_m, s);
+    if (nblk <= 256) return launch_one<64, 4, GATEUP, FMT>(a, R, K, n_groups, max_m, s);
+    if (nblk <= 512) return launch_one<64, 8, GATEUP, FMT>(a, R, K, n_groups, max_m, s);
     return moe::fail(MOE_E_SHAPE, "expert_ffn: K=%d too large (max 16384)", K);
 }
 
@@ -275,16 +313,19 @@ int launch_phase(const moe::FfnArgs &a, int n_groups, int max_m, hipStream_t s) 
 
 namespace moe {
 
-int ffn_gemv_gate_up(const FfnArgs &a, int max_m, hipStream_t s) {
+template <bool GATEUP>
+int gemv_phase(const FfnArgs &a, int max_m, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     if (n_groups == 0) return MOE_OK;
-    return launch_phase<true>(a, n_groups, max_m, s);
+    switch (a.fmt) {
+        case 0: return launch_phase<GATEUP, 0>(a, n_groups, max_m, s);
+        case 1: return launch_phase<GATEUP, 1>(a, n_groups, max_m, s);
+        case 2: return launch_phase<GATEUP, 2>(a, n_groups, max_m, s);
+    }
+    return fail(MOE_E_ARG, "grouped GEMV: weight format %d", a.fmt);
 }
 
-int ffn_gemv_down(const FfnArgs &a, int max_m, hipStream_t s) {
-    const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
-    if (n_groups == 0) return MOE_OK;
-    return launch_phase<false>(a, n_groups, max_m, s);
-}
+int ffn_gemv_gate_up(const FfnArgs &a, int max_m, hipStream_t s) { return gemv_phase<true>(a, max_m, s); }
+int ffn_gemv_down(const FfnArgs &a, int max_m, hipStream_t s) { return gemv_phase<false>(a, max_m, s); }
 
 }  // namespace moe

@@ -103,9 +103,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void *lds) {
 // the ring's stages apart); completion is tracked with explicit vmcnt waits
 // instead.  The memory clobber keeps the compiler's own loads in program order
 // around it, which the wait counts rely on.
-// base (uniform, in SGPRs) + off (this lane's 32-bit byte offset)
+// base (uniform, in SGPRs) + off (this lane's 32-bit byte offset).
+// The s_nop gives the 5 wait states a vector memory instruction needs after a
+// VALU instruction wrote an SGPR it reads (and the one after an M0 write): the
+// compiler inserts these for its own instructions but cannot see into inline
+// asm, and under register pressure it restores a spilled base half with
+// v_readlane right before the load -- without the wait the load can use the
+// stale half and go to a wrong address.
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 constexpr int kWaitVm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
@@ -225,6 +231,32 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, float sc, float c_l
     return __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, w45, w67));
 }
 
+// MXFP4: 8 consecutive weights of one row (codes dword, the block's scale
+// 2^(v-127) as a float) -> bf16x8 in column order: gfx950's scaled convert
+// turns byte j of the dword (columns 2j, 2j+1) into two bf16 values, exactly
+// (an E2M1 value times a power of two needs two significant bits).
+__device__ __forceinline__ bf16x8_t dequant8_mx(uint32_t codes, float scale) {
+    const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+    const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+    const uint32_t w45 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+    const uint32_t w67 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+    return __builtin_bit_cast(bf16x8_t, make_uint4(w01, w23, w45, w67));
+}
+
+// E8M0 scale byte -> 2^(v-127) (v = 255: NaN)
+__device__ __forceinline__ float e8m0_scale(uint32_t v) {
+    return v == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)v - 127);
+}
+
+// Super-block header -> block j's scale d*s_j and min -dmin*m_j (exact in fp32).
+__device__ __forceinline__ void sb_block_params(const uint4 hdr, int j, float &sc, float &mn) {
+    const float d = fp16_bits_to_f32(hdr.x & 0xFFFFu), dmin = fp16_bits_to_f32(hdr.x >> 16);
+    const uint64_t fs = (uint64_t)hdr.y | ((uint64_t)(hdr.z & 0xFFFFu) << 32);
+    const uint64_t fm = (uint64_t)(hdr.z >> 16) | ((uint64_t)hdr.w << 16);
+    sc = d * (float)(uint32_t)((fs >> (6 * j)) & 63u);
+    mn = -dmin * (float)(uint32_t)((fm >> (6 * j)) & 63u);
+}
+
 // 16 bytes at base (uniform) + off (this lane's 32-bit byte offset): one load
 // with the base in SGPRs, so a lane keeps only its 32-bit offsets
 __device__ __forceinline__ uint4 load_u4(const uint8_t *base, uint32_t off) {
@@ -240,7 +272,11 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int i) { return i == 0 
 
 // GATEUP: W1 and W3 (tiles 0, 1 of each: the wave's 32 rows), h = bf16(silu(g) * u);
 // otherwise W2 (tiles 0..3: the wave's 64 rows), y = W2 h.
-template <bool GATEUP>
+// FMT: weight format.  The codes are laid out alike in all three; the block
+// parameters of a 4-group step of a row are 64 bytes of (scale, min) records
+// (format 0), 16 E8M0 scale bytes (1: every lane quarter loads the same 16) or
+// two 16-byte super-block headers (2: quarter q loads header q & 1).
+template <bool GATEUP, int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void mfma_ffn_kernel(moe::FfnArgs a,
                                                                                                    int ntiles,
                                                                                                    int n_groups) {
@@ -334,15 +370,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     uint32_t woff[kTM];
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm) {
-        const moe::MatRows m = GATEUP ? (tm < kTM / 2 ? moe::slab_w1(slab, a.H, a.I) : moe::slab_w3(slab, a.H, a.I))
-                                      : moe::slab_w2(slab, a.H, a.I);
+        const moe::MatRows m = GATEUP ? (tm < kTM / 2 ? moe::slab_w1<FMT>(slab, a.H, a.I)
+                                                       : moe::slab_w3<FMT>(slab, a.H, a.I))
+                                      : moe::slab_w2<FMT>(slab, a.H, a.I);
         const int row = active ? (GATEUP ? wrow0 + 16 * (tm % (kTM / 2)) : wrow0 + 16 * tm) + r : r;
         woff[tm] = (uint32_t)(m.row0 - slab) + (uint32_t)row * (uint32_t)m.stride + 16 * q;
     }
+    constexpr int kStepRec = FMT == 0 ? 64 : FMT == 1 ? 16 : 32;  // parameter bytes of a row per step
     auto code_base = [&](int gg) { return slab + 64 * min(gg, ng - 1); };
-    auto rec_base = [&](int hh) { return slab + K / 2 + 64 * min(hh, nh - 1); };
-    auto rec_off = [&](int tm, int hh) {  // lanes whose four blocks lie past the last group
-        return 4 * min(hh, nh - 1) + q < ng ? woff[tm] : woff[tm] - 16 * q;
+    auto rec_base = [&](int hh) { return slab + K / 2 + kStepRec * min(hh, nh - 1); };
+    auto rec_off = [&](int tm, int hh) -> uint32_t {
+        if constexpr (FMT == 0)  // lanes whose four blocks lie past the last group read the step's first
+            return 4 * min(hh, nh - 1) + q < ng ? woff[tm] : woff[tm] - 16 * q;
+        else if constexpr (FMT == 1)
+            return woff[tm] - 16 * q;
+        else  // header 2*hh + (q & 1), or header 2*hh where that is the row's last
+            return 2 * min(hh, nh - 1) + (q & 1) < ng / 2 ? woff[tm] - 16 * q + 16 * (q & 1) : woff[tm] - 16 * q;
     };
 
     __shared__ XStage ring[kStages];
@@ -443,23 +486,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                 // are skipped
                 if (active && gg < ng) {
                     const uint8_t *st = &ring[gg % kStages].x[0];
-                    // each tile's block record: scale and the two extraction offsets
+                    // each tile's block parameters (block 16h + 4b + q of this lane's
+                    // row): scale and the two extraction offsets, or the MXFP4 scale
                     float sc[kTM], clo[kTM], chi[kTM];
 #pragma unroll
                     for (int tm = 0; tm < kTM; ++tm) {
-                        // block 16h + 4b + q of this lane's row: lane (row r, quarter b)'s word q
-                        const uint32_t rec = *reinterpret_cast<const uint32_t *>(rbuf + tm * 1024 + (16 * b + r) * 16 + 4 * q);
-                        sc[tm] = fp16_bits_to_f32(rec & 0xFFFFu);
-                        const float mn = fp16_bits_to_f32(rec >> 16);
-                        clo[tm] = fmaf(-1024.0f, sc[tm], mn);
-                        chi[tm] = fmaf(-64.0f, sc[tm], mn);
+                        const uint8_t *rt = rbuf + tm * 1024;
+                        if constexpr (FMT == 1) {  // byte 4b + q of the row's 16 (quarter 0's copy)
+                            sc[tm] = e8m0_scale(rt[r * 16 + 4 * b + q]);
+                            clo[tm] = chi[tm] = 0.0f;
+                        } else {
+                            float mn;
+                            if constexpr (FMT == 0) {  // lane (row r, quarter b)'s word q
+                                const uint32_t rec = *reinterpret_cast<const uint32_t *>(rt + (16 * b + r) * 16 + 4 * q);
+                                sc[tm] = fp16_bits_to_f32(rec & 0xFFFFu);
+                                mn = fp16_bits_to_f32(rec >> 16);
+                            } else {  // header b / 2 of the step (quarter b / 2's copy), block 4 (b % 2) + q of it
+                                const uint4 hdr = *reinterpret_cast<const uint4 *>(rt + (16 * (b >> 1) + r) * 16);
+                                sb_block_params(hdr, 4 * (b & 1) + q, sc[tm], mn);
+                            }
+                            clo[tm] = fmaf(-1024.0f, sc[tm], mn);
+                            chi[tm] = fmaf(-64.0f, sc[tm], mn);
+                        }
                     }
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         bf16x8_t bo[kTM];
 #pragma unroll
-                        for (int tm = 0; tm < kTM; ++tm)
-                            bo[tm] = dequant8(word(cring[slot][tm], s), sc[tm], clo[tm], chi[tm], dq);
+                        for (int tm = 0; tm < kTM; ++tm) {
+                            if constexpr (FMT == 1)
+                                bo[tm] = dequant8_mx(word(cring[slot][tm], s), sc[tm]);
+                            else
+                                bo[tm] = dequant8(word(cring[slot][tm], s), sc[tm], clo[tm], chi[tm], dq);
+                        }
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) {
                             const int m = 16 * mt + r;
@@ -534,12 +593,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
 namespace moe {
 
-bool mfma_supported(const FfnArgs &a) { return a.grouped && a.H % 128 == 0 && a.I % 128 == 0; }
+bool mfma_supported(const FfnArgs &a) {
+    const int mult = a.fmt == 2 ? 256 : 128;  // super-blocks: whole headers per 4-group step pair
+    return a.grouped && a.H % mult == 0 && a.I % mult == 0 && a.fmt >= 0 && a.fmt <= 2;
+}
 
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-template <bool GATEUP>
+template <bool GATEUP, int FMT>
 int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     const int rows = GATEUP ? a.I : a.H, per = GATEUP ? kRowsGateUp : kRowsDown;
@@ -549,12 +611,22 @@ int launch_mfma(const FfnArgs &a, hipStream_t s) {
         grid = (unsigned)(n_groups * ntiles);
     else
         grid = (unsigned)((n_groups + kXcds - 1) / kXcds * kXcds * ntiles);
-    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP>), dim3(grid), dim3(kThreads), 0, s, a, ntiles, n_groups);
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, FMT>), dim3(grid), dim3(kThreads), 0, s, a, ntiles, n_groups);
     MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
 
-int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return launch_mfma<true>(a, s); }
-int mfma_down(const FfnArgs &a, hipStream_t s) { return launch_mfma<false>(a, s); }
+template <bool GATEUP>
+int mfma_phase(const FfnArgs &a, hipStream_t s) {
+    switch (a.fmt) {
+        case 0: return launch_mfma<GATEUP, 0>(a, s);
+        case 1: return launch_mfma<GATEUP, 1>(a, s);
+        case 2: return launch_mfma<GATEUP, 2>(a, s);
+    }
+    return fail(MOE_E_ARG, "MFMA FFN: weight format %d", a.fmt);
+}
+
+int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return mfma_phase<true>(a, s); }
+int mfma_down(const FfnArgs &a, hipStream_t s) { return mfma_phase<false>(a, s); }
 
 }  // namespace moe

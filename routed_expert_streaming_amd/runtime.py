@@ -141,10 +141,8 @@ class MoEStack:
         torch.cuda.set_device(self.dev)
         self.copy_stream = torch.cuda.Stream(self.dev)  # default priority
         self.copy_stream2 = torch.cuda.Stream(self.dev) if split_copies else None
-        # 0: fp16 scale/min blocks; 1: MXFP4; 2: super-blocks (1 and 2: one-token decode entry points)
+        # 0: fp16 scale/min blocks; 1: MXFP4; 2: super-blocks
         self.fmt = cfg.fmt
-        if self.fmt != 0 and cfg.tokens != 1:
-            raise ValueError("MXFP4 and super-block stacks run the one-token decode entry points only (tokens = 1)")
         self.slab = [L.moe_expert_bytes, L.moe_expert_bytes_mx, L.moe_expert_bytes_sb][self.fmt](self.H, self.I)
         assert self.slab == synth.slab_bytes(self.H, self.I, self.fmt)
         Lyr, T, H, I, E, k = self.L, self.T, self.H, self.I, self.E, self.k
@@ -219,12 +217,15 @@ class MoEStack:
         half = max(1, self.C // 2)
         self.max_waves = (E + half - 1) // half + 1
         self.masks = torch.zeros((Lyr, self.max_waves, E), dtype=torch.uint8, device=self.dev)
-        # gate/up timing of the MFMA path (see ffn); the permutation and h buffers it uses
+        # gate/up timing of the MFMA path (see ffn); the expert grouping (permutation)
+        # and h buffers of the grouped paths (more than 64 (token, slot) pairs), so
+        # that a layer's waves share one permutation
         self.kernel_log = None
+        grouped = T * k > 64 and path in (L.MOE_FFN_AUTO, L.MOE_FFN_GROUPED, L.MOE_FFN_MFMA, L.MOE_FFN_SPLIT)
         self._perm = (torch.empty(E, dtype=torch.int32, device=self.dev),
                       torch.empty(E + 1, dtype=torch.int32, device=self.dev),
-                      torch.empty(T * k, dtype=torch.int32, device=self.dev)) if T >= 128 else None
-        self._h = torch.empty((P, I), dtype=torch.bfloat16, device=self.dev) if T >= 128 else None
+                      torch.empty(T * k, dtype=torch.int32, device=self.dev)) if grouped else None
+        self._h = torch.empty((P, I), dtype=torch.bfloat16, device=self.dev) if grouped else None
         self.pidx = torch.empty((Lyr, T, k), dtype=torch.int32, device=self.dev)  # predicted experts
         self.pw = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
         self._idx_host = PinnedHost(max(Lyr, 2) * T * k * 4) if self.streaming else None
@@ -282,31 +283,38 @@ class MoEStack:
         L.moe_router_topk_layers(x, self.L, self.T, self.H, self.wr, self.bias, self.E, self.k, self.idx, self.w,
                                  self.router_ws, self.router_ws_bytes, self.stream)
 
-    def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True, experts=None):
+    def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True, experts=None, permuted=False):
         """Gate/up + SwiGLU and down projection of layer l's pairs whose expert the
-        mask admits (all when None) into y.  With kernel_log set to a list and many
-        tokens (the MFMA kernels), the same kernels run as three calls -- the
-        permutation, gate/up, down -- with timing events before gate/up, between
-        the two and after down, and (the three events, layer, experts, shared
-        expert included) is appended to the log."""
-        self._format0_only("ffn (masked FFN into y)")
+        mask admits (all when None) into y.  With more than 64 (token, slot) pairs
+        the kernels run in expert grouping as three calls -- the permutation,
+        gate/up, down -- and permuted=True reuses the permutation of the same
+        layer's routing computed by an earlier call (the layer's earlier waves).
+        With kernel_log set to a list and many tokens (the MFMA kernels), timing
+        events go before gate/up, between the two and after down, and (the three
+        events, layer, experts, shared expert included) is appended to the log."""
         sh = self.shared[l] if (self.has_shared and shared) else None
-        if self.kernel_log is None or self.T < 128 or self.path not in (L.MOE_FFN_AUTO, L.MOE_FFN_MFMA):
-            L.moe_expert_ffn(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l], sh, mask,
-                             self.y, self.ffn_ws, self.ffn_ws_bytes, self.path, self.stream)
+        if self._perm is None:
+            L.moe_expert_ffn_fmt(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l], sh, mask,
+                                 self.y, self.ffn_ws, self.ffn_ws_bytes, self.path, self.fmt, self.stream)
             return
         T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
         cnt, off, por = self._perm
-        L.moe_permute(self.idx[l], T, k, E, cnt, off, por, self.stream)
-        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record(self.stream)
-        L.moe_expert_gate_up(x[l], T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask, self._h,
-                             self.path, self.stream)
-        b.record(self.stream)
-        L.moe_expert_down(self._h, T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask, self.y,
-                          self.path, self.stream)
-        c.record(self.stream)
-        self.kernel_log.append((a, b, c, l, list(range(E)) if experts is None else list(experts), sh is not None))
+        if not permuted:
+            L.moe_permute(self.idx[l], T, k, E, cnt, off, por, self.stream)
+        log = self.kernel_log is not None and T >= 128 and self.path in (L.MOE_FFN_AUTO, L.MOE_FFN_MFMA)
+        if log:
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(self.stream)
+        L.moe_expert_gate_up_fmt(x[l], T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask,
+                                 self._h, self.path, self.fmt, self.stream)
+        if log:
+            b.record(self.stream)
+        L.moe_expert_down_fmt(self._h, T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask, self.y,
+                              self.path, self.fmt, self.stream)
+        if log:
+            c.record(self.stream)
+            self.kernel_log.append((a, b, c, l, list(range(E)) if experts is None else list(experts),
+                                    sh is not None))
 
     def ffn_combine(self, x: torch.Tensor, l: int, out: torch.Tensor):
         """Gate/up, down and the weighted combine of layer l (every needed expert resident)."""
@@ -334,25 +342,17 @@ class MoEStack:
     def combine(self, l: int, out: torch.Tensor):
         L.moe_combine(self.y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l], self.stream)
 
-    def _format0_only(self, what: str):
-        # the format-0 kernels read format-0 row sizes: on MXFP4 slabs they would
-        # read past the end of each slab
-        if self.fmt != 0:
-            raise ValueError(f"{what} runs format-0 kernels; this stack holds format-{self.fmt} slabs")
-
     def gate_up_only(self, x: torch.Tensor, l: int, h: torch.Tensor):
         """Only the dequant + gate/up + SwiGLU kernel of layer l (pair grouping), for timing it."""
-        self._format0_only("gate_up_only")
-        L.moe_expert_gate_up(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
-                             self.table[l], self.shared[l] if self.has_shared else None, None, h,
-                             L.MOE_FFN_PAIRS, self.stream)
+        L.moe_expert_gate_up_fmt(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
+                                 self.table[l], self.shared[l] if self.has_shared else None, None, h,
+                                 L.MOE_FFN_PAIRS, self.fmt, self.stream)
 
     def down_only(self, h: torch.Tensor, l: int):
         """Only the dequant + down-projection kernel of layer l (pair grouping), for timing it."""
-        self._format0_only("down_only")
-        L.moe_expert_down(h, self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
-                          self.table[l], self.shared[l] if self.has_shared else None, None, self.y,
-                          L.MOE_FFN_PAIRS, self.stream)
+        L.moe_expert_down_fmt(h, self.T, self.H, self.I, self.E, self.idx[l], self.k, None, None, None,
+                              self.table[l], self.shared[l] if self.has_shared else None, None, self.y,
+                              L.MOE_FFN_PAIRS, self.fmt, self.stream)
 
     def plan_waves(self, l: int, ids, masks=None):
         """The library's step plan of layer l (moe_cache_plan): its top-k ids split
@@ -510,7 +510,7 @@ class MoEStack:
                 continue
             for wv, experts in enumerate(waves):
                 st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
-                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts)
+                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts, permuted=wv > 0)
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
             self.combine(l, out)
@@ -539,7 +539,7 @@ class MoEStack:
             for wv in range(int(nw[l])):
                 experts = ne[l, starts[l, wv]:starts[l, wv + 1]]
                 st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
-                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts)
+                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts, permuted=wv > 0)
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
             self.combine(l, out)

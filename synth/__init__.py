@@ -143,6 +143,13 @@ CONFIGS = {
                                 "decode batch 1 with super-block expert weights, cache cap 25% per layer, Zipf(1.1) "
                                 "router bias, streamed misses", 2),
 }
+# the 32-token decode and 2048-token prefill configurations with the other weight formats
+for _fmt, _tag, _what in ((1, "mx", "MXFP4"), (2, "sb", "super-block")):
+    for _base, _seed in (("decode32_stream", 20261214), ("prefill2048_stream", 20261216)):
+        _c = CONFIGS[_base]
+        _name = _base.replace("_stream", f"_{_tag}_stream")
+        CONFIGS[_name] = replace(_c, name=_name, seed=_seed + _fmt - 1, fmt=_fmt,
+                                 description=f"{_c.description}; {_what} expert weights")
 ORDER = ["tiny", "decode1", "decode1_stream", "decode32_stream", "prefill2048_stream"]
 
 

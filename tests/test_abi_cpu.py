@@ -332,7 +332,7 @@ def test_split_copies_validation_and_state():
 
 
 def test_mx_sizes_and_validation():
-    """MXFP4 slab sizes, and the one-token entry points' checks (no kernel runs)."""
+    """MXFP4 slab sizes, and the format entry points' checks (no kernel runs)."""
     assert L.moe_expert_bytes_mx(4096, 1536) == 3 * 4096 * 1536 * 17 // 32
     assert L.moe_expert_bytes_mx(96, 64) == 2 * 64 * 64 + 96 * 48  # rows of 51 -> 64 and 34 -> 48 bytes
     assert L.moe_expert_bytes_mx(100, 64) == 0
@@ -342,18 +342,28 @@ def test_mx_sizes_and_validation():
     w = np.zeros((2, 8), np.float32)
     out = np.zeros((2, 4096), np.uint16)
     table = np.zeros(128, np.int64)
-    # T = 0: no-op; T = 2: MXFP4 slabs need one token
+    # T = 0: no-op
     L.moe_mx_expert_ffn_combine(x, 0, 4096, 1536, 128, idx, w, 8, table, None, out, ws, ws.size)
-    with pytest.raises(L.MoEError) as e:
-        L.moe_mx_expert_ffn_combine(x, 2, 4096, 1536, 128, idx, w, 8, table, None, out, ws, ws.size)
+    with pytest.raises(L.MoEError) as e:  # I not a multiple of 32
+        L.moe_mx_expert_ffn_combine(x, 2, 4096, 1000, 128, idx, w, 8, table, None, out, ws, ws.size)
     assert e.value.status == L.MOE_E_SHAPE
-    with pytest.raises(L.MoEError) as e:  # I = 1024 has no MXFP4 down kernel
-        L.moe_mx_expert_ffn_combine(x, 1, 4096, 1024, 128, idx, w, 8, table, None, out, ws, ws.size)
-    assert e.value.status == L.MOE_E_SHAPE
+    with pytest.raises(L.MoEError) as e:  # several tokens: the grouped paths' workspace is checked first
+        L.moe_mx_expert_ffn_combine(x, 2, 4096, 1536, 128, idx, w, 8, table, None, out, ws, 1024)
+    assert e.value.status == L.MOE_E_NOMEM
     wr = np.zeros((128, 4096), np.float32)
     with pytest.raises(L.MoEError) as e:
-        L.moe_mx_route_ffn_combine(x, 2, 4096, 1536, wr, None, 128, 8, table, None, idx, w, out, ws, ws.size)
-    assert e.value.status == L.MOE_E_SHAPE
+        L.moe_mx_route_ffn_combine(x, 2, 4096, 1536, wr, None, 128, 8, table, None, idx, w, out, ws, 1024)
+    assert e.value.status == L.MOE_E_NOMEM
+    y = np.zeros((16, 4096), np.float32)
+    for fmt in (-1, 3):  # formats 0, 1, 2 only
+        with pytest.raises(L.MoEError) as e:
+            L.moe_expert_ffn_fmt(x, 2, 4096, 1536, 128, idx, 8, table, None, None, y, ws, ws.size, L.MOE_FFN_AUTO,
+                                 fmt)
+        assert e.value.status == L.MOE_E_ARG
+        with pytest.raises(L.MoEError) as e:
+            L.moe_expert_gate_up_fmt(x, 2, 4096, 1536, 128, idx, 8, None, None, None, table, None, None, y,
+                                     L.MOE_FFN_PAIRS, fmt)
+        assert e.value.status == L.MOE_E_ARG
     d = L.moe_cache_desc(1, 4, 64, 32, 2, 3)
     with pytest.raises(L.MoEError) as e:
         L.moe_cache_create_recording(d)
@@ -369,10 +379,15 @@ def test_superblock_sizes_and_validation():
     w = np.zeros((2, 8), np.float32)
     out = np.zeros((2, 4096), np.uint16)
     table = np.zeros(128, np.int64)
-    for T, H, I in ((2, 4096, 1536), (1, 4096, 1024 + 32)):
+    for T, H, I in ((2, 4096, 1504), (1, 4096, 1024 + 32), (2, 4000, 1536)):  # H, I multiples of 256 only
         with pytest.raises(L.MoEError) as e:
             L.moe_sb_expert_ffn_combine(x, T, H, I, 128, idx, w, 8, table, None, out, ws, ws.size)
         assert e.value.status == L.MOE_E_SHAPE, (T, H, I)
+    y = np.zeros((16, 4096), np.float32)
+    with pytest.raises(L.MoEError) as e:
+        L.moe_expert_down_fmt(x, 2, 4096, 1504, 128, idx, 8, None, None, None, table, None, None, y,
+                              L.MOE_FFN_PAIRS, 2)
+    assert e.value.status == L.MOE_E_SHAPE
     with pytest.raises(L.MoEError) as e:
         L.moe_cache_create_recording(L.moe_cache_desc(1, 4, 64, 32, 2, 2))
     assert e.value.status == L.MOE_E_SHAPE

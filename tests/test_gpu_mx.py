@@ -1,5 +1,6 @@
 """GPU parity of the MXFP4 (format 1) and super-block (format 2) weight formats
-(one-token decode) against the oracle.
+(one-token decode: the fused one-token kernels, and the separate gate/up and
+down calls) against the oracle.
 
 Bars: expert indices bit-exact; outputs within 2e-2 * max|ref| of the fp64
 oracle reading the same MXFP4 slabs; the one-call layer bit-identical to the
@@ -62,9 +63,17 @@ def test_format_layers_match_oracle_and_split_calls(name, over):
             assert (st.idx.cpu().numpy() == idx1).all()
             assert (bits(out2) == ob).all()
             xb = bits(x)
-            # the format-0 calls refuse these slabs (their row sizes differ)
-            with pytest.raises(ValueError):
-                st.gate_up_only(x, 0, torch.empty((1, cfg.inter), dtype=torch.bfloat16, device="cuda"))
+            # the separate gate/up and down calls on these slabs (the dequant-GEMV
+            # in pair grouping), then the combine: checked against the oracle too
+            out3 = st.new_output()
+            h = torch.empty((st.T * st.k + (st.T if st.has_shared else 0), cfg.inter), dtype=torch.bfloat16,
+                            device="cuda")
+            for l in range(layers):
+                st.gate_up_only(x, l, h)
+                st.down_only(h, l)
+                st.combine(l, out3)
+            torch.cuda.synchronize()
+            o3 = bits(out3)
             for l in range(layers):
                 wr = st.wr[l].cpu().numpy()
                 bias = None if st.bias is None else st.bias[l].cpu().numpy()
@@ -72,7 +81,8 @@ def test_format_layers_match_oracle_and_split_calls(name, over):
                                      fmt=cfg.fmt)
                 assert (o["idx"] == idx1[l]).all()
                 ratio = check_close(ob[l], o["out64"], f"{name} {over} step {s} layer {l}")
-                print(f"{name} {over} step {s} layer {l}: max err / max|ref| = {ratio:.2e}")
+                ratio3 = check_close(o3[l], o["out64"], f"{name} {over} step {s} layer {l} (two calls)")
+                print(f"{name} {over} step {s} layer {l}: max err / max|ref| = {ratio:.2e} (two calls {ratio3:.2e})")
     finally:
         st.close()
 
