@@ -454,6 +454,10 @@ def layer_leg(torch, name: str, path: int, iters: int):
                                                                st.table[0], shared, None, h, path, st.fmt))
     res["down_ms"] = timed(lambda: L.moe_expert_down_fmt(h, T, H, I, E, st.idx[0], k, cnt, off, por, st.table[0],
                                                          shared, None, st.y, path, st.fmt))
+    # the FFN as one call (permutation included); for MXFP4 on the MFMA path this
+    # is the block-scaled matrix-core route (activation digit pairs, no dequant)
+    res["ffn_call_ms"] = timed(lambda: L.moe_expert_ffn_fmt(x[0], T, H, I, E, st.idx[0], k, st.table[0], shared,
+                                                            None, st.y, st.ffn_ws, st.ffn_ws_bytes, path, st.fmt))
     res["combine_ms"] = timed(lambda: st.combine(0, out))
     res["layer_ms"] = timed(lambda: (st.route(x, 0), st.ffn_combine(x, 0, out)))
     idx = st.idx[0].cpu().numpy()
@@ -461,6 +465,9 @@ def layer_leg(torch, name: str, path: int, iters: int):
     w_bytes = n_exp * st.slab
     flops = 2 * 3 * H * I * P
     ffn_ms = res["gate_up_ms"] + res["down_ms"]
+    if st.fmt == 1 and path == L.MOE_FFN_MFMA:
+        ffn_ms = res["ffn_call_ms"]  # the separate calls dequantise to bf16; the one call is the scaled route
+        res["scaled_matrix_cores"] = True
     res.update({"experts_used": n_exp, "weight_bytes": w_bytes, "ffn_flops": flops,
                 "ffn_weights_GBps": round(w_bytes / (ffn_ms * 1e-3) / 1e9, 1),
                 "ffn_TFLOPs": round(flops / (ffn_ms * 1e-3) / 1e12, 2),

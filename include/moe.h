@@ -331,6 +331,31 @@ int moe_expert_down_fmt(const uint16_t *h, int T, int H, int I, int E, const int
                         const void *const *expert_table, const void *shared_slab, const uint8_t *expert_mask,
                         float *y, int path, int format, void *stream);
 
+/* MXFP4 on gfx950's block-scaled FP4 matrix cores (the MXFP4 decode paths the
+ * pages name, LayerStoRm README, "License and attributions", with the OCP MX
+ * v1.0 block scaling the hardware applies): on the MFMA path (automatic for T >=
+ * 128 with H, I multiples of 128, or MOE_FFN_MFMA) moe_expert_ffn_fmt with
+ * format 1 -- and so moe_mx_expert_ffn_combine / moe_mx_route_ffn_combine -- run
+ * v_mfma_scale_f32_16x16x128_f8f6f4 with the slab's codes as its FP4 operand and
+ * their E8M0 bytes as its scales, and no dequantisation.  Its other operand
+ * takes FP8 (E4M3) values, so each bf16 activation row is first written as two
+ * E4M3 digits per element, hi + lo, under one E8M0 scale 2^u per row:
+ *   u = e - 8 for the row's largest magnitude f * 2^e (f in [0.5, 1));
+ *   hi = x / 2^u truncated to E4M3 (3 mantissa bits; multiples of 2^-9 below
+ *        2^-6), lo = x / 2^u - hi rounded to nearest-even E4M3;
+ * hi + lo = x / 2^u exactly for every |x| >= 2^(u-2), i.e. within 2^10 of the
+ * row's largest element (smaller ones are off by at most 2^(u-10)), so the
+ * products equal those of the bf16 activations up to fp32 summation order.
+ * moe_quant_act_mx does this conversion: x [rows, K] bf16 -> out [rows, 2K]
+ * bytes, per 128-column group 128 hi then 128 lo bytes, each as four 32-byte
+ * chunks q holding columns 16q..16q+15 then 64+16q..64+16q+15 (the operand
+ * layout of lane quarter q); scales [rows] int32 = u + 127 (the E8M0 byte).
+ * out may equal x (in place).  Device pointers; MOE_E_SHAPE unless K is a
+ * multiple of 128 up to 16384, MOE_E_ARG for rows < 0 or NULL (rows = 0: no-op).
+ * The FFN calls keep the digit pairs in their workspace (x's in the y area, h's
+ * in place of h). */
+int moe_quant_act_mx(const uint16_t *x, int rows, int K, uint8_t *out, int32_t *scales, void *stream);
+
 /* ------------------------------------------------------------------ combine
  * Weighted combine of a token's expert outputs (LayerStoRm README, "TL;DR": the
  * selected experts' outputs are combined into the layer output; "Serve" notes: a

@@ -81,6 +81,7 @@ def lib():
             "moe_expert_ffn_fmt": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, sz, i, i, vp], i),
             "moe_expert_gate_up_fmt": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp], i),
             "moe_expert_down_fmt": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, vp], i),
+            "moe_quant_act_mx": ([vp, i, i, vp, vp, vp], i),
             "moe_expert_down": ([vp, i, i, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, vp], i),
             "moe_expert_ffn_combine": ([vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, i, vp], i),
             "moe_route_ffn_combine_workspace_bytes": ([i, i, i, i, i, i], sz),
@@ -383,6 +384,10 @@ def moe_expert_down_fmt(h, T, H, I, E, topk_idx, k, count, offset, pair_of_row, 
     _check(lib().moe_expert_down_fmt(_ptr(h), T, H, I, E, _ptr(topk_idx), k, _ptr(count), _ptr(offset),
                                      _ptr(pair_of_row), _ptr(expert_table), _ptr(shared_slab), _ptr(expert_mask),
                                      _ptr(y), path, format, _stream(stream)), "moe_expert_down_fmt")
+
+
+def moe_quant_act_mx(x, rows, K, out, scales, stream=None):
+    _check(lib().moe_quant_act_mx(_ptr(x), rows, K, _ptr(out), _ptr(scales), _stream(stream)), "moe_quant_act_mx")
 
 
 def moe_expert_ffn_combine(x, T, H, I, E, topk_idx, topk_w, k, expert_table, shared_slab, out, workspace,

@@ -25,6 +25,8 @@ struct FfnArgs {
     int compact;                // MFMA kernel: workgroups take the active groups in rank order (see the kernel)
     const uint8_t *prefetch;    // or nullptr: bytes the one-token down kernel reads into the device caches
     size_t prefetch_bytes;      // for the caller's next call (read and discarded, 1 KB per wave)
+    const int32_t *act_scale;   // scaled MXFP4 MFMA kernels: E8M0 scale of each activation row (x or h),
+                                // whose elements are then FP8 digit pairs (moe_quant_act_mx), not bf16
 };
 
 // Router finish fused into the one-token gate/up kernel: the per-slice fp64
@@ -59,6 +61,13 @@ int decode1_routed_gate_up(const FfnArgs &a, const RouteArgs &ra, hipStream_t s)
 bool mfma_supported(const FfnArgs &a);
 int mfma_gate_up(const FfnArgs &a, hipStream_t s);
 int mfma_down(const FfnArgs &a, hipStream_t s);
+// MXFP4 on the block-scaled FP4 matrix cores: a.x (gate/up) or a.h (down) hold
+// FP8 digit pairs from quant_act with their row scales in a.act_scale.
+int mfma_gate_up_scaled(const FfnArgs &a, hipStream_t s);
+int mfma_down_scaled(const FfnArgs &a, hipStream_t s);
+// bf16 rows -> FP8 digit pairs (hi, lo) in the scaled kernels' A-operand order
+// plus one E8M0 scale per row (in place allowed: out may equal x).
+int quant_act(const uint16_t *x, int rows, int K, uint8_t *out, int32_t *scale, hipStream_t s);
 
 // (token, slot) pairs the one-token down kernel combines (routed slots + shared).
 constexpr int kDown1MaxPairs = 16;

@@ -156,7 +156,7 @@ extern "C" int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t
 namespace {
 
 struct FfnLayout {
-    size_t h, count, offset, pairs, y, slabs, total;
+    size_t h, count, offset, pairs, y, slabs, scale, total;
 };
 
 FfnLayout ffn_layout(int T, int H, int I, int E, int k, int has_shared) {
@@ -175,6 +175,8 @@ FfnLayout ffn_layout(int T, int H, int I, int E, int k, int has_shared) {
     o += moe::align_up(P * H * sizeof(float), 256);
     L.slabs = o;
     o += moe::align_up(P * sizeof(void *), 256);
+    L.scale = o;  // MXFP4 on the scaled matrix cores: the E8M0 scales of x's T rows and h's P rows
+    o += moe::align_up(((size_t)T + P) * sizeof(int32_t), 256);
     L.total = o;
     return L;
 }
@@ -400,6 +402,31 @@ int ffn_impl(const uint16_t *x, int T, int H, int I, int E, const int32_t *topk_
         pairs = (int32_t *)(ws + Ly.pairs);
         rc = moe::permute_launch(topk_idx, T, k, E, count, offset, pairs, s);
         if (rc != MOE_OK) return rc;
+    }
+    if (fmt == 1 && path == MOE_FFN_MFMA && H % 128 == 0 && I % 128 == 0) {
+        // MXFP4 on the block-scaled FP4 matrix cores: x's rows as FP8 digit pairs
+        // in the y area (y is written only by the down projection, after the
+        // gate/up products are done with them), then h's rows in place
+        const int P = T * k + (shared_slab ? T : 0);
+        uint8_t *xq = (uint8_t *)(ws + Ly.y);
+        int32_t *xs = (int32_t *)(ws + Ly.scale), *hs = xs + T;
+        rc = moe::quant_act(x, T, H, xq, xs, s);
+        if (rc != MOE_OK) return rc;
+        moe::FfnArgs a;
+        int max_m = 1;
+        rc = make_args(a, (const uint16_t *)xq, h, nullptr, T, H, I, E, topk_idx, k, count, offset, pairs,
+                       expert_table, shared_slab, expert_mask, MOE_FFN_MFMA, &max_m, "expert_ffn", fmt);
+        if (rc != MOE_OK) return rc;
+        a.act_scale = xs;
+        rc = moe::mfma_gate_up_scaled(a, s);
+        if (rc != MOE_OK) return rc;
+        rc = moe::quant_act(h, P, I, (uint8_t *)h, hs, s);
+        if (rc != MOE_OK) return rc;
+        rc = make_args(a, nullptr, h, y, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab,
+                       expert_mask, MOE_FFN_MFMA, &max_m, "expert_ffn", fmt);
+        if (rc != MOE_OK) return rc;
+        a.act_scale = hs;
+        return moe::mfma_down_scaled(a, s);
     }
     rc = gate_up_impl(x, T, H, I, E, topk_idx, k, count, offset, pairs, expert_table, shared_slab, expert_mask, h, path,
                       fork, stream, fmt);
@@ -683,6 +710,13 @@ extern "C" int moe_sb_route_ffn_combine(const uint16_t *x, int T, int H, int I, 
     return fmt_route_ffn_combine(2, "sb_route_ffn_combine", x, T, H, I, w_router, bias, E, k, expert_table,
                                  shared_slab, topk_idx, topk_w, out, workspace, workspace_bytes, prefetch,
                                  prefetch_bytes, stream);
+}
+
+extern "C" int moe_quant_act_mx(const uint16_t *x, int rows, int K, uint8_t *out, int32_t *scales, void *stream) {
+    if (rows < 0) return moe::fail(MOE_E_ARG, "quant_act_mx: rows=%d < 0", rows);
+    if (rows == 0) return MOE_OK;
+    if (!x || !out || !scales) return moe::fail(MOE_E_ARG, "quant_act_mx: NULL pointer");
+    return moe::quant_act(x, rows, K, out, scales, (hipStream_t)stream);
 }
 
 extern "C" int moe_combine(const float *y, const float *topk_w, int T, int k, int H, int has_shared, uint16_t *out,

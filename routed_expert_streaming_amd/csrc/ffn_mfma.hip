@@ -57,6 +57,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 #ifndef MOE_MFMA_SCHED_BARRIER
 #define MOE_MFMA_SCHED_BARRIER 0
@@ -276,10 +277,18 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int i) { return i == 0 
 // parameters of a 4-group step of a row are 64 bytes of (scale, min) records
 // (format 0), 16 E8M0 scale bytes (1: every lane quarter loads the same 16) or
 // two 16-byte super-block headers (2: quarter q loads header q & 1).
-template <bool GATEUP, int FMT>
+// SCALED (MXFP4 only): the products run on v_mfma_scale_f32_16x16x128_f8f6f4
+// with the codes as its FP4 B operand (lane quarter q's 16 code bytes are block
+// q of the 128-column group, K = 32q..32q+31: exactly the ring's loads) and the
+// block's E8M0 byte as B's scale; the activations are FP8 digit pairs (hi, lo)
+// with one E8M0 scale per row (quant_act below), hi and lo each the A operand
+// of one product (A lane quarter q: columns 16q..16q+15 and 64+16q..64+16q+15,
+// the order quant_act writes).  No dequantisation.
+template <bool GATEUP, int FMT, bool SCALED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void mfma_ffn_kernel(moe::FfnArgs a,
                                                                                                    int ntiles,
                                                                                                    int n_groups) {
+    static_assert(!SCALED || FMT == 1, "the block-scaled products take MXFP4 weights");
     const int K = GATEUP ? a.H : a.I;        // reduction length (a multiple of 128)
     const int nrows = GATEUP ? a.I : a.H;    // weight rows (output columns)
     const int wg_rows = GATEUP ? kRowsGateUp : kRowsDown;
@@ -393,8 +402,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(16))) uint8_t rring[2][kWaves][kTM][1024];
     __shared__ int s_src[kMC];  // activation row of each M row
     __shared__ int s_dst[kMC];  // output row of each M row (-1 = padding)
+    __shared__ int s_asc[kMC];  // SCALED: E8M0 scale of each M row's activation row
     const uint32_t ring_lds = lds_addr(&ring[0]);
-    const Dequant dq = dequant_consts();
+    const Dequant dq = SCALED ? Dequant{} : dequant_consts();
 
     for (int m0 = 0; m0 < M; m0 += kMC) {
         const int mc = min(kMC, M - m0);
@@ -412,6 +422,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                 src = GATEUP ? m : dst;
             }
             s_src[tid] = src;
+            if constexpr (SCALED) s_asc[tid] = a.act_scale[src];
             s_dst[tid] = tid < mc ? dst : -1;
         }
         __syncthreads();
@@ -484,7 +495,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                 // last group they re-read it), so that the compiler's own load
                 // counts never meet a path that skipped them; only the products
                 // are skipped
-                if (active && gg < ng) {
+                if (SCALED && active && gg < ng) {
+                    // B: the group's codes as loaded; its scale the block's E8M0 byte
+                    // (byte 4b + q of the row's 16, quarter 0's copy)
+                    const uint8_t *st = &ring[gg % kStages].x[0];
+                    i32x8_t bv[kTM];
+                    int bsc[kTM];
+#pragma unroll
+                    for (int tm = 0; tm < kTM; ++tm) {
+                        const uint4 c = cring[slot][tm];
+                        bv[tm] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+                        bsc[tm] = rbuf[tm * 1024 + r * 16 + 4 * b + q];
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        // A: row m's hi digits in units 2q, 2q+1 and lo digits in units
+                        // 8+2q, 9+2q of its 16 (stored at unit ^ (m % 16), m % 16 = r)
+                        const int m = 16 * mt + r;
+                        const uint8_t *row = st + m * kXRow;
+                        const uint4 h0 = *reinterpret_cast<const uint4 *>(row + 16 * ((2 * q) ^ r));
+                        const uint4 h1 = *reinterpret_cast<const uint4 *>(row + 16 * ((2 * q + 1) ^ r));
+                        const uint4 l0 = *reinterpret_cast<const uint4 *>(row + 16 * ((8 + 2 * q) ^ r));
+                        const uint4 l1 = *reinterpret_cast<const uint4 *>(row + 16 * ((9 + 2 * q) ^ r));
+                        const i32x8_t ahi{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w,
+                                          (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+                        const i32x8_t alo{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w,
+                                          (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+                        const int asc = s_asc[m];
+#pragma unroll
+                        for (int tm = 0; tm < kTM; ++tm) {
+                            // cbsz 0: A is FP8 E4M3; blgp 4: B is FP4 E2M1
+                            acc[tm][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                ahi, bv[tm], acc[tm][mt], 0, 4, 0, asc, 0, bsc[tm]);
+                            acc[tm][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                alo, bv[tm], acc[tm][mt], 0, 4, 0, asc, 0, bsc[tm]);
+                        }
+                    }
+                }
+                if (!SCALED && active && gg < ng) {
                     const uint8_t *st = &ring[gg % kStages].x[0];
                     // each tile's block parameters (block 16h + 4b + q of this lane's
                     // row): scale and the two extraction offsets, or the MXFP4 scale
@@ -589,6 +637,85 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
 }
 
+// ---------------------------------------------------------------- activations for the scaled products
+// A bf16 row x becomes FP8 (E4M3) digit pairs with one E8M0 scale 2^u per row:
+// u = e - 8 for the row's largest magnitude f * 2^e (f in [0.5, 1)), so every
+// |x| / 2^u < 256; hi = x / 2^u truncated to E4M3 (3 mantissa bits; below 2^-6,
+// E4M3's subnormals, to a multiple of 2^-9) and lo = x / 2^u - hi (exact in
+// fp32) rounded to nearest even E4M3.  hi + lo equals x / 2^u whenever |x| >=
+// 2^u / 4 (then lo's last bit is at or above E4M3's 2^-9): every element within
+// 2^10 of the row's largest; smaller ones are off by at most 2^u * 2^-10.
+// Output row, 2 bytes per element like the input: per 128-column group, 128 hi
+// bytes then 128 lo bytes, each as four 32-byte chunks q holding columns
+// 16q..16q+15 then 64+16q..64+16q+15 (the A operand of lane quarter q).
+constexpr int kQuantThreads = 256;
+
+// E4M3 byte of a value that E4M3 holds exactly (|v| < 256)
+__device__ __forceinline__ uint32_t e4m3_exact(float v) {
+    const uint32_t b = __float_as_uint(v), sign = (b >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a < 0.015625f) return sign | (uint32_t)(a * 512.0f);  // subnormal (or zero): m * 2^-9
+    const uint32_t e = ((b >> 23) & 0xFFu) - 127u + 7u, m = (b >> 20) & 7u;
+    return sign | (e << 3) | m;
+}
+
+// E4M3 byte of v rounded to nearest, ties to even (|v| < 16 here)
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+    const uint32_t b = __float_as_uint(v), sign = (b >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // 8 (rounded up) is the encoding of 2^-6
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t rb = ab + 0x7FFFFu + ((ab >> 20) & 1u);  // round the mantissa to 3 bits
+    const uint32_t e = ((rb >> 23) & 0xFFu) - 127u + 7u, m = (rb >> 20) & 7u;
+    return sign | (e << 3) | m;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const uint16_t *x, int K, uint8_t *out,
+                                                                  int32_t *scale) {
+    extern __shared__ uint4 srow4[];  // the row, K bf16
+    __shared__ float wmax[kQuantThreads / 64];
+    const uint16_t *srow = reinterpret_cast<const uint16_t *>(srow4);
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)row * K);
+    float mx = 0.0f;
+    for (int i = tid; i < K / 8; i += kQuantThreads) {
+        const uint4 v = xr[i];
+        srow4[i] = v;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            mx = fmaxf(mx, fmaxf(fabsf(bf16_bits_to_f32(w[j] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[j] >> 16))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+    __syncthreads();  // also: the whole row is read before anything is written (out may alias x)
+#pragma unroll
+    for (int w = 0; w < kQuantThreads / 64; ++w) mx = fmaxf(mx, wmax[w]);
+    int e = 0;
+    (void)frexpf(mx, &e);
+    const int u = mx > 0.0f ? max(-127, min(127, e - 8)) : -127;
+    if (tid == 0) scale[row] = u + 127;
+    uint32_t *orow = reinterpret_cast<uint32_t *>(out + (size_t)row * K * 2);
+    for (int d = tid; d < K / 4; d += kQuantThreads) {  // hi dword d: group d/32, chunk (d%32)/8, bytes 4(d%8)..
+        const int g = d >> 5, dd = d & 31, q = dd >> 3, j0 = 4 * (dd & 7);
+        const int c0 = 128 * g + (j0 < 16 ? 16 * q + j0 : 64 + 16 * q + j0 - 16);
+        uint32_t hi = 0, lo = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float y = ldexpf(bf16_bits_to_f32(srow[c0 + j]), -u);
+            const float ay = fabsf(y);
+            float h = ay < 0.015625f ? truncf(ay * 512.0f) * 0.001953125f
+                                     : __uint_as_float(__float_as_uint(ay) & 0xFFF00000u);
+            h = copysignf(h, y);
+            hi |= e4m3_exact(h) << (8 * j);
+            lo |= e4m3_rne(y - h) << (8 * j);
+        }
+        orow[64 * g + dd] = hi;
+        orow[64 * g + 32 + dd] = lo;
+    }
+}
+
 }  // namespace
 
 namespace moe {
@@ -601,7 +728,7 @@ bool mfma_supported(const FfnArgs &a) {
 // Grid: kXcds workgroups per "expert slot" position, so that workgroup b runs on
 // XCD b % kXcds and holds tile (b / kXcds) % ntiles of expert
 // ((b / kXcds) / ntiles) * kXcds + b % kXcds (padding experts return at once).
-template <bool GATEUP, int FMT>
+template <bool GATEUP, int FMT, bool SCALED = false>
 int launch_mfma(const FfnArgs &a, hipStream_t s) {
     const int n_groups = a.n_routed_groups + (a.shared ? 1 : 0);
     const int rows = GATEUP ? a.I : a.H, per = GATEUP ? kRowsGateUp : kRowsDown;
@@ -611,7 +738,7 @@ int launch_mfma(const FfnArgs &a, hipStream_t s) {
         grid = (unsigned)(n_groups * ntiles);
     else
         grid = (unsigned)((n_groups + kXcds - 1) / kXcds * kXcds * ntiles);
-    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, FMT>), dim3(grid), dim3(kThreads), 0, s, a, ntiles, n_groups);
+    hipLaunchKernelGGL((mfma_ffn_kernel<GATEUP, FMT, SCALED>), dim3(grid), dim3(kThreads), 0, s, a, ntiles, n_groups);
     MOE_LAUNCH_CHECK(GATEUP ? "mfma_ffn_kernel<gate_up>" : "mfma_ffn_kernel<down>");
     return MOE_OK;
 }
@@ -628,5 +755,30 @@ int mfma_phase(const FfnArgs &a, hipStream_t s) {
 
 int mfma_gate_up(const FfnArgs &a, hipStream_t s) { return mfma_phase<true>(a, s); }
 int mfma_down(const FfnArgs &a, hipStream_t s) { return mfma_phase<false>(a, s); }
+
+int mfma_gate_up_scaled(const FfnArgs &a, hipStream_t s) {
+    if (a.fmt != 1 || !a.act_scale) return fail(MOE_E_ARG, "scaled MFMA gate/up: MXFP4 slabs and row scales needed");
+    return launch_mfma<true, 1, true>(a, s);
+}
+int mfma_down_scaled(const FfnArgs &a, hipStream_t s) {
+    if (a.fmt != 1 || !a.act_scale) return fail(MOE_E_ARG, "scaled MFMA down: MXFP4 slabs and row scales needed");
+    return launch_mfma<false, 1, true>(a, s);
+}
+
+int quant_act(const uint16_t *x, int rows, int K, uint8_t *out, int32_t *scale, hipStream_t s) {
+    if (rows <= 0) return MOE_OK;
+    if (K <= 0 || K % 128 || K > 16384) return fail(MOE_E_SHAPE, "quant_act: K=%d (a multiple of 128, at most 16384)", K);
+    const size_t lds = (size_t)K * 2;
+    static bool raised = false;
+    if (!raised) {
+        hipError_t e = hipFuncSetAttribute((const void *)quant_act_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           16384 * 2);
+        if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(quant_act_kernel)");
+        raised = true;
+    }
+    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)rows), dim3(kQuantThreads), lds, s, x, K, out, scale);
+    MOE_LAUNCH_CHECK("quant_act_kernel");
+    return MOE_OK;
+}
 
 }  // namespace moe

@@ -293,7 +293,10 @@ class MoEStack:
         events go before gate/up, between the two and after down, and (the three
         events, layer, experts, shared expert included) is appended to the log."""
         sh = self.shared[l] if (self.has_shared and shared) else None
-        if self._perm is None:
+        # MXFP4 prefill runs on the block-scaled matrix cores, whose activation
+        # digit pairs live in the one-call FFN's workspace
+        scaled = self.fmt == 1 and self.T >= 128 and self.path in (L.MOE_FFN_AUTO, L.MOE_FFN_MFMA)
+        if self._perm is None or scaled:
             L.moe_expert_ffn_fmt(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l], sh, mask,
                                  self.y, self.ffn_ws, self.ffn_ws_bytes, self.path, self.fmt, self.stream)
             return
