@@ -41,7 +41,7 @@ METRIC = "routed-MoE layer tokens/s at 1 GPU; achieved HBM GB/s and PCIe H2D GB/
 # the one-token gate/up kernel as launched alone (units per lane, ring depth, no routing)
 GATE_UP_KERNEL = "decode1_gate_up_kernel<2, 1, 0, 0>"
 # the prefill gate/up kernel (matrix cores; W1/W3 rows, SwiGLU epilogue), by weight format
-MFMA_GATE_UP_KERNEL = "mfma_ffn_kernel<true, {fmt}>"
+MFMA_GATE_UP_KERNEL = "mfma_ffn_kernel<true, {fmt}, false>"
 
 
 def log(msg):
