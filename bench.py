@@ -56,7 +56,10 @@ def parse():
     ap.add_argument("--workload", default="prefill2048_stream",
                     help="streamed headline configuration (prefill2048_stream, decode32_stream, decode1_stream)")
     ap.add_argument("--layers", type=int, default=0, help="layers of the headline stack (0 = the configuration's)")
-    ap.add_argument("--inputs", type=int, default=4, help="distinct resident input steps cycled through")
+    ap.add_argument("--inputs", type=int, default=0,
+                    help="distinct resident input steps cycled through (0: 4 when a step has at least 128 tokens, "
+                         "whose every step needs more experts than a layer holds; otherwise one per step, so that "
+                         "the cache cannot end up holding a repeating working set)")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens in the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-legs", action="store_true", help="only the headline (no extra legs)")
@@ -581,7 +584,8 @@ def headline(torch, args, cfg):
     link = link_peak(torch, st.slab)
     log(f"pinned H2D: {link[0]:.1f} GB/s (1 GiB copies), {link[1]:.1f} GB/s (back-to-back slabs), "
         f"{link[2]:.1f} GB/s (slabs split over two streams)")
-    n_in = max(1, min(args.inputs, args.steps + args.warmup))
+    want = args.inputs or (4 if cfg.tokens >= 128 else args.steps + args.warmup)
+    n_in = max(1, min(want, args.steps + args.warmup))
     xs = [st.make_inputs(s) for s in range(n_in)]
     out = st.new_output()
     dev_stream = torch.cuda.current_stream()
