@@ -25,9 +25,17 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
     __shared__ int cur[kPermMaxE];
     extern __shared__ int rows[];  // n entries
     const int tid = threadIdx.x, nt = blockDim.x;
+    // this thread's experts, pairs tid, tid + 1024, ... (n <= 16384: at most 16),
+    // all requested before any is used
+    constexpr int kPer = kPermMaxPairs / 1024;
+    int ex[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) ex[i] = tid + 1024 * i < n ? idx[tid + 1024 * i] : -1;
     for (int e = tid; e < E; e += nt) cnt[e] = 0;
     __syncthreads();
-    for (int p = tid; p < n; p += nt) atomicAdd(&cnt[idx[p]], 1);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
     __syncthreads();
     {  // exclusive scan of the counts, one expert per thread (E <= 1024 = blockDim.x):
        // inclusive scan inside each wave, then over the wave totals
@@ -66,7 +74,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
     }
     if (tid == 0) offset[E] = off[E];
     __syncthreads();
-    for (int p = tid; p < n; p += nt) rows[atomicAdd(&cur[idx[p]], 1)] = p;
+    int slot[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) slot[i] = ex[i] >= 0 ? atomicAdd(&cur[ex[i]], 1) : -1;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (slot[i] >= 0) rows[slot[i]] = tid + 1024 * i;
     __syncthreads();
     // one wavefront per expert segment
     const int wave = tid >> 6, lane = tid & 63, nwaves = nt >> 6;
@@ -74,8 +87,16 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
         const int base = off[e], len = cnt[e];
         for (int j = lane; j < len; j += 64) {
             const int v = rows[base + j];
-            int rank = 0;
-            for (int l = 0; l < len; ++l) rank += rows[base + l] < v;
+            // rank among the segment, 8 independent reads at a time
+            int rank = 0, l = 0;
+            for (; l + 8 <= len; l += 8) {
+                int r[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) r[u] = rows[base + l + u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) rank += r[u] < v;
+            }
+            for (; l < len; ++l) rank += rows[base + l] < v;
             pair_of_row[base + rank] = v;
         }
     }
