@@ -224,6 +224,8 @@ def copy_timing_summary(torch, st, nbytes: int, steps: int, ms_step: float, link
            "slab_copy_split_GBps": round(split_rate, 2), "split_copies": st.copy_stream2 is not None,
            "frac_of_link_peak": round(over_busy / peak, 4) if over_busy else None,
            "wall_over_copy_busy": round(ms_step / busy_step, 4) if busy_step > 0 else None,
+           # the step against the time its bytes take at the measured link peak
+           "wall_over_link_time": round(ms_step / (nbytes / steps / (peak * 1e9) * 1e3), 4) if nbytes else None,
            "exposed_ms_per_step": round(ms_step - busy_step, 3)}
     if compute_ms_step is not None and busy_step > 0 and compute_ms_step > 0:
         res["compute_ms_per_step"] = round(compute_ms_step, 3)
