@@ -215,12 +215,15 @@ void moe_cache_destroy(moe_cache *cache);
  * warehouse": the host manages the cache and moves the data).  ids_host: the
  * layer's n_ids top-k expert ids of the step (host memory, repeats allowed).  The
  * distinct experts are split into waves that each fit the layer's slots: one
- * wave when there are at most slots_per_layer of them; otherwise the fewest
- * waves of at most max(1, slots/2) experts, sizes differing by at most one (the
- * first ones larger), taking the experts already resident first and then the
- * misses (each group in ascending id), every wave sorted ascending -- so that
- * each wave's misses can stream into slots released two waves earlier while
- * the previous wave computes.  Outputs (host memory): wave_experts_host [number of distinct
+ * wave when there are at most slots_per_layer of them; otherwise, with
+ * half = max(1, slots/2) and edge = max(1, half/8), a first and a last wave of
+ * edge experts and between them the fewest waves of at most half experts, sizes
+ * differing by at most one (the first ones larger), taking the experts already
+ * resident first and then the misses (each group in ascending id), every wave
+ * sorted ascending -- so that each wave's misses can stream into slots
+ * released two waves earlier while the previous wave computes, the small first
+ * wave frees slots soon after the layer starts and the small last wave leaves
+ * little compute after the layer's last copy.  At most ceil(n/half) + 2 waves.  Outputs (host memory): wave_experts_host [number of distinct
  * experts] the experts wave by wave; wave_start_host [max_waves + 1], wave w
  * being wave_experts_host[wave_start_host[w] .. wave_start_host[w+1]); masks_host
  * NULL or [max_waves][n_experts] uint8, set to 1 at each wave's experts and 0

@@ -653,16 +653,32 @@ extern "C" int moe_cache_plan(const moe_cache *c, int layer, const int32_t *ids_
     for (int e = 0; e < E; ++e)
         if (seen[e] && slot_of[e] < 0) order.push_back(e);
     const int n = (int)order.size();
-    // one wave if they fit; else the fewest waves of at most half the slots,
-    // their sizes differing by at most one (the first n % waves one larger)
+    // one wave if they fit.  Otherwise a small first wave and a small last wave
+    // of `edge` experts each, and between them the fewest waves of at most half
+    // the slots, sizes differing by at most one (the first ones larger).  The
+    // small first wave (resident experts) computes and frees slots soon after the
+    // layer starts, so the copy stream, idle since the previous layer's last
+    // copy, resumes early; the small last wave leaves little compute after the
+    // layer's last copy.
     const int half = std::max(1, Cs / 2);
-    const int waves = n == 0 ? 0 : n <= Cs ? 1 : (n + half - 1) / half;
+    std::vector<int> sizes;
+    if (n > 0 && n <= Cs) {
+        sizes.push_back(n);
+    } else if (n > Cs) {
+        const int edge = std::max(1, half / 8);
+        const int mid = n - 2 * edge;  // >= 0: n > Cs >= 1 and edge <= max(1, Cs / 16)
+        const int nm = (mid + half - 1) / half;
+        sizes.push_back(edge);
+        for (int v = 0; v < nm; ++v) sizes.push_back(mid / nm + (v < mid % nm ? 1 : 0));
+        sizes.push_back(edge);
+    }
+    const int waves = (int)sizes.size();
     if (waves > max_waves) return moe::fail(MOE_E_CAPACITY, "cache_plan: %d waves > max_waves %d", waves, max_waves);
     if (masks_host) std::memset(masks_host, 0, (size_t)max_waves * E);
     wave_start_host[0] = 0;
     int b = 0;
     for (int v = 0; v < waves; ++v) {
-        const int e_ = b + n / waves + (v < n % waves ? 1 : 0);
+        const int e_ = b + sizes[v];
         std::sort(order.begin() + b, order.begin() + e_);
         for (int i = b; i < e_; ++i) {
             wave_experts_host[i] = order[i];

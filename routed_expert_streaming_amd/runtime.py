@@ -22,9 +22,9 @@ In forward, the routing of every layer is known at the start of a step because e
 (step, layer) gets its own synthetic hidden states; the copies of later layers
 therefore overlap the FFN of earlier ones (LayerStoRm README "TL;DR": streaming
 is overlapped with compute).  When a layer needs more distinct experts than it has
-slots, it runs in waves of half its slots, hits first: each wave's misses go
-into slots that the wave before last released, so they stream while the
-previous wave computes.
+slots, it runs in waves of at most half its slots, hits first, with a small first
+and last wave: each wave's misses go into slots that the wave before last
+released, so they stream while the previous wave computes.
 """
 from __future__ import annotations
 
@@ -215,7 +215,7 @@ class MoEStack:
         P = T * k + (T if self.has_shared else 0)
         self.y = torch.empty((P, H), dtype=torch.float32, device=self.dev)
         half = max(1, self.C // 2)
-        self.max_waves = (E + half - 1) // half + 1
+        self.max_waves = (E + half - 1) // half + 2  # moe_cache_plan: at most ceil(n / half) + 2 waves
         self.masks = torch.zeros((Lyr, self.max_waves, E), dtype=torch.uint8, device=self.dev)
         # gate/up timing of the MFMA path (see ffn); the expert grouping (permutation)
         # and h buffers of the grouped paths (more than 64 (token, slot) pairs), so
@@ -479,7 +479,7 @@ class MoEStack:
                     continue
                 cpu_sets[l] = set()
             # the library's plan: one wave when the layer's experts fit its slots,
-            # else waves of half the slots, hits first
+            # else waves of at most half the slots, hits first, small first and last waves
             plans.append(self.plan_waves(l, idx3[l], masks=mh[l]))
         self.last_cpu_sets = cpu_sets
         if any(len(p) > 1 for p in plans) or lane_jobs:

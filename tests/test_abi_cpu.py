@@ -408,7 +408,7 @@ def test_step_plan_drives_overflowing_layers_through_the_abi(seed, experts, slot
     model = LRUModel(2, experts, slots)
     expected = []
     half = max(1, slots // 2)
-    max_waves = (experts + half - 1) // half + 1
+    max_waves = (experts + half - 1) // half + 2
     for step in range(40):
         l = step % 2
         ids = np.stack([rng.choice(experts, k, replace=False) for _ in range(tokens)]).astype(np.int32)
@@ -420,12 +420,14 @@ def test_step_plan_drives_overflowing_layers_through_the_abi(seed, experts, slot
         order = resident + [e for e in needed if e not in model.slot_of[l]]
         if len(order) <= slots:
             assert waves == [sorted(order)]
-        else:  # the fewest waves of at most half the slots, balanced, resident experts first
-            nw = -(-len(order) // half)
-            sizes = [len(order) // nw + (1 if v < len(order) % nw else 0) for v in range(nw)]
+        else:  # small first and last waves, between them the fewest of at most half the slots, balanced
+            edge = max(1, half // 8)
+            mid = len(order) - 2 * edge
+            nw = -(-mid // half)
+            sizes = [edge] + [mid // nw + (1 if v < mid % nw else 0) for v in range(nw)] + [edge]
             assert max(sizes) <= half
             bounds = np.cumsum([0] + sizes)
-            assert waves == [sorted(order[bounds[v]:bounds[v + 1]]) for v in range(nw)]
+            assert waves == [sorted(order[bounds[v]:bounds[v + 1]]) for v in range(len(sizes))]
         assert all(len(v) <= slots for v in waves)
         for v in range(max_waves):
             want = np.zeros(experts, np.uint8)
@@ -459,7 +461,7 @@ def test_step_plan_equals_per_layer_plans_and_issues_single_wave_layers():
     a = L.moe_cache_create_recording(_desc(Ln, E, C), 1 << 40)
     b = L.moe_cache_create_recording(_desc(Ln, E, C), 1 << 40)
     half = C // 2
-    mw = (E + half - 1) // half + 1
+    mw = (E + half - 1) // half + 2
     for step in range(6):
         ids = np.stack([rng.choice(E, n, replace=(l % 2 == 1)) for l in range(Ln)]).astype(np.int32)
         ids[0, :] = rng.integers(0, 5, n)  # a layer with few distinct experts

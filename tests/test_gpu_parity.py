@@ -438,18 +438,21 @@ def test_stack_decode1_full_and_deterministic():
 
 def documented_waves(order, C):
     """The waves of a layer's experts in the documented order (resident first):
-    one wave if they fit the C slots, else the fewest waves of at most C // 2,
-    sizes differing by at most one, the first ones larger."""
+    one wave if they fit the C slots, else a first and a last wave of
+    max(1, (C // 2) // 8) experts and between them the fewest waves of at most
+    C // 2, sizes differing by at most one, the first ones larger."""
     n = len(order)
     if n <= C:
         return [sorted(order)] if n else []
     half = max(1, C // 2)
-    nw = (n + half - 1) // half
+    edge = max(1, half // 8)
+    mid = n - 2 * edge
+    nw = (mid + half - 1) // half
+    sizes = [edge] + [mid // nw + (1 if v < mid % nw else 0) for v in range(nw)] + [edge]
     waves, b = [], 0
-    for v in range(nw):
-        e = b + n // nw + (1 if v < n % nw else 0)
-        waves.append(sorted(order[b:e]))
-        b = e
+    for s in sizes:
+        waves.append(sorted(order[b:b + s]))
+        b += s
     return waves
 
 
