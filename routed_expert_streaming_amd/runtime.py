@@ -226,6 +226,12 @@ class MoEStack:
                       torch.empty(E + 1, dtype=torch.int32, device=self.dev),
                       torch.empty(T * k, dtype=torch.int32, device=self.dev)) if grouped else None
         self._h = torch.empty((P, I), dtype=torch.bfloat16, device=self.dev) if grouped else None
+        # a second y and permutation for layers that run in waves: the streamed step
+        # runs a layer's leading waves before the previous layer's last one, so two
+        # adjacent layers are in flight (buffers taken by layer parity)
+        overflow = self.streaming and T * k > self.C
+        self._y2 = torch.empty_like(self.y) if overflow else None
+        self._perm2 = tuple(torch.empty_like(t) for t in self._perm) if (overflow and grouped) else None
         self.pidx = torch.empty((Lyr, T, k), dtype=torch.int32, device=self.dev)  # predicted experts
         self.pw = torch.empty((Lyr, T, k), dtype=torch.float32, device=self.dev)
         self._idx_host = PinnedHost(max(Lyr, 2) * T * k * 4) if self.streaming else None
@@ -283,7 +289,7 @@ class MoEStack:
         L.moe_router_topk_layers(x, self.L, self.T, self.H, self.wr, self.bias, self.E, self.k, self.idx, self.w,
                                  self.router_ws, self.router_ws_bytes, self.stream)
 
-    def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True, experts=None, permuted=False):
+    def ffn(self, x: torch.Tensor, l: int, mask=None, shared=True, experts=None, permuted=False, y=None, perm=None):
         """Gate/up + SwiGLU and down projection of layer l's pairs whose expert the
         mask admits (all when None) into y.  With more than 64 (token, slot) pairs
         the kernels run in expert grouping as three calls -- the permutation,
@@ -291,17 +297,20 @@ class MoEStack:
         layer's routing computed by an earlier call (the layer's earlier waves).
         With kernel_log set to a list and many tokens (the MFMA kernels), timing
         events go before gate/up, between the two and after down, and (the three
-        events, layer, experts, shared expert included) is appended to the log."""
+        events, layer, experts, shared expert included) is appended to the log.
+        y / perm: the output rows and the permutation buffers to use (default
+        self.y and self._perm)."""
         sh = self.shared[l] if (self.has_shared and shared) else None
+        y = self.y if y is None else y
         # MXFP4 prefill runs on the block-scaled matrix cores, whose activation
         # digit pairs live in the one-call FFN's workspace
         scaled = self.fmt == 1 and self.T >= 128 and self.path in (L.MOE_FFN_AUTO, L.MOE_FFN_MFMA)
         if self._perm is None or scaled:
             L.moe_expert_ffn_fmt(x[l], self.T, self.H, self.I, self.E, self.idx[l], self.k, self.table[l], sh, mask,
-                                 self.y, self.ffn_ws, self.ffn_ws_bytes, self.path, self.fmt, self.stream)
+                                 y, self.ffn_ws, self.ffn_ws_bytes, self.path, self.fmt, self.stream)
             return
         T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
-        cnt, off, por = self._perm
+        cnt, off, por = self._perm if perm is None else perm
         if not permuted:
             L.moe_permute(self.idx[l], T, k, E, cnt, off, por, self.stream)
         log = self.kernel_log is not None and T >= 128 and self.path in (L.MOE_FFN_AUTO, L.MOE_FFN_MFMA)
@@ -312,7 +321,7 @@ class MoEStack:
                                  self._h, self.path, self.fmt, self.stream)
         if log:
             b.record(self.stream)
-        L.moe_expert_down_fmt(self._h, T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask, self.y,
+        L.moe_expert_down_fmt(self._h, T, H, I, E, self.idx[l], k, cnt, off, por, self.table[l], sh, mask, y,
                               self.path, self.fmt, self.stream)
         if log:
             c.record(self.stream)
@@ -342,8 +351,9 @@ class MoEStack:
                                 self.idx[l], self.w[l], out[l], self.layer_ws, self.layer_ws_bytes, self.stream,
                                 prefetch=nxt, prefetch_bytes=nxt.numel() * 4)
 
-    def combine(self, l: int, out: torch.Tensor):
-        L.moe_combine(self.y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l], self.stream)
+    def combine(self, l: int, out: torch.Tensor, y=None):
+        L.moe_combine(self.y if y is None else y, self.w[l], self.T, self.k, self.H, self.has_shared, out[l],
+                      self.stream)
 
     def gate_up_only(self, x: torch.Tensor, l: int, h: torch.Tensor):
         """Only the dequant + gate/up + SwiGLU kernel of layer l (pair grouping), for timing it."""
@@ -483,7 +493,7 @@ class MoEStack:
             plans.append(self.plan_waves(l, idx3[l], masks=mh[l]))
         self.last_cpu_sets = cpu_sets
         if any(len(p) > 1 for p in plans) or lane_jobs:
-            self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
+            self._upload_masks(mh)
         # single-wave layers: every copy is queued before the first FFN launch, so
         # the copy engine starts as soon as the plan is known (each layer evicts
         # only its own slots, released in the previous step); the compute stream
@@ -519,33 +529,77 @@ class MoEStack:
             self.combine(l, out)
         return st
 
+    def _upload_masks(self, mh: np.ndarray):
+        """Copy the step's wave masks (pinned host) to the device over the copy
+        stream, ahead of the step's slab copies, and make the compute stream wait
+        for them.  On the compute stream the upload is a DMA command of its own
+        queue, which the DMA engine can leave behind the copy streams' waits for
+        slot releases that only later compute-stream work records (measured: the
+        first FFN of a step started ~4 ms late)."""
+        with torch.cuda.stream(self.copy_stream):
+            self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
+        self.stream.wait_stream(self.copy_stream)
+
     def _forward_planned(self, x, out, idx_host, mh, st: StepStats) -> StepStats:
         """The streamed step after routing, without a CPU lane: one library call
         plans every layer and queues the copies of the layers that fit their slots
         (the copy engine starts right away); then per layer the wait, the FFN
         (wave by wave for layers that need more experts than they have slots) and
-        the release."""
+        the release.
+
+        Two adjacent layers that both run in waves overlap: the next layer's
+        leading waves (its first two, at most all but one; resident experts come
+        first) go before this layer's last wave.  They compute while this layer's
+        last misses stream and free slots of the next layer, so its first misses
+        stream right after this layer's last ones instead of after this layer's
+        last wave, its combine and the next layer's first waves have computed.
+        The step's layers take their own inputs, so the order of their kernels
+        does not change any result; the two layers in flight use the y rows and
+        permutation buffers of their parity, and every layer still calls the
+        cache in its own wave order (its hits, misses and victims do not change)."""
         ne = self._plan_experts
         starts = self._plan_starts
         nw = self._plan_nwaves
+        # a layer can need more waves than one only when its top-k ids outnumber its
+        # slots; then the masks go up before any copy of the step is queued
+        may_overflow = self.T * self.k > self.C
         st.copies += L.moe_cache_plan_step(self.cache, idx_host, self.T * self.k, ne, starts, self.max_waves, mh, nw,
-                                           True)
-        if (nw > 1).any():
-            self.masks.view(-1).copy_(torch.from_numpy(mh.reshape(-1)), non_blocking=True)
+                                           not may_overflow)
+        if may_overflow:
+            if (nw > 1).any():
+                self._upload_masks(mh)
+            for l in range(self.L):
+                if nw[l] == 1:
+                    st.copies += L.moe_cache_prefetch_async(self.cache, l, ne[l, :starts[l, 1]])
+        def wave(l: int, wv: int):
+            experts = ne[l, starts[l, wv]:starts[l, wv + 1]]
+            st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
+            par = self._y2 is not None and l % 2 == 1
+            self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts, permuted=wv > 0,
+                     y=self._y2 if par else None, perm=self._perm2 if par else None)
+            L.moe_cache_release(self.cache, l, self.stream)
+            st.waves += 1
+
+        overlap = self._y2 is not None and (self._perm is None or self._perm2 is not None)
+        led = 0  # waves of layer l already run ahead of layer l-1's last wave
         for l in range(self.L):
             if nw[l] == 1:
                 L.moe_cache_wait(self.cache, l, self.stream)
                 self.ffn_combine(x, l, out)
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
+                led = 0
                 continue
-            for wv in range(int(nw[l])):
-                experts = ne[l, starts[l, wv]:starts[l, wv + 1]]
-                st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
-                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts, permuted=wv > 0)
-                L.moe_cache_release(self.cache, l, self.stream)
-                st.waves += 1
-            self.combine(l, out)
+            last = int(nw[l]) - 1
+            for wv in range(led, last):
+                wave(l, wv)
+            led = 0
+            if overlap and l + 1 < self.L and nw[l + 1] > 1:
+                led = min(2, int(nw[l + 1]) - 1)
+                for wv in range(led):
+                    wave(l + 1, wv)
+            wave(l, last)
+            self.combine(l, out, y=self._y2 if (self._y2 is not None and l % 2 == 1) else None)
         self.last_cpu_sets = [set() for _ in range(self.L)]
         return st
 
