@@ -15,7 +15,15 @@ copies, their average size, duration and rate, and over the last two thirds of
 the trace the average idle gap between consecutive copies (gaps under 1 ms) and
 the share of that span the copies were running; with --events N AT, N kernels
 and copies in start order from the AT-th dispatch of the router partial kernel
-counted from the end (1 = the last), times in microseconds from the first one.
+counted from the end (1 = the last), times in microseconds from the first one;
+with --copy-gaps ANCHOR (a trace taken with --memory-copy-trace), per step
+(a step starts at a dispatch of the kernel named ANCHOR that follows more than
+5 ms without one) the H2D slab copies (over 1 MB) of both copy streams merged
+into busy intervals: the step's span, bytes, busy time and rate over it, the
+head (step start to first copy), the tail (last copy to the step's last kernel
+end), the idle gaps between busy intervals, and the time with one and with two
+copies in flight; then the gaps over 100 us of the last step with the kernels
+that ran in them.
 """
 from __future__ import annotations
 
@@ -117,6 +125,45 @@ def events(db: str, n: int, at: int, anchor: str = "router_partial_kernel"):
     return [((s - t0) / 1e3, (e - t0) / 1e3, (e - s) / 1e3, name) for s, e, name in ev[i0:i0 + n]]
 
 
+def copy_gaps(db: str, anchor: str):
+    c = sqlite3.connect(db)
+    ks = sorted((s, e, short_name(n)) for n, s, e in c.execute("select name, start, end from kernels"))
+    cps = sorted((s, e, z) for s, e, z in c.execute("select start, end, size from memory_copies where size > 1000000"))
+    marks = [s for s, e, n in ks if n.startswith(anchor)]
+    if not marks:
+        return [], []
+    starts = [marks[0]] + [b for a, b in zip(marks, marks[1:]) if b - a > 5_000_000]
+    end_all = max(e for s, e, n in ks)
+    rows, last_gaps = [], []
+    for i, t0 in enumerate(starts):
+        t1 = starts[i + 1] if i + 1 < len(starts) else end_all + 1
+        cp = [x for x in cps if t0 <= x[0] < t1]
+        kk = [x for x in ks if t0 <= x[0] < t1]
+        if not cp or not kk:
+            continue
+        merged = []
+        for s, e, _ in cp:
+            if merged and s <= merged[-1][1]:
+                merged[-1][1] = max(merged[-1][1], e)
+            else:
+                merged.append([s, e])
+        busy = sum(e - s for s, e in merged)
+        gaps = [(a[1], b[0]) for a, b in zip(merged, merged[1:])]
+        kend = max(e for s, e, n in kk)
+        level, last, in_flight = 0, cp[0][0], collections.Counter()
+        for t, d in sorted([(s, 1) for s, e, z in cp] + [(e, -1) for s, e, z in cp]):
+            in_flight[min(level, 2)] += t - last
+            level += d
+            last = t
+        nbytes = sum(z for s, e, z in cp)
+        rows.append((i, (kend - t0) / 1e6, len(cp), nbytes / 1e9, busy / 1e6, nbytes / busy, (merged[0][0] - t0) / 1e6,
+                     (kend - merged[-1][1]) / 1e6, len(gaps), sum(b - a for a, b in gaps) / 1e6, in_flight[1] / 1e6,
+                     in_flight[2] / 1e6))
+        last_gaps = [((a - t0) / 1e3, (b - a) / 1e3, [n for s, e, n in kk if s < b and e > a])
+                     for a, b in gaps if b - a > 100_000]
+    return rows, last_gaps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("db")
@@ -125,7 +172,19 @@ def main():
     ap.add_argument("--timeline", action="store_true")
     ap.add_argument("--copies", action="store_true")
     ap.add_argument("--events", nargs=2, type=int, metavar=("N", "AT"))
+    ap.add_argument("--copy-gaps", metavar="ANCHOR")
     args = ap.parse_args()
+    if args.copy_gaps:
+        rows, gaps = copy_gaps(args.db, args.copy_gaps)
+        print(f"{'step':>4s} {'span_ms':>9s} {'copies':>6s} {'GB':>6s} {'busy_ms':>9s} {'GB/s':>6s} {'head_ms':>8s} "
+              f"{'tail_ms':>8s} {'gaps':>5s} {'gap_ms':>7s} {'one_ms':>7s} {'two_ms':>8s}")
+        for r in rows:
+            print(f"{r[0]:4d} {r[1]:9.2f} {r[2]:6d} {r[3]:6.2f} {r[4]:9.2f} {r[5]:6.2f} {r[6]:8.3f} {r[7]:8.3f} "
+                  f"{r[8]:5d} {r[9]:7.3f} {r[10]:7.2f} {r[11]:8.2f}")
+        print("gaps over 100 us in the last step (start us after its first anchor, length us, kernels in the gap):")
+        for at, length, names in gaps:
+            print(f"  {at:10.1f} {length:8.1f}  {' | '.join(n[:32] for n in names[:6])}")
+        return
     if args.events:
         print(f"{'start_us':>9s} {'end_us':>9s} {'dur_us':>8s}  event")
         for s0, e, d, name in events(args.db, *args.events):
