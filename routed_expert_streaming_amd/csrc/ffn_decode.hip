@@ -643,9 +643,12 @@ __global__ __launch_bounds__(256) void decode_down_kernel(moe::FfnArgs a, const 
 constexpr int kDown1MaxRows = 64;  // rows per workgroup
 constexpr int kDown1MaxPairs = moe::kDown1MaxPairs;
 
-template <int BPL, int D, bool COMBINE, int FMT = 0>
+template <int BPL, int D, bool COMBINE, int FMT = 0, int ROWS = 16>
 __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, const float *__restrict__ topk_w,
-                                                            uint16_t *__restrict__ out, int rows_per_wg) {
+                                                            uint16_t *__restrict__ out) {
+    static_assert(ROWS % 4 == 0 && ROWS <= kDown1MaxRows && D >= 1, "rows per workgroup, units in flight");
+    constexpr int rows_per_wg = ROWS;
+    constexpr int U = ROWS / 4;  // rows per 16-lane group
     const int H = a.H, I = a.I, k = a.k;
     const int P = k + (a.shared ? 1 : 0);
     __shared__ float part[kDown1MaxRows][kDown1MaxPairs + 1];
@@ -654,7 +657,6 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
     const int lane = threadIdx.x & 63, sub = lane >> 4, c = lane & 15;
     const int p = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r0 = blockIdx.x * rows_per_wg;
-    const int U = rows_per_wg >> 2;  // rows per 16-lane group
     // routing weights requested now, stored to LDS just before the barrier
     const float my_w = (COMBINE && lane < k) ? topk_w[lane] : 0.0f;
 
@@ -698,8 +700,8 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
         constexpr uint32_t RB = FMT == 1 ? 1u : 4u;  // record bytes per block (format 2: a 16-byte header)
         const uint32_t code_off = 16u * c,
                        rec_off = (uint32_t)(I / 2) + (FMT == 2 ? 2u * (uint32_t)(c & ~7) : RB * c);
-        uint4 cw[D][BPL];
-        std::conditional_t<FMT == 2, uint4, uint32_t> pw[D][BPL];
+        uint4 cw[D < U ? D : U][BPL];
+        std::conditional_t<FMT == 2, uint4, uint32_t> pw[D < U ? D : U][BPL];
         int ui = 0;
         auto issue = [&](int j) {
             int row = r0 + sub + 4 * ui;
@@ -717,8 +719,12 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
             }
             ++ui;
         };
+        // a ring of min(D, U) units: every unit's loads are issued once (the unit
+        // count is a compile-time constant, so the compiler's wait counts are exact
+        // and no load is issued for a unit past the last)
+        constexpr int DR = D < U ? D : U;
 #pragma unroll
-        for (int j = 0; j < D; ++j) issue(j);
+        for (int j = 0; j < DR; ++j) issue(j);
         __builtin_amdgcn_sched_barrier(0);  // the weight requests go out before waiting for h
 
         uint4 X[BPL][4];
@@ -734,31 +740,29 @@ __global__ __launch_bounds__(1024) void decode1_down_kernel(moe::FfnArgs a, cons
             }
         }
 
-        for (int base = 0; base < U; base += D) {
 #pragma unroll
-            for (int j = 0; j < D; ++j) {
-                if (base + j >= U) break;
-                const int rl = sub + 4 * (base + j), row = r0 + rl;
-                float v = 0.0f;
+        for (int u = 0; u < U; ++u) {
+            const int j = u % DR;
+            const int rl = sub + 4 * u, row = r0 + rl;
+            float v = 0.0f;
 #pragma unroll
-                for (int b = 0; b < BPL; ++b) {
-                    if constexpr (FMT == 2)
-                        v += moe_sb_block_value(pw[j][b], c & 7, moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
-                    else if constexpr (FMT == 1)
-                        v += moe_mx_block_value(pw[j][b], moe_mx_block_dot(cw[j][b], X[b]));
-                    else
-                        v += moe_block_value(pw[j][b], moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
-                }
-                v = moe_group_sum<16>(v);
-                if (c == 15 && row < H) {
-                    if (COMBINE)
-                        part[rl][p] = v;
-                    else
-                        a.y[(size_t)p * H + row] = v;
-                }
-                issue(j);
-                if (pf && base + j == U - 2) pfv = load_global_u4(a.prefetch + pf_off);
+            for (int b = 0; b < BPL; ++b) {
+                if constexpr (FMT == 2)
+                    v += moe_sb_block_value(pw[j][b], c & 7, moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
+                else if constexpr (FMT == 1)
+                    v += moe_mx_block_value(pw[j][b], moe_mx_block_dot(cw[j][b], X[b]));
+                else
+                    v += moe_block_value(pw[j][b], moe_block_dot(cw[j][b], X[b], 1, magic), S[b]);
             }
+            v = moe_group_sum<16>(v);
+            if (c == 15 && row < H) {
+                if (COMBINE)
+                    part[rl][p] = v;
+                else
+                    a.y[(size_t)p * H + row] = v;
+            }
+            if (u + DR < U) issue(j);
+            if (pf && u == U - 2) pfv = load_global_u4(a.prefetch + pf_off);
         }
     }
     // keeps the prefetch loads (their values are never needed)
@@ -866,23 +870,26 @@ int launch_down(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipSt
 }
 
 #ifndef MOE_DOWN1_ROWS
-#define MOE_DOWN1_ROWS 16 // rows per workgroup, one-token down kernel
+// rows per workgroup, one-token down kernel (same measurement: 16 rows 9.5 us,
+// 8 rows 9.8 us, 4 rows 12.3 us, one unit in flight)
+#define MOE_DOWN1_ROWS 16
 #endif
 #ifndef MOE_DOWN1_D
-#define MOE_DOWN1_D 1  // units in flight per lane group, one-token down kernel
+// units in flight per lane group, one-token down kernel (measured at H 4096, I 1536,
+// 9 pairs, the kernel alone: 1 unit 9.5 us, 2 units 8.9 us, 4 units 9.7 us)
+#define MOE_DOWN1_D 2
 #endif
 
 template <int BPL, int FMT = 0>
 int launch_down1(const moe::FfnArgs &a, const float *topk_w, uint16_t *out, hipStream_t s) {
-    static_assert(MOE_DOWN1_ROWS % 4 == 0 && MOE_DOWN1_ROWS <= kDown1MaxRows, "rows per workgroup");
     const int P = a.k + (a.shared ? 1 : 0);
     const int grid = (a.H + MOE_DOWN1_ROWS - 1) / MOE_DOWN1_ROWS;
     if (out)
-        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, true, FMT>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
-                           out, MOE_DOWN1_ROWS);
+        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, true, FMT, MOE_DOWN1_ROWS>), dim3(grid), dim3(64 * P),
+                           0, s, a, topk_w, out);
     else
-        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, false, FMT>), dim3(grid), dim3(64 * P), 0, s, a, topk_w,
-                           out, MOE_DOWN1_ROWS);
+        hipLaunchKernelGGL((decode1_down_kernel<BPL, MOE_DOWN1_D, false, FMT, MOE_DOWN1_ROWS>), dim3(grid),
+                           dim3(64 * P), 0, s, a, topk_w, out);
     MOE_LAUNCH_CHECK("decode1_down_kernel");
     return MOE_OK;
 }

@@ -548,8 +548,9 @@ class MoEStack:
         the release.
 
         Two adjacent layers that both run in waves overlap: the next layer's
-        leading waves (its first two, at most all but one; resident experts come
-        first) go before this layer's last wave.  They compute while this layer's
+        leading waves (its first two at most, and only those whose experts are
+        all resident, so they need no copy; resident experts come first) go
+        before this layer's last wave.  They compute while this layer's
         last misses stream and free slots of the next layer, so its first misses
         stream right after this layer's last ones instead of after this layer's
         last wave, its combine and the next layer's first waves have computed.
@@ -581,6 +582,19 @@ class MoEStack:
             st.waves += 1
 
         overlap = self._y2 is not None and (self._perm is None or self._perm2 is not None)
+
+        def resident_lead(l: int) -> int:
+            # leading waves of layer l (all but its last) whose experts are all
+            # resident now: they need no copy, so they can run ahead (the layer's
+            # slots change only through its own prefetches)
+            n = 0
+            for wv in range(int(nw[l]) - 1):
+                experts = ne[l, starts[l, wv]:starts[l, wv + 1]]
+                if L.moe_cache_lookup(self.cache, l, experts)[1] != len(experts):
+                    break
+                n += 1
+            return n
+
         led = 0  # waves of layer l already run ahead of layer l-1's last wave
         for l in range(self.L):
             if nw[l] == 1:
@@ -595,7 +609,7 @@ class MoEStack:
                 wave(l, wv)
             led = 0
             if overlap and l + 1 < self.L and nw[l + 1] > 1:
-                led = min(2, int(nw[l + 1]) - 1)
+                led = min(2, resident_lead(l + 1))
                 for wv in range(led):
                     wave(l + 1, wv)
             wave(l, last)
