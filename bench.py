@@ -67,7 +67,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=400, help="timed steps of the resident batch-1 decode leg")
     ap.add_argument("--decode-warmup", type=int, default=40)
     ap.add_argument("--graph", action="store_true",
-                    help="resident decode leg: replay one HIP graph per step instead of launching eagerly")
+                    help="resident decode leg: replay one HIP graph per step instead of launching eagerly (the "
+                         "capture slows the streamed legs that follow it)")
     ap.add_argument("--kernel-iters", type=int, default=50, help="iterations of the per-kernel event timing")
     ap.add_argument("--no-stream", action="store_true", help="skip the streamed batch-1 decode (PCIe) leg")
     ap.add_argument("--stream-workload", default="decode1_stream")
@@ -801,11 +802,42 @@ def decode_leg(torch, args):
     elapsed = max(wall, gpu_ms / 1e3)
     ms_per_step = elapsed / steps * 1e3
     log(f"decode leg: {steps} steps, {ms_per_step * 1e3:.1f} us/step, {steps / elapsed:.1f} tokens/s")
+    sb = step_bytes(stack)
+    res = {"workload": cfg.name, "layers": cfg.layers, "resident": True, "graph": graphs is not None,
+           "tokens_per_s": round(steps / elapsed, 2), "ms_per_step": round(ms_per_step, 4), "steps": steps,
+           "warmup": args.decode_warmup, "step_hbm_bytes": sb, "step_hbm_GBps": round(sb / (ms_per_step * 1e-3) / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        x_layers = [np.concatenate([synth.x_bf16(cfg.seed, s, l, 1, cfg.hidden) for s in range(8)])
+                    for l in range(stack.L)]
+        wr = [synth.router_w(cfg.seed, l, cfg.experts, cfg.hidden) for l in range(stack.L)]
+        bias = [synth.router_bias(cfg, l) for l in range(stack.L)]
+        slabs = {l: stack.host_slabs(l) for l in range(stack.L)}
+        shared = {l: stack.host_shared(l) for l in range(stack.L)}
+        t_all = oracle_sample(torch, cfg, stack.L, x_layers, wr, bias, slabs.get, shared.get, list(range(8)), threads)
+        t_one = oracle_sample(torch, cfg, stack.L, x_layers, wr, bias, slabs.get, shared.get, [0], 1)
+        res["cpu_baseline"] = {"tokens_per_s": round(8 / t_all, 4), "threads": threads, "cpu_model": cpu_model(),
+                               "sample": f"8 decode tokens (steps 0..7) through all {stack.L} layers, {t_all:.1f} s",
+                               "one_thread_tokens_per_s": round(1 / t_one, 4),
+                               "one_thread_sample": f"1 decode token through all {stack.L} layers, {t_one:.1f} s"}
+    del graphs, outs[1:]
+    log(f"decode leg: {res}")
+    return res, (stack, xs[0], outs[0])
 
-    # the gate/up and down kernels launched alone, timed with events on their stream
+
+def decode_kernels_alone(torch, args, res, held):
+    """The resident decode's gate/up and down kernels launched alone, timed with
+    HIP events around a HIP graph of back-to-back launches (the gate/up kernel's
+    roofline).  Run after every streamed leg: once a process has captured a HIP
+    graph, its later streamed steps run slower (measured: the batch-1 streamed
+    decode 2.84 -> 3.10 ms per step after one graph capture of a single
+    elementwise kernel, the copy engine idling longer between copies)."""
+    stack, x0, out0 = held
+    cfg = stack.cfg
+    dev_stream = torch.cuda.current_stream()
     h = torch.empty((cfg.tokens * cfg.top_k + cfg.tokens * cfg.shared, cfg.inter), dtype=torch.bfloat16,
                     device="cuda")
-    stack.forward(xs[0], outs[0])  # routing of input 0 for every layer
+    stack.forward(x0, out0)  # routing of input 0 for every layer
 
     # back-to-back launches of one kernel between two events, captured in one HIP
     # graph and replayed, so host launch cost does not show up as idle time
@@ -828,39 +860,18 @@ def decode_leg(torch, args):
         del g
         return a.elapsed_time(b) * 1e3 / (iters * stack.L)
 
-    gu_us = time_launches(lambda l: stack.gate_up_only(xs[0], l, h), args.kernel_iters)
+    gu_us = time_launches(lambda l: stack.gate_up_only(x0, l, h), args.kernel_iters)
     dn_us = time_launches(lambda l: stack.down_only(h, l), args.kernel_iters)
     gu_b, dn_b = gate_up_bytes(stack), down_bytes(stack)
-    sb = step_bytes(stack)
-    res = {"workload": cfg.name, "layers": cfg.layers, "resident": True, "graph": graphs is not None,
-           "tokens_per_s": round(steps / elapsed, 2), "ms_per_step": round(ms_per_step, 4), "steps": steps,
-           "warmup": args.decode_warmup,
-           "gate_up_alone": {"kernel": GATE_UP_KERNEL, "us_per_launch": round(gu_us, 3), "bytes_per_launch": gu_b,
-                             "GBps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
-                             "frac": round(gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                             "traffic": counter_traffic(GATE_UP_KERNEL, "decode1_gate_up_hbm_traffic.md")},
-           "down_alone": {"us_per_launch": round(dn_us, 3), "bytes_per_launch": dn_b,
-                          "GBps": round(dn_b / (dn_us * 1e-6) / 1e9, 1)},
-           "step_hbm_bytes": sb, "step_hbm_GBps": round(sb / (ms_per_step * 1e-3) / 1e9, 1)}
-    if not args.no_cpu_baseline:
-        threads = len(os.sched_getaffinity(0))
-        x_layers = [np.concatenate([synth.x_bf16(cfg.seed, s, l, 1, cfg.hidden) for s in range(8)])
-                    for l in range(stack.L)]
-        wr = [synth.router_w(cfg.seed, l, cfg.experts, cfg.hidden) for l in range(stack.L)]
-        bias = [synth.router_bias(cfg, l) for l in range(stack.L)]
-        slabs = {l: stack.host_slabs(l) for l in range(stack.L)}
-        shared = {l: stack.host_shared(l) for l in range(stack.L)}
-        t_all = oracle_sample(torch, cfg, stack.L, x_layers, wr, bias, slabs.get, shared.get, list(range(8)), threads)
-        t_one = oracle_sample(torch, cfg, stack.L, x_layers, wr, bias, slabs.get, shared.get, [0], 1)
-        res["cpu_baseline"] = {"tokens_per_s": round(8 / t_all, 4), "threads": threads, "cpu_model": cpu_model(),
-                               "sample": f"8 decode tokens (steps 0..7) through all {stack.L} layers, {t_all:.1f} s",
-                               "one_thread_tokens_per_s": round(1 / t_one, 4),
-                               "one_thread_sample": f"1 decode token through all {stack.L} layers, {t_one:.1f} s"}
+    res["gate_up_alone"] = {"kernel": GATE_UP_KERNEL, "us_per_launch": round(gu_us, 3), "bytes_per_launch": gu_b,
+                            "GBps": round(gu_b / (gu_us * 1e-6) / 1e9, 1),
+                            "frac": round(gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": counter_traffic(GATE_UP_KERNEL, "decode1_gate_up_hbm_traffic.md")}
+    res["down_alone"] = {"us_per_launch": round(dn_us, 3), "bytes_per_launch": dn_b,
+                         "GBps": round(dn_b / (dn_us * 1e-6) / 1e9, 1)}
     stack.close()
-    del stack, graphs, xs, outs
-    torch.cuda.empty_cache()
-    log(f"decode leg: {res}")
-    return res
+    del stack, x0, out0, h
+    log(f"decode kernels alone: gate/up {res['gate_up_alone']}, down {res['down_alone']}")
 
 
 def tiny_leg(torch, args):
@@ -917,7 +928,7 @@ def main():
         raise SystemExit("the headline workload is a streamed configuration; the resident decode is an extra leg")
     result = headline(torch, args, cfg)
     if not args.no_legs:
-        decode = decode_leg(torch, args)
+        decode, held = decode_leg(torch, args)
         result["decode1"] = decode
         if not args.no_stream:
             result["decode1_stream"] = streaming_leg(torch, args, decode["ms_per_step"])
@@ -936,6 +947,10 @@ def main():
                     result[f"layer_decode32_{tag}"] = layer_leg(torch, f"decode32_{tag}_stream", L.MOE_FFN_SPLIT, 20)
                     result[f"layer_prefill2048_{tag}"] = layer_leg(torch, f"prefill2048_{tag}_stream",
                                                                    L.MOE_FFN_MFMA, 3)
+        # last: the kernel timing captures a HIP graph, after which streamed steps run slower
+        decode_kernels_alone(torch, args, decode, held)
+        del held
+        torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
 
 
