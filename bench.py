@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--stream-workload", default="decode1_stream")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
+    ap.add_argument("--c4-steps", type=int, default=16, help="timed steps of the streamed batch-32 decode leg")
+    ap.add_argument("--c4-warmup", type=int, default=8)
     ap.add_argument("--chain-steps", type=int, default=128,
                     help="timed steps of each chained-layer run of the streamed decode leg (0 skips them)")
     ap.add_argument("--chain-warmup", type=int, default=32)
@@ -303,6 +305,25 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     if lane:
         res["cpu_lane"] = lane
     log(f"streaming: {res}")
+    return res
+
+
+def decode32_stream_leg(torch, args):
+    """The streamed batch-32 decode through all 16 layers (hidden 6144, 256
+    experts + 1 shared, intermediate 2048, top-8, Zipf(1.1) routing, 102 slots per
+    layer): tokens/s and the PCIe figures, measured as the headline measures its
+    own configuration (no oracle sample)."""
+    import copy
+    import synth
+
+    a = copy.copy(args)
+    a.steps, a.warmup, a.layers, a.inputs = args.c4_steps, args.c4_warmup, 0, 0
+    a.no_cpu_baseline, a.traffic_calibration = True, False
+    r = headline(torch, a, synth.get("decode32_stream"))
+    res = {"workload": r["config"]["workload"], "layers": r["config"]["layers"], "tokens_per_step": r["config"]["tokens_per_step"],
+           "tokens_per_s": r["value"], "ms_per_step": r["ms_per_step"], "steps": a.steps, "warmup": a.warmup,
+           **r["streaming"]}
+    log(f"decode32 streamed: {res}")
     return res
 
 
@@ -932,6 +953,7 @@ def main():
         result["decode1"] = decode
         if not args.no_stream:
             result["decode1_stream"] = streaming_leg(torch, args, decode["ms_per_step"])
+            result["decode32_stream"] = decode32_stream_leg(torch, args)
         result["tiny"] = tiny_leg(torch, args)
         if not args.no_mx:
             result["mx"] = format_leg(torch, args, "decode1_mx", "decode1_mx_stream", decode["ms_per_step"],
