@@ -74,6 +74,7 @@ def parse():
     ap.add_argument("--stream-workload", default="decode1_stream")
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
+    ap.add_argument("--no-c4", action="store_true", help="skip the streamed batch-32 decode leg")
     ap.add_argument("--c4-steps", type=int, default=16, help="timed steps of the streamed batch-32 decode leg")
     ap.add_argument("--c4-warmup", type=int, default=8)
     ap.add_argument("--chain-steps", type=int, default=128,
@@ -953,7 +954,8 @@ def main():
         result["decode1"] = decode
         if not args.no_stream:
             result["decode1_stream"] = streaming_leg(torch, args, decode["ms_per_step"])
-            result["decode32_stream"] = decode32_stream_leg(torch, args)
+            if not args.no_c4:
+                result["decode32_stream"] = decode32_stream_leg(torch, args)
         result["tiny"] = tiny_leg(torch, args)
         if not args.no_mx:
             result["mx"] = format_leg(torch, args, "decode1_mx", "decode1_mx_stream", decode["ms_per_step"],
