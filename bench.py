@@ -230,6 +230,8 @@ def copy_timing_summary(torch, st, nbytes: int, steps: int, ms_step: float, link
            "h2d_GBps_over_copy_busy": round(over_busy, 2) if over_busy else None,
            "link_peak_GBps": round(peak, 2), "slab_copy_one_stream_GBps": round(one_rate, 2),
            "slab_copy_split_GBps": round(split_rate, 2), "split_copies": st.copy_stream2 is not None,
+           # hipMemcpyAsync from pinned host memory runs on the SDMA engines unless HSA_ENABLE_SDMA=0 (blit kernels)
+           "copy_engine": "blit kernels" if os.environ.get("HSA_ENABLE_SDMA", "1") == "0" else "SDMA",
            "frac_of_link_peak": round(over_busy / peak, 4) if over_busy else None,
            # the copy-timed steps against their own copy-busy time
            "copy_timed_ms_per_step": round(timed_ms_step, 3),
