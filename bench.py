@@ -322,10 +322,23 @@ def decode32_stream_leg(torch, args):
     a = copy.copy(args)
     a.steps, a.warmup, a.layers, a.inputs = args.c4_steps, args.c4_warmup, 0, 0
     a.no_cpu_baseline, a.traffic_calibration = True, False
-    r = headline(torch, a, synth.get("decode32_stream"))
+    cfg = synth.get("decode32_stream")
+    r = headline(torch, a, cfg)
     res = {"workload": r["config"]["workload"], "layers": r["config"]["layers"], "tokens_per_step": r["config"]["tokens_per_step"],
            "tokens_per_s": r["value"], "ms_per_step": r["ms_per_step"], "steps": a.steps, "warmup": a.warmup,
            **r["streaming"]}
+    if args.cpu_lane_threads > 0:
+        # the same steps with the CPU lane (row f2): each step's misses split
+        # between the copy engine and host cores
+        from routed_expert_streaming_amd.runtime import MoEStack
+        st = MoEStack(cfg)
+        xs = [st.make_inputs(s) for s in range(a.steps + a.warmup)]
+        la = copy.copy(args)
+        la.stream_steps, la.stream_warmup, la.chain_steps = a.steps, a.warmup, 0
+        res["cpu_lane"] = cpu_lane_run(torch, st, la, xs, r["value"])
+        st.close()
+        del st, xs
+        torch.cuda.empty_cache()
     log(f"decode32 streamed: {res}")
     return res
 
