@@ -468,11 +468,12 @@ class MoEStack:
         idx3 = idx_host.reshape(self.L, self.T, self.k)
         mh = np.frombuffer(self._mask_host.array, dtype=np.uint8,
                            count=self.L * self.max_waves * self.E).reshape(self.L, self.max_waves, self.E)
-        # CPU lane: some misses are computed on the host; a layer uses it when the
-        # rest of its experts fit its slots (one wave)
-        cpu_sets, lane_jobs = [set() for _ in range(self.L)], {}
+        # CPU lane: some misses are computed on the host; the rest of the layer's
+        # experts run on the GPU in one wave when they fit its slots, else in the
+        # library's waves
         if self.lane is None:
             return self._forward_planned(x, out, idx_host, mh, st)
+        lane_jobs = {}
         needed_by_layer = [sorted(set(row)) for row in idx_host.reshape(self.L, -1).tolist()]
         cpu_sets = self.plan_cpu_lane(needed_by_layer, idx3)
         plans = []
@@ -483,11 +484,12 @@ class MoEStack:
                     plans.append([gpu_side])
                     mh[l] = 0
                     mh[l, 0, gpu_side] = 1
-                    lane_jobs[l] = self.submit_cpu_lane(l, cpu_sets[l], idx3[l])
-                    st.cpu_experts += len(cpu_sets[l])
-                    st.cpu_pairs += len(lane_jobs[l][1])
-                    continue
-                cpu_sets[l] = set()
+                else:  # the library's waves over the GPU's experts
+                    plans.append(self.plan_waves(l, np.array(gpu_side, dtype=np.int32), masks=mh[l]))
+                lane_jobs[l] = self.submit_cpu_lane(l, cpu_sets[l], idx3[l])
+                st.cpu_experts += len(cpu_sets[l])
+                st.cpu_pairs += len(lane_jobs[l][1])
+                continue
             # the library's plan: one wave when the layer's experts fit its slots,
             # else waves of at most half the slots, hits first, small first and last waves
             plans.append(self.plan_waves(l, idx3[l], masks=mh[l]))
@@ -526,6 +528,10 @@ class MoEStack:
                 self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts, permuted=wv > 0)
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
+            if l in lane_jobs:  # the CPU lane's rows join the GPU's before the combine
+                ticket, rows = lane_jobs[l]
+                L.moe_cpu_lane_wait(self.lane, ticket)
+                self.upload_cpu_rows(l, rows)
             self.combine(l, out)
         return st
 

@@ -156,3 +156,51 @@ def test_chained_with_cpu_lane_against_oracle():
         assert n_cpu > 0
     finally:
         st.close()
+
+
+def test_cpu_lane_with_layers_in_waves_against_oracle():
+    """The lane beside layers whose GPU experts still exceed their slots: the
+    32-token decode shape at a cap of 10% (25 slots per layer), every other miss
+    of a layer on the host; the rest run in the library's waves (resident first).
+    Indices bit-exact, every output within the bar, and the cache's hits and
+    misses equal to an LRU replay of the documented waves of the GPU's experts."""
+    from tests.test_gpu_parity import documented_waves
+    cfg = synth.get("decode32_stream")
+    layers, steps, k = 2, 2, cfg.top_k
+    rows = list(range(0, 32, 3))
+    st = MoEStack(cfg, layers=layers, cap=0.10, cpu_lane=4)
+    try:
+        assert st.streaming and st.lane and st.C == 25
+        st.lane_pick = lambda l, misses: misses[::2]
+        wr = [st.wr[l].cpu().numpy() for l in range(layers)]
+        bias = [st.bias[l].cpu().numpy() for l in range(layers)]
+        model = LRUModel(layers, 10 ** 6, st.C)
+        out = st.new_output()
+        n_cpu = most_waves = 0
+        for s in range(steps):
+            x = st.make_inputs(s)
+            r = st.forward(x, out)
+            torch.cuda.synchronize()
+            n_cpu += r.cpu_experts
+            xb, ob, idx = bits(x), bits(out), st.idx.cpu().numpy()
+            for l in range(layers):
+                needed = sorted(set(int(e) for e in idx[l].ravel()))
+                gpu_side = [e for e in needed if e not in st.last_cpu_sets[l]]
+                resident = [e for e in gpu_side if e in model.slot_of[l]]
+                order = resident + [e for e in gpu_side if e not in model.slot_of[l]]
+                waves = documented_waves(order, st.C)
+                most_waves = max(most_waves, len(waves))
+                for wave in waves:
+                    assert model.prefetch(l, wave)[0] == "ok"
+                    model.release(l)
+                o = oracle.moe_layer(xb[l], wr[l], bias[l], k, pool_slabs(st, l), st.host_shared(l), cfg.inter,
+                                     rows=rows)
+                assert (o["idx"][rows] == idx[l][rows]).all(), (s, l)
+                ratio = check_close(ob[l][rows], o["out64"][rows], f"lane + waves step {s} layer {l}")
+                print(f"step {s} layer {l}: {len(st.last_cpu_sets[l])} experts on the CPU lane, {len(waves)} GPU "
+                      f"waves, max err / max|ref| = {ratio:.2e}")
+        hits, misses, nbytes = st.stats()
+        assert (hits, misses) == (model.hits, model.misses)
+        assert n_cpu > 0 and most_waves > 1  # the lane ran beside layers in waves
+    finally:
+        st.close()
