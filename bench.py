@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--stream-steps", type=int, default=256)
     ap.add_argument("--stream-warmup", type=int, default=64)
     ap.add_argument("--no-c4", action="store_true", help="skip the streamed batch-32 decode leg")
+    ap.add_argument("--no-lane", action="store_true", help="no CPU-lane runs beside the streamed headline and C4 leg")
+    ap.add_argument("--lane-steps", type=int, default=6, help="steps of the headline's CPU-lane run")
     ap.add_argument("--c4-steps", type=int, default=16, help="timed steps of the streamed batch-32 decode leg")
     ap.add_argument("--c4-warmup", type=int, default=8)
     ap.add_argument("--chain-steps", type=int, default=128,
@@ -327,18 +329,8 @@ def decode32_stream_leg(torch, args):
     res = {"workload": r["config"]["workload"], "layers": r["config"]["layers"], "tokens_per_step": r["config"]["tokens_per_step"],
            "tokens_per_s": r["value"], "ms_per_step": r["ms_per_step"], "steps": a.steps, "warmup": a.warmup,
            **r["streaming"]}
-    if args.cpu_lane_threads > 0:
-        # the same steps with the CPU lane (row f2): each step's misses split
-        # between the copy engine and host cores
-        from routed_expert_streaming_amd.runtime import MoEStack
-        st = MoEStack(cfg)
-        xs = [st.make_inputs(s) for s in range(a.steps + a.warmup)]
-        la = copy.copy(args)
-        la.stream_steps, la.stream_warmup, la.chain_steps = a.steps, a.warmup, 0
-        res["cpu_lane"] = cpu_lane_run(torch, st, la, xs, r["value"])
-        st.close()
-        del st, xs
-        torch.cuda.empty_cache()
+    if "cpu_lane" in r:
+        res["cpu_lane"] = r["cpu_lane"]
     log(f"decode32 streamed: {res}")
     return res
 
@@ -732,6 +724,20 @@ def headline(torch, args, cfg):
         pcie["control_ms_per_step_untimed"] = round((time.perf_counter() - t1) / ctrl * 1e3, 3)
     log(f"pcie: {pcie}")
 
+    # the same stack with the CPU lane (row f2): each step's misses split between
+    # the copy engine and host cores computing them from the pinned pool (decode
+    # shapes only: on the 2048-token chunk it measured slower, 1594 against 1982
+    # tokens/s -- an expert's 57 tokens cost the host ~5 ms against 0.43 ms of
+    # copy, and the host waits for a layer's lane rows before queuing the next
+    # layer's waves)
+    lane = None
+    if args.cpu_lane_threads > 0 and st.fmt == 0 and not args.no_lane and st.T <= 64:
+        import copy
+        la = copy.copy(args)
+        la.stream_steps = min(args.steps, args.lane_steps)
+        la.stream_warmup, la.chain_steps = min(args.warmup, 2), 0
+        lane = cpu_lane_run(torch, st, la, xs, value)
+
     hits, misses = h1 - h0, m1 - m0
     result = {
         "metric": METRIC,
@@ -772,6 +778,8 @@ def headline(torch, args, cfg):
         }
         result["ffn"] = {"gate_up_ms_per_step": kern["gate_up_ms_per_step"], "ffn_ms_per_step": kern["ffn_ms_per_step"]}
     result["streaming"] = {"hit_rate": round(hits / max(hits + misses, 1), 4), **pcie}
+    if lane:
+        result["cpu_lane"] = lane
 
     # ---------------- CPU baseline: the oracle on a bounded sample
     if not args.no_cpu_baseline:

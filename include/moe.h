@@ -359,6 +359,16 @@ int moe_expert_down_fmt(const uint16_t *h, int T, int H, int I, int E, const int
  * in place of h). */
 int moe_quant_act_mx(const uint16_t *x, int rows, int K, uint8_t *out, int32_t *scales, void *stream);
 
+/* Place rows computed elsewhere among the expert outputs before the combine
+ * (glm-flash-lite page, "How it works": a CPU lane computes some experts beside
+ * the GPU's; their rows join the GPU's): dst[rows[i],:] = src[i,:] for i < n.
+ * src [n, H] fp32 (device, e.g. the CPU lane's rows uploaded in one copy); rows
+ * [n] int32 (device), distinct and inside dst; dst [*, H] fp32 (device: the y of
+ * moe_expert_ffn).  The caller owns every buffer.  MOE_E_ARG for n < 0, H <= 0
+ * or a NULL pointer, MOE_E_SHAPE unless H % 4 == 0 and n <= 65535; n = 0 is a
+ * no-op.  Rows are not checked against dst's extent (the caller's contract). */
+int moe_scatter_rows(const float *src, const int32_t *rows, int n, int H, float *dst, void *stream);
+
 /* ------------------------------------------------------------------ combine
  * Weighted combine of a token's expert outputs (LayerStoRm README, "TL;DR": the
  * selected experts' outputs are combined into the layer output; "Serve" notes: a

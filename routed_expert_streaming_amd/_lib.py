@@ -87,6 +87,7 @@ def lib():
             "moe_route_ffn_combine_workspace_bytes": ([i, i, i, i, i, i], sz),
             "moe_route_ffn_combine": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp], i),
             "moe_combine": ([vp, vp, i, i, i, i, vp, vp], i),
+            "moe_scatter_rows": ([vp, vp, i, i, vp, vp], i),
             "moe_noalloc_scratch_bytes": ([], sz),
             "moe_route_ffn_combine_noalloc": ([vp, i, i, i, vp, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp], i),
             "moe_residual_norm": ([vp, vp, i, i, ctypes.c_float, vp, vp], i),
@@ -424,6 +425,10 @@ def moe_route_ffn_combine_noalloc(x, T, H, I, w_router, bias, E, k, expert_table
 def moe_combine(y, topk_w, T, k, H, has_shared, out, stream=None):
     _check(lib().moe_combine(_ptr(y), _ptr(topk_w), T, k, H, int(bool(has_shared)), _ptr(out), _stream(stream)),
            "moe_combine")
+
+
+def moe_scatter_rows(src, rows, n, H, dst, stream=None):
+    _check(lib().moe_scatter_rows(_ptr(src), _ptr(rows), n, H, _ptr(dst), _stream(stream)), "moe_scatter_rows")
 
 
 def moe_residual_norm(add, resid, T, H, eps, x_next, stream=None):

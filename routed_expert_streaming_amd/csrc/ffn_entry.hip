@@ -102,6 +102,16 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
     }
 }
 
+// dst row rows[i] = src row i (H floats), one workgroup per (row group, column block)
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float *__restrict__ src, const int32_t *__restrict__ rows,
+                                                           int n, int H, float *__restrict__ dst) {
+    const int i = blockIdx.y;
+    const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n || j >= H) return;
+    const float4 v = *reinterpret_cast<const float4 *>(src + (size_t)i * H + j);
+    *reinterpret_cast<float4 *>(dst + (size_t)rows[i] * H + j) = v;
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w, int T,
                                                       int k, int H, int has_shared, uint16_t *__restrict__ out) {
     const int t = blockIdx.y;
@@ -749,6 +759,18 @@ extern "C" int moe_combine(const float *y, const float *topk_w, int T, int k, in
     dim3 grid((H / 4 + 255) / 256, T);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, (hipStream_t)stream, y, topk_w, T, k, H, has_shared, out);
     MOE_LAUNCH_CHECK("combine_kernel");
+    return MOE_OK;
+}
+
+extern "C" int moe_scatter_rows(const float *src, const int32_t *rows, int n, int H, float *dst, void *stream) {
+    if (n < 0 || H <= 0) return moe::fail(MOE_E_ARG, "scatter_rows: n=%d H=%d", n, H);
+    if (n == 0) return MOE_OK;
+    if (!src || !rows || !dst) return moe::fail(MOE_E_ARG, "scatter_rows: NULL pointer");
+    if (H % 4) return moe::fail(MOE_E_SHAPE, "scatter_rows: H=%d must be a multiple of 4", H);
+    if (n > 65535) return moe::fail(MOE_E_SHAPE, "scatter_rows: n=%d above 65535 rows per call", n);
+    dim3 grid((H / 4 + 255) / 256, n);
+    hipLaunchKernelGGL(scatter_rows_kernel, grid, dim3(256), 0, (hipStream_t)stream, src, rows, n, H, dst);
+    MOE_LAUNCH_CHECK("scatter_rows_kernel");
     return MOE_OK;
 }
 

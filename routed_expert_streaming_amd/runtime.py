@@ -381,7 +381,12 @@ class MoEStack:
         self.lane = L.moe_cpu_lane_create(threads)
         self.lane_threads = threads
         self._x_host = torch.empty((self.L, self.T, self.H), dtype=torch.bfloat16, pin_memory=True)
+        # the lane's rows of layer l, compact (in submission order), their pair rows
+        # in y, and the device copies they are uploaded to before moe_scatter_rows
         self._y_host = torch.empty((self.L, P, self.H), dtype=torch.float32, pin_memory=True)
+        self._rows_host = torch.empty((self.L, P), dtype=torch.int32, pin_memory=True)
+        self._y_stage = torch.empty((P, self.H), dtype=torch.float32, device=self.dev)
+        self._rows_dev = torch.empty((self.L, P), dtype=torch.int32, device=self.dev)
         self.t_cpu1, self.t_cpu8 = self.calibrate_lane()
 
     def t_cpu(self, tokens: int) -> float:
@@ -429,26 +434,32 @@ class MoEStack:
         return cpu
 
     def submit_cpu_lane(self, l: int, experts, idx_l: np.ndarray):
-        """Queue layer l's CPU-lane experts; returns (last ticket, sorted pair rows)."""
+        """Queue layer l's CPU-lane experts, their rows written compactly into
+        layer l's host rows in submission order; returns (last ticket, the pair row
+        in y of each compact row)."""
         ticket, rows = 0, []
         for e in sorted(experts):
             ts, iis = np.nonzero(idx_l == e)
             pairs = [int(t) * self.k + int(i) for t, i in zip(ts, iis)]
+            n0 = len(rows)
             ticket = L.moe_cpu_lane_submit(self.lane, self.host_slab_ptr(l, e), self.H, self.I, len(pairs),
                                            [self._x_host[l, int(t)].data_ptr() for t in ts],
-                                           [self._y_host[l, p].data_ptr() for p in pairs])
+                                           [self._y_host[l, n0 + j].data_ptr() for j in range(len(pairs))])
             rows += pairs
-        return ticket, sorted(rows)
+        return ticket, rows
 
     def upload_cpu_rows(self, l: int, rows):
-        """Copy the CPU lane's rows of layer l into y (runs of adjacent rows as one copy)."""
-        i = 0
-        while i < len(rows):
-            j = i
-            while j + 1 < len(rows) and rows[j + 1] == rows[j] + 1:
-                j += 1
-            self.y[rows[i]:rows[j] + 1].copy_(self._y_host[l, rows[i]:rows[j] + 1], non_blocking=True)
-            i = j + 1
+        """The CPU lane's rows of layer l into their pair rows of y: one copy of the
+        compact rows (and one of their row numbers), then moe_scatter_rows."""
+        n = len(rows)
+        if n == 0:
+            return
+        self._rows_host[l, :n].numpy()[:] = rows
+        self._y_stage[:n].copy_(self._y_host[l, :n], non_blocking=True)
+        self._rows_dev[l, :n].copy_(self._rows_host[l, :n], non_blocking=True)
+        for i in range(0, n, 65535):
+            m = min(65535, n - i)
+            L.moe_scatter_rows(self._y_stage[i:], self._rows_dev[l, i:], m, self.H, self.y, self.stream)
 
     # ------------------------------------------------------------------ steps
     def forward(self, x: torch.Tensor, out: torch.Tensor) -> StepStats:

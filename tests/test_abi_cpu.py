@@ -95,6 +95,13 @@ def test_ffn_combine_permute_validation():
                        FAKE, path) == L.MOE_E_ARG
     assert _status(L.moe_combine, None, FAKE, 4, 2, 256, 0, FAKE) == L.MOE_E_ARG
     assert _status(L.moe_combine, FAKE, FAKE, 4, 2, 254, 0, FAKE) == L.MOE_E_SHAPE
+    assert _status(L.moe_scatter_rows, FAKE, FAKE, -1, 256, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_scatter_rows, None, FAKE, 4, 256, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_scatter_rows, FAKE, None, 4, 256, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_scatter_rows, FAKE, FAKE, 4, 0, FAKE) == L.MOE_E_ARG
+    assert _status(L.moe_scatter_rows, FAKE, FAKE, 4, 254, FAKE) == L.MOE_E_SHAPE
+    assert _status(L.moe_scatter_rows, FAKE, FAKE, 65536, 256, FAKE) == L.MOE_E_SHAPE
+    L.moe_scatter_rows(None, None, 0, 256, None)  # no rows: nothing to do
     assert _status(L.moe_permute, FAKE, 4096, 8, 256, FAKE, FAKE, FAKE) == L.MOE_E_SHAPE
     assert _status(L.moe_permute, FAKE, 4, 8, 4, FAKE, FAKE, FAKE) == L.MOE_E_SHAPE
     assert _status(L.moe_debug_dequant, FAKE, 256, 128, 3, FAKE) == L.MOE_E_ARG

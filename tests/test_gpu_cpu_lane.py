@@ -204,3 +204,19 @@ def test_cpu_lane_with_layers_in_waves_against_oracle():
         assert n_cpu > 0 and most_waves > 1  # the lane ran beside layers in waves
     finally:
         st.close()
+
+
+def test_scatter_rows_places_rows_exactly():
+    """moe_scatter_rows: dst[rows[i]] = src[i], bit for bit; other rows untouched."""
+    rng = np.random.default_rng(7)
+    for n, H, R in [(1, 4, 3), (37, 256, 100), (700, 6144, 2048)]:
+        src = torch.from_numpy(rng.standard_normal((n, H)).astype(np.float32)).cuda()
+        rows_np = rng.permutation(R)[:n].astype(np.int32)
+        rows = torch.from_numpy(rows_np).cuda()
+        dst0 = rng.standard_normal((R, H)).astype(np.float32)
+        dst = torch.from_numpy(dst0.copy()).cuda()
+        L.moe_scatter_rows(src, rows, n, H, dst)
+        torch.cuda.synchronize()
+        want = dst0.copy()
+        want[rows_np] = src.cpu().numpy()
+        assert np.array_equal(dst.cpu().numpy().view(np.uint32), want.view(np.uint32)), (n, H, R)
