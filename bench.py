@@ -76,7 +76,6 @@ def parse():
     ap.add_argument("--stream-warmup", type=int, default=64)
     ap.add_argument("--no-c4", action="store_true", help="skip the streamed batch-32 decode leg")
     ap.add_argument("--no-lane", action="store_true", help="no CPU-lane runs beside the streamed headline and C4 leg")
-    ap.add_argument("--lane-steps", type=int, default=6, help="steps of the headline's CPU-lane run")
     ap.add_argument("--c4-steps", type=int, default=16, help="timed steps of the streamed batch-32 decode leg")
     ap.add_argument("--c4-warmup", type=int, default=8)
     ap.add_argument("--chain-steps", type=int, default=128,
@@ -734,8 +733,7 @@ def headline(torch, args, cfg):
     if args.cpu_lane_threads > 0 and st.fmt == 0 and not args.no_lane and st.T <= 64:
         import copy
         la = copy.copy(args)
-        la.stream_steps = min(args.steps, args.lane_steps)
-        la.stream_warmup, la.chain_steps = min(args.warmup, 2), 0
+        la.stream_steps, la.stream_warmup, la.chain_steps = args.steps, args.warmup, 0
         lane = cpu_lane_run(torch, st, la, xs, value)
 
     hits, misses = h1 - h0, m1 - m0
