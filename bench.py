@@ -725,10 +725,9 @@ def headline(torch, args, cfg):
 
     # the same stack with the CPU lane (row f2): each step's misses split between
     # the copy engine and host cores computing them from the pinned pool (decode
-    # shapes only: on the 2048-token chunk it measured slower, 1594 against 1982
-    # tokens/s -- an expert's 57 tokens cost the host ~5 ms against 0.43 ms of
-    # copy, and the host waits for a layer's lane rows before queuing the next
-    # layer's waves)
+    # shapes only: on the 2048-token chunk it measured slower, 1797 against 1962
+    # tokens/s -- an expert's 64 tokens cost the host ~6.6 ms against 0.43 ms of
+    # copy, so the lane can take only ~8% of the misses)
     lane = None
     if args.cpu_lane_threads > 0 and st.fmt == 0 and not args.no_lane and st.T <= 64:
         import copy

@@ -388,18 +388,28 @@ class MoEStack:
         self._y_stage = torch.empty((P, self.H), dtype=torch.float32, device=self.dev)
         self._rows_dev = torch.empty((self.L, P), dtype=torch.int32, device=self.dev)
         self.t_cpu1, self.t_cpu8 = self.calibrate_lane()
+        self.t_cpu_big = None
+        if self.T > 8:  # a third point: an expert's average token count at this batch
+            m = max(9, min(self.T, (self.T * self.k + self.E - 1) // self.E))
+            self.t_cpu_big = (m, self.calibrate_lane(counts=(m,))[0])
 
     def t_cpu(self, tokens: int) -> float:
-        """CPU lane seconds for one expert and `tokens` tokens (calibrated at 1 and 8)."""
-        return self.t_cpu1 + (tokens - 1) * (self.t_cpu8 - self.t_cpu1) / 7.0
+        """CPU lane seconds for one expert and `tokens` tokens: linear through the
+        calibrated 1 and 8 tokens, and above 8 through 8 and the third calibrated
+        count (stacks of more than 8 tokens)."""
+        if tokens <= 8 or self.t_cpu_big is None:
+            return self.t_cpu1 + (tokens - 1) * (self.t_cpu8 - self.t_cpu1) / 7.0
+        m, t_m = self.t_cpu_big
+        return self.t_cpu8 + (tokens - 8) * (t_m - self.t_cpu8) / (m - 8)
 
-    def calibrate_lane(self, reps: int = 3):
-        """Time the lane on layer 0's first slabs (1 and 8 tokens), best of reps."""
+    def calibrate_lane(self, reps: int = 3, counts=(1, 8)):
+        """Time the lane on layer 0's first slabs (for each token count), best of reps."""
         import time
-        ys = torch.empty((8, self.H), dtype=torch.float32)
-        xs = torch.zeros((8, self.H), dtype=torch.bfloat16)
+        n = max(counts)
+        ys = torch.empty((n, self.H), dtype=torch.float32)
+        xs = torch.zeros((n, self.H), dtype=torch.bfloat16)
         out = []
-        for M in (1, 8):
+        for M in counts:
             best = float("inf")
             for r in range(reps + 1):
                 slab = self.host_slab_ptr(0, r % self.E)
@@ -410,7 +420,7 @@ class MoEStack:
                 if r:  # the first run warms the threads
                     best = min(best, time.perf_counter() - t0)
             out.append(best)
-        return out[0], out[1]
+        return tuple(out)
 
     def plan_cpu_lane(self, needed_by_layer, idx_host, layers=None, cpu_head: float = 0.0):
         """Experts of each layer that the CPU lane computes (layers: the layer ids
@@ -448,9 +458,10 @@ class MoEStack:
             rows += pairs
         return ticket, rows
 
-    def upload_cpu_rows(self, l: int, rows):
-        """The CPU lane's rows of layer l into their pair rows of y: one copy of the
-        compact rows (and one of their row numbers), then moe_scatter_rows."""
+    def upload_cpu_rows(self, l: int, rows, y=None):
+        """The CPU lane's rows of layer l into their pair rows of y (default self.y):
+        one copy of the compact rows (and one of their row numbers), then
+        moe_scatter_rows."""
         n = len(rows)
         if n == 0:
             return
@@ -459,7 +470,8 @@ class MoEStack:
         self._rows_dev[l, :n].copy_(self._rows_host[l, :n], non_blocking=True)
         for i in range(0, n, 65535):
             m = min(65535, n - i)
-            L.moe_scatter_rows(self._y_stage[i:], self._rows_dev[l, i:], m, self.H, self.y, self.stream)
+            L.moe_scatter_rows(self._y_stage[i:], self._rows_dev[l, i:], m, self.H, self.y if y is None else y,
+                               self.stream)
 
     # ------------------------------------------------------------------ steps
     def forward(self, x: torch.Tensor, out: torch.Tensor) -> StepStats:
@@ -515,7 +527,19 @@ class MoEStack:
         for l, waves in enumerate(plans):
             if single[l]:
                 st.copies += L.moe_cache_prefetch_async(self.cache, l, waves[0])
+        pending = []  # a layer in waves whose lane rows and combine wait for the next layer's waves
+
+        def flush():
+            while pending:
+                lp, yp = pending.pop()
+                ticket, rows = lane_jobs[lp]
+                L.moe_cpu_lane_wait(self.lane, ticket)
+                self.upload_cpu_rows(lp, rows, y=yp)
+                self.combine(lp, out, y=yp)
+
         for l, waves in enumerate(plans):
+            if single[l]:
+                flush()
             if single[l] and l in lane_jobs:
                 # GPU lane: the layer's hits and streamed misses (masked call), then
                 # the CPU lane's rows, then the combine of all of them
@@ -534,16 +558,22 @@ class MoEStack:
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
                 continue
+            # a layer in waves: its y rows by layer parity, so that the lane rows and
+            # the combine of the layer before it can wait until this layer's waves
+            # are queued (the host's wait for the lane then leaves the copy engine
+            # this layer's copies to work on)
+            y = self._y2 if (self._y2 is not None and l % 2 == 1) else self.y
             for wv, experts in enumerate(waves):
                 st.copies += L.moe_cache_prefetch(self.cache, l, experts, self.stream)
-                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts, permuted=wv > 0)
+                self.ffn(x, l, mask=self.masks[l, wv], shared=(wv == 0), experts=experts, permuted=wv > 0, y=y)
                 L.moe_cache_release(self.cache, l, self.stream)
                 st.waves += 1
-            if l in lane_jobs:  # the CPU lane's rows join the GPU's before the combine
-                ticket, rows = lane_jobs[l]
-                L.moe_cpu_lane_wait(self.lane, ticket)
-                self.upload_cpu_rows(l, rows)
-            self.combine(l, out)
+            flush()
+            if l in lane_jobs:
+                pending.append((l, y))
+            else:
+                self.combine(l, out, y=y)
+        flush()
         return st
 
     def _upload_masks(self, mh: np.ndarray):
