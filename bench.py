@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--stream-warmup", type=int, default=64)
     ap.add_argument("--no-c4", action="store_true", help="skip the streamed batch-32 decode leg")
     ap.add_argument("--no-lane", action="store_true", help="no CPU-lane runs beside the streamed headline and C4 leg")
+    ap.add_argument("--no-stream-half-cap", dest="stream_half_cap", action="store_false",
+                    help="skip the streamed batch-1 decode at half the slots")
     ap.add_argument("--c4-steps", type=int, default=16, help="timed steps of the streamed batch-32 decode leg")
     ap.add_argument("--c4-warmup", type=int, default=8)
     ap.add_argument("--chain-steps", type=int, default=128,
@@ -298,12 +300,36 @@ def streaming_leg(torch, args, resident_ms_per_step: float):
     lane = (cpu_lane_run(torch, st, args, xs, args.stream_steps * cfg.tokens / wall)
             if args.cpu_lane_threads > 0 and st.T <= 64 and st.fmt == 0 else None)
     st.close()
+    # the same configuration at half the slots (the harder end of the 60-80% hit
+    # range of the configuration's description): tokens/s, hit rate, link time
+    half = None
+    if args.stream_half_cap:
+        sh = MoEStack(cfg, cap=cfg.cap / 2)
+        for s in range(args.stream_warmup):
+            sh.forward(xs[s % n_in], out)
+        torch.cuda.synchronize()
+        g0, q0, c0 = sh.stats()
+        t2 = time.perf_counter()
+        for s in range(args.stream_steps):
+            sh.forward(xs[s % n_in], out)
+        torch.cuda.synchronize()
+        w2 = time.perf_counter() - t2
+        g1, q1, c1 = sh.stats()
+        nb = (c1 - c0) / args.stream_steps
+        half = {"cache_slots_per_layer": sh.C, "tokens_per_s": round(args.stream_steps * cfg.tokens / w2, 2),
+                "ms_per_step": round(w2 / args.stream_steps * 1e3, 3),
+                "hit_rate": round((g1 - g0) / max(g1 - g0 + q1 - q0, 1), 4), "h2d_bytes_per_step": int(nb),
+                "wall_over_link_time": round((w2 / args.stream_steps) / (nb / (link[0] * 1e9)), 4) if nb else None}
+        sh.close()
+        del sh
     hits, misses = h1 - h0, m1 - m0
     res = {"workload": cfg.name, "layers": st.L, "cache_slots_per_layer": st.C,
            "tokens_per_s": round(args.stream_steps * cfg.tokens / wall, 2),
            "ms_per_step": round(wall / args.stream_steps * 1e3, 3),
            "hit_rate": round(hits / max(hits + misses, 1), 4), "resident_ms_per_step": round(resident_ms_per_step, 3),
            "pcie": pcie, "steps": args.stream_steps, "warmup": args.stream_warmup}
+    if half:
+        res["half_cap"] = half
     if chained:
         res["chained"] = chained
     if lane:
